@@ -1,0 +1,291 @@
+"""CPU oracle for dynamic block-sparse attention (TEST INFRASTRUCTURE ONLY).
+
+This module is the plain, slow, obviously-correct statement of what the GPU
+library computes. Only the tests, the package's smoke check and the benchmark's
+CPU-baseline leg may import it; the product path never does. It shares no code
+with the HIP library and imports nothing from the package.
+
+It follows the InfiniteHiP page (2502.08910), section 3.4:
+  * "Formal Mechanism of a Single Pruning Stage", steps 1-8 (query blocking,
+    chunk partitioning, per-head representative, chunk score, top-K chunks,
+    index assembly, query-block propagation);
+  * "The Representative Token Selection Algorithm (SelectRep)" (Algorithm 3);
+  * "Important: Sink and Streaming Tokens Are Never Pruned" (Algorithm 1,
+    initial candidate set) and "The Sink/Streaming Token Special Handling";
+and the attention over the active key set as written on the InfLLM blog page
+("Mathematical Formulation of Efficient Softmax Normalization") and as the
+masked softmax of the MInference page (section on the sparse-attention
+problem formulation), with causal masking inside the kernel.
+
+Readings taken where the pages are silent or garbled (each is listed with its
+reason in the project's design notes):
+  * scores are unscaled fp32 dot products; the softmax scale is applied only in
+    attention (the pages omit the constant scale "for brevity");
+  * chunk score = max over ALL query heads and all queries of the block, each
+    head using its own representative; GQA head h reads kv head h // (Hq/Hkv);
+  * SelectRep midpoint = (a + z + 1) // 2 on a 0-based inclusive range [a, z];
+    the right branch wins only if its score is strictly greater;
+  * top-K orders chunks by (score descending, chunk index ascending); a stage
+    with no more chunks than it keeps keeps them all;
+  * the prunable middle of query block [s, e) is [n_sink, e - n_window); the
+    window is the n_window most recent keys [e - n_window, e) (it contains the
+    block itself); the stage-1 chunk grid is anchored at n_sink and the tail
+    that does not fill a whole chunk joins the window;
+  * masked keys are excluded exactly (the additive -c(1-M) form with c=1e5
+    underflows to the same result), key p is visible to query t iff p <= t;
+  * softmax and the P.V product are evaluated in fp64 and cast to fp32.
+
+Every function here is pinned by tests/test_oracle.py against what the pages
+and the mathematics fix (closed forms, brute force, special cases reducing to
+textbook attention, invariants). The one part with no pin is the recall of
+SelectRep against exact top-k on real attention (the pages only give
+model-based recall): that quality figure is reported, never graded.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Callable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Params:
+    """One pruning configuration: the stage tuples (l_c, k) of the InfiniteHiP
+    page ("Stage Configuration") with a single query block size b_q, plus the
+    always-kept sink and window counts."""
+    block_q: int
+    chunk: Tuple[int, ...]
+    keep: Tuple[int, ...]
+    n_sink: int
+    n_window: int
+
+
+def index_width(p: Params) -> int:
+    """Row width of the index output: the largest possible row (sinks, the last
+    stage's keep, window plus the chunk-grid tail), rounded up to 64."""
+    n = p.n_sink + p.keep[-1] + p.n_window + p.chunk[0] - 1
+    return (n + 63) // 64 * 64
+
+
+# --------------------------------------------------------------------------- #
+# geometry of one query block (Algorithm 1 initial set; step 3 chunk grid)     #
+# --------------------------------------------------------------------------- #
+@dataclass(frozen=True)
+class Geometry:
+    s: int          # first query of the block
+    e: int          # one past the last query
+    sink_hi: int    # sinks are [0, sink_hi)
+    mid_lo: int     # prunable middle [mid_lo, mid_hi)
+    mid_hi: int
+    n1: int         # whole stage-1 chunks in the middle
+
+
+def geometry(s: int, e: int, p: Params) -> Geometry:
+    w0 = e - p.n_window                       # window = [w0, e)
+    m = max(0, w0 - p.n_sink)                 # size of the prunable middle
+    n1 = m // p.chunk[0]
+    mid_hi = p.n_sink + n1 * p.chunk[0]       # the tail [mid_hi, w0) joins the window
+    return Geometry(s, e, min(p.n_sink, e), p.n_sink, max(mid_hi, p.n_sink), n1)
+
+
+# --------------------------------------------------------------------------- #
+# scores                                                                      #
+# --------------------------------------------------------------------------- #
+def rep_score(qh: np.ndarray, krows: np.ndarray) -> np.ndarray:
+    """sigma(k) = max_t q_t . k for each key row, fp32 dot products.
+
+    qh: [b_q, d] float32, krows: [n, d] float32 -> [n] float32.
+    """
+    qh = np.asarray(qh, dtype=np.float32)
+    krows = np.asarray(krows, dtype=np.float32)
+    if krows.shape[0] == 0:
+        return np.zeros(0, dtype=np.float32)
+    return (qh @ krows.T).max(axis=0).astype(np.float32)
+
+
+def select_rep(qh: np.ndarray, K, g: int, chunk: np.ndarray,
+               visit: Optional[Callable[[int], None]] = None) -> int:
+    """SelectRep (Algorithm 3) for one head and one chunk of key positions.
+
+    Halves the range ceil(log2 l) times; each time the first key of each half
+    represents it, and the half whose representative scores strictly higher
+    wins (ties go left). Returns the chosen key position.
+    """
+    l = len(chunk)
+    a, z = 0, l - 1
+    n_iter = int(np.ceil(np.log2(l))) if l > 1 else 0
+    for _ in range(n_iter):
+        mid = (a + z + 1) // 2
+        rows = K[g, np.array([chunk[a], chunk[mid]])]
+        sig = rep_score(qh, rows)
+        if visit is not None:
+            visit(int(chunk[a]))
+            visit(int(chunk[mid]))
+        if sig[1] > sig[0]:
+            a = mid
+        else:
+            z = mid - 1
+    assert a == z or l == 1
+    return int(chunk[a])
+
+
+def select_rep_all(qh: np.ndarray, K, g: int, P2: np.ndarray,
+                   visited: Optional[list] = None) -> np.ndarray:
+    """select_rep applied to every row of P2 ([n_chunks, l]) at once: the same
+    per-chunk steps, with the dot products of all chunks batched. If
+    ``visited`` is a list, the arrays of key positions read are appended."""
+    nc, l = P2.shape
+    a = np.zeros(nc, dtype=np.int64)
+    z = np.full(nc, l - 1, dtype=np.int64)
+    n_iter = int(np.ceil(np.log2(l))) if l > 1 else 0
+    rows = np.arange(nc)
+    for _ in range(n_iter):
+        mid = (a + z + 1) // 2
+        sl = rep_score(qh, K[g, P2[rows, a]])
+        sr = rep_score(qh, K[g, P2[rows, mid]])
+        if visited is not None:
+            visited.append(P2[rows, a])
+            visited.append(P2[rows, mid])
+        right = sr > sl
+        a = np.where(right, mid, a)
+        z = np.where(right, z, mid - 1)
+    assert np.all(a == z) or l == 1
+    return P2[rows, a]
+
+
+def chunk_scores(Q: np.ndarray, K, P: np.ndarray, l: int,
+                 visited: Optional[list] = None) -> np.ndarray:
+    """Step 4-5: s_j = max over heads h and block queries t of q_{h,t} . k_{r_{h,j}}.
+
+    Q: [Hq, b_q, d]; K indexable as K[g, positions] -> [n, d]; P: the ascending
+    candidate positions, partitioned into contiguous groups of l entries.
+    If ``visited`` is a list, (kv head, positions read) pairs are appended.
+    """
+    Hq = Q.shape[0]
+    Hkv = K.shape[0]
+    G = Hq // Hkv
+    nc = len(P) // l
+    P2 = np.asarray(P).reshape(nc, l)
+    s = np.full(nc, -np.inf, dtype=np.float32)
+    for h in range(Hq):
+        g = h // G
+        vis = [] if visited is not None else None
+        r = select_rep_all(Q[h], K, g, P2, vis)
+        if visited is not None:
+            visited.extend((g, v) for v in vis)
+        s = np.maximum(s, rep_score(Q[h], K[g, r]))
+    return s
+
+
+def top_k(s: np.ndarray, k: int) -> np.ndarray:
+    """Step 6: indices of the k highest scores, ties to the lower index; a full
+    sort by (score descending, index ascending). Returned in ascending order."""
+    n = len(s)
+    if n <= k:
+        return np.arange(n)
+    order = np.lexsort((np.arange(n), -np.asarray(s, dtype=np.float64)))
+    return np.sort(order[:k])
+
+
+# --------------------------------------------------------------------------- #
+# pruning of one query block                                                  #
+# --------------------------------------------------------------------------- #
+def prune_block(Q: np.ndarray, K, s: int, e: int, p: Params,
+                trace: Optional[list] = None) -> np.ndarray:
+    """The index row of query block [s, e): sinks, pruned middle, window.
+
+    Q: [Hq, e-s, d] float32 (the block's queries); K: [Hkv, >=e, d] indexable.
+    Returns the ascending int64 array of key positions (no padding).
+    If ``trace`` is a list, one entry per executed stage is appended:
+    (stage, n_chunks, kept chunk ids, representative positions per head).
+    """
+    geo = geometry(s, e, p)
+    P = np.arange(geo.mid_lo, geo.mid_hi, dtype=np.int64)
+    for i, (l, k) in enumerate(zip(p.chunk, p.keep)):
+        nc = len(P) // l
+        kc = k // l
+        if nc <= kc:
+            continue
+        sc = chunk_scores(Q, K, P, l)
+        sel = top_k(sc, kc)
+        if trace is not None:
+            trace.append((i, nc, sel, sc))
+        P = np.asarray(P).reshape(nc, l)[sel].reshape(-1)
+    row = np.concatenate([np.arange(0, geo.sink_hi, dtype=np.int64), P,
+                          np.arange(geo.mid_hi, e, dtype=np.int64)])
+    return row
+
+
+def visited_rows(Q: np.ndarray, K, s: int, e: int, p: Params) -> List[int]:
+    """Per stage, the number of distinct (kv head, key position) rows SelectRep
+    reads for block [s, e) (0 for a stage that keeps everything): the
+    algorithmic K traffic of the stage."""
+    geo = geometry(s, e, p)
+    P = np.arange(geo.mid_lo, geo.mid_hi, dtype=np.int64)
+    out = []
+    for l, k in zip(p.chunk, p.keep):
+        nc = len(P) // l
+        kc = k // l
+        if nc <= kc:
+            out.append(0)
+            continue
+        vis: list = []
+        sc = chunk_scores(Q, K, P, l, visited=vis)
+        keys = np.unique(np.concatenate([g * (1 << 40) + v for g, v in vis]))
+        out.append(int(keys.size))
+        P = P.reshape(nc, l)[top_k(sc, kc)].reshape(-1)
+    return out
+
+
+def block_bounds(m: int, T: int, p: Params, decode: bool) -> Tuple[int, int]:
+    """Step 1 query blocking: block m is [m*b_q, (m+1)*b_q); a decode step is the
+    single query T-1."""
+    if decode:
+        return T - 1, T
+    return m * p.block_q, (m + 1) * p.block_q
+
+
+def pad_row(row: np.ndarray, width: int) -> np.ndarray:
+    out = np.full(width, -1, dtype=np.int32)
+    out[:len(row)] = row
+    return out
+
+
+# --------------------------------------------------------------------------- #
+# attention over an index row                                                 #
+# --------------------------------------------------------------------------- #
+def attend_block(Q: np.ndarray, K, V, row: np.ndarray, s: int, scale: float) -> np.ndarray:
+    """out[h, t] = sum_{p in row, p <= s+t} softmax_p(scale * q_{h,s+t} . k_p) v_p.
+
+    Q: [Hq, n_q, d] float32; K, V: [Hkv, >=T, d] indexable; row: key positions
+    (entries < 0 are padding and ignored). Dot products are fp32 (exact on the
+    input grid), softmax and P.V are fp64, the result is cast to fp32.
+    """
+    row = np.asarray(row, dtype=np.int64)
+    row = row[row >= 0]
+    Hq, nq, d = Q.shape
+    Hkv = K.shape[0]
+    G = Hq // Hkv
+    out = np.zeros((Hq, nq, d), dtype=np.float32)
+    tpos = s + np.arange(nq)
+    visible = row[None, :] <= tpos[:, None]               # causal mask [nq, n]
+    for g in range(Hkv):
+        kr = np.asarray(K[g, row], dtype=np.float32)
+        vr = np.asarray(V[g, row], dtype=np.float64)
+        for h in range(g * G, (g + 1) * G):
+            z = (np.asarray(Q[h], dtype=np.float32) @ kr.T).astype(np.float64) * scale
+            z = np.where(visible, z, -np.inf)
+            zmax = z.max(axis=1, keepdims=True)
+            w = np.exp(z - zmax)
+            out[h] = ((w @ vr) / w.sum(axis=1, keepdims=True)).astype(np.float32)
+    return out
+
+
+def dense_block(Q: np.ndarray, K, V, s: int, e: int, scale: float) -> np.ndarray:
+    """Exact causal attention of queries [s, e) over keys [0, e)."""
+    return attend_block(Q, K, V, np.arange(e, dtype=np.int64), s, scale)
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / np.sqrt(d)

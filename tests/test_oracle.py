@@ -1,0 +1,392 @@
+"""Pins for the CPU oracle: what the pages and the mathematics fix.
+
+None of these tests touches the GPU or the HIP library. Each checks the oracle
+against something other than itself: values printed on the pages (fixtures in
+tests/golden/), closed forms, brute force on tiny inputs, and special cases that
+reduce to textbook attention computed by a library routine.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from dynamic_sparse_attention_query_amd import gen
+from oracle import ref
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def grid(rng, shape):
+    return rng.integers(-8, 9, size=shape).astype(np.float32) / np.float32(8)
+
+
+# --------------------------------------------------------------------------- #
+# exactness of scores on the input grid                                       #
+# --------------------------------------------------------------------------- #
+def test_grid_dot_products_are_exact_in_any_order():
+    rng = np.random.default_rng(0)
+    q = rng.integers(-8, 9, size=(16, 128))
+    k = rng.integers(-8, 9, size=(300, 128))
+    exact = (q @ k.T).astype(np.float64) / 64.0               # integer arithmetic
+    blas = ref.rep_score(q.astype(np.float32) / 8, k.astype(np.float32) / 8)
+    assert np.array_equal(blas.astype(np.float64), exact.max(axis=0))
+    qf, kf = q.astype(np.float32) / 8, k.astype(np.float32) / 8
+    for trial in range(3):
+        perm = rng.permutation(128)
+        acc = np.zeros((16, 300), dtype=np.float32)
+        for i in perm:                                         # shuffled fp32 summation
+            acc = (acc + qf[:, i:i + 1] * kf[None, :, i]).astype(np.float32)
+        assert np.array_equal(acc.astype(np.float64), exact)
+
+
+# --------------------------------------------------------------------------- #
+# a1: candidate set, sinks, window -- the pages' worked counts                #
+# --------------------------------------------------------------------------- #
+def test_page_counts_at_one_million_tokens():
+    g = _load("p1_counts.json")
+    p = ref.Params(1, tuple(g["stage_chunk"]), tuple(g["stage_keep"]), g["n_sink"], g["n_stream"])
+    T = g["T"]
+    s, e = ref.block_bounds(0, T, p, decode=True)
+    geo = ref.geometry(s, e, p)
+    always = geo.sink_hi + (e - (geo.mid_lo + (e - p.n_window - geo.mid_lo)))  # sinks + window
+    middle = (e - p.n_window) - geo.mid_lo
+    assert middle == g["pruned_middle"]
+    assert geo.sink_hi + p.n_window == g["always_kept"] == always
+    assert abs(geo.n1 - g["stage1_chunks_approx"]) / g["stage1_chunks_approx"] < 0.01
+    assert abs(p.keep[0] // p.chunk[1] - g["stage2_chunks_approx"]) / 1000 < 0.03
+    assert abs(p.keep[1] // p.chunk[2] - g["stage3_chunks_approx"]) / 1000 < 0.03
+
+
+def test_infllm_active_length():
+    g = _load("p2_active.json")
+    S, Kc, C, W = g["S"], g["K"], g["C"], g["W"]
+    p = ref.Params(1, (C,), (Kc * C,), S, W)
+    T = S + W + 20 * C                       # middle is a whole number of chunks
+    rng = np.random.default_rng(1)
+    K = grid(rng, (1, T, 16))
+    q = grid(rng, (1, 1, 16))
+    s, e = ref.block_bounds(0, T, p, decode=True)
+    row = ref.prune_block(q, K, s, e, p)
+    assert len(row) == g["L_active"]
+
+
+# --------------------------------------------------------------------------- #
+# a2: SelectRep                                                               #
+# --------------------------------------------------------------------------- #
+def select_rep_recursive(qh, K, g, chunk):
+    """The tournament as a recursion: a range is represented by its first key;
+    split at the round-half-up midpoint; the right half wins only on a strictly
+    greater representative score."""
+    def sig(pos):
+        return float((qh @ K[g, pos]).max())
+
+    def go(lo, hi):                          # inclusive range of chunk offsets
+        if lo == hi:
+            return lo
+        mid = (lo + hi + 1) // 2
+        if sig(chunk[mid]) > sig(chunk[lo]):
+            return go(mid, hi)
+        return go(lo, mid - 1)
+    return int(chunk[go(0, len(chunk) - 1)])
+
+
+@pytest.mark.parametrize("l", [1, 2, 4, 8, 16, 32, 64, 256])
+def test_selectrep_iterative_matches_recursive(l):
+    rng = np.random.default_rng(l)
+    d, bq = 16, 4
+    K = grid(rng, (2, 2048, d))
+    for trial in range(20):
+        qh = grid(rng, (bq, d))
+        g = int(rng.integers(0, 2))
+        st = int(rng.integers(0, 2048 - l))
+        chunk = np.arange(st, st + l)
+        r_rec = select_rep_recursive(qh, K, g, chunk)
+        r_it = ref.select_rep(qh, K, g, chunk)
+        r_vec = ref.select_rep_all(qh, K, g, chunk[None, :])[0]
+        assert r_rec == r_it == r_vec
+
+
+def test_selectrep_evaluation_count():
+    g = _load("p1_counts.json")["selectrep_evaluations"]
+    rng = np.random.default_rng(3)
+    K = grid(rng, (1, 4096, 8))
+    qh = grid(rng, (2, 8))
+    for l_str, n_eval in g.items():
+        l = int(l_str)
+        seen = []
+        ref.select_rep(qh, K, 0, np.arange(100, 100 + l), visit=seen.append)
+        assert len(seen) == n_eval == 2 * math.ceil(math.log2(l))
+        assert len(set(seen)) == 1 + int(math.log2(l))
+
+
+def test_selectrep_monotone_chunks_reach_true_argmax():
+    d = 8
+    q = np.zeros((1, d), dtype=np.float32)
+    q[0, 0] = 1.0
+    for l in (4, 16, 64):
+        K = np.zeros((1, l, d), dtype=np.float32)
+        K[0, :, 0] = np.arange(l) / 64.0                # score strictly increasing
+        assert ref.select_rep(q, K, 0, np.arange(l)) == l - 1
+        K[0, :, 0] = -np.arange(l) / 64.0               # strictly decreasing
+        assert ref.select_rep(q, K, 0, np.arange(l)) == 0
+
+
+def test_selectrep_score_dominates_first_and_visited():
+    rng = np.random.default_rng(5)
+    K = grid(rng, (1, 1024, 16))
+    for trial in range(50):
+        qh = grid(rng, (3, 16))
+        chunk = np.arange(64 * trial % 960, 64 * trial % 960 + 32)
+        seen = []
+        r = ref.select_rep(qh, K, 0, chunk, visit=seen.append)
+        sig = lambda p: (qh @ K[0, p]).max()
+        assert sig(r) >= sig(chunk[0])
+        assert sig(r) == max(sig(p) for p in seen)
+
+
+# --------------------------------------------------------------------------- #
+# a3 + a4 + a5: chunk score, top-K, assembly                                  #
+# --------------------------------------------------------------------------- #
+def _token_scores(Q, K, G):
+    """max over heads and block queries of q.k for every key (library matmul)."""
+    Hq = Q.shape[0]
+    S = np.stack([Q[h] @ K[h // G].T for h in range(Hq)])   # [Hq, bq, T]
+    return S.max(axis=(0, 1))
+
+
+def test_chunk_size_one_is_token_topk():
+    """l_c = 1: SelectRep is the token itself, so a stage is plain token-level
+    top-k of max_{h,t} q.k, ties to the lower position."""
+    rng = np.random.default_rng(7)
+    Hq, Hkv, d, bq, T = 4, 2, 16, 8, 512
+    Q = grid(rng, (Hq, T, d))
+    K = grid(rng, (Hkv, T, d))
+    p = ref.Params(bq, (1,), (40,), 8, 32)
+    for m in (20, 45, 63):
+        s, e = ref.block_bounds(m, T, p, decode=False)
+        row = ref.prune_block(Q[:, s:e], K, s, e, p)
+        geo = ref.geometry(s, e, p)
+        sc = _token_scores(Q[:, s:e], K, Hq // Hkv)[geo.mid_lo:geo.mid_hi]
+        order = np.argsort(-sc.astype(np.float64), kind="stable")[:40]
+        expect = np.sort(order + geo.mid_lo)
+        mid = row[(row >= geo.mid_lo) & (row < geo.mid_hi)]
+        assert np.array_equal(mid, expect)
+
+
+def test_constant_chunks_rank_by_max_over_heads_and_queries():
+    """Keys constant inside each stage-1 chunk (per kv head): every
+    representative has the chunk's exact score, so the two-stage result is the
+    top (k2) tokens by max over ALL heads and queries, ties to the lower
+    position (a mean over heads, or one head only, fails this)."""
+    rng = np.random.default_rng(11)
+    Hq, Hkv, d, bq = 8, 2, 16, 4
+    l1, l2 = 16, 4
+    T = 16 * 80
+    K = np.repeat(grid(rng, (Hkv, T // l1, d)), l1, axis=1)
+    Q = grid(rng, (Hq, T, d))
+    p = ref.Params(bq, (l1, l2), (160, 48), 16, 64)
+    for m in (100, 250, 319):
+        s, e = ref.block_bounds(m, T, p, decode=False)
+        row = ref.prune_block(Q[:, s:e], K, s, e, p)
+        geo = ref.geometry(s, e, p)
+        sc = _token_scores(Q[:, s:e], K, Hq // Hkv)[geo.mid_lo:geo.mid_hi]
+        expect = np.sort(np.argsort(-sc.astype(np.float64), kind="stable")[:48] + geo.mid_lo)
+        mid = row[(row >= geo.mid_lo) & (row < geo.mid_hi)]
+        assert np.array_equal(mid, expect)
+
+
+def test_topk_matches_brute_force_with_ties():
+    rng = np.random.default_rng(13)
+    for trial in range(200):
+        n = int(rng.integers(1, 13))
+        k = int(rng.integers(0, n + 2))
+        s = rng.integers(-3, 4, size=n).astype(np.float32)   # heavy ties
+        got = ref.top_k(s, k)
+        if n <= k:
+            assert np.array_equal(got, np.arange(n))
+            continue
+        valid = []
+        for S in itertools.combinations(range(n), k):
+            Sset = set(S)
+            ok = all(s[j] > s[o] or (s[j] == s[o] and j < o)
+                     for j in Sset for o in range(n) if o not in Sset)
+            if ok:
+                valid.append(S)
+        assert len(valid) == 1
+        assert tuple(got.tolist()) == valid[0]
+
+
+def _small_case(seed, Hq=4, Hkv=2, d=16, T=1024):
+    rng = np.random.default_rng(seed)
+    Q = grid(rng, (Hq, T, d))
+    K = grid(rng, (Hkv, T, d))
+    V = rng.standard_normal((Hkv, T, d)).astype(np.float32)
+    return Q, K, V
+
+
+def test_row_invariants_and_count():
+    Q, K, V = _small_case(17)
+    T = Q.shape[1]
+    p = ref.Params(16, (32, 8), (256, 64), 16, 64)
+    for m in range(T // 16):
+        s, e = ref.block_bounds(m, T, p, decode=False)
+        row = ref.prune_block(Q[:, s:e], K, s, e, p)
+        geo = ref.geometry(s, e, p)
+        assert np.all(np.diff(row) > 0) and row[-1] == e - 1 and row[0] == 0
+        assert set(range(min(16, e))) <= set(row.tolist())                  # sinks
+        assert set(range(max(0, e - 64), e)) <= set(row.tolist())           # window
+        n_mid = geo.mid_hi - geo.mid_lo
+        assert len(row) == geo.sink_hi + min(64, n_mid) + (e - geo.mid_hi)
+        assert len(row) <= ref.index_width(p)
+        if n_mid >= 64:
+            rem = (e - 64 - 16) % 32
+            assert len(row) == 16 + 64 + 64 + rem
+
+
+# --------------------------------------------------------------------------- #
+# a6-a8: attention                                                            #
+# --------------------------------------------------------------------------- #
+def _sdpa(Q, K, V, scale, mask=None, causal=False):
+    torch = pytest.importorskip("torch")
+    Hq, Hkv = Q.shape[0], K.shape[0]
+    G = Hq // Hkv
+    q = torch.from_numpy(Q.astype(np.float64))[None]
+    k = torch.from_numpy(np.repeat(K, G, axis=0).astype(np.float64))[None]
+    v = torch.from_numpy(np.repeat(V, G, axis=0).astype(np.float64))[None]
+    if mask is not None:
+        mask = torch.from_numpy(mask)
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask,
+                                                         is_causal=causal, scale=scale)
+    return o[0].numpy()
+
+
+def test_dense_matches_library_causal_attention():
+    Q, K, V = _small_case(19, T=256)
+    scale = ref.default_scale(16)
+    out = np.concatenate([ref.dense_block(Q[:, s:s + 32], K, V, s, s + 32, scale)
+                          for s in range(0, 256, 32)], axis=1)
+    expect = _sdpa(Q, K, V, scale, causal=True)
+    np.testing.assert_allclose(out, expect, rtol=2e-6, atol=2e-6)
+
+
+def test_full_budget_is_dense_attention_bitwise():
+    Q, K, V = _small_case(23)
+    T = Q.shape[1]
+    p = ref.Params(32, (32, 8), (T, T), 16, 64)
+    scale = ref.default_scale(16)
+    for m in (0, 5, 17, 31):
+        s, e = ref.block_bounds(m, T, p, decode=False)
+        row = ref.prune_block(Q[:, s:e], K, s, e, p)
+        assert np.array_equal(row, np.arange(e))
+        a = ref.attend_block(Q[:, s:e], K, V, row, s, scale)
+        b = ref.dense_block(Q[:, s:e], K, V, s, e, scale)
+        assert np.array_equal(a, b)
+
+
+def test_zero_budget_is_sink_plus_window_attention():
+    """keep = 0: only sinks and the local window remain (the A-shape /
+    StreamingLLM pattern), checked against a library attention with that mask.
+    The sizes make the middle a whole number of chunks, so no grid tail joins
+    the window."""
+    Q, K, V = _small_case(29, T=512)
+    T = 512
+    n_sink, n_win, bq = 16, 48, 16
+    p = ref.Params(bq, (16,), (0,), n_sink, n_win)
+    scale = ref.default_scale(16)
+    t = np.arange(T)
+    e_of = (t // bq + 1) * bq                       # block end of each query
+    ok = (t[None, :] <= t[:, None]) & ((t[None, :] < n_sink) |
+                                        (t[None, :] >= e_of[:, None] - n_win))
+    expect = _sdpa(Q, K, V, scale, mask=ok)
+    for m in range(T // bq):
+        s, e = ref.block_bounds(m, T, p, decode=False)
+        row = ref.prune_block(Q[:, s:e], K, s, e, p)
+        assert np.array_equal(row, np.flatnonzero(ok[e - 1]))
+        out = ref.attend_block(Q[:, s:e], K, V, row, s, scale)
+        np.testing.assert_allclose(out, expect[:, s:e], rtol=2e-6, atol=2e-6)
+
+
+def test_no_causal_leak():
+    Q, K, V = _small_case(31)
+    T = Q.shape[1]
+    p = ref.Params(32, (32, 8), (256, 64), 16, 64)
+    scale = ref.default_scale(16)
+    rng = np.random.default_rng(99)
+    for m in (3, 12, 30):
+        s, e = ref.block_bounds(m, T, p, decode=False)
+        row = ref.prune_block(Q[:, s:e], K, s, e, p)
+        out = ref.attend_block(Q[:, s:e], K, V, row, s, scale)
+        K2, V2 = K.copy(), V.copy()
+        K2[:, e:] = grid(rng, K2[:, e:].shape)
+        V2[:, e:] = rng.standard_normal(V2[:, e:].shape)
+        row2 = ref.prune_block(Q[:, s:e], K2, s, e, p)
+        assert np.array_equal(row, row2)
+        assert np.array_equal(out, ref.attend_block(Q[:, s:e], K2, V2, row2, s, scale))
+        # and within the block: future keys of each query are ignored
+        for tq in range(s, e, 7):
+            K3, V3 = K.copy(), V.copy()
+            K3[:, tq + 1:] = grid(rng, K3[:, tq + 1:].shape)
+            V3[:, tq + 1:] = rng.standard_normal(V3[:, tq + 1:].shape)
+            o3 = ref.attend_block(Q[:, tq:tq + 1], K3, V3, row, tq, scale)
+            assert np.array_equal(o3[:, 0], out[:, tq - s])
+
+
+def test_decode_is_last_query_of_prefill():
+    Q, K, V = _small_case(37, T=700)
+    T = 700
+    p = ref.Params(1, (32, 8), (128, 64), 16, 64)
+    scale = ref.default_scale(16)
+    s, e = ref.block_bounds(0, T, p, decode=True)
+    assert (s, e) == (T - 1, T)
+    row = ref.prune_block(Q[:, s:e], K, s, e, p)
+    out = ref.attend_block(Q[:, s:e], K, V, row, s, scale)
+    mask = np.zeros((1, T), dtype=bool)
+    mask[0, row] = True
+    expect = _sdpa(Q[:, s:e], K, V, scale, mask=mask)
+    np.testing.assert_allclose(out, expect, rtol=2e-6, atol=2e-6)
+
+
+# --------------------------------------------------------------------------- #
+# workloads: planted structure is found                                       #
+# --------------------------------------------------------------------------- #
+def test_needles_survive_pruning_prefill_32k():
+    case = gen.make_case("c2")
+    cfg = case.cfg
+    p = ref.Params(cfg.block_q, cfg.chunk, cfg.keep, cfg.n_sink, cfg.n_window)
+    for nd in case.needles:
+        m = nd.query // cfg.block_q
+        s, e = ref.block_bounds(m, cfg.t, p, decode=False)
+        Q = case.q.sub(nd.b)[:, s:e]
+        row = ref.prune_block(Q, case.k[nd.b], s, e, p)
+        geo = ref.geometry(s, e, p)
+        assert geo.n1 * cfg.chunk[0] > cfg.keep[-1]                  # pruning really happens
+        assert set(range(nd.slot_start, nd.slot_start + nd.length)) <= set(row.tolist())
+
+
+def test_visited_rows_bounds():
+    rng = np.random.default_rng(41)
+    Hq, Hkv, d, T = 8, 2, 16, 4096
+    Q = grid(rng, (Hq, 1, d))
+    K = grid(rng, (Hkv, T, d))
+    p = ref.Params(1, (64, 8), (1024, 256), 16, 64)
+    s, e = ref.block_bounds(0, T, p, decode=True)
+    vis = ref.visited_rows(Q, K, s, e, p)
+    geo = ref.geometry(s, e, p)
+    nc = [geo.n1, 1024 // 8]
+    G = Hq // Hkv
+    for i, (n, l) in enumerate(zip(nc, p.chunk)):
+        lo = n * Hkv * (1 + int(math.log2(l)))
+        hi = n * Hkv * min(G * int(math.log2(l)) + 1, l)
+        assert lo <= vis[i] <= hi
+    # identical queries in a GQA group share every representative
+    Q2 = np.repeat(Q[::G], G, axis=0)
+    vis2 = ref.visited_rows(Q2, K, s, e, p)
+    assert vis2[0] == nc[0] * Hkv * (1 + int(math.log2(p.chunk[0])))
