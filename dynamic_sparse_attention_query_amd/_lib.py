@@ -1,0 +1,168 @@
+"""ctypes binding of libdsa (include/dsa.h): argument marshalling only.
+
+Every computation runs in the HIP library. PyTorch supplies device memory and
+streams; tensors are passed as raw device pointers. If libdsa.so has not been
+built, importing the binding raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdsa.so")
+
+DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = range(5)
+DSA_F32, DSA_BF16 = 0, 1
+DSA_PREFILL, DSA_DECODE = 0, 1
+MAX_STAGES = 4
+
+EXPORTS = ("dsa_index_width", "dsa_workspace_bytes", "dsa_prune_select", "dsa_sparse_attn",
+           "dsa_dense_attn", "dsa_status_str", "dsa_last_error")
+
+
+class CParams(ctypes.Structure):
+    _fields_ = [("n_stages", ctypes.c_int32), ("block_q", ctypes.c_int32),
+                ("chunk", ctypes.c_int32 * MAX_STAGES), ("keep", ctypes.c_int32 * MAX_STAGES),
+                ("n_sink", ctypes.c_int32), ("n_window", ctypes.c_int32)]
+
+
+class CShape(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("batch", ctypes.c_int32), ("hq", ctypes.c_int32), ("hkv", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("t", ctypes.c_int32),
+                ("seq_lens", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+                ("page_size", ctypes.c_int32), ("max_pages", ctypes.c_int32)]
+
+
+class DsaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{status_str(status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libdsa.so (once) and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m dynamic_sparse_attention_query_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    lib.dsa_index_width.argtypes = [ctypes.POINTER(CParams)]
+    lib.dsa_index_width.restype = ctypes.c_int32
+    lib.dsa_workspace_bytes.argtypes = [ctypes.POINTER(CShape), ctypes.POINTER(CParams), ctypes.POINTER(sz)]
+    lib.dsa_workspace_bytes.restype = ctypes.c_int
+    lib.dsa_prune_select.argtypes = [ctypes.POINTER(CShape), vp, vp, ctypes.POINTER(CParams), vp, vp, sz, vp, vp]
+    lib.dsa_prune_select.restype = ctypes.c_int
+    lib.dsa_sparse_attn.argtypes = [ctypes.POINTER(CShape), vp, vp, vp, vp, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_float, vp, vp, sz, vp]
+    lib.dsa_sparse_attn.restype = ctypes.c_int
+    lib.dsa_dense_attn.argtypes = [ctypes.POINTER(CShape), vp, vp, vp, ctypes.c_float, vp, vp, sz, vp]
+    lib.dsa_dense_attn.restype = ctypes.c_int
+    lib.dsa_status_str.argtypes = [ctypes.c_int]
+    lib.dsa_status_str.restype = ctypes.c_char_p
+    lib.dsa_last_error.argtypes = []
+    lib.dsa_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_str(st: int) -> str:
+    return load().dsa_status_str(st).decode()
+
+
+def _check(st: int):
+    if st != DSA_OK:
+        raise DsaError(st, load().dsa_last_error().decode())
+
+
+# --------------------------------------------------------------------------- #
+# parameter / shape records                                                   #
+# --------------------------------------------------------------------------- #
+@dataclass(frozen=True)
+class Params:
+    block_q: int
+    chunk: Sequence[int]
+    keep: Sequence[int]
+    n_sink: int
+    n_window: int
+
+    def c(self) -> CParams:
+        p = CParams()
+        p.n_stages = len(self.chunk)
+        p.block_q = self.block_q
+        for i in range(MAX_STAGES):
+            p.chunk[i] = self.chunk[i] if i < len(self.chunk) else 0
+            p.keep[i] = self.keep[i] if i < len(self.keep) else 0
+        p.n_sink = self.n_sink
+        p.n_window = self.n_window
+        return p
+
+
+@dataclass
+class Shape:
+    mode: int
+    dtype: int
+    batch: int
+    hq: int
+    hkv: int
+    d: int
+    t: int
+    seq_lens: int = 0          # device pointer
+    block_table: int = 0       # device pointer
+    page_size: int = 0
+    max_pages: int = 0
+
+    def c(self) -> CShape:
+        s = CShape()
+        s.mode, s.dtype = self.mode, self.dtype
+        s.batch, s.hq, s.hkv, s.d, s.t = self.batch, self.hq, self.hkv, self.d, self.t
+        s.seq_lens = self.seq_lens or None
+        s.block_table = self.block_table or None
+        s.page_size, s.max_pages = self.page_size, self.max_pages
+        return s
+
+
+# --------------------------------------------------------------------------- #
+# raw entry points (pointers in, status checked)                              #
+# --------------------------------------------------------------------------- #
+def index_width(p: Params) -> int:
+    cp = p.c()
+    return load().dsa_index_width(ctypes.byref(cp))
+
+
+def workspace_bytes(shape: Shape, p: Optional[Params]) -> int:
+    cs = shape.c()
+    cp = p.c() if p is not None else None
+    out = ctypes.c_size_t(0)
+    _check(load().dsa_workspace_bytes(ctypes.byref(cs), ctypes.byref(cp) if cp is not None else None,
+                                      ctypes.byref(out)))
+    return out.value
+
+
+def prune_select_raw(shape: Shape, q: int, k: int, p: Params, idx: int, ws: int, ws_bytes: int,
+                     visited: int = 0, stream: int = 0):
+    cs, cp = shape.c(), p.c()
+    _check(load().dsa_prune_select(ctypes.byref(cs), q, k, ctypes.byref(cp), idx, ws, ws_bytes,
+                                   visited or None, stream or None))
+
+
+def sparse_attn_raw(shape: Shape, q: int, k: int, v: int, idx: int, idx_width: int, block_q: int,
+                    scale: float, out: int, ws: int, ws_bytes: int, stream: int = 0):
+    cs = shape.c()
+    _check(load().dsa_sparse_attn(ctypes.byref(cs), q, k, v, idx, idx_width, block_q, scale, out,
+                                  ws or None, ws_bytes, stream or None))
+
+
+def dense_attn_raw(shape: Shape, q: int, k: int, v: int, scale: float, out: int, ws: int, ws_bytes: int,
+                   stream: int = 0):
+    cs = shape.c()
+    _check(load().dsa_dense_attn(ctypes.byref(cs), q, k, v, scale, out, ws or None, ws_bytes,
+                                 stream or None))

@@ -1,0 +1,147 @@
+"""Tensor-level entry points over the C ABI (PyTorch supplies memory and streams).
+
+    idx = prune_select(q, k, params)                    # prefill, or decode with seq_lens=
+    out = sparse_attn(q, k, v, idx, params)
+    out = dense_attn(q, k, v)
+
+Layouts are those of include/dsa.h. Prefill: q [B,Hq,T,d], k/v [B,Hkv,T,d].
+Decode: q [B,Hq,d] with seq_lens [B] (int32, on the GPU) and either contiguous
+k/v [B,Hkv,t,d] or page pools [n_pages,Hkv,page_size,d] with block_table
+[B,max_pages]. Outputs are float32.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import DSA_BF16, DSA_DECODE, DSA_F32, DSA_PREFILL, Params, Shape
+
+_WS: Dict[Tuple[int, int], torch.Tensor] = {}
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DSA_BF16
+    if t.dtype == torch.float32:
+        return DSA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _need(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def make_shape(q: torch.Tensor, k: torch.Tensor, *, seq_lens: Optional[torch.Tensor] = None,
+               block_table: Optional[torch.Tensor] = None, t: Optional[int] = None) -> Shape:
+    """Describe the problem from the tensors (see the module docstring)."""
+    _need(q, "q")
+    _need(k, "k")
+    dt = _dtype_code(q)
+    if k.dtype != q.dtype:
+        raise TypeError("q and k must share a dtype")
+    if seq_lens is None:
+        if q.dim() != 4 or k.dim() != 4:
+            raise ValueError("prefill expects q [B,Hq,T,d] and k [B,Hkv,T,d]")
+        B, Hq, T, d = q.shape
+        if k.shape[0] != B or k.shape[2] != T or k.shape[3] != d:
+            raise ValueError("k shape does not match q")
+        return Shape(DSA_PREFILL, dt, B, Hq, k.shape[1], d, T)
+    _need(seq_lens, "seq_lens")
+    if seq_lens.dtype != torch.int32:
+        raise TypeError("seq_lens must be int32")
+    if q.dim() != 3:
+        raise ValueError("decode expects q [B,Hq,d]")
+    B, Hq, d = q.shape
+    if seq_lens.numel() != B:
+        raise ValueError("seq_lens must have B entries")
+    if block_table is None:
+        if k.dim() != 4 or k.shape[0] != B or k.shape[3] != d:
+            raise ValueError("contiguous decode expects k [B,Hkv,t,d]")
+        return Shape(DSA_DECODE, dt, B, Hq, k.shape[1], d, k.shape[2], seq_lens.data_ptr())
+    _need(block_table, "block_table")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 [B, max_pages]")
+    if k.dim() != 4 or k.shape[3] != d:
+        raise ValueError("paged decode expects k [n_pages,Hkv,page_size,d]")
+    ps = k.shape[2]
+    maxp = block_table.shape[1]
+    return Shape(DSA_DECODE, dt, B, Hq, k.shape[1], d, t if t is not None else maxp * ps,
+                 seq_lens.data_ptr(), block_table.data_ptr(), ps, maxp)
+
+
+def workspace(shape: Shape, params: Optional[Params], device: torch.device) -> Tuple[int, int]:
+    """A per-device scratch buffer large enough for this call (grown on demand)."""
+    nbytes = _lib.workspace_bytes(shape, params)
+    key = (device.index if device.index is not None else torch.cuda.current_device(), 0)
+    buf = _WS.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _WS[key] = buf
+    return buf.data_ptr(), buf.numel()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def prune_select(q: torch.Tensor, k: torch.Tensor, params: Params, *,
+                 seq_lens: Optional[torch.Tensor] = None, block_table: Optional[torch.Tensor] = None,
+                 t: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                 visited: Optional[torch.Tensor] = None) -> torch.Tensor:
+    shape = make_shape(q, k, seq_lens=seq_lens, block_table=block_table, t=t)
+    L = _lib.index_width(params)
+    if L < 0:
+        raise _lib.DsaError(_lib.DSA_ERR_INVALID_ARG, "invalid params")
+    rows = shape.batch * (1 if shape.mode == DSA_DECODE else shape.t // params.block_q)
+    if out is None:
+        out = torch.empty(rows * L, dtype=torch.int32, device=q.device)
+    if out.numel() != rows * L or out.dtype != torch.int32:
+        raise ValueError("idx buffer has the wrong size or dtype")
+    ws, wsb = workspace(shape, params, q.device)
+    vis = 0
+    if visited is not None:
+        if visited.dtype != torch.int64 or visited.numel() < len(params.chunk):
+            raise ValueError("visited must be int64 with one entry per stage")
+        vis = visited.data_ptr()
+    _lib.prune_select_raw(shape, q.data_ptr(), k.data_ptr(), params, out.data_ptr(), ws, wsb, vis, _stream())
+    if shape.mode == DSA_DECODE:
+        return out.view(shape.batch, L)
+    return out.view(shape.batch, shape.t // params.block_q, L)
+
+
+def sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor, params: Params, *,
+                scale: float = 0.0, seq_lens: Optional[torch.Tensor] = None,
+                block_table: Optional[torch.Tensor] = None, t: Optional[int] = None,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Attention over the index rows written by prune_select with the same params."""
+    shape = make_shape(q, k, seq_lens=seq_lens, block_table=block_table, t=t)
+    _need(v, "v")
+    _need(idx, "idx")
+    if v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("v must match k")
+    if idx.dtype != torch.int32:
+        raise TypeError("idx must be int32")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    ws, wsb = workspace(shape, params, q.device)
+    _lib.sparse_attn_raw(shape, q.data_ptr(), k.data_ptr(), v.data_ptr(), idx.data_ptr(), idx.shape[-1],
+                         params.block_q, scale, out.data_ptr(), ws, wsb, _stream())
+    return out
+
+
+def dense_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: float = 0.0,
+               seq_lens: Optional[torch.Tensor] = None, block_table: Optional[torch.Tensor] = None,
+               t: Optional[int] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    shape = make_shape(q, k, seq_lens=seq_lens, block_table=block_table, t=t)
+    _need(v, "v")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    ws, wsb = workspace(shape, None, q.device)
+    _lib.dense_attn_raw(shape, q.data_ptr(), k.data_ptr(), v.data_ptr(), scale, out.data_ptr(), ws, wsb,
+                        _stream())
+    return out

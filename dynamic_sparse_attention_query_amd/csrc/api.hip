@@ -1,0 +1,281 @@
+// C ABI of libdsa: argument validation, workspace layout and launch order.
+// The rules checked here are the ones documented in include/dsa.h.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "dsa.h"
+#include "dsa_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+dsa_status fail(dsa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+bool is_pow2(long long x) { return x > 0 && (x & (x - 1)) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+dsa_status check_shape(const dsa_shape* s) {
+  if (!s) return fail(DSA_ERR_INVALID_ARG, "shape is NULL");
+  if (s->mode != DSA_PREFILL && s->mode != DSA_DECODE)
+    return fail(DSA_ERR_INVALID_ARG, "mode %d is not DSA_PREFILL or DSA_DECODE", s->mode);
+  if (s->dtype != DSA_F32 && s->dtype != DSA_BF16)
+    return fail(DSA_ERR_INVALID_ARG, "dtype %d is not DSA_F32 or DSA_BF16", s->dtype);
+  if (s->batch < 1 || s->hq < 1 || s->hkv < 1 || s->t < 1)
+    return fail(DSA_ERR_INVALID_ARG, "batch, hq, hkv and t must be >= 1");
+  if (s->hq % s->hkv != 0) return fail(DSA_ERR_INVALID_ARG, "hq %% hkv != 0");
+  const int G = s->hq / s->hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(DSA_ERR_UNSUPPORTED, "hq / hkv = %d; supported group sizes are 1, 2, 4, 8", G);
+  if (s->d != 64 && s->d != 128) return fail(DSA_ERR_UNSUPPORTED, "d = %d; supported: 64, 128", s->d);
+  if (s->mode == DSA_DECODE) {
+    if (!s->seq_lens) return fail(DSA_ERR_INVALID_ARG, "decode needs seq_lens");
+    if (s->block_table) {
+      if (!is_pow2(s->page_size)) return fail(DSA_ERR_INVALID_ARG, "page_size must be a power of two");
+      if (s->max_pages < 1 || static_cast<long long>(s->max_pages) * s->page_size < s->t)
+        return fail(DSA_ERR_INVALID_ARG, "max_pages * page_size must be >= t");
+    }
+  }
+  return DSA_OK;
+}
+
+dsa_status check_params(const dsa_shape* s, const dsa_params* p) {
+  if (!p) return fail(DSA_ERR_INVALID_ARG, "params is NULL");
+  if (p->n_stages < 1 || p->n_stages > DSA_MAX_STAGES)
+    return fail(DSA_ERR_INVALID_ARG, "n_stages = %d not in [1, %d]", p->n_stages, DSA_MAX_STAGES);
+  for (int i = 0; i < p->n_stages; ++i) {
+    if (!is_pow2(p->chunk[i])) return fail(DSA_ERR_INVALID_ARG, "chunk[%d] = %d is not a power of two", i, p->chunk[i]);
+    if (p->keep[i] < 0 || p->keep[i] % p->chunk[i] != 0)
+      return fail(DSA_ERR_INVALID_ARG, "keep[%d] = %d is not a non-negative multiple of chunk[%d]", i, p->keep[i], i);
+    if (i > 0) {
+      if (p->chunk[i - 1] % p->chunk[i] != 0)
+        return fail(DSA_ERR_INVALID_ARG, "chunk[%d] does not divide chunk[%d]", i, i - 1);
+      if (p->keep[i] > p->keep[i - 1]) return fail(DSA_ERR_INVALID_ARG, "keep[%d] > keep[%d]", i, i - 1);
+    }
+    if (p->keep[i] / p->chunk[i] > 8192)
+      return fail(DSA_ERR_UNSUPPORTED, "keep[%d] / chunk[%d] > 8192 kept chunks", i, i);
+  }
+  if (p->n_sink < 0 || p->n_window < 0) return fail(DSA_ERR_INVALID_ARG, "n_sink and n_window must be >= 0");
+  if (s) {
+    if (s->mode == DSA_DECODE) {
+      if (p->block_q != 1) return fail(DSA_ERR_INVALID_ARG, "decode requires block_q == 1");
+      if (16 % s->hkv != 0) return fail(DSA_ERR_UNSUPPORTED, "decode pruning needs hkv to divide 16");
+    } else {
+      if (p->block_q < 4 || p->block_q > 64 || !is_pow2(p->block_q))
+        return fail(DSA_ERR_UNSUPPORTED, "prefill block_q = %d; supported: 4, 8, 16, 32, 64", p->block_q);
+      if (s->t % p->block_q != 0) return fail(DSA_ERR_INVALID_ARG, "t %% block_q != 0");
+    }
+  }
+  return DSA_OK;
+}
+
+long long index_width_ll(const dsa_params* p) {
+  long long n = static_cast<long long>(p->n_sink) + p->keep[p->n_stages - 1] + p->n_window + p->chunk[0] - 1;
+  return (n + 63) / 64 * 64;
+}
+
+struct PruneLayout {
+  long long R, maxK, maxNC, n1max;
+  size_t off_cnt, off_starts, off_scores, bytes;
+};
+
+PruneLayout prune_layout(const dsa_shape* s, const dsa_params* p) {
+  PruneLayout L{};
+  const long long nblk = s->mode == DSA_DECODE ? 1 : s->t / p->block_q;
+  L.R = static_cast<long long>(s->batch) * nblk;
+  long long maxK = 1, maxNC = 1;
+  for (int i = 0; i < p->n_stages; ++i) maxK = std::max<long long>(maxK, p->keep[i] / p->chunk[i]);
+  const long long mid = std::max<long long>(0, static_cast<long long>(s->t) - p->n_window - p->n_sink);
+  L.n1max = mid / p->chunk[0];
+  maxNC = std::max<long long>(maxNC, L.n1max);
+  for (int i = 1; i < p->n_stages; ++i) maxNC = std::max<long long>(maxNC, p->keep[i - 1] / p->chunk[i]);
+  L.maxK = maxK;
+  L.maxNC = maxNC;
+  L.off_cnt = 0;
+  L.off_starts = align256(L.off_cnt + static_cast<size_t>(L.R) * dsa::kMaxStages * 4);
+  L.off_scores = align256(L.off_starts + 2 * static_cast<size_t>(L.R) * maxK * 4);
+  L.bytes = align256(L.off_scores + static_cast<size_t>(L.R) * maxNC * 4);
+  return L;
+}
+
+// decode split geometry: at most ~2048 splits per (sequence, kv head)
+int keys_per_split(long long n_total) {
+  const long long per = (n_total + 64LL * 2048 - 1) / (64LL * 2048);
+  return static_cast<int>(64 * std::max<long long>(1, per));
+}
+
+size_t attn_bytes(const dsa_shape* s, long long n_total) {
+  if (s->mode != DSA_DECODE) return 0;
+  const int kps = keys_per_split(n_total);
+  const long long n_splits = (n_total + kps - 1) / kps;
+  return align256(static_cast<size_t>(s->batch) * s->hq * n_splits * (s->d + 2) * 4);
+}
+
+dsa::KvLayout make_kv(const dsa_shape* s, int bq) {
+  dsa::KvLayout kv{};
+  kv.B = s->batch;
+  kv.Hq = s->hq;
+  kv.Hkv = s->hkv;
+  kv.D = s->d;
+  kv.T = s->t;
+  kv.decode = s->mode == DSA_DECODE;
+  kv.bq = kv.decode ? 1 : bq;
+  kv.nblk = kv.decode ? 1 : s->t / bq;
+  kv.seq_lens = kv.decode ? s->seq_lens : nullptr;
+  kv.block_table = kv.decode ? s->block_table : nullptr;
+  kv.page_size = kv.block_table ? s->page_size : 1;
+  int shift = 0;
+  while ((1 << shift) < kv.page_size) ++shift;
+  kv.page_shift = shift;
+  kv.max_pages = kv.block_table ? s->max_pages : 0;
+  return kv;
+}
+
+dsa_status run_attn(const dsa_shape* s, const void* q, const void* k, const void* v, const int32_t* idx,
+                    int32_t L, int bq, float scale, float* out, void* ws, size_t ws_bytes, void* stream) {
+  const long long n_total = idx ? L : s->t;
+  const size_t need = attn_bytes(s, n_total);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, need);
+  dsa::AttnArgs a{};
+  a.kv = make_kv(s, bq);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.idx = idx;
+  a.L = L;
+  a.out = out;
+  a.part = static_cast<float*>(ws);
+  a.kps = keys_per_split(n_total);
+  a.n_splits = static_cast<int>((n_total + a.kps - 1) / a.kps);
+  const float sc = scale > 0.f ? scale : 1.0f / std::sqrt(static_cast<float>(s->d));
+  a.scale_log2 = sc * 1.4426950408889634f;
+  hipError_t err = dsa::launch_sparse_attn(a, s->dtype, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(DSA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(err));
+  return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_status_str(dsa_status s) {
+  switch (s) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_INVALID_ARG: return "DSA_ERR_INVALID_ARG";
+    case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED";
+    case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE";
+    case DSA_ERR_HIP: return "DSA_ERR_HIP";
+  }
+  return "DSA_ERR_UNKNOWN";
+}
+
+const char* dsa_last_error(void) { return g_err; }
+
+int32_t dsa_index_width(const dsa_params* p) {
+  if (check_params(nullptr, p) != DSA_OK) return -1;
+  const long long w = index_width_ll(p);
+  if (w > (1LL << 30)) return -1;
+  return static_cast<int32_t>(w);
+}
+
+dsa_status dsa_workspace_bytes(const dsa_shape* s, const dsa_params* p, size_t* out_bytes) {
+  g_err[0] = 0;
+  if (!out_bytes) return fail(DSA_ERR_INVALID_ARG, "out_bytes is NULL");
+  dsa_status st = check_shape(s);
+  if (st != DSA_OK) return st;
+  size_t bytes = attn_bytes(s, s->t);
+  if (p) {
+    st = check_params(s, p);
+    if (st != DSA_OK) return st;
+    bytes = std::max(bytes, prune_layout(s, p).bytes);
+    bytes = std::max(bytes, attn_bytes(s, index_width_ll(p)));
+  }
+  *out_bytes = bytes;
+  return DSA_OK;
+}
+
+dsa_status dsa_prune_select(const dsa_shape* s, const void* q, const void* k, const dsa_params* p,
+                            int32_t* idx, void* ws, size_t ws_bytes, uint64_t* visited, void* stream) {
+  g_err[0] = 0;
+  dsa_status st = check_shape(s);
+  if (st != DSA_OK) return st;
+  st = check_params(s, p);
+  if (st != DSA_OK) return st;
+  if (!q || !k || !idx) return fail(DSA_ERR_INVALID_ARG, "q, k and idx must be non-NULL");
+  const long long L = index_width_ll(p);
+  if (L > (1LL << 30)) return fail(DSA_ERR_INVALID_ARG, "index width overflows");
+  const PruneLayout lay = prune_layout(s, p);
+  if (lay.maxNC > 65536)
+    return fail(DSA_ERR_UNSUPPORTED, "a stage would score %lld chunks per row (limit 65536)", lay.maxNC);
+  if (!ws || ws_bytes < lay.bytes)
+    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, lay.bytes);
+  dsa::PruneArgs a{};
+  a.kv = make_kv(s, p->block_q);
+  a.q = q;
+  a.k = k;
+  a.n_stages = p->n_stages;
+  for (int i = 0; i < DSA_MAX_STAGES; ++i) {
+    a.chunk[i] = i < p->n_stages ? p->chunk[i] : 1;
+    a.keep[i] = i < p->n_stages ? p->keep[i] : 0;
+  }
+  a.n_sink = p->n_sink;
+  a.n_window = p->n_window;
+  a.idx = idx;
+  a.L = static_cast<int>(L);
+  a.R = static_cast<int>(lay.R);
+  a.maxK = static_cast<int>(lay.maxK);
+  a.maxNC = static_cast<int>(lay.maxNC);
+  a.n1max = static_cast<int>(lay.n1max);
+  char* w = static_cast<char*>(ws);
+  a.cnt = reinterpret_cast<int32_t*>(w + lay.off_cnt);
+  a.starts = reinterpret_cast<int32_t*>(w + lay.off_starts);
+  a.scores = reinterpret_cast<uint32_t*>(w + lay.off_scores);
+  a.visited = reinterpret_cast<unsigned long long*>(visited);
+  hipError_t err = dsa::launch_prune(a, s->dtype, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(DSA_ERR_HIP, "prune launch failed: %s", hipGetErrorString(err));
+  return DSA_OK;
+}
+
+dsa_status dsa_sparse_attn(const dsa_shape* s, const void* q, const void* k, const void* v,
+                           const int32_t* idx, int32_t idx_width, int32_t block_q, float scale,
+                           float* out, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  dsa_status st = check_shape(s);
+  if (st != DSA_OK) return st;
+  if (!q || !k || !v || !idx || !out) return fail(DSA_ERR_INVALID_ARG, "q, k, v, idx and out must be non-NULL");
+  if (idx_width < 1) return fail(DSA_ERR_INVALID_ARG, "idx_width must be >= 1");
+  if (s->mode == DSA_DECODE) {
+    if (block_q != 1) return fail(DSA_ERR_INVALID_ARG, "decode requires block_q == 1");
+  } else {
+    if (block_q < 4 || block_q > 64 || !is_pow2(block_q))
+      return fail(DSA_ERR_UNSUPPORTED, "prefill block_q = %d; supported: 4, 8, 16, 32, 64", block_q);
+    if (s->t % block_q != 0) return fail(DSA_ERR_INVALID_ARG, "t %% block_q != 0");
+  }
+  return run_attn(s, q, k, v, idx, idx_width, block_q, scale, out, ws, ws_bytes, stream);
+}
+
+dsa_status dsa_dense_attn(const dsa_shape* s, const void* q, const void* k, const void* v, float scale,
+                          float* out, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  dsa_status st = check_shape(s);
+  if (st != DSA_OK) return st;
+  if (!q || !k || !v || !out) return fail(DSA_ERR_INVALID_ARG, "q, k, v and out must be non-NULL");
+  int bq = 64;
+  if (s->mode == DSA_PREFILL) {
+    while (bq > 4 && s->t % bq != 0) bq >>= 1;
+    if (s->t % bq != 0) return fail(DSA_ERR_UNSUPPORTED, "dense prefill needs t to be a multiple of 4");
+  }
+  return run_attn(s, q, k, v, nullptr, 0, bq, scale, out, ws, ws_bytes, stream);
+}
+
+}  // extern "C"

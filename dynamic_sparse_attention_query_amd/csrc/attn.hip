@@ -1,0 +1,329 @@
+// Attention over an index row (sparse) or over every causal key (dense).
+//
+// out[h, t] = sum_{p in row, p <= t} softmax_p(scale * q_{h,t} . k_p) v_p
+// (InfLLM blog page, "Mathematical Formulation of Efficient Softmax
+// Normalization"; MInference page, masked attention with in-kernel causal
+// masking). Masked keys are excluded exactly. The softmax runs in the base-2
+// domain with the scale folded into log2(e).
+//
+// Decode ("Flash Decoding", InfiniteHiP page, "Block Sparse Attention
+// Implementation"): the row is cut into splits of `kps` entries; one
+// workgroup per (split, kv head, sequence) produces an unnormalised partial
+// (running max m, sum l, o[d]) for each query head of the group; a second
+// kernel merges the partials.
+// Prefill: one workgroup per (query block, query head) streams 64-key tiles of
+// the row through LDS with an online softmax (generic FMA path).
+#include "dsa_internal.h"
+
+namespace dsa {
+
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_f(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ------------------------------------------------------------------------- //
+// decode: split partials                                                    //
+// ------------------------------------------------------------------------- //
+template <typename T, int D, int G>
+__global__ void __launch_bounds__(256) k_decode_partial(AttnArgs a) {
+  constexpr int EPL = D / 16;
+  constexpr int NO = (G * D + 255) / 256;
+  const KvLayout& kv = a.kv;
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int Tb = kv.seq_lens[b];
+  const int tq = Tb - 1;
+  const int tid = threadIdx.x, gi = tid >> 4, li = tid & 15, lane = tid & 63, w = tid >> 6;
+  __shared__ float sv[64][D + 4];
+  __shared__ float sp[G][64];
+  __shared__ int spos[64];
+  __shared__ float sm[G], sl[G], salpha[G];
+  const T* Q = static_cast<const T*>(a.q);
+  const T* K = static_cast<const T*>(a.k);
+  const T* V = static_cast<const T*>(a.v);
+
+  float q[G][EPL];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh)
+    SliceLoad<T, EPL>::run(Q + (static_cast<size_t>(b) * kv.Hq + g * G + hh) * D + li * EPL, q[hh]);
+  if (tid < G) {
+    sm[tid] = kNegBig;
+    sl[tid] = 0.f;
+  }
+  float acc[NO];
+#pragma unroll
+  for (int i = 0; i < NO; ++i) acc[i] = 0.f;
+
+  const int n_total = a.idx ? a.L : Tb;
+  const int k_begin = split * a.kps;
+  const int k_end = min(n_total, k_begin + a.kps);
+  const int32_t* row = a.idx ? a.idx + static_cast<size_t>(b) * a.L : nullptr;
+
+  for (int kb = k_begin; kb < k_end; kb += 64) {
+    __syncthreads();
+    if (tid < 64) {
+      const int i = kb + tid;
+      int p = -1;
+      if (i < k_end) {
+        p = row ? row[i] : i;
+        if (p < 0 || p > tq) p = -1;
+      }
+      spos[tid] = p;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int kk = gi + 16 * u;
+      const int p = spos[kk];
+      float kr[EPL], vr[EPL];
+      if (p >= 0) {
+        const size_t off = kv_offset(kv, b, g, p) + li * EPL;
+        SliceLoad<T, EPL>::run(K + off, kr);
+        SliceLoad<T, EPL>::run(V + off, vr);
+      } else {
+#pragma unroll
+        for (int x = 0; x < EPL; ++x) { kr[x] = 0.f; vr[x] = 0.f; }
+      }
+#pragma unroll
+      for (int x = 0; x < EPL; ++x) sv[kk][li * EPL + x] = vr[x];
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        float d = 0.f;
+#pragma unroll
+        for (int x = 0; x < EPL; ++x) d = fmaf(q[hh][x], kr[x], d);
+        d = group16_sum(d);
+        if (li == 0) sp[hh][kk] = (p >= 0) ? d * a.scale_log2 : -INFINITY;
+      }
+    }
+    __syncthreads();
+    for (int hh = w; hh < G; hh += 4) {
+      const float z = sp[hh][lane];
+      const float m_old = sm[hh];
+      const float m_new = fmaxf(m_old, wave_max_f(z));
+      const float pz = (z == -INFINITY) ? 0.f : exp2f(z - m_new);
+      const float ls = wave_sum_f(pz);
+      sp[hh][lane] = pz;
+      if (lane == 0) {
+        const float alpha = exp2f(m_old - m_new);
+        salpha[hh] = alpha;
+        sl[hh] = sl[hh] * alpha + ls;
+        sm[hh] = m_new;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NO; ++i) {
+      const int o = tid + 256 * i;
+      if (o < G * D) {
+        const int hh = o / D, dd = o - hh * D;
+        float v = acc[i] * salpha[hh];
+#pragma unroll 8
+        for (int kk = 0; kk < 64; ++kk) v = fmaf(sp[hh][kk], sv[kk][dd], v);
+        acc[i] = v;
+      }
+    }
+  }
+  __syncthreads();
+  float* P = a.part;
+#pragma unroll
+  for (int i = 0; i < NO; ++i) {
+    const int o = tid + 256 * i;
+    if (o < G * D) {
+      const int hh = o / D, dd = o - hh * D;
+      P[((static_cast<size_t>(b) * kv.Hq + g * G + hh) * a.n_splits + split) * (D + 2) + dd] = acc[i];
+    }
+  }
+  if (tid < G) {
+    float* mlp = P + ((static_cast<size_t>(b) * kv.Hq + g * G + tid) * a.n_splits + split) * (D + 2) + D;
+    mlp[0] = sm[tid];
+    mlp[1] = sl[tid];
+  }
+}
+
+// Merge split partials: M = max m_s, out = sum o_s 2^(m_s-M) / sum l_s 2^(m_s-M).
+template <int D>
+__global__ void __launch_bounds__(256) k_decode_combine(AttnArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const size_t base = (static_cast<size_t>(b) * a.kv.Hq + h) * a.n_splits;
+  const float* P = a.part + base * (D + 2);
+  __shared__ float red[4];
+  __shared__ float sM;
+  // global max of the split maxima
+  float m = kNegBig;
+  for (int s = tid; s < a.n_splits; s += 256) m = fmaxf(m, P[static_cast<size_t>(s) * (D + 2) + D]);
+  m = wave_max_f(m);
+  if (lane == 0) red[w] = m;
+  __syncthreads();
+  if (tid == 0) sM = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  const float M = sM;
+  // thread layout: 256 threads = (split lane group of 256/D) x D dims
+  constexpr int SG = 256 / D;
+  const int dd = tid % D, sg = tid / D;
+  float o = 0.f, l = 0.f;
+  for (int s = sg; s < a.n_splits; s += SG) {
+    const float* ps = P + static_cast<size_t>(s) * (D + 2);
+    const float f = exp2f(ps[D] - M);
+    o = fmaf(ps[dd], f, o);
+    l = fmaf(ps[D + 1], f, l);
+  }
+  __shared__ float so[SG][D];
+  __shared__ float slr[SG];
+  so[sg][dd] = o;
+  if (dd == 0) slr[sg] = l;
+  __syncthreads();
+  if (sg == 0) {
+    float ot = 0.f, lt = 0.f;
+#pragma unroll
+    for (int x = 0; x < SG; ++x) { ot += so[x][dd]; lt += slr[x]; }
+    a.out[(static_cast<size_t>(b) * a.kv.Hq + h) * D + dd] = ot / lt;
+  }
+}
+
+// ------------------------------------------------------------------------- //
+// prefill: generic FMA flash attention over gathered 64-key tiles           //
+// ------------------------------------------------------------------------- //
+template <typename T, int D>
+__global__ void __launch_bounds__(256) k_prefill_generic(AttnArgs a) {
+  const KvLayout& kv = a.kv;
+  const int m = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int bq = kv.bq;
+  const int s = m * bq, e = s + bq;
+  const int G = kv.Hq / kv.Hkv;
+  const int g = h / G;
+  const int TPR = 256 / bq;           // threads per query row (4 .. 64)
+  const int DPT = D / TPR;            // output dims per thread
+  const int tid = threadIdx.x;
+  const int q = tid / TPR, sub = tid - q * TPR;
+  const int tq = s + q;
+  __shared__ float qs[64][D + 1];
+  __shared__ float ks[64][D + 1];
+  __shared__ float vs[64][D + 1];
+  __shared__ float ps[64][65];
+  __shared__ int spos[64];
+  const T* Q = static_cast<const T*>(a.q);
+  const T* K = static_cast<const T*>(a.k);
+  const T* V = static_cast<const T*>(a.v);
+
+  for (int x = tid; x < bq * D; x += 256) {
+    const int t = x / D, dd = x - t * D;
+    qs[t][dd] = load_one<T>(Q + ((static_cast<size_t>(b) * kv.Hq + h) * kv.T + s + t) * D + dd);
+  }
+  const int r = b * kv.nblk + m;
+  const int32_t* row = a.idx ? a.idx + static_cast<size_t>(r) * a.L : nullptr;
+  const int n_ent = row ? a.L : e;
+  float mrun = kNegBig, lrun = 0.f;
+  float o[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) o[j] = 0.f;
+
+  for (int kb = 0; kb < n_ent; kb += 64) {
+    __syncthreads();
+    if (tid < 64) {
+      const int i = kb + tid;
+      int p = -1;
+      if (i < n_ent) {
+        p = row ? row[i] : i;
+        if (p < 0 || p >= e) p = -1;
+      }
+      spos[tid] = p;
+    }
+    __syncthreads();
+    for (int x = tid; x < 64 * D; x += 256) {
+      const int kk = x / D, dd = x - kk * D;
+      const int p = spos[kk];
+      float kvv = 0.f, vvv = 0.f;
+      if (p >= 0) {
+        const size_t off = kv_offset(kv, b, g, p) + dd;
+        kvv = load_one<T>(K + off);
+        vvv = load_one<T>(V + off);
+      }
+      ks[kk][dd] = kvv;
+      vs[kk][dd] = vvv;
+    }
+    __syncthreads();
+    float tmax = -INFINITY;
+    for (int i = 0; i < 64 / TPR; ++i) {
+      const int kk = sub + TPR * i;
+      const int p = spos[kk];
+      float d = 0.f;
+#pragma unroll 8
+      for (int x = 0; x < D; ++x) d = fmaf(qs[q][x], ks[kk][x], d);
+      const float z = (p >= 0 && p <= tq) ? d * a.scale_log2 : -INFINITY;
+      ps[q][kk] = z;
+      tmax = fmaxf(tmax, z);
+    }
+    for (int off = TPR >> 1; off >= 1; off >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, off, TPR));
+    const float m_new = fmaxf(mrun, tmax);
+    const float alpha = exp2f(mrun - m_new);
+    float psum = 0.f;
+    for (int i = 0; i < 64 / TPR; ++i) {
+      const int kk = sub + TPR * i;
+      const float z = ps[q][kk];
+      const float pz = (z == -INFINITY) ? 0.f : exp2f(z - m_new);
+      ps[q][kk] = pz;
+      psum += pz;
+    }
+    for (int off = TPR >> 1; off >= 1; off >>= 1) psum += __shfl_xor(psum, off, TPR);
+    lrun = lrun * alpha + psum;
+    mrun = m_new;
+    __syncthreads();
+    for (int j = 0; j < DPT; ++j) {
+      const int dd = sub + TPR * j;
+      float v = o[j] * alpha;
+#pragma unroll 8
+      for (int kk = 0; kk < 64; ++kk) v = fmaf(ps[q][kk], vs[kk][dd], v);
+      o[j] = v;
+    }
+  }
+  float* out = a.out + ((static_cast<size_t>(b) * kv.Hq + h) * kv.T + tq) * D;
+  for (int j = 0; j < DPT; ++j) out[sub + TPR * j] = o[j] / lrun;
+}
+
+// ------------------------------------------------------------------------- //
+// launcher                                                                  //
+// ------------------------------------------------------------------------- //
+template <typename T, int D, int G>
+static void launch_decode(const AttnArgs& a, hipStream_t st) {
+  dim3 grid(a.n_splits, a.kv.Hkv, a.kv.B);
+  hipLaunchKernelGGL((k_decode_partial<T, D, G>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((k_decode_combine<D>), dim3(a.kv.Hq, a.kv.B), dim3(256), 0, st, a);
+}
+
+template <typename T, int D>
+static hipError_t launch_attn_typed(const AttnArgs& a, hipStream_t st) {
+  if (a.kv.decode) {
+    switch (a.kv.Hq / a.kv.Hkv) {
+      case 1: launch_decode<T, D, 1>(a, st); break;
+      case 2: launch_decode<T, D, 2>(a, st); break;
+      case 4: launch_decode<T, D, 4>(a, st); break;
+      case 8: launch_decode<T, D, 8>(a, st); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    dim3 grid(a.kv.nblk, a.kv.Hq, a.kv.B);
+    hipLaunchKernelGGL((k_prefill_generic<T, D>), grid, dim3(256), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_attn(const AttnArgs& a, int dtype, hipStream_t st) {
+  if (dtype == 1) {
+    if (a.kv.D == 128) return launch_attn_typed<uint16_t, 128>(a, st);
+    if (a.kv.D == 64) return launch_attn_typed<uint16_t, 64>(a, st);
+  } else {
+    if (a.kv.D == 128) return launch_attn_typed<float, 128>(a, st);
+    if (a.kv.D == 64) return launch_attn_typed<float, 64>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dsa

@@ -1,0 +1,185 @@
+// Internal declarations shared by the libdsa translation units: argument
+// blocks passed by value to kernels, device helpers, and host launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+constexpr int kMaxStages = 4;
+constexpr float kNegBig = -1.0e30f;   // finite "no key yet" running max
+
+// ------------------------------------------------------------------------- //
+// argument blocks                                                           //
+// ------------------------------------------------------------------------- //
+struct KvLayout {
+  int B, Hq, Hkv, D;
+  int T;                     // prefill length, or decode token stride / capacity
+  int decode;                // 0 prefill, 1 decode
+  int nblk, bq;              // query blocks per sequence and their size (decode: 1, 1)
+  const int32_t* seq_lens;   // decode only
+  const int32_t* block_table;// decode paged, else nullptr
+  int page_size, page_shift, max_pages;
+};
+
+struct PruneArgs {
+  KvLayout kv;
+  const void* q;
+  const void* k;
+  int n_stages;
+  int chunk[kMaxStages];
+  int keep[kMaxStages];
+  int n_sink, n_window;
+  int32_t* idx;              // [R, L]
+  int L;
+  int R;                     // rows = B * nblk
+  int maxK;                  // longest chunk-start list of any stage
+  int maxNC;                 // longest chunk-score list of any stage
+  int n1max;                 // most stage-1 chunks of any row
+  int32_t* cnt;              // [R, kMaxStages] chunks kept by each stage
+  int32_t* starts;           // [2, R, maxK] chunk starts, ping-pong by stage parity
+  uint32_t* scores;          // [R, maxNC] orderable chunk-score keys
+  unsigned long long* visited;  // [n_stages] or nullptr
+};
+
+struct AttnArgs {
+  KvLayout kv;
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* idx;        // nullptr => dense causal rows [0, e)
+  int L;                     // idx row width
+  float* out;
+  float* part;               // decode split partials [B, Hq, n_splits, D + 2]
+  int n_splits;
+  int kps;                   // decode keys per split (multiple of 64)
+  float scale_log2;          // softmax scale * log2(e)
+};
+
+// ------------------------------------------------------------------------- //
+// device helpers                                                            //
+// ------------------------------------------------------------------------- //
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Monotone map float -> uint32 (larger float => larger key) with -0 == +0.
+__device__ __forceinline__ uint32_t score_key(float x) {
+  if (x == 0.0f) x = 0.0f;
+  uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+struct Geo {
+  int s, e;        // query block [s, e)
+  int sink_hi;     // sinks [0, sink_hi)
+  int mid_hi;      // prunable middle [n_sink, mid_hi), window [mid_hi, e)
+  int n1;          // whole stage-1 chunks
+};
+
+__device__ __forceinline__ Geo make_geo(int s, int e, int n_sink, int n_window, int l1) {
+  Geo g;
+  g.s = s;
+  g.e = e;
+  g.sink_hi = min(n_sink, e);
+  int mid = max(0, e - n_window - n_sink);
+  g.n1 = mid / l1;
+  g.mid_hi = n_sink + g.n1 * l1;
+  return g;
+}
+
+// Query block bounds of row r (decode: the last position of sequence r).
+__device__ __forceinline__ void row_bounds(const KvLayout& kv, int r, int& b, int& s, int& e) {
+  if (kv.decode) {
+    b = r;
+    e = kv.seq_lens[r];
+    s = e - 1;
+  } else {
+    b = r / kv.nblk;
+    s = (r % kv.nblk) * kv.bq;
+    e = s + kv.bq;
+  }
+}
+
+// Element offset of key/value row (b, g, p).
+__device__ __forceinline__ size_t kv_offset(const KvLayout& kv, int b, int g, int p) {
+  if (kv.block_table) {
+    int page = kv.block_table[static_cast<size_t>(b) * kv.max_pages + (p >> kv.page_shift)];
+    return ((static_cast<size_t>(page) * kv.Hkv + g) * kv.page_size + (p & (kv.page_size - 1))) *
+           kv.D;
+  }
+  return ((static_cast<size_t>(b) * kv.Hkv + g) * kv.T + p) * kv.D;
+}
+
+// Load N consecutive elements starting at ptr into fp32 registers.
+template <typename T, int N>
+struct SliceLoad;
+
+template <int N>
+struct SliceLoad<uint16_t, N> {
+  static __device__ __forceinline__ void run(const uint16_t* ptr, float* out) {
+    static_assert(N % 4 == 0, "bf16 slices are loaded 4 at a time");
+#pragma unroll
+    for (int i = 0; i < N; i += 4) {
+      uint2 w = *reinterpret_cast<const uint2*>(ptr + i);
+      out[i + 0] = __uint_as_float(w.x << 16);
+      out[i + 1] = __uint_as_float(w.x & 0xffff0000u);
+      out[i + 2] = __uint_as_float(w.y << 16);
+      out[i + 3] = __uint_as_float(w.y & 0xffff0000u);
+    }
+  }
+};
+
+template <int N>
+struct SliceLoad<float, N> {
+  static __device__ __forceinline__ void run(const float* ptr, float* out) {
+    static_assert(N % 4 == 0, "fp32 slices are loaded 4 at a time");
+#pragma unroll
+    for (int i = 0; i < N; i += 4) {
+      float4 w = *reinterpret_cast<const float4*>(ptr + i);
+      out[i + 0] = w.x;
+      out[i + 1] = w.y;
+      out[i + 2] = w.z;
+      out[i + 3] = w.w;
+    }
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ float load_one(const T* p);
+template <>
+__device__ __forceinline__ float load_one<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
+template <>
+__device__ __forceinline__ float load_one<float>(const float* p) { return *p; }
+
+// Sum / max over the 16 lanes of an aligned lane group (all lanes get the result).
+__device__ __forceinline__ float group16_sum(float v) {
+  v += __shfl_xor(v, 8, 16);
+  v += __shfl_xor(v, 4, 16);
+  v += __shfl_xor(v, 2, 16);
+  v += __shfl_xor(v, 1, 16);
+  return v;
+}
+__device__ __forceinline__ float group16_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 8, 16));
+  v = fmaxf(v, __shfl_xor(v, 4, 16));
+  v = fmaxf(v, __shfl_xor(v, 2, 16));
+  v = fmaxf(v, __shfl_xor(v, 1, 16));
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ------------------------------------------------------------------------- //
+// host launchers (defined in prune.hip / attn.hip)                          //
+// ------------------------------------------------------------------------- //
+hipError_t launch_prune(const PruneArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_sparse_attn(const AttnArgs& a, int dtype, hipStream_t stream);
+
+}  // namespace dsa

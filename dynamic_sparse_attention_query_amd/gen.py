@@ -23,6 +23,8 @@ Workload shapes follow the pages: Llama-3-8B-shaped attention (32 query heads,
 from __future__ import annotations
 
 import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 from typing import List, Optional, Sequence, Tuple
 
@@ -168,21 +170,74 @@ class Case:
         return self.cfg.batch
 
 
-def _grid(rng, shape) -> np.ndarray:
-    return rng.integers(-GRID_MAX, GRID_MAX + 1, size=shape, dtype=np.int8)
+BLOCK = 1 << 22          # values per independently seeded block
+_NORMAL_LEVELS = None
 
 
-def _normal(rng, shape, dtype: str) -> Values:
+def _pool_map(fn, n):
+    workers = max(1, min(16, os.cpu_count() or 1))
+    if n <= 1 or workers == 1:
+        return [fn(i) for i in range(n)]
+    with ThreadPoolExecutor(workers) as ex:
+        return list(ex.map(fn, range(n)))
+
+
+def _grid_fill(shape, seed: int, tag: int) -> np.ndarray:
+    """Uniform integer codes in [-8, 8]. Block i of BLOCK values is drawn from
+    SeedSequence([seed, tag, i]): 15 base-17 digits of one uniform draw below
+    17**15 give 15 exactly uniform codes."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.int8)
+
+    def block(i):
+        lo, hi = i * BLOCK, min(n, (i + 1) * BLOCK)
+        m = hi - lo
+        rng = np.random.default_rng([seed, tag, i])
+        x = rng.integers(0, 17 ** 15, size=(m + 14) // 15, dtype=np.uint64)
+        dig = np.empty((15, x.size), dtype=np.int8)
+        for r in range(15):
+            dig[r] = (x % np.uint64(17)).astype(np.int8) - GRID_MAX
+            x //= np.uint64(17)
+        out[lo:hi] = dig.reshape(-1)[:m]
+
+    _pool_map(block, (n + BLOCK - 1) // BLOCK)
+    return out.reshape(shape)
+
+
+def _normal_levels() -> np.ndarray:
+    """bf16 bit patterns of the standard-normal quantiles at (i + 0.5) / 65536."""
+    global _NORMAL_LEVELS
+    if _NORMAL_LEVELS is None:
+        from scipy.special import ndtri
+        u = (np.arange(65536, dtype=np.float64) + 0.5) / 65536.0
+        _NORMAL_LEVELS = bf16_round_bits(ndtri(u).astype(np.float32))
+    return _NORMAL_LEVELS
+
+
+def _normal_fill(shape, seed: int, tag: int, dtype: str) -> "Values":
+    """Standard-normal values. fp32: numpy normals per seeded block. bf16:
+    inverse-CDF sampling on a 65536-level quantile grid (finer than bf16's
+    resolution), stored as bf16 bit patterns."""
+    n = int(np.prod(shape))
     if dtype == "f32":
-        return Values(rng.standard_normal(size=shape, dtype=np.float32), "f32")
-    out = np.empty(shape, dtype=np.uint16)
-    flat = out.reshape(-1)
-    step = 1 << 24
-    n = flat.size
-    for i in range(0, n, step):           # bounded host memory for 1M/3M contexts
-        m = min(step, n - i)
-        flat[i:i + m] = bf16_round_bits(rng.standard_normal(size=m, dtype=np.float32))
-    return Values(out, "bf16")
+        out32 = np.empty(n, dtype=np.float32)
+
+        def block32(i):
+            lo, hi = i * BLOCK, min(n, (i + 1) * BLOCK)
+            out32[lo:hi] = np.random.default_rng([seed, tag, i]).standard_normal(size=hi - lo, dtype=np.float32)
+
+        _pool_map(block32, (n + BLOCK - 1) // BLOCK)
+        return Values(out32.reshape(shape), "f32")
+    lv = _normal_levels()
+    out = np.empty(n, dtype=np.uint16)
+
+    def block(i):
+        lo, hi = i * BLOCK, min(n, (i + 1) * BLOCK)
+        u = np.random.default_rng([seed, tag, i]).integers(0, 65536, size=hi - lo, dtype=np.uint16)
+        out[lo:hi] = lv[u]
+
+    _pool_map(block, (n + BLOCK - 1) // BLOCK)
+    return Values(out.reshape(shape), "bf16")
 
 
 def _sign_codes(codes: np.ndarray) -> np.ndarray:
@@ -197,19 +252,21 @@ def eligible_slots(origin: int, align: int, limit: int) -> int:
 def make_case(cfg: Config | str, **overrides) -> Case:
     """Draw the seeded inputs of a workload.
 
-    Draw order: lengths (ragged decode only), Q, K, V, then planted structure,
-    then the page permutation (paged decode only).
+    Every array is drawn from its own seed stream: tag 1 lengths, 2 Q, 3 the
+    Q block directions and perturbations (planted structure), 100 + b the keys
+    of sequence b, 200 + b its values, 4 the planted structure, 5 the page
+    permutation.
     """
     if isinstance(cfg, str):
         cfg = CONFIGS[cfg]
     if overrides:
         cfg = cfg.replace(**overrides)
-    rng = np.random.default_rng(cfg.seed)
     B, Hq, Hkv, d = cfg.batch, cfg.hq, cfg.hkv, cfg.d
+    seed = cfg.seed
 
     if cfg.ragged is not None:
         lo, hi = cfg.ragged
-        seq_lens = rng.integers(lo, hi + 1, size=B).astype(np.int32)
+        seq_lens = np.random.default_rng([seed, 1]).integers(lo, hi + 1, size=B).astype(np.int32)
     else:
         seq_lens = np.full(B, cfg.t, dtype=np.int32)
 
@@ -218,21 +275,22 @@ def make_case(cfg: Config | str, **overrides) -> Case:
     if cfg.mode == "prefill":
         if cfg.structure == "planted":
             nblk = cfg.t // cfg.block_q
-            u = _grid(rng, (B, Hq, nblk, d)).astype(np.int16)
-            eps = rng.integers(-2, 3, size=(B, Hq, cfg.t, d)).astype(np.int16)
+            u = _grid_fill((B, Hq, nblk, d), seed, 3).astype(np.int16)
+            eps = np.random.default_rng([seed, 3, 1]).integers(-2, 3, size=(B, Hq, cfg.t, d)).astype(np.int16)
             qc = np.clip(np.repeat(u, cfg.block_q, axis=2) + eps, -GRID_MAX, GRID_MAX).astype(np.int8)
         else:
-            qc = _grid(rng, (B, Hq, cfg.t, d))
+            qc = _grid_fill((B, Hq, cfg.t, d), seed, 2)
     else:
-        qc = _grid(rng, (cfg.n_queries, B, Hq, d))
+        qc = _grid_fill((cfg.n_queries, B, Hq, d), seed, 2)
     q = Values(qc, "grid")
 
     # ---- K, V ---------------------------------------------------------------
     k_list, v_list = [], []
     for b in range(B):
-        k_list.append(Values(_grid(rng, (Hkv, int(seq_lens[b]), d)), "grid"))
+        k_list.append(Values(_grid_fill((Hkv, int(seq_lens[b]), d), seed, 100 + b), "grid"))
     for b in range(B):
-        v_list.append(_normal(rng, (Hkv, int(seq_lens[b]), d), cfg.dtype))
+        v_list.append(_normal_fill((Hkv, int(seq_lens[b]), d), seed, 200 + b, cfg.dtype))
+    rng = np.random.default_rng([seed, 4])
 
     case = Case(cfg=cfg, q=q, k=k_list, v=v_list, seq_lens=seq_lens)
 
@@ -273,8 +331,9 @@ def make_case(cfg: Config | str, **overrides) -> Case:
             h = int(rng.integers(0, Hq))
             g = h * Hkv // Hq
             if cfg.mode == "prefill":
-                # random target query t* late enough to have middle keys before it
-                tq = int(rng.integers(origin + align + lag + cfg.block_q, T))
+                # random target query t* in the second half of the sequence,
+                # where the middle is long enough to be pruned
+                tq = int(rng.integers(max(T // 2, origin + align + lag + cfg.block_q), T))
                 ns = eligible_slots(origin, align, (tq // cfg.block_q) * cfg.block_q - lag)
                 j = int(rng.integers(0, ns))
                 qsrc = qc[b, h, tq]
@@ -294,7 +353,7 @@ def make_case(cfg: Config | str, **overrides) -> Case:
         ps = cfg.page_size
         pages = [-(-int(L) // ps) for L in seq_lens]
         total = int(sum(pages))
-        perm = rng.permutation(total).astype(np.int32)
+        perm = np.random.default_rng([seed, 5]).permutation(total).astype(np.int32)
         maxp = max(pages)
         bt = np.zeros((B, maxp), dtype=np.int32)
         off = 0

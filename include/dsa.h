@@ -1,0 +1,166 @@
+/*
+ * dsa.h -- C ABI of libdsa: dynamic, per-input block-sparse attention on
+ * AMD MI355X (gfx950).
+ *
+ * Two steps, each a stream-ordered call on caller-owned device memory:
+ *
+ *   dsa_prune_select  Hierarchical context pruning: for every query block,
+ *                     N stages each score the current key chunks through one
+ *                     SelectRep representative per (chunk, query head), take the
+ *                     max over heads and block queries, and keep the top-K
+ *                     chunks. The surviving keys plus the attention-sink and
+ *                     local-window keys form one ascending index row per block.
+ *                     (InfiniteHiP page, 2502.08910, section 3.4: "Formal
+ *                     Mechanism of a Single Pruning Stage", steps 1-8;
+ *                     "The Representative Token Selection Algorithm
+ *                     (SelectRep)"; "Important: Sink and Streaming Tokens Are
+ *                     Never Pruned".)
+ *   dsa_sparse_attn   Causal softmax attention of each block's queries over the
+ *                     keys of its index row: a gathered FlashAttention pass for
+ *                     prefill, a split-key Flash-Decoding pass for decode.
+ *                     (InfiniteHiP page, "Block Sparse Attention
+ *                     Implementation"; InfLLM blog page, "Mathematical
+ *                     Formulation of Efficient Softmax Normalization";
+ *                     MInference page, masked-attention formulation and
+ *                     in-kernel causal masking.)
+ *   dsa_dense_attn    Exact causal attention over all keys: the comparison
+ *                     point (InfiniteHiP page, "Dense Attention Optimizations"
+ *                     and "Formal Background: Standard Multi-Head Attention").
+ *
+ * Conventions
+ *   - Every pointer argument named q, k, v, idx, out, seq_lens, block_table,
+ *     ws or visited is DEVICE memory owned by the caller; dsa_shape and
+ *     dsa_params are HOST structs read only during the call.
+ *   - The library never allocates, frees or synchronises. Scratch memory is
+ *     the caller's workspace `ws` of at least dsa_workspace_bytes() bytes; one
+ *     workspace must not be shared by calls that may run concurrently.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Calls only
+ *     enqueue kernels; errors detected on the host are returned before any
+ *     launch, launch failures return DSA_ERR_HIP, device faults surface at the
+ *     caller's next synchronisation. Nothing throws across the ABI.
+ *   - Results are bitwise deterministic run to run.
+ *
+ * Layouts (row-major, contiguous unless stated)
+ *   PREFILL  q [B, Hq, T, d]; k, v [B, Hkv, T, d]; out [B, Hq, T, d] fp32;
+ *            idx [B, T / block_q, L] int32.
+ *   DECODE   q [B, Hq, d] (the query at position seq_lens[b]-1);
+ *            k, v either contiguous [B, Hkv, t, d] (sequence b uses its first
+ *            seq_lens[b] positions) or, when block_table != NULL, page pools
+ *            [n_pages, Hkv, page_size, d] with position p of sequence b in page
+ *            block_table[b * max_pages + p / page_size] at slot p % page_size;
+ *            out [B, Hq, d] fp32; idx [B, L] int32.
+ *   Query head h reads kv head h / (Hq / Hkv).
+ *   q, k, v share one dtype (fp32 or bf16); out is always fp32.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = 1,   /* a parameter, shape or pointer violates a rule below */
+  DSA_ERR_UNSUPPORTED = 2,   /* valid but not implemented (e.g. d not in {64,128}) */
+  DSA_ERR_WORKSPACE = 3,     /* ws NULL or ws_bytes < dsa_workspace_bytes() */
+  DSA_ERR_HIP = 4            /* a HIP launch failed; see dsa_last_error() */
+} dsa_status;
+
+typedef enum { DSA_F32 = 0, DSA_BF16 = 1 } dsa_dtype;
+typedef enum { DSA_PREFILL = 0, DSA_DECODE = 1 } dsa_mode;
+
+#define DSA_MAX_STAGES 4
+
+/* One pruning configuration: the stage tuples (l_c, k) with a single query
+ * block size b_q (InfiniteHiP page, "Stage Configuration"), plus the
+ * always-kept sink and window counts.
+ *   n_stages   1..DSA_MAX_STAGES
+ *   block_q    b_q: PREFILL requires T % block_q == 0 and block_q <= 64;
+ *              DECODE requires block_q == 1
+ *   chunk[i]   l_c of stage i: a power of two; chunk[i+1] divides chunk[i]
+ *   keep[i]    k of stage i: a multiple of chunk[i], >= 0; keep[i+1] <= keep[i]
+ *   n_sink     keys [0, n_sink) are always kept (>= 0)
+ *   n_window   the n_window most recent keys of a block, [e - n_window, e)
+ *              with e one past the block's last query, are always kept (>= 0)
+ * The prunable middle of block [s, e) is [n_sink, e - n_window); stage 1
+ * partitions it into whole chunks of chunk[0] keys starting at n_sink, and the
+ * tail that does not fill a chunk is kept with the window. */
+typedef struct {
+  int32_t n_stages;
+  int32_t block_q;
+  int32_t chunk[DSA_MAX_STAGES];
+  int32_t keep[DSA_MAX_STAGES];
+  int32_t n_sink;
+  int32_t n_window;
+} dsa_params;
+
+/* Problem shape.
+ *   mode, dtype   dsa_mode / dsa_dtype values
+ *   batch, hq, hkv, d   B >= 1; hq % hkv == 0, hq / hkv <= 8; d in {64, 128}
+ *   t             PREFILL: tokens per sequence. DECODE: the largest context
+ *                 length any sequence may have, and the token stride of
+ *                 contiguous k / v
+ *   seq_lens      DECODE: device int32 [B], each in [1, t]; ignored for PREFILL
+ *   block_table   DECODE: device int32 [B, max_pages] or NULL (contiguous)
+ *   page_size, max_pages   paged DECODE only: page_size a power of two;
+ *                 max_pages * page_size >= t */
+typedef struct {
+  int32_t mode;
+  int32_t dtype;
+  int32_t batch, hq, hkv, d;
+  int32_t t;
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  int32_t page_size, max_pages;
+} dsa_shape;
+
+/* Width L of an index row: n_sink + keep[n_stages-1] + n_window + chunk[0] - 1
+ * rounded up to a multiple of 64; -1 if p is NULL or invalid. */
+int32_t dsa_index_width(const dsa_params* p);
+
+/* Workspace bytes for any of the three calls on this shape (p may be NULL when
+ * only dsa_dense_attn is used). Returns DSA_ERR_INVALID_ARG for an invalid
+ * shape or params. */
+dsa_status dsa_workspace_bytes(const dsa_shape* shape, const dsa_params* p, size_t* out_bytes);
+
+/* Hierarchical pruning (see above). Writes idx: every row fully, with the
+ * kept key positions strictly ascending followed by -1 padding to L =
+ * dsa_index_width(p). Stage scores are unscaled dot products; the right half of
+ * a SelectRep split wins only on a strictly greater score; top-K breaks score
+ * ties towards the lower chunk index; a stage with no more chunks than it keeps
+ * keeps them all.
+ * visited: NULL, or device uint64 [n_stages] that is INCREMENTED by the number
+ * of distinct (kv head, key position) rows SelectRep reads in each stage (a
+ * traffic diagnostic; costs extra atomics). */
+dsa_status dsa_prune_select(const dsa_shape* shape, const void* q, const void* k,
+                            const dsa_params* p, int32_t* idx,
+                            void* ws, size_t ws_bytes, uint64_t* visited, void* stream);
+
+/* out[h, t] = sum over p in row, p <= t, of softmax_p(scale * q_{h,t} . k_p) v_p,
+ * for every query t of each block (row = idx row of the block; negative
+ * entries are ignored, as are entries beyond the block's last query).
+ * block_q is the query block size the rows were built with (PREFILL: a power
+ * of two in [4, 64] dividing t; DECODE: 1). idx_width is the row width (>= 1).
+ * scale <= 0 selects 1/sqrt(d). */
+dsa_status dsa_sparse_attn(const dsa_shape* shape, const void* q, const void* k, const void* v,
+                           const int32_t* idx, int32_t idx_width, int32_t block_q, float scale,
+                           float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Exact causal attention over keys [0, t] for every query t. */
+dsa_status dsa_dense_attn(const dsa_shape* shape, const void* q, const void* k, const void* v,
+                          float scale, float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* dsa_status_str(dsa_status s);
+
+/* Message of the last error returned on the calling host thread ("" if none). */
+const char* dsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_H */

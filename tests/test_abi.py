@@ -1,0 +1,105 @@
+"""The C ABI boundary on the host: the library loads, exports what include/dsa.h
+declares, sizes workspaces, and rejects invalid arguments with status codes
+before launching anything (no call here reaches the GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from dynamic_sparse_attention_query_amd import _lib
+from dynamic_sparse_attention_query_amd._lib import (DSA_BF16, DSA_DECODE, DSA_ERR_INVALID_ARG,
+                                                     DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_F32,
+                                                     DSA_PREFILL, Params, Shape)
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "dsa.h")
+
+P2 = Params(64, (64, 32, 8), (16384, 8192, 4096), 64, 1024)
+P3 = Params(1, (256, 32, 8), (32768, 8192, 4096), 64, 1024)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\*]+\s+)+\**(dsa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_index_width():
+    assert _lib.index_width(P2) == 5248          # 64 + 4096 + 1024 + 63 -> 5248
+    assert _lib.index_width(P3) == 5440          # 64 + 4096 + 1024 + 255 -> 5440
+    assert _lib.index_width(Params(32, (16, 4), (2048, 512), 16, 64)) == 640
+    assert _lib.index_width(Params(1, (3,), (6,), 0, 0)) == -1          # chunk not a power of two
+    assert _lib.index_width(Params(1, (16, 8), (64, 128), 0, 0)) == -1  # keep grows
+    assert _lib.index_width(Params(1, (16, 32), (64, 64), 0, 0)) == -1  # chunk does not divide
+    assert _lib.index_width(Params(1, (16,), (24,), 0, 0)) == -1        # keep not a multiple
+
+
+def test_workspace_sizes():
+    s = Shape(DSA_PREFILL, DSA_BF16, 1, 32, 8, 128, 131072)
+    assert _lib.workspace_bytes(s, P2) > 2048 * 2030 * 4
+    d = Shape(DSA_DECODE, DSA_BF16, 1, 32, 8, 128, 1 << 20, seq_lens=1)
+    assert _lib.workspace_bytes(d, P3) >= 32 * 2048 * 130 * 4
+    assert _lib.workspace_bytes(d, None) > 0
+
+
+@pytest.mark.parametrize("shape,params,code", [
+    (Shape(DSA_PREFILL, DSA_BF16, 1, 32, 8, 128, 100), P2, DSA_ERR_INVALID_ARG),     # t % b_q
+    (Shape(DSA_PREFILL, DSA_BF16, 1, 30, 8, 128, 4096), P2, DSA_ERR_INVALID_ARG),    # hq % hkv
+    (Shape(DSA_PREFILL, DSA_BF16, 1, 32, 8, 96, 4096), P2, DSA_ERR_UNSUPPORTED),     # d
+    (Shape(DSA_PREFILL, 7, 1, 32, 8, 128, 4096), P2, DSA_ERR_INVALID_ARG),           # dtype
+    (Shape(DSA_DECODE, DSA_BF16, 1, 32, 8, 128, 4096), P3, DSA_ERR_INVALID_ARG),     # no seq_lens
+    (Shape(DSA_DECODE, DSA_BF16, 1, 32, 8, 128, 4096, seq_lens=1), P2, DSA_ERR_INVALID_ARG),  # b_q
+    (Shape(DSA_DECODE, DSA_BF16, 1, 32, 8, 128, 4096, seq_lens=1, block_table=1, page_size=48,
+           max_pages=100), P3, DSA_ERR_INVALID_ARG),                                # page size
+    (Shape(DSA_DECODE, DSA_BF16, 1, 32, 8, 128, 4096, seq_lens=1, block_table=1, page_size=64,
+           max_pages=10), P3, DSA_ERR_INVALID_ARG),                                 # too few pages
+    (Shape(DSA_PREFILL, DSA_F32, 1, 48, 4, 64, 4096), Params(32, (16,), (512,), 16, 64),
+     DSA_ERR_UNSUPPORTED),                                                          # group of 12
+])
+def test_invalid_arguments_are_rejected(shape, params, code):
+    with pytest.raises(_lib.DsaError) as ei:
+        _lib.workspace_bytes(shape, params)
+    assert ei.value.status == code
+
+
+def test_prune_select_rejects_before_launch(lib):
+    s = Shape(DSA_PREFILL, DSA_BF16, 1, 32, 8, 128, 4096)
+    # null pointers
+    with pytest.raises(_lib.DsaError) as ei:
+        _lib.prune_select_raw(s, 0, 0, P2, 0, 0, 0)
+    assert ei.value.status == DSA_ERR_INVALID_ARG
+    # undersized workspace (pointers are never dereferenced on this path)
+    with pytest.raises(_lib.DsaError) as ei:
+        _lib.prune_select_raw(s, 16, 16, P2, 16, 16, 8)
+    assert ei.value.status == DSA_ERR_WORKSPACE
+    assert "workspace" in lib.dsa_last_error().decode()
+
+
+def test_attention_rejects_before_launch():
+    s = Shape(DSA_PREFILL, DSA_BF16, 1, 32, 8, 128, 4096)
+    with pytest.raises(_lib.DsaError) as ei:
+        _lib.sparse_attn_raw(s, 16, 16, 16, 16, 5248, 48, 0.0, 16, 16, 1 << 20)   # b_q not pow2
+    assert ei.value.status == DSA_ERR_UNSUPPORTED
+    with pytest.raises(_lib.DsaError) as ei:
+        _lib.sparse_attn_raw(s, 16, 16, 16, 16, 0, 64, 0.0, 16, 16, 1 << 20)      # width 0
+    assert ei.value.status == DSA_ERR_INVALID_ARG
+    d = Shape(DSA_DECODE, DSA_BF16, 1, 32, 8, 128, 1 << 20, seq_lens=16)
+    with pytest.raises(_lib.DsaError) as ei:
+        _lib.dense_attn_raw(d, 16, 16, 16, 0.0, 16, 16, 64)                       # workspace
+    assert ei.value.status == DSA_ERR_WORKSPACE
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert _lib.status_str(code).startswith("DSA_")
