@@ -1,0 +1,352 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse-attention hot path on one MI355X.
+
+Headline: 1M-context decode attention, one step = prune_select (three pruning
+stages) + sparse_attn for one new query of a batch-1 sequence with 32 query /
+8 KV heads, d=128, T=1,048,576 bf16. Reported as microseconds per token, with
+the step's algorithmic HBM bytes / time against the 8 TB/s HBM peak.
+
+Secondary figures on the same JSON line: 128K sparse prefill TFLOP/s against
+the bf16 MFMA peak, the library's dense decode at 1M, per-kernel durations
+from HIP events on the launch stream, and the CPU oracle timed on the host.
+
+    python bench.py [--steps K] [--warmup W] [--no-prefill] [--no-dense] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode attn us/token @1M ctx (HBM GB/s, % peak); 128K sparse prefill TFLOP/s"
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--replicas", type=int, default=8,
+                    help="KV copies cycled through so consecutive steps share no cache lines")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+# --------------------------------------------------------------------------- #
+# decode at 1M                                                                #
+# --------------------------------------------------------------------------- #
+def decode_bench(args, res):
+    import torch
+    from dynamic_sparse_attention_query_amd import _lib, gen
+    from dynamic_sparse_attention_query_amd._lib import DSA_BF16, DSA_DECODE, Shape
+    from dynamic_sparse_attention_query_amd.inputs import params_of, to_device
+
+    t0 = time.time()
+    case = gen.make_case("c3")
+    cfg = case.cfg
+    dev = to_device(case)
+    log(f"decode inputs ready in {time.time() - t0:.1f}s")
+    p = params_of(cfg)
+    lib = _lib.load()
+    T, Hq, Hkv, d = cfg.t, cfg.hq, cfg.hkv, cfg.d
+    Ks = [dev.k] + [dev.k.clone() for _ in range(args.replicas - 1)]
+    Vs = [dev.v] + [dev.v.clone() for _ in range(args.replicas - 1)]
+    NQ = dev.q.shape[0]
+    Qs = [dev.q[i].contiguous() for i in range(NQ)]
+    shape = Shape(DSA_DECODE, DSA_BF16, 1, Hq, Hkv, d, T, seq_lens=dev.seq_lens.data_ptr())
+    L = _lib.index_width(p)
+    wsb = _lib.workspace_bytes(shape, p)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    idx = torch.empty(L, dtype=torch.int32, device="cuda")
+    out = torch.empty((1, Hq, d), dtype=torch.float32, device="cuda")
+    cs, cp = shape.c(), p.c()
+
+    def launch(i, visited=None):
+        q, r = Qs[i % NQ], i % args.replicas
+        sp = torch.cuda.current_stream().cuda_stream
+        st = lib.dsa_prune_select(ctypes.byref(cs), q.data_ptr(), Ks[r].data_ptr(), ctypes.byref(cp),
+                                  idx.data_ptr(), ws.data_ptr(), wsb,
+                                  visited.data_ptr() if visited is not None else None, sp)
+        st |= lib.dsa_sparse_attn(ctypes.byref(cs), q.data_ptr(), Ks[r].data_ptr(), Vs[r].data_ptr(),
+                                  idx.data_ptr(), L, 1, 0.0, out.data_ptr(), ws.data_ptr(), wsb, sp)
+        if st:
+            raise RuntimeError(lib.dsa_last_error().decode())
+
+    # algorithmic bytes of each query's step: distinct K rows SelectRep reads
+    # (counted by the kernels) + K and V rows of every kept key
+    row_bytes = d * 2
+    stage_bytes = np.zeros((NQ, len(p.chunk)))
+    attn_bytes = np.zeros(NQ)
+    vis = torch.zeros(len(p.chunk), dtype=torch.int64, device="cuda")
+    for i in range(NQ):
+        vis.zero_()
+        launch(i, vis)
+        torch.cuda.synchronize()
+        stage_bytes[i] = vis.cpu().numpy() * row_bytes
+        attn_bytes[i] = int((idx >= 0).sum().item()) * Hkv * 2 * row_bytes
+    step_bytes = stage_bytes.sum(1) + attn_bytes
+
+    K, W = args.steps, args.warmup
+    graphs = None
+    if not args.eager:
+        graphs = []
+        torch.cuda.synchronize()
+        for i in range(NQ):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                launch(i)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run(i):
+        if graphs is not None:
+            graphs[i % NQ].replay()
+        else:
+            launch(i)
+
+    for i in range(W):
+        run(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start = time.perf_counter()
+    e0.record()
+    for i in range(W, W + K):
+        run(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_start) * 1e3
+    ev_ms = e0.elapsed_time(e1)
+    used = [i % NQ for i in range(W, W + K)]
+    bytes_avg = float(step_bytes[used].mean())
+    us_step = wall_ms * 1e3 / K
+    log(f"decode 1M: {us_step:.1f} us/step wall, {ev_ms * 1e3 / K:.1f} us/step events")
+
+    # per-kernel durations from HIP events on the launch stream (eager pass)
+    _lib.profile_begin()
+    for i in range(W, W + K):
+        launch(i)
+    prof = _lib.profile_end()
+    kern_us = {k: v[1] * 1e3 / v[0] for k, v in prof.items()}
+    per_launch_bytes = {
+        "prune_score_stage1": float(stage_bytes[used, 0].mean()),
+        "prune_score_stage2": float(stage_bytes[used, 1].mean()),
+        "prune_score_stage3": float(stage_bytes[used, 2].mean()),
+        "attn_decode_partial": float(attn_bytes[used].mean()),
+    }
+    dom = max(kern_us, key=kern_us.get)
+    roof = None
+    if dom in per_launch_bytes:
+        ach = per_launch_bytes[dom] / (kern_us[dom] * 1e-6) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": None,
+                "avg_us": round(kern_us[dom], 2), "algorithmic_bytes_per_launch": int(per_launch_bytes[dom])}
+    res["decode"] = dict(us_per_step=us_step, event_us_per_step=ev_ms * 1e3 / K, wall_ms=wall_ms,
+                         bytes_per_step=bytes_avg, stage_rows=(stage_bytes[used].mean(0) / row_bytes).tolist(),
+                         kernels_us={k: round(v, 2) for k, v in kern_us.items()}, roofline=roof,
+                         mode="graph" if graphs is not None else "eager")
+
+    if not args.no_dense:
+        reps = 5
+        dshape_ws = _lib.workspace_bytes(shape, None)
+        dws = torch.empty(dshape_ws, dtype=torch.uint8, device="cuda")
+        for i in range(reps + 1):
+            if i == 1:
+                torch.cuda.synchronize()
+                e0.record()
+            r = i % args.replicas
+            st = lib.dsa_dense_attn(ctypes.byref(cs), Qs[i].data_ptr(), Ks[r].data_ptr(), Vs[r].data_ptr(),
+                                    0.0, out.data_ptr(), dws.data_ptr(), dshape_ws,
+                                    torch.cuda.current_stream().cuda_stream)
+            if st:
+                raise RuntimeError(lib.dsa_last_error().decode())
+        e1.record()
+        torch.cuda.synchronize()
+        dense_us = e0.elapsed_time(e1) * 1e3 / reps
+        kv_bytes = 2 * Hkv * T * d * 2
+        res["dense"] = dict(us=dense_us, gbps=kv_bytes / (dense_us * 1e-6) / 1e9, bytes=kv_bytes)
+        del dws
+    del Ks, Vs, dev, ws
+    torch.cuda.empty_cache()
+    return case
+
+
+# --------------------------------------------------------------------------- #
+# prefill at 128K                                                             #
+# --------------------------------------------------------------------------- #
+def prefill_algorithmic_flops(cfg, n_row: np.ndarray):
+    """SelectRep evaluations (b_q * 2d flops each, one per distinct representative
+    per (chunk, query head) of every stage that prunes) and attention over the
+    visible (query, key) pairs (4d flops each: q.k and p.v)."""
+    bq, d, Hq = cfg.block_q, cfg.d, cfg.hq
+    nblk = cfg.t // bq
+    sel = 0
+    for m in range(nblk):
+        e = (m + 1) * bq
+        nc = max(0, e - cfg.n_window - cfg.n_sink) // cfg.chunk[0]
+        for i, (l, k) in enumerate(zip(cfg.chunk, cfg.keep)):
+            if i > 0:
+                nc = kept * (cfg.chunk[i - 1] // l)
+            kc = k // l
+            if nc > kc:
+                sel += nc * Hq * (1 + int(math.log2(l)))
+            kept = min(nc, kc)
+    sel_flops = sel * bq * 2 * d
+    assert cfg.n_window >= bq
+    pairs = (bq * (n_row.astype(np.int64) - bq) + bq * (bq + 1) // 2).sum()
+    attn_flops = int(pairs) * Hq * 4 * d
+    return sel_flops, attn_flops
+
+
+def prefill_bench(args, res):
+    import torch
+    from dynamic_sparse_attention_query_amd import _lib, api, gen
+    from dynamic_sparse_attention_query_amd.inputs import params_of, to_device
+
+    t0 = time.time()
+    case = gen.make_case("c2_128k")
+    cfg = case.cfg
+    dev = to_device(case)
+    del case
+    log(f"prefill inputs ready in {time.time() - t0:.1f}s")
+    p = params_of(cfg)
+    idx = api.prune_select(dev.q, dev.k, p)
+    out = api.sparse_attn(dev.q, dev.k, dev.v, idx, p)
+    torch.cuda.synchronize()
+    reps = 3
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        api.prune_select(dev.q, dev.k, p, out=idx.view(-1))
+        api.sparse_attn(dev.q, dev.k, dev.v, idx, p, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    _lib.profile_begin()
+    api.prune_select(dev.q, dev.k, p, out=idx.view(-1))
+    api.sparse_attn(dev.q, dev.k, dev.v, idx, p, out=out)
+    prof = _lib.profile_end()
+    n_row = (idx >= 0).sum(-1).view(-1).cpu().numpy()
+    sel_f, attn_f = prefill_algorithmic_flops(cfg, n_row)
+    tot = sel_f + attn_f
+    prune_ms = sum(v[1] for k, v in prof.items() if k.startswith("prune_"))
+    attn_ms = sum(v[1] for k, v in prof.items() if k.startswith("attn_"))
+    res["prefill"] = dict(ms=ms, tflops=tot / (ms * 1e-3) / 1e12, algorithmic_tflop=tot / 1e12,
+                          selectrep_tflop=sel_f / 1e12, attn_tflop=attn_f / 1e12,
+                          prune_ms=prune_ms, attn_ms=attn_ms,
+                          attn_tflops=attn_f / (attn_ms * 1e-3) / 1e12 if attn_ms else None,
+                          kernels_ms={k: round(v[1] / v[0], 3) for k, v in prof.items()})
+    log(f"prefill 128K: {ms:.1f} ms, {res['prefill']['tflops']:.1f} TFLOP/s")
+    del dev, idx, out
+    torch.cuda.empty_cache()
+
+
+# --------------------------------------------------------------------------- #
+# CPU oracle baseline                                                         #
+# --------------------------------------------------------------------------- #
+def cpu_baseline(args, case, res):
+    from threadpoolctl import threadpool_limits
+
+    from oracle import ref
+    cfg = case.cfg
+    rp = ref.Params(1, cfg.chunk, cfg.keep, cfg.n_sink, cfg.n_window)
+    T = cfg.t
+    n = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while time.perf_counter() - t0 < args.cpu_seconds and n < case.q.shape[0]:
+            Q = case.q.sub((n, 0))[:, None, :]
+            row = ref.prune_block(Q, case.k[0], T - 1, T, rp)
+            ref.attend_block(Q, case.k[0], case.v[0], row, T - 1, ref.default_scale(cfg.d))
+            n += 1
+    el = time.perf_counter() - t0
+    res["cpu"] = {"value": round(el / n * 1e6, 1), "unit": "us/token", "cores": 1, "kind": "oracle",
+                  "sample": f"{n} decode steps (distinct queries) of the 1M-token workload, "
+                            f"oracle prune + attend, single thread, {el:.1f}s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} (WORLD_SIZE {world}) is not supported; "
+              "this build has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    res = {}
+    case = decode_bench(args, res)
+    if not args.no_prefill:
+        prefill_bench(args, res)
+    if not args.no_cpu:
+        cpu_baseline(args, case, res)
+
+    dec = res["decode"]
+    gbps = dec["bytes_per_step"] / (dec["us_per_step"] * 1e-6) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(dec["us_per_step"], 2),
+        "unit": "us/token",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["us_per_step"] / 1e3, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "c3-decode-1m: B=1, 32 q / 8 kv heads, d=128, T=1048576 bf16 grid K, N(0,1) V; "
+                               "stages (l_c, k) = (256, 32768), (32, 8192), (8, 4096); 64 sink, 1024 window; "
+                               "fresh query each step, 8 KV replicas cycled",
+                   "global_batch": 1, "seq_len": 1048576, "parallelism": "none (1 GPU)"},
+        "hbm_gbps": round(gbps, 1),
+        "hbm_pct_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),
+        "algorithmic_bytes_per_step": int(dec["bytes_per_step"]),
+        "selectrep_rows_per_stage": [round(x) for x in dec["stage_rows"]],
+        "timing_mode": dec["mode"],
+        "kernels_us": dec["kernels_us"],
+        "roofline": dec["roofline"],
+    }
+    if "dense" in res:
+        line["dense_decode_1m"] = {"us": round(res["dense"]["us"], 1), "gbps": round(res["dense"]["gbps"], 1),
+                                   "pct_peak": round(100 * res["dense"]["gbps"] / PEAK_HBM_GBPS, 2),
+                                   "sparse_speedup": round(res["dense"]["us"] / dec["us_per_step"], 2)}
+    if "prefill" in res:
+        pf = res["prefill"]
+        line["prefill_128k"] = {"ms": round(pf["ms"], 2), "tflops": round(pf["tflops"], 2),
+                                "pct_bf16_peak": round(100 * pf["tflops"] / PEAK_BF16_TFLOPS, 2),
+                                "algorithmic_tflop": round(pf["algorithmic_tflop"], 2),
+                                "selectrep_tflop": round(pf["selectrep_tflop"], 2),
+                                "attn_tflop": round(pf["attn_tflop"], 2),
+                                "prune_ms": round(pf["prune_ms"], 2), "attn_ms": round(pf["attn_ms"], 2),
+                                "kernels_ms": pf["kernels_ms"]}
+    if "cpu" in res:
+        line["cpu_baseline"] = res["cpu"]
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

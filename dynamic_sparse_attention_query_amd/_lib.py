@@ -20,7 +20,7 @@ DSA_PREFILL, DSA_DECODE = 0, 1
 MAX_STAGES = 4
 
 EXPORTS = ("dsa_index_width", "dsa_workspace_bytes", "dsa_prune_select", "dsa_sparse_attn",
-           "dsa_dense_attn", "dsa_status_str", "dsa_last_error")
+           "dsa_dense_attn", "dsa_profile_begin", "dsa_profile_end", "dsa_status_str", "dsa_last_error")
 
 
 class CParams(ctypes.Structure):
@@ -35,6 +35,10 @@ class CShape(ctypes.Structure):
                 ("d", ctypes.c_int32), ("t", ctypes.c_int32),
                 ("seq_lens", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
                 ("page_size", ctypes.c_int32), ("max_pages", ctypes.c_int32)]
+
+
+class CKernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double)]
 
 
 class DsaError(RuntimeError):
@@ -66,6 +70,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dsa_sparse_attn.restype = ctypes.c_int
     lib.dsa_dense_attn.argtypes = [ctypes.POINTER(CShape), vp, vp, vp, ctypes.c_float, vp, vp, sz, vp]
     lib.dsa_dense_attn.restype = ctypes.c_int
+    lib.dsa_profile_begin.argtypes = []
+    lib.dsa_profile_begin.restype = ctypes.c_int
+    lib.dsa_profile_end.argtypes = [ctypes.POINTER(CKernelTime), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
+    lib.dsa_profile_end.restype = ctypes.c_int
     lib.dsa_status_str.argtypes = [ctypes.c_int]
     lib.dsa_status_str.restype = ctypes.c_char_p
     lib.dsa_last_error.argtypes = []
@@ -166,3 +174,15 @@ def dense_attn_raw(shape: Shape, q: int, k: int, v: int, scale: float, out: int,
     cs = shape.c()
     _check(load().dsa_dense_attn(ctypes.byref(cs), q, k, v, scale, out, ws or None, ws_bytes,
                                  stream or None))
+
+
+def profile_begin():
+    _check(load().dsa_profile_begin())
+
+
+def profile_end() -> dict:
+    """{kernel name: (launches, total ms)} recorded since profile_begin()."""
+    buf = (CKernelTime * 64)()
+    n = ctypes.c_int32(0)
+    _check(load().dsa_profile_end(buf, 64, ctypes.byref(n)))
+    return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms)) for i in range(min(n.value, 64))}

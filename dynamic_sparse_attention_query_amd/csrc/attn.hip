@@ -294,8 +294,10 @@ __global__ void __launch_bounds__(256) k_prefill_generic(AttnArgs a) {
 template <typename T, int D, int G>
 static void launch_decode(const AttnArgs& a, hipStream_t st) {
   dim3 grid(a.n_splits, a.kv.Hkv, a.kv.B);
-  hipLaunchKernelGGL((k_decode_partial<T, D, G>), grid, dim3(256), 0, st, a);
-  hipLaunchKernelGGL((k_decode_combine<D>), dim3(a.kv.Hq, a.kv.B), dim3(256), 0, st, a);
+  DSA_LAUNCH(a.idx ? "attn_decode_partial" : "dense_decode_partial", (k_decode_partial<T, D, G>), grid,
+             dim3(256), st, a);
+  DSA_LAUNCH(a.idx ? "attn_decode_combine" : "dense_decode_combine", (k_decode_combine<D>),
+             dim3(a.kv.Hq, a.kv.B), dim3(256), st, a);
 }
 
 template <typename T, int D>
@@ -310,7 +312,7 @@ static hipError_t launch_attn_typed(const AttnArgs& a, hipStream_t st) {
     }
   } else {
     dim3 grid(a.kv.nblk, a.kv.Hq, a.kv.B);
-    hipLaunchKernelGGL((k_prefill_generic<T, D>), grid, dim3(256), 0, st, a);
+    DSA_LAUNCH(a.idx ? "attn_prefill" : "dense_prefill", (k_prefill_generic<T, D>), grid, dim3(256), st, a);
   }
   return hipGetLastError();
 }

@@ -177,6 +177,19 @@ __device__ __forceinline__ int wave_sum_int(int v) {
 }
 
 // ------------------------------------------------------------------------- //
+// launch with optional per-kernel timing (profile.hip)                      //
+// ------------------------------------------------------------------------- //
+void* prof_begin(const char* name, hipStream_t st);
+void prof_end(void* token, hipStream_t st);
+
+#define DSA_LAUNCH(NAME, KERNEL, GRID, BLOCK, STREAM, ...)                 \
+  do {                                                                     \
+    void* dsa_tok_ = ::dsa::prof_begin(NAME, STREAM);                      \
+    hipLaunchKernelGGL(KERNEL, GRID, BLOCK, 0, STREAM, __VA_ARGS__);       \
+    ::dsa::prof_end(dsa_tok_, STREAM);                                     \
+  } while (0)
+
+// ------------------------------------------------------------------------- //
 // host launchers (defined in prune.hip / attn.hip)                          //
 // ------------------------------------------------------------------------- //
 hipError_t launch_prune(const PruneArgs& a, int dtype, hipStream_t stream);

@@ -412,11 +412,16 @@ __global__ void __launch_bounds__(NT) k_topk(PruneArgs a, int stage) {
 // ------------------------------------------------------------------------- //
 // launcher                                                                  //
 // ------------------------------------------------------------------------- //
+static const char* const kScoreNames[kMaxStages] = {"prune_score_stage1", "prune_score_stage2",
+                                                    "prune_score_stage3", "prune_score_stage4"};
+static const char* const kTopkNames[kMaxStages] = {"prune_topk_stage1", "prune_topk_stage2",
+                                                   "prune_topk_stage3", "prune_topk_stage4"};
+
 template <typename T, int D, int G>
 static void launch_decode_score(const PruneArgs& a, int stage, int max_chunks, hipStream_t st) {
   const int cpw = 16 / a.kv.Hkv;
   dim3 grid((max_chunks + cpw - 1) / cpw, a.R);
-  hipLaunchKernelGGL((k_score_decode<T, D, G>), grid, dim3(256), 0, st, a, stage);
+  DSA_LAUNCH(kScoreNames[stage], (k_score_decode<T, D, G>), grid, dim3(256), st, a, stage);
 }
 
 template <typename T, int D>
@@ -441,18 +446,18 @@ static hipError_t launch_typed(const PruneArgs& a, hipStream_t st) {
         }
       } else {
         dim3 grid((max_chunks + 15) / 16, a.R);
-        hipLaunchKernelGGL((k_score_prefill<T, D>), grid, dim3(256), 0, st, a, stage);
+        DSA_LAUNCH(kScoreNames[stage], (k_score_prefill<T, D>), grid, dim3(256), st, a, stage);
       }
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int cap = a.maxNC;
     if (cap <= 1024 * 4) {
-      hipLaunchKernelGGL((k_topk<1024, 4>), dim3(a.R), dim3(1024), 0, st, a, stage);
+      DSA_LAUNCH(kTopkNames[stage], (k_topk<1024, 4>), dim3(a.R), dim3(1024), st, a, stage);
     } else if (cap <= 1024 * 16) {
-      hipLaunchKernelGGL((k_topk<1024, 16>), dim3(a.R), dim3(1024), 0, st, a, stage);
+      DSA_LAUNCH(kTopkNames[stage], (k_topk<1024, 16>), dim3(a.R), dim3(1024), st, a, stage);
     } else {
-      hipLaunchKernelGGL((k_topk<1024, 64>), dim3(a.R), dim3(1024), 0, st, a, stage);
+      DSA_LAUNCH(kTopkNames[stage], (k_topk<1024, 64>), dim3(a.R), dim3(1024), st, a, stage);
     }
     err = hipGetLastError();
     if (err != hipSuccess) return err;

@@ -154,6 +154,22 @@ dsa_status dsa_sparse_attn(const dsa_shape* shape, const void* q, const void* k,
 dsa_status dsa_dense_attn(const dsa_shape* shape, const void* q, const void* k, const void* v,
                           float scale, float* out, void* ws, size_t ws_bytes, void* stream);
 
+/* Per-kernel timing, a diagnostic for latency breakdowns. Between
+ * dsa_profile_begin() and dsa_profile_end(), every kernel the library launches
+ * is bracketed by HIP events recorded on its stream (do not profile inside
+ * graph capture). dsa_profile_end() waits for those events, stops recording
+ * and writes up to `capacity` aggregates (kernel name, launches, total
+ * milliseconds) to `out` (host memory); *n_out receives the number of kernels
+ * seen. */
+typedef struct {
+  char name[48];
+  int64_t launches;
+  double total_ms;
+} dsa_kernel_time;
+
+dsa_status dsa_profile_begin(void);
+dsa_status dsa_profile_end(dsa_kernel_time* out, int32_t capacity, int32_t* n_out);
+
 /* Static description of a status code. */
 const char* dsa_status_str(dsa_status s);
 
