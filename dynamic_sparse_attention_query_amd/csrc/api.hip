@@ -107,9 +107,9 @@ PruneLayout prune_layout(const dsa_shape* s, const dsa_params* p) {
   return L;
 }
 
-// decode split geometry: at most ~2048 splits per (sequence, kv head)
+// decode split geometry: 64-key sub-tiles, at most ~512 splits per (sequence, kv head)
 int keys_per_split(long long n_total) {
-  const long long per = (n_total + 64LL * 2048 - 1) / (64LL * 2048);
+  const long long per = (n_total + 64LL * 512 - 1) / (64LL * 512);
   return static_cast<int>(64 * std::max<long long>(1, per));
 }
 
@@ -215,8 +215,8 @@ dsa_status dsa_prune_select(const dsa_shape* s, const void* q, const void* k, co
   const long long L = index_width_ll(p);
   if (L > (1LL << 30)) return fail(DSA_ERR_INVALID_ARG, "index width overflows");
   const PruneLayout lay = prune_layout(s, p);
-  if (lay.maxNC > 65536)
-    return fail(DSA_ERR_UNSUPPORTED, "a stage would score %lld chunks per row (limit 65536)", lay.maxNC);
+  if (lay.maxNC > 32768)
+    return fail(DSA_ERR_UNSUPPORTED, "a stage would score %lld chunks per row (limit 32768)", lay.maxNC);
   if (!ws || ws_bytes < lay.bytes)
     return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, lay.bytes);
   dsa::PruneArgs a{};
@@ -226,6 +226,8 @@ dsa_status dsa_prune_select(const dsa_shape* s, const void* q, const void* k, co
   a.n_stages = p->n_stages;
   for (int i = 0; i < DSA_MAX_STAGES; ++i) {
     a.chunk[i] = i < p->n_stages ? p->chunk[i] : 1;
+    a.lchunk[i] = 0;
+    while ((1 << a.lchunk[i]) < a.chunk[i]) ++a.lchunk[i];
     a.keep[i] = i < p->n_stages ? p->keep[i] : 0;
   }
   a.n_sink = p->n_sink;

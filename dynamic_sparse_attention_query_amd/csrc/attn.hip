@@ -77,28 +77,30 @@ __global__ void __launch_bounds__(256) k_decode_partial(AttnArgs a) {
       spos[tid] = p;
     }
     __syncthreads();
+    // issue every K/V row load of the sub-tile before any arithmetic; padding
+    // entries read row 0 (always present) and are masked below
+    float kr[4][EPL], vr[4][EPL];
+    int pu[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      pu[u] = spos[gi + 16 * u];
+      const size_t off = kv_offset(kv, b, g, max(pu[u], 0)) + li * EPL;
+      SliceLoad<T, EPL>::run(K + off, kr[u]);
+      SliceLoad<T, EPL>::run(V + off, vr[u]);
+    }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int kk = gi + 16 * u;
-      const int p = spos[kk];
-      float kr[EPL], vr[EPL];
-      if (p >= 0) {
-        const size_t off = kv_offset(kv, b, g, p) + li * EPL;
-        SliceLoad<T, EPL>::run(K + off, kr);
-        SliceLoad<T, EPL>::run(V + off, vr);
-      } else {
+      const bool ok = pu[u] >= 0;
 #pragma unroll
-        for (int x = 0; x < EPL; ++x) { kr[x] = 0.f; vr[x] = 0.f; }
-      }
-#pragma unroll
-      for (int x = 0; x < EPL; ++x) sv[kk][li * EPL + x] = vr[x];
+      for (int x = 0; x < EPL; ++x) sv[kk][li * EPL + x] = ok ? vr[u][x] : 0.f;
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
         float d = 0.f;
 #pragma unroll
-        for (int x = 0; x < EPL; ++x) d = fmaf(q[hh][x], kr[x], d);
+        for (int x = 0; x < EPL; ++x) d = fmaf(q[hh][x], kr[u][x], d);
         d = group16_sum(d);
-        if (li == 0) sp[hh][kk] = (p >= 0) ? d * a.scale_log2 : -INFINITY;
+        if (li == 0) sp[hh][kk] = ok ? d * a.scale_log2 : -INFINITY;
       }
     }
     __syncthreads();
@@ -147,44 +149,62 @@ __global__ void __launch_bounds__(256) k_decode_partial(AttnArgs a) {
 }
 
 // Merge split partials: M = max m_s, out = sum o_s 2^(m_s-M) / sum l_s 2^(m_s-M).
+// 1024 threads: split weights go to LDS, then 1024/D groups of D threads each
+// sum a strided share of the splits with independent (unrolled) loads.
+constexpr int kCombineThreads = 1024;
+constexpr int kMaxSplits = 4096;
+
 template <int D>
-__global__ void __launch_bounds__(256) k_decode_combine(AttnArgs a) {
+__global__ void __launch_bounds__(kCombineThreads) k_decode_combine(AttnArgs a) {
   const int h = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
-  const size_t base = (static_cast<size_t>(b) * a.kv.Hq + h) * a.n_splits;
-  const float* P = a.part + base * (D + 2);
-  __shared__ float red[4];
-  __shared__ float sM;
-  // global max of the split maxima
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  constexpr int NW = kCombineThreads / 64;
+  const int ns = a.n_splits;
+  const float* P = a.part + (static_cast<size_t>(b) * a.kv.Hq + h) * ns * (D + 2);
+  __shared__ float wsh[kMaxSplits];
+  __shared__ float red[NW];
+  __shared__ float red2[NW];
   float m = kNegBig;
-  for (int s = tid; s < a.n_splits; s += 256) m = fmaxf(m, P[static_cast<size_t>(s) * (D + 2) + D]);
+  for (int s = tid; s < ns; s += kCombineThreads) m = fmaxf(m, P[static_cast<size_t>(s) * (D + 2) + D]);
   m = wave_max_f(m);
   if (lane == 0) red[w] = m;
   __syncthreads();
-  if (tid == 0) sM = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  const float M = sM;
-  // thread layout: 256 threads = (split lane group of 256/D) x D dims
-  constexpr int SG = 256 / D;
-  const int dd = tid % D, sg = tid / D;
-  float o = 0.f, l = 0.f;
-  for (int s = sg; s < a.n_splits; s += SG) {
+  float M = red[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) M = fmaxf(M, red[i]);
+  float lsum = 0.f;
+  for (int s = tid; s < ns; s += kCombineThreads) {
     const float* ps = P + static_cast<size_t>(s) * (D + 2);
     const float f = exp2f(ps[D] - M);
-    o = fmaf(ps[dd], f, o);
-    l = fmaf(ps[D + 1], f, l);
+    wsh[s] = f;
+    lsum = fmaf(ps[D + 1], f, lsum);
   }
+  lsum = wave_sum_f(lsum);
+  if (lane == 0) red2[w] = lsum;
+  __syncthreads();
+  float Ltot = 0.f;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) Ltot += red2[i];
+  constexpr int SG = kCombineThreads / D;
+  const int dd = tid % D, sg = tid / D;
+  float o = 0.f;
+  int s = sg;
+  for (; s + 7 * SG < ns; s += 8 * SG) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = P[static_cast<size_t>(s + u * SG) * (D + 2) + dd];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) o = fmaf(v[u], wsh[s + u * SG], o);
+  }
+  for (; s < ns; s += SG) o = fmaf(P[static_cast<size_t>(s) * (D + 2) + dd], wsh[s], o);
   __shared__ float so[SG][D];
-  __shared__ float slr[SG];
   so[sg][dd] = o;
-  if (dd == 0) slr[sg] = l;
   __syncthreads();
   if (sg == 0) {
-    float ot = 0.f, lt = 0.f;
+    float ot = 0.f;
 #pragma unroll
-    for (int x = 0; x < SG; ++x) { ot += so[x][dd]; lt += slr[x]; }
-    a.out[(static_cast<size_t>(b) * a.kv.Hq + h) * D + dd] = ot / lt;
+    for (int x = 0; x < SG; ++x) ot += so[x][dd];
+    a.out[(static_cast<size_t>(b) * a.kv.Hq + h) * D + dd] = ot / Ltot;
   }
 }
 
@@ -297,7 +317,7 @@ static void launch_decode(const AttnArgs& a, hipStream_t st) {
   DSA_LAUNCH(a.idx ? "attn_decode_partial" : "dense_decode_partial", (k_decode_partial<T, D, G>), grid,
              dim3(256), st, a);
   DSA_LAUNCH(a.idx ? "attn_decode_combine" : "dense_decode_combine", (k_decode_combine<D>),
-             dim3(a.kv.Hq, a.kv.B), dim3(256), st, a);
+             dim3(a.kv.Hq, a.kv.B), dim3(kCombineThreads), st, a);
 }
 
 template <typename T, int D>

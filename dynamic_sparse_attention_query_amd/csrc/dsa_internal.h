@@ -30,6 +30,7 @@ struct PruneArgs {
   const void* k;
   int n_stages;
   int chunk[kMaxStages];
+  int lchunk[kMaxStages];    // log2 of chunk[]
   int keep[kMaxStages];
   int n_sink, n_window;
   int32_t* idx;              // [R, L]
@@ -144,6 +145,49 @@ struct SliceLoad<float, N> {
       out[i + 2] = w.z;
       out[i + 3] = w.w;
     }
+  }
+};
+
+// A lane's slice of one row, kept in its storage format: bf16 stays packed in
+// pairs and dot products use the packed bf16 dot instruction (exact on the
+// input grid: every product and partial sum is representable in fp32).
+template <typename T, int N>
+struct RowSlice;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+template <int N>
+struct RowSlice<uint16_t, N> {
+  static_assert(N == 4 || N == 8, "bf16 slices hold 4 or 8 values");
+  uint32_t w[N / 2];
+  __device__ __forceinline__ void load(const uint16_t* p) {
+    if constexpr (N == 8) {
+      const uint4 x = *reinterpret_cast<const uint4*>(p);
+      w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
+    } else {
+      const uint2 x = *reinterpret_cast<const uint2*>(p);
+      w[0] = x.x; w[1] = x.y;
+    }
+  }
+  __device__ __forceinline__ float dot(const RowSlice& o) const {
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[i]),
+                                            __builtin_bit_cast(bf16x2_t, o.w[i]), acc, false);
+    return acc;
+  }
+};
+
+template <int N>
+struct RowSlice<float, N> {
+  float v[N];
+  __device__ __forceinline__ void load(const float* p) { SliceLoad<float, N>::run(p, v); }
+  __device__ __forceinline__ float dot(const RowSlice& o) const {
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < N; ++i) acc = fmaf(v[i], o.v[i], acc);
+    return acc;
   }
 };
 

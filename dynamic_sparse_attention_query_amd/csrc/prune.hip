@@ -3,14 +3,16 @@
 // "The Representative Token Selection Algorithm (SelectRep)").
 //
 // One prune_select call runs, for each stage i:
-//   score_i : every (row, chunk) of the stage's input list is scored: for each
-//             query head a SelectRep tournament picks one representative key,
-//             the chunk score is the max over heads and block queries of the
-//             representative's dot product (unscaled);
-//   topk_i  : one workgroup per row keeps the K = keep/chunk best chunks
-//             (score descending, chunk index ascending), writes their start
-//             positions in ascending order, and after the last stage writes
-//             the index row: sinks, kept chunks, window, -1 padding.
+//   score : every (row, chunk) of the stage's input list is scored: for each
+//           query head a SelectRep tournament picks one representative key;
+//           the chunk score is the max over heads and block queries of the
+//           representative's dot product (unscaled);
+//   top-K : per row, keep the K = keep/chunk best chunks (score descending,
+//           chunk index ascending), write their start positions in ascending
+//           order, and after the last stage write the index row: sinks, kept
+//           chunks, window, -1 padding.
+// The top-K is the stage's single global synchronisation point; it runs as its
+// own kernel, one workgroup per row.
 // Every chunk of every stage is a contiguous run of positions: stage 1 tiles
 // [n_sink, mid_hi) and each later chunk size divides the previous one.
 #include "dsa_internal.h"
@@ -23,16 +25,206 @@ namespace dsa {
 __device__ __forceinline__ int stage_input_chunks(const PruneArgs& a, int stage, int r,
                                                   const Geo& geo) {
   if (stage == 0) return geo.n1;
-  return a.cnt[r * kMaxStages + stage - 1] * (a.chunk[stage - 1] / a.chunk[stage]);
+  return a.cnt[r * kMaxStages + stage - 1] << (a.lchunk[stage - 1] - a.lchunk[stage]);
 }
 
-// First key position of chunk j of stage `stage` in row r.
+// First key position of chunk j of stage `stage` in row r (chunk sizes are
+// powers of two, so the parent chunk and the offset inside it are shifts).
 __device__ __forceinline__ int chunk_start(const PruneArgs& a, int stage, int r, int j) {
-  if (stage == 0) return a.n_sink + j * a.chunk[0];
-  const int ratio = a.chunk[stage - 1] / a.chunk[stage];
+  if (stage == 0) return a.n_sink + (j << a.lchunk[0]);
+  const int sh = a.lchunk[stage - 1] - a.lchunk[stage];
   const int32_t* prev =
       a.starts + static_cast<size_t>((stage - 1) & 1) * a.R * a.maxK + static_cast<size_t>(r) * a.maxK;
-  return prev[j / ratio] + (j % ratio) * a.chunk[stage];
+  return prev[j >> sh] + ((j & ((1 << sh) - 1)) << a.lchunk[stage]);
+}
+
+// ------------------------------------------------------------------------- //
+// top-K of one row + index assembly                                         //
+// ------------------------------------------------------------------------- //
+constexpr int kTopkThreads = 256;
+constexpr int kTopkWaves = kTopkThreads / 64;
+constexpr int kTopkMaxE = 128;          // rows of up to 32768 chunks (128 KiB of keys in LDS)
+
+__device__ __forceinline__ uint32_t wave_and_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v &= static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), o, 64));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_or_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), o, 64));
+  return v;
+}
+// number of lanes below this one whose bit is set in `mask`
+__device__ __forceinline__ int lanes_below(unsigned long long mask) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0));
+}
+
+// Run by all 256 threads of one workgroup. The row's keys are staged in LDS;
+// thread t handles keys j = x*256 + t (x < E), so for each x a wave covers 64
+// consecutive chunk indices and wave ballots give counts and in-order ranks
+// without shuffles. The K-th largest key tau is found by a
+// most-significant-first bit search over the bits that vary across the row's
+// keys (one barrier per bit); then every key > tau is kept plus the
+// lowest-index keys == tau until K are kept.
+template <int MAXE>
+__device__ void topk_row(const PruneArgs& a, int stage, int r, const Geo& geo, int nc) {
+  constexpr int NXW = MAXE * kTopkWaves;          // (x, wave) slots in index order
+  const int l = a.chunk[stage];
+  const int kc = a.keep[stage] >> a.lchunk[stage];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  __shared__ uint32_t red[2][kTopkWaves];
+  __shared__ int cnt[2][kTopkWaves];
+  __shared__ int wgt[NXW], weq[NXW];              // per-slot counts of keys > tau, == tau
+  __shared__ int bgt[NXW], beq[NXW];              // exclusive prefixes of the same
+  __shared__ int s_ngt;
+  __shared__ uint32_t skey[MAXE * kTopkThreads];
+  int32_t* out = a.starts + static_cast<size_t>(stage & 1) * a.R * a.maxK + static_cast<size_t>(r) * a.maxK;
+  int n_sel;
+  if (nc <= kc) {
+    int32_t* sel = reinterpret_cast<int32_t*>(skey);
+    for (int j = tid; j < nc; j += kTopkThreads) {
+      const int p = chunk_start(a, stage, r, j);
+      out[j] = p;
+      sel[j] = p;
+    }
+    n_sel = nc;
+  } else {
+    // keys are padded with 0 (below every real key) so every pass below is
+    // branch-free over all MAXE slots
+    const uint32_t* sc = a.scores + static_cast<size_t>(r) * a.maxNC;
+    uint32_t vand = 0xffffffffu, vor = 0u;
+    constexpr int LB = MAXE < 8 ? MAXE : 8;         // loads issued per batch
+#pragma unroll
+    for (int x0 = 0; x0 < MAXE; x0 += LB) {
+      uint32_t kreg[LB];
+#pragma unroll
+      for (int u = 0; u < LB; ++u) {
+        const int j = (x0 + u) * kTopkThreads + tid;
+        kreg[u] = j < nc ? sc[j] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < LB; ++u) {
+        skey[(x0 + u) * kTopkThreads + tid] = kreg[u];
+        if (kreg[u] != 0u) { vand &= kreg[u]; vor |= kreg[u]; }
+      }
+    }
+    vand = wave_and_u32(vand);
+    vor = wave_or_u32(vor);
+    if (lane == 0) { red[0][w] = vand; red[1][w] = vor; }
+    __syncthreads();
+    vand = 0xffffffffu;
+    vor = 0u;
+#pragma unroll
+    for (int i = 0; i < kTopkWaves; ++i) { vand &= red[0][i]; vor |= red[1][i]; }
+    const uint32_t varying = vand ^ vor;
+    uint32_t tau = vand;
+    int par = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      if (!((varying >> bit) & 1u)) continue;
+      const uint32_t c = tau | (1u << bit);
+      int n = 0;
+#pragma unroll
+      for (int x = 0; x < MAXE; ++x) n += __popcll(__ballot(skey[x * kTopkThreads + tid] >= c));
+      if (lane == 0) cnt[par][w] = n;
+      __syncthreads();
+      int tot = 0;
+#pragma unroll
+      for (int i = 0; i < kTopkWaves; ++i) tot += cnt[par][i];
+      if (tot >= kc) tau = c;
+      par ^= 1;
+    }
+    // per (x, wave) slot: counts of keys > tau and == tau
+#pragma unroll
+    for (int x = 0; x < MAXE; ++x) {
+      const uint32_t k = skey[x * kTopkThreads + tid];
+      const int ng = __popcll(__ballot(k > tau));
+      const int ne = __popcll(__ballot(k == tau));
+      if (lane == 0) { wgt[x * kTopkWaves + w] = ng; weq[x * kTopkWaves + w] = ne; }
+    }
+    __syncthreads();
+    if (w == 0) {                                    // exclusive scans over the slots
+      int cg = 0, ce = 0;
+      for (int i0 = 0; i0 < NXW; i0 += 64) {
+        const int i = i0 + lane;
+        const int g0 = i < NXW ? wgt[i] : 0, e0 = i < NXW ? weq[i] : 0;
+        int g = g0, e = e0;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int gu = __shfl_up(g, o, 64), eu = __shfl_up(e, o, 64);
+          if (lane >= o) { g += gu; e += eu; }
+        }
+        if (i < NXW) { bgt[i] = cg + g - g0; beq[i] = ce + e - e0; }
+        cg += __shfl(g, 63, 64);
+        ce += __shfl(e, 63, 64);
+      }
+      if (lane == 0) s_ngt = cg;
+    }
+    __syncthreads();
+    const int need = kc - s_ngt;                    // >= 1 keys equal to tau are kept
+    int rank[MAXE];
+#pragma unroll
+    for (int x = 0; x < MAXE; ++x) {
+      const uint32_t k = skey[x * kTopkThreads + tid];
+      const int bq_eq = beq[x * kTopkWaves + w], bq_gt = bgt[x * kTopkWaves + w];
+      const unsigned long long eqm = __ballot(k == tau);
+      const bool take = (k > tau) || (k == tau && bq_eq + lanes_below(eqm) < need);
+      const unsigned long long tm = __ballot(take);
+      rank[x] = take ? bq_gt + min(need, bq_eq) + lanes_below(tm) : -1;
+    }
+    __syncthreads();                                // skey is reused for the kept list
+    int32_t* sel = reinterpret_cast<int32_t*>(skey);
+    constexpr int PB = MAXE < 8 ? MAXE : 8;         // start lookups issued per batch
+#pragma unroll
+    for (int x0 = 0; x0 < MAXE; x0 += PB) {
+      int pos[PB];
+#pragma unroll
+      for (int u = 0; u < PB; ++u)                  // unconditional, so the loads batch
+        pos[u] = chunk_start(a, stage, r, min((x0 + u) * kTopkThreads + tid, nc - 1));
+#pragma unroll
+      for (int u = 0; u < PB; ++u) {
+        if (rank[x0 + u] >= 0) {
+          out[rank[x0 + u]] = pos[u];
+          sel[rank[x0 + u]] = pos[u];
+        }
+      }
+    }
+    n_sel = kc;
+  }
+  if (tid == 0) a.cnt[r * kMaxStages + stage] = n_sel;
+  if (stage != a.n_stages - 1) return;
+
+  // final stage: write the index row from the kept starts in LDS
+  __syncthreads();
+  const int32_t* sel = reinterpret_cast<const int32_t*>(skey);
+  int32_t* row = a.idx + static_cast<size_t>(r) * a.L;
+  const int n_pr = n_sel * l;
+  const int n_win = max(0, geo.e - geo.mid_hi);
+  for (int i = tid; i < a.L; i += kTopkThreads) {
+    int v;
+    if (i < geo.sink_hi) {
+      v = i;
+    } else if (i < geo.sink_hi + n_pr) {
+      const int k = i - geo.sink_hi;
+      const int c = k >> a.lchunk[stage];
+      v = sel[c] + (k & (l - 1));
+    } else if (i < geo.sink_hi + n_pr + n_win) {
+      v = geo.mid_hi + (i - geo.sink_hi - n_pr);
+    } else {
+      v = -1;
+    }
+    row[i] = v;
+  }
+}
+
+template <int MAXE>
+__global__ void __launch_bounds__(kTopkThreads) k_topk(PruneArgs a, int stage) {
+  const int r = blockIdx.x;
+  int b, s, e;
+  row_bounds(a.kv, r, b, s, e);
+  const Geo geo = make_geo(s, e, a.n_sink, a.n_window, a.chunk[0]);
+  topk_row<MAXE>(a, stage, r, geo, stage_input_chunks(a, stage, r, geo));
 }
 
 // ------------------------------------------------------------------------- //
@@ -42,9 +234,14 @@ __device__ __forceinline__ int chunk_start(const PruneArgs& a, int stage, int r,
 // and runs the G SelectRep tournaments of that kv head's query heads side by
 // side, so each step issues G independent 16-lane row loads (256 B per row at
 // bf16 d=128, fully coalesced). The first split's two representatives are
-// shared by all heads. Group results are max-reduced per chunk in LDS.
-template <typename T, int D, int G>
-__global__ void __launch_bounds__(256) k_score_decode(PruneArgs a, int stage) {
+// shared by all heads. With SPEC, the 8 keys that can represent the first
+// three splits (positions i*l/8) are loaded in one round and the first three
+// splits are decided from them, trading up to 1/8 more row reads for two
+// fewer dependent load rounds. Group results are max-reduced per chunk in
+// LDS.
+template <typename T, int D, int G, bool SPEC>
+__global__ void __launch_bounds__(256, G > 4 ? 2 : ((SPEC || sizeof(T) == 4) ? 4 : 8))
+k_score_decode(PruneArgs a, int stage) {
   constexpr int EPL = D / 16;
   const KvLayout& kv = a.kv;
   const int r = blockIdx.y;
@@ -53,7 +250,7 @@ __global__ void __launch_bounds__(256) k_score_decode(PruneArgs a, int stage) {
   const Geo geo = make_geo(s, e, a.n_sink, a.n_window, a.chunk[0]);
   const int nc = stage_input_chunks(a, stage, r, geo);
   const int l = a.chunk[stage];
-  if (nc <= a.keep[stage] / l) return;          // stage keeps everything for this row
+  if (nc <= (a.keep[stage] >> a.lchunk[stage])) return;   // stage keeps everything for this row
   const int cpw = 16 / kv.Hkv;                  // chunks per workgroup
   const int j0 = blockIdx.x * cpw;
   if (j0 >= nc) return;
@@ -62,7 +259,7 @@ __global__ void __launch_bounds__(256) k_score_decode(PruneArgs a, int stage) {
   const int gi = tid >> 4, li = tid & 15;
   const int cl = gi / kv.Hkv, g = gi - cl * kv.Hkv;
   const int j = j0 + cl;
-  const bool active = (cl < cpw) && (j < nc);
+  const bool active = j < nc;
   __shared__ float red[16];
 
   float best = -INFINITY;
@@ -70,68 +267,102 @@ __global__ void __launch_bounds__(256) k_score_decode(PruneArgs a, int stage) {
     const T* K = static_cast<const T*>(a.k);
     const T* Q = static_cast<const T*>(a.q);
     const int st = chunk_start(a, stage, r, j);
-    float q[G][EPL];
+    using Row = RowSlice<T, EPL>;
+    Row q[G];
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh)
-      SliceLoad<T, EPL>::run(Q + (static_cast<size_t>(b) * kv.Hq + g * G + hh) * D + li * EPL, q[hh]);
+    for (int hh = 0; hh < G; ++hh) q[hh].load(Q + (static_cast<size_t>(b) * kv.Hq + g * G + hh) * D + li * EPL);
+    auto dot = [&](const Row& kr, int hh) { return group16_sum(kr.dot(q[hh])); };
+    auto row_at = [&](int pos) {
+      Row x;
+      x.load(K + kv_offset(kv, b, g, pos) + li * EPL);
+      return x;
+    };
 
     float sa[G];
     int lo[G], hi[G];
     unsigned long long nvis = 0;
-    float k0[EPL];
-    SliceLoad<T, EPL>::run(static_cast<const T*>(K) + kv_offset(kv, b, g, st) + li * EPL, k0);
+    int width;                                   // size of every head's remaining range
     if (l == 1) {
+      const Row k0 = row_at(st);
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) { sa[hh] = dot(k0, hh); lo[hh] = hi[hh] = 0; }
+      nvis = 1;
+      width = 1;
+    } else if (SPEC && l >= 8) {
+      const int u = l >> 3;
+      float sc8[G][8];
+      {
+        Row kr[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) kr[i] = row_at(st + i * u);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) sc8[hh][i] = dot(kr[i], hh);
+      }
+      int a1[G], a2[G];
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
-        float acc = 0.f;
-#pragma unroll
-        for (int x = 0; x < EPL; ++x) acc = fmaf(q[hh][x], k0[x], acc);
-        sa[hh] = group16_sum(acc);
+        int A = 0;
+        float s0 = sc8[hh][0];
+        if (sc8[hh][4] > s0) { A = 4; s0 = sc8[hh][4]; }
+        a1[hh] = A;
+        const float s2 = A ? sc8[hh][6] : sc8[hh][2];
+        if (s2 > s0) { A += 2; s0 = s2; }
+        a2[hh] = A;
+        const float s3 = A == 0 ? sc8[hh][1] : A == 2 ? sc8[hh][3] : A == 4 ? sc8[hh][5] : sc8[hh][7];
+        if (s3 > s0) { A += 1; s0 = s3; }
+        lo[hh] = A * u;
+        hi[hh] = A * u + u - 1;
+        sa[hh] = s0;
       }
-      nvis = 1;
+      if (a.visited) {
+        nvis = 2;                                 // split 1: keys 0 and l/2
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {          // splits 2 and 3: distinct midpoints
+          bool f2 = true, f3 = true;
+#pragma unroll
+          for (int h2 = 0; h2 < hh; ++h2) {
+            f2 = f2 && (a1[h2] != a1[hh]);
+            f3 = f3 && (a2[h2] != a2[hh]);
+          }
+          nvis += (f2 ? 1 : 0) + (f3 ? 1 : 0);
+        }
+      }
+      width = u;
     } else {
       const int mid0 = l >> 1;
-      float k1[EPL];
-      SliceLoad<T, EPL>::run(K + kv_offset(kv, b, g, st + mid0) + li * EPL, k1);
+      const Row k0 = row_at(st), k1 = row_at(st + mid0);
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
-        float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-        for (int x = 0; x < EPL; ++x) {
-          a0 = fmaf(q[hh][x], k0[x], a0);
-          a1 = fmaf(q[hh][x], k1[x], a1);
-        }
-        a0 = group16_sum(a0);
-        a1 = group16_sum(a1);
+        const float a0 = dot(k0, hh), a1 = dot(k1, hh);
         if (a1 > a0) { lo[hh] = mid0; hi[hh] = l - 1; sa[hh] = a1; }
         else         { lo[hh] = 0;    hi[hh] = mid0 - 1; sa[hh] = a0; }
       }
       nvis = 2;
-      for (int w = l >> 2; w >= 1; w >>= 1) {   // remaining log2(l) - 1 splits
-        float kk[G][EPL];
-        int mid[G];
+      width = mid0;
+    }
+    for (int wdt = width >> 1; wdt >= 1; wdt >>= 1) {   // remaining splits
+      Row kk[G];
+      int mid[G];
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        mid[hh] = (lo[hh] + hi[hh] + 1) >> 1;
+        kk[hh] = row_at(st + mid[hh]);
+      }
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const float acc = dot(kk[hh], hh);
+        if (acc > sa[hh]) { lo[hh] = mid[hh]; sa[hh] = acc; }
+        else              { hi[hh] = mid[hh] - 1; }
+      }
+      if (a.visited) {
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
-          mid[hh] = (lo[hh] + hi[hh] + 1) >> 1;
-          SliceLoad<T, EPL>::run(K + kv_offset(kv, b, g, st + mid[hh]) + li * EPL, kk[hh]);
-        }
+          bool fresh = true;
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-          float acc = 0.f;
-#pragma unroll
-          for (int x = 0; x < EPL; ++x) acc = fmaf(q[hh][x], kk[hh][x], acc);
-          acc = group16_sum(acc);
-          if (acc > sa[hh]) { lo[hh] = mid[hh]; sa[hh] = acc; }
-          else              { hi[hh] = mid[hh] - 1; }
-        }
-        if (a.visited) {
-#pragma unroll
-          for (int hh = 0; hh < G; ++hh) {
-            bool fresh = true;
-#pragma unroll
-            for (int h2 = 0; h2 < hh; ++h2) fresh = fresh && (mid[h2] != mid[hh]);
-            nvis += fresh ? 1 : 0;
-          }
+          for (int h2 = 0; h2 < hh; ++h2) fresh = fresh && (mid[h2] != mid[hh]);
+          nvis += fresh ? 1 : 0;
         }
       }
     }
@@ -168,7 +399,7 @@ __global__ void __launch_bounds__(256) k_score_prefill(PruneArgs a, int stage) {
   const Geo geo = make_geo(s, e, a.n_sink, a.n_window, a.chunk[0]);
   const int nc = stage_input_chunks(a, stage, r, geo);
   const int l = a.chunk[stage];
-  if (nc <= a.keep[stage] / l) return;
+  if (nc <= (a.keep[stage] >> a.lchunk[stage])) return;
   const int j0 = blockIdx.x * 16;
   if (j0 >= nc) return;
 
@@ -230,236 +461,62 @@ __global__ void __launch_bounds__(256) k_score_prefill(PruneArgs a, int stage) {
 }
 
 // ------------------------------------------------------------------------- //
-// top-K per row + index assembly                                            //
-// ------------------------------------------------------------------------- //
-template <int NT>
-__device__ __forceinline__ int block_sum(int v, int* sh) {
-  v = wave_sum_int(v);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  if (lane == 0) sh[w] = v;
-  __syncthreads();
-  int t = 0;
-#pragma unroll
-  for (int i = 0; i < NT / 64; ++i) t += sh[i];
-  __syncthreads();
-  return t;
-}
-
-template <int NT>
-__device__ __forceinline__ uint32_t block_and(uint32_t v, uint32_t* sh) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v &= static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), o, 64));
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  if (lane == 0) sh[w] = v;
-  __syncthreads();
-  uint32_t t = 0xffffffffu;
-#pragma unroll
-  for (int i = 0; i < NT / 64; ++i) t &= sh[i];
-  __syncthreads();
-  return t;
-}
-
-template <int NT>
-__device__ __forceinline__ uint32_t block_or(uint32_t v, uint32_t* sh) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), o, 64));
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  if (lane == 0) sh[w] = v;
-  __syncthreads();
-  uint32_t t = 0u;
-#pragma unroll
-  for (int i = 0; i < NT / 64; ++i) t |= sh[i];
-  __syncthreads();
-  return t;
-}
-
-// Exclusive prefix sum over threads in thread order; `total` gets the sum.
-template <int NT>
-__device__ __forceinline__ int block_excl_scan(int v, int* sh, int& total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) sh[w] = x;
-  __syncthreads();
-  int base = 0;
-  total = 0;
-#pragma unroll
-  for (int i = 0; i < NT / 64; ++i) {
-    const int t = sh[i];
-    base += (i < w) ? t : 0;
-    total += t;
-  }
-  __syncthreads();
-  return base + x - v;
-}
-
-constexpr int kSelCap = 8192;   // longest kept-chunk list held in LDS
-
-// One workgroup per row. Keys live in registers: thread t owns the contiguous
-// segment [t*E, t*E + E) so thread order is chunk-index order.
-// The K-th largest key tau is found by a most-significant-first bit search
-// restricted to the bits that vary across the row's keys; then every key >
-// tau is kept plus the lowest-index keys == tau until K are kept.
-template <int NT, int MAXE>
-__global__ void __launch_bounds__(NT) k_topk(PruneArgs a, int stage) {
-  const KvLayout& kv = a.kv;
-  const int r = blockIdx.x;
-  int b, s, e;
-  row_bounds(kv, r, b, s, e);
-  const Geo geo = make_geo(s, e, a.n_sink, a.n_window, a.chunk[0]);
-  const int nc = stage_input_chunks(a, stage, r, geo);
-  const int l = a.chunk[stage];
-  const int kc = a.keep[stage] / l;
-  const int tid = threadIdx.x;
-  __shared__ int sh[NT / 64];
-  __shared__ uint32_t shu[NT / 64];
-  __shared__ int sel[kSelCap];
-  int32_t* out = a.starts + static_cast<size_t>(stage & 1) * a.R * a.maxK + static_cast<size_t>(r) * a.maxK;
-  int n_sel;
-  if (nc <= kc) {
-    for (int j = tid; j < nc; j += NT) {
-      const int p = chunk_start(a, stage, r, j);
-      out[j] = p;
-      sel[j] = p;
-    }
-    n_sel = nc;
-  } else {
-    const int E = (nc + NT - 1) / NT;
-    const int base = tid * E;
-    uint32_t key[MAXE];
-    uint32_t vand = 0xffffffffu, vor = 0u;
-    const uint32_t* sc = a.scores + static_cast<size_t>(r) * a.maxNC;
-#pragma unroll
-    for (int x = 0; x < MAXE; ++x) {
-      const int j = base + x;
-      const bool ok = (x < E) && (j < nc);
-      key[x] = ok ? sc[j] : 0u;
-      if (ok) { vand &= key[x]; vor |= key[x]; }
-    }
-    vand = block_and<NT>(vand, shu);
-    vor = block_or<NT>(vor, shu);
-    const uint32_t varying = vand ^ vor;
-    uint32_t tau = vand;
-    for (int bit = 31; bit >= 0; --bit) {
-      if (!((varying >> bit) & 1u)) continue;
-      const uint32_t c = tau | (1u << bit);
-      int n = 0;
-#pragma unroll
-      for (int x = 0; x < MAXE; ++x) n += (key[x] >= c) ? 1 : 0;
-      if (block_sum<NT>(n, sh) >= kc) tau = c;
-    }
-    int ngt = 0, neq = 0;
-#pragma unroll
-    for (int x = 0; x < MAXE; ++x) {
-      ngt += (key[x] > tau) ? 1 : 0;
-      neq += (key[x] == tau) ? 1 : 0;
-    }
-    const int need = kc - block_sum<NT>(ngt, sh);
-    int tot;
-    int eq_before = block_excl_scan<NT>(neq, sh, tot);
-    bool take[MAXE];
-    int nt = 0;
-#pragma unroll
-    for (int x = 0; x < MAXE; ++x) {
-      bool t = key[x] > tau;
-      if (key[x] == tau) {
-        t = eq_before < need;
-        ++eq_before;
-      }
-      take[x] = t;
-      nt += t ? 1 : 0;
-    }
-    int rank = block_excl_scan<NT>(nt, sh, tot);
-#pragma unroll
-    for (int x = 0; x < MAXE; ++x) {
-      if (take[x]) {
-        const int p = chunk_start(a, stage, r, base + x);
-        out[rank] = p;
-        sel[rank] = p;
-        ++rank;
-      }
-    }
-    n_sel = kc;
-  }
-  if (tid == 0) a.cnt[r * kMaxStages + stage] = n_sel;
-  if (stage != a.n_stages - 1) return;
-
-  // final stage: write the index row
-  __syncthreads();
-  int32_t* row = a.idx + static_cast<size_t>(r) * a.L;
-  const int n_pr = n_sel * l;
-  const int n_win = max(0, e - geo.mid_hi);
-  for (int i = tid; i < a.L; i += NT) {
-    int v;
-    if (i < geo.sink_hi) {
-      v = i;
-    } else if (i < geo.sink_hi + n_pr) {
-      const int k = i - geo.sink_hi;
-      v = sel[k / l] + (k % l);
-    } else if (i < geo.sink_hi + n_pr + n_win) {
-      v = geo.mid_hi + (i - geo.sink_hi - n_pr);
-    } else {
-      v = -1;
-    }
-    row[i] = v;
-  }
-}
-
-// ------------------------------------------------------------------------- //
 // launcher                                                                  //
 // ------------------------------------------------------------------------- //
 static const char* const kScoreNames[kMaxStages] = {"prune_score_stage1", "prune_score_stage2",
                                                     "prune_score_stage3", "prune_score_stage4"};
 static const char* const kTopkNames[kMaxStages] = {"prune_topk_stage1", "prune_topk_stage2",
                                                    "prune_topk_stage3", "prune_topk_stage4"};
+constexpr int kSpecMaxChunk = 64;       // chunks this small preload their first three splits
 
 template <typename T, int D, int G>
 static void launch_decode_score(const PruneArgs& a, int stage, int max_chunks, hipStream_t st) {
   const int cpw = 16 / a.kv.Hkv;
+  if (max_chunks <= 0) return;
   dim3 grid((max_chunks + cpw - 1) / cpw, a.R);
-  DSA_LAUNCH(kScoreNames[stage], (k_score_decode<T, D, G>), grid, dim3(256), st, a, stage);
+  const char* nm = kScoreNames[stage];
+  if (a.chunk[stage] >= 8 && a.chunk[stage] <= kSpecMaxChunk)
+    DSA_LAUNCH(nm, (k_score_decode<T, D, G, true>), grid, dim3(256), st, a, stage);
+  else
+    DSA_LAUNCH(nm, (k_score_decode<T, D, G, false>), grid, dim3(256), st, a, stage);
+}
+
+static void launch_topk(const PruneArgs& a, int stage, int max_chunks, hipStream_t st) {
+  const char* nm = kTopkNames[stage];
+  if (max_chunks <= kTopkThreads * 4) {
+    DSA_LAUNCH(nm, (k_topk<4>), dim3(a.R), dim3(kTopkThreads), st, a, stage);
+  } else if (max_chunks <= kTopkThreads * 16) {
+    DSA_LAUNCH(nm, (k_topk<16>), dim3(a.R), dim3(kTopkThreads), st, a, stage);
+  } else if (max_chunks <= kTopkThreads * 64) {
+    DSA_LAUNCH(nm, (k_topk<64>), dim3(a.R), dim3(kTopkThreads), st, a, stage);
+  } else {
+    DSA_LAUNCH(nm, (k_topk<kTopkMaxE>), dim3(a.R), dim3(kTopkThreads), st, a, stage);
+  }
 }
 
 template <typename T, int D>
 static hipError_t launch_typed(const PruneArgs& a, hipStream_t st) {
   const int G = a.kv.Hq / a.kv.Hkv;
   for (int stage = 0; stage < a.n_stages; ++stage) {
-    // largest input list any row can present to this stage
-    int max_chunks;
-    if (stage == 0) {
-      max_chunks = a.n1max;
+    // longest input list any row can present to this stage
+    const int max_chunks = stage == 0 ? a.n1max : a.keep[stage - 1] / a.chunk[stage];
+    if (a.kv.decode) {
+      switch (G) {
+        case 1: launch_decode_score<T, D, 1>(a, stage, max_chunks, st); break;
+        case 2: launch_decode_score<T, D, 2>(a, stage, max_chunks, st); break;
+        case 4: launch_decode_score<T, D, 4>(a, stage, max_chunks, st); break;
+        case 8: launch_decode_score<T, D, 8>(a, stage, max_chunks, st); break;
+        default: return hipErrorInvalidValue;
+      }
+      launch_topk(a, stage, max_chunks, st);
     } else {
-      max_chunks = a.keep[stage - 1] / a.chunk[stage];
-    }
-    if (max_chunks > 0) {
-      if (a.kv.decode) {
-        switch (G) {
-          case 1: launch_decode_score<T, D, 1>(a, stage, max_chunks, st); break;
-          case 2: launch_decode_score<T, D, 2>(a, stage, max_chunks, st); break;
-          case 4: launch_decode_score<T, D, 4>(a, stage, max_chunks, st); break;
-          case 8: launch_decode_score<T, D, 8>(a, stage, max_chunks, st); break;
-          default: return hipErrorInvalidValue;
-        }
-      } else {
+      if (max_chunks > 0) {
         dim3 grid((max_chunks + 15) / 16, a.R);
         DSA_LAUNCH(kScoreNames[stage], (k_score_prefill<T, D>), grid, dim3(256), st, a, stage);
       }
+      launch_topk(a, stage, max_chunks, st);
     }
     hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    const int cap = a.maxNC;
-    if (cap <= 1024 * 4) {
-      DSA_LAUNCH(kTopkNames[stage], (k_topk<1024, 4>), dim3(a.R), dim3(1024), st, a, stage);
-    } else if (cap <= 1024 * 16) {
-      DSA_LAUNCH(kTopkNames[stage], (k_topk<1024, 16>), dim3(a.R), dim3(1024), st, a, stage);
-    } else {
-      DSA_LAUNCH(kTopkNames[stage], (k_topk<1024, 64>), dim3(a.R), dim3(1024), st, a, stage);
-    }
-    err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
