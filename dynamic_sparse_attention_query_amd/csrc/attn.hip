@@ -331,6 +331,7 @@ static hipError_t launch_attn_typed(const AttnArgs& a, hipStream_t st) {
       default: return hipErrorInvalidValue;
     }
   } else {
+    if (sizeof(T) == 2 && launch_prefill_mfma(a, st)) return hipGetLastError();
     dim3 grid(a.kv.nblk, a.kv.Hq, a.kv.B);
     DSA_LAUNCH(a.idx ? "attn_prefill" : "dense_prefill", (k_prefill_generic<T, D>), grid, dim3(256), st, a);
   }

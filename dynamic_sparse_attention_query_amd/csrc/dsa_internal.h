@@ -2,6 +2,7 @@
 // blocks passed by value to kernels, device helpers, and host launchers.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -223,14 +224,21 @@ __device__ __forceinline__ int wave_sum_int(int v) {
 // ------------------------------------------------------------------------- //
 // launch with optional per-kernel timing (profile.hip)                      //
 // ------------------------------------------------------------------------- //
-void* prof_begin(const char* name, hipStream_t st);
-void prof_end(void* token, hipStream_t st);
+// While profiling is on, prof_slot() hands out a start/stop event pair that the
+// launch records at the kernel's own start and end (hipExtLaunchKernelGGL).
+struct ProfSlot {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+ProfSlot prof_slot(const char* name);
 
-#define DSA_LAUNCH(NAME, KERNEL, GRID, BLOCK, STREAM, ...)                 \
-  do {                                                                     \
-    void* dsa_tok_ = ::dsa::prof_begin(NAME, STREAM);                      \
-    hipLaunchKernelGGL(KERNEL, GRID, BLOCK, 0, STREAM, __VA_ARGS__);       \
-    ::dsa::prof_end(dsa_tok_, STREAM);                                     \
+#define DSA_LAUNCH(NAME, KERNEL, GRID, BLOCK, STREAM, ...)                                  \
+  do {                                                                                      \
+    const ::dsa::ProfSlot dsa_ps_ = ::dsa::prof_slot(NAME);                                 \
+    if (dsa_ps_.start)                                                                      \
+      hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, 0, STREAM, dsa_ps_.start, dsa_ps_.stop, 0, \
+                            __VA_ARGS__);                                                   \
+    else                                                                                    \
+      hipLaunchKernelGGL(KERNEL, GRID, BLOCK, 0, STREAM, __VA_ARGS__);                      \
   } while (0)
 
 // ------------------------------------------------------------------------- //
@@ -238,5 +246,6 @@ void prof_end(void* token, hipStream_t st);
 // ------------------------------------------------------------------------- //
 hipError_t launch_prune(const PruneArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_sparse_attn(const AttnArgs& a, int dtype, hipStream_t stream);
+bool launch_prefill_mfma(const AttnArgs& a, hipStream_t stream);   // bf16, b_q = 64
 
 }  // namespace dsa

@@ -1,8 +1,7 @@
-// Optional per-kernel timing: while enabled, every library launch is
-// bracketed by a pair of HIP events recorded on the launch's stream; reading
-// the profile synchronises those events and aggregates per kernel name. This
-// is a diagnostic (it adds event records between launches) and must not be
-// enabled inside graph capture.
+// Optional per-kernel timing: while enabled, every library launch records a
+// pair of HIP events at the kernel's own start and end (hipExtLaunchKernelGGL);
+// reading the profile synchronises those events and aggregates per kernel
+// name. This is a diagnostic and must not be enabled inside graph capture.
 #include <atomic>
 #include <cstring>
 #include <mutex>
@@ -38,22 +37,17 @@ hipEvent_t take_event() {
 
 }  // namespace
 
-void* prof_begin(const char* name, hipStream_t st) {
-  if (!g_on.load(std::memory_order_relaxed)) return nullptr;
+ProfSlot prof_slot(const char* name) {
+  ProfSlot ps;
+  if (!g_on.load(std::memory_order_relaxed)) return ps;
   std::lock_guard<std::mutex> lk(g_mu);
-  if (!g_on) return nullptr;
+  if (!g_on) return ps;
   Rec r{name, take_event(), take_event()};
-  if (!r.start || !r.stop) return nullptr;
-  hipEventRecord(r.start, st);
+  if (!r.start || !r.stop) return ps;
   g_recs.push_back(r);
-  return reinterpret_cast<void*>(g_recs.size());
-}
-
-void prof_end(void* token, hipStream_t st) {
-  if (!token) return;
-  std::lock_guard<std::mutex> lk(g_mu);
-  const size_t i = reinterpret_cast<size_t>(token) - 1;
-  if (i < g_recs.size()) hipEventRecord(g_recs[i].stop, st);
+  ps.start = r.start;
+  ps.stop = r.stop;
+  return ps;
 }
 
 }  // namespace dsa

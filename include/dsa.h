@@ -156,8 +156,8 @@ dsa_status dsa_dense_attn(const dsa_shape* shape, const void* q, const void* k, 
 
 /* Per-kernel timing, a diagnostic for latency breakdowns. Between
  * dsa_profile_begin() and dsa_profile_end(), every kernel the library launches
- * is bracketed by HIP events recorded on its stream (do not profile inside
- * graph capture). dsa_profile_end() waits for those events, stops recording
+ * records a pair of HIP events at its own start and end on its stream (do not
+ * profile inside graph capture). dsa_profile_end() waits for those events, stops recording
  * and writes up to `capacity` aggregates (kernel name, launches, total
  * milliseconds) to `out` (host memory); *n_out receives the number of kernels
  * seen. */
