@@ -247,5 +247,8 @@ ProfSlot prof_slot(const char* name);
 hipError_t launch_prune(const PruneArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_sparse_attn(const AttnArgs& a, int dtype, hipStream_t stream);
 bool launch_prefill_mfma(const AttnArgs& a, hipStream_t stream);   // bf16, b_q = 64
+struct PruneArgs;
+bool launch_score_prefill_mfma(const PruneArgs& a, int stage, int max_chunks, hipStream_t stream,
+                               const char* name);                  // bf16, b_q = 64
 
 }  // namespace dsa

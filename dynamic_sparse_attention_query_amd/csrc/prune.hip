@@ -15,28 +15,9 @@
 // own kernel, one workgroup per row.
 // Every chunk of every stage is a contiguous run of positions: stage 1 tiles
 // [n_sink, mid_hi) and each later chunk size divides the previous one.
-#include "dsa_internal.h"
+#include "prune_common.h"
 
 namespace dsa {
-
-// ------------------------------------------------------------------------- //
-// shared stage helpers                                                      //
-// ------------------------------------------------------------------------- //
-__device__ __forceinline__ int stage_input_chunks(const PruneArgs& a, int stage, int r,
-                                                  const Geo& geo) {
-  if (stage == 0) return geo.n1;
-  return a.cnt[r * kMaxStages + stage - 1] << (a.lchunk[stage - 1] - a.lchunk[stage]);
-}
-
-// First key position of chunk j of stage `stage` in row r (chunk sizes are
-// powers of two, so the parent chunk and the offset inside it are shifts).
-__device__ __forceinline__ int chunk_start(const PruneArgs& a, int stage, int r, int j) {
-  if (stage == 0) return a.n_sink + (j << a.lchunk[0]);
-  const int sh = a.lchunk[stage - 1] - a.lchunk[stage];
-  const int32_t* prev =
-      a.starts + static_cast<size_t>((stage - 1) & 1) * a.R * a.maxK + static_cast<size_t>(r) * a.maxK;
-  return prev[j >> sh] + ((j & ((1 << sh) - 1)) << a.lchunk[stage]);
-}
 
 // ------------------------------------------------------------------------- //
 // top-K of one row + index assembly                                         //
@@ -510,7 +491,8 @@ static hipError_t launch_typed(const PruneArgs& a, hipStream_t st) {
       }
       launch_topk(a, stage, max_chunks, st);
     } else {
-      if (max_chunks > 0) {
+      if (max_chunks > 0 &&
+          !(sizeof(T) == 2 && launch_score_prefill_mfma(a, stage, max_chunks, st, kScoreNames[stage]))) {
         dim3 grid((max_chunks + 15) / 16, a.R);
         DSA_LAUNCH(kScoreNames[stage], (k_score_prefill<T, D>), grid, dim3(256), st, a, stage);
       }
