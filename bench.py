@@ -37,6 +37,27 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None if there is none or the kernel source changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "decode_1m_counters.md")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        line = line.strip()
+        for key in ("traffic_kernel", "traffic_bytes_per_launch", "source_sha256", "source_files"):
+            if line.startswith(key + ":"):
+                kv[key] = line.split(":", 1)[1].strip()
+    if kv.get("traffic_kernel") != kernel or "source_files" not in kv:
+        return None
+    h = hashlib.sha256(b"".join(open(os.path.join(ROOT, f), "rb").read() for f in kv["source_files"].split()))
+    if h.hexdigest() != kv.get("source_sha256"):
+        return None
+    return int(kv["traffic_bytes_per_launch"])
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -49,7 +70,98 @@ def parse():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-ref", action="store_true",
+                    help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
+
+
+# --------------------------------------------------------------------------- #
+# per-kernel durations in graph mode                                          #
+# --------------------------------------------------------------------------- #
+class _Dim3(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_uint32), ("y", ctypes.c_uint32), ("z", ctypes.c_uint32)]
+
+
+class _KernelNodeParams(ctypes.Structure):
+    _fields_ = [("blockDim", _Dim3), ("extra", ctypes.c_void_p), ("func", ctypes.c_void_p),
+                ("gridDim", _Dim3), ("kernelParams", ctypes.c_void_p), ("sharedMemBytes", ctypes.c_uint32)]
+
+
+def graph_kernel_times(launches, repeat=16, reps=4):
+    """Average duration (us) of each kernel of one step, in launch order.
+
+    Eager launches on this GPU pay a large per-launch release between dependent
+    kernels, so kernels are timed in graph mode instead: each callable in
+    `launches` (the same step on different KV replicas) is captured into a HIP
+    graph; for each kernel position a graph chaining `repeat` copies of that
+    kernel node, cycling through the captures so consecutive copies read
+    different replicas (no cache reuse), is replayed `reps` times between HIP
+    events on the launch stream. Every library kernel is idempotent given the
+    step's final state, so re-running a node reproduces its real work."""
+    import torch
+    hip = ctypes.CDLL("libamdhip64.so")
+    vp = ctypes.c_void_p
+
+    def ck(err, what):
+        if err != 0:
+            raise RuntimeError(f"{what} failed with HIP error {err}")
+
+    stream = torch.cuda.Stream()
+    graphs, chains = [], []
+    for launch in launches:
+        graph = vp()
+        with torch.cuda.stream(stream):
+            torch.cuda.synchronize()
+            ck(hip.hipStreamBeginCapture(vp(stream.cuda_stream), 0), "hipStreamBeginCapture")
+            launch()
+            ck(hip.hipStreamEndCapture(vp(stream.cuda_stream), ctypes.byref(graph)), "hipStreamEndCapture")
+        graphs.append(graph)
+        # walk the captured chain from its root
+        nodes = []
+        n = ctypes.c_size_t(1)
+        root = vp()
+        ck(hip.hipGraphGetRootNodes(graph, ctypes.byref(root), ctypes.byref(n)), "hipGraphGetRootNodes")
+        node = root if n.value == 1 else None
+        while node is not None and node.value:
+            ty = ctypes.c_int(-1)
+            ck(hip.hipGraphNodeGetType(node, ctypes.byref(ty)), "hipGraphNodeGetType")
+            if ty.value == 0:
+                prm = _KernelNodeParams()
+                ck(hip.hipGraphKernelNodeGetParams(node, ctypes.byref(prm)), "hipGraphKernelNodeGetParams")
+                nodes.append(prm)
+            nd = ctypes.c_size_t(1)
+            nxt = vp()
+            ck(hip.hipGraphNodeGetDependentNodes(node, ctypes.byref(nxt), ctypes.byref(nd)),
+               "hipGraphNodeGetDependentNodes")
+            node = nxt if nd.value == 1 else None
+        chains.append(nodes)
+    times = []
+    for k in range(len(chains[0])):
+        g2 = vp()
+        ck(hip.hipGraphCreate(ctypes.byref(g2), ctypes.c_uint(0)), "hipGraphCreate")
+        prev = vp()
+        for i in range(repeat):
+            prm = chains[i % len(chains)][k]
+            cur = vp()
+            deps = ctypes.byref(prev) if i else None
+            ck(hip.hipGraphAddKernelNode(ctypes.byref(cur), g2, deps, ctypes.c_size_t(1 if i else 0),
+                                         ctypes.byref(prm)), "hipGraphAddKernelNode")
+            prev = cur
+        ex = vp()
+        ck(hip.hipGraphInstantiate(ctypes.byref(ex), g2, None, None, ctypes.c_size_t(0)), "hipGraphInstantiate")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ck(hip.hipGraphLaunch(ex, vp(stream.cuda_stream)), "hipGraphLaunch")     # warm
+        e0.record(stream)
+        for _ in range(reps):
+            ck(hip.hipGraphLaunch(ex, vp(stream.cuda_stream)), "hipGraphLaunch")
+        e1.record(stream)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3 / (reps * repeat))
+        hip.hipGraphExecDestroy(ex)
+        hip.hipGraphDestroy(g2)
+    for g in graphs:
+        hip.hipGraphDestroy(g)
+    return times
 
 
 # --------------------------------------------------------------------------- #
@@ -141,12 +253,16 @@ def decode_bench(args, res):
     us_step = wall_ms * 1e3 / K
     log(f"decode 1M: {us_step:.1f} us/step wall, {ev_ms * 1e3 / K:.1f} us/step events")
 
-    # per-kernel durations from HIP events on the launch stream (eager pass)
+    # per-kernel durations: HIP events around graph replays of each kernel of a
+    # captured step (kernel names from the library's own launch record)
     _lib.profile_begin()
-    for i in range(W, W + K):
-        launch(i)
+    launch(W)
     prof = _lib.profile_end()
-    kern_us = {k: v[1] * 1e3 / v[0] for k, v in prof.items()}
+    names = list(prof.keys())
+    gt = graph_kernel_times([lambda i=i: launch(i) for i in range(W, W + args.replicas)])
+    if len(gt) != len(names):
+        raise RuntimeError(f"captured {len(gt)} kernels, expected {len(names)}")
+    kern_us = dict(zip(names, gt))
     per_launch_bytes = {
         "prune_score_stage1": float(stage_bytes[used, 0].mean()),
         "prune_score_stage2": float(stage_bytes[used, 1].mean()),
@@ -157,8 +273,9 @@ def decode_bench(args, res):
     roof = None
     if dom in per_launch_bytes:
         ach = per_launch_bytes[dom] / (kern_us[dom] * 1e-6) / 1e9
+        tr = measured_traffic(dom)
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS,
-                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": tr,
                 "avg_us": round(kern_us[dom], 2), "algorithmic_bytes_per_launch": int(per_launch_bytes[dom])}
     res["decode"] = dict(us_per_step=us_step, event_us_per_step=ev_ms * 1e3 / K, wall_ms=wall_ms,
                          bytes_per_step=bytes_avg, stage_rows=(stage_bytes[used].mean(0) / row_bytes).tolist(),
@@ -297,6 +414,13 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
     res = {}
+    if args.copy_ref:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     case = decode_bench(args, res)
     if not args.no_prefill:
         prefill_bench(args, res)

@@ -31,7 +31,9 @@ hipEvent_t take_event() {
     return e;
   }
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  // timing-only events: no system-scope fence (a fence would write back the
+  // L2 of every XCD and inflate the measured kernel)
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 
