@@ -31,6 +31,10 @@ def build(verbose: bool = False) -> str:
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
            # packed fp32 instructions stay off on this target
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           # matrix-core accumulators in ordinary VGPRs: the softmax and
+           # max-reductions read them with vector ALU instructions, which
+           # cannot address the accumulation registers directly
+           "-mllvm", "-amdgpu-mfma-vgpr-form=1",
            "-Wno-unused-command-line-argument",
            "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
            *srcs, "-o", tmp]
