@@ -99,7 +99,7 @@ PruneLayout prune_layout(const dsa_shape* s, const dsa_params* p) {
   maxNC = std::max<long long>(maxNC, L.n1max);
   for (int i = 1; i < p->n_stages; ++i) maxNC = std::max<long long>(maxNC, p->keep[i - 1] / p->chunk[i]);
   L.maxK = maxK;
-  L.maxNC = maxNC;
+  L.maxNC = (maxNC + 63) / 64 * 64;   // rows of whole 16-byte key groups
   L.off_cnt = 0;
   L.off_starts = align256(L.off_cnt + static_cast<size_t>(L.R) * dsa::kMaxStages * 4);
   L.off_scores = align256(L.off_starts + 2 * static_cast<size_t>(L.R) * maxK * 4);

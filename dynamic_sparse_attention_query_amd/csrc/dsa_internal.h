@@ -199,26 +199,85 @@ __device__ __forceinline__ float load_one<uint16_t>(const uint16_t* p) { return 
 template <>
 __device__ __forceinline__ float load_one<float>(const float* p) { return *p; }
 
-// Sum / max over the 16 lanes of an aligned lane group (all lanes get the result).
+// ------------------------------------------------------------------------- //
+// cross-lane primitives on DPP operand routing (VALU latency, no LDS round  //
+// trip): a wave is 4 rows of 16 lanes                                       //
+// ------------------------------------------------------------------------- //
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kDppRowMirror = 0x140;    // lane i <- 15 - i within the row
+constexpr int kDppHalfMirror = 0x141;   // lane i <- 7 - i within each 8 lanes
+constexpr int kDppRowShr = 0x110;       // + n: lane i <- i - n within the row
+constexpr int kDppBcast15 = 0x142;      // lane 15 of a row -> the next row
+constexpr int kDppBcast31 = 0x143;      // lane 31 -> rows 2 and 3
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_perm(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+}
+// src routed by CTRL into the enabled rows; 0 where the row is masked off or
+// the source lane lies outside the row
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_or0(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_perm_f(float v) {
+  return __int_as_float(dpp_perm<CTRL>(__float_as_int(v)));
+}
+
+// Sum / max over the 16 lanes of a row (all lanes get the same bits: every
+// lane combines the same partial results, in commuted order at most).
 __device__ __forceinline__ float group16_sum(float v) {
-  v += __shfl_xor(v, 8, 16);
-  v += __shfl_xor(v, 4, 16);
-  v += __shfl_xor(v, 2, 16);
-  v += __shfl_xor(v, 1, 16);
+  v += dpp_perm_f<kDppXor1>(v);
+  v += dpp_perm_f<kDppXor2>(v);
+  v += dpp_perm_f<kDppHalfMirror>(v);
+  v += dpp_perm_f<kDppRowMirror>(v);
   return v;
 }
 __device__ __forceinline__ float group16_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 8, 16));
-  v = fmaxf(v, __shfl_xor(v, 4, 16));
-  v = fmaxf(v, __shfl_xor(v, 2, 16));
-  v = fmaxf(v, __shfl_xor(v, 1, 16));
+  v = fmaxf(v, dpp_perm_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_perm_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_perm_f<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_perm_f<kDppRowMirror>(v));
   return v;
 }
 
+// Whole-wave reductions: rows first, then the four row results through
+// scalar registers (the result is wave-uniform).
+template <typename Op>
+__device__ __forceinline__ int wave_reduce_int(int v, Op op) {
+  v = op(v, dpp_perm<kDppXor1>(v));
+  v = op(v, dpp_perm<kDppXor2>(v));
+  v = op(v, dpp_perm<kDppHalfMirror>(v));
+  v = op(v, dpp_perm<kDppRowMirror>(v));
+  return op(op(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+            op(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
 __device__ __forceinline__ int wave_sum_int(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  return wave_reduce_int(v, [](int x, int y) { return x + y; });
+}
+__device__ __forceinline__ float wave_max_f(float v) {
+  return __int_as_float(wave_reduce_int(__float_as_int(v), [](int x, int y) {
+    return __float_as_int(fmaxf(__int_as_float(x), __int_as_float(y)));
+  }));
+}
+__device__ __forceinline__ float wave_sum_f(float v) {
+  return __int_as_float(wave_reduce_int(__float_as_int(v), [](int x, int y) {
+    return __float_as_int(__int_as_float(x) + __int_as_float(y));
+  }));
+}
+
+// Inclusive prefix sum over the 64 lanes (lane order).
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
+  int x = static_cast<int>(v);
+  x += dpp_or0<kDppRowShr + 1, 0xF>(x);
+  x += dpp_or0<kDppRowShr + 2, 0xF>(x);
+  x += dpp_or0<kDppRowShr + 4, 0xF>(x);
+  x += dpp_or0<kDppRowShr + 8, 0xF>(x);
+  x += dpp_or0<kDppBcast15, 0xA>(x);    // rows 1, 3 += last lane of rows 0, 2
+  x += dpp_or0<kDppBcast31, 0xC>(x);    // rows 2, 3 += last lane of row 1
+  return static_cast<uint32_t>(x);
 }
 
 // ------------------------------------------------------------------------- //

@@ -24,188 +24,227 @@ namespace dsa {
 // ------------------------------------------------------------------------- //
 constexpr int kTopkThreads = 256;
 constexpr int kTopkWaves = kTopkThreads / 64;
-constexpr int kTopkMaxE = 128;          // rows of up to 32768 chunks (128 KiB of keys in LDS)
+constexpr int kTopkMaxE = 128;          // rows of up to 32768 chunks
+constexpr int kMaxKeptChunks = 8192;    // keep / chunk of any stage (validated by the API)
 
 __device__ __forceinline__ uint32_t wave_and_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v &= static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), o, 64));
-  return v;
+  return static_cast<uint32_t>(wave_reduce_int(static_cast<int>(v), [](int x, int y) { return x & y; }));
 }
 __device__ __forceinline__ uint32_t wave_or_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), o, 64));
-  return v;
-}
-// number of lanes below this one whose bit is set in `mask`
-__device__ __forceinline__ int lanes_below(unsigned long long mask) {
-  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
-                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0));
+  return static_cast<uint32_t>(wave_reduce_int(static_cast<int>(v), [](int x, int y) { return x | y; }));
 }
 
-// Run by all 256 threads of one workgroup. The row's keys are staged in LDS;
-// thread t handles keys j = x*256 + t (x < E), so for each x a wave covers 64
-// consecutive chunk indices and wave ballots give counts and in-order ranks
-// without shuffles. The K-th largest key tau is found by a
-// most-significant-first bit search over the bits that vary across the row's
-// keys (one barrier per bit); then every key > tau is kept plus the
-// lowest-index keys == tau until K are kept.
-template <int MAXE>
-__device__ void topk_row(const PruneArgs& a, int stage, int r, const Geo& geo, int nc) {
-  constexpr int NXW = MAXE * kTopkWaves;          // (x, wave) slots in index order
-  const int l = a.chunk[stage];
-  const int kc = a.keep[stage] >> a.lchunk[stage];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  __shared__ uint32_t red[2][kTopkWaves];
-  __shared__ int cnt[2][kTopkWaves];
-  __shared__ int wgt[NXW], weq[NXW];              // per-slot counts of keys > tau, == tau
-  __shared__ int bgt[NXW], beq[NXW];              // exclusive prefixes of the same
-  __shared__ int s_ngt;
-  __shared__ uint32_t skey[MAXE * kTopkThreads];
-  int32_t* out = a.starts + static_cast<size_t>(stage & 1) * a.R * a.maxK + static_cast<size_t>(r) * a.maxK;
-  int n_sel;
-  if (nc <= kc) {
-    int32_t* sel = reinterpret_cast<int32_t*>(skey);
-    for (int j = tid; j < nc; j += kTopkThreads) {
-      const int p = chunk_start(a, stage, r, j);
-      out[j] = p;
-      sel[j] = p;
-    }
-    n_sel = nc;
-  } else {
-    // keys are padded with 0 (below every real key) so every pass below is
-    // branch-free over all MAXE slots
-    const uint32_t* sc = a.scores + static_cast<size_t>(r) * a.maxNC;
-    uint32_t vand = 0xffffffffu, vor = 0u;
-    constexpr int LB = MAXE < 8 ? MAXE : 8;         // loads issued per batch
-#pragma unroll
-    for (int x0 = 0; x0 < MAXE; x0 += LB) {
-      uint32_t kreg[LB];
-#pragma unroll
-      for (int u = 0; u < LB; ++u) {
-        const int j = (x0 + u) * kTopkThreads + tid;
-        kreg[u] = j < nc ? sc[j] : 0u;
-      }
-#pragma unroll
-      for (int u = 0; u < LB; ++u) {
-        skey[(x0 + u) * kTopkThreads + tid] = kreg[u];
-        if (kreg[u] != 0u) { vand &= kreg[u]; vor |= kreg[u]; }
-      }
-    }
-    vand = wave_and_u32(vand);
-    vor = wave_or_u32(vor);
-    if (lane == 0) { red[0][w] = vand; red[1][w] = vor; }
-    __syncthreads();
-    vand = 0xffffffffu;
-    vor = 0u;
-#pragma unroll
-    for (int i = 0; i < kTopkWaves; ++i) { vand &= red[0][i]; vor |= red[1][i]; }
-    const uint32_t varying = vand ^ vor;
-    uint32_t tau = vand;
-    int par = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-      if (!((varying >> bit) & 1u)) continue;
-      const uint32_t c = tau | (1u << bit);
-      int n = 0;
-#pragma unroll
-      for (int x = 0; x < MAXE; ++x) n += __popcll(__ballot(skey[x * kTopkThreads + tid] >= c));
-      if (lane == 0) cnt[par][w] = n;
-      __syncthreads();
-      int tot = 0;
-#pragma unroll
-      for (int i = 0; i < kTopkWaves; ++i) tot += cnt[par][i];
-      if (tot >= kc) tau = c;
-      par ^= 1;
-    }
-    // per (x, wave) slot: counts of keys > tau and == tau
-#pragma unroll
-    for (int x = 0; x < MAXE; ++x) {
-      const uint32_t k = skey[x * kTopkThreads + tid];
-      const int ng = __popcll(__ballot(k > tau));
-      const int ne = __popcll(__ballot(k == tau));
-      if (lane == 0) { wgt[x * kTopkWaves + w] = ng; weq[x * kTopkWaves + w] = ne; }
-    }
-    __syncthreads();
-    if (w == 0) {                                    // exclusive scans over the slots
-      int cg = 0, ce = 0;
-      for (int i0 = 0; i0 < NXW; i0 += 64) {
-        const int i = i0 + lane;
-        const int g0 = i < NXW ? wgt[i] : 0, e0 = i < NXW ? weq[i] : 0;
-        int g = g0, e = e0;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int gu = __shfl_up(g, o, 64), eu = __shfl_up(e, o, 64);
-          if (lane >= o) { g += gu; e += eu; }
-        }
-        if (i < NXW) { bgt[i] = cg + g - g0; beq[i] = ce + e - e0; }
-        cg += __shfl(g, 63, 64);
-        ce += __shfl(e, 63, 64);
-      }
-      if (lane == 0) s_ngt = cg;
-    }
-    __syncthreads();
-    const int need = kc - s_ngt;                    // >= 1 keys equal to tau are kept
-    int rank[MAXE];
-#pragma unroll
-    for (int x = 0; x < MAXE; ++x) {
-      const uint32_t k = skey[x * kTopkThreads + tid];
-      const int bq_eq = beq[x * kTopkWaves + w], bq_gt = bgt[x * kTopkWaves + w];
-      const unsigned long long eqm = __ballot(k == tau);
-      const bool take = (k > tau) || (k == tau && bq_eq + lanes_below(eqm) < need);
-      const unsigned long long tm = __ballot(take);
-      rank[x] = take ? bq_gt + min(need, bq_eq) + lanes_below(tm) : -1;
-    }
-    __syncthreads();                                // skey is reused for the kept list
-    int32_t* sel = reinterpret_cast<int32_t*>(skey);
-    constexpr int PB = MAXE < 8 ? MAXE : 8;         // start lookups issued per batch
-#pragma unroll
-    for (int x0 = 0; x0 < MAXE; x0 += PB) {
-      int pos[PB];
-#pragma unroll
-      for (int u = 0; u < PB; ++u)                  // unconditional, so the loads batch
-        pos[u] = chunk_start(a, stage, r, min((x0 + u) * kTopkThreads + tid, nc - 1));
-#pragma unroll
-      for (int u = 0; u < PB; ++u) {
-        if (rank[x0 + u] >= 0) {
-          out[rank[x0 + u]] = pos[u];
-          sel[rank[x0 + u]] = pos[u];
-        }
-      }
-    }
-    n_sel = kc;
-  }
-  if (tid == 0) a.cnt[r * kMaxStages + stage] = n_sel;
-  if (stage != a.n_stages - 1) return;
-
-  // final stage: write the index row from the kept starts in LDS
-  __syncthreads();
-  const int32_t* sel = reinterpret_cast<const int32_t*>(skey);
-  int32_t* row = a.idx + static_cast<size_t>(r) * a.L;
-  const int n_pr = n_sel * l;
-  const int n_win = max(0, geo.e - geo.mid_hi);
-  for (int i = tid; i < a.L; i += kTopkThreads) {
-    int v;
-    if (i < geo.sink_hi) {
-      v = i;
-    } else if (i < geo.sink_hi + n_pr) {
-      const int k = i - geo.sink_hi;
-      const int c = k >> a.lchunk[stage];
-      v = sel[c] + (k & (l - 1));
-    } else if (i < geo.sink_hi + n_pr + n_win) {
-      v = geo.mid_hi + (i - geo.sink_hi - n_pr);
-    } else {
-      v = -1;
-    }
-    row[i] = v;
-  }
-}
-
-template <int MAXE>
+// One workgroup per row. Thread t holds the keys of chunks j = t*E .. t*E+E-1
+// in registers (index order = thread order, so one block-wide scan ranks
+// everything). The K-th largest key is found by radix selection over the bits
+// that vary across the row: 8-bit digits from the most significant varying
+// bit down, each pass a per-wave LDS histogram of the keys still tied with the
+// prefix chosen so far, scanned by one wave. A pass stops the search as soon
+// as the boundary digit's keys are all kept. Keys above the threshold are
+// kept, plus the lowest-index keys equal to it until K are kept; a kept
+// chunk's output slot is the number of kept chunks of lower index.
+template <int E>
 __global__ void __launch_bounds__(kTopkThreads) k_topk(PruneArgs a, int stage) {
+  static_assert(E % 4 == 0, "keys are loaded four at a time");
+  __shared__ uint32_t hist[2][kTopkWaves][256];
+  __shared__ int sprev[kMaxKeptChunks];
+  __shared__ uint32_t sred[2][kTopkWaves];
+  __shared__ uint32_t sscan[kTopkWaves];
+  __shared__ int sdec[3];
+
   const int r = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int b, s, e;
   row_bounds(a.kv, r, b, s, e);
   const Geo geo = make_geo(s, e, a.n_sink, a.n_window, a.chunk[0]);
-  topk_row<MAXE>(a, stage, r, geo, stage_input_chunks(a, stage, r, geo));
+  const int lg = a.lchunk[stage], l = 1 << lg;
+  const int kc = a.keep[stage] >> lg;
+  const bool last = stage == a.n_stages - 1;
+  const int nc = stage_input_chunks(a, stage, r, geo);
+
+  // all loads up front: this thread's keys (clamped into the row; masked by
+  // nc below) and the previous stage's kept starts
+  const int j0 = tid * E;
+  uint32_t key[E];
+  {
+    const uint4* sc4 = reinterpret_cast<const uint4*>(a.scores + static_cast<size_t>(r) * a.maxNC);
+    const int nv = a.maxNC >> 2;
+#pragma unroll
+    for (int v = 0; v < E / 4; ++v) {
+      const uint4 u = sc4[min((j0 >> 2) + v, nv - 1)];
+      key[4 * v + 0] = u.x; key[4 * v + 1] = u.y; key[4 * v + 2] = u.z; key[4 * v + 3] = u.w;
+    }
+  }
+  int sh = 0;
+  if (stage > 0) {
+    sh = a.lchunk[stage - 1] - lg;
+    const int kprev = a.keep[stage - 1] >> a.lchunk[stage - 1];
+    const int32_t* prev =
+        a.starts + static_cast<size_t>((stage - 1) & 1) * a.R * a.maxK + static_cast<size_t>(r) * a.maxK;
+    for (int i0 = 0; i0 < kprev; i0 += 4 * kTopkThreads) {
+      int v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * kTopkThreads + tid;
+        v[u] = i < kprev ? prev[i] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * kTopkThreads + tid;
+        if (i < kprev) sprev[i] = v[u];
+      }
+    }
+  }
+  const bool keep_all = nc <= kc;
+  const int n_sel = keep_all ? nc : kc;
+  int32_t* out = a.starts + static_cast<size_t>(stage & 1) * a.R * a.maxK + static_cast<size_t>(r) * a.maxK;
+  int32_t* row = a.idx + static_cast<size_t>(r) * a.L;
+  if (tid == 0) a.cnt[r * kMaxStages + stage] = n_sel;
+  if (last) {                                      // sinks, window and padding of the index row
+    const int n_pr = n_sel * l;
+    const int n_win = max(0, geo.e - geo.mid_hi);
+    for (int i = tid; i < a.L; i += kTopkThreads) {
+      if (i < geo.sink_hi) row[i] = i;
+      else if (i >= geo.sink_hi + n_pr) {
+        const int k = i - geo.sink_hi - n_pr;
+        row[i] = k < n_win ? geo.mid_hi + k : -1;
+      }
+    }
+  }
+  // kept chunk j lands in output slot pos
+  auto emit = [&](int j, int pos) {
+    const int st = stage == 0 ? a.n_sink + (j << lg) : sprev[j >> sh] + ((j & ((1 << sh) - 1)) << lg);
+    out[pos] = st;
+    if (last) {
+      int32_t* dst = row + geo.sink_hi + pos * l;
+      for (int u = 0; u < l; ++u) dst[u] = st + u;
+    }
+  };
+
+  // common bits of the row's keys (0 marks chunks beyond nc: real keys are
+  // never 0); the histograms are cleared under the same barrier
+  uint32_t vand = 0xffffffffu, vor = 0u;
+#pragma unroll
+  for (int x = 0; x < E; ++x) {
+    if (j0 + x >= nc) key[x] = 0u;
+    if (key[x] != 0u) { vand &= key[x]; vor |= key[x]; }
+  }
+  vand = wave_and_u32(vand);
+  vor = wave_or_u32(vor);
+  if (lane == 0) { sred[0][w] = vand; sred[1][w] = vor; }
+  {
+    uint32_t* h = &hist[0][0][0];
+#pragma unroll
+    for (int i = 0; i < 2 * kTopkWaves * 256 / kTopkThreads; ++i) h[i * kTopkThreads + tid] = 0u;
+  }
+  __syncthreads();                                 // also publishes sprev
+  if (keep_all) {
+    for (int j = j0; j < min(j0 + E, nc); ++j) emit(j, j);
+    return;
+  }
+  vand = 0xffffffffu;
+  vor = 0u;
+#pragma unroll
+  for (int i = 0; i < kTopkWaves; ++i) { vand &= sred[0][i]; vor |= sred[1][i]; }
+  const uint32_t varying = vand ^ vor;
+
+  // radix passes: bits [shift, 32) of the threshold are decided
+  int shift = varying ? 32 - __clz(static_cast<int>(varying)) : 0;
+  uint32_t prefix = shift >= 32 ? 0u : (vand & (~0u << shift));
+  int need = kc;                                   // keys still to keep among the tied ones
+  bool whole = false;                              // the boundary digit is kept whole
+  for (int p = 0; shift > 0; ++p) {
+    const int wd = min(8, shift);
+    shift -= wd;
+    const uint32_t himask = shift + wd >= 32 ? 0u : (~0u << (shift + wd));
+    const uint32_t dmask = (1u << wd) - 1u;
+    uint32_t (*H)[256] = hist[p & 1];
+    {
+      uint32_t* h = &hist[(p + 1) & 1][0][0];      // next pass's buffer, idle since the last scan
+#pragma unroll
+      for (int i = 0; i < kTopkWaves * 256 / kTopkThreads; ++i) h[i * kTopkThreads + tid] = 0u;
+    }
+#pragma unroll
+    for (int x = 0; x < E; ++x) {
+      const uint32_t k = key[x];
+      if (k != 0u && ((k ^ prefix) & himask) == 0u) atomicAdd(&H[w][(k >> shift) & dmask], 1u);
+    }
+    __syncthreads();
+    if (w == 0) {
+      // lane handles bins 255-4*lane .. 252-4*lane, so lane order is digit
+      // order from the top
+      uint32_t c[4], tot = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int bin = 255 - (4 * lane + i);
+        c[i] = 0;
+#pragma unroll
+        for (int ww = 0; ww < kTopkWaves; ++ww) c[i] += H[ww][bin];
+        tot += c[i];
+      }
+      const uint32_t inc = wave_incl_scan_u32(tot);
+      const unsigned long long m = __ballot(inc >= static_cast<uint32_t>(need));
+      if (lane == __ffsll(static_cast<long long>(m)) - 1) {
+        uint32_t run = inc - tot;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (run + c[i] >= static_cast<uint32_t>(need)) {
+            sdec[0] = 255 - (4 * lane + i);
+            sdec[1] = need - static_cast<int>(run);
+            sdec[2] = static_cast<int>(c[i]);
+            break;
+          }
+          run += c[i];
+        }
+      }
+    }
+    __syncthreads();
+    prefix |= static_cast<uint32_t>(sdec[0]) << shift;
+    need = sdec[1];
+    if (sdec[2] == need) { whole = true; break; }
+  }
+
+  // kept: key > tau, or key == tau among the first need_eq such keys; with a
+  // whole boundary digit, every key >= prefix. Per-thread bit masks of the
+  // two classes, then one packed (strict << 16 | equal) block-wide scan.
+  const uint32_t tau = prefix;
+  const int need_eq = whole ? 0 : need;
+  constexpr int NM = (E + 31) / 32;
+  uint32_t sm[NM], em[NM];
+#pragma unroll
+  for (int m = 0; m < NM; ++m) { sm[m] = 0u; em[m] = 0u; }
+#pragma unroll
+  for (int x = 0; x < E; ++x) {
+    const uint32_t k = key[x];
+    const bool strict = k != 0u && (whole ? k >= tau : k > tau);
+    const bool eq = !whole && k == tau && k != 0u;
+    sm[x >> 5] |= (strict ? 1u : 0u) << (x & 31);
+    em[x >> 5] |= (eq ? 1u : 0u) << (x & 31);
+  }
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int m = 0; m < NM; ++m) cnt += (static_cast<uint32_t>(__popc(sm[m])) << 16) + __popc(em[m]);
+  const uint32_t inc = wave_incl_scan_u32(cnt);
+  if (lane == 63) sscan[w] = inc;
+  __syncthreads();
+  uint32_t base = inc - cnt;
+#pragma unroll
+  for (int i = 0; i < kTopkWaves; ++i)
+    if (i < w) base += sscan[i];
+  int cs = static_cast<int>(base >> 16), ce = static_cast<int>(base & 0xffffu);
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    for (uint32_t rest = sm[m] | em[m]; rest != 0u; rest &= rest - 1u) {
+      const int bit = __ffs(static_cast<int>(rest)) - 1;
+      const uint32_t below = (1u << bit) - 1u;
+      const int ps = cs + __popc(sm[m] & below);       // strict keys of lower index
+      const int pe = ce + __popc(em[m] & below);       // equal keys of lower index
+      if ((sm[m] >> bit) & 1u) emit(j0 + 32 * m + bit, ps + min(need_eq, pe));
+      else if (pe < need_eq) emit(j0 + 32 * m + bit, ps + pe);
+    }
+    cs += __popc(sm[m]);
+    ce += __popc(em[m]);
+  }
 }
 
 // ------------------------------------------------------------------------- //
