@@ -48,6 +48,7 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk(PruneArgs a, int stage) {
   static_assert(E % 4 == 0, "keys are loaded four at a time");
   __shared__ uint32_t hist[2][kTopkWaves][256];
   __shared__ int sprev[kMaxKeptChunks];
+  __shared__ int ssel[kMaxKeptChunks];             // final stage: kept starts in output order
   __shared__ uint32_t sred[2][kTopkWaves];
   __shared__ uint32_t sscan[kTopkWaves];
   __shared__ int sdec[3];
@@ -99,26 +100,11 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk(PruneArgs a, int stage) {
   const int n_sel = keep_all ? nc : kc;
   int32_t* out = a.starts + static_cast<size_t>(stage & 1) * a.R * a.maxK + static_cast<size_t>(r) * a.maxK;
   int32_t* row = a.idx + static_cast<size_t>(r) * a.L;
-  if (tid == 0) a.cnt[r * kMaxStages + stage] = n_sel;
-  if (last) {                                      // sinks, window and padding of the index row
-    const int n_pr = n_sel * l;
-    const int n_win = max(0, geo.e - geo.mid_hi);
-    for (int i = tid; i < a.L; i += kTopkThreads) {
-      if (i < geo.sink_hi) row[i] = i;
-      else if (i >= geo.sink_hi + n_pr) {
-        const int k = i - geo.sink_hi - n_pr;
-        row[i] = k < n_win ? geo.mid_hi + k : -1;
-      }
-    }
-  }
   // kept chunk j lands in output slot pos
   auto emit = [&](int j, int pos) {
     const int st = stage == 0 ? a.n_sink + (j << lg) : sprev[j >> sh] + ((j & ((1 << sh) - 1)) << lg);
     out[pos] = st;
-    if (last) {
-      int32_t* dst = row + geo.sink_hi + pos * l;
-      for (int u = 0; u < l; ++u) dst[u] = st + u;
-    }
+    if (last) ssel[pos] = st;
   };
 
   // common bits of the row's keys (0 marks chunks beyond nc: real keys are
@@ -138,112 +124,135 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk(PruneArgs a, int stage) {
     for (int i = 0; i < 2 * kTopkWaves * 256 / kTopkThreads; ++i) h[i * kTopkThreads + tid] = 0u;
   }
   __syncthreads();                                 // also publishes sprev
+  // stores only after every load has been consumed: stores share the vector
+  // memory counter with loads, so an earlier store would hold up their wait
+  if (tid == 0) a.cnt[r * kMaxStages + stage] = n_sel;
   if (keep_all) {
     for (int j = j0; j < min(j0 + E, nc); ++j) emit(j, j);
-    return;
-  }
-  vand = 0xffffffffu;
-  vor = 0u;
+  } else {
+    vand = 0xffffffffu;
+    vor = 0u;
 #pragma unroll
-  for (int i = 0; i < kTopkWaves; ++i) { vand &= sred[0][i]; vor |= sred[1][i]; }
-  const uint32_t varying = vand ^ vor;
+    for (int i = 0; i < kTopkWaves; ++i) { vand &= sred[0][i]; vor |= sred[1][i]; }
+    const uint32_t varying = vand ^ vor;
 
-  // radix passes: bits [shift, 32) of the threshold are decided
-  int shift = varying ? 32 - __clz(static_cast<int>(varying)) : 0;
-  uint32_t prefix = shift >= 32 ? 0u : (vand & (~0u << shift));
-  int need = kc;                                   // keys still to keep among the tied ones
-  bool whole = false;                              // the boundary digit is kept whole
-  for (int p = 0; shift > 0; ++p) {
-    const int wd = min(8, shift);
-    shift -= wd;
-    const uint32_t himask = shift + wd >= 32 ? 0u : (~0u << (shift + wd));
-    const uint32_t dmask = (1u << wd) - 1u;
-    uint32_t (*H)[256] = hist[p & 1];
-    {
-      uint32_t* h = &hist[(p + 1) & 1][0][0];      // next pass's buffer, idle since the last scan
+    // radix passes: bits [shift, 32) of the threshold are decided
+    int shift = varying ? 32 - __clz(static_cast<int>(varying)) : 0;
+    uint32_t prefix = shift >= 32 ? 0u : (vand & (~0u << shift));
+    int need = kc;                                   // keys still to keep among the tied ones
+    bool whole = false;                              // the boundary digit is kept whole
+    for (int p = 0; shift > 0; ++p) {
+      const int wd = min(8, shift);
+      shift -= wd;
+      const uint32_t himask = shift + wd >= 32 ? 0u : (~0u << (shift + wd));
+      const uint32_t dmask = (1u << wd) - 1u;
+      uint32_t (*H)[256] = hist[p & 1];
+      {
+        uint32_t* h = &hist[(p + 1) & 1][0][0];      // next pass's buffer, idle since the last scan
 #pragma unroll
-      for (int i = 0; i < kTopkWaves * 256 / kTopkThreads; ++i) h[i * kTopkThreads + tid] = 0u;
+        for (int i = 0; i < kTopkWaves * 256 / kTopkThreads; ++i) h[i * kTopkThreads + tid] = 0u;
+      }
+#pragma unroll
+      for (int x = 0; x < E; ++x) {
+        const uint32_t k = key[x];
+        if (k != 0u && ((k ^ prefix) & himask) == 0u) atomicAdd(&H[w][(k >> shift) & dmask], 1u);
+      }
+      __syncthreads();
+      if (w == 0) {
+        // lane handles bins 255-4*lane .. 252-4*lane, so lane order is digit
+        // order from the top
+        uint32_t c[4], tot = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int bin = 255 - (4 * lane + i);
+          c[i] = 0;
+#pragma unroll
+          for (int ww = 0; ww < kTopkWaves; ++ww) c[i] += H[ww][bin];
+          tot += c[i];
+        }
+        const uint32_t inc = wave_incl_scan_u32(tot);
+        const unsigned long long m = __ballot(inc >= static_cast<uint32_t>(need));
+        if (lane == __ffsll(static_cast<long long>(m)) - 1) {
+          uint32_t run = inc - tot;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (run + c[i] >= static_cast<uint32_t>(need)) {
+              sdec[0] = 255 - (4 * lane + i);
+              sdec[1] = need - static_cast<int>(run);
+              sdec[2] = static_cast<int>(c[i]);
+              break;
+            }
+            run += c[i];
+          }
+        }
+      }
+      __syncthreads();
+      prefix |= static_cast<uint32_t>(sdec[0]) << shift;
+      need = sdec[1];
+      if (sdec[2] == need) { whole = true; break; }
     }
+
+    // kept: key > tau, or key == tau among the first need_eq such keys; with a
+    // whole boundary digit, every key >= prefix. Per-thread bit masks of the
+    // two classes, then one packed (strict << 16 | equal) block-wide scan.
+    const uint32_t tau = prefix;
+    const int need_eq = whole ? 0 : need;
+    constexpr int NM = (E + 31) / 32;
+    uint32_t sm[NM], em[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) { sm[m] = 0u; em[m] = 0u; }
 #pragma unroll
     for (int x = 0; x < E; ++x) {
       const uint32_t k = key[x];
-      if (k != 0u && ((k ^ prefix) & himask) == 0u) atomicAdd(&H[w][(k >> shift) & dmask], 1u);
+      const bool strict = k != 0u && (whole ? k >= tau : k > tau);
+      const bool eq = !whole && k == tau && k != 0u;
+      sm[x >> 5] |= (strict ? 1u : 0u) << (x & 31);
+      em[x >> 5] |= (eq ? 1u : 0u) << (x & 31);
     }
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) cnt += (static_cast<uint32_t>(__popc(sm[m])) << 16) + __popc(em[m]);
+    const uint32_t inc = wave_incl_scan_u32(cnt);
+    if (lane == 63) sscan[w] = inc;
     __syncthreads();
-    if (w == 0) {
-      // lane handles bins 255-4*lane .. 252-4*lane, so lane order is digit
-      // order from the top
-      uint32_t c[4], tot = 0;
+    uint32_t base = inc - cnt;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int bin = 255 - (4 * lane + i);
-        c[i] = 0;
+    for (int i = 0; i < kTopkWaves; ++i)
+      if (i < w) base += sscan[i];
+    int cs = static_cast<int>(base >> 16), ce = static_cast<int>(base & 0xffffu);
 #pragma unroll
-        for (int ww = 0; ww < kTopkWaves; ++ww) c[i] += H[ww][bin];
-        tot += c[i];
+    for (int m = 0; m < NM; ++m) {
+      for (uint32_t rest = sm[m] | em[m]; rest != 0u; rest &= rest - 1u) {
+        const int bit = __ffs(static_cast<int>(rest)) - 1;
+        const uint32_t below = (1u << bit) - 1u;
+        const int ps = cs + __popc(sm[m] & below);       // strict keys of lower index
+        const int pe = ce + __popc(em[m] & below);       // equal keys of lower index
+        if ((sm[m] >> bit) & 1u) emit(j0 + 32 * m + bit, ps + min(need_eq, pe));
+        else if (pe < need_eq) emit(j0 + 32 * m + bit, ps + pe);
       }
-      const uint32_t inc = wave_incl_scan_u32(tot);
-      const unsigned long long m = __ballot(inc >= static_cast<uint32_t>(need));
-      if (lane == __ffsll(static_cast<long long>(m)) - 1) {
-        uint32_t run = inc - tot;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (run + c[i] >= static_cast<uint32_t>(need)) {
-            sdec[0] = 255 - (4 * lane + i);
-            sdec[1] = need - static_cast<int>(run);
-            sdec[2] = static_cast<int>(c[i]);
-            break;
-          }
-          run += c[i];
-        }
-      }
+      cs += __popc(sm[m]);
+      ce += __popc(em[m]);
     }
-    __syncthreads();
-    prefix |= static_cast<uint32_t>(sdec[0]) << shift;
-    need = sdec[1];
-    if (sdec[2] == need) { whole = true; break; }
   }
+  if (!last) return;
 
-  // kept: key > tau, or key == tau among the first need_eq such keys; with a
-  // whole boundary digit, every key >= prefix. Per-thread bit masks of the
-  // two classes, then one packed (strict << 16 | equal) block-wide scan.
-  const uint32_t tau = prefix;
-  const int need_eq = whole ? 0 : need;
-  constexpr int NM = (E + 31) / 32;
-  uint32_t sm[NM], em[NM];
-#pragma unroll
-  for (int m = 0; m < NM; ++m) { sm[m] = 0u; em[m] = 0u; }
-#pragma unroll
-  for (int x = 0; x < E; ++x) {
-    const uint32_t k = key[x];
-    const bool strict = k != 0u && (whole ? k >= tau : k > tau);
-    const bool eq = !whole && k == tau && k != 0u;
-    sm[x >> 5] |= (strict ? 1u : 0u) << (x & 31);
-    em[x >> 5] |= (eq ? 1u : 0u) << (x & 31);
-  }
-  uint32_t cnt = 0;
-#pragma unroll
-  for (int m = 0; m < NM; ++m) cnt += (static_cast<uint32_t>(__popc(sm[m])) << 16) + __popc(em[m]);
-  const uint32_t inc = wave_incl_scan_u32(cnt);
-  if (lane == 63) sscan[w] = inc;
+  // final stage: the index row (sinks, kept chunks, window, -1 padding) in
+  // 16-byte stores; L is a multiple of 64
   __syncthreads();
-  uint32_t base = inc - cnt;
+  const int n_pr = n_sel * l;
+  const int win0 = geo.sink_hi + n_pr;
+  const int n_win = max(0, geo.e - geo.mid_hi);
+  for (int i4 = tid; i4 < (a.L >> 2); i4 += kTopkThreads) {
+    int v[4];
 #pragma unroll
-  for (int i = 0; i < kTopkWaves; ++i)
-    if (i < w) base += sscan[i];
-  int cs = static_cast<int>(base >> 16), ce = static_cast<int>(base & 0xffffu);
-#pragma unroll
-  for (int m = 0; m < NM; ++m) {
-    for (uint32_t rest = sm[m] | em[m]; rest != 0u; rest &= rest - 1u) {
-      const int bit = __ffs(static_cast<int>(rest)) - 1;
-      const uint32_t below = (1u << bit) - 1u;
-      const int ps = cs + __popc(sm[m] & below);       // strict keys of lower index
-      const int pe = ce + __popc(em[m] & below);       // equal keys of lower index
-      if ((sm[m] >> bit) & 1u) emit(j0 + 32 * m + bit, ps + min(need_eq, pe));
-      else if (pe < need_eq) emit(j0 + 32 * m + bit, ps + pe);
+    for (int u = 0; u < 4; ++u) {
+      const int i = 4 * i4 + u;
+      if (i < geo.sink_hi) v[u] = i;
+      else if (i < win0) v[u] = ssel[(i - geo.sink_hi) >> lg] + ((i - geo.sink_hi) & (l - 1));
+      else if (i < win0 + n_win) v[u] = geo.mid_hi + (i - win0);
+      else v[u] = -1;
     }
-    cs += __popc(sm[m]);
-    ce += __popc(em[m]);
+    reinterpret_cast<int4*>(row)[i4] = make_int4(v[0], v[1], v[2], v[3]);
   }
 }
 
@@ -263,34 +272,47 @@ template <typename T, int D, int G, bool SPEC>
 __global__ void __launch_bounds__(256, G > 4 ? 2 : ((SPEC || sizeof(T) == 4) ? 4 : 8))
 k_score_decode(PruneArgs a, int stage) {
   constexpr int EPL = D / 16;
+  using Row = RowSlice<T, EPL>;
   const KvLayout& kv = a.kv;
-  const int r = blockIdx.y;
-  int b, s, e;
-  row_bounds(kv, r, b, s, e);
-  const Geo geo = make_geo(s, e, a.n_sink, a.n_window, a.chunk[0]);
-  const int nc = stage_input_chunks(a, stage, r, geo);
-  const int l = a.chunk[stage];
-  if (nc <= (a.keep[stage] >> a.lchunk[stage])) return;   // stage keeps everything for this row
+  const int r = blockIdx.y, b = r;              // one row per sequence
   const int cpw = 16 / kv.Hkv;                  // chunks per workgroup
   const int j0 = blockIdx.x * cpw;
-  if (j0 >= nc) return;
-
   const int tid = threadIdx.x;
   const int gi = tid >> 4, li = tid & 15;
   const int cl = gi / kv.Hkv, g = gi - cl * kv.Hkv;
   const int j = j0 + cl;
-  const bool active = j < nc;
+  const int l = a.chunk[stage];
+  const T* K = static_cast<const T*>(a.k);
+  const T* Q = static_cast<const T*>(a.q);
   __shared__ float red[16];
+
+  // Loads that need only the launch coordinates go out together, before the
+  // checks that use them: the sequence length, the previous stage's kept
+  // count, this chunk's start (read within the start list for every j of
+  // the grid) and the query rows.
+  const int e = kv.seq_lens[r];
+  int nc_prev = 0, st;
+  if (stage == 0) {
+    st = a.n_sink + (j << a.lchunk[0]);
+  } else {
+    const int sh = a.lchunk[stage - 1] - a.lchunk[stage];
+    nc_prev = a.cnt[r * kMaxStages + stage - 1];
+    const int32_t* prev =
+        a.starts + static_cast<size_t>((stage - 1) & 1) * a.R * a.maxK + static_cast<size_t>(r) * a.maxK;
+    st = prev[min(j >> sh, a.maxK - 1)] + ((j & ((1 << sh) - 1)) << a.lchunk[stage]);
+  }
+  Row q[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) q[hh].load(Q + (static_cast<size_t>(b) * kv.Hq + g * G + hh) * D + li * EPL);
+
+  const Geo geo = make_geo(e - 1, e, a.n_sink, a.n_window, a.chunk[0]);
+  const int nc = stage == 0 ? geo.n1 : nc_prev << (a.lchunk[stage - 1] - a.lchunk[stage]);
+  if (nc <= (a.keep[stage] >> a.lchunk[stage])) return;   // stage keeps everything for this row
+  if (j0 >= nc) return;
+  const bool active = j < nc;
 
   float best = -INFINITY;
   if (active) {
-    const T* K = static_cast<const T*>(a.k);
-    const T* Q = static_cast<const T*>(a.q);
-    const int st = chunk_start(a, stage, r, j);
-    using Row = RowSlice<T, EPL>;
-    Row q[G];
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) q[hh].load(Q + (static_cast<size_t>(b) * kv.Hq + g * G + hh) * D + li * EPL);
     auto dot = [&](const Row& kr, int hh) { return group16_sum(kr.dot(q[hh])); };
     auto row_at = [&](int pos) {
       Row x;
