@@ -12,23 +12,51 @@
 // and partial sums of grid-valued inputs are exact in fp32, so the MFMA
 // result equals the scalar dot product bit for bit.
 //
-// Workgroup = 4 waves x 32 chunks of one row (query block); the waves split
-// the query heads, each running its heads' tournaments for the 32 chunks; the
-// chunk score (max over all heads) is reduced in LDS.
+// Workgroup = 4 waves x 32*T chunks of one row (query block); the waves split
+// the query heads. For each of its heads a wave runs T groups of 32
+// tournaments side by side (the groups share the head's query fragments), so
+// every dependent round of key-row loads has T independent row sets in
+// flight. Rows reach the matrix-core operand layout through a per-wave LDS
+// staging buffer: a wave-wide 16-byte load covers whole rows (PPR lanes per
+// row, 4 rows per load at d = 128) instead of touching 32 rows at once, and
+// the fragments are then read from LDS. The query block of each head takes the
+// same path. The chunk score (max over all heads) is reduced in LDS.
 #include "prune_common.h"
 
 namespace dsa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));   // 16-byte staging word
 
-template <int D>
-__global__ void __launch_bounds__(256) k_score_prefill_mfma(PruneArgs a, int stage) {
+constexpr int kRowGroup = 16;           // neighbouring query blocks scheduled together
+constexpr int kScoreGroups = 2;         // T: 32-chunk tournament groups per wave
+
+template <int D, int T>
+__global__ void __launch_bounds__(256) k_score_prefill_mfma(PruneArgs a, int stage, int ncg) {
+  static_assert(T == 1 || T == 2, "the staging buffer holds 64 rows");
   constexpr int KS = D / 16;
+  constexpr int CPB = 32 * T;           // chunks per workgroup
+  constexpr int PPR = D / 8;            // 16-byte pieces per row
+  constexpr int RPI = 64 / PPR;         // rows per wave-wide load
+  constexpr int LPS = 32 / RPI;         // loads per 32-row set
+  constexpr int KROW = D + 8;           // staging row stride (bf16): shifts banks by 4 words per row
+  __shared__ __align__(16) uint16_t sbuf[4][64 * KROW];
+  __shared__ int spos[4][2 * T][32];
+  __shared__ float red[4][CPB];
+
   const KvLayout& kv = a.kv;
-  // rows vary fastest, so concurrently running workgroups score the same
-  // chunk positions for neighbouring query blocks (shared rows in L2)
-  const int r = blockIdx.x, j0 = blockIdx.y * 32;
+  // XCD-aware order: consecutive workgroup ids go to different XCDs. Groups
+  // of kRowGroup neighbouring query blocks are dealt to the XCDs in turn, and
+  // each XCD walks its groups one at a time over all chunk groups, so the
+  // blocks running together on one XCD score the same chunk positions with
+  // similar queries and share the key rows in that XCD's L2.
+  const int x = blockIdx.x & 7, i = blockIdx.x >> 3;
+  const int per_group = ncg * kRowGroup;
+  const int rbl = i / per_group, rem = i - rbl * per_group;
+  const int r = ((rbl << 3) + x) * kRowGroup + rem % kRowGroup;
+  const int j0 = (rem / kRowGroup) * CPB;
+  if (r >= a.R) return;
   int b, s, e;
   row_bounds(kv, r, b, s, e);
   const Geo geo = make_geo(s, e, a.n_sink, a.n_window, a.chunk[0]);
@@ -38,100 +66,165 @@ __global__ void __launch_bounds__(256) k_score_prefill_mfma(PruneArgs a, int sta
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int j = j0 + l32;
-  const bool active = j < nc;
-  const int st = chunk_start(a, stage, r, active ? j : j0);
+  const int piece = lane % PPR, rsub = lane / PPR;          // loader view of the lane
+  uint16_t* buf = sbuf[w];
+  int st[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int j = j0 + 32 * t + l32;
+    st[t] = chunk_start(a, stage, r, j < nc ? j : j0);   // idle columns score chunk j0
+  }
   const int l = a.chunk[stage];
   const int G = kv.Hq / kv.Hkv;
   const uint16_t* Q = static_cast<const uint16_t*>(a.q);
   const uint16_t* K = static_cast<const uint16_t*>(a.k);
-  __shared__ float red[4][32];
 
-  float best = -INFINITY;
+  // Sets of 32 key rows: the column owners publish the positions in spos,
+  // the loader lanes fetch whole rows, and the rows are staged two sets at a
+  // time (slots 0 and 1 of the buffer).
+#define DSA_FETCH(base, set, v)                                                                 \
+  _Pragma("unroll") for (int u = 0; u < LPS; ++u) {                                           \
+    const int p_ = spos[w][set][u * RPI + rsub];                                              \
+    (v)[u] = *reinterpret_cast<const u32x4_t*>((base) + static_cast<size_t>(p_) * D + piece * 8); \
+  }
+#define DSA_STAGE(slot, v)                                                                     \
+  _Pragma("unroll") for (int u = 0; u < LPS; ++u)                                             \
+    *reinterpret_cast<u32x4_t*>(buf + ((slot) * 32 + u * RPI + rsub) * KROW + piece * 8) = (v)[u];
+
+  float best[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) best[t] = -INFINITY;
   for (int h = w; h < kv.Hq; h += 4) {
     const int g = h / G;
-    const size_t kvbase = (static_cast<size_t>(b) * kv.Hkv + g) * kv.T;
+    const uint16_t* Kg = K + (static_cast<size_t>(b) * kv.Hkv + g) * kv.T * D;
     bf16x8_t qf[2][KS];
+    {
+      const uint16_t* qblk = Q + ((static_cast<size_t>(b) * kv.Hq + h) * kv.T + s) * D;
+      u32x4_t v[2 * LPS];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      const uint16_t* qrow = Q + ((static_cast<size_t>(b) * kv.Hq + h) * kv.T + s + qt * 32 + l32) * D;
+      for (int u = 0; u < 2 * LPS; ++u)
+        v[u] = *reinterpret_cast<const u32x4_t*>(qblk + (u * RPI + rsub) * D + piece * 8);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        qf[qt][ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qrow + ks * 16 + hi * 8));
+      for (int u = 0; u < 2 * LPS; ++u)
+        *reinterpret_cast<u32x4_t*>(buf + (u * RPI + rsub) * KROW + piece * 8) = v[u];
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          qf[qt][ks] = *reinterpret_cast<const bf16x8_t*>(buf + (qt * 32 + l32) * KROW + ks * 16 + hi * 8);
     }
-    // sigma of the key at position `pos` for this lane's chunk
-    auto sigma_of = [&](const bf16x8_t* kf) {
+    // sigma of the staged key in slot `slot` for this lane's chunk
+    auto sigma_of = [&](int slot) __attribute__((always_inline)) {
       f32x16_t acc[2];
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[qt][i] = 0.f;
+        for (int i2 = 0; i2 < 16; ++i2) acc[qt][i2] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8_t kf =
+            *reinterpret_cast<const bf16x8_t*>(buf + (slot * 32 + l32) * KROW + ks * 16 + hi * 8);
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt)
-          acc[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[qt][ks], kf[ks], acc[qt], 0, 0, 0);
+          acc[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[qt][ks], kf, acc[qt], 0, 0, 0);
+      }
       float m = acc[0][0];
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) m = fmaxf(m, acc[qt][i]);
+        for (int i2 = 0; i2 < 16; ++i2) m = fmaxf(m, acc[qt][i2]);
       return fmaxf(m, __shfl_xor(m, 32, 64));
     };
-    auto load_row = [&](int pos, bf16x8_t* kf) {
-      const uint16_t* krow = K + (kvbase + pos) * D + hi * 8;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        kf[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(krow + ks * 16));
-    };
 
-    float sa;
+    float sa[T];
     if (l == 1) {
-      bf16x8_t k0[KS];
-      load_row(st, k0);
-      sa = sigma_of(k0);
+      if (hi == 0) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) spos[w][t][l32] = st[t];
+      }
+      u32x4_t v0[LPS], v1[LPS];
+      DSA_FETCH(Kg, 0, v0);
+      if (T > 1) { DSA_FETCH(Kg, T - 1, v1); }
+      DSA_STAGE(0, v0);
+      if (T > 1) { DSA_STAGE(1, v1); }
+#pragma unroll
+      for (int t = 0; t < T; ++t) sa[t] = sigma_of(t);
     } else {
-      // first split: both representatives are loaded in one round
+      // first split: both representatives of every group in one round
       const int mid0 = l >> 1;
-      int lo, hi_r;
+      int lo[T], hi_r[T];
+      if (hi == 0) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          spos[w][2 * t][l32] = st[t];
+          spos[w][2 * t + 1][l32] = st[t] + mid0;
+        }
+      }
       {
-        bf16x8_t k0[KS], k1[KS];
-        load_row(st, k0);
-        load_row(st + mid0, k1);
-        const float s0 = sigma_of(k0), s1 = sigma_of(k1);
-        if (s1 > s0) { lo = mid0; hi_r = l - 1; sa = s1; }
-        else         { lo = 0;    hi_r = mid0 - 1; sa = s0; }
+        u32x4_t v0[LPS], v1[LPS], v2[LPS], v3[LPS];
+        DSA_FETCH(Kg, 0, v0);
+        DSA_FETCH(Kg, 1, v1);
+        if (T > 1) { DSA_FETCH(Kg, 2 * T - 2, v2); DSA_FETCH(Kg, 2 * T - 1, v3); }
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          if (t == 0) { DSA_STAGE(0, v0); DSA_STAGE(1, v1); }
+          else        { DSA_STAGE(0, v2); DSA_STAGE(1, v3); }
+          const float s0 = sigma_of(0), s1 = sigma_of(1);
+          if (s1 > s0) { lo[t] = mid0; hi_r[t] = l - 1; sa[t] = s1; }
+          else         { lo[t] = 0;    hi_r[t] = mid0 - 1; sa[t] = s0; }
+        }
       }
       for (int wd = mid0 >> 1; wd >= 1; wd >>= 1) {
-        const int mid = (lo + hi_r + 1) >> 1;
-        bf16x8_t km[KS];
-        load_row(st + mid, km);
-        const float sm = sigma_of(km);
-        if (sm > sa) { lo = mid; sa = sm; }
-        else         { hi_r = mid - 1; }
+        int mid[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          mid[t] = (lo[t] + hi_r[t] + 1) >> 1;
+          if (hi == 0) spos[w][t][l32] = st[t] + mid[t];
+        }
+        u32x4_t v0[LPS], v1[LPS];
+        DSA_FETCH(Kg, 0, v0);
+        if (T > 1) { DSA_FETCH(Kg, T - 1, v1); }
+        DSA_STAGE(0, v0);
+        if (T > 1) { DSA_STAGE(1, v1); }
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const float sm = sigma_of(t);
+          if (sm > sa[t]) { lo[t] = mid[t]; sa[t] = sm; }
+          else            { hi_r[t] = mid[t] - 1; }
+        }
       }
     }
-    best = fmaxf(best, sa);
+#pragma unroll
+    for (int t = 0; t < T; ++t) best[t] = fmaxf(best[t], sa[t]);
   }
-  if (hi == 0) red[w][l32] = best;
+  if (hi == 0) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) red[w][32 * t + l32] = best[t];
+  }
   __syncthreads();
-  if (tid < 32 && j0 + tid < nc) {
-    const float m = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
-    a.scores[static_cast<size_t>(r) * a.maxNC + j0 + tid] = score_key(m);
+  for (int c = tid; c < CPB; c += 256) {
+    if (j0 + c < nc) {
+      const float m = fmaxf(fmaxf(red[0][c], red[1][c]), fmaxf(red[2][c], red[3][c]));
+      a.scores[static_cast<size_t>(r) * a.maxNC + j0 + c] = score_key(m);
+    }
   }
 }
+#undef DSA_FETCH
+#undef DSA_STAGE
 
 // bf16 prefill with query blocks of 64: score stage `stage` on the matrix cores.
 bool launch_score_prefill_mfma(const PruneArgs& a, int stage, int max_chunks, hipStream_t st,
                                const char* name) {
   if (a.kv.decode || a.kv.bq != 64 || max_chunks <= 0) return false;
-  dim3 grid(a.R, (max_chunks + 31) / 32);
+  const int ncg = (max_chunks + 32 * kScoreGroups - 1) / (32 * kScoreGroups);
+  const long long groups = (a.R + 8LL * kRowGroup - 1) / (8LL * kRowGroup);   // per XCD
+  const dim3 grid(static_cast<unsigned>(groups * 8 * kRowGroup * ncg));
   if (a.kv.D == 128) {
-    DSA_LAUNCH(name, (k_score_prefill_mfma<128>), grid, dim3(256), st, a, stage);
+    DSA_LAUNCH(name, (k_score_prefill_mfma<128, kScoreGroups>), grid, dim3(256), st, a, stage, ncg);
     return true;
   }
   if (a.kv.D == 64) {
-    DSA_LAUNCH(name, (k_score_prefill_mfma<64>), grid, dim3(256), st, a, stage);
+    DSA_LAUNCH(name, (k_score_prefill_mfma<64, kScoreGroups>), grid, dim3(256), st, a, stage, ncg);
     return true;
   }
   return false;
