@@ -26,6 +26,17 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef i16x4_t __attribute__((address_space(3))) lds_i16x4_t;
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane 4a+c receives element c
+// of the 64-bit words addressed by lanes a, a+4, a+8, a+12 (in that order).
+// With lane s addressing row (s >> 2) at column 4 * (s & 3) of a row-major
+// 16-bit tile, lane i of the group therefore receives column i of 4
+// consecutive rows: a transposed read.
+__device__ __forceinline__ i16x4_t lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
+}
 
 // two floats to packed bf16 (round to nearest even) in one conversion
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -38,9 +49,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // 32 queries' fragments and its O^T accumulators in registers, so a workgroup
 // needs only the two key tiles in LDS and two workgroups share a CU; their
 // independent barriers let one workgroup's matrix products overlap the
-// other's softmax. K rows are fetched whole-row per load (coalesced) and
-// staged row-major; V rows are fetched in 16-key groups and staged
-// transposed; the two tiles in flight use alternating LDS buffers.
+// other's softmax. K and V rows are fetched whole-row per load (coalesced)
+// and staged row-major; the V^T operand is read with LDS transpose reads. The
+// two tiles in flight use alternating LDS buffers.
 template <int D, int NH, int QH>
 __global__ void __launch_bounds__(64 * NH * QH) k_prefill_mfma(AttnArgs a) {
   constexpr int NWV = NH * QH;        // waves
@@ -49,14 +60,13 @@ __global__ void __launch_bounds__(64 * NH * QH) k_prefill_mfma(AttnArgs a) {
   constexpr int DT = D / 32;          // 32-row tiles of O^T
   constexpr int PPR = D / 8;          // 16-byte pieces per key row
   constexpr int KROW = D + 8;         // K tile row stride (bf16 elements)
-  constexpr int VROW = 64 + 4;        // V^T tile row stride (bf16 elements), 34 dwords
-  constexpr int KPER = 64 * PPR / NT; // K pieces per thread per tile
-  constexpr int VPER = KPER;          // V pieces per thread per tile
+  constexpr int VROW = D + 16;        // V tile row stride: 4 rows of a transpose read hit disjoint banks
+  constexpr int KPER = 64 * PPR / NT; // K (and V) pieces per thread per tile
   static_assert(KPER >= 1 && (64 * PPR) % NT == 0, "tile loads must split evenly");
   // two tile buffers: tile i is computed from one while tile i+1 is written
   // to the other, so one barrier per tile separates the phases
   __shared__ __align__(16) uint16_t sk[2][64 * KROW];
-  __shared__ __align__(16) uint16_t svt[2][D * VROW];
+  __shared__ __align__(16) uint16_t sv[2][64 * VROW];
   __shared__ __align__(16) int spos[2][64];
   __shared__ int sneed[2][NWV], sany[2][NWV];
 
@@ -81,6 +91,9 @@ __global__ void __launch_bounds__(64 * NH * QH) k_prefill_mfma(AttnArgs a) {
   const int s = m * 64, e = s + 64;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
+  // transpose-read addressing of this lane: row (lane & 15) >> 2, column
+  // 4 * (lane & 3) within its 16-lane group, groups 1 and 3 on d-rows 16..31
+  const int tr_row = (lane & 15) >> 2, tr_col = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
   const int hw = w % NH, qg = w / NH;
   const int h = g * G + (hg % HG) * NH + hw;
   const int q0 = s + (qsplit * QH + qg) * 32;     // this wave's first query
@@ -120,16 +133,12 @@ __global__ void __launch_bounds__(64 * NH * QH) k_prefill_mfma(AttnArgs a) {
     }
     return p;
   };
-  // loader views: K piece u covers (row, 16-byte piece) with 16 lanes per
-  // row; V piece u covers (16-key group, 4-piece group) so that its transposed
-  // LDS writes are contiguous along keys
+  // loader view: piece u covers (row, 16-byte piece), PPR lanes per row
   auto krow_of = [&](int u) { return (u * NT + tid) / PPR; };
   auto kpiece_of = [&](int u) { return (u * NT + tid) % PPR; };
-  auto vkey_of = [&](int u) { return ((u * NWV + w) & 3) * 16 + (lane & 15); };
-  auto vpiece_of = [&](int u) { return ((u * NWV + w) >> 2) * 4 + (lane >> 4); };
 
-  int pk[KPER], pkn[KPER], pv[VPER], pvn[VPER];
-  u32x4_t kreg[KPER], vreg[VPER];
+  int pk[KPER], pkn[KPER];
+  u32x4_t kreg[KPER], vreg[KPER];
   // registers -> tile buffer `bi`, with the tile's mask / visibility flags
 #define DSA_STAGE_TILE(bi)                                                                          \
   do {                                                                                              \
@@ -142,13 +151,8 @@ __global__ void __launch_bounds__(64 * NH * QH) k_prefill_mfma(AttnArgs a) {
       const u32x4_t zero_ = {0u, 0u, 0u, 0u};                                                       \
       *reinterpret_cast<u32x4_t*>(sk[bi] + krow_of(u) * KROW + kpiece_of(u) * 8) =                  \
           p_ >= 0 ? kreg[u] : zero_;                                                                \
-    }                                                                                               \
-    _Pragma("unroll") for (int u = 0; u < VPER; ++u) {                                              \
-      const u32x4_t vv_ = vreg[u];                                                                  \
-      const bool ok_ = pv[u] >= 0;                                                                  \
-      const int key_ = vkey_of(u), pc_ = vpiece_of(u);                                              \
-      _Pragma("unroll") for (int j = 0; j < 8; ++j) svt[bi][(pc_ * 8 + j) * VROW + key_] =          \
-          ok_ ? static_cast<uint16_t>(vv_[j >> 1] >> ((j & 1) * 16)) : 0;                           \
+      *reinterpret_cast<u32x4_t*>(sv[bi] + krow_of(u) * VROW + kpiece_of(u) * 8) =                  \
+          p_ >= 0 ? vreg[u] : zero_;                                                                \
     }                                                                                               \
     const unsigned long long nb_ = __ballot(need_), ab_ = __ballot(any_);                           \
     if (lane == 0) { sneed[bi][w] = nb_ != 0; sany[bi][w] = ab_ != 0; }                             \
@@ -156,23 +160,20 @@ __global__ void __launch_bounds__(64 * NH * QH) k_prefill_mfma(AttnArgs a) {
   // issue the loads of the tile whose positions are in pk / pv
 #define DSA_LOAD_TILE()                                                                             \
   do {                                                                                              \
-    _Pragma("unroll") for (int u = 0; u < KPER; ++u) kreg[u] =                                      \
-        *reinterpret_cast<const u32x4_t*>(K + (kvbase + max(pk[u], 0)) * D + kpiece_of(u) * 8);     \
-    _Pragma("unroll") for (int u = 0; u < VPER; ++u) vreg[u] =                                      \
-        *reinterpret_cast<const u32x4_t*>(V + (kvbase + max(pv[u], 0)) * D + vpiece_of(u) * 8);     \
+    _Pragma("unroll") for (int u = 0; u < KPER; ++u) {                                              \
+      const size_t off_ = (kvbase + max(pk[u], 0)) * D + kpiece_of(u) * 8;                          \
+      kreg[u] = *reinterpret_cast<const u32x4_t*>(K + off_);                                        \
+      vreg[u] = *reinterpret_cast<const u32x4_t*>(V + off_);                                        \
+    }                                                                                               \
   } while (0)
 
   // prologue: tile 0 staged in buffer 0, tile 1 in flight, positions of tile 2
 #pragma unroll
   for (int u = 0; u < KPER; ++u) { pk[u] = entry(krow_of(u)); pkn[u] = entry(64 + krow_of(u)); }
-#pragma unroll
-  for (int u = 0; u < VPER; ++u) { pv[u] = entry(vkey_of(u)); pvn[u] = entry(64 + vkey_of(u)); }
   DSA_LOAD_TILE();
   DSA_STAGE_TILE(0);
 #pragma unroll
   for (int u = 0; u < KPER; ++u) { pk[u] = pkn[u]; pkn[u] = entry(128 + krow_of(u)); }
-#pragma unroll
-  for (int u = 0; u < VPER; ++u) { pv[u] = pvn[u]; pvn[u] = entry(128 + vkey_of(u)); }
   if (n_tiles > 1) DSA_LOAD_TILE();
   __syncthreads();
 
@@ -187,7 +188,7 @@ __global__ void __launch_bounds__(64 * NH * QH) k_prefill_mfma(AttnArgs a) {
     flag = __builtin_amdgcn_readfirstlane(flag);   // uniform: scalar branches below
     if (!(flag & 2)) {
       const uint16_t* skc = sk[cur];
-      const uint16_t* svc = svt[cur];
+      const uint16_t* svc = sv[cur];
       // S^T tiles [key tile kt]: 32 keys x this wave's 32 queries
       f32x16_t sacc[2];
 #pragma unroll
@@ -261,11 +262,13 @@ __global__ void __launch_bounds__(64 * NH * QH) k_prefill_mfma(AttnArgs a) {
         const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, u);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const uint16_t* vr = svc + (dt * 32 + l32) * VROW + ks * 16 + hi * 4;
-          const uint2 lo4 = *reinterpret_cast<const uint2*>(vr);
-          const uint2 hi4 = *reinterpret_cast<const uint2*>(vr + 8);
-          const u32x4_t w4 = {lo4.x, lo4.y, hi4.x, hi4.y};
-          const bf16x8_t av = __builtin_bit_cast(bf16x8_t, w4);
+          // A operand V^T: lane (hi, n) takes d-row dt*32+n at keys
+          // ks*16 + hi*4 + 0..3 and ks*16 + 8 + hi*4 + 0..3, matching P^T
+          const uint16_t* vr = svc + (ks * 16 + hi * 4 + tr_row) * VROW + dt * 32 + tr_col;
+          const i16x4_t lo4 = lds_read_tr16(vr);
+          const i16x4_t hi4 = lds_read_tr16(vr + 8 * VROW);
+          const bf16x8_t av = __builtin_bit_cast(
+              bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
           o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb, o[dt], 0, 0, 0);
         }
       }
@@ -277,8 +280,6 @@ __global__ void __launch_bounds__(64 * NH * QH) k_prefill_mfma(AttnArgs a) {
       if (ti + 2 < n_tiles) {
 #pragma unroll
         for (int u = 0; u < KPER; ++u) { pk[u] = pkn[u]; pkn[u] = entry((ti + 3) * 64 + krow_of(u)); }
-#pragma unroll
-        for (int u = 0; u < VPER; ++u) { pv[u] = pvn[u]; pvn[u] = entry((ti + 3) * 64 + vkey_of(u)); }
         DSA_LOAD_TILE();
       }
     }
