@@ -103,7 +103,7 @@ PruneLayout prune_layout(const dsa_shape* s, const dsa_params* p) {
   L.off_cnt = 0;
   L.off_starts = align256(L.off_cnt + static_cast<size_t>(L.R) * dsa::kMaxStages * 4);
   L.off_scores = align256(L.off_starts + 2 * static_cast<size_t>(L.R) * maxK * 4);
-  L.bytes = align256(L.off_scores + static_cast<size_t>(L.R) * maxNC * 4);
+  L.bytes = align256(L.off_scores + 2 * static_cast<size_t>(L.R) * L.maxNC * 4);   // two score lists
   return L;
 }
 

@@ -60,7 +60,7 @@ __global__ void __launch_bounds__(64 * NH * QH) k_prefill_mfma(AttnArgs a) {
   constexpr int DT = D / 32;          // 32-row tiles of O^T
   constexpr int PPR = D / 8;          // 16-byte pieces per key row
   constexpr int KROW = D + 8;         // K tile row stride (bf16 elements)
-  constexpr int VROW = D + 16;        // V tile row stride: 4 rows of a transpose read hit disjoint banks
+  constexpr int VROW = D + 32;        // V tile row stride: the 4 rows x 2 groups of a transpose read hit 64 distinct banks
   constexpr int KPER = 64 * PPR / NT; // K (and V) pieces per thread per tile
   static_assert(KPER >= 1 && (64 * PPR) % NT == 0, "tile loads must split evenly");
   // two tile buffers: tile i is computed from one while tile i+1 is written

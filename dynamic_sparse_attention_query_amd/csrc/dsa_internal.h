@@ -42,7 +42,7 @@ struct PruneArgs {
   int n1max;                 // most stage-1 chunks of any row
   int32_t* cnt;              // [R, kMaxStages] chunks kept by each stage
   int32_t* starts;           // [2, R, maxK] chunk starts, ping-pong by stage parity
-  uint32_t* scores;          // [R, maxNC] orderable chunk-score keys
+  uint32_t* scores;          // [2, R, maxNC] orderable chunk-score keys, by stage parity
   unsigned long long* visited;  // [n_stages] or nullptr
 };
 

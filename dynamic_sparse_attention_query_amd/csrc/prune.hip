@@ -15,6 +15,8 @@
 // own kernel, one workgroup per row.
 // Every chunk of every stage is a contiguous run of positions: stage 1 tiles
 // [n_sink, mid_hi) and each later chunk size divides the previous one.
+#include <algorithm>
+
 #include "prune_common.h"
 
 namespace dsa {
@@ -34,79 +36,64 @@ __device__ __forceinline__ uint32_t wave_or_u32(uint32_t v) {
   return static_cast<uint32_t>(wave_reduce_int(static_cast<int>(v), [](int x, int y) { return x | y; }));
 }
 
-// One workgroup per row. Thread t holds the keys of chunks j = t*E .. t*E+E-1
-// in registers (index order = thread order, so one block-wide scan ranks
-// everything). The K-th largest key is found by radix selection over the bits
-// that vary across the row: 8-bit digits from the most significant varying
-// bit down, each pass a per-wave LDS histogram of the keys still tied with the
-// prefix chosen so far, scanned by one wave. A pass stops the search as soon
-// as the boundary digit's keys are all kept. Keys above the threshold are
-// kept, plus the lowest-index keys equal to it until K are kept; a kept
-// chunk's output slot is the number of kept chunks of lower index.
+// LDS of one row's top-K selection
+struct SelectLds {
+  uint32_t hist[2][kTopkWaves][256];
+  uint32_t sred[2][kTopkWaves];
+  uint32_t sscan[kTopkWaves];
+  int sdec[3];
+};
+
+// This thread's keys: chunks j0 .. j0+E-1 of row r's score list of `stage` (read within
+// the row for every j0 of the launch; the selection masks j >= nc).
 template <int E>
-__global__ void __launch_bounds__(kTopkThreads) k_topk(PruneArgs a, int stage) {
+__device__ __forceinline__ void load_keys(const PruneArgs& a, int stage, int r, int j0, uint32_t (&key)[E]) {
   static_assert(E % 4 == 0, "keys are loaded four at a time");
-  __shared__ uint32_t hist[2][kTopkWaves][256];
-  __shared__ int sprev[kMaxKeptChunks];
-  __shared__ int ssel[kMaxKeptChunks];             // final stage: kept starts in output order
-  __shared__ uint32_t sred[2][kTopkWaves];
-  __shared__ uint32_t sscan[kTopkWaves];
-  __shared__ int sdec[3];
+  const uint4* sc4 = reinterpret_cast<const uint4*>(stage_scores(a, stage, r));
+  const int nv = a.maxNC >> 2;
+#pragma unroll
+  for (int v = 0; v < E / 4; ++v) {
+    const uint4 u = sc4[min((j0 >> 2) + v, nv - 1)];
+    key[4 * v + 0] = u.x; key[4 * v + 1] = u.y; key[4 * v + 2] = u.z; key[4 * v + 3] = u.w;
+  }
+}
 
-  const int r = blockIdx.x;
+// The kept starts of stage `stage` for row r (at most keep/chunk of them)
+// into LDS; published by the caller's next barrier.
+__device__ __forceinline__ void load_kept_starts(const PruneArgs& a, int stage, int r, int* sp) {
+  const int tid = threadIdx.x;
+  const int kmax = a.keep[stage] >> a.lchunk[stage];
+  const int32_t* src = a.starts + static_cast<size_t>(stage & 1) * a.R * a.maxK + static_cast<size_t>(r) * a.maxK;
+  for (int i0 = 0; i0 < kmax; i0 += 4 * kTopkThreads) {
+    int v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * kTopkThreads + tid;
+      v[u] = i < kmax ? src[i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * kTopkThreads + tid;
+      if (i < kmax) sp[i] = v[u];
+    }
+  }
+}
+
+// Top-K of one row, run by all kTopkThreads threads of the workgroup. Thread
+// t holds the keys of chunks j = t*E .. t*E+E-1 in registers (index order =
+// thread order, so one block-wide scan ranks everything). The K-th largest
+// key is found by radix selection over the bits that vary across the row:
+// 8-bit digits from the most significant varying bit down, each pass a
+// per-wave LDS histogram of the keys still tied with the prefix chosen so
+// far, scanned by one wave. A pass stops the search as soon as the boundary
+// digit's keys are all kept. Keys above the threshold are kept, plus the
+// lowest-index keys equal to it until K are kept; emit(j, pos) is called for
+// every kept chunk j with its output slot pos = the number of kept chunks of
+// lower index. With nc <= kc every chunk j < nc is kept at slot j.
+template <int E, typename Emit>
+__device__ __forceinline__ void select_row(uint32_t (&key)[E], int j0, int nc, int kc, SelectLds& L,
+                                           Emit&& emit) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  int b, s, e;
-  row_bounds(a.kv, r, b, s, e);
-  const Geo geo = make_geo(s, e, a.n_sink, a.n_window, a.chunk[0]);
-  const int lg = a.lchunk[stage], l = 1 << lg;
-  const int kc = a.keep[stage] >> lg;
-  const bool last = stage == a.n_stages - 1;
-  const int nc = stage_input_chunks(a, stage, r, geo);
-
-  // all loads up front: this thread's keys (clamped into the row; masked by
-  // nc below) and the previous stage's kept starts
-  const int j0 = tid * E;
-  uint32_t key[E];
-  {
-    const uint4* sc4 = reinterpret_cast<const uint4*>(a.scores + static_cast<size_t>(r) * a.maxNC);
-    const int nv = a.maxNC >> 2;
-#pragma unroll
-    for (int v = 0; v < E / 4; ++v) {
-      const uint4 u = sc4[min((j0 >> 2) + v, nv - 1)];
-      key[4 * v + 0] = u.x; key[4 * v + 1] = u.y; key[4 * v + 2] = u.z; key[4 * v + 3] = u.w;
-    }
-  }
-  int sh = 0;
-  if (stage > 0) {
-    sh = a.lchunk[stage - 1] - lg;
-    const int kprev = a.keep[stage - 1] >> a.lchunk[stage - 1];
-    const int32_t* prev =
-        a.starts + static_cast<size_t>((stage - 1) & 1) * a.R * a.maxK + static_cast<size_t>(r) * a.maxK;
-    for (int i0 = 0; i0 < kprev; i0 += 4 * kTopkThreads) {
-      int v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = i0 + u * kTopkThreads + tid;
-        v[u] = i < kprev ? prev[i] : 0;
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = i0 + u * kTopkThreads + tid;
-        if (i < kprev) sprev[i] = v[u];
-      }
-    }
-  }
-  const bool keep_all = nc <= kc;
-  const int n_sel = keep_all ? nc : kc;
-  int32_t* out = a.starts + static_cast<size_t>(stage & 1) * a.R * a.maxK + static_cast<size_t>(r) * a.maxK;
-  int32_t* row = a.idx + static_cast<size_t>(r) * a.L;
-  // kept chunk j lands in output slot pos
-  auto emit = [&](int j, int pos) {
-    const int st = stage == 0 ? a.n_sink + (j << lg) : sprev[j >> sh] + ((j & ((1 << sh) - 1)) << lg);
-    out[pos] = st;
-    if (last) ssel[pos] = st;
-  };
-
   // common bits of the row's keys (0 marks chunks beyond nc: real keys are
   // never 0); the histograms are cleared under the same barrier
   uint32_t vand = 0xffffffffu, vor = 0u;
@@ -117,23 +104,20 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk(PruneArgs a, int stage) {
   }
   vand = wave_and_u32(vand);
   vor = wave_or_u32(vor);
-  if (lane == 0) { sred[0][w] = vand; sred[1][w] = vor; }
+  if (lane == 0) { L.sred[0][w] = vand; L.sred[1][w] = vor; }
   {
-    uint32_t* h = &hist[0][0][0];
+    uint32_t* h = &L.hist[0][0][0];
 #pragma unroll
     for (int i = 0; i < 2 * kTopkWaves * 256 / kTopkThreads; ++i) h[i * kTopkThreads + tid] = 0u;
   }
-  __syncthreads();                                 // also publishes sprev
-  // stores only after every load has been consumed: stores share the vector
-  // memory counter with loads, so an earlier store would hold up their wait
-  if (tid == 0) a.cnt[r * kMaxStages + stage] = n_sel;
-  if (keep_all) {
+  __syncthreads();                                 // also publishes the caller's LDS data
+  if (nc <= kc) {                                  // every chunk is kept, in index order
     for (int j = j0; j < min(j0 + E, nc); ++j) emit(j, j);
   } else {
     vand = 0xffffffffu;
     vor = 0u;
 #pragma unroll
-    for (int i = 0; i < kTopkWaves; ++i) { vand &= sred[0][i]; vor |= sred[1][i]; }
+    for (int i = 0; i < kTopkWaves; ++i) { vand &= L.sred[0][i]; vor |= L.sred[1][i]; }
     const uint32_t varying = vand ^ vor;
 
     // radix passes: bits [shift, 32) of the threshold are decided
@@ -146,9 +130,9 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk(PruneArgs a, int stage) {
       shift -= wd;
       const uint32_t himask = shift + wd >= 32 ? 0u : (~0u << (shift + wd));
       const uint32_t dmask = (1u << wd) - 1u;
-      uint32_t (*H)[256] = hist[p & 1];
+      uint32_t (*H)[256] = L.hist[p & 1];
       {
-        uint32_t* h = &hist[(p + 1) & 1][0][0];      // next pass's buffer, idle since the last scan
+        uint32_t* h = &L.hist[(p + 1) & 1][0][0];      // next pass's buffer, idle since the last scan
 #pragma unroll
         for (int i = 0; i < kTopkWaves * 256 / kTopkThreads; ++i) h[i * kTopkThreads + tid] = 0u;
       }
@@ -177,9 +161,9 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk(PruneArgs a, int stage) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             if (run + c[i] >= static_cast<uint32_t>(need)) {
-              sdec[0] = 255 - (4 * lane + i);
-              sdec[1] = need - static_cast<int>(run);
-              sdec[2] = static_cast<int>(c[i]);
+              L.sdec[0] = 255 - (4 * lane + i);
+              L.sdec[1] = need - static_cast<int>(run);
+              L.sdec[2] = static_cast<int>(c[i]);
               break;
             }
             run += c[i];
@@ -187,9 +171,9 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk(PruneArgs a, int stage) {
         }
       }
       __syncthreads();
-      prefix |= static_cast<uint32_t>(sdec[0]) << shift;
-      need = sdec[1];
-      if (sdec[2] == need) { whole = true; break; }
+      prefix |= static_cast<uint32_t>(L.sdec[0]) << shift;
+      need = L.sdec[1];
+      if (L.sdec[2] == need) { whole = true; break; }
     }
 
     // kept: key > tau, or key == tau among the first need_eq such keys; with a
@@ -213,12 +197,12 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk(PruneArgs a, int stage) {
 #pragma unroll
     for (int m = 0; m < NM; ++m) cnt += (static_cast<uint32_t>(__popc(sm[m])) << 16) + __popc(em[m]);
     const uint32_t inc = wave_incl_scan_u32(cnt);
-    if (lane == 63) sscan[w] = inc;
+    if (lane == 63) L.sscan[w] = inc;
     __syncthreads();
     uint32_t base = inc - cnt;
 #pragma unroll
     for (int i = 0; i < kTopkWaves; ++i)
-      if (i < w) base += sscan[i];
+      if (i < w) base += L.sscan[i];
     int cs = static_cast<int>(base >> 16), ce = static_cast<int>(base & 0xffffu);
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
@@ -234,6 +218,44 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk(PruneArgs a, int stage) {
       ce += __popc(em[m]);
     }
   }
+}
+
+// One workgroup per row: select the stage's kept chunks, write their starts
+// (and their count), and after the last stage the index row.
+template <int E>
+__global__ void __launch_bounds__(kTopkThreads) k_topk(PruneArgs a, int stage) {
+  __shared__ SelectLds L;
+  __shared__ int sprev[kMaxKeptChunks];
+  __shared__ int ssel[kMaxKeptChunks];             // final stage: kept starts in output order
+
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  int b, s, e;
+  row_bounds(a.kv, r, b, s, e);
+  const Geo geo = make_geo(s, e, a.n_sink, a.n_window, a.chunk[0]);
+  const int lg = a.lchunk[stage], l = 1 << lg;
+  const int kc = a.keep[stage] >> lg;
+  const bool last = stage == a.n_stages - 1;
+  const int nc = stage_input_chunks(a, stage, r, geo);
+
+  // all loads up front: this thread's keys and the previous stage's kept starts
+  const int j0 = tid * E;
+  uint32_t key[E];
+  load_keys<E>(a, stage, r, j0, key);
+  const int sh = stage > 0 ? a.lchunk[stage - 1] - lg : 0;
+  if (stage > 0) load_kept_starts(a, stage - 1, r, sprev);
+  const int n_sel = nc <= kc ? nc : kc;
+  int32_t* out = a.starts + static_cast<size_t>(stage & 1) * a.R * a.maxK + static_cast<size_t>(r) * a.maxK;
+  int32_t* row = a.idx + static_cast<size_t>(r) * a.L;
+  // stores only after every load has been consumed (inside the selection):
+  // stores share the vector memory counter with loads, so an earlier store
+  // would hold up their wait
+  select_row<E>(key, j0, nc, kc, L, [&](int j, int pos) {
+    const int st = stage == 0 ? a.n_sink + (j << lg) : sprev[j >> sh] + ((j & ((1 << sh) - 1)) << lg);
+    out[pos] = st;
+    if (last) ssel[pos] = st;
+  });
+  if (tid == 0) a.cnt[r * kMaxStages + stage] = n_sel;
   if (!last) return;
 
   // final stage: the index row (sinks, kept chunks, window, -1 padding) in
@@ -259,6 +281,119 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk(PruneArgs a, int stage) {
 // ------------------------------------------------------------------------- //
 // decode scoring: one query per row                                         //
 // ------------------------------------------------------------------------- //
+// One lane group's SelectRep tournaments: the G query heads of kv head g over
+// the chunk of l = chunk[stage] keys starting at st; returns the best
+// representative score over the heads.
+template <typename T, int D, int G, bool SPEC>
+__device__ __forceinline__ float score_group(const PruneArgs& a, int stage, int b, int g, int li, int st,
+                                             const RowSlice<T, D / 16> (&q)[G]) {
+  constexpr int EPL = D / 16;
+  using Row = RowSlice<T, EPL>;
+  const KvLayout& kv = a.kv;
+  const T* K = static_cast<const T*>(a.k);
+  const int l = a.chunk[stage];
+  float best = -INFINITY;
+  auto dot = [&](const Row& kr, int hh) { return group16_sum(kr.dot(q[hh])); };
+  auto row_at = [&](int pos) {
+    Row x;
+    x.load(K + kv_offset(kv, b, g, pos) + li * EPL);
+    return x;
+  };
+
+  float sa[G];
+  int lo[G], hi[G];
+  unsigned long long nvis = 0;
+  int width;                                   // size of every head's remaining range
+  if (l == 1) {
+    const Row k0 = row_at(st);
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) { sa[hh] = dot(k0, hh); lo[hh] = hi[hh] = 0; }
+    nvis = 1;
+    width = 1;
+  } else if (SPEC && l >= 8) {
+    const int u = l >> 3;
+    float sc8[G][8];
+    {
+      Row kr[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) kr[i] = row_at(st + i * u);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) sc8[hh][i] = dot(kr[i], hh);
+    }
+    int a1[G], a2[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      int A = 0;
+      float s0 = sc8[hh][0];
+      if (sc8[hh][4] > s0) { A = 4; s0 = sc8[hh][4]; }
+      a1[hh] = A;
+      const float s2 = A ? sc8[hh][6] : sc8[hh][2];
+      if (s2 > s0) { A += 2; s0 = s2; }
+      a2[hh] = A;
+      const float s3 = A == 0 ? sc8[hh][1] : A == 2 ? sc8[hh][3] : A == 4 ? sc8[hh][5] : sc8[hh][7];
+      if (s3 > s0) { A += 1; s0 = s3; }
+      lo[hh] = A * u;
+      hi[hh] = A * u + u - 1;
+      sa[hh] = s0;
+    }
+    if (a.visited) {
+      nvis = 2;                                 // split 1: keys 0 and l/2
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {          // splits 2 and 3: distinct midpoints
+        bool f2 = true, f3 = true;
+#pragma unroll
+        for (int h2 = 0; h2 < hh; ++h2) {
+          f2 = f2 && (a1[h2] != a1[hh]);
+          f3 = f3 && (a2[h2] != a2[hh]);
+        }
+        nvis += (f2 ? 1 : 0) + (f3 ? 1 : 0);
+      }
+    }
+    width = u;
+  } else {
+    const int mid0 = l >> 1;
+    const Row k0 = row_at(st), k1 = row_at(st + mid0);
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const float a0 = dot(k0, hh), a1 = dot(k1, hh);
+      if (a1 > a0) { lo[hh] = mid0; hi[hh] = l - 1; sa[hh] = a1; }
+      else         { lo[hh] = 0;    hi[hh] = mid0 - 1; sa[hh] = a0; }
+    }
+    nvis = 2;
+    width = mid0;
+  }
+  for (int wdt = width >> 1; wdt >= 1; wdt >>= 1) {   // remaining splits
+    Row kk[G];
+    int mid[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      mid[hh] = (lo[hh] + hi[hh] + 1) >> 1;
+      kk[hh] = row_at(st + mid[hh]);
+    }
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const float acc = dot(kk[hh], hh);
+      if (acc > sa[hh]) { lo[hh] = mid[hh]; sa[hh] = acc; }
+      else              { hi[hh] = mid[hh] - 1; }
+    }
+    if (a.visited) {
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        bool fresh = true;
+#pragma unroll
+        for (int h2 = 0; h2 < hh; ++h2) fresh = fresh && (mid[h2] != mid[hh]);
+        nvis += fresh ? 1 : 0;
+      }
+    }
+  }
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) best = fmaxf(best, sa[hh]);
+  if (a.visited && li == 0) atomicAdd(a.visited + stage, nvis);
+  return best;
+}
+
 // Workgroup = 16 lane groups of 16 lanes; a group owns one (chunk, kv head)
 // and runs the G SelectRep tournaments of that kv head's query heads side by
 // side, so each step issues G independent 16-lane row loads (256 B per row at
@@ -282,7 +417,6 @@ k_score_decode(PruneArgs a, int stage) {
   const int cl = gi / kv.Hkv, g = gi - cl * kv.Hkv;
   const int j = j0 + cl;
   const int l = a.chunk[stage];
-  const T* K = static_cast<const T*>(a.k);
   const T* Q = static_cast<const T*>(a.q);
   __shared__ float red[16];
 
@@ -312,106 +446,7 @@ k_score_decode(PruneArgs a, int stage) {
   const bool active = j < nc;
 
   float best = -INFINITY;
-  if (active) {
-    auto dot = [&](const Row& kr, int hh) { return group16_sum(kr.dot(q[hh])); };
-    auto row_at = [&](int pos) {
-      Row x;
-      x.load(K + kv_offset(kv, b, g, pos) + li * EPL);
-      return x;
-    };
-
-    float sa[G];
-    int lo[G], hi[G];
-    unsigned long long nvis = 0;
-    int width;                                   // size of every head's remaining range
-    if (l == 1) {
-      const Row k0 = row_at(st);
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) { sa[hh] = dot(k0, hh); lo[hh] = hi[hh] = 0; }
-      nvis = 1;
-      width = 1;
-    } else if (SPEC && l >= 8) {
-      const int u = l >> 3;
-      float sc8[G][8];
-      {
-        Row kr[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) kr[i] = row_at(st + i * u);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-          for (int hh = 0; hh < G; ++hh) sc8[hh][i] = dot(kr[i], hh);
-      }
-      int a1[G], a2[G];
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        int A = 0;
-        float s0 = sc8[hh][0];
-        if (sc8[hh][4] > s0) { A = 4; s0 = sc8[hh][4]; }
-        a1[hh] = A;
-        const float s2 = A ? sc8[hh][6] : sc8[hh][2];
-        if (s2 > s0) { A += 2; s0 = s2; }
-        a2[hh] = A;
-        const float s3 = A == 0 ? sc8[hh][1] : A == 2 ? sc8[hh][3] : A == 4 ? sc8[hh][5] : sc8[hh][7];
-        if (s3 > s0) { A += 1; s0 = s3; }
-        lo[hh] = A * u;
-        hi[hh] = A * u + u - 1;
-        sa[hh] = s0;
-      }
-      if (a.visited) {
-        nvis = 2;                                 // split 1: keys 0 and l/2
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) {          // splits 2 and 3: distinct midpoints
-          bool f2 = true, f3 = true;
-#pragma unroll
-          for (int h2 = 0; h2 < hh; ++h2) {
-            f2 = f2 && (a1[h2] != a1[hh]);
-            f3 = f3 && (a2[h2] != a2[hh]);
-          }
-          nvis += (f2 ? 1 : 0) + (f3 ? 1 : 0);
-        }
-      }
-      width = u;
-    } else {
-      const int mid0 = l >> 1;
-      const Row k0 = row_at(st), k1 = row_at(st + mid0);
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        const float a0 = dot(k0, hh), a1 = dot(k1, hh);
-        if (a1 > a0) { lo[hh] = mid0; hi[hh] = l - 1; sa[hh] = a1; }
-        else         { lo[hh] = 0;    hi[hh] = mid0 - 1; sa[hh] = a0; }
-      }
-      nvis = 2;
-      width = mid0;
-    }
-    for (int wdt = width >> 1; wdt >= 1; wdt >>= 1) {   // remaining splits
-      Row kk[G];
-      int mid[G];
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        mid[hh] = (lo[hh] + hi[hh] + 1) >> 1;
-        kk[hh] = row_at(st + mid[hh]);
-      }
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        const float acc = dot(kk[hh], hh);
-        if (acc > sa[hh]) { lo[hh] = mid[hh]; sa[hh] = acc; }
-        else              { hi[hh] = mid[hh] - 1; }
-      }
-      if (a.visited) {
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-          bool fresh = true;
-#pragma unroll
-          for (int h2 = 0; h2 < hh; ++h2) fresh = fresh && (mid[h2] != mid[hh]);
-          nvis += fresh ? 1 : 0;
-        }
-      }
-    }
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) best = fmaxf(best, sa[hh]);
-    if (a.visited && li == 0) atomicAdd(a.visited + stage, nvis);
-  }
+  if (active) best = score_group<T, D, G, SPEC>(a, stage, b, g, li, st, q);
   if (li == 0) red[gi] = best;
   __syncthreads();
   if (tid < cpw) {
@@ -419,7 +454,81 @@ k_score_decode(PruneArgs a, int stage) {
     if (jj < nc) {
       float m = red[tid * kv.Hkv];
       for (int x = 1; x < kv.Hkv; ++x) m = fmaxf(m, red[tid * kv.Hkv + x]);
-      a.scores[static_cast<size_t>(r) * a.maxNC + jj] = score_key(m);
+      stage_scores(a, stage, r)[jj] = score_key(m);
+    }
+  }
+}
+
+// Top-K of stage `stage - 1` fused with the SelectRep scoring of stage `stage`
+// (decode, bf16). Every workgroup of the scoring launch selects the row's kept
+// chunks of the previous stage itself from that stage's complete score list,
+// so the two steps meet at one kernel boundary instead of two; workgroup 0
+// also writes the kept starts and their count for the stages after. The
+// tournaments are those of k_score_decode.
+template <typename T, int D, int G, bool SPEC, int E>
+__global__ void __launch_bounds__(256, 2) k_topk_score_decode(PruneArgs a, int stage) {
+  constexpr int EPL = D / 16;
+  using Row = RowSlice<T, EPL>;
+  __shared__ SelectLds L;
+  __shared__ int sprev[kMaxKeptChunks];
+  __shared__ int ssel[kMaxKeptChunks];
+  __shared__ float red[16];
+  const KvLayout& kv = a.kv;
+  const int ps = stage - 1;                     // the stage selected here
+  const int r = blockIdx.y, b = r;              // one row per sequence
+  const int cpw = 16 / kv.Hkv;                  // chunks per workgroup
+  const int j0 = blockIdx.x * cpw;
+  const int tid = threadIdx.x;
+  const int gi = tid >> 4, li = tid & 15;
+  const int cl = gi / kv.Hkv, g = gi - cl * kv.Hkv;
+  const T* Q = static_cast<const T*>(a.q);
+
+  // independent loads first: sequence length, the count before stage ps,
+  // this thread's keys of stage ps, the kept starts of stage ps-1, the query
+  const int e = kv.seq_lens[r];
+  const int nc_before = ps > 0 ? a.cnt[r * kMaxStages + ps - 1] : 0;
+  const int js = tid * E;
+  uint32_t key[E];
+  load_keys<E>(a, ps, r, js, key);
+  if (ps > 0) load_kept_starts(a, ps - 1, r, sprev);
+  Row q[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) q[hh].load(Q + (static_cast<size_t>(b) * kv.Hq + g * G + hh) * D + li * EPL);
+
+  const Geo geo = make_geo(e - 1, e, a.n_sink, a.n_window, a.chunk[0]);
+  const int lgp = a.lchunk[ps];
+  const int shp = ps > 0 ? a.lchunk[ps - 1] - lgp : 0;
+  const int nc_ps = ps == 0 ? geo.n1 : nc_before << shp;
+  const int kc_ps = a.keep[ps] >> lgp;
+  const int n_sel = nc_ps <= kc_ps ? nc_ps : kc_ps;
+  const bool writer = blockIdx.x == 0;
+  int32_t* out = a.starts + static_cast<size_t>(ps & 1) * a.R * a.maxK + static_cast<size_t>(r) * a.maxK;
+  select_row<E>(key, js, nc_ps, kc_ps, L, [&](int j, int pos) {
+    const int st = ps == 0 ? a.n_sink + (j << lgp) : sprev[j >> shp] + ((j & ((1 << shp) - 1)) << lgp);
+    ssel[pos] = st;
+    if (writer) out[pos] = st;
+  });
+  if (writer && tid == 0) a.cnt[r * kMaxStages + ps] = n_sel;
+  __syncthreads();                              // the kept starts are in ssel
+
+  // stage `stage`: chunks of chunk[stage] keys tiling the kept chunks
+  const int sh = lgp - a.lchunk[stage];
+  const int nc = n_sel << sh;
+  if (nc <= (a.keep[stage] >> a.lchunk[stage])) return;   // stage keeps everything for this row
+  if (j0 >= nc) return;
+  const int j = j0 + cl;
+  const bool active = j < nc;
+  const int st = ssel[min(j >> sh, n_sel - 1)] + ((j & ((1 << sh) - 1)) << a.lchunk[stage]);
+  float best = -INFINITY;
+  if (active) best = score_group<T, D, G, SPEC>(a, stage, b, g, li, st, q);
+  if (li == 0) red[gi] = best;
+  __syncthreads();
+  if (tid < cpw) {
+    const int jj = j0 + tid;
+    if (jj < nc) {
+      float m = red[tid * kv.Hkv];
+      for (int x = 1; x < kv.Hkv; ++x) m = fmaxf(m, red[tid * kv.Hkv + x]);
+      stage_scores(a, stage, r)[jj] = score_key(m);
     }
   }
 }
@@ -499,7 +608,7 @@ __global__ void __launch_bounds__(256) k_score_prefill(PruneArgs a, int stage) {
     best = fmaxf(best, sa);
   }
   (void)nvis;
-  if (active && li == 0) a.scores[static_cast<size_t>(r) * a.maxNC + j] = score_key(best);
+  if (active && li == 0) stage_scores(a, stage, r)[j] = score_key(best);
 }
 
 // ------------------------------------------------------------------------- //
@@ -509,6 +618,8 @@ static const char* const kScoreNames[kMaxStages] = {"prune_score_stage1", "prune
                                                     "prune_score_stage3", "prune_score_stage4"};
 static const char* const kTopkNames[kMaxStages] = {"prune_topk_stage1", "prune_topk_stage2",
                                                    "prune_topk_stage3", "prune_topk_stage4"};
+static const char* const kFusedNames[kMaxStages] = {"", "prune_topk1_score2", "prune_topk2_score3",
+                                                    "prune_topk3_score4"};
 constexpr int kSpecMaxChunk = 64;       // chunks this small preload their first three splits
 
 template <typename T, int D, int G>
@@ -536,29 +647,72 @@ static void launch_topk(const PruneArgs& a, int stage, int max_chunks, hipStream
   }
 }
 
+// Top-K of stage-1 and scoring of `stage` in one launch (bf16 decode, at most
+// 4096 chunks in the selected stage); false if this shape takes the separate
+// kernels.
+template <typename T, int D, int G>
+static bool launch_decode_fused(const PruneArgs& a, int stage, int max_chunks, int sel_chunks,
+                                hipStream_t st) {
+  if constexpr (sizeof(T) != 2) {
+    return false;
+  } else {
+    const int cpw = 16 / a.kv.Hkv;
+    // at least one workgroup: workgroup 0 writes the selected stage's starts
+    const dim3 grid(std::max(1, (max_chunks + cpw - 1) / cpw), a.R);
+    const bool spec = a.chunk[stage] >= 8 && a.chunk[stage] <= kSpecMaxChunk;
+    const char* nm = kFusedNames[stage];
+    if (sel_chunks <= kTopkThreads * 4) {
+      if (spec) DSA_LAUNCH(nm, (k_topk_score_decode<T, D, G, true, 4>), grid, dim3(256), st, a, stage);
+      else      DSA_LAUNCH(nm, (k_topk_score_decode<T, D, G, false, 4>), grid, dim3(256), st, a, stage);
+    } else if (sel_chunks <= kTopkThreads * 16) {
+      if (spec) DSA_LAUNCH(nm, (k_topk_score_decode<T, D, G, true, 16>), grid, dim3(256), st, a, stage);
+      else      DSA_LAUNCH(nm, (k_topk_score_decode<T, D, G, false, 16>), grid, dim3(256), st, a, stage);
+    } else {
+      return false;
+    }
+    return true;
+  }
+}
+
+// Decode: score stage 1; for every later stage, the previous stage's top-K
+// and this stage's scoring (fused where possible); the last top-K writes idx.
+template <typename T, int D, int G>
+static void launch_decode(const PruneArgs& a, hipStream_t st) {
+  auto chunks_of = [&](int stage) {               // longest input list of a stage
+    return stage == 0 ? a.n1max : a.keep[stage - 1] / a.chunk[stage];
+  };
+  launch_decode_score<T, D, G>(a, 0, chunks_of(0), st);
+  for (int stage = 1; stage < a.n_stages; ++stage) {
+    if (!launch_decode_fused<T, D, G>(a, stage, chunks_of(stage), chunks_of(stage - 1), st)) {
+      launch_topk(a, stage - 1, chunks_of(stage - 1), st);
+      launch_decode_score<T, D, G>(a, stage, chunks_of(stage), st);
+    }
+  }
+  launch_topk(a, a.n_stages - 1, chunks_of(a.n_stages - 1), st);
+}
+
 template <typename T, int D>
 static hipError_t launch_typed(const PruneArgs& a, hipStream_t st) {
   const int G = a.kv.Hq / a.kv.Hkv;
+  if (a.kv.decode) {
+    switch (G) {
+      case 1: launch_decode<T, D, 1>(a, st); break;
+      case 2: launch_decode<T, D, 2>(a, st); break;
+      case 4: launch_decode<T, D, 4>(a, st); break;
+      case 8: launch_decode<T, D, 8>(a, st); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   for (int stage = 0; stage < a.n_stages; ++stage) {
     // longest input list any row can present to this stage
     const int max_chunks = stage == 0 ? a.n1max : a.keep[stage - 1] / a.chunk[stage];
-    if (a.kv.decode) {
-      switch (G) {
-        case 1: launch_decode_score<T, D, 1>(a, stage, max_chunks, st); break;
-        case 2: launch_decode_score<T, D, 2>(a, stage, max_chunks, st); break;
-        case 4: launch_decode_score<T, D, 4>(a, stage, max_chunks, st); break;
-        case 8: launch_decode_score<T, D, 8>(a, stage, max_chunks, st); break;
-        default: return hipErrorInvalidValue;
-      }
-      launch_topk(a, stage, max_chunks, st);
-    } else {
-      if (max_chunks > 0 &&
-          !(sizeof(T) == 2 && launch_score_prefill_mfma(a, stage, max_chunks, st, kScoreNames[stage]))) {
-        dim3 grid((max_chunks + 15) / 16, a.R);
-        DSA_LAUNCH(kScoreNames[stage], (k_score_prefill<T, D>), grid, dim3(256), st, a, stage);
-      }
-      launch_topk(a, stage, max_chunks, st);
+    if (max_chunks > 0 &&
+        !(sizeof(T) == 2 && launch_score_prefill_mfma(a, stage, max_chunks, st, kScoreNames[stage]))) {
+      dim3 grid((max_chunks + 15) / 16, a.R);
+      DSA_LAUNCH(kScoreNames[stage], (k_score_prefill<T, D>), grid, dim3(256), st, a, stage);
     }
+    launch_topk(a, stage, max_chunks, st);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

@@ -205,7 +205,7 @@ __global__ void __launch_bounds__(256) k_score_prefill_mfma(PruneArgs a, int sta
   for (int c = tid; c < CPB; c += 256) {
     if (j0 + c < nc) {
       const float m = fmaxf(fmaxf(red[0][c], red[1][c]), fmaxf(red[2][c], red[3][c]));
-      a.scores[static_cast<size_t>(r) * a.maxNC + j0 + c] = score_key(m);
+      stage_scores(a, stage, r)[j0 + c] = score_key(m);
     }
   }
 }
