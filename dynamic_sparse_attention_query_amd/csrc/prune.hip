@@ -42,6 +42,10 @@ struct SelectLds {
   uint32_t sred[2][kTopkWaves];
   uint32_t sscan[kTopkWaves];
   int sdec[3];
+  int wcand[kTopkWaves];                         // small boundary digit: per-wave counts,
+  uint32_t ckey[kTopkWaves][64];                 // keys and chunk ids (each wave's share is
+  int cidx[kTopkWaves][64];                      // below 64: the digit holds at most 64 keys)
+  uint32_t sfin[2];
 };
 
 // This thread's keys: chunks j0 .. j0+E-1 of row r's score list of `stage` (read within
@@ -173,7 +177,56 @@ __device__ __forceinline__ void select_row(uint32_t (&key)[E], int j0, int nc, i
       __syncthreads();
       prefix |= static_cast<uint32_t>(L.sdec[0]) << shift;
       need = L.sdec[1];
-      if (L.sdec[2] == need) { whole = true; break; }
+      const int cd = L.sdec[2];
+      if (cd == need) { whole = true; break; }
+      if (shift > 0 && cd <= 64) {
+        // Few keys share the boundary digit: gather them and let one wave
+        // rank them exactly (score descending, chunk index ascending). The
+        // need-th of them is the threshold tau; keys above it are kept, and
+        // of the keys equal to it the lowest-index ones up to need.
+        const uint32_t hm = ~0u << shift;
+        int run = 0;                               // this wave's candidates so far (uniform)
+#pragma unroll
+        for (int x = 0; x < E; ++x) {
+          const uint32_t k = key[x];
+          const bool c = k != 0u && ((k ^ prefix) & hm) == 0u;
+          const unsigned long long cb = __ballot(c);
+          if (c) {
+            const int slot = run + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(cb >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(cb), 0));
+            L.ckey[w][slot] = k;
+            L.cidx[w][slot] = j0 + x;
+          }
+          run += __popcll(cb);
+        }
+        if (lane == 0) L.wcand[w] = run;
+        __syncthreads();
+        if (w == 0) {
+          // lane l takes candidate l of the waves' shares in wave order
+          int src_w = 0, src_i = lane;
+#pragma unroll
+          for (int ww = 0; ww < kTopkWaves - 1; ++ww)
+            if (src_w == ww && src_i >= L.wcand[ww]) { src_i -= L.wcand[ww]; src_w = ww + 1; }
+          const bool valid = lane < cd;
+          const uint32_t kl = valid ? L.ckey[src_w][src_i] : 0u;
+          const int il = valid ? L.cidx[src_w][src_i] : 0x7fffffff;
+          int rank = 0;
+          for (int m = 0; m < cd; ++m) {
+            const uint32_t km = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(kl), m));
+            const int im = __builtin_amdgcn_readlane(il, m);
+            rank += (km > kl || (km == kl && im < il)) ? 1 : 0;
+          }
+          const unsigned long long bm = __ballot(valid && rank == need - 1);
+          const uint32_t t = static_cast<uint32_t>(
+              __builtin_amdgcn_readlane(static_cast<int>(kl), __ffsll(static_cast<long long>(bm)) - 1));
+          const int ngt = __popcll(__ballot(valid && kl > t));
+          if (lane == 0) { L.sfin[0] = t; L.sfin[1] = need - ngt; }
+        }
+        __syncthreads();
+        prefix = L.sfin[0];                       // tau, every bit decided
+        need = static_cast<int>(L.sfin[1]);       // keys equal to tau to keep
+        break;
+      }
     }
 
     // kept: key > tau, or key == tau among the first need_eq such keys; with a
