@@ -98,6 +98,21 @@ def test_prefill_three_stages_full_array():
     assert torch.equal(out, out2)
 
 
+@pytest.mark.parametrize("hq,hkv,d,batch", [(8, 4, 64, 2), (4, 4, 128, 1), (16, 2, 128, 1)])
+def test_prefill_bf16_group_shapes(hq, hkv, d, batch):
+    """bf16 prefill on the matrix-core kernels for the other GQA group sizes
+    (2, 1, 8), head size 64 and a batch of two sequences."""
+    case = gen.make_case("c2", t=2048, hq=hq, hkv=hkv, d=d, batch=batch, keep=(512, 256, 128),
+                         n_window=128, n_needles=2)
+    H.say(f"bf16 prefill Hq={hq} Hkv={hkv} d={d} B={batch}")
+    dev = to_device(case)
+    p = params_of(case.cfg)
+    idx, out = gpu_prefill(dev, p)
+    nblk = case.cfg.t // case.cfg.block_q
+    for b in range(batch):
+        check_prefill_blocks(case, idx, out, range(nblk), attn_blocks=range(b, nblk, 7), b=b)
+
+
 def test_prefill_dense_matches_oracle():
     case = gen.make_case("c2", t=2048, n_needles=0)
     dev = to_device(case)
