@@ -304,6 +304,259 @@ __global__ void __launch_bounds__(64 * NH * QH) k_prefill_mfma(AttnArgs a) {
     }
 }
 
+// XOR swizzle of an unpadded 256-byte tile row: LDS slot s of row r holds the
+// row's 16-byte piece s ^ swz(r). Sixteen consecutive rows read at one piece
+// (the K fragments) and four consecutive rows read at four consecutive
+// pieces (the V^T transpose reads) both land in 16 distinct slots, i.e. all
+// 64 banks once.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// d = 128 variant of k_prefill_mfma whose K/V tiles go straight from global
+// memory into LDS (global_load_lds_dwordx4: a wave-wide load fills 1 KB of LDS
+// in lane order, here 4 swizzled rows), so no registers stage the tiles and
+// no LDS stores copy them. The loads of tile i+1 are issued after the barrier
+// that retires tile i-1 and run under tile i's products; invisible and
+// padding rows load key 0 and are removed by the mask.
+template <int NH, int QH>
+__global__ void __launch_bounds__(64 * NH * QH) k_prefill_mfma_lds(AttnArgs a) {
+  constexpr int D = 128;
+  constexpr int NWV = NH * QH;        // waves
+  constexpr int KS = D / 16;          // 16-wide steps over d
+  constexpr int DT = D / 32;          // 32-row tiles of O^T
+  constexpr int LPT = 64 / (4 * NWV); // wave-wide loads per tile and matrix (4 rows each)
+  static_assert(64 % (4 * NWV) == 0, "tile loads must split evenly");
+  // Two tile buffers as distinct objects, used alternately by the unrolled
+  // loop below: the compiler can then tell the reads of one buffer from the
+  // loads landing in the other and need not wait for those loads.
+  __shared__ __align__(16) uint16_t sk0[64 * D], sk1[64 * D];
+  __shared__ __align__(16) uint16_t sv0[64 * D], sv1[64 * D];
+  __shared__ __align__(16) int spos0[64], spos1[64];
+  __shared__ int sflag0[2][NWV], sflag1[2][NWV];
+  // the buffers are written only by the loads below: make that visible
+  asm volatile("" ::"r"(sk0), "r"(sk1), "r"(sv0), "r"(sv1) : "memory");
+
+  const KvLayout& kv = a.kv;
+  // XCD-aware order, as in k_prefill_mfma
+  const int G = kv.Hq / kv.Hkv;
+  const int HG = G / NH;
+  constexpr int NQS = 2 / QH;
+  const int nwork = kv.B * kv.Hkv * HG * kv.nblk * NQS;
+  const int per_xcd = gridDim.x >> 3;
+  int work = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (work >= nwork) return;
+  const int qsplit = work % NQS;
+  work /= NQS;
+  const int m = work % kv.nblk;
+  work /= kv.nblk;
+  const int hg = work % (kv.Hkv * HG);
+  const int b = work / (kv.Hkv * HG);
+  const int g = hg / HG;
+  const int s = m * 64, e = s + 64;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  // transpose-read addressing of this lane (see lds_read_tr16): row
+  // (lane & 15) >> 2 of four, column 4 * (lane & 3), groups 1 and 3 on d-rows 16..31
+  const int tr_row = (lane & 15) >> 2, tr_col = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
+  const int hw = w % NH, qg = w / NH;
+  const int h = g * G + (hg % HG) * NH + hw;
+  const int q0 = s + (qsplit * QH + qg) * 32;     // this wave's first query
+  const int wq_lo = s + qsplit * QH * 32;         // the workgroup's query range
+  const int wq_hi = wq_lo + QH * 32 - 1;
+  const uint16_t* Q = static_cast<const uint16_t*>(a.q);
+  const uint16_t* K = static_cast<const uint16_t*>(a.k);
+  const uint16_t* V = static_cast<const uint16_t*>(a.v);
+  const size_t kvbase = (static_cast<size_t>(b) * kv.Hkv + g) * kv.T;
+
+  bf16x8_t qf[KS];
+  {
+    const uint16_t* qrow = Q + ((static_cast<size_t>(b) * kv.Hq + h) * kv.T + q0 + l32) * D + hi * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + ks * 16);
+  }
+  f32x16_t o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
+  float mrun = kNegBig, lrun = 0.f;
+
+  const int r = b * kv.nblk + m;
+  const int32_t* row = a.idx ? a.idx + static_cast<size_t>(r) * a.L : nullptr;
+  const int n_ent = row ? a.L : e;
+  const int n_tiles = (n_ent + 63) / 64;
+  // Row entries are fetched two tiles ahead and kept raw: judging them (a
+  // use of the loaded value) happens only when their tile is issued, so no
+  // wait for them, which would also wait for every earlier load, comes early.
+  auto raw_entry = [&](int i) { return i < n_ent ? (row ? row[i] : i) : -1; };
+  auto visible = [&](int p) { return (p < 0 || p > wq_hi) ? -1 : p; };
+  // load u of this wave covers tile rows (u * NWV + w) * 4 .. +3; the lane
+  // takes row + (lane >> 4) and LDS slot lane & 15
+  const int lrow = lane >> 4, lslot = lane & 15;
+  int pr[LPT], prn[LPT];                          // raw entries of the next two tiles
+  // tile with raw entries pr -> buffers: the loads, the positions for the
+  // mask and the tile's mask / visibility flags
+  auto issue = [&](uint16_t* skb, uint16_t* svb, int* sposb, int (*sflagb)[NWV]) __attribute__((always_inline)) {
+    bool need = false, any = false;
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      const int base = (u * NWV + w) * 4;
+      const int rr = base + lrow;
+      const int p = visible(pr[u]);
+      need |= (p < 0 || p > wq_lo);
+      any |= (p >= 0);
+      if (lslot == 0) sposb[rr] = p;
+      const size_t off = (kvbase + max(p, 0)) * D + (lslot ^ swz(rr)) * 8;
+      __builtin_amdgcn_global_load_lds(K + off, skb + base * D, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(V + off, svb + base * D, 16, 0, 0);
+    }
+    const unsigned long long nb = __ballot(need), ab = __ballot(any);
+    if (lane == 0) { sflagb[0][w] = nb != 0; sflagb[1][w] = ab != 0; }
+  };
+  auto advance = [&](int ti) __attribute__((always_inline)) {   // entries: tile ti+2 -> pr, ti+3 -> prn
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      pr[u] = prn[u];
+      prn[u] = raw_entry((ti + 3) * 64 + (u * NWV + w) * 4 + lrow);
+    }
+  };
+  // one tile: products from buffers c, loads of the next tile into buffers n
+  auto step = [&](int ti, const uint16_t* skc, const uint16_t* svc, const int* sposc, const int (*sflagc)[NWV],
+                  uint16_t* skn, uint16_t* svn, int* sposn, int (*sflagn)[NWV]) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0);                // this wave's loads of tile ti are in LDS
+    __syncthreads();                              // everyone's; and tile ti-1 is retired
+    if (ti + 1 < n_tiles) {
+      issue(skn, svn, sposn, sflagn);
+      advance(ti);
+    }
+    int flag = 2;
+#pragma unroll
+    for (int i = 0; i < NWV; ++i) {
+      flag |= sflagc[0][i] ? 1 : 0;
+      if (sflagc[1][i]) flag &= ~2;
+    }
+    flag = __builtin_amdgcn_readfirstlane(flag);
+    if (flag & 2) return;                         // nothing visible in this tile
+    // S^T tiles [key tile kt]: 32 keys x this wave's 32 queries
+    f32x16_t sacc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[kt][i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const int rr = kt * 32 + l32;
+        const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(skc + rr * D + ((2 * ks + hi) ^ swz(rr)) * 8);
+        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[ks], sacc[kt], 0, 0, 0);
+      }
+    }
+    if (flag & 1) {
+      const unsigned t = static_cast<unsigned>(q0 + l32);   // padding (-1) compares as the largest
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int rn = 0; rn < 4; ++rn) {
+          const int4 p4 = *reinterpret_cast<const int4*>(sposc + kt * 32 + rn * 8 + hi * 4);
+          const int pp[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if (static_cast<unsigned>(pp[c]) > t) sacc[kt][rn * 4 + c] = -INFINITY;
+        }
+    }
+    {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kt][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * a.scale_log2;
+      const bool raise = mx > mrun + 8.0f;
+      const float m_use = raise ? mx : mrun;
+      const float alpha = __builtin_amdgcn_exp2f(mrun - m_use);
+      float ps = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float pz = __builtin_amdgcn_exp2f(fmaf(sacc[kt][i], a.scale_log2, -m_use));
+          sacc[kt][i] = pz;
+          ps += pz;
+        }
+      ps += __shfl_xor(ps, 32, 64);
+      lrun = lrun * alpha + ps;
+      mrun = m_use;
+      if (__ballot(raise)) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int kt = ks >> 1, half = ks & 1;
+      u32x4_t u;
+      u[0] = pack_bf16x2(sacc[kt][half * 8 + 0], sacc[kt][half * 8 + 1]);
+      u[1] = pack_bf16x2(sacc[kt][half * 8 + 2], sacc[kt][half * 8 + 3]);
+      u[2] = pack_bf16x2(sacc[kt][half * 8 + 4], sacc[kt][half * 8 + 5]);
+      u[3] = pack_bf16x2(sacc[kt][half * 8 + 6], sacc[kt][half * 8 + 7]);
+      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, u);
+      const int r0 = ks * 16 + hi * 4 + tr_row, r1 = r0 + 8;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int c = dt * 32 + tr_col;           // 4 consecutive d inside one 16-byte piece
+        const i16x4_t lo4 = lds_read_tr16(svc + r0 * D + (((c >> 3) ^ swz(r0)) << 3) + (c & 7));
+        const i16x4_t hi4 = lds_read_tr16(svc + r1 * D + (((c >> 3) ^ swz(r1)) << 3) + (c & 7));
+        const bf16x8_t av = __builtin_bit_cast(
+            bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb, o[dt], 0, 0, 0);
+      }
+    }
+  };
+
+  // prologue: tile 0 into buffers 0, entries of tiles 1 and 2 in hand
+#pragma unroll
+  for (int u = 0; u < LPT; ++u) {
+    const int rr = (u * NWV + w) * 4 + lrow;
+    pr[u] = raw_entry(rr);
+    prn[u] = raw_entry(64 + rr);
+  }
+  issue(sk0, sv0, spos0, sflag0);
+#pragma unroll
+  for (int u = 0; u < LPT; ++u) {
+    pr[u] = prn[u];
+    prn[u] = raw_entry(128 + (u * NWV + w) * 4 + lrow);
+  }
+  for (int ti = 0; ti < n_tiles; ti += 2) {
+    step(ti, sk0, sv0, spos0, sflag0, sk1, sv1, spos1, sflag1);
+    if (ti + 1 < n_tiles) step(ti + 1, sk1, sv1, spos1, sflag1, sk0, sv0, spos0, sflag0);
+  }
+
+  const float inv = 1.0f / lrun;
+  float* orow = a.out + ((static_cast<size_t>(b) * kv.Hq + h) * kv.T + q0 + l32) * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      float4 v;
+      v.x = o[dt][i4 * 4 + 0] * inv;
+      v.y = o[dt][i4 * 4 + 1] * inv;
+      v.z = o[dt][i4 * 4 + 2] * inv;
+      v.w = o[dt][i4 * 4 + 3] * inv;
+      *reinterpret_cast<float4*>(orow + dt * 32 + i4 * 8 + hi * 4) = v;
+    }
+}
+
+template <int NH, int QH>
+static void launch_mfma_lds(const AttnArgs& a, hipStream_t st) {
+  const int G = a.kv.Hq / a.kv.Hkv;
+  const int nwork = a.kv.B * a.kv.Hkv * (G / NH) * a.kv.nblk * (2 / QH);
+  const int grid = (nwork + 7) / 8 * 8;
+  DSA_LAUNCH(a.idx ? "attn_prefill" : "dense_prefill", (k_prefill_mfma_lds<NH, QH>), dim3(grid),
+             dim3(64 * NH * QH), st, a);
+}
+
 template <int D, int NH, int QH>
 static void launch_mfma(const AttnArgs& a, hipStream_t st) {
   const int G = a.kv.Hq / a.kv.Hkv;
@@ -319,9 +572,9 @@ bool launch_prefill_mfma(const AttnArgs& a, hipStream_t st) {
   if (a.kv.decode || a.kv.bq != 64) return false;
   const int G = a.kv.Hq / a.kv.Hkv;
   if (a.kv.D == 128) {
-    if (G >= 4) { launch_mfma<128, 4, 1>(a, st); return true; }
-    if (G == 2) { launch_mfma<128, 2, 2>(a, st); return true; }
-    if (G == 1) { launch_mfma<128, 1, 2>(a, st); return true; }
+    if (G >= 4) { launch_mfma_lds<4, 1>(a, st); return true; }
+    if (G == 2) { launch_mfma_lds<2, 2>(a, st); return true; }
+    if (G == 1) { launch_mfma_lds<1, 2>(a, st); return true; }
   } else if (a.kv.D == 64) {
     if (G >= 4) { launch_mfma<64, 4, 1>(a, st); return true; }
     if (G == 2) { launch_mfma<64, 2, 2>(a, st); return true; }
