@@ -15,7 +15,9 @@ It follows the InfiniteHiP page (2502.08910), section 3.4:
 and the attention over the active key set as written on the InfLLM blog page
 ("Mathematical Formulation of Efficient Softmax Normalization") and as the
 masked softmax of the MInference page (section on the sparse-attention
-problem formulation), with causal masking inside the kernel.
+problem formulation), with causal masking inside the kernel; and, for decoding
+with remembered masks, the InfiniteHiP page's "Sparse Attention Mask Caching"
+(per-stage refresh intervals, stage 1 refreshed with the newest query).
 
 Readings taken where the pages are silent or garbled (each is listed with its
 reason in the project's design notes):
@@ -33,7 +35,11 @@ reason in the project's design notes):
     that does not fill a whole chunk joins the window;
   * masked keys are excluded exactly (the additive -c(1-M) form with c=1e5
     underflows to the same result), key p is visible to query t iff p <= t;
-  * softmax and the P.V product are evaluated in fp64 and cast to fp32.
+  * softmax and the P.V product are evaluated in fp64 and cast to fp32;
+  * mask caching: one step counter per call for the whole batch; a due stage
+    reads the current output of the stage before it (fresh or remembered);
+    keys that slid out of the window since the stage-1 refresh a row descends
+    from were never scored and are kept with the window.
 
 Every function here is pinned by tests/test_oracle.py against what the pages
 and the mathematics fix (closed forms, brute force, special cases reducing to
@@ -236,6 +242,79 @@ def visited_rows(Q: np.ndarray, K, s: int, e: int, p: Params) -> List[int]:
         out.append(int(keys.size))
         P = P.reshape(nc, l)[top_k(sc, kc)].reshape(-1)
     return out
+
+
+# --------------------------------------------------------------------------- #
+# mask caching across decode steps ("Sparse Attention Mask Caching")          #
+# --------------------------------------------------------------------------- #
+@dataclass
+class StageRecord:
+    """The remembered output of one pruning stage for one sequence: the
+    ascending key positions it kept (whole chunks of the stage's size) and the
+    end of the stage-1 middle those positions were drawn from."""
+    kept: np.ndarray
+    mid_end: int
+
+
+def stages_due(step: int, refresh: Sequence[int]) -> List[bool]:
+    """Stage i recomputes its output at decode step ``step`` exactly when
+    step mod n_refresh^(i) == 0; otherwise its remembered output is reused."""
+    if step < 0 or any(n < 1 for n in refresh):
+        raise ValueError("step must be >= 0 and every refresh interval >= 1")
+    return [step % n == 0 for n in refresh]
+
+
+def prune_decode_cached(q: np.ndarray, K, e: int, p: Params, refresh: Sequence[int],
+                        step: int, cache: List[Optional[StageRecord]],
+                        trace: Optional[list] = None) -> np.ndarray:
+    """Index row of the decode query at position e-1 with per-stage mask caching.
+
+    q: [Hq, d] float32, the newest query; K: [Hkv, >=e, d] indexable; cache: a
+    list of n_stages records (None before the first refresh), updated in place.
+    A stage that is due takes the current output of the stage before it (the
+    one just recomputed if that stage was due too, its remembered one
+    otherwise; for stage 1 the whole middle of the current context), scores it
+    with the newest query exactly as an uncached stage does, and remembers what
+    it keeps. The row is the current sinks, the last stage's remembered keys,
+    and every position from the end of the middle those keys came from up to
+    the newest token: keys that left the window since the last stage-1 refresh
+    were never scored, so they stay with the window until the next one.
+    If ``trace`` is a list, the indices of the recomputed stages are appended.
+    """
+    if len(cache) != len(p.chunk) or len(refresh) != len(p.chunk):
+        raise ValueError("one cache record and one refresh interval per stage")
+    geo = geometry(e - 1, e, p)
+    due = stages_due(step, refresh)
+    for i, (l, k) in enumerate(zip(p.chunk, p.keep)):
+        if not due[i]:
+            if cache[i] is None:
+                raise ValueError(f"stage {i + 1} is not due at step {step} and has no record")
+            continue
+        if i == 0:
+            P = np.arange(geo.mid_lo, geo.mid_hi, dtype=np.int64)
+            mid_end = geo.mid_hi
+        else:
+            P = cache[i - 1].kept
+            mid_end = cache[i - 1].mid_end
+        nc = len(P) // l
+        kc = k // l
+        if nc > kc:
+            sel = top_k(chunk_scores(q[:, None, :], K, P, l), kc)
+            P = np.asarray(P).reshape(nc, l)[sel].reshape(-1)
+        cache[i] = StageRecord(np.array(P, dtype=np.int64), int(mid_end))
+        if trace is not None:
+            trace.append(i)
+    last = cache[-1]
+    if last.mid_end > e:
+        raise ValueError("the context is shorter than when its stage-1 record was made")
+    return np.concatenate([np.arange(0, geo.sink_hi, dtype=np.int64), last.kept,
+                           np.arange(last.mid_end, e, dtype=np.int64)])
+
+
+def cached_row_bound(p: Params, growth: int) -> int:
+    """Most entries a cached decode row can hold when the context has grown by
+    ``growth`` tokens since the stage-1 refresh its keys descend from."""
+    return p.n_sink + p.keep[-1] + p.n_window + p.chunk[0] - 1 + growth
 
 
 def block_bounds(m: int, T: int, p: Params, decode: bool) -> Tuple[int, int]:

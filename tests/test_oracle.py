@@ -390,3 +390,127 @@ def test_visited_rows_bounds():
     Q2 = np.repeat(Q[::G], G, axis=0)
     vis2 = ref.visited_rows(Q2, K, s, e, p)
     assert vis2[0] == nc[0] * Hkv * (1 + int(math.log2(p.chunk[0])))
+
+
+# --------------------------------------------------------------------------- #
+# mask caching across decode steps (InfiniteHiP "Sparse Attention Mask        #
+# Caching"): the refresh schedule of Figure 7, and reductions to the uncached #
+# pruning                                                                     #
+# --------------------------------------------------------------------------- #
+def test_refresh_schedule_matches_figure_7():
+    g = _load("p1_fig7_refresh.json")
+    refresh = tuple(g["presets"]["default"])
+    n = g["fig7_steps"]
+    for i in range(3):
+        got = [st for st in range(n) if ref.stages_due(st, refresh)[i]]
+        assert got == g["fig7_refresh_steps"][str(i + 1)]
+    assert ref.stages_due(g["fig7_only_stage3_step"], refresh) == [False, False, True]
+    # the same schedule seen through the cached pruning itself
+    rng = np.random.default_rng(5)
+    Hq, Hkv, d, T = 4, 2, 16, 1600
+    K = grid(rng, (Hkv, T + n, d))
+    p = ref.Params(1, (32, 8, 4), (256, 128, 64), 16, 64)
+    cache = [None, None, None]
+    for st in range(n):
+        trace = []
+        ref.prune_decode_cached(grid(rng, (Hq, d)), K, T + st, p, refresh, st, cache, trace)
+        assert trace == [i for i in range(3) if st in g["fig7_refresh_steps"][str(i + 1)]]
+    for name, iv in g["presets"].items():
+        assert all(ref.stages_due(0, iv)) and not any(ref.stages_due(1, iv)), name
+
+
+def test_cached_with_refresh_every_step_is_uncached():
+    rng = np.random.default_rng(6)
+    Hq, Hkv, d, T = 4, 2, 16, 1500
+    K = grid(rng, (Hkv, T + 40, d))
+    p = ref.Params(1, (32, 8), (256, 64), 16, 64)
+    cache = [None, None]
+    for st in range(40):
+        q = grid(rng, (Hq, d))
+        e = T + st
+        got = ref.prune_decode_cached(q, K, e, p, (1, 1), st, cache)
+        want = ref.prune_block(q[:, None, :], K, e - 1, e, p)
+        assert np.array_equal(got, want), st
+
+
+def test_cached_constant_query_equals_uncached():
+    # With the same query and a middle that does not move (the context grows
+    # inside one stage-1 chunk), every remembered stage equals a fresh one, so
+    # the cached row must equal the uncached row at every step.
+    rng = np.random.default_rng(7)
+    Hq, Hkv, d = 8, 2, 16
+    p = ref.Params(1, (64, 16, 4), (512, 256, 64), 16, 64)
+    e0 = 16 + 64 + 40 * 64                       # middle ends exactly at a chunk boundary
+    K = grid(rng, (Hkv, e0 + 64, d))
+    q = grid(rng, (Hq, d))
+    cache = [None, None, None]
+    for st in range(63):
+        e = e0 + st
+        got = ref.prune_decode_cached(q, K, e, p, (16, 8, 4), st, cache)
+        want = ref.prune_block(q[:, None, :], K, e - 1, e, p)
+        assert np.array_equal(got, want), st
+
+
+def test_cached_stage3_refresh_is_token_topk_of_remembered_stage2():
+    # Keys constant over every stage-3 chunk make SelectRep irrelevant there:
+    # a stage-3 refresh must keep the remembered stage-2 chunks whose token
+    # score max_h q_h . k is among the top keep3/l3 (ties to lower positions),
+    # computed here with a library sort, plus sinks and everything from the
+    # stage-1 middle end up to the newest token.
+    rng = np.random.default_rng(8)
+    Hq, Hkv, d = 4, 2, 16
+    p = ref.Params(1, (64, 32, 8), (1024, 512, 128), 16, 64)
+    T = 16 + 64 + 60 * 64 + 37
+    codes = rng.integers(-2, 3, size=(Hkv, (T + 16) // 8 + 1, d))
+    K = np.repeat(codes, 8, axis=1)[:, :T + 16].astype(np.float32) / 8
+    cache = [None, None, None]
+    ref.prune_decode_cached(grid(rng, (Hq, d)), K, T, p, (16, 8, 4), 0, cache)
+    stage2 = cache[1].kept.copy()
+    mid_end = cache[0].mid_end
+    # stage 2's record equals a fresh two-stage pruning of the step-0 context
+    assert mid_end == ref.geometry(T - 1, T, p).mid_hi
+    for st in (1, 2, 3, 4):
+        q = grid(rng, (Hq, d))
+        e = T + st
+        got = ref.prune_decode_cached(q, K, e, p, (16, 8, 4), st, cache)
+        assert np.array_equal(cache[1].kept, stage2)
+        tail = np.arange(mid_end, e)
+        if st < 4:                               # nothing due: the row only grows
+            continue
+        ch = stage2.reshape(-1, 8)[:, 0]
+        Kf = K.astype(np.float64)
+        G = Hq // Hkv
+        sc = np.max([Kf[h // G, ch] @ q[h].astype(np.float64) for h in range(Hq)], axis=0)
+        order = np.lexsort((np.arange(len(ch)), -sc))[:128 // 8]
+        kept = np.sort(ch[order])
+        want = np.concatenate([np.arange(16), (kept[:, None] + np.arange(8)).reshape(-1), tail])
+        assert np.array_equal(got, want)
+
+
+def test_cached_row_keeps_keys_that_left_the_window():
+    rng = np.random.default_rng(9)
+    Hq, Hkv, d = 4, 2, 16
+    p = ref.Params(1, (32, 8), (256, 64), 16, 64)
+    T = 2000
+    K = grid(rng, (Hkv, T + 100, d))
+    cache = [None, None]
+    refresh = (48, 8)
+    for st in range(100):
+        e = T + st
+        row = ref.prune_decode_cached(grid(rng, (Hq, d)), K, e, p, refresh, st, cache)
+        mid_end = cache[0].mid_end
+        assert np.all(np.diff(row) > 0) and row[-1] == e - 1
+        assert set(range(16)) <= set(row.tolist())
+        assert set(range(mid_end, e)) <= set(row.tolist())       # nothing was dropped
+        assert set(range(e - 64, e)) <= set(row.tolist())        # the window is always there
+        assert len(row) == 16 + 64 + (e - mid_end)
+        growth = e - (T + (st // 48) * 48)
+        assert len(row) <= ref.cached_row_bound(p, growth)
+
+
+def test_cached_decode_rejects_missing_records():
+    rng = np.random.default_rng(10)
+    K = grid(rng, (2, 1200, 16))
+    p = ref.Params(1, (32, 8), (256, 64), 16, 64)
+    with pytest.raises(ValueError):
+        ref.prune_decode_cached(grid(rng, (4, 16)), K, 1100, p, (16, 4), 3, [None, None])
