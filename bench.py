@@ -10,7 +10,10 @@ Secondary figures on the same JSON line: 128K sparse prefill TFLOP/s against
 the bf16 MFMA peak, the library's dense decode at 1M, per-kernel durations
 from HIP events on the launch stream, and the CPU oracle timed on the host.
 
-    python bench.py [--steps K] [--warmup W] [--no-prefill] [--no-dense] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--no-prefill] [--no-dense] [--no-cached] [--no-cpu]
+
+Also on the line: decoding with remembered stage outputs (mask caching, the
+default refresh intervals 16/8/4) at 1M, as amortised microseconds per token.
 """
 from __future__ import annotations
 
@@ -68,6 +71,7 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-cached", action="store_true", help="skip decoding with remembered stages")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-ref", action="store_true",
@@ -282,6 +286,9 @@ def decode_bench(args, res):
                          kernels_us={k: round(v, 2) for k, v in kern_us.items()}, roofline=roof,
                          mode="graph" if graphs is not None else "eager")
 
+    if not args.no_cached:
+        res["cached"] = cached_decode(args, lib, p, Qs, Ks, Vs, shape, ws, wsb, out, dev.seq_lens)
+
     if not args.no_dense:
         reps = 5
         dshape_ws = _lib.workspace_bytes(shape, None)
@@ -305,6 +312,88 @@ def decode_bench(args, res):
     del Ks, Vs, dev, ws
     torch.cuda.empty_cache()
     return case
+
+
+def cached_decode(args, lib, p, Qs, Ks, Vs, shape, ws, wsb, out, seq_lens_full, refresh=(16, 8, 4)):
+    """Decode with remembered stage outputs at 1M: one refresh cycle of
+    refresh[0] steps (every stage due at step 0, then each stage at its own
+    interval), the context growing by one token per step up to T, a fresh query
+    and the next KV replica each step. Returns the amortised time per token."""
+    import torch
+    from dynamic_sparse_attention_query_amd import _lib
+    from dynamic_sparse_attention_query_amd._lib import Shape
+    n = refresh[0]
+    T = shape.t
+    NQ = len(Qs)
+    sls = [torch.full((1,), T - n + 1 + i, dtype=torch.int32, device="cuda") for i in range(n)]
+    shapes = [Shape(shape.mode, shape.dtype, 1, shape.hq, shape.hkv, shape.d, T, seq_lens=sl.data_ptr())
+              for sl in sls]
+    cshapes = [sh.c() for sh in shapes]
+    cp = p.c()
+    L = _lib.cached_index_width(p, n - 1)
+    cb = _lib.mask_cache_bytes(shapes[0], p)
+    cache = torch.zeros(cb, dtype=torch.uint8, device="cuda")
+    idx = torch.empty(L, dtype=torch.int32, device="cuda")
+    rf = (ctypes.c_int32 * 4)(*(list(refresh) + [1] * (4 - len(refresh))))
+
+    def launch(i, visited=None):
+        step = i % n
+        q, r = Qs[i % NQ], i % args.replicas
+        sp = torch.cuda.current_stream().cuda_stream
+        cs = cshapes[step]
+        st = lib.dsa_prune_select_cached(ctypes.byref(cs), q.data_ptr(), Ks[r].data_ptr(), ctypes.byref(cp),
+                                         rf, step, cache.data_ptr(), cb, idx.data_ptr(), L, ws.data_ptr(), wsb,
+                                         visited.data_ptr() if visited is not None else None, sp)
+        st |= lib.dsa_sparse_attn(ctypes.byref(cs), q.data_ptr(), Ks[r].data_ptr(), Vs[r].data_ptr(),
+                                  idx.data_ptr(), L, 1, 0.0, out.data_ptr(), ws.data_ptr(), wsb, sp)
+        if st:
+            raise RuntimeError(lib.dsa_last_error().decode())
+
+    # algorithmic bytes of one cycle: SelectRep rows of the stages that ran
+    # (counted by the kernels) + K and V rows of every step's kept keys
+    row_bytes = shape.d * 2
+    vis = torch.zeros(len(p.chunk), dtype=torch.int64, device="cuda")
+    cyc_bytes = 0.0
+    for i in range(n):
+        launch(i, vis)
+        torch.cuda.synchronize()
+        cyc_bytes += int((idx >= 0).sum().item()) * shape.hkv * 2 * row_bytes
+    cyc_bytes += float(vis.sum().item()) * row_bytes
+    assert int(cache[:4].view(torch.int32).item()) == 0, "cached row overflow"
+
+    graphs = []
+    torch.cuda.synchronize()
+    for i in range(n * 2):                       # two cycles: replicas alternate between them
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            launch(i)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    cycles = max(2, args.steps // n)
+    for i in range(n * 2):
+        graphs[i].replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for c in range(cycles):
+        for i in range(n):
+            graphs[(c % 2) * n + i].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us_tok = e0.elapsed_time(e1) * 1e3 / (cycles * n)
+    # per-step-kind times: a step with every stage due vs one that only assembles
+    def step_us(i, reps=8):
+        e0.record()
+        for _ in range(reps):
+            graphs[i].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+    full_us, reuse_us = step_us(0), step_us(1)
+    log(f"cached decode 1M {refresh}: {us_tok:.1f} us/token amortised "
+        f"(all stages due {full_us:.1f} us, none due {reuse_us:.1f} us)")
+    return dict(refresh=list(refresh), us_per_token=us_tok, steps=cycles * n,
+                bytes_per_token=cyc_bytes / n, full_refresh_step_us=full_us, reuse_step_us=reuse_us)
 
 
 # --------------------------------------------------------------------------- #
@@ -458,6 +547,15 @@ def main():
         line["dense_decode_1m"] = {"us": round(res["dense"]["us"], 1), "gbps": round(res["dense"]["gbps"], 1),
                                    "pct_peak": round(100 * res["dense"]["gbps"] / PEAK_HBM_GBPS, 2),
                                    "sparse_speedup": round(res["dense"]["us"] / dec["us_per_step"], 2)}
+    if "cached" in res:
+        c = res["cached"]
+        g = c["bytes_per_token"] / (c["us_per_token"] * 1e-6) / 1e9
+        line["decode_cached_1m"] = {"refresh": c["refresh"], "us_per_token": round(c["us_per_token"], 2),
+                                    "gbps": round(g, 1), "pct_peak": round(100 * g / PEAK_HBM_GBPS, 2),
+                                    "algorithmic_bytes_per_token": int(c["bytes_per_token"]),
+                                    "all_stages_due_step_us": round(c["full_refresh_step_us"], 2),
+                                    "no_stage_due_step_us": round(c["reuse_step_us"], 2),
+                                    "speedup_vs_uncached": round(dec["us_per_step"] / c["us_per_token"], 2)}
     if "prefill" in res:
         pf = res["prefill"]
         line["prefill_128k"] = {"ms": round(pf["ms"], 2), "tflops": round(pf["tflops"], 2),

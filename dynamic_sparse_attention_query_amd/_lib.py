@@ -20,7 +20,8 @@ DSA_PREFILL, DSA_DECODE = 0, 1
 MAX_STAGES = 4
 
 EXPORTS = ("dsa_index_width", "dsa_workspace_bytes", "dsa_prune_select", "dsa_sparse_attn",
-           "dsa_dense_attn", "dsa_profile_begin", "dsa_profile_end", "dsa_status_str", "dsa_last_error")
+           "dsa_dense_attn", "dsa_mask_cache_bytes", "dsa_cached_index_width", "dsa_prune_select_cached",
+           "dsa_profile_begin", "dsa_profile_end", "dsa_status_str", "dsa_last_error")
 
 
 class CParams(ctypes.Structure):
@@ -65,6 +66,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dsa_workspace_bytes.restype = ctypes.c_int
     lib.dsa_prune_select.argtypes = [ctypes.POINTER(CShape), vp, vp, ctypes.POINTER(CParams), vp, vp, sz, vp, vp]
     lib.dsa_prune_select.restype = ctypes.c_int
+    lib.dsa_mask_cache_bytes.argtypes = [ctypes.POINTER(CShape), ctypes.POINTER(CParams), ctypes.POINTER(sz)]
+    lib.dsa_mask_cache_bytes.restype = ctypes.c_int
+    lib.dsa_cached_index_width.argtypes = [ctypes.POINTER(CParams), ctypes.c_int32]
+    lib.dsa_cached_index_width.restype = ctypes.c_int32
+    lib.dsa_prune_select_cached.argtypes = [ctypes.POINTER(CShape), vp, vp, ctypes.POINTER(CParams),
+                                            ctypes.POINTER(ctypes.c_int32), ctypes.c_int64, vp, sz, vp,
+                                            ctypes.c_int32, vp, sz, vp, vp]
+    lib.dsa_prune_select_cached.restype = ctypes.c_int
     lib.dsa_sparse_attn.argtypes = [ctypes.POINTER(CShape), vp, vp, vp, vp, ctypes.c_int32, ctypes.c_int32,
                                     ctypes.c_float, vp, vp, sz, vp]
     lib.dsa_sparse_attn.restype = ctypes.c_int
@@ -160,6 +169,28 @@ def prune_select_raw(shape: Shape, q: int, k: int, p: Params, idx: int, ws: int,
     cs, cp = shape.c(), p.c()
     _check(load().dsa_prune_select(ctypes.byref(cs), q, k, ctypes.byref(cp), idx, ws, ws_bytes,
                                    visited or None, stream or None))
+
+
+def mask_cache_bytes(shape: Shape, p: Params) -> int:
+    cs, cp = shape.c(), p.c()
+    out = ctypes.c_size_t(0)
+    _check(load().dsa_mask_cache_bytes(ctypes.byref(cs), ctypes.byref(cp), ctypes.byref(out)))
+    return out.value
+
+
+def cached_index_width(p: Params, max_growth: int) -> int:
+    cp = p.c()
+    return load().dsa_cached_index_width(ctypes.byref(cp), max_growth)
+
+
+def prune_select_cached_raw(shape: Shape, q: int, k: int, p: Params, refresh: Sequence[int], step: int,
+                            cache: int, cache_bytes: int, idx: int, idx_width: int, ws: int, ws_bytes: int,
+                            visited: int = 0, stream: int = 0):
+    cs, cp = shape.c(), p.c()
+    rf = (ctypes.c_int32 * MAX_STAGES)(*([int(x) for x in refresh] + [1] * (MAX_STAGES - len(refresh))))
+    _check(load().dsa_prune_select_cached(ctypes.byref(cs), q, k, ctypes.byref(cp), rf, step, cache or None,
+                                          cache_bytes, idx, idx_width, ws, ws_bytes, visited or None,
+                                          stream or None))
 
 
 def sparse_attn_raw(shape: Shape, q: int, k: int, v: int, idx: int, idx_width: int, block_q: int,

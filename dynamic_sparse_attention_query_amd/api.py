@@ -114,6 +114,58 @@ def prune_select(q: torch.Tensor, k: torch.Tensor, params: Params, *,
     return out.view(shape.batch, shape.t // params.block_q, L)
 
 
+class MaskCache:
+    """Remembered stage outputs of one stream of decode steps (mask caching).
+
+    Holds the device buffer the library reads and writes, the refresh
+    intervals and the row width; `status` views the per-sequence overflow flags.
+    Allocate it for the largest context the stream will reach (`t`).
+    """
+
+    def __init__(self, q: torch.Tensor, k: torch.Tensor, params: Params, refresh, *,
+                 seq_lens: torch.Tensor, block_table: Optional[torch.Tensor] = None,
+                 t: Optional[int] = None, max_growth: Optional[int] = None):
+        if len(refresh) != len(params.chunk):
+            raise ValueError("one refresh interval per stage")
+        shape = make_shape(q, k, seq_lens=seq_lens, block_table=block_table, t=t)
+        self.params = params
+        self.refresh = tuple(int(x) for x in refresh)
+        self.batch = shape.batch
+        growth = self.refresh[0] - 1 if max_growth is None else max_growth
+        self.width = _lib.cached_index_width(params, growth)
+        if self.width < 0:
+            raise _lib.DsaError(_lib.DSA_ERR_INVALID_ARG, "invalid params or growth")
+        self.buf = torch.zeros(_lib.mask_cache_bytes(shape, params), dtype=torch.uint8, device=q.device)
+
+    @property
+    def status(self) -> torch.Tensor:
+        return self.buf[: 4 * self.batch].view(torch.int32)
+
+
+def prune_select_cached(q: torch.Tensor, k: torch.Tensor, cache: MaskCache, step: int, *,
+                        seq_lens: torch.Tensor, block_table: Optional[torch.Tensor] = None,
+                        t: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                        visited: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode step of pruning with remembered stages: [B, cache.width] rows."""
+    shape = make_shape(q, k, seq_lens=seq_lens, block_table=block_table, t=t)
+    params = cache.params
+    L = cache.width
+    if out is None:
+        out = torch.empty(shape.batch * L, dtype=torch.int32, device=q.device)
+    if out.numel() != shape.batch * L or out.dtype != torch.int32:
+        raise ValueError("idx buffer has the wrong size or dtype")
+    ws, wsb = workspace(shape, params, q.device)
+    vis = 0
+    if visited is not None:
+        if visited.dtype != torch.int64 or visited.numel() < len(params.chunk):
+            raise ValueError("visited must be int64 with one entry per stage")
+        vis = visited.data_ptr()
+    _lib.prune_select_cached_raw(shape, q.data_ptr(), k.data_ptr(), params, cache.refresh, step,
+                                 cache.buf.data_ptr(), cache.buf.numel(), out.data_ptr(), L, ws, wsb, vis,
+                                 _stream())
+    return out.view(shape.batch, L)
+
+
 def sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor, params: Params, *,
                 scale: float = 0.0, seq_lens: Optional[torch.Tensor] = None,
                 block_table: Optional[torch.Tensor] = None, t: Optional[int] = None,

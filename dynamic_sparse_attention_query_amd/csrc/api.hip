@@ -204,21 +204,15 @@ dsa_status dsa_workspace_bytes(const dsa_shape* s, const dsa_params* p, size_t* 
   return DSA_OK;
 }
 
-dsa_status dsa_prune_select(const dsa_shape* s, const void* q, const void* k, const dsa_params* p,
-                            int32_t* idx, void* ws, size_t ws_bytes, uint64_t* visited, void* stream) {
-  g_err[0] = 0;
-  dsa_status st = check_shape(s);
-  if (st != DSA_OK) return st;
-  st = check_params(s, p);
-  if (st != DSA_OK) return st;
-  if (!q || !k || !idx) return fail(DSA_ERR_INVALID_ARG, "q, k and idx must be non-NULL");
-  const long long L = index_width_ll(p);
-  if (L > (1LL << 30)) return fail(DSA_ERR_INVALID_ARG, "index width overflows");
-  const PruneLayout lay = prune_layout(s, p);
-  if (lay.maxNC > 32768)
-    return fail(DSA_ERR_UNSUPPORTED, "a stage would score %lld chunks per row (limit 32768)", lay.maxNC);
-  if (!ws || ws_bytes < lay.bytes)
-    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, lay.bytes);
+}  // extern "C"
+
+namespace {
+
+// Argument block of a pruning call (validated by the caller); the kept-start
+// lists and counts live in the workspace unless a mask cache supplies them.
+dsa::PruneArgs prune_args(const dsa_shape* s, const void* q, const void* k, const dsa_params* p,
+                          int32_t* idx, long long L, const PruneLayout& lay, void* ws,
+                          uint64_t* visited) {
   dsa::PruneArgs a{};
   a.kv = make_kv(s, p->block_q);
   a.q = q;
@@ -241,9 +235,117 @@ dsa_status dsa_prune_select(const dsa_shape* s, const void* q, const void* k, co
   char* w = static_cast<char*>(ws);
   a.cnt = reinterpret_cast<int32_t*>(w + lay.off_cnt);
   a.starts = reinterpret_cast<int32_t*>(w + lay.off_starts);
+  for (int i = 0; i < DSA_MAX_STAGES; ++i) a.slot[i] = i & 1;
   a.scores = reinterpret_cast<uint32_t*>(w + lay.off_scores);
   a.visited = reinterpret_cast<unsigned long long*>(visited);
+  return a;
+}
+
+// Mask cache layout: status [B], then per-sequence stage records (kept counts,
+// middle ends) and the kept-start lists, one slot per stage.
+struct CacheLayout {
+  size_t off_cnt, off_mid, off_starts, bytes;
+};
+
+CacheLayout cache_layout(const dsa_shape* s, const dsa_params* p, const PruneLayout& lay) {
+  CacheLayout c{};
+  const size_t B = static_cast<size_t>(s->batch);
+  c.off_cnt = align256(B * 4);
+  c.off_mid = c.off_cnt + align256(B * dsa::kMaxStages * 4);
+  c.off_starts = c.off_mid + align256(B * dsa::kMaxStages * 4);
+  c.bytes = align256(c.off_starts + static_cast<size_t>(p->n_stages) * B * lay.maxK * 4);
+  return c;
+}
+
+long long cached_width_ll(const dsa_params* p, long long max_growth) {
+  const long long n = static_cast<long long>(p->n_sink) + p->keep[p->n_stages - 1] + p->n_window +
+                      p->chunk[0] - 1 + max_growth;
+  return (n + 63) / 64 * 64;
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status dsa_prune_select(const dsa_shape* s, const void* q, const void* k, const dsa_params* p,
+                            int32_t* idx, void* ws, size_t ws_bytes, uint64_t* visited, void* stream) {
+  g_err[0] = 0;
+  dsa_status st = check_shape(s);
+  if (st != DSA_OK) return st;
+  st = check_params(s, p);
+  if (st != DSA_OK) return st;
+  if (!q || !k || !idx) return fail(DSA_ERR_INVALID_ARG, "q, k and idx must be non-NULL");
+  const long long L = index_width_ll(p);
+  if (L > (1LL << 30)) return fail(DSA_ERR_INVALID_ARG, "index width overflows");
+  const PruneLayout lay = prune_layout(s, p);
+  if (lay.maxNC > 32768)
+    return fail(DSA_ERR_UNSUPPORTED, "a stage would score %lld chunks per row (limit 32768)", lay.maxNC);
+  if (!ws || ws_bytes < lay.bytes)
+    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, lay.bytes);
+  const dsa::PruneArgs a = prune_args(s, q, k, p, idx, L, lay, ws, visited);
   hipError_t err = dsa::launch_prune(a, s->dtype, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(DSA_ERR_HIP, "prune launch failed: %s", hipGetErrorString(err));
+  return DSA_OK;
+}
+
+int32_t dsa_cached_index_width(const dsa_params* p, int32_t max_growth) {
+  if (check_params(nullptr, p) != DSA_OK || max_growth < 0) return -1;
+  const long long w = cached_width_ll(p, max_growth);
+  if (w > (1LL << 30)) return -1;
+  return static_cast<int32_t>(w);
+}
+
+dsa_status dsa_mask_cache_bytes(const dsa_shape* s, const dsa_params* p, size_t* out_bytes) {
+  g_err[0] = 0;
+  if (!out_bytes) return fail(DSA_ERR_INVALID_ARG, "out_bytes is NULL");
+  dsa_status st = check_shape(s);
+  if (st != DSA_OK) return st;
+  if (s->mode != DSA_DECODE) return fail(DSA_ERR_INVALID_ARG, "mask caching is a decode feature");
+  st = check_params(s, p);
+  if (st != DSA_OK) return st;
+  *out_bytes = cache_layout(s, p, prune_layout(s, p)).bytes;
+  return DSA_OK;
+}
+
+dsa_status dsa_prune_select_cached(const dsa_shape* s, const void* q, const void* k, const dsa_params* p,
+                                   const int32_t* refresh, int64_t step, void* cache, size_t cache_bytes,
+                                   int32_t* idx, int32_t idx_width, void* ws, size_t ws_bytes,
+                                   uint64_t* visited, void* stream) {
+  g_err[0] = 0;
+  dsa_status st = check_shape(s);
+  if (st != DSA_OK) return st;
+  if (s->mode != DSA_DECODE) return fail(DSA_ERR_INVALID_ARG, "mask caching is a decode feature");
+  st = check_params(s, p);
+  if (st != DSA_OK) return st;
+  if (!q || !k || !idx || !cache) return fail(DSA_ERR_INVALID_ARG, "q, k, idx and cache must be non-NULL");
+  if (!refresh) return fail(DSA_ERR_INVALID_ARG, "refresh is NULL");
+  if (step < 0) return fail(DSA_ERR_INVALID_ARG, "step must be >= 0");
+  bool due[DSA_MAX_STAGES] = {false, false, false, false};
+  for (int i = 0; i < p->n_stages; ++i) {
+    if (refresh[i] < 1) return fail(DSA_ERR_INVALID_ARG, "refresh[%d] = %d must be >= 1", i, refresh[i]);
+    due[i] = step % refresh[i] == 0;
+  }
+  if (idx_width < index_width_ll(p) || idx_width % 64 != 0)
+    return fail(DSA_ERR_INVALID_ARG, "idx_width %d must be a multiple of 64 and >= dsa_index_width (%lld)",
+                idx_width, index_width_ll(p));
+  if (reinterpret_cast<uintptr_t>(idx) % 16 != 0 || reinterpret_cast<uintptr_t>(cache) % 16 != 0)
+    return fail(DSA_ERR_INVALID_ARG, "idx and cache must be 16-byte aligned");
+  const PruneLayout lay = prune_layout(s, p);
+  if (lay.maxNC > 32768)
+    return fail(DSA_ERR_UNSUPPORTED, "a stage would score %lld chunks per row (limit 32768)", lay.maxNC);
+  if (!ws || ws_bytes < lay.bytes)
+    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, lay.bytes);
+  const CacheLayout cl = cache_layout(s, p, lay);
+  if (cache_bytes < cl.bytes)
+    return fail(DSA_ERR_INVALID_ARG, "mask cache of %zu bytes is smaller than the %zu needed", cache_bytes, cl.bytes);
+  dsa::PruneArgs a = prune_args(s, q, k, p, idx, idx_width, lay, ws, visited);
+  char* c = static_cast<char*>(cache);
+  a.row_status = reinterpret_cast<int32_t*>(c);
+  a.cnt = reinterpret_cast<int32_t*>(c + cl.off_cnt);
+  a.mid_end = reinterpret_cast<int32_t*>(c + cl.off_mid);
+  a.starts = reinterpret_cast<int32_t*>(c + cl.off_starts);
+  for (int i = 0; i < DSA_MAX_STAGES; ++i) a.slot[i] = i < p->n_stages ? i : 0;
+  hipError_t err = dsa::launch_prune_cached(a, due, s->dtype, static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return fail(DSA_ERR_HIP, "prune launch failed: %s", hipGetErrorString(err));
   return DSA_OK;
 }

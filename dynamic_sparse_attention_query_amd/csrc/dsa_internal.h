@@ -41,7 +41,12 @@ struct PruneArgs {
   int maxNC;                 // longest chunk-score list of any stage
   int n1max;                 // most stage-1 chunks of any row
   int32_t* cnt;              // [R, kMaxStages] chunks kept by each stage
-  int32_t* starts;           // [2, R, maxK] chunk starts, ping-pong by stage parity
+  int32_t* starts;           // [slots, R, maxK] kept chunk starts; stage i uses slot[i]
+  int slot[kMaxStages];      // one call: slots alternate by stage parity; with remembered
+                             // stages (mask caching) every stage owns its slot
+  int32_t* mid_end;          // mask caching: [R, kMaxStages] end of the stage-1 middle each
+                             // stage's record descends from; nullptr otherwise
+  int32_t* row_status;       // mask caching: [R] 1 if the last row did not fit in L; or nullptr
   uint32_t* scores;          // [2, R, maxNC] orderable chunk-score keys, by stage parity
   unsigned long long* visited;  // [n_stages] or nullptr
 };
@@ -304,6 +309,8 @@ ProfSlot prof_slot(const char* name);
 // host launchers (defined in prune.hip / attn.hip)                          //
 // ------------------------------------------------------------------------- //
 hipError_t launch_prune(const PruneArgs& a, int dtype, hipStream_t stream);
+// decode with remembered stages: only the stages flagged in due[] are recomputed
+hipError_t launch_prune_cached(const PruneArgs& a, const bool* due, int dtype, hipStream_t stream);
 hipError_t launch_sparse_attn(const AttnArgs& a, int dtype, hipStream_t stream);
 bool launch_prefill_mfma(const AttnArgs& a, hipStream_t stream);   // bf16, b_q = 64
 struct PruneArgs;

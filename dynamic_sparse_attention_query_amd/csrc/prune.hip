@@ -67,7 +67,7 @@ __device__ __forceinline__ void load_keys(const PruneArgs& a, int stage, int r, 
 __device__ __forceinline__ void load_kept_starts(const PruneArgs& a, int stage, int r, int* sp) {
   const int tid = threadIdx.x;
   const int kmax = a.keep[stage] >> a.lchunk[stage];
-  const int32_t* src = a.starts + static_cast<size_t>(stage & 1) * a.R * a.maxK + static_cast<size_t>(r) * a.maxK;
+  const int32_t* src = stage_starts(a, stage, r);
   for (int i0 = 0; i0 < kmax; i0 += 4 * kTopkThreads) {
     int v[4];
 #pragma unroll
@@ -273,6 +273,33 @@ __device__ __forceinline__ void select_row(uint32_t (&key)[E], int j0, int nc, i
   }
 }
 
+// The index row of row r: sinks [0, sink_hi), the n_sel kept chunks of 2^lg
+// keys starting at sel[] (ascending), then every position from win_lo (the end
+// of the stage-1 middle the kept chunks descend from) up to the newest key,
+// then -1 padding; 16-byte stores, L a multiple of 64. A row that would not
+// fit (possible only when stages are remembered across steps) keeps its first
+// L entries and is flagged in row_status.
+__device__ __forceinline__ void write_index_row(const PruneArgs& a, int r, const Geo& geo, const int* sel,
+                                                int n_sel, int lg, int win_lo) {
+  const int l = 1 << lg;
+  const int win0 = geo.sink_hi + n_sel * l;
+  const int n_win = max(0, geo.e - win_lo);
+  int32_t* row = a.idx + static_cast<size_t>(r) * a.L;
+  for (int i4 = threadIdx.x; i4 < (a.L >> 2); i4 += kTopkThreads) {
+    int v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = 4 * i4 + u;
+      if (i < geo.sink_hi) v[u] = i;
+      else if (i < win0) v[u] = sel[(i - geo.sink_hi) >> lg] + ((i - geo.sink_hi) & (l - 1));
+      else if (i < win0 + n_win) v[u] = win_lo + (i - win0);
+      else v[u] = -1;
+    }
+    reinterpret_cast<int4*>(row)[i4] = make_int4(v[0], v[1], v[2], v[3]);
+  }
+  if (a.row_status && threadIdx.x == 0) a.row_status[r] = win0 + n_win > a.L ? 1 : 0;
+}
+
 // One workgroup per row: select the stage's kept chunks, write their starts
 // (and their count), and after the last stage the index row.
 template <int E>
@@ -298,8 +325,7 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk(PruneArgs a, int stage) {
   const int sh = stage > 0 ? a.lchunk[stage - 1] - lg : 0;
   if (stage > 0) load_kept_starts(a, stage - 1, r, sprev);
   const int n_sel = nc <= kc ? nc : kc;
-  int32_t* out = a.starts + static_cast<size_t>(stage & 1) * a.R * a.maxK + static_cast<size_t>(r) * a.maxK;
-  int32_t* row = a.idx + static_cast<size_t>(r) * a.L;
+  int32_t* out = stage_starts(a, stage, r);
   // stores only after every load has been consumed (inside the selection):
   // stores share the vector memory counter with loads, so an earlier store
   // would hold up their wait
@@ -308,27 +334,25 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk(PruneArgs a, int stage) {
     out[pos] = st;
     if (last) ssel[pos] = st;
   });
-  if (tid == 0) a.cnt[r * kMaxStages + stage] = n_sel;
+  if (tid == 0) record_stage(a, stage, r, n_sel, geo);
   if (!last) return;
-
-  // final stage: the index row (sinks, kept chunks, window, -1 padding) in
-  // 16-byte stores; L is a multiple of 64
   __syncthreads();
-  const int n_pr = n_sel * l;
-  const int win0 = geo.sink_hi + n_pr;
-  const int n_win = max(0, geo.e - geo.mid_hi);
-  for (int i4 = tid; i4 < (a.L >> 2); i4 += kTopkThreads) {
-    int v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = 4 * i4 + u;
-      if (i < geo.sink_hi) v[u] = i;
-      else if (i < win0) v[u] = ssel[(i - geo.sink_hi) >> lg] + ((i - geo.sink_hi) & (l - 1));
-      else if (i < win0 + n_win) v[u] = geo.mid_hi + (i - win0);
-      else v[u] = -1;
-    }
-    reinterpret_cast<int4*>(row)[i4] = make_int4(v[0], v[1], v[2], v[3]);
-  }
+  write_index_row(a, r, geo, ssel, n_sel, lg, stage_mid_end(a, stage, r, geo));
+}
+
+// The last stage's remembered output turned into the index row of the current
+// step (mask caching, when the last stage is not due): one workgroup per row.
+__global__ void __launch_bounds__(kTopkThreads) k_assemble(PruneArgs a) {
+  __shared__ int ssel[kMaxKeptChunks];
+  const int r = blockIdx.x;
+  const int last = a.n_stages - 1;
+  int b, s, e;
+  row_bounds(a.kv, r, b, s, e);
+  const Geo geo = make_geo(s, e, a.n_sink, a.n_window, a.chunk[0]);
+  const int n_sel = max(0, min(a.cnt[r * kMaxStages + last], a.keep[last] >> a.lchunk[last]));
+  load_kept_starts(a, last, r, ssel);
+  __syncthreads();
+  write_index_row(a, r, geo, ssel, n_sel, a.lchunk[last], a.mid_end[r * kMaxStages + last]);
 }
 
 // ------------------------------------------------------------------------- //
@@ -484,8 +508,7 @@ k_score_decode(PruneArgs a, int stage) {
   } else {
     const int sh = a.lchunk[stage - 1] - a.lchunk[stage];
     nc_prev = a.cnt[r * kMaxStages + stage - 1];
-    const int32_t* prev =
-        a.starts + static_cast<size_t>((stage - 1) & 1) * a.R * a.maxK + static_cast<size_t>(r) * a.maxK;
+    const int32_t* prev = stage_starts(a, stage - 1, r);
     st = prev[min(j >> sh, a.maxK - 1)] + ((j & ((1 << sh) - 1)) << a.lchunk[stage]);
   }
   Row q[G];
@@ -555,13 +578,13 @@ __global__ void __launch_bounds__(256, 2) k_topk_score_decode(PruneArgs a, int s
   const int kc_ps = a.keep[ps] >> lgp;
   const int n_sel = nc_ps <= kc_ps ? nc_ps : kc_ps;
   const bool writer = blockIdx.x == 0;
-  int32_t* out = a.starts + static_cast<size_t>(ps & 1) * a.R * a.maxK + static_cast<size_t>(r) * a.maxK;
+  int32_t* out = stage_starts(a, ps, r);
   select_row<E>(key, js, nc_ps, kc_ps, L, [&](int j, int pos) {
     const int st = ps == 0 ? a.n_sink + (j << lgp) : sprev[j >> shp] + ((j & ((1 << shp) - 1)) << lgp);
     ssel[pos] = st;
     if (writer) out[pos] = st;
   });
-  if (writer && tid == 0) a.cnt[r * kMaxStages + ps] = n_sel;
+  if (writer && tid == 0) record_stage(a, ps, r, n_sel, geo);
   __syncthreads();                              // the kept starts are in ssel
 
   // stage `stage`: chunks of chunk[stage] keys tiling the kept chunks
@@ -742,6 +765,61 @@ static void launch_decode(const PruneArgs& a, hipStream_t st) {
     }
   }
   launch_topk(a, a.n_stages - 1, chunks_of(a.n_stages - 1), st);
+}
+
+// Decode with remembered stages: each due stage is scored from the current
+// record of the stage before it (or the whole middle for stage 1) and its
+// top-K replaces its record; the top-K of a due stage whose successor is due
+// too is fused into that successor's scoring as in launch_decode. When the
+// last stage is not due, its record is only turned into the index row.
+template <typename T, int D, int G>
+static void launch_decode_cached(const PruneArgs& a, const bool* due, hipStream_t st) {
+  auto chunks_of = [&](int stage) {
+    return stage == 0 ? a.n1max : a.keep[stage - 1] / a.chunk[stage];
+  };
+  const int S = a.n_stages;
+  bool pending = false;                           // a stage scored here still needs its top-K
+  for (int stage = 0; stage < S; ++stage) {
+    if (!due[stage]) continue;
+    if (pending) {                                // stage - 1 was scored in this call
+      if (!launch_decode_fused<T, D, G>(a, stage, chunks_of(stage), chunks_of(stage - 1), st)) {
+        launch_topk(a, stage - 1, chunks_of(stage - 1), st);
+        launch_decode_score<T, D, G>(a, stage, chunks_of(stage), st);
+      }
+    } else {
+      launch_decode_score<T, D, G>(a, stage, chunks_of(stage), st);
+    }
+    pending = true;
+    if (stage + 1 == S || !due[stage + 1]) {
+      launch_topk(a, stage, chunks_of(stage), st);
+      pending = false;
+    }
+  }
+  if (!due[S - 1]) DSA_LAUNCH("prune_assemble", k_assemble, dim3(a.R), dim3(kTopkThreads), st, a);
+}
+
+template <typename T, int D>
+static hipError_t launch_cached_typed(const PruneArgs& a, const bool* due, hipStream_t st) {
+  switch (a.kv.Hq / a.kv.Hkv) {
+    case 1: launch_decode_cached<T, D, 1>(a, due, st); break;
+    case 2: launch_decode_cached<T, D, 2>(a, due, st); break;
+    case 4: launch_decode_cached<T, D, 4>(a, due, st); break;
+    case 8: launch_decode_cached<T, D, 8>(a, due, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prune_cached(const PruneArgs& a, const bool* due, int dtype, hipStream_t st) {
+  if (!a.kv.decode || !a.mid_end) return hipErrorInvalidValue;
+  if (dtype == 1) {
+    if (a.kv.D == 128) return launch_cached_typed<uint16_t, 128>(a, due, st);
+    if (a.kv.D == 64) return launch_cached_typed<uint16_t, 64>(a, due, st);
+  } else {
+    if (a.kv.D == 128) return launch_cached_typed<float, 128>(a, due, st);
+    if (a.kv.D == 64) return launch_cached_typed<float, 64>(a, due, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <typename T, int D>

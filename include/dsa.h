@@ -140,6 +140,46 @@ dsa_status dsa_prune_select(const dsa_shape* shape, const void* q, const void* k
                             const dsa_params* p, int32_t* idx,
                             void* ws, size_t ws_bytes, uint64_t* visited, void* stream);
 
+/* ---- Decoding with remembered stage outputs ("mask caching") -------------
+ * InfiniteHiP page, section 3.4 "Sparse Attention Mask Caching": stage i of
+ * the pruning recomputes its output only at decode steps where
+ * step mod refresh[i] == 0 (the page's presets: (16, 8, 4) default,
+ * (32, 16, 8) fast, (96, 24, 8) flash) and otherwise reuses the output it
+ * remembered. A due stage scores the current output of the stage before it
+ * (remembered or just recomputed; the whole middle of the current context for
+ * stage 1) with the newest query. The index row of every step is the sinks,
+ * the last stage's remembered keys, and every position from the end of the
+ * stage-1 middle those keys descend from up to the newest token (keys that
+ * left the window since that stage-1 refresh were never scored and stay).
+ *
+ * The mask cache is caller-owned DEVICE memory of dsa_mask_cache_bytes()
+ * bytes, 16-byte aligned, one per (layer, batch) stream of decode steps. It
+ * begins with int32 status[B]: after each call, status[b] is 1 if the row of
+ * sequence b did not fit in idx_width (the row then holds its first idx_width
+ * keys), else 0. The rest is opaque. The first call on a cache must be at a
+ * step where every stage is due (e.g. step 0); the library cannot check this.
+ * Calls on one cache must not overlap. */
+
+/* Bytes of the mask cache for this decode shape and params. */
+dsa_status dsa_mask_cache_bytes(const dsa_shape* shape, const dsa_params* p, size_t* out_bytes);
+
+/* Row width for cached decoding: n_sink + keep[n_stages-1] + n_window +
+ * chunk[0] - 1 + max_growth rounded up to 64, where max_growth is the most
+ * tokens a sequence gains between stage-1 refreshes (refresh[0] - 1 when each
+ * step appends one token); -1 if p is invalid or max_growth < 0. */
+int32_t dsa_cached_index_width(const dsa_params* p, int32_t max_growth);
+
+/* One decode step of hierarchical pruning with remembered stages (see above).
+ * shape.mode must be DSA_DECODE; refresh is a HOST array [n_stages] of
+ * intervals >= 1; step >= 0 is the decode step counter shared by the batch;
+ * idx [B, idx_width] with idx_width a multiple of 64 and >= dsa_index_width(p),
+ * 16-byte aligned; ws, visited, stream as for dsa_prune_select. Rows are
+ * written as by dsa_prune_select (ascending, -1 padded). */
+dsa_status dsa_prune_select_cached(const dsa_shape* shape, const void* q, const void* k,
+                                   const dsa_params* p, const int32_t* refresh, int64_t step,
+                                   void* cache, size_t cache_bytes, int32_t* idx, int32_t idx_width,
+                                   void* ws, size_t ws_bytes, uint64_t* visited, void* stream);
+
 /* out[h, t] = sum over p in row, p <= t, of softmax_p(scale * q_{h,t} . k_p) v_p,
  * for every query t of each block (row = idx row of the block; negative
  * entries are ignored, as are entries beyond the block's last query).

@@ -103,3 +103,40 @@ def test_attention_rejects_before_launch():
 def test_status_strings(lib):
     for code in range(5):
         assert _lib.status_str(code).startswith("DSA_")
+
+
+def test_mask_cache_sizes_and_widths():
+    d = Shape(DSA_DECODE, DSA_BF16, 4, 32, 8, 128, 1 << 20, seq_lens=16)
+    nbytes = _lib.mask_cache_bytes(d, P3)
+    assert nbytes % 256 == 0
+    assert nbytes >= 4 * 4 + 3 * 4 * (32768 // 256) * 4       # status + three kept-start lists
+    assert _lib.cached_index_width(P3, 0) == _lib.index_width(P3)
+    assert _lib.cached_index_width(P3, 15) == 5504            # 5439 + 15 -> 5454 -> 5504
+    assert _lib.cached_index_width(P3, -1) == -1
+    with pytest.raises(_lib.DsaError) as ei:                  # prefill has no mask cache
+        _lib.mask_cache_bytes(Shape(DSA_PREFILL, DSA_BF16, 1, 32, 8, 128, 4096), P2)
+    assert ei.value.status == DSA_ERR_INVALID_ARG
+
+
+def test_prune_select_cached_rejects_before_launch():
+    d = Shape(DSA_DECODE, DSA_BF16, 1, 32, 8, 128, 1 << 20, seq_lens=16)
+    cb = _lib.mask_cache_bytes(d, P3)
+    ws = _lib.workspace_bytes(d, P3)
+    L = _lib.cached_index_width(P3, 15)
+    cases = [
+        (dict(refresh=(16, 8, 0)), DSA_ERR_INVALID_ARG),                       # interval 0
+        (dict(step=-1), DSA_ERR_INVALID_ARG),                                  # negative step
+        (dict(width=L - 1), DSA_ERR_INVALID_ARG),                              # not a multiple of 64
+        (dict(width=64), DSA_ERR_INVALID_ARG),                                 # narrower than a row
+        (dict(cache_bytes=cb - 256), DSA_ERR_INVALID_ARG),                     # small cache
+        (dict(ws_bytes=64), DSA_ERR_WORKSPACE),                                # small workspace
+        (dict(cache=0), DSA_ERR_INVALID_ARG),                                  # no cache
+        (dict(shape=Shape(DSA_PREFILL, DSA_BF16, 1, 32, 8, 128, 4096)), DSA_ERR_INVALID_ARG),
+    ]
+    for over, code in cases:
+        a = dict(shape=d, refresh=(16, 8, 4), step=0, cache=256, cache_bytes=cb, width=L, ws_bytes=ws)
+        a.update(over)
+        with pytest.raises(_lib.DsaError) as ei:
+            _lib.prune_select_cached_raw(a["shape"], 256, 256, P3, a["refresh"], a["step"], a["cache"],
+                                         a["cache_bytes"], 256, a["width"], 256, a["ws_bytes"])
+        assert ei.value.status == code, over
