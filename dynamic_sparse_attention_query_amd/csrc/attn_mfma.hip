@@ -311,27 +311,42 @@ __global__ void __launch_bounds__(64 * NH * QH) k_prefill_mfma(AttnArgs a) {
 // 64 banks once.
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
+// A buffer resource over `bytes` bytes at `base` (raw dword loads; offsets at
+// or beyond `bytes` read as zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
 // d = 128 variant of k_prefill_mfma whose K/V tiles go straight from global
-// memory into LDS (global_load_lds_dwordx4: a wave-wide load fills 1 KB of LDS
-// in lane order, here 4 swizzled rows), so no registers stage the tiles and
+// memory into LDS (buffer_load_dwordx4 ... lds: a wave-wide load fills 1 KB of
+// LDS in lane order, here 4 swizzled rows), so no registers stage the tiles and
 // no LDS stores copy them. The loads of tile i+1 are issued after the barrier
-// that retires tile i-1 and run under tile i's products; invisible and
-// padding rows load key 0 and are removed by the mask.
+// that retires tile i-1 and run under tile i's products.
+//
+// Tile entry e (0..63) lives in LDS row 16 * (e % 4) + e / 4: the 16 lanes of
+// lane group g = 4 * wave + lane / 16 take entries 4g .. 4g+3 (one 16-byte
+// load of the index row) and their four row loads land in rows 16u + g. Keys
+// in any order give the same result (softmax and P.V are sums over keys), so
+// the permutation only has to be the same for K, V and the positions used by
+// the mask. Addresses are 32-bit offsets into buffer resources of this kv
+// head's K and V; invisible entries load key 0 (or, beyond the tensor, zeros
+// through the resource's range check) and are removed by the mask.
 template <int NH, int QH>
-__global__ void __launch_bounds__(64 * NH * QH) k_prefill_mfma_lds(AttnArgs a) {
+__global__ void __launch_bounds__(64 * NH * QH, 2) k_prefill_mfma_lds(AttnArgs a) {
   constexpr int D = 128;
   constexpr int NWV = NH * QH;        // waves
   constexpr int KS = D / 16;          // 16-wide steps over d
   constexpr int DT = D / 32;          // 32-row tiles of O^T
-  constexpr int LPT = 64 / (4 * NWV); // wave-wide loads per tile and matrix (4 rows each)
-  static_assert(64 % (4 * NWV) == 0, "tile loads must split evenly");
+  static_assert(NWV == 4, "each of 16 lane groups loads four entries of a 64-entry tile");
   // Two tile buffers as distinct objects, used alternately by the unrolled
   // loop below: the compiler can then tell the reads of one buffer from the
   // loads landing in the other and need not wait for those loads.
   __shared__ __align__(16) uint16_t sk0[64 * D], sk1[64 * D];
   __shared__ __align__(16) uint16_t sv0[64 * D], sv1[64 * D];
-  __shared__ __align__(16) int spos0[64], spos1[64];
-  __shared__ int sflag0[2][NWV], sflag1[2][NWV];
+  __shared__ __align__(16) int spos0[64], spos1[64];     // positions by LDS row
+  __shared__ __align__(16) int sflag0[NWV], sflag1[NWV];   // per wave: 1 = needs the mask, 2 = visible keys
   // the buffers are written only by the loads below: make that visible
   asm volatile("" ::"r"(sk0), "r"(sk1), "r"(sv0), "r"(sv1) : "memory");
 
@@ -352,7 +367,8 @@ __global__ void __launch_bounds__(64 * NH * QH) k_prefill_mfma_lds(AttnArgs a) {
   const int b = work / (kv.Hkv * HG);
   const int g = hg / HG;
   const int s = m * 64, e = s + 64;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   // transpose-read addressing of this lane (see lds_read_tr16): row
   // (lane & 15) >> 2 of four, column 4 * (lane & 3), groups 1 and 3 on d-rows 16..31
@@ -363,9 +379,10 @@ __global__ void __launch_bounds__(64 * NH * QH) k_prefill_mfma_lds(AttnArgs a) {
   const int wq_lo = s + qsplit * QH * 32;         // the workgroup's query range
   const int wq_hi = wq_lo + QH * 32 - 1;
   const uint16_t* Q = static_cast<const uint16_t*>(a.q);
-  const uint16_t* K = static_cast<const uint16_t*>(a.k);
-  const uint16_t* V = static_cast<const uint16_t*>(a.v);
   const size_t kvbase = (static_cast<size_t>(b) * kv.Hkv + g) * kv.T;
+  const uint32_t kv_bytes = static_cast<uint32_t>(kv.T) * D * 2;
+  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(static_cast<const uint16_t*>(a.k) + kvbase * D, kv_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(static_cast<const uint16_t*>(a.v) + kvbase * D, kv_bytes);
 
   bf16x8_t qf[KS];
   {
@@ -382,60 +399,63 @@ __global__ void __launch_bounds__(64 * NH * QH) k_prefill_mfma_lds(AttnArgs a) {
 
   const int r = b * kv.nblk + m;
   const int32_t* row = a.idx ? a.idx + static_cast<size_t>(r) * a.L : nullptr;
-  const int n_ent = row ? a.L : e;
+  const int n_ent = row ? a.L : e;                // a multiple of 64 (index width, or e)
   const int n_tiles = (n_ent + 63) / 64;
-  // Row entries are fetched two tiles ahead and kept raw: judging them (a
-  // use of the loaded value) happens only when their tile is issued, so no
-  // wait for them, which would also wait for every earlier load, comes early.
-  auto raw_entry = [&](int i) { return i < n_ent ? (row ? row[i] : i) : -1; };
-  auto visible = [&](int p) { return (p < 0 || p > wq_hi) ? -1 : p; };
-  // load u of this wave covers tile rows (u * NWV + w) * 4 .. +3; the lane
-  // takes row + (lane >> 4) and LDS slot lane & 15
-  const int lrow = lane >> 4, lslot = lane & 15;
-  int pr[LPT], prn[LPT];                          // raw entries of the next two tiles
-  // tile with raw entries pr -> buffers: the loads, the positions for the
-  // mask and the tile's mask / visibility flags
-  auto issue = [&](uint16_t* skb, uint16_t* svb, int* sposb, int (*sflagb)[NWV]) __attribute__((always_inline)) {
-    bool need = false, any = false;
-#pragma unroll
-    for (int u = 0; u < LPT; ++u) {
-      const int base = (u * NWV + w) * 4;
-      const int rr = base + lrow;
-      const int p = visible(pr[u]);
-      need |= (p < 0 || p > wq_lo);
-      any |= (p >= 0);
-      if (lslot == 0) sposb[rr] = p;
-      const size_t off = (kvbase + max(p, 0)) * D + (lslot ^ swz(rr)) * 8;
-      __builtin_amdgcn_global_load_lds(K + off, skb + base * D, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(V + off, svb + base * D, 16, 0, 0);
+  const int lg = 4 * w + (lane >> 4);             // this lane's group: entries 4lg .. 4lg+3
+  const int lslot = lane & 15;                    // and its 16-byte piece of each row
+  // raw entries of tile ti (fetched two tiles ahead; judged only when issued)
+  auto raw_entries = [&](int ti) {
+    int4 v = make_int4(-1, -1, -1, -1);
+    if (ti < n_tiles) {
+      if (row) {
+        v = *reinterpret_cast<const int4*>(row + ti * 64 + 4 * lg);
+      } else {
+        const int p0 = ti * 64 + 4 * lg;
+        v = make_int4(p0, p0 + 1, p0 + 2, p0 + 3);
+      }
     }
-    const unsigned long long nb = __ballot(need), ab = __ballot(any);
-    if (lane == 0) { sflagb[0][w] = nb != 0; sflagb[1][w] = ab != 0; }
+    return v;
   };
-  auto advance = [&](int ti) __attribute__((always_inline)) {   // entries: tile ti+2 -> pr, ti+3 -> prn
+  int4 pr, prn;                                   // entries of the next two tiles
+  // tile with entries pr -> buffers: the row loads, the positions for the
+  // mask and the tile's mask / visibility flags
+  auto issue = [&](uint16_t* skb, uint16_t* svb, int* sposb, int* sflagb) __attribute__((always_inline)) {
+    const int pp[4] = {pr.x, pr.y, pr.z, pr.w};
 #pragma unroll
-    for (int u = 0; u < LPT; ++u) {
-      pr[u] = prn[u];
-      prn[u] = raw_entry((ti + 3) * 64 + (u * NWV + w) * 4 + lrow);
+    for (int u = 0; u < 4; ++u) {
+      const int rr = 16 * u + lg;                 // LDS row of entry 4lg + u
+      const int off = max(pp[u], 0) * (D * 2) + ((lslot ^ swz(rr)) << 4);
+      const int lbase = (16 * u + 4 * w) * D;     // the wave's 4 rows of this load
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void_t*)(skb + lbase), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void_t*)(svb + lbase), 16, off, 0, 0, 0);
     }
+    int pv = pr.x;                                // lanes 0..3 of the group store entries 0..3
+    pv = lslot == 1 ? pr.y : pv;
+    pv = lslot == 2 ? pr.z : pv;
+    pv = lslot == 3 ? pr.w : pv;
+    if (lslot < 4) sposb[16 * lslot + lg] = pv;
+    // unsigned: padding (-1) is the largest
+    const unsigned umax = max(max(static_cast<unsigned>(pr.x), static_cast<unsigned>(pr.y)),
+                              max(static_cast<unsigned>(pr.z), static_cast<unsigned>(pr.w)));
+    const unsigned umin = min(min(static_cast<unsigned>(pr.x), static_cast<unsigned>(pr.y)),
+                              min(static_cast<unsigned>(pr.z), static_cast<unsigned>(pr.w)));
+    const unsigned long long nb = __ballot(umax > static_cast<unsigned>(wq_lo));
+    const unsigned long long ab = __ballot(umin <= static_cast<unsigned>(wq_hi));
+    if (lane == 0) sflagb[w] = (nb != 0 ? 1 : 0) | (ab != 0 ? 2 : 0);
   };
   // one tile: products from buffers c, loads of the next tile into buffers n
-  auto step = [&](int ti, const uint16_t* skc, const uint16_t* svc, const int* sposc, const int (*sflagc)[NWV],
-                  uint16_t* skn, uint16_t* svn, int* sposn, int (*sflagn)[NWV]) __attribute__((always_inline)) {
+  auto step = [&](int ti, const uint16_t* skc, const uint16_t* svc, const int* sposc, const int* sflagc,
+                  uint16_t* skn, uint16_t* svn, int* sposn, int* sflagn) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0);                // this wave's loads of tile ti are in LDS
     __syncthreads();                              // everyone's; and tile ti-1 is retired
     if (ti + 1 < n_tiles) {
       issue(skn, svn, sposn, sflagn);
-      advance(ti);
+      pr = prn;
+      prn = raw_entries(ti + 3);
     }
-    int flag = 2;
-#pragma unroll
-    for (int i = 0; i < NWV; ++i) {
-      flag |= sflagc[0][i] ? 1 : 0;
-      if (sflagc[1][i]) flag &= ~2;
-    }
-    flag = __builtin_amdgcn_readfirstlane(flag);
-    if (flag & 2) return;                         // nothing visible in this tile
+    const int4 f4 = *reinterpret_cast<const int4*>(sflagc);
+    const int flag = __builtin_amdgcn_readfirstlane(f4.x | f4.y | f4.z | f4.w);
+    if (!(flag & 2)) return;                      // nothing visible in this tile
     // S^T tiles [key tile kt]: 32 keys x this wave's 32 queries
     f32x16_t sacc[2];
 #pragma unroll
@@ -452,6 +472,7 @@ __global__ void __launch_bounds__(64 * NH * QH) k_prefill_mfma_lds(AttnArgs a) {
       }
     }
     if (flag & 1) {
+      // accumulator element 4rn + c of key tile kt is LDS row 32kt + 8rn + 4hi + c
       const unsigned t = static_cast<unsigned>(q0 + l32);   // padding (-1) compares as the largest
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -464,6 +485,10 @@ __global__ void __launch_bounds__(64 * NH * QH) k_prefill_mfma_lds(AttnArgs a) {
             if (static_cast<unsigned>(pp[c]) > t) sacc[kt][rn * 4 + c] = -INFINITY;
         }
     }
+    // online softmax per query column, base 2. The running max is raised
+    // only when a score exceeds it by more than 2^8 (p stays <= 256, exact in
+    // the final normalisation). The row sum adds the bf16-rounded p that the
+    // P.V product uses, two at a time.
     {
       float mx = -INFINITY;
 #pragma unroll
@@ -474,17 +499,10 @@ __global__ void __launch_bounds__(64 * NH * QH) k_prefill_mfma_lds(AttnArgs a) {
       const bool raise = mx > mrun + 8.0f;
       const float m_use = raise ? mx : mrun;
       const float alpha = __builtin_amdgcn_exp2f(mrun - m_use);
-      float ps = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float pz = __builtin_amdgcn_exp2f(fmaf(sacc[kt][i], a.scale_log2, -m_use));
-          sacc[kt][i] = pz;
-          ps += pz;
-        }
-      ps += __shfl_xor(ps, 32, 64);
-      lrun = lrun * alpha + ps;
+        for (int i = 0; i < 16; ++i) sacc[kt][i] = __builtin_amdgcn_exp2f(fmaf(sacc[kt][i], a.scale_log2, -m_use));
       mrun = m_use;
       if (__ballot(raise)) {
 #pragma unroll
@@ -492,15 +510,22 @@ __global__ void __launch_bounds__(64 * NH * QH) k_prefill_mfma_lds(AttnArgs a) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
       }
+      lrun *= alpha;
     }
+    const bf16x2_t ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+    float ps = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int kt = ks >> 1, half = ks & 1;
       u32x4_t u;
-      u[0] = pack_bf16x2(sacc[kt][half * 8 + 0], sacc[kt][half * 8 + 1]);
-      u[1] = pack_bf16x2(sacc[kt][half * 8 + 2], sacc[kt][half * 8 + 3]);
-      u[2] = pack_bf16x2(sacc[kt][half * 8 + 4], sacc[kt][half * 8 + 5]);
-      u[3] = pack_bf16x2(sacc[kt][half * 8 + 6], sacc[kt][half * 8 + 7]);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        // the packed pair feeds the sum from its own register (reading it
+        // back out of the vector has been compiled to the wrong element)
+        const uint32_t pw = pack_bf16x2(sacc[kt][half * 8 + 2 * x], sacc[kt][half * 8 + 2 * x + 1]);
+        ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw), ones, ps, false);
+        u[x] = pw;
+      }
       const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, u);
       const int r0 = ks * 16 + hi * 4 + tr_row, r1 = r0 + 8;
 #pragma unroll
@@ -513,21 +538,15 @@ __global__ void __launch_bounds__(64 * NH * QH) k_prefill_mfma_lds(AttnArgs a) {
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb, o[dt], 0, 0, 0);
       }
     }
+    lrun += ps + __shfl_xor(ps, 32, 64);
   };
 
   // prologue: tile 0 into buffers 0, entries of tiles 1 and 2 in hand
-#pragma unroll
-  for (int u = 0; u < LPT; ++u) {
-    const int rr = (u * NWV + w) * 4 + lrow;
-    pr[u] = raw_entry(rr);
-    prn[u] = raw_entry(64 + rr);
-  }
+  pr = raw_entries(0);
+  prn = raw_entries(1);
   issue(sk0, sv0, spos0, sflag0);
-#pragma unroll
-  for (int u = 0; u < LPT; ++u) {
-    pr[u] = prn[u];
-    prn[u] = raw_entry(128 + (u * NWV + w) * 4 + lrow);
-  }
+  pr = prn;
+  prn = raw_entries(2);
   for (int ti = 0; ti < n_tiles; ti += 2) {
     step(ti, sk0, sv0, spos0, sflag0, sk1, sv1, spos1, sflag1);
     if (ti + 1 < n_tiles) step(ti + 1, sk1, sv1, spos1, sflag1, sk0, sv0, spos0, sflag0);
@@ -571,10 +590,14 @@ static void launch_mfma(const AttnArgs& a, hipStream_t st) {
 bool launch_prefill_mfma(const AttnArgs& a, hipStream_t st) {
   if (a.kv.decode || a.kv.bq != 64) return false;
   const int G = a.kv.Hq / a.kv.Hkv;
-  if (a.kv.D == 128) {
+  // the LDS-direct kernel addresses a kv head's rows with 32-bit offsets and
+  // reads each index row 16 bytes at a time
+  const bool lds_ok = static_cast<long long>(a.kv.T) * 256 <= 0x7fffffffLL &&
+                      (reinterpret_cast<uintptr_t>(a.idx) & 15) == 0;
+  if (a.kv.D == 128 && lds_ok) {
     if (G >= 4) { launch_mfma_lds<4, 1>(a, st); return true; }
     if (G == 2) { launch_mfma_lds<2, 2>(a, st); return true; }
-    if (G == 1) { launch_mfma_lds<1, 2>(a, st); return true; }
+    if (G == 1) { launch_mfma<128, 1, 2>(a, st); return true; }
   } else if (a.kv.D == 64) {
     if (G >= 4) { launch_mfma<64, 4, 1>(a, st); return true; }
     if (G == 2) { launch_mfma<64, 2, 2>(a, st); return true; }
