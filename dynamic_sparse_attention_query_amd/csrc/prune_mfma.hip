@@ -19,8 +19,13 @@
 // flight. Rows reach the matrix-core operand layout through a per-wave LDS
 // staging buffer: a wave-wide 16-byte load covers whole rows (PPR lanes per
 // row, 4 rows per load at d = 128) instead of touching 32 rows at once, and
-// the fragments are then read from LDS. The query block of each head takes the
-// same path. The chunk score (max over all heads) is reduced in LDS.
+// the fragments are then read from LDS. The buffer holds one 32-row set
+// (8.5 KB), so the query block of each head is staged in two halves and the
+// first split's two representatives are fetched as two rounds: the rows in
+// flight never exceed T sets per wave, the kernel stays under 168 registers
+// and three waves share each SIMD, which hides more of each round's
+// dependent gather latency than two waves with twice the rows each. The chunk
+// score (max over all heads) is reduced in LDS.
 #include "prune_common.h"
 
 namespace dsa {
@@ -33,24 +38,18 @@ constexpr int kRowGroup = 16;           // neighbouring query blocks scheduled t
 constexpr int kScoreGroups = 2;         // T: 32-chunk tournament groups per wave
 
 template <int D, int T>
-__global__ void __launch_bounds__(256) k_score_prefill_mfma(PruneArgs a, int stage, int ncg) {
-  static_assert(T == 1 || T == 2, "the staging buffer holds 64 rows");
+__global__ void __launch_bounds__(256, 3) k_score_prefill_mfma(PruneArgs a, int stage, int ncg) {
   constexpr int KS = D / 16;
   constexpr int CPB = 32 * T;           // chunks per workgroup
   constexpr int PPR = D / 8;            // 16-byte pieces per row
   constexpr int RPI = 64 / PPR;         // rows per wave-wide load
   constexpr int LPS = 32 / RPI;         // loads per 32-row set
   constexpr int KROW = D + 8;           // staging row stride (bf16): shifts banks by 4 words per row
-  __shared__ __align__(16) uint16_t sbuf[4][64 * KROW];
-  __shared__ int spos[4][2 * T][32];
+  __shared__ __align__(16) uint16_t sbuf[4][32 * KROW];
+  __shared__ int spos[4][T][32];
   __shared__ float red[4][CPB];
 
   const KvLayout& kv = a.kv;
-  // XCD-aware order: consecutive workgroup ids go to different XCDs. Groups
-  // of kRowGroup neighbouring query blocks are dealt to the XCDs in turn, and
-  // each XCD walks its groups one at a time over all chunk groups, so the
-  // blocks running together on one XCD score the same chunk positions with
-  // similar queries and share the key rows in that XCD's L2.
   const int x = blockIdx.x & 7, i = blockIdx.x >> 3;
   const int per_group = ncg * kRowGroup;
   const int rbl = i / per_group, rem = i - rbl * per_group;
@@ -64,7 +63,8 @@ __global__ void __launch_bounds__(256) k_score_prefill_mfma(PruneArgs a, int sta
   if (nc <= (a.keep[stage] >> a.lchunk[stage])) return;    // stage keeps everything
   if (j0 >= nc) return;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int piece = lane % PPR, rsub = lane / PPR;          // loader view of the lane
   uint16_t* buf = sbuf[w];
@@ -79,17 +79,19 @@ __global__ void __launch_bounds__(256) k_score_prefill_mfma(PruneArgs a, int sta
   const uint16_t* Q = static_cast<const uint16_t*>(a.q);
   const uint16_t* K = static_cast<const uint16_t*>(a.k);
 
-  // Sets of 32 key rows: the column owners publish the positions in spos,
-  // the loader lanes fetch whole rows, and the rows are staged two sets at a
-  // time (slots 0 and 1 of the buffer).
-#define DSA_FETCH(base, set, v)                                                                 \
-  _Pragma("unroll") for (int u = 0; u < LPS; ++u) {                                           \
-    const int p_ = spos[w][set][u * RPI + rsub];                                              \
-    (v)[u] = *reinterpret_cast<const u32x4_t*>((base) + static_cast<size_t>(p_) * D + piece * 8); \
-  }
-#define DSA_STAGE(slot, v)                                                                     \
-  _Pragma("unroll") for (int u = 0; u < LPS; ++u)                                             \
-    *reinterpret_cast<u32x4_t*>(buf + ((slot) * 32 + u * RPI + rsub) * KROW + piece * 8) = (v)[u];
+  // a set of 32 rows at the positions published in spos[w][set]
+  auto fetch = [&](const uint16_t* base, int set, u32x4_t (&v)[LPS]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < LPS; ++u) {
+      const int p_ = spos[w][set][u * RPI + rsub];
+      v[u] = *reinterpret_cast<const u32x4_t*>(base + static_cast<size_t>(p_) * D + piece * 8);
+    }
+  };
+  auto stage_set = [&](const u32x4_t (&v)[LPS]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < LPS; ++u)
+      *reinterpret_cast<u32x4_t*>(buf + (u * RPI + rsub) * KROW + piece * 8) = v[u];
+  };
 
   float best[T];
 #pragma unroll
@@ -100,21 +102,20 @@ __global__ void __launch_bounds__(256) k_score_prefill_mfma(PruneArgs a, int sta
     bf16x8_t qf[2][KS];
     {
       const uint16_t* qblk = Q + ((static_cast<size_t>(b) * kv.Hq + h) * kv.T + s) * D;
-      u32x4_t v[2 * LPS];
 #pragma unroll
-      for (int u = 0; u < 2 * LPS; ++u)
-        v[u] = *reinterpret_cast<const u32x4_t*>(qblk + (u * RPI + rsub) * D + piece * 8);
+      for (int qt = 0; qt < 2; ++qt) {
+        u32x4_t v[LPS];
 #pragma unroll
-      for (int u = 0; u < 2 * LPS; ++u)
-        *reinterpret_cast<u32x4_t*>(buf + (u * RPI + rsub) * KROW + piece * 8) = v[u];
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
+        for (int u = 0; u < LPS; ++u)
+          v[u] = *reinterpret_cast<const u32x4_t*>(qblk + (qt * 32 + u * RPI + rsub) * D + piece * 8);
+        stage_set(v);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          qf[qt][ks] = *reinterpret_cast<const bf16x8_t*>(buf + (qt * 32 + l32) * KROW + ks * 16 + hi * 8);
+          qf[qt][ks] = *reinterpret_cast<const bf16x8_t*>(buf + l32 * KROW + ks * 16 + hi * 8);
+      }
     }
-    // sigma of the staged key in slot `slot` for this lane's chunk
-    auto sigma_of = [&](int slot) __attribute__((always_inline)) {
+    // sigma of the staged key for this lane's chunk column
+    auto sigma_staged = [&]() __attribute__((always_inline)) {
       f32x16_t acc[2];
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt)
@@ -122,8 +123,7 @@ __global__ void __launch_bounds__(256) k_score_prefill_mfma(PruneArgs a, int sta
         for (int i2 = 0; i2 < 16; ++i2) acc[qt][i2] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8_t kf =
-            *reinterpret_cast<const bf16x8_t*>(buf + (slot * 32 + l32) * KROW + ks * 16 + hi * 8);
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(buf + l32 * KROW + ks * 16 + hi * 8);
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt)
           acc[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[qt][ks], kf, acc[qt], 0, 0, 0);
@@ -135,63 +135,42 @@ __global__ void __launch_bounds__(256) k_score_prefill_mfma(PruneArgs a, int sta
         for (int i2 = 0; i2 < 16; ++i2) m = fmaxf(m, acc[qt][i2]);
       return fmaxf(m, __shfl_xor(m, 32, 64));
     };
+    // one round: the rows at offsets off[t] of every group, scored
+    auto round = [&](const int (&off)[T], float (&sg)[T]) __attribute__((always_inline)) {
+      if (hi == 0) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) spos[w][t][l32] = st[t] + off[t];
+      }
+      u32x4_t v[T][LPS];
+#pragma unroll
+      for (int t = 0; t < T; ++t) fetch(Kg, t, v[t]);
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        stage_set(v[t]);
+        sg[t] = sigma_staged();
+      }
+    };
 
     float sa[T];
-    if (l == 1) {
-      if (hi == 0) {
+    int lo[T], hi_r[T];
+    {
+      int off[T];
 #pragma unroll
-        for (int t = 0; t < T; ++t) spos[w][t][l32] = st[t];
-      }
-      u32x4_t v0[LPS], v1[LPS];
-      DSA_FETCH(Kg, 0, v0);
-      if (T > 1) { DSA_FETCH(Kg, T - 1, v1); }
-      DSA_STAGE(0, v0);
-      if (T > 1) { DSA_STAGE(1, v1); }
+      for (int t = 0; t < T; ++t) off[t] = 0;
+      round(off, sa);
 #pragma unroll
-      for (int t = 0; t < T; ++t) sa[t] = sigma_of(t);
-    } else {
-      // first split: both representatives of every group in one round
-      const int mid0 = l >> 1;
-      int lo[T], hi_r[T];
-      if (hi == 0) {
+      for (int t = 0; t < T; ++t) { lo[t] = 0; hi_r[t] = l - 1; }
+    }
+    for (int wd = l >> 1; wd >= 1; wd >>= 1) {
+      int mid[T];
+      float sm[T];
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-          spos[w][2 * t][l32] = st[t];
-          spos[w][2 * t + 1][l32] = st[t] + mid0;
-        }
-      }
-      {
-        u32x4_t v0[LPS], v1[LPS], v2[LPS], v3[LPS];
-        DSA_FETCH(Kg, 0, v0);
-        DSA_FETCH(Kg, 1, v1);
-        if (T > 1) { DSA_FETCH(Kg, 2 * T - 2, v2); DSA_FETCH(Kg, 2 * T - 1, v3); }
+      for (int t = 0; t < T; ++t) mid[t] = (lo[t] + hi_r[t] + 1) >> 1;
+      round(mid, sm);
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-          if (t == 0) { DSA_STAGE(0, v0); DSA_STAGE(1, v1); }
-          else        { DSA_STAGE(0, v2); DSA_STAGE(1, v3); }
-          const float s0 = sigma_of(0), s1 = sigma_of(1);
-          if (s1 > s0) { lo[t] = mid0; hi_r[t] = l - 1; sa[t] = s1; }
-          else         { lo[t] = 0;    hi_r[t] = mid0 - 1; sa[t] = s0; }
-        }
-      }
-      for (int wd = mid0 >> 1; wd >= 1; wd >>= 1) {
-        int mid[T];
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-          mid[t] = (lo[t] + hi_r[t] + 1) >> 1;
-          if (hi == 0) spos[w][t][l32] = st[t] + mid[t];
-        }
-        u32x4_t v0[LPS], v1[LPS];
-        DSA_FETCH(Kg, 0, v0);
-        if (T > 1) { DSA_FETCH(Kg, T - 1, v1); }
-        DSA_STAGE(0, v0);
-        if (T > 1) { DSA_STAGE(1, v1); }
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-          const float sm = sigma_of(t);
-          if (sm > sa[t]) { lo[t] = mid[t]; sa[t] = sm; }
-          else            { hi_r[t] = mid[t] - 1; }
-        }
+      for (int t = 0; t < T; ++t) {
+        if (sm[t] > sa[t]) { lo[t] = mid[t]; sa[t] = sm[t]; }
+        else               { hi_r[t] = mid[t] - 1; }
       }
     }
 #pragma unroll
@@ -209,8 +188,6 @@ __global__ void __launch_bounds__(256) k_score_prefill_mfma(PruneArgs a, int sta
     }
   }
 }
-#undef DSA_FETCH
-#undef DSA_STAGE
 
 // bf16 prefill with query blocks of 64: score stage `stage` on the matrix cores.
 bool launch_score_prefill_mfma(const PruneArgs& a, int stage, int max_chunks, hipStream_t st,
