@@ -72,6 +72,7 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cached", action="store_true", help="skip decoding with remembered stages")
+    ap.add_argument("--no-other", action="store_true", help="skip the batch-32 paged and 3M-token decodes")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-ref", action="store_true",
@@ -467,6 +468,56 @@ def prefill_bench(args, res):
 
 
 # --------------------------------------------------------------------------- #
+# the other decode workloads: batch-32 ragged paged, and 3M tokens            #
+# --------------------------------------------------------------------------- #
+def other_decode(args, name, reps=20):
+    """Graph-replayed decode step (prune_select + sparse_attn) of workload
+    `name`: microseconds per step, and HBM GB/s of its algorithmic bytes
+    (SelectRep rows counted by the kernels + K/V rows of every kept key)."""
+    import torch
+    from dynamic_sparse_attention_query_amd import _lib, api, gen
+    from dynamic_sparse_attention_query_amd.inputs import params_of, to_device
+
+    t0 = time.time()
+    case = gen.make_case(name)
+    cfg = case.cfg
+    dev = to_device(case)
+    del case
+    log(f"{name} inputs ready in {time.time() - t0:.1f}s")
+    p = params_of(cfg)
+    q = dev.q[0].contiguous()
+    kw = dict(seq_lens=dev.seq_lens, block_table=dev.block_table, t=dev.t)
+    vis = torch.zeros(len(p.chunk), dtype=torch.int64, device="cuda")
+    idx = api.prune_select(q, dev.k, p, visited=vis, **kw)
+    out = api.sparse_attn(q, dev.k, dev.v, idx, p, **kw)
+    torch.cuda.synchronize()
+    row_bytes = cfg.d * 2
+    nbytes = float(vis.sum().item()) * row_bytes + int((idx >= 0).sum().item()) * cfg.hkv * 2 * row_bytes
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        api.prune_select(q, dev.k, p, out=idx.view(-1), **kw)
+        api.sparse_attn(q, dev.k, dev.v, idx, p, out=out, **kw)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    res = {"us_per_step": round(us, 2), "batch": cfg.batch, "us_per_token": round(us / cfg.batch, 2),
+           "algorithmic_bytes_per_step": int(nbytes), "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
+           "pct_peak": round(100 * nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 2),
+           "tokens_in_context": int(dev.seq_lens.sum().item()),
+           "note": "back-to-back graph replays of one step (same query, one KV copy)"}
+    log(f"{name}: {us:.1f} us/step, {res['gbps']} GB/s")
+    del dev, idx, out, g
+    torch.cuda.empty_cache()
+    return res
+
+
+# --------------------------------------------------------------------------- #
 # CPU oracle baseline                                                         #
 # --------------------------------------------------------------------------- #
 def cpu_baseline(args, case, res):
@@ -511,6 +562,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     case = decode_bench(args, res)
+    if not args.no_other:
+        res["c4"] = other_decode(args, "c4")
+        res["c5"] = other_decode(args, "c5")
     if not args.no_prefill:
         prefill_bench(args, res)
     if not args.no_cpu:
@@ -556,6 +610,10 @@ def main():
                                     "all_stages_due_step_us": round(c["full_refresh_step_us"], 2),
                                     "no_stage_due_step_us": round(c["reuse_step_us"], 2),
                                     "speedup_vs_uncached": round(dec["us_per_step"] / c["us_per_token"], 2)}
+    if "c4" in res:
+        line["decode_b32_paged_ragged"] = res["c4"]
+    if "c5" in res:
+        line["decode_3m"] = res["c5"]
     if "prefill" in res:
         pf = res["prefill"]
         line["prefill_128k"] = {"ms": round(pf["ms"], 2), "tflops": round(pf["tflops"], 2),

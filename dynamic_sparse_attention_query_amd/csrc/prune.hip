@@ -358,6 +358,7 @@ __global__ void __launch_bounds__(kTopkThreads) k_assemble(PruneArgs a) {
 // ------------------------------------------------------------------------- //
 // decode scoring: one query per row                                         //
 // ------------------------------------------------------------------------- //
+constexpr int kChunkPages = 4;          // page ids a paged chunk loads up front
 // One lane group's SelectRep tournaments: the G query heads of kv head g over
 // the chunk of l = chunk[stage] keys starting at st; returns the best
 // representative score over the heads.
@@ -371,9 +372,30 @@ __device__ __forceinline__ float score_group(const PruneArgs& a, int stage, int 
   const int l = a.chunk[stage];
   float best = -INFINITY;
   auto dot = [&](const Row& kr, int hh) { return group16_sum(kr.dot(q[hh])); };
+  // Paged K: the chunk covers at most kChunkPages pages in the common case;
+  // their ids are loaded once, together, so a tournament step costs one
+  // dependent load (the row) instead of two (table entry, then row).
+  const bool paged = kv.block_table != nullptr;
+  const int pg0 = paged ? st >> kv.page_shift : 0;
+  const int npg = paged ? ((st + l - 1) >> kv.page_shift) - pg0 + 1 : 0;
+  const bool hoist = paged && npg <= kChunkPages;
+  int pid[kChunkPages];
+#pragma unroll
+  for (int i = 0; i < kChunkPages; ++i)
+    pid[i] = hoist && i < npg ? kv.block_table[static_cast<size_t>(b) * kv.max_pages + pg0 + i] : 0;
   auto row_at = [&](int pos) {
+    size_t off;
+    if (hoist) {
+      const int k = (pos >> kv.page_shift) - pg0;
+      int page = pid[0];
+#pragma unroll
+      for (int i = 1; i < kChunkPages; ++i) page = k == i ? pid[i] : page;
+      off = ((static_cast<size_t>(page) * kv.Hkv + g) * kv.page_size + (pos & (kv.page_size - 1))) * kv.D;
+    } else {
+      off = kv_offset(kv, b, g, pos);
+    }
     Row x;
-    x.load(K + kv_offset(kv, b, g, pos) + li * EPL);
+    x.load(K + off + li * EPL);
     return x;
   };
 
@@ -697,6 +719,7 @@ static const char* const kTopkNames[kMaxStages] = {"prune_topk_stage1", "prune_t
 static const char* const kFusedNames[kMaxStages] = {"", "prune_topk1_score2", "prune_topk2_score3",
                                                     "prune_topk3_score4"};
 constexpr int kSpecMaxChunk = 64;       // chunks this small preload their first three splits
+constexpr long long kFuseMaxWorkgroups = 2048;   // largest fused top-K + scoring launch
 
 template <typename T, int D, int G>
 static void launch_decode_score(const PruneArgs& a, int stage, int max_chunks, hipStream_t st) {
@@ -735,6 +758,10 @@ static bool launch_decode_fused(const PruneArgs& a, int stage, int max_chunks, i
     const int cpw = 16 / a.kv.Hkv;
     // at least one workgroup: workgroup 0 writes the selected stage's starts
     const dim3 grid(std::max(1, (max_chunks + cpw - 1) / cpw), a.R);
+    // every workgroup repeats the row's selection: worth it only while that
+    // redundant work is small next to a kernel boundary (one sequence); a
+    // batch takes the one-workgroup-per-row selection kernel instead
+    if (static_cast<long long>(grid.x) * grid.y > kFuseMaxWorkgroups) return false;
     const bool spec = a.chunk[stage] >= 8 && a.chunk[stage] <= kSpecMaxChunk;
     const char* nm = kFusedNames[stage];
     if (sel_chunks <= kTopkThreads * 4) {
