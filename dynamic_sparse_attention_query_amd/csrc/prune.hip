@@ -273,31 +273,45 @@ __device__ __forceinline__ void select_row(uint32_t (&key)[E], int j0, int nc, i
   }
 }
 
-// The index row of row r: sinks [0, sink_hi), the n_sel kept chunks of 2^lg
-// keys starting at sel[] (ascending), then every position from win_lo (the end
-// of the stage-1 middle the kept chunks descend from) up to the newest key,
-// then -1 padding; 16-byte stores, L a multiple of 64. A row that would not
-// fit (possible only when stages are remembered across steps) keeps its first
-// L entries and is flagged in row_status.
-__device__ __forceinline__ void write_index_row(const PruneArgs& a, int r, const Geo& geo, const int* sel,
-                                                int n_sel, int lg, int win_lo) {
-  const int l = 1 << lg;
-  const int win0 = geo.sink_hi + n_sel * l;
-  const int n_win = max(0, geo.e - win_lo);
-  int32_t* row = a.idx + static_cast<size_t>(r) * a.L;
-  for (int i4 = threadIdx.x; i4 < (a.L >> 2); i4 += kTopkThreads) {
-    int v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = 4 * i4 + u;
-      if (i < geo.sink_hi) v[u] = i;
-      else if (i < win0) v[u] = sel[(i - geo.sink_hi) >> lg] + ((i - geo.sink_hi) & (l - 1));
-      else if (i < win0 + n_win) v[u] = win_lo + (i - win0);
-      else v[u] = -1;
-    }
-    reinterpret_cast<int4*>(row)[i4] = make_int4(v[0], v[1], v[2], v[3]);
+// The index row of row r is sinks [0, sink_hi), the n_sel kept chunks of l
+// keys (ascending), every position from win_lo (the end of the stage-1 middle
+// the kept chunks descend from) up to the newest key, then -1 padding; L is a
+// multiple of 64. The kept chunks are written by whoever selects them
+// (write_chunk_entries); write_row_rest writes everything else, so no part of
+// the row waits for another. A row that would not fit (possible only when
+// stages are remembered across steps) keeps its first L entries and is
+// flagged in row_status.
+__device__ __forceinline__ void write_chunk_entries(int32_t* row, int L, int i0, int st, int l) {
+  if (((i0 | l) & 3) == 0) {
+    for (int x = 0; x < l && i0 + x < L; x += 4)
+      *reinterpret_cast<int4*>(row + i0 + x) = make_int4(st + x, st + x + 1, st + x + 2, st + x + 3);
+  } else {
+    for (int x = 0; x < l && i0 + x < L; ++x) row[i0 + x] = st + x;
   }
-  if (a.row_status && threadIdx.x == 0) a.row_status[r] = win0 + n_win > a.L ? 1 : 0;
+}
+
+__device__ __forceinline__ void write_row_rest(const PruneArgs& a, int r, const Geo& geo, int n_sel, int l,
+                                               int win_lo) {
+  const int win0 = geo.sink_hi + n_sel * l;        // kept chunks fill [sink_hi, win0)
+  const int end = win0 + max(0, geo.e - win_lo);
+  int32_t* row = a.idx + static_cast<size_t>(r) * a.L;
+  auto value = [&](int i) { return i < geo.sink_hi ? i : i < end ? win_lo + (i - win0) : -1; };
+  const int n4 = a.L >> 2;
+  const int head4 = (geo.sink_hi + 3) >> 2;         // 16-byte slots holding sinks
+  const int tail4 = min(win0 >> 2, n4);             // first slot holding window or padding
+  const int n_rest = head4 + (n4 - tail4);
+  for (int k = threadIdx.x; k < n_rest; k += kTopkThreads) {
+    const int i4 = k < head4 ? k : tail4 + (k - head4);
+    const int i = 4 * i4;
+    if (i + 4 <= geo.sink_hi || i >= win0) {
+      *reinterpret_cast<int4*>(row + i) = make_int4(value(i), value(i + 1), value(i + 2), value(i + 3));
+    } else {                                        // a slot shared with kept-chunk entries
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (i + u < geo.sink_hi || i + u >= win0) row[i + u] = value(i + u);
+    }
+  }
+  if (a.row_status && threadIdx.x == 0) a.row_status[r] = end > a.L ? 1 : 0;
 }
 
 // One workgroup per row: select the stage's kept chunks, write their starts
@@ -306,7 +320,6 @@ template <int E>
 __global__ void __launch_bounds__(kTopkThreads) k_topk(PruneArgs a, int stage) {
   __shared__ SelectLds L;
   __shared__ int sprev[kMaxKeptChunks];
-  __shared__ int ssel[kMaxKeptChunks];             // final stage: kept starts in output order
 
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
@@ -326,33 +339,37 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk(PruneArgs a, int stage) {
   if (stage > 0) load_kept_starts(a, stage - 1, r, sprev);
   const int n_sel = nc <= kc ? nc : kc;
   int32_t* out = stage_starts(a, stage, r);
+  int32_t* row = a.idx + static_cast<size_t>(r) * a.L;
+  const int win_lo = last ? stage_mid_end(a, stage, r, geo) : 0;
   // stores only after every load has been consumed (inside the selection):
   // stores share the vector memory counter with loads, so an earlier store
-  // would hold up their wait
+  // would hold up their wait. After the last stage each kept chunk writes
+  // its own entries of the index row.
   select_row<E>(key, j0, nc, kc, L, [&](int j, int pos) {
     const int st = stage == 0 ? a.n_sink + (j << lg) : sprev[j >> sh] + ((j & ((1 << sh) - 1)) << lg);
     out[pos] = st;
-    if (last) ssel[pos] = st;
+    if (last) write_chunk_entries(row, a.L, geo.sink_hi + pos * l, st, l);
   });
   if (tid == 0) record_stage(a, stage, r, n_sel, geo);
-  if (!last) return;
-  __syncthreads();
-  write_index_row(a, r, geo, ssel, n_sel, lg, stage_mid_end(a, stage, r, geo));
+  if (last) write_row_rest(a, r, geo, n_sel, l, win_lo);
 }
 
 // The last stage's remembered output turned into the index row of the current
 // step (mask caching, when the last stage is not due): one workgroup per row.
 __global__ void __launch_bounds__(kTopkThreads) k_assemble(PruneArgs a) {
-  __shared__ int ssel[kMaxKeptChunks];
   const int r = blockIdx.x;
   const int last = a.n_stages - 1;
   int b, s, e;
   row_bounds(a.kv, r, b, s, e);
   const Geo geo = make_geo(s, e, a.n_sink, a.n_window, a.chunk[0]);
+  const int l = a.chunk[last];
   const int n_sel = max(0, min(a.cnt[r * kMaxStages + last], a.keep[last] >> a.lchunk[last]));
-  load_kept_starts(a, last, r, ssel);
-  __syncthreads();
-  write_index_row(a, r, geo, ssel, n_sel, a.lchunk[last], a.mid_end[r * kMaxStages + last]);
+  const int win_lo = a.mid_end[r * kMaxStages + last];
+  const int32_t* starts = stage_starts(a, last, r);
+  int32_t* row = a.idx + static_cast<size_t>(r) * a.L;
+  for (int c = threadIdx.x; c < n_sel; c += kTopkThreads)
+    write_chunk_entries(row, a.L, geo.sink_hi + c * l, starts[c], l);
+  write_row_rest(a, r, geo, n_sel, l, win_lo);
 }
 
 // ------------------------------------------------------------------------- //
@@ -362,7 +379,7 @@ constexpr int kChunkPages = 4;          // page ids a paged chunk loads up front
 // One lane group's SelectRep tournaments: the G query heads of kv head g over
 // the chunk of l = chunk[stage] keys starting at st; returns the best
 // representative score over the heads.
-template <typename T, int D, int G, bool SPEC>
+template <typename T, int D, int G, bool SPEC, bool PAGED>
 __device__ __forceinline__ float score_group(const PruneArgs& a, int stage, int b, int g, int li, int st,
                                              const RowSlice<T, D / 16> (&q)[G]) {
   constexpr int EPL = D / 16;
@@ -372,30 +389,38 @@ __device__ __forceinline__ float score_group(const PruneArgs& a, int stage, int 
   const int l = a.chunk[stage];
   float best = -INFINITY;
   auto dot = [&](const Row& kr, int hh) { return group16_sum(kr.dot(q[hh])); };
-  // Paged K: the chunk covers at most kChunkPages pages in the common case;
-  // their ids are loaded once, together, so a tournament step costs one
-  // dependent load (the row) instead of two (table entry, then row).
-  const bool paged = kv.block_table != nullptr;
-  const int pg0 = paged ? st >> kv.page_shift : 0;
-  const int npg = paged ? ((st + l - 1) >> kv.page_shift) - pg0 + 1 : 0;
-  const bool hoist = paged && npg <= kChunkPages;
+  // Paged K (compile-time): the chunk covers at most kChunkPages pages in the
+  // common case; their ids are loaded once, together, so a tournament step
+  // costs one dependent load (the row) instead of two (table entry, then row).
+  int pg0 = 0, npg = 0;
+  bool hoist = false;
   int pid[kChunkPages];
+  if constexpr (PAGED) {
+    pg0 = st >> kv.page_shift;
+    npg = ((st + l - 1) >> kv.page_shift) - pg0 + 1;
+    hoist = npg <= kChunkPages;
 #pragma unroll
-  for (int i = 0; i < kChunkPages; ++i)
-    pid[i] = hoist && i < npg ? kv.block_table[static_cast<size_t>(b) * kv.max_pages + pg0 + i] : 0;
+    for (int i = 0; i < kChunkPages; ++i)
+      pid[i] = hoist && i < npg ? kv.block_table[static_cast<size_t>(b) * kv.max_pages + pg0 + i] : 0;
+  }
+  const T* Kc = K + (static_cast<size_t>(b) * kv.Hkv + g) * kv.T * D + li * EPL;   // contiguous K
   auto row_at = [&](int pos) {
-    size_t off;
-    if (hoist) {
-      const int k = (pos >> kv.page_shift) - pg0;
-      int page = pid[0];
-#pragma unroll
-      for (int i = 1; i < kChunkPages; ++i) page = k == i ? pid[i] : page;
-      off = ((static_cast<size_t>(page) * kv.Hkv + g) * kv.page_size + (pos & (kv.page_size - 1))) * kv.D;
-    } else {
-      off = kv_offset(kv, b, g, pos);
-    }
     Row x;
-    x.load(K + off + li * EPL);
+    if constexpr (PAGED) {
+      size_t off;
+      if (hoist) {
+        const int k = (pos >> kv.page_shift) - pg0;
+        int page = pid[0];
+#pragma unroll
+        for (int i = 1; i < kChunkPages; ++i) page = k == i ? pid[i] : page;
+        off = ((static_cast<size_t>(page) * kv.Hkv + g) * kv.page_size + (pos & (kv.page_size - 1))) * D;
+      } else {
+        off = kv_offset(kv, b, g, pos);
+      }
+      x.load(K + off + li * EPL);
+    } else {
+      x.load(Kc + static_cast<size_t>(pos) * D);
+    }
     return x;
   };
 
@@ -502,7 +527,7 @@ __device__ __forceinline__ float score_group(const PruneArgs& a, int stage, int 
 // splits are decided from them, trading up to 1/8 more row reads for two
 // fewer dependent load rounds. Group results are max-reduced per chunk in
 // LDS.
-template <typename T, int D, int G, bool SPEC>
+template <typename T, int D, int G, bool SPEC, bool PAGED>
 __global__ void __launch_bounds__(256, G > 4 ? 2 : ((SPEC || sizeof(T) == 4) ? 4 : 8))
 k_score_decode(PruneArgs a, int stage) {
   constexpr int EPL = D / 16;
@@ -544,7 +569,7 @@ k_score_decode(PruneArgs a, int stage) {
   const bool active = j < nc;
 
   float best = -INFINITY;
-  if (active) best = score_group<T, D, G, SPEC>(a, stage, b, g, li, st, q);
+  if (active) best = score_group<T, D, G, SPEC, PAGED>(a, stage, b, g, li, st, q);
   if (li == 0) red[gi] = best;
   __syncthreads();
   if (tid < cpw) {
@@ -563,7 +588,7 @@ k_score_decode(PruneArgs a, int stage) {
 // so the two steps meet at one kernel boundary instead of two; workgroup 0
 // also writes the kept starts and their count for the stages after. The
 // tournaments are those of k_score_decode.
-template <typename T, int D, int G, bool SPEC, int E>
+template <typename T, int D, int G, bool SPEC, int E, bool PAGED>
 __global__ void __launch_bounds__(256, 2) k_topk_score_decode(PruneArgs a, int stage) {
   constexpr int EPL = D / 16;
   using Row = RowSlice<T, EPL>;
@@ -618,7 +643,7 @@ __global__ void __launch_bounds__(256, 2) k_topk_score_decode(PruneArgs a, int s
   const bool active = j < nc;
   const int st = ssel[min(j >> sh, n_sel - 1)] + ((j & ((1 << sh) - 1)) << a.lchunk[stage]);
   float best = -INFINITY;
-  if (active) best = score_group<T, D, G, SPEC>(a, stage, b, g, li, st, q);
+  if (active) best = score_group<T, D, G, SPEC, PAGED>(a, stage, b, g, li, st, q);
   if (li == 0) red[gi] = best;
   __syncthreads();
   if (tid < cpw) {
@@ -727,10 +752,14 @@ static void launch_decode_score(const PruneArgs& a, int stage, int max_chunks, h
   if (max_chunks <= 0) return;
   dim3 grid((max_chunks + cpw - 1) / cpw, a.R);
   const char* nm = kScoreNames[stage];
-  if (a.chunk[stage] >= 8 && a.chunk[stage] <= kSpecMaxChunk)
-    DSA_LAUNCH(nm, (k_score_decode<T, D, G, true>), grid, dim3(256), st, a, stage);
-  else
-    DSA_LAUNCH(nm, (k_score_decode<T, D, G, false>), grid, dim3(256), st, a, stage);
+  const bool spec = a.chunk[stage] >= 8 && a.chunk[stage] <= kSpecMaxChunk;
+  if (a.kv.block_table) {
+    if (spec) DSA_LAUNCH(nm, (k_score_decode<T, D, G, true, true>), grid, dim3(256), st, a, stage);
+    else      DSA_LAUNCH(nm, (k_score_decode<T, D, G, false, true>), grid, dim3(256), st, a, stage);
+  } else {
+    if (spec) DSA_LAUNCH(nm, (k_score_decode<T, D, G, true, false>), grid, dim3(256), st, a, stage);
+    else      DSA_LAUNCH(nm, (k_score_decode<T, D, G, false, false>), grid, dim3(256), st, a, stage);
+  }
 }
 
 static void launch_topk(const PruneArgs& a, int stage, int max_chunks, hipStream_t st) {
@@ -764,12 +793,14 @@ static bool launch_decode_fused(const PruneArgs& a, int stage, int max_chunks, i
     if (static_cast<long long>(grid.x) * grid.y > kFuseMaxWorkgroups) return false;
     const bool spec = a.chunk[stage] >= 8 && a.chunk[stage] <= kSpecMaxChunk;
     const char* nm = kFusedNames[stage];
+    // the fused launch is for one sequence: contiguous K only
+    if (a.kv.block_table) return false;
     if (sel_chunks <= kTopkThreads * 4) {
-      if (spec) DSA_LAUNCH(nm, (k_topk_score_decode<T, D, G, true, 4>), grid, dim3(256), st, a, stage);
-      else      DSA_LAUNCH(nm, (k_topk_score_decode<T, D, G, false, 4>), grid, dim3(256), st, a, stage);
+      if (spec) DSA_LAUNCH(nm, (k_topk_score_decode<T, D, G, true, 4, false>), grid, dim3(256), st, a, stage);
+      else      DSA_LAUNCH(nm, (k_topk_score_decode<T, D, G, false, 4, false>), grid, dim3(256), st, a, stage);
     } else if (sel_chunks <= kTopkThreads * 16) {
-      if (spec) DSA_LAUNCH(nm, (k_topk_score_decode<T, D, G, true, 16>), grid, dim3(256), st, a, stage);
-      else      DSA_LAUNCH(nm, (k_topk_score_decode<T, D, G, false, 16>), grid, dim3(256), st, a, stage);
+      if (spec) DSA_LAUNCH(nm, (k_topk_score_decode<T, D, G, true, 16, false>), grid, dim3(256), st, a, stage);
+      else      DSA_LAUNCH(nm, (k_topk_score_decode<T, D, G, false, 16, false>), grid, dim3(256), st, a, stage);
     } else {
       return false;
     }
