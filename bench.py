@@ -40,23 +40,33 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary, or None if there is none or the kernel source changed since."""
+def _counter_summary(name: str):
+    """Machine-readable fields of a committed rocprofv3 counter summary under
+    profiles/, or None if it is missing or its kernel sources changed since."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "decode_1m_counters.md")
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     kv = {}
     for line in open(path):
         line = line.strip()
-        for key in ("traffic_kernel", "traffic_bytes_per_launch", "source_sha256", "source_files"):
-            if line.startswith(key + ":"):
-                kv[key] = line.split(":", 1)[1].strip()
-    if kv.get("traffic_kernel") != kernel or "source_files" not in kv:
+        if ":" in line and not line.startswith(("|", "#", "rocprofv3")):
+            key, val = line.split(":", 1)
+            if key.isidentifier():
+                kv[key] = val.strip()
+    if "source_files" not in kv:
         return None
     h = hashlib.sha256(b"".join(open(os.path.join(ROOT, f), "rb").read() for f in kv["source_files"].split()))
     if h.hexdigest() != kv.get("source_sha256"):
+        return None
+    return kv
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None if there is none or the kernel source changed since."""
+    kv = _counter_summary("decode_1m_counters.md")
+    if not kv or kv.get("traffic_kernel") != kernel:
         return None
     return int(kv["traffic_bytes_per_launch"])
 
@@ -623,6 +633,12 @@ def main():
                                 "attn_tflop": round(pf["attn_tflop"], 2),
                                 "prune_ms": round(pf["prune_ms"], 2), "attn_ms": round(pf["attn_ms"], 2),
                                 "kernels_ms": pf["kernels_ms"]}
+        kv = _counter_summary("prefill_128k_counters.md")
+        if kv and "prefill_hbm_read_bytes" in kv:
+            rb = int(kv["prefill_hbm_read_bytes"])
+            line["prefill_128k"]["hbm_read_bytes_measured"] = rb
+            line["prefill_128k"]["hbm_read_gbps"] = round(rb / (pf["ms"] * 1e-3) / 1e9, 1)
+            line["prefill_128k"]["hbm_read_pct_peak"] = round(100 * rb / (pf["ms"] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2)
     if "cpu" in res:
         line["cpu_baseline"] = res["cpu"]
     print(json.dumps(line), flush=True)
