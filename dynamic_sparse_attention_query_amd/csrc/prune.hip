@@ -379,7 +379,7 @@ constexpr int kChunkPages = 4;          // page ids a paged chunk loads up front
 // One lane group's SelectRep tournaments: the G query heads of kv head g over
 // the chunk of l = chunk[stage] keys starting at st; returns the best
 // representative score over the heads.
-template <typename T, int D, int G, bool SPEC, bool PAGED>
+template <typename T, int D, int G, int SPEC, bool PAGED>
 __device__ __forceinline__ float score_group(const PruneArgs& a, int stage, int b, int g, int li, int st,
                                              const RowSlice<T, D / 16> (&q)[G]) {
   constexpr int EPL = D / 16;
@@ -434,7 +434,45 @@ __device__ __forceinline__ float score_group(const PruneArgs& a, int stage, int 
     for (int hh = 0; hh < G; ++hh) { sa[hh] = dot(k0, hh); lo[hh] = hi[hh] = 0; }
     nvis = 1;
     width = 1;
-  } else if (SPEC && l >= 8) {
+  } else if (SPEC == 4 && l >= 4) {
+    // the 4 keys that can represent the first two splits (positions i*l/4)
+    // in one round
+    const int u = l >> 2;
+    float sc4[G][4];
+    {
+      Row kr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kr[i] = row_at(st + i * u);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) sc4[hh][i] = dot(kr[i], hh);
+    }
+    int a1[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      int A = 0;
+      float s0 = sc4[hh][0];
+      if (sc4[hh][2] > s0) { A = 2; s0 = sc4[hh][2]; }
+      a1[hh] = A;
+      const float s2 = A ? sc4[hh][3] : sc4[hh][1];
+      if (s2 > s0) { A += 1; s0 = s2; }
+      lo[hh] = A * u;
+      hi[hh] = A * u + u - 1;
+      sa[hh] = s0;
+    }
+    if (a.visited) {
+      nvis = 2;                                 // split 1: keys 0 and l/2
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {          // split 2: distinct midpoints
+        bool f2 = true;
+#pragma unroll
+        for (int h2 = 0; h2 < hh; ++h2) f2 = f2 && (a1[h2] != a1[hh]);
+        nvis += f2 ? 1 : 0;
+      }
+    }
+    width = u;
+  } else if (SPEC == 8 && l >= 8) {
     const int u = l >> 3;
     float sc8[G][8];
     {
@@ -527,8 +565,8 @@ __device__ __forceinline__ float score_group(const PruneArgs& a, int stage, int 
 // splits are decided from them, trading up to 1/8 more row reads for two
 // fewer dependent load rounds. Group results are max-reduced per chunk in
 // LDS.
-template <typename T, int D, int G, bool SPEC, bool PAGED>
-__global__ void __launch_bounds__(256, G > 4 ? 2 : ((SPEC || sizeof(T) == 4) ? 4 : 8))
+template <typename T, int D, int G, int SPEC, bool PAGED>
+__global__ void __launch_bounds__(256, G > 4 ? 2 : ((SPEC == 8 || sizeof(T) == 4) ? 4 : 8))
 k_score_decode(PruneArgs a, int stage) {
   constexpr int EPL = D / 16;
   using Row = RowSlice<T, EPL>;
@@ -588,7 +626,7 @@ k_score_decode(PruneArgs a, int stage) {
 // so the two steps meet at one kernel boundary instead of two; workgroup 0
 // also writes the kept starts and their count for the stages after. The
 // tournaments are those of k_score_decode.
-template <typename T, int D, int G, bool SPEC, int E, bool PAGED>
+template <typename T, int D, int G, int SPEC, int E, bool PAGED>
 __global__ void __launch_bounds__(256, 2) k_topk_score_decode(PruneArgs a, int stage) {
   constexpr int EPL = D / 16;
   using Row = RowSlice<T, EPL>;
@@ -744,6 +782,12 @@ static const char* const kTopkNames[kMaxStages] = {"prune_topk_stage1", "prune_t
 static const char* const kFusedNames[kMaxStages] = {"", "prune_topk1_score2", "prune_topk2_score3",
                                                     "prune_topk3_score4"};
 constexpr int kSpecMaxChunk = 64;       // chunks this small preload their first three splits
+
+// Speculative first round of a decode tournament: chunks of 8..64 keys load
+// the 8 keys that can represent the first three splits at once, longer chunks
+// the 4 of the first two (8 rows would cost too many registers for the
+// stage-1 launch to keep every workgroup resident), shorter ones none.
+static int spec_of(int l) { return l >= 8 && l <= kSpecMaxChunk ? 8 : l > kSpecMaxChunk ? 4 : 0; }
 constexpr long long kFuseMaxWorkgroups = 2048;   // largest fused top-K + scoring launch
 
 template <typename T, int D, int G>
@@ -752,13 +796,15 @@ static void launch_decode_score(const PruneArgs& a, int stage, int max_chunks, h
   if (max_chunks <= 0) return;
   dim3 grid((max_chunks + cpw - 1) / cpw, a.R);
   const char* nm = kScoreNames[stage];
-  const bool spec = a.chunk[stage] >= 8 && a.chunk[stage] <= kSpecMaxChunk;
+  const int spec = spec_of(a.chunk[stage]);
   if (a.kv.block_table) {
-    if (spec) DSA_LAUNCH(nm, (k_score_decode<T, D, G, true, true>), grid, dim3(256), st, a, stage);
-    else      DSA_LAUNCH(nm, (k_score_decode<T, D, G, false, true>), grid, dim3(256), st, a, stage);
+    if (spec == 8)      DSA_LAUNCH(nm, (k_score_decode<T, D, G, 8, true>), grid, dim3(256), st, a, stage);
+    else if (spec == 4) DSA_LAUNCH(nm, (k_score_decode<T, D, G, 4, true>), grid, dim3(256), st, a, stage);
+    else                DSA_LAUNCH(nm, (k_score_decode<T, D, G, 0, true>), grid, dim3(256), st, a, stage);
   } else {
-    if (spec) DSA_LAUNCH(nm, (k_score_decode<T, D, G, true, false>), grid, dim3(256), st, a, stage);
-    else      DSA_LAUNCH(nm, (k_score_decode<T, D, G, false, false>), grid, dim3(256), st, a, stage);
+    if (spec == 8)      DSA_LAUNCH(nm, (k_score_decode<T, D, G, 8, false>), grid, dim3(256), st, a, stage);
+    else if (spec == 4) DSA_LAUNCH(nm, (k_score_decode<T, D, G, 4, false>), grid, dim3(256), st, a, stage);
+    else                DSA_LAUNCH(nm, (k_score_decode<T, D, G, 0, false>), grid, dim3(256), st, a, stage);
   }
 }
 
@@ -791,16 +837,18 @@ static bool launch_decode_fused(const PruneArgs& a, int stage, int max_chunks, i
     // redundant work is small next to a kernel boundary (one sequence); a
     // batch takes the one-workgroup-per-row selection kernel instead
     if (static_cast<long long>(grid.x) * grid.y > kFuseMaxWorkgroups) return false;
-    const bool spec = a.chunk[stage] >= 8 && a.chunk[stage] <= kSpecMaxChunk;
+    const int spec = spec_of(a.chunk[stage]);
     const char* nm = kFusedNames[stage];
     // the fused launch is for one sequence: contiguous K only
     if (a.kv.block_table) return false;
     if (sel_chunks <= kTopkThreads * 4) {
-      if (spec) DSA_LAUNCH(nm, (k_topk_score_decode<T, D, G, true, 4, false>), grid, dim3(256), st, a, stage);
-      else      DSA_LAUNCH(nm, (k_topk_score_decode<T, D, G, false, 4, false>), grid, dim3(256), st, a, stage);
+      if (spec == 8)      DSA_LAUNCH(nm, (k_topk_score_decode<T, D, G, 8, 4, false>), grid, dim3(256), st, a, stage);
+      else if (spec == 4) DSA_LAUNCH(nm, (k_topk_score_decode<T, D, G, 4, 4, false>), grid, dim3(256), st, a, stage);
+      else                DSA_LAUNCH(nm, (k_topk_score_decode<T, D, G, 0, 4, false>), grid, dim3(256), st, a, stage);
     } else if (sel_chunks <= kTopkThreads * 16) {
-      if (spec) DSA_LAUNCH(nm, (k_topk_score_decode<T, D, G, true, 16, false>), grid, dim3(256), st, a, stage);
-      else      DSA_LAUNCH(nm, (k_topk_score_decode<T, D, G, false, 16, false>), grid, dim3(256), st, a, stage);
+      if (spec == 8)      DSA_LAUNCH(nm, (k_topk_score_decode<T, D, G, 8, 16, false>), grid, dim3(256), st, a, stage);
+      else if (spec == 4) DSA_LAUNCH(nm, (k_topk_score_decode<T, D, G, 4, 16, false>), grid, dim3(256), st, a, stage);
+      else                DSA_LAUNCH(nm, (k_topk_score_decode<T, D, G, 0, 16, false>), grid, dim3(256), st, a, stage);
     } else {
       return false;
     }
