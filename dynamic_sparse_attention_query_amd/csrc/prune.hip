@@ -26,7 +26,6 @@ namespace dsa {
 // ------------------------------------------------------------------------- //
 constexpr int kTopkThreads = 256;
 constexpr int kTopkWaves = kTopkThreads / 64;
-constexpr int kTopkMaxE = 128;          // rows of up to 32768 chunks
 constexpr int kMaxKeptChunks = 8192;    // keep / chunk of any stage (validated by the API)
 
 __device__ __forceinline__ uint32_t wave_and_u32(uint32_t v) {
@@ -36,15 +35,16 @@ __device__ __forceinline__ uint32_t wave_or_u32(uint32_t v) {
   return static_cast<uint32_t>(wave_reduce_int(static_cast<int>(v), [](int x, int y) { return x | y; }));
 }
 
-// LDS of one row's top-K selection
+// LDS of one row's top-K selection by NW waves
+template <int NW = kTopkWaves>
 struct SelectLds {
-  uint32_t hist[2][kTopkWaves][256];
-  uint32_t sred[2][kTopkWaves];
-  uint32_t sscan[kTopkWaves];
+  uint32_t hist[2][NW][256];
+  uint32_t sred[2][NW];
+  uint32_t sscan[NW];
   int sdec[3];
-  int wcand[kTopkWaves];                         // small boundary digit: per-wave counts,
-  uint32_t ckey[kTopkWaves][64];                 // keys and chunk ids (each wave's share is
-  int cidx[kTopkWaves][64];                      // below 64: the digit holds at most 64 keys)
+  int wcand[NW];                                 // small boundary digit: per-wave counts,
+  uint32_t ckey[NW][64];                         // keys and chunk ids (each wave's share is
+  int cidx[NW][64];                              // below 64: the digit holds at most 64 keys)
   uint32_t sfin[2];
 };
 
@@ -64,20 +64,21 @@ __device__ __forceinline__ void load_keys(const PruneArgs& a, int stage, int r, 
 
 // The kept starts of stage `stage` for row r (at most keep/chunk of them)
 // into LDS; published by the caller's next barrier.
+template <int NT = kTopkThreads>
 __device__ __forceinline__ void load_kept_starts(const PruneArgs& a, int stage, int r, int* sp) {
   const int tid = threadIdx.x;
   const int kmax = a.keep[stage] >> a.lchunk[stage];
   const int32_t* src = stage_starts(a, stage, r);
-  for (int i0 = 0; i0 < kmax; i0 += 4 * kTopkThreads) {
+  for (int i0 = 0; i0 < kmax; i0 += 4 * NT) {
     int v[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * kTopkThreads + tid;
+      const int i = i0 + u * NT + tid;
       v[u] = i < kmax ? src[i] : 0;
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * kTopkThreads + tid;
+      const int i = i0 + u * NT + tid;
       if (i < kmax) sp[i] = v[u];
     }
   }
@@ -94,9 +95,11 @@ __device__ __forceinline__ void load_kept_starts(const PruneArgs& a, int stage, 
 // lowest-index keys equal to it until K are kept; emit(j, pos) is called for
 // every kept chunk j with its output slot pos = the number of kept chunks of
 // lower index. With nc <= kc every chunk j < nc is kept at slot j.
-template <int E, typename Emit>
-__device__ __forceinline__ void select_row(uint32_t (&key)[E], int j0, int nc, int kc, SelectLds& L,
+template <int E, int NT = kTopkThreads, typename Emit>
+__device__ __forceinline__ void select_row(uint32_t (&key)[E], int j0, int nc, int kc, SelectLds<NT / 64>& L,
                                            Emit&& emit) {
+  constexpr int kTopkThreads = NT;              // this selection's threads and waves
+  constexpr int kTopkWaves = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   // common bits of the row's keys (0 marks chunks beyond nc: real keys are
   // never 0); the histograms are cleared under the same barrier
@@ -300,7 +303,7 @@ __device__ __forceinline__ void write_row_rest(const PruneArgs& a, int r, const 
   const int head4 = (geo.sink_hi + 3) >> 2;         // 16-byte slots holding sinks
   const int tail4 = min(win0 >> 2, n4);             // first slot holding window or padding
   const int n_rest = head4 + (n4 - tail4);
-  for (int k = threadIdx.x; k < n_rest; k += kTopkThreads) {
+  for (int k = threadIdx.x; k < n_rest; k += blockDim.x) {
     const int i4 = k < head4 ? k : tail4 + (k - head4);
     const int i = 4 * i4;
     if (i + 4 <= geo.sink_hi || i >= win0) {
@@ -316,9 +319,9 @@ __device__ __forceinline__ void write_row_rest(const PruneArgs& a, int r, const 
 
 // One workgroup per row: select the stage's kept chunks, write their starts
 // (and their count), and after the last stage the index row.
-template <int E>
-__global__ void __launch_bounds__(kTopkThreads) k_topk(PruneArgs a, int stage) {
-  __shared__ SelectLds L;
+template <int E, int NT = kTopkThreads>
+__global__ void __launch_bounds__(NT) k_topk(PruneArgs a, int stage) {
+  __shared__ SelectLds<NT / 64> L;
   __shared__ int sprev[kMaxKeptChunks];
 
   const int r = blockIdx.x;
@@ -336,7 +339,7 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk(PruneArgs a, int stage) {
   uint32_t key[E];
   load_keys<E>(a, stage, r, j0, key);
   const int sh = stage > 0 ? a.lchunk[stage - 1] - lg : 0;
-  if (stage > 0) load_kept_starts(a, stage - 1, r, sprev);
+  if (stage > 0) load_kept_starts<NT>(a, stage - 1, r, sprev);
   const int n_sel = nc <= kc ? nc : kc;
   int32_t* out = stage_starts(a, stage, r);
   int32_t* row = a.idx + static_cast<size_t>(r) * a.L;
@@ -345,7 +348,7 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk(PruneArgs a, int stage) {
   // stores share the vector memory counter with loads, so an earlier store
   // would hold up their wait. After the last stage each kept chunk writes
   // its own entries of the index row.
-  select_row<E>(key, j0, nc, kc, L, [&](int j, int pos) {
+  select_row<E, NT>(key, j0, nc, kc, L, [&](int j, int pos) {
     const int st = stage == 0 ? a.n_sink + (j << lg) : sprev[j >> sh] + ((j & ((1 << sh) - 1)) << lg);
     out[pos] = st;
     if (last) write_chunk_entries(row, a.L, geo.sink_hi + pos * l, st, l);
@@ -367,7 +370,7 @@ __global__ void __launch_bounds__(kTopkThreads) k_assemble(PruneArgs a) {
   const int win_lo = a.mid_end[r * kMaxStages + last];
   const int32_t* starts = stage_starts(a, last, r);
   int32_t* row = a.idx + static_cast<size_t>(r) * a.L;
-  for (int c = threadIdx.x; c < n_sel; c += kTopkThreads)
+  for (int c = threadIdx.x; c < n_sel; c += blockDim.x)
     write_chunk_entries(row, a.L, geo.sink_hi + c * l, starts[c], l);
   write_row_rest(a, r, geo, n_sel, l, win_lo);
 }
@@ -630,7 +633,7 @@ template <typename T, int D, int G, int SPEC, int E, bool PAGED>
 __global__ void __launch_bounds__(256, 2) k_topk_score_decode(PruneArgs a, int stage) {
   constexpr int EPL = D / 16;
   using Row = RowSlice<T, EPL>;
-  __shared__ SelectLds L;
+  __shared__ SelectLds<> L;
   __shared__ int sprev[kMaxKeptChunks];
   __shared__ int ssel[kMaxKeptChunks];
   __shared__ float red[16];
@@ -814,10 +817,10 @@ static void launch_topk(const PruneArgs& a, int stage, int max_chunks, hipStream
     DSA_LAUNCH(nm, (k_topk<4>), dim3(a.R), dim3(kTopkThreads), st, a, stage);
   } else if (max_chunks <= kTopkThreads * 16) {
     DSA_LAUNCH(nm, (k_topk<16>), dim3(a.R), dim3(kTopkThreads), st, a, stage);
-  } else if (max_chunks <= kTopkThreads * 64) {
-    DSA_LAUNCH(nm, (k_topk<64>), dim3(a.R), dim3(kTopkThreads), st, a, stage);
+  } else if (max_chunks <= 1024 * 16) {   // large rows: 16 waves, 16 keys per thread
+    DSA_LAUNCH(nm, (k_topk<16, 1024>), dim3(a.R), dim3(1024), st, a, stage);
   } else {
-    DSA_LAUNCH(nm, (k_topk<kTopkMaxE>), dim3(a.R), dim3(kTopkThreads), st, a, stage);
+    DSA_LAUNCH(nm, (k_topk<32, 1024>), dim3(a.R), dim3(1024), st, a, stage);
   }
 }
 
