@@ -15,9 +15,12 @@ It follows the InfiniteHiP page (2502.08910), section 3.4:
 and the attention over the active key set as written on the InfLLM blog page
 ("Mathematical Formulation of Efficient Softmax Normalization") and as the
 masked softmax of the MInference page (section on the sparse-attention
-problem formulation), with causal masking inside the kernel; and, for decoding
+problem formulation), with causal masking inside the kernel; for decoding
 with remembered masks, the InfiniteHiP page's "Sparse Attention Mask Caching"
-(per-stage refresh intervals, stage 1 refreshed with the newest query).
+(per-stage refresh intervals, stage 1 refreshed with the newest query); and
+the MInference page's Block-Sparse head estimation ("Online Dynamic Index
+Estimation: Block-Sparse Heads (Algorithm 3)": mean pooling, block-causal
+pooled logits, top-k_b blocks per query head and block).
 
 Readings taken where the pages are silent or garbled (each is listed with its
 reason in the project's design notes):
@@ -39,7 +42,11 @@ reason in the project's design notes):
   * mask caching: one step counter per call for the whole batch; a due stage
     reads the current output of the stage before it (fresh or remembered);
     keys that slid out of the window since the stage-1 refresh a row descends
-    from were never scored and are kept with the window.
+    from were never scored and are kept with the window;
+  * block-sparse estimation: a key block is masked for query block m when it
+    lies strictly after it (j > m; the diagonal block stays); blocks are ranked
+    by the pooled logits in fp64 rounded to fp32 (the softmax and the scale are
+    monotone), ties to the lower block; each query head has its own rows.
 
 Every function here is pinned by tests/test_oracle.py against what the pages
 and the mathematics fix (closed forms, brute force, special cases reducing to
@@ -329,6 +336,61 @@ def pad_row(row: np.ndarray, width: int) -> np.ndarray:
     out = np.full(width, -1, dtype=np.int32)
     out[:len(row)] = row
     return out
+
+
+# --------------------------------------------------------------------------- #
+# MInference Block-Sparse heads: per-input block index estimation             #
+# ("Online Dynamic Index Estimation: Block-Sparse Heads (Algorithm 3)")       #
+# --------------------------------------------------------------------------- #
+def bs_pool(X: np.ndarray, block: int) -> np.ndarray:
+    """Step 1: the mean of every `block` consecutive token rows, per head.
+
+    X: [H, T, d] (T a multiple of block) -> [H, T/block, d] float64."""
+    X = np.asarray(X, dtype=np.float64)
+    H, T, d = X.shape
+    return X.reshape(H, T // block, block, d).mean(axis=2)
+
+
+def bs_block_scores(Qp: np.ndarray, Kp: np.ndarray, h: int, m: int) -> np.ndarray:
+    """Steps 2-3 ranking key of query block m for query head h: the pooled
+    logits q~_m . k~_j of key blocks j = 0..m (strictly later key blocks are
+    masked out), evaluated in fp64 and rounded once to fp32. The row softmax
+    of step 2 and the 1/sqrt(d) scale are monotone, so they do not change which
+    blocks score highest and are not applied.
+
+    Qp: [Hq, nblk, d], Kp: [Hkv, nblk, d] pooled; kv head of h is h // (Hq/Hkv)."""
+    G = Qp.shape[0] // Kp.shape[0]
+    return (Kp[h // G, :m + 1] @ Qp[h, m]).astype(np.float32)
+
+
+def bs_select(scores: np.ndarray, k_blocks: int) -> np.ndarray:
+    """Step 3: the k_b key blocks with the highest scores (ties to the lower
+    block index), ascending; every block when there are no more than k_b."""
+    return top_k(scores, k_blocks)
+
+
+def bs_rows(Q: np.ndarray, K, block: int, k_blocks: int) -> List[List[np.ndarray]]:
+    """Step 4's block index lists as index rows: for every query head h and
+    query block m, the ascending key positions of its selected blocks.
+
+    Q: [Hq, T, d], K: [Hkv, T, d] (one sequence). Returns rows[h][m]."""
+    Qp = bs_pool(Q, block)
+    Kp = bs_pool(np.asarray(K[:, :Q.shape[1]]), block)
+    Hq, nblk = Qp.shape[0], Qp.shape[1]
+    rows = []
+    for h in range(Hq):
+        rh = []
+        for m in range(nblk):
+            sel = bs_select(bs_block_scores(Qp, Kp, h, m), k_blocks)
+            rh.append((sel[:, None] * block + np.arange(block)[None, :]).reshape(-1).astype(np.int64))
+        rows.append(rh)
+    return rows
+
+
+def bs_index_width(block: int, k_blocks: int) -> int:
+    """Width of a block-sparse index row: k_b blocks of `block` positions,
+    rounded up to 64."""
+    return (block * k_blocks + 63) // 64 * 64
 
 
 # --------------------------------------------------------------------------- #

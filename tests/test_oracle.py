@@ -514,3 +514,146 @@ def test_cached_decode_rejects_missing_records():
     p = ref.Params(1, (32, 8), (256, 64), 16, 64)
     with pytest.raises(ValueError):
         ref.prune_decode_cached(grid(rng, (4, 16)), K, 1100, p, (16, 4), 3, [None, None])
+
+
+# --------------------------------------------------------------------------- #
+# f2: block-sparse estimation (MInference page, "Online Dynamic Index         #
+# Estimation: Block-Sparse Heads (Algorithm 3)")                              #
+# --------------------------------------------------------------------------- #
+def _int_grid(rng, shape):
+    return rng.integers(-8, 9, size=shape)
+
+
+def test_block_sparse_pool_is_integer_block_mean():
+    rng = np.random.default_rng(40)
+    X = _int_grid(rng, (3, 64 * 7, 16))
+    P = ref.bs_pool(X.astype(np.float32) / 8, 64)
+    assert P.shape == (3, 7, 16)
+    csum = np.concatenate([np.zeros((3, 1, 16), np.int64), np.cumsum(X, axis=1)], axis=1)
+    sums = csum[:, 64::64] - csum[:, 0:-1:64]                  # integer block sums
+    assert np.array_equal(P * 512, sums.astype(np.float64))   # mean of k/8 over 64 = sum/512
+    const = np.broadcast_to(np.arange(5, dtype=np.float32)[None, :, None, None], (2, 5, 64, 4))
+    assert np.array_equal(ref.bs_pool(const.reshape(2, 320, 4), 64)[0, :, 0], np.arange(5.0))
+
+
+def test_block_sparse_scores_are_exact_block_causal_logits():
+    rng = np.random.default_rng(41)
+    Hq, Hkv, nb, d = 4, 2, 9, 32
+    Qi, Ki = _int_grid(rng, (Hq, 64 * nb, d)), _int_grid(rng, (Hkv, 64 * nb, d))
+    Qp = ref.bs_pool(Qi.astype(np.float32) / 8, 64)
+    Kp = ref.bs_pool(Ki.astype(np.float32) / 8, 64)
+    for h in range(Hq):
+        for m in range(nb):
+            sc = ref.bs_block_scores(Qp, Kp, h, m)
+            assert sc.dtype == np.float32 and len(sc) == m + 1      # no key block after m
+            qs = [int(v) for v in Qi[h, 64 * m:64 * m + 64].sum(axis=0)]
+            for j in range(m + 1):
+                ks = [int(v) for v in Ki[h // 2, 64 * j:64 * j + 64].sum(axis=0)]
+                exact = sum(a * b for a, b in zip(qs, ks))           # integer numerator over 2^18
+                assert sc[j] == np.float32(exact / 2.0 ** 18)
+
+
+def test_block_sparse_select_is_argtopk_of_block_softmax():
+    """Ranking pooled logits equals ranking the masked block softmax of step 2
+    (scale 1/sqrt(d), future blocks at -inf), checked against a full sort."""
+    rng = np.random.default_rng(42)
+    nb, d, kb = 40, 16, 7
+    Qp = rng.normal(size=(1, nb, d))
+    Kp = rng.normal(size=(1, nb, d))
+    for m in range(nb):
+        sc = ref.bs_block_scores(Qp, Kp, 0, m)
+        sel = ref.bs_select(sc, kb)
+        logits = np.full(nb, -np.inf)
+        logits[:m + 1] = (Kp[0, :m + 1] @ Qp[0, m]) / math.sqrt(d)
+        A = np.exp(logits - logits.max())
+        A /= A.sum()
+        want = sorted(range(nb), key=lambda j: (-A[j], j))[:min(kb, m + 1)]
+        assert list(sel) == sorted(want)
+        assert A[sel].min() >= np.sort(A)[::-1][min(kb, m + 1) - 1]
+
+
+def test_block_sparse_select_ties_go_to_lower_blocks():
+    sc = np.array([1, 3, 3, 2, 3, 3], dtype=np.float32)
+    assert list(ref.bs_select(sc, 3)) == [1, 2, 4]
+    assert list(ref.bs_select(sc, 10)) == list(range(6))
+    brute = sorted(range(6), key=lambda j: (-sc[j], j))[:4]
+    assert list(ref.bs_select(sc, 4)) == sorted(brute)
+
+
+def test_block_sparse_rows_structure():
+    rng = np.random.default_rng(43)
+    Q = grid(rng, (2, 64 * 12, 8))
+    K = grid(rng, (1, 64 * 12, 8))
+    kb = 5
+    rows = ref.bs_rows(Q, K, 64, kb)
+    assert len(rows) == 2 and all(len(r) == 12 for r in rows)
+    for h in range(2):
+        for m, row in enumerate(rows[h]):
+            assert len(row) == 64 * min(m + 1, kb)
+            assert np.all(np.diff(row) > 0) and row.max() < 64 * (m + 1)
+            blocks = row.reshape(-1, 64)
+            assert np.array_equal(blocks, blocks[:, :1] + np.arange(64))   # whole 64-runs
+            assert np.all(blocks[:, 0] % 64 == 0)
+    assert ref.bs_index_width(64, 100) == 6400 and ref.bs_index_width(16, 5) == 128
+
+
+def test_block_sparse_full_budget_is_dense_causal_attention():
+    """k_b >= number of blocks keeps every causal block, so block-sparse
+    attention of every head is dense causal attention (library softmax)."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(44)
+    Hq, Hkv, nb, d = 4, 2, 4, 16
+    T = 64 * nb
+    Q, K = grid(rng, (Hq, T, d)), grid(rng, (Hkv, T, d))
+    V = rng.normal(size=(Hkv, T, d)).astype(np.float32)
+    rows = ref.bs_rows(Q, K, 64, nb)
+    scale = ref.default_scale(d)
+    out = np.zeros((Hq, T, d), np.float32)
+    for h in range(Hq):
+        g = h // (Hq // Hkv)
+        for m in range(nb):
+            out[h:h + 1, 64 * m:64 * m + 64] = ref.attend_block(
+                Q[h:h + 1, 64 * m:64 * m + 64], K[g:g + 1], V[g:g + 1], rows[h][m], 64 * m, scale)
+    Kx = torch.from_numpy(np.repeat(K, 2, axis=0)).double()
+    Vx = torch.from_numpy(np.repeat(V, 2, axis=0)).double()
+    want = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(Q).double(), Kx, Vx, is_causal=True, scale=scale).numpy()
+    assert np.abs(out - want).max() < 1e-5
+
+
+def test_block_sparse_planted_block_is_found():
+    """A key block built to align with one query block's mean direction wins
+    that row (and every later row whose query block shares the direction)."""
+    rng = np.random.default_rng(45)
+    nb, d = 24, 32
+    Q = grid(rng, (1, 64 * nb, d)) * np.float32(0.25)
+    K = grid(rng, (1, 64 * nb, d)) * np.float32(0.25)
+    u = np.sign(rng.normal(size=d)).astype(np.float32)
+    Q[0, 64 * 17:64 * 18] += u
+    K[0, 64 * 3:64 * 4] += u
+    rows = ref.bs_rows(Q, K, 64, 2)
+    assert 64 * 3 in rows[0][17][::64]
+    assert ref.bs_block_scores(ref.bs_pool(Q, 64), ref.bs_pool(K, 64), 0, 17).argmax() == 3
+
+
+def test_block_sparse_equation_3_speedup():
+    """The page's Equation 3: the pairs the rows admit under the causal mask,
+    against dense causal attention, approach S / (2 B k_b) for S >> B k_b;
+    the page's 1M-token figures follow from the same geometry."""
+    g = _load("p3_block_sparse.json")
+    B, kb = g["block"], g["k_blocks"]
+    S = g["S_1m"]
+    assert abs(S / B - g["blocks_per_row_1m_approx"]) < 1
+    assert abs((S / B) ** 2 * g["d_h"] / g["pooled_matmul_flops_per_head_1m_approx"] - 1) < 0.02
+    assert abs(S / (2 * B * kb) / g["speedup_eq3_1m_approx"] - 1) < 0.01
+    rng = np.random.default_rng(46)
+    nb, kb_s = 320, 8
+    S_s = 64 * nb
+    Q, K = grid(rng, (1, S_s, 4)), grid(rng, (1, S_s, 4))
+    rows = ref.bs_rows(Q, K, 64, kb_s)
+    pairs = 0
+    for m, row in enumerate(rows[0]):
+        t = 64 * m + np.arange(64)
+        pairs += int((row[None, :] <= t[:, None]).sum())
+    dense = S_s * (S_s + 1) // 2
+    assert abs((dense / pairs) / (S_s / (2 * 64 * kb_s)) - 1) < 0.03
