@@ -21,7 +21,8 @@ MAX_STAGES = 4
 
 EXPORTS = ("dsa_index_width", "dsa_workspace_bytes", "dsa_prune_select", "dsa_sparse_attn",
            "dsa_dense_attn", "dsa_mask_cache_bytes", "dsa_cached_index_width", "dsa_prune_select_cached",
-           "dsa_profile_begin", "dsa_profile_end", "dsa_status_str", "dsa_last_error")
+           "dsa_block_sparse_index_width", "dsa_block_sparse_workspace_bytes", "dsa_block_sparse_select",
+           "dsa_sparse_attn_heads", "dsa_profile_begin", "dsa_profile_end", "dsa_status_str", "dsa_last_error")
 
 
 class CParams(ctypes.Structure):
@@ -79,6 +80,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dsa_sparse_attn.restype = ctypes.c_int
     lib.dsa_dense_attn.argtypes = [ctypes.POINTER(CShape), vp, vp, vp, ctypes.c_float, vp, vp, sz, vp]
     lib.dsa_dense_attn.restype = ctypes.c_int
+    lib.dsa_block_sparse_index_width.argtypes = [ctypes.c_int32]
+    lib.dsa_block_sparse_index_width.restype = ctypes.c_int32
+    lib.dsa_block_sparse_workspace_bytes.argtypes = [ctypes.POINTER(CShape), ctypes.c_int32, ctypes.POINTER(sz)]
+    lib.dsa_block_sparse_workspace_bytes.restype = ctypes.c_int
+    lib.dsa_block_sparse_select.argtypes = [ctypes.POINTER(CShape), vp, vp, ctypes.c_int32, vp, vp, sz, vp]
+    lib.dsa_block_sparse_select.restype = ctypes.c_int
+    lib.dsa_sparse_attn_heads.argtypes = [ctypes.POINTER(CShape), vp, vp, vp, vp, ctypes.c_int32, ctypes.c_float,
+                                          vp, vp]
+    lib.dsa_sparse_attn_heads.restype = ctypes.c_int
     lib.dsa_profile_begin.argtypes = []
     lib.dsa_profile_begin.restype = ctypes.c_int
     lib.dsa_profile_end.argtypes = [ctypes.POINTER(CKernelTime), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
@@ -205,6 +215,33 @@ def dense_attn_raw(shape: Shape, q: int, k: int, v: int, scale: float, out: int,
     cs = shape.c()
     _check(load().dsa_dense_attn(ctypes.byref(cs), q, k, v, scale, out, ws or None, ws_bytes,
                                  stream or None))
+
+
+def block_sparse_index_width(k_blocks: int) -> int:
+    w = load().dsa_block_sparse_index_width(k_blocks)
+    if w < 0:
+        raise DsaError(1, f"invalid k_blocks {k_blocks}")
+    return w
+
+
+def block_sparse_workspace_bytes(shape: Shape, k_blocks: int) -> int:
+    cs, n = shape.c(), ctypes.c_size_t(0)
+    _check(load().dsa_block_sparse_workspace_bytes(ctypes.byref(cs), k_blocks, ctypes.byref(n)))
+    return n.value
+
+
+def block_sparse_select_raw(shape: Shape, q: int, k: int, k_blocks: int, idx: int, ws: int, ws_bytes: int,
+                            stream: int = 0):
+    cs = shape.c()
+    _check(load().dsa_block_sparse_select(ctypes.byref(cs), q, k, k_blocks, idx, ws or None, ws_bytes,
+                                          stream or None))
+
+
+def sparse_attn_heads_raw(shape: Shape, q: int, k: int, v: int, idx: int, idx_width: int, scale: float,
+                          out: int, stream: int = 0):
+    cs = shape.c()
+    _check(load().dsa_sparse_attn_heads(ctypes.byref(cs), q, k, v, idx, idx_width, scale, out,
+                                        stream or None))
 
 
 def profile_begin():

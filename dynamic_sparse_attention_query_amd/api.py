@@ -76,7 +76,10 @@ def make_shape(q: torch.Tensor, k: torch.Tensor, *, seq_lens: Optional[torch.Ten
 
 def workspace(shape: Shape, params: Optional[Params], device: torch.device) -> Tuple[int, int]:
     """A per-device scratch buffer large enough for this call (grown on demand)."""
-    nbytes = _lib.workspace_bytes(shape, params)
+    return _scratch(_lib.workspace_bytes(shape, params), device)
+
+
+def _scratch(nbytes: int, device: torch.device) -> Tuple[int, int]:
     key = (device.index if device.index is not None else torch.cuda.current_device(), 0)
     buf = _WS.get(key)
     if buf is None or buf.numel() < nbytes:
@@ -197,3 +200,44 @@ def dense_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: floa
     _lib.dense_attn_raw(shape, q.data_ptr(), k.data_ptr(), v.data_ptr(), scale, out.data_ptr(), ws, wsb,
                         _stream())
     return out
+
+
+# --------------------------------------------------------------------------- #
+# block-sparse heads                                                          #
+# --------------------------------------------------------------------------- #
+def block_sparse_select(q: torch.Tensor, k: torch.Tensor, k_blocks: int, *,
+                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per-head block index estimation (prefill): [B, Hq, T/64, 64*k_blocks] rows."""
+    shape = make_shape(q, k)
+    if shape.mode != DSA_PREFILL:
+        raise ValueError("block-sparse estimation is a prefill call")
+    L = _lib.block_sparse_index_width(k_blocks)
+    nblk = shape.t // 64
+    n = shape.batch * shape.hq * nblk * L
+    if out is None:
+        out = torch.empty(n, dtype=torch.int32, device=q.device)
+    if out.numel() != n or out.dtype != torch.int32 or not out.is_contiguous():
+        raise ValueError("idx buffer has the wrong size, dtype or layout")
+    ws, wsb = _scratch(_lib.block_sparse_workspace_bytes(shape, k_blocks), q.device)
+    _lib.block_sparse_select_raw(shape, q.data_ptr(), k.data_ptr(), k_blocks, out.data_ptr(), ws, wsb, _stream())
+    return out.view(shape.batch, shape.hq, nblk, L)
+
+
+def sparse_attn_heads(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor, *,
+                      scale: float = 0.0, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Prefill attention over per-head index rows idx [B, Hq, T/64, L]."""
+    shape = make_shape(q, k)
+    _need(v, "v")
+    _need(idx, "idx")
+    if v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("v must match k")
+    if idx.dtype != torch.int32:
+        raise TypeError("idx must be int32")
+    if tuple(idx.shape[:3]) != (shape.batch, shape.hq, shape.t // 64):
+        raise ValueError("idx must be [B, Hq, T/64, L]")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    _lib.sparse_attn_heads_raw(shape, q.data_ptr(), k.data_ptr(), v.data_ptr(), idx.data_ptr(), idx.shape[-1],
+                               scale, out.data_ptr(), _stream())
+    return out
+

@@ -382,4 +382,118 @@ dsa_status dsa_dense_attn(const dsa_shape* s, const void* q, const void* k, cons
   return run_attn(s, q, k, v, nullptr, 0, bq, scale, out, ws, ws_bytes, stream);
 }
 
+
+}  // extern "C"
+
+namespace {
+
+constexpr int kBsBlock = 64;
+constexpr long long kBsMaxBlocks = 16384;          // query blocks per sequence the top-K holds
+
+dsa_status check_block_sparse(const dsa_shape* s, int32_t k_blocks) {
+  dsa_status st = check_shape(s);
+  if (st != DSA_OK) return st;
+  if (s->mode != DSA_PREFILL) return fail(DSA_ERR_INVALID_ARG, "block-sparse estimation is a prefill call");
+  if (s->t % kBsBlock != 0) return fail(DSA_ERR_INVALID_ARG, "t = %d is not a multiple of 64", s->t);
+  if (s->t / kBsBlock > kBsMaxBlocks)
+    return fail(DSA_ERR_UNSUPPORTED, "t = %d; block-sparse estimation supports up to %lld tokens", s->t,
+                kBsMaxBlocks * kBsBlock);
+  if (k_blocks < 1 || k_blocks > kBsMaxBlocks)
+    return fail(DSA_ERR_INVALID_ARG, "k_blocks = %d not in [1, %lld]", k_blocks, kBsMaxBlocks);
+  return DSA_OK;
+}
+
+struct BsLayout {
+  long long nblk, nblkp;
+  size_t off_qp, off_kp, off_keys, bytes;
+};
+
+BsLayout bs_layout(const dsa_shape* s) {
+  BsLayout L{};
+  L.nblk = s->t / kBsBlock;
+  L.nblkp = (L.nblk + 3) / 4 * 4;
+  const size_t rows_q = static_cast<size_t>(s->batch) * s->hq * L.nblk;
+  const size_t rows_k = static_cast<size_t>(s->batch) * s->hkv * L.nblk;
+  L.off_qp = 0;
+  L.off_kp = align256(L.off_qp + rows_q * s->d * sizeof(double));
+  L.off_keys = align256(L.off_kp + rows_k * s->d * sizeof(double));
+  L.bytes = align256(L.off_keys + rows_q * L.nblkp * 4);
+  return L;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t dsa_block_sparse_index_width(int32_t k_blocks) {
+  if (k_blocks < 1 || k_blocks > kBsMaxBlocks) return -1;
+  return k_blocks * kBsBlock;
+}
+
+dsa_status dsa_block_sparse_workspace_bytes(const dsa_shape* s, int32_t k_blocks, size_t* out_bytes) {
+  g_err[0] = 0;
+  if (!out_bytes) return fail(DSA_ERR_INVALID_ARG, "out_bytes is NULL");
+  dsa_status st = check_block_sparse(s, k_blocks);
+  if (st != DSA_OK) return st;
+  *out_bytes = bs_layout(s).bytes;
+  return DSA_OK;
+}
+
+dsa_status dsa_block_sparse_select(const dsa_shape* s, const void* q, const void* k, int32_t k_blocks,
+                                   int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  dsa_status st = check_block_sparse(s, k_blocks);
+  if (st != DSA_OK) return st;
+  if (!q || !k || !idx) return fail(DSA_ERR_INVALID_ARG, "q, k and idx must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(idx))
+    return fail(DSA_ERR_INVALID_ARG, "q, k and idx must be 16-byte aligned");
+  const BsLayout lay = bs_layout(s);
+  if (!ws || ws_bytes < lay.bytes)
+    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, lay.bytes);
+  if (!aligned16(ws)) return fail(DSA_ERR_INVALID_ARG, "ws must be 16-byte aligned");
+  dsa::BsArgs a{};
+  a.kv = make_kv(s, kBsBlock);
+  a.q = q;
+  a.k = k;
+  a.k_blocks = k_blocks;
+  a.nblkp = static_cast<int>(lay.nblkp);
+  char* w = static_cast<char*>(ws);
+  a.qp = reinterpret_cast<double*>(w + lay.off_qp);
+  a.kp = reinterpret_cast<double*>(w + lay.off_kp);
+  a.keys = reinterpret_cast<uint32_t*>(w + lay.off_keys);
+  a.idx = idx;
+  a.L = k_blocks * kBsBlock;
+  hipError_t err = dsa::launch_block_sparse(a, s->dtype, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(DSA_ERR_HIP, "block-sparse launch failed: %s", hipGetErrorString(err));
+  return DSA_OK;
+}
+
+dsa_status dsa_sparse_attn_heads(const dsa_shape* s, const void* q, const void* k, const void* v,
+                                 const int32_t* idx, int32_t idx_width, float scale, float* out,
+                                 void* stream) {
+  g_err[0] = 0;
+  dsa_status st = check_shape(s);
+  if (st != DSA_OK) return st;
+  if (s->mode != DSA_PREFILL) return fail(DSA_ERR_INVALID_ARG, "per-head rows are a prefill layout");
+  if (s->t % kBsBlock != 0) return fail(DSA_ERR_INVALID_ARG, "t = %d is not a multiple of 64", s->t);
+  if (!q || !k || !v || !idx || !out) return fail(DSA_ERR_INVALID_ARG, "q, k, v, idx and out must be non-NULL");
+  if (idx_width < 1) return fail(DSA_ERR_INVALID_ARG, "idx_width must be >= 1");
+  dsa::AttnArgs a{};
+  a.kv = make_kv(s, kBsBlock);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.idx = idx;
+  a.L = idx_width;
+  a.out = out;
+  a.row_heads = 1;
+  const float sc = scale > 0.f ? scale : 1.0f / std::sqrt(static_cast<float>(s->d));
+  a.scale_log2 = sc * 1.4426950408889634f;
+  hipError_t err = dsa::launch_sparse_attn(a, s->dtype, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(DSA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(err));
+  return DSA_OK;
+}
+
 }  // extern "C"

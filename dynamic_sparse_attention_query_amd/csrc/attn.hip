@@ -227,7 +227,7 @@ __global__ void __launch_bounds__(256) k_prefill_generic(AttnArgs a) {
     const int t = x / D, dd = x - t * D;
     qs[t][dd] = load_one<T>(Q + ((static_cast<size_t>(b) * kv.Hq + h) * kv.T + s + t) * D + dd);
   }
-  const int r = b * kv.nblk + m;
+  const int r = a.row_heads ? (b * kv.Hq + h) * kv.nblk + m : b * kv.nblk + m;
   const int32_t* row = a.idx ? a.idx + static_cast<size_t>(r) * a.L : nullptr;
   const int n_ent = row ? a.L : e;
   float mrun = kNegBig, lrun = 0.f;
@@ -323,7 +323,8 @@ static hipError_t launch_attn_typed(const AttnArgs& a, hipStream_t st) {
   } else {
     if (sizeof(T) == 2 && launch_prefill_mfma(a, st)) return hipGetLastError();
     dim3 grid(a.kv.nblk, a.kv.Hq, a.kv.B);
-    DSA_LAUNCH(a.idx ? "attn_prefill" : "dense_prefill", (k_prefill_generic<T, D>), grid, dim3(256), st, a);
+    const char* name = a.row_heads ? "attn_prefill_heads" : a.idx ? "attn_prefill" : "dense_prefill";
+    DSA_LAUNCH(name, (k_prefill_generic<T, D>), grid, dim3(256), st, a);
   }
   return hipGetLastError();
 }

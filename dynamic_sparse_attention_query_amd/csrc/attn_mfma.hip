@@ -118,7 +118,8 @@ __global__ void __launch_bounds__(64 * NH * QH) k_prefill_mfma(AttnArgs a) {
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
   float mrun = kNegBig, lrun = 0.f;
 
-  const int r = b * kv.nblk + m;
+  // with per-head rows the workgroup holds a single head (NH == 1)
+  const int r = a.row_heads ? (b * kv.Hq + h) * kv.nblk + m : b * kv.nblk + m;
   const int32_t* row = a.idx ? a.idx + static_cast<size_t>(r) * a.L : nullptr;
   const int n_ent = row ? a.L : e;
   const int n_tiles = (n_ent + 63) / 64;
@@ -581,8 +582,8 @@ static void launch_mfma(const AttnArgs& a, hipStream_t st) {
   const int G = a.kv.Hq / a.kv.Hkv;
   const int nwork = a.kv.B * a.kv.Hkv * (G / NH) * a.kv.nblk * (2 / QH);
   const int grid = (nwork + 7) / 8 * 8;
-  DSA_LAUNCH(a.idx ? "attn_prefill" : "dense_prefill", (k_prefill_mfma<D, NH, QH>), dim3(grid),
-             dim3(64 * NH * QH), st, a);
+  const char* name = a.row_heads ? "attn_prefill_heads" : a.idx ? "attn_prefill" : "dense_prefill";
+  DSA_LAUNCH(name, (k_prefill_mfma<D, NH, QH>), dim3(grid), dim3(64 * NH * QH), st, a);
 }
 
 // bf16 prefill with query blocks of 64 rows; 4 waves per workgroup: the 4
@@ -594,6 +595,11 @@ bool launch_prefill_mfma(const AttnArgs& a, hipStream_t st) {
   // reads each index row 16 bytes at a time
   const bool lds_ok = static_cast<long long>(a.kv.T) * 256 <= 0x7fffffffLL &&
                       (reinterpret_cast<uintptr_t>(a.idx) & 15) == 0;
+  if (a.row_heads) {                              // one head per workgroup
+    if (a.kv.D == 128) { launch_mfma<128, 1, 2>(a, st); return true; }
+    if (a.kv.D == 64) { launch_mfma<64, 1, 2>(a, st); return true; }
+    return false;
+  }
   if (a.kv.D == 128 && lds_ok) {
     if (G >= 4) { launch_mfma_lds<4, 1>(a, st); return true; }
     if (G == 2) { launch_mfma_lds<2, 2>(a, st); return true; }

@@ -63,6 +63,23 @@ struct AttnArgs {
   int n_splits;
   int kps;                   // decode keys per split (multiple of 64)
   float scale_log2;          // softmax scale * log2(e)
+  int row_heads;             // prefill: 0 = one idx row per (b, block) shared by the heads,
+                             // 1 = one row per (b, q head, block): row (b * Hq + h) * nblk + m
+};
+
+// Block-sparse index estimation (MInference page, "Online Dynamic Index
+// Estimation: Block-Sparse Heads (Algorithm 3)"): prefill, blocks of 64.
+struct BsArgs {
+  KvLayout kv;               // prefill layout; kv.nblk = T / 64
+  const void* q;
+  const void* k;
+  int k_blocks;              // k_b: key blocks kept per (q head, query block)
+  int nblkp;                 // score row stride (nblk rounded up to 4)
+  double* qp;                // [B, Hq, nblk, D] pooled queries (fp64)
+  double* kp;                // [B, Hkv, nblk, D] pooled keys (fp64)
+  uint32_t* keys;            // [B, Hq, nblk, nblkp] orderable pooled-logit keys
+  int32_t* idx;              // [B, Hq, nblk, L] index rows
+  int L;                     // row width: 64 * k_blocks
 };
 
 // ------------------------------------------------------------------------- //
@@ -312,6 +329,7 @@ hipError_t launch_prune(const PruneArgs& a, int dtype, hipStream_t stream);
 // decode with remembered stages: only the stages flagged in due[] are recomputed
 hipError_t launch_prune_cached(const PruneArgs& a, const bool* due, int dtype, hipStream_t stream);
 hipError_t launch_sparse_attn(const AttnArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_block_sparse(const BsArgs& a, int dtype, hipStream_t stream);
 bool launch_prefill_mfma(const AttnArgs& a, hipStream_t stream);   // bf16, b_q = 64
 struct PruneArgs;
 bool launch_score_prefill_mfma(const PruneArgs& a, int stage, int max_chunks, hipStream_t stream,

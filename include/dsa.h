@@ -23,6 +23,10 @@
  *                     Formulation of Efficient Softmax Normalization";
  *                     MInference page, masked-attention formulation and
  *                     in-kernel causal masking.)
+ *   dsa_block_sparse_select, dsa_sparse_attn_heads
+ *                     The MInference page's Block-Sparse heads: per-head block
+ *                     index estimation from mean-pooled queries and keys, and
+ *                     attention over per-head index rows (see below).
  *   dsa_dense_attn    Exact causal attention over all keys: the comparison
  *                     point (InfiniteHiP page, "Dense Attention Optimizations"
  *                     and "Formal Background: Standard Multi-Head Attention").
@@ -193,6 +197,47 @@ dsa_status dsa_sparse_attn(const dsa_shape* shape, const void* q, const void* k,
 /* Exact causal attention over keys [0, t] for every query t. */
 dsa_status dsa_dense_attn(const dsa_shape* shape, const void* q, const void* k, const void* v,
                           float scale, float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- Block-sparse heads --------------------------------------------------
+ * MInference page, "Online Dynamic Index Estimation: Block-Sparse Heads
+ * (Algorithm 3)" and "Block-Sparse FlashAttention Kernel (Appendix C.4.1)".
+ * Prefill only, blocks of 64 tokens (the page's block size): for every query
+ * head h and query block m, the queries of the block and the keys of kv head
+ * h / (Hq / Hkv) are mean-pooled per 64 rows; the pooled logits q~_m . k~_j of
+ * the key blocks j <= m (later blocks are masked; the diagonal block stays) are
+ * evaluated in fp64 and rounded once to fp32; the k_blocks blocks with the
+ * highest logits (ties to the lower block) are kept. Softmax and the 1/sqrt(d)
+ * scale are monotone and do not change the selection. Each query head has its
+ * own index rows.
+ *
+ * Layout: idx [B, Hq, T / 64, L] int32 with L = dsa_block_sparse_index_width();
+ * row (b, h, m) holds the kept blocks in ascending order as runs of 64
+ * positions (64 j .. 64 j + 63), min(m + 1, k_blocks) runs, then -1 padding.
+ * Requires t a multiple of 64 with t / 64 <= 16384. */
+
+/* Row width 64 * k_blocks; -1 if k_blocks is not in [1, 16384]. */
+int32_t dsa_block_sparse_index_width(int32_t k_blocks);
+
+/* Workspace bytes of dsa_block_sparse_select for this shape: the pooled
+ * queries and keys in fp64 and one orderable logit key per (q head, query
+ * block, key block), i.e. 8 d (B Hq + B Hkv) T/64 + 4 B Hq (T/64) ceil4(T/64)
+ * bytes plus alignment. */
+dsa_status dsa_block_sparse_workspace_bytes(const dsa_shape* shape, int32_t k_blocks, size_t* out_bytes);
+
+/* Writes every index row of idx (see above). shape.mode must be DSA_PREFILL;
+ * q [B, Hq, T, d], k [B, Hkv, T, d] (fp32 or bf16); q, k, idx and ws 16-byte
+ * aligned; ws of at least dsa_block_sparse_workspace_bytes() bytes. */
+dsa_status dsa_block_sparse_select(const dsa_shape* shape, const void* q, const void* k, int32_t k_blocks,
+                                   int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+
+/* dsa_sparse_attn with one index row per query head: out[h, t] = sum over p in
+ * the row of (h, t / 64), p <= t, of softmax_p(scale * q_{h,t} . k_p) v_p.
+ * shape.mode must be DSA_PREFILL with t a multiple of 64; idx [B, Hq, T / 64,
+ * idx_width] (negative entries are ignored); scale <= 0 selects 1/sqrt(d).
+ * Needs no workspace. */
+dsa_status dsa_sparse_attn_heads(const dsa_shape* shape, const void* q, const void* k, const void* v,
+                                 const int32_t* idx, int32_t idx_width, float scale, float* out,
+                                 void* stream);
 
 /* Per-kernel timing, a diagnostic for latency breakdowns. Between
  * dsa_profile_begin() and dsa_profile_end(), every kernel the library launches

@@ -140,3 +140,44 @@ def test_prune_select_cached_rejects_before_launch():
             _lib.prune_select_cached_raw(a["shape"], 256, 256, P3, a["refresh"], a["step"], a["cache"],
                                          a["cache_bytes"], 256, a["width"], 256, a["ws_bytes"])
         assert ei.value.status == code, over
+
+
+def test_block_sparse_sizes():
+    assert _lib.block_sparse_index_width(100) == 6400
+    assert _lib.block_sparse_index_width(1) == 64
+    with pytest.raises(_lib.DsaError):
+        _lib.block_sparse_index_width(0)
+    s = Shape(DSA_PREFILL, DSA_BF16, 1, 32, 8, 128, 131072)
+    nb = 131072 // 64
+    want = 8 * 128 * (32 + 8) * nb + 4 * 32 * nb * nb        # pooled rows + one key per block pair
+    got = _lib.block_sparse_workspace_bytes(s, 100)
+    assert want <= got <= want + 3 * 256 and got % 256 == 0
+    r = Shape(DSA_PREFILL, DSA_F32, 2, 1, 1, 64, 64 * 5)          # 5 blocks: rows padded to 8 keys
+    assert _lib.block_sparse_workspace_bytes(r, 3) >= 8 * 64 * 2 * 2 * 5 + 4 * 2 * 5 * 8
+
+
+def test_block_sparse_rejects_before_launch():
+    good = Shape(DSA_PREFILL, DSA_BF16, 1, 32, 8, 128, 4096)
+    ws = _lib.block_sparse_workspace_bytes(good, 100)
+    cases = [
+        (dict(shape=Shape(DSA_PREFILL, DSA_BF16, 1, 32, 8, 128, 4096 + 32)), DSA_ERR_INVALID_ARG),   # t % 64
+        (dict(shape=Shape(DSA_DECODE, DSA_BF16, 1, 32, 8, 128, 4096, seq_lens=16)), DSA_ERR_INVALID_ARG),
+        (dict(shape=Shape(DSA_PREFILL, DSA_BF16, 1, 32, 8, 128, 64 * 16385)), DSA_ERR_UNSUPPORTED),
+        (dict(kb=0), DSA_ERR_INVALID_ARG),
+        (dict(ws_bytes=ws - 256), DSA_ERR_WORKSPACE),
+        (dict(idx=8), DSA_ERR_INVALID_ARG),                                                       # misaligned
+        (dict(q=0), DSA_ERR_INVALID_ARG),
+    ]
+    for over, code in cases:
+        a = dict(shape=good, kb=100, q=256, idx=256, ws_bytes=ws)
+        a.update(over)
+        with pytest.raises(_lib.DsaError) as ei:
+            _lib.block_sparse_select_raw(a["shape"], a["q"], 256, a["kb"], a["idx"], 256, a["ws_bytes"])
+        assert ei.value.status == code, over
+    with pytest.raises(_lib.DsaError) as ei:                                  # per-head attention
+        _lib.sparse_attn_heads_raw(Shape(DSA_PREFILL, DSA_BF16, 1, 32, 8, 128, 4000), 16, 16, 16, 16, 6400,
+                                   0.0, 16)
+    assert ei.value.status == DSA_ERR_INVALID_ARG
+    with pytest.raises(_lib.DsaError) as ei:
+        _lib.sparse_attn_heads_raw(good, 16, 16, 16, 16, 0, 0.0, 16)
+    assert ei.value.status == DSA_ERR_INVALID_ARG
