@@ -83,6 +83,7 @@ def parse():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cached", action="store_true", help="skip decoding with remembered stages")
     ap.add_argument("--no-other", action="store_true", help="skip the batch-32 paged and 3M-token decodes")
+    ap.add_argument("--no-block-sparse", action="store_true", help="skip the block-sparse heads prefill")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-ref", action="store_true",
@@ -478,6 +479,68 @@ def prefill_bench(args, res):
 
 
 # --------------------------------------------------------------------------- #
+# block-sparse heads at the 128K prefill shape                                #
+# --------------------------------------------------------------------------- #
+BS_K_BLOCKS = 100          # the page's k_b for Block-Sparse heads
+
+
+def block_sparse_bench(args, res, reps=3):
+    """Block-sparse estimation + per-head attention over the 128K Llama-shaped
+    prefill (k_b = 100), with the dense causal path at the same shape."""
+    import torch
+    from dynamic_sparse_attention_query_amd import _lib, api, gen
+    from dynamic_sparse_attention_query_amd.inputs import to_device
+
+    case = gen.make_case("c2_128k")
+    cfg = case.cfg
+    dev = to_device(case)
+    del case
+    idx = api.block_sparse_select(dev.q, dev.k, BS_K_BLOCKS)
+    out = api.sparse_attn_heads(dev.q, dev.k, dev.v, idx)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        api.block_sparse_select(dev.q, dev.k, BS_K_BLOCKS, out=idx.view(-1))
+        api.sparse_attn_heads(dev.q, dev.k, dev.v, idx, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    _lib.profile_begin()
+    api.block_sparse_select(dev.q, dev.k, BS_K_BLOCKS, out=idx.view(-1))
+    api.sparse_attn_heads(dev.q, dev.k, dev.v, idx, out=out)
+    prof = _lib.profile_end()
+    # visible (query, key) pairs: whole 64 x 64 blocks below the diagonal, the
+    # causal half (64 * 65 / 2) of a kept diagonal block
+    nblk, d, Hq = cfg.t // 64, cfg.d, cfg.hq
+    starts = idx[..., ::64]
+    m_pos = (torch.arange(nblk, device=idx.device, dtype=torch.int32) * 64).view(1, 1, nblk, 1)
+    below = ((starts >= 0) & (starts < m_pos)).sum().item()
+    diag = (starts == m_pos).sum().item()
+    pairs = below * 64 * 64 + diag * (64 * 65 // 2)
+    attn_f = pairs * 4 * d
+    est_f = Hq * cfg.batch * (nblk * (nblk + 1) // 2) * 2 * d          # pooled logits (fp64)
+    est_ms = sum(v[1] for k, v in prof.items() if k.startswith("bs_"))
+    attn_ms = sum(v[1] for k, v in prof.items() if k.startswith("attn_"))
+    dense_ms = None
+    if not args.no_dense:
+        api.dense_attn(dev.q, dev.k, dev.v, out=out)
+        torch.cuda.synchronize()
+        e0.record()
+        api.dense_attn(dev.q, dev.k, dev.v, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        dense_ms = e0.elapsed_time(e1)
+    res["block_sparse"] = dict(ms=ms, attn_tflop=attn_f / 1e12, est_tflop_fp64=est_f / 1e12,
+                               est_ms=est_ms, attn_ms=attn_ms, dense_ms=dense_ms,
+                               kernels_ms={k: round(v[1] / v[0], 3) for k, v in prof.items()})
+    log(f"block-sparse 128K: {ms:.2f} ms (estimation {est_ms:.2f}, attention {attn_ms:.2f}), "
+        f"{attn_f / (ms * 1e-3) / 1e12:.1f} TFLOP/s" + (f", dense {dense_ms:.1f} ms" if dense_ms else ""))
+    del dev, idx, out
+    torch.cuda.empty_cache()
+
+
+# --------------------------------------------------------------------------- #
 # the other decode workloads: batch-32 ragged paged, and 3M tokens            #
 # --------------------------------------------------------------------------- #
 def other_decode(args, name, reps=20):
@@ -577,6 +640,8 @@ def main():
         res["c5"] = other_decode(args, "c5")
     if not args.no_prefill:
         prefill_bench(args, res)
+    if not args.no_block_sparse:
+        block_sparse_bench(args, res)
     if not args.no_cpu:
         cpu_baseline(args, case, res)
 
@@ -639,6 +704,18 @@ def main():
             line["prefill_128k"]["hbm_read_bytes_measured"] = rb
             line["prefill_128k"]["hbm_read_gbps"] = round(rb / (pf["ms"] * 1e-3) / 1e9, 1)
             line["prefill_128k"]["hbm_read_pct_peak"] = round(100 * rb / (pf["ms"] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2)
+    if "block_sparse" in res:
+        bs = res["block_sparse"]
+        tf = bs["attn_tflop"] / (bs["ms"] * 1e-3)
+        line["block_sparse_prefill_128k"] = {
+            "k_blocks": BS_K_BLOCKS, "ms": round(bs["ms"], 2),
+            "tflops": round(tf, 2), "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+            "attn_tflop": round(bs["attn_tflop"], 2), "estimation_tflop_fp64": round(bs["est_tflop_fp64"], 3),
+            "estimation_ms": round(bs["est_ms"], 3), "attn_ms": round(bs["attn_ms"], 2),
+            "attn_only_pct_bf16_peak": round(100 * bs["attn_tflop"] / (bs["attn_ms"] * 1e-3) / PEAK_BF16_TFLOPS, 2),
+            "dense_ms": round(bs["dense_ms"], 1) if bs["dense_ms"] else None,
+            "speedup_vs_dense": round(bs["dense_ms"] / bs["ms"], 2) if bs["dense_ms"] else None,
+            "kernels_ms": bs["kernels_ms"]}
     if "cpu" in res:
         line["cpu_baseline"] = res["cpu"]
     print(json.dumps(line), flush=True)

@@ -78,15 +78,31 @@ __global__ void __launch_bounds__(64 * NH * QH) k_prefill_mfma(AttnArgs a) {
   const int HG = G / NH;                          // head groups per kv head
   constexpr int NQS = 2 / QH;                     // query-half splits across workgroups
   const int nwork = kv.B * kv.Hkv * HG * kv.nblk * NQS;
-  const int per_xcd = gridDim.x >> 3;
-  int work = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (work >= nwork) return;
-  const int qsplit = work % NQS;
-  work /= NQS;
-  const int m = work % kv.nblk;
-  work /= kv.nblk;
-  const int hg = work % (kv.Hkv * HG);
-  const int b = work / (kv.Hkv * HG);
+  int qsplit, m, hg, b;
+  if (a.row_heads) {
+    // Per-head rows gather different keys for every head, so reuse comes from
+    // the last-level cache: the whole grid walks one kv head at a time (its
+    // K and V stay resident there) and deals neighbouring work to all XCDs.
+    int work = blockIdx.x;
+    if (work >= nwork) return;
+    const int hw = work % HG;
+    work /= HG;
+    m = work % kv.nblk;
+    work /= kv.nblk;
+    hg = (work % kv.Hkv) * HG + hw;
+    b = work / kv.Hkv;
+    qsplit = 0;
+  } else {
+    const int per_xcd = gridDim.x >> 3;
+    int work = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    if (work >= nwork) return;
+    qsplit = work % NQS;
+    work /= NQS;
+    m = work % kv.nblk;
+    work /= kv.nblk;
+    hg = work % (kv.Hkv * HG);
+    b = work / (kv.Hkv * HG);
+  }
   const int g = hg / HG;
   const int s = m * 64, e = s + 64;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -568,6 +584,249 @@ __global__ void __launch_bounds__(64 * NH * QH, 2) k_prefill_mfma_lds(AttnArgs a
     }
 }
 
+// Per-head index rows (one row per sequence, query head and query block, as
+// the block-sparse heads of the MInference page produce: "Block-Sparse
+// FlashAttention Kernel (Appendix C.4.1)"), d = 128. No two heads share a key
+// tile, so a workgroup owns one head's 64-query block: two waves of 32
+// queries. K and V have one LDS tile each (33 KB in all, four workgroups per
+// CU) and are refilled as soon as their readers are done, straight from
+// global memory (buffer_load_dwordx4 ... lds):
+//   wait K_i, barrier | issue V_i | S = K_i Q^T, mask | barrier | issue K_i+1
+//   | softmax | wait V_i, barrier | O^T += V_i^T P^T
+// so V_i loads under the QK product and the softmax, K_i+1 under the softmax
+// and the PV product. Tile entry e (0..63) lives in LDS row 8 * (e % 8) + e / 8:
+// lane group g = 4 * wave + lane / 16 (0..7) takes entries 8g .. 8g+7 and its
+// eight row loads land in rows 8u + g. Entries that are padding (or tiles past
+// the row) load through an out-of-range offset: zeros, no memory traffic.
+// Workgroup barrier that leaves this wave's loads into LDS in flight: LDS
+// reads and writes are complete (lgkmcnt 0), vector memory is not waited.
+// (The compiler's own barrier waits for every load into LDS still pending.)
+__device__ __forceinline__ void barrier_keep_loads() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);           // lgkmcnt(0); vmcnt, expcnt not waited
+  asm volatile("s_barrier" ::: "memory");
+}
+
+__global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) k_prefill_heads(AttnArgs a) {
+  constexpr int D = 128;
+  constexpr int KS = D / 16;
+  constexpr int DT = D / 32;
+  __shared__ __align__(16) uint16_t skb[64 * D];
+  __shared__ __align__(16) uint16_t svb[64 * D];
+  __shared__ __align__(16) int spos0[64], spos1[64];     // positions by LDS row
+  __shared__ __align__(16) int sflag0[2], sflag1[2];     // per wave: 1 = needs the mask, 2 = visible keys
+  asm volatile("" ::"r"(skb), "r"(svb) : "memory");
+
+  const KvLayout& kv = a.kv;
+  const int G = kv.Hq / kv.Hkv;
+  // the grid walks one kv head at a time (its K and V stay in the
+  // last-level cache), the heads of a group next to each other
+  int work = blockIdx.x;
+  if (work >= kv.B * kv.Hq * kv.nblk) return;
+  const int hw = work % G;
+  work /= G;
+  const int m = work % kv.nblk;
+  work /= kv.nblk;
+  const int g = work % kv.Hkv;
+  const int b = work / kv.Hkv;
+  const int h = g * G + hw;
+  const int s = m * 64;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int tr_row = (lane & 15) >> 2, tr_col = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
+  const int q0 = s + w * 32;                      // this wave's first query
+  const int wq_lo = s, wq_hi = s + 63;
+  const uint16_t* Q = static_cast<const uint16_t*>(a.q);
+  const size_t kvbase = (static_cast<size_t>(b) * kv.Hkv + g) * kv.T;
+  const uint32_t kv_bytes = static_cast<uint32_t>(kv.T) * D * 2;
+  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(static_cast<const uint16_t*>(a.k) + kvbase * D, kv_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(static_cast<const uint16_t*>(a.v) + kvbase * D, kv_bytes);
+
+  bf16x8_t qf[KS];
+  {
+    const uint16_t* qrow = Q + ((static_cast<size_t>(b) * kv.Hq + h) * kv.T + q0 + l32) * D + hi * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + ks * 16);
+  }
+  f32x16_t o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
+  float mrun = kNegBig, lrun = 0.f;
+
+  const int32_t* row = a.idx + (static_cast<size_t>(b * kv.Hq + h) * kv.nblk + m) * a.L;
+  const int n_tiles = (a.L + 63) / 64;
+  const int lg = 4 * w + (lane >> 4);             // entries 8lg .. 8lg+7 of a tile
+  const int lslot = lane & 15;
+  // Entries 8lg .. 8lg+7 of a tile: two 16-byte loads at clamped addresses
+  // inside the row (L is a multiple of 4), issued a step before their use and
+  // decoded only then (-1 for padding, beyond the row, or past the last
+  // tile), so each step issues exactly two such loads and never waits on them
+  // early: the waits below count them.
+  auto load_raw = [&](int ti, int4& v0, int4& v1) __attribute__((always_inline)) {
+    const int i0 = min(ti, n_tiles - 1) * 64 + 8 * lg;
+    v0 = *reinterpret_cast<const int4*>(row + min(i0, a.L - 4));
+    v1 = *reinterpret_cast<const int4*>(row + min(i0 + 4, a.L - 4));
+  };
+  auto decode = [&](int ti, const int4& v0, const int4& v1, int (&p)[8]) __attribute__((always_inline)) {
+    const int i0 = min(ti, n_tiles - 1) * 64 + 8 * lg;
+    const int raw[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    const bool live = ti < n_tiles;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) p[x] = (live && i0 + x < a.L) ? raw[x] : -1;
+  };
+  auto issue = [&](const __amdgpu_buffer_rsrc_t& rs, uint16_t* dst, const int (&p)[8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int rr = 8 * u + lg;                  // LDS row of entry 8lg + u
+      const int off = p[u] < 0 ? static_cast<int>(kv_bytes) : p[u] * (D * 2) + ((lslot ^ swz(rr)) << 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + (8 * u + 4 * w) * D), 16, off, 0, 0, 0);
+    }
+  };
+  auto publish = [&](const int (&p)[8], int* sposb, int* sflagb) __attribute__((always_inline)) {
+    int pv = p[0];
+#pragma unroll
+    for (int x = 1; x < 8; ++x) pv = lslot == x ? p[x] : pv;
+    if (lslot < 8) sposb[8 * lslot + lg] = pv;
+    unsigned umax = 0u, umin = 0xffffffffu;       // unsigned: padding (-1) is the largest
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      umax = max(umax, static_cast<unsigned>(p[x]));
+      umin = min(umin, static_cast<unsigned>(p[x]));
+    }
+    const unsigned long long nb = __ballot(umax > static_cast<unsigned>(wq_lo));
+    const unsigned long long ab = __ballot(umin <= static_cast<unsigned>(wq_hi));
+    if (lane == 0) sflagb[w] = (nb != 0 ? 1 : 0) | (ab != 0 ? 2 : 0);
+  };
+
+  int cur[8];                                     // decoded entries of the tile in hand
+  int4 r0, r1;                                    // raw entries of the next tile
+  load_raw(0, r0, r1);
+  decode(0, r0, r1, cur);
+  load_raw(1, r0, r1);
+  issue(krs, skb, cur);
+  publish(cur, spos0, sflag0);
+
+  auto step = [&](int ti, const int* sposc, const int* sflagc, int* sposn, int* sflagn) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0);                // this wave's K_i rows are in LDS
+    barrier_keep_loads();                         // everyone's; V is free again
+    issue(vrs, svb, cur);
+    asm volatile("" ::: "memory");
+    decode(ti + 1, r0, r1, cur);
+    load_raw(ti + 2, r0, r1);
+    asm volatile("" ::: "memory");
+    const int2 f2 = *reinterpret_cast<const int2*>(sflagc);
+    const int flag = __builtin_amdgcn_readfirstlane(f2.x | f2.y);
+    f32x16_t sacc[2];
+    if (flag & 2) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[kt][i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const int rr = kt * 32 + l32;
+          const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(skb + rr * D + ((2 * ks + hi) ^ swz(rr)) * 8);
+          sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[ks], sacc[kt], 0, 0, 0);
+        }
+      }
+      if (flag & 1) {
+        // accumulator element 4rn + c of key tile kt is LDS row 32kt + 8rn + 4hi + c
+        const unsigned t = static_cast<unsigned>(q0 + l32);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int rn = 0; rn < 4; ++rn) {
+            const int4 p4 = *reinterpret_cast<const int4*>(sposc + kt * 32 + rn * 8 + hi * 4);
+            const int pp[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              if (static_cast<unsigned>(pp[c]) > t) sacc[kt][rn * 4 + c] = -INFINITY;
+          }
+      }
+    }
+    barrier_keep_loads();                         // K is free: refill it with tile i + 1
+    issue(krs, skb, cur);
+    publish(cur, sposn, sflagn);
+    asm volatile("" ::: "memory");
+    if (flag & 2) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kt][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * a.scale_log2;
+      const bool raise = mx > mrun + 8.0f;
+      const float m_use = raise ? mx : mrun;
+      const float alpha = __builtin_amdgcn_exp2f(mrun - m_use);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[kt][i] = __builtin_amdgcn_exp2f(fmaf(sacc[kt][i], a.scale_log2, -m_use));
+      mrun = m_use;
+      if (__ballot(raise)) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+      }
+      lrun *= alpha;
+    }
+    // V_i was issued before the entries of tile i + 2 and K_i+1 (2 + 8 loads)
+    __builtin_amdgcn_s_waitcnt(0x0F7A);           // vmcnt(10); expcnt, lgkmcnt not waited
+    barrier_keep_loads();
+    if (flag & 2) {
+      const bf16x2_t ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+      float ps = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int kt = ks >> 1, half = ks & 1;
+        u32x4_t u;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const uint32_t pw = pack_bf16x2(sacc[kt][half * 8 + 2 * x], sacc[kt][half * 8 + 2 * x + 1]);
+          ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw), ones, ps, false);
+          u[x] = pw;
+        }
+        const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, u);
+        const int r0 = ks * 16 + hi * 4 + tr_row, r1 = r0 + 8;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int c = dt * 32 + tr_col;
+          const i16x4_t lo4 = lds_read_tr16(svb + r0 * D + (((c >> 3) ^ swz(r0)) << 3) + (c & 7));
+          const i16x4_t hi4 = lds_read_tr16(svb + r1 * D + (((c >> 3) ^ swz(r1)) << 3) + (c & 7));
+          const bf16x8_t av = __builtin_bit_cast(
+              bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb, o[dt], 0, 0, 0);
+        }
+      }
+      lrun += ps + __shfl_xor(ps, 32, 64);
+    }
+  };
+  for (int ti = 0; ti < n_tiles; ti += 2) {
+    step(ti, spos0, sflag0, spos1, sflag1);
+    if (ti + 1 < n_tiles) step(ti + 1, spos1, sflag1, spos0, sflag0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);                  // no load into LDS outlives the workgroup
+
+  const float inv = 1.0f / lrun;
+  float* orow = a.out + ((static_cast<size_t>(b) * kv.Hq + h) * kv.T + q0 + l32) * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      float4 v;
+      v.x = o[dt][i4 * 4 + 0] * inv;
+      v.y = o[dt][i4 * 4 + 1] * inv;
+      v.z = o[dt][i4 * 4 + 2] * inv;
+      v.w = o[dt][i4 * 4 + 3] * inv;
+      *reinterpret_cast<float4*>(orow + dt * 32 + i4 * 8 + hi * 4) = v;
+    }
+}
+
 template <int NH, int QH>
 static void launch_mfma_lds(const AttnArgs& a, hipStream_t st) {
   const int G = a.kv.Hq / a.kv.Hkv;
@@ -591,16 +850,23 @@ static void launch_mfma(const AttnArgs& a, hipStream_t st) {
 bool launch_prefill_mfma(const AttnArgs& a, hipStream_t st) {
   if (a.kv.decode || a.kv.bq != 64) return false;
   const int G = a.kv.Hq / a.kv.Hkv;
-  // the LDS-direct kernel addresses a kv head's rows with 32-bit offsets and
-  // reads each index row 16 bytes at a time
+  // the LDS-direct kernels address a kv head's rows with 32-bit offsets and
+  // read index rows 16 bytes at a time, whole 64-entry tiles for the shared
+  // rows (the per-head kernel checks the end of its rows)
   const bool lds_ok = static_cast<long long>(a.kv.T) * 256 <= 0x7fffffffLL &&
-                      (reinterpret_cast<uintptr_t>(a.idx) & 15) == 0;
+                      (reinterpret_cast<uintptr_t>(a.idx) & 15) == 0 && (a.L & 3) == 0;
+  const bool whole_tiles = a.idx == nullptr || (a.L & 63) == 0;
   if (a.row_heads) {                              // one head per workgroup
+    if (a.kv.D == 128 && lds_ok) {
+      const int nwork = a.kv.B * a.kv.Hq * a.kv.nblk;
+      DSA_LAUNCH("attn_prefill_heads", k_prefill_heads, dim3(nwork), dim3(128), st, a);
+      return true;
+    }
     if (a.kv.D == 128) { launch_mfma<128, 1, 2>(a, st); return true; }
     if (a.kv.D == 64) { launch_mfma<64, 1, 2>(a, st); return true; }
     return false;
   }
-  if (a.kv.D == 128 && lds_ok) {
+  if (a.kv.D == 128 && lds_ok && whole_tiles) {
     if (G >= 4) { launch_mfma_lds<4, 1>(a, st); return true; }
     if (G == 2) { launch_mfma_lds<2, 2>(a, st); return true; }
     if (G == 1) { launch_mfma<128, 1, 2>(a, st); return true; }

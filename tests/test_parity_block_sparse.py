@@ -163,3 +163,34 @@ def test_bs_ties_go_to_lower_blocks():
     for m in range(nblk):
         want = np.arange(64 * min(m + 1, kb))
         assert np.array_equal(idx[0, 0, m].cpu().numpy()[:len(want)], want)
+
+
+@pytest.mark.parametrize("width,d", [(100, 128), (50, 128), (72, 64)])
+def test_heads_attention_arbitrary_rows(width, d):
+    """Per-head rows that are not whole 64-key blocks: ascending causal
+    positions of each head's own choosing, -1 padded, widths that end inside a
+    tile (100), are not a multiple of 4 (50, the register-staged kernel) or use
+    d = 64."""
+    rng = np.random.default_rng(width)
+    hq, hkv, nblk = 4, 2, 6
+    t = 64 * nblk
+    Q = rng.integers(-8, 9, size=(1, hq, t, d)).astype(np.float32) / 8
+    K = rng.integers(-8, 9, size=(1, hkv, t, d)).astype(np.float32) / 8
+    V = rng.normal(size=(1, hkv, t, d)).astype(np.float32)
+    idx = np.full((1, hq, nblk, width), -1, dtype=np.int32)
+    for h in range(hq):
+        for m in range(nblk):
+            e = 64 * (m + 1)
+            n = int(rng.integers(1, min(width, e) + 1))
+            # key 0 in every row: each query sees at least one key
+            pos = np.union1d([0], rng.choice(np.arange(1, e), size=n - 1, replace=False))
+            idx[0, h, m, :n] = pos
+    q, k, v = (torch.from_numpy(x).to("cuda", torch.bfloat16) for x in (Q, K, V))
+    H.say(f"per-head rows width={width} d={d}")
+    out = api.sparse_attn_heads(q, k, v, torch.from_numpy(idx).cuda())
+    torch.cuda.synchronize()
+    host = Host(Q[0], K[0], v[0].float().cpu().numpy())
+    out_np = out[0].cpu().numpy()
+    for h in range(hq):
+        for m in range(nblk):
+            H.assert_close(out_np[h, 64 * m:64 * m + 64], host.attend(h, m, idx[0, h, m]), f"(h={h}, m={m})")
