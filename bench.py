@@ -716,6 +716,13 @@ def main():
             "dense_ms": round(bs["dense_ms"], 1) if bs["dense_ms"] else None,
             "speedup_vs_dense": round(bs["dense_ms"] / bs["ms"], 2) if bs["dense_ms"] else None,
             "kernels_ms": bs["kernels_ms"]}
+        kv = _counter_summary("block_sparse_128k_counters.md")
+        if kv and "bs_attn_fabric_read_bytes" in kv:
+            rb = int(kv["bs_attn_fabric_read_bytes"])
+            g = rb / (bs["attn_ms"] * 1e-3) / 1e9
+            line["block_sparse_prefill_128k"]["attn_fabric_read_bytes_measured"] = rb
+            line["block_sparse_prefill_128k"]["attn_fabric_read_gbps"] = round(g, 1)
+            line["block_sparse_prefill_128k"]["attn_fabric_read_pct_hbm_peak"] = round(100 * g / PEAK_HBM_GBPS, 2)
     if "cpu" in res:
         line["cpu_baseline"] = res["cpu"]
     print(json.dumps(line), flush=True)
