@@ -827,6 +827,228 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
 }
 
+// Shared rows, d = 128, groups of at least 4 query heads: one workgroup per
+// (query block, 4 heads of a kv group) with all 64 queries, eight waves
+// (4 heads x 2 query halves), so each K/V tile is loaded into LDS once for 256
+// (query, head) rows. Three tile buffers: the loads of tile i+2 are issued
+// when tile i begins and run under two tiles of products. Tile entry e lives
+// in LDS row 32 * (e % 2) + e / 2: lane group g = 4 * wave + lane / 16 (0..31)
+// takes entries 2g, 2g+1 (one 8-byte load of the index row, made two tiles
+// ahead of its use) and its two row loads land in rows 32u + g. Padding and
+// tiles past the row load through an out-of-range offset (zeros, no traffic).
+// The barriers leave the loads in flight; the vector-memory waits are counted
+// by hand: each step issues four row loads and one index load per wave.
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) k_prefill_gqa8(AttnArgs a) {
+  constexpr int D = 128;
+  constexpr int NH = 4;
+  constexpr int NWV = 8;
+  constexpr int KS = D / 16;
+  constexpr int DT = D / 32;
+  __shared__ __align__(16) uint16_t sk0[64 * D], sk1[64 * D], sk2[64 * D];
+  __shared__ __align__(16) uint16_t sv0[64 * D], sv1[64 * D], sv2[64 * D];
+  __shared__ __align__(16) int spos0[64], spos1[64], spos2[64];
+  __shared__ __align__(16) int sflag0[NWV], sflag1[NWV], sflag2[NWV];
+  asm volatile("" ::"r"(sk0), "r"(sk1), "r"(sk2), "r"(sv0), "r"(sv1), "r"(sv2) : "memory");
+
+  const KvLayout& kv = a.kv;
+  const int G = kv.Hq / kv.Hkv;
+  const int HG = G / NH;
+  const int nwork = kv.B * kv.Hkv * HG * kv.nblk;
+  const int per_xcd = gridDim.x >> 3;
+  int work = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (work >= nwork) return;
+  const int m = work % kv.nblk;
+  work /= kv.nblk;
+  const int hg = work % (kv.Hkv * HG);
+  const int b = work / (kv.Hkv * HG);
+  const int g = hg / HG;
+  const int s = m * 64;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int tr_row = (lane & 15) >> 2, tr_col = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
+  const int hw = w % NH, qg = w / NH;
+  const int h = g * G + (hg % HG) * NH + hw;
+  const int q0 = s + qg * 32;
+  const int wq_lo = s, wq_hi = s + 63;
+  const uint16_t* Q = static_cast<const uint16_t*>(a.q);
+  const size_t kvbase = (static_cast<size_t>(b) * kv.Hkv + g) * kv.T;
+  const uint32_t kv_bytes = static_cast<uint32_t>(kv.T) * D * 2;
+  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(static_cast<const uint16_t*>(a.k) + kvbase * D, kv_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(static_cast<const uint16_t*>(a.v) + kvbase * D, kv_bytes);
+
+  bf16x8_t qf[KS];
+  {
+    const uint16_t* qrow = Q + ((static_cast<size_t>(b) * kv.Hq + h) * kv.T + q0 + l32) * D + hi * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + ks * 16);
+  }
+  f32x16_t o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
+  float mrun = kNegBig, lrun = 0.f;
+
+  const int32_t* row = a.idx + static_cast<size_t>(b * kv.nblk + m) * a.L;
+  const int n_tiles = a.L / 64;                   // whole tiles (checked by the launcher)
+  const int lg = 4 * w + (lane >> 4);
+  const int lslot = lane & 15;
+  auto load_raw = [&](int ti) __attribute__((always_inline)) {
+    return *reinterpret_cast<const int2*>(row + min(ti, n_tiles - 1) * 64 + 2 * lg);
+  };
+  auto issue = [&](int ti, int2 raw, uint16_t* skb, uint16_t* svb, int* sposb, int* sflagb) __attribute__((always_inline)) {
+    const bool live = ti < n_tiles;
+    const int pp[2] = {live ? raw.x : -1, live ? raw.y : -1};
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int rr = 32 * u + lg;
+      const int off = pp[u] < 0 ? static_cast<int>(kv_bytes) : pp[u] * (D * 2) + ((lslot ^ swz(rr)) << 4);
+      const int lbase = (32 * u + 4 * w) * D;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void_t*)(skb + lbase), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void_t*)(svb + lbase), 16, off, 0, 0, 0);
+    }
+    if (lslot < 2) sposb[32 * lslot + lg] = lslot == 0 ? pp[0] : pp[1];
+    const unsigned u0 = static_cast<unsigned>(pp[0]), u1 = static_cast<unsigned>(pp[1]);
+    const unsigned long long nb = __ballot(max(u0, u1) > static_cast<unsigned>(wq_lo));
+    const unsigned long long ab = __ballot(min(u0, u1) <= static_cast<unsigned>(wq_hi));
+    if (lane == 0) sflagb[w] = (nb != 0 ? 1 : 0) | (ab != 0 ? 2 : 0);
+  };
+
+  // The prologue issues exactly what two steps would (tile rows, then the
+  // index load two tiles ahead), so every step sees the same loads in flight
+  // and the compiler's own waits before LDS reads match the steady state.
+  int2 rc = load_raw(0), rd = load_raw(1);
+  issue(0, rc, sk0, sv0, spos0, sflag0);
+  rc = load_raw(2);
+  issue(1, rd, sk1, sv1, spos1, sflag1);
+  rd = load_raw(3);
+  // raw entries in hand at step i: tiles i+2 (rc) and i+3 (rd)
+
+  auto step = [&](int ti, const uint16_t* skc, const uint16_t* svc, const int* sposc, const int* sflagc,
+                  uint16_t* skn, uint16_t* svn, int* sposn, int* sflagn) __attribute__((always_inline)) {
+    // tile ti's rows were followed by an index load, the next tile's four row
+    // loads and another index load
+    __builtin_amdgcn_s_waitcnt(0x0F76);            // vmcnt(6); expcnt, lgkmcnt not waited
+    barrier_keep_loads();                          // everyone's rows of tile ti; tile ti-1 retired
+    issue(ti + 2, rc, skn, svn, sposn, sflagn);
+    rc = rd;
+    asm volatile("" ::: "memory");
+    rd = load_raw(ti + 4);
+    asm volatile("" ::: "memory");
+    int flag = 2;
+#pragma unroll
+    for (int i = 0; i < NWV; ++i) {
+      flag |= sflagc[i] & 1;
+      if (sflagc[i] & 2) flag &= ~2;
+    }
+    flag = __builtin_amdgcn_readfirstlane(flag ^ 2);  // bit 1 now set when some key is visible
+    if (!(flag & 2)) return;
+    f32x16_t sacc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[kt][i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const int rr = kt * 32 + l32;
+        const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(skc + rr * D + ((2 * ks + hi) ^ swz(rr)) * 8);
+        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[ks], sacc[kt], 0, 0, 0);
+      }
+    }
+    if (flag & 1) {
+      const unsigned t = static_cast<unsigned>(q0 + l32);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int rn = 0; rn < 4; ++rn) {
+          const int4 p4 = *reinterpret_cast<const int4*>(sposc + kt * 32 + rn * 8 + hi * 4);
+          const int pp[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if (static_cast<unsigned>(pp[c]) > t) sacc[kt][rn * 4 + c] = -INFINITY;
+        }
+    }
+    {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kt][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * a.scale_log2;
+      const bool raise = mx > mrun + 8.0f;
+      const float m_use = raise ? mx : mrun;
+      const float alpha = __builtin_amdgcn_exp2f(mrun - m_use);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[kt][i] = __builtin_amdgcn_exp2f(fmaf(sacc[kt][i], a.scale_log2, -m_use));
+      mrun = m_use;
+      if (__ballot(raise)) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+      }
+      lrun *= alpha;
+    }
+    const bf16x2_t ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+    float ps = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int kt = ks >> 1, half = ks & 1;
+      u32x4_t u;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const uint32_t pw = pack_bf16x2(sacc[kt][half * 8 + 2 * x], sacc[kt][half * 8 + 2 * x + 1]);
+        ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw), ones, ps, false);
+        u[x] = pw;
+      }
+      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, u);
+      const int r0 = ks * 16 + hi * 4 + tr_row, r1 = r0 + 8;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int c = dt * 32 + tr_col;
+        const i16x4_t lo4 = lds_read_tr16(svc + r0 * D + (((c >> 3) ^ swz(r0)) << 3) + (c & 7));
+        const i16x4_t hi4 = lds_read_tr16(svc + r1 * D + (((c >> 3) ^ swz(r1)) << 3) + (c & 7));
+        const bf16x8_t av = __builtin_bit_cast(
+            bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb, o[dt], 0, 0, 0);
+      }
+    }
+    lrun += ps + __shfl_xor(ps, 32, 64);
+  };
+  // whole rounds of three steps, then the one or two left: the loop body has no
+  // branch around a step, so every step's loads in flight are the same
+  int ti = 0;
+  for (; ti + 3 <= n_tiles; ti += 3) {
+    step(ti, sk0, sv0, spos0, sflag0, sk2, sv2, spos2, sflag2);
+    step(ti + 1, sk1, sv1, spos1, sflag1, sk0, sv0, spos0, sflag0);
+    step(ti + 2, sk2, sv2, spos2, sflag2, sk1, sv1, spos1, sflag1);
+  }
+  if (ti < n_tiles) {
+    step(ti, sk0, sv0, spos0, sflag0, sk2, sv2, spos2, sflag2);
+    if (ti + 1 < n_tiles) step(ti + 1, sk1, sv1, spos1, sflag1, sk0, sv0, spos0, sflag0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);                  // no load into LDS outlives the workgroup
+
+  const float inv = 1.0f / lrun;
+  float* orow = a.out + ((static_cast<size_t>(b) * kv.Hq + h) * kv.T + q0 + l32) * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      float4 v;
+      v.x = o[dt][i4 * 4 + 0] * inv;
+      v.y = o[dt][i4 * 4 + 1] * inv;
+      v.z = o[dt][i4 * 4 + 2] * inv;
+      v.w = o[dt][i4 * 4 + 3] * inv;
+      *reinterpret_cast<float4*>(orow + dt * 32 + i4 * 8 + hi * 4) = v;
+    }
+}
+
 template <int NH, int QH>
 static void launch_mfma_lds(const AttnArgs& a, hipStream_t st) {
   const int G = a.kv.Hq / a.kv.Hkv;
@@ -867,6 +1089,11 @@ bool launch_prefill_mfma(const AttnArgs& a, hipStream_t st) {
     return false;
   }
   if (a.kv.D == 128 && lds_ok && whole_tiles) {
+    if (G >= 4 && a.idx) {
+      const int nwork = a.kv.B * a.kv.Hkv * (G / 4) * a.kv.nblk;
+      DSA_LAUNCH("attn_prefill", k_prefill_gqa8, dim3((nwork + 7) / 8 * 8), dim3(512), st, a);
+      return true;
+    }
     if (G >= 4) { launch_mfma_lds<4, 1>(a, st); return true; }
     if (G == 2) { launch_mfma_lds<2, 2>(a, st); return true; }
     if (G == 1) { launch_mfma<128, 1, 2>(a, st); return true; }
