@@ -20,7 +20,11 @@ with remembered masks, the InfiniteHiP page's "Sparse Attention Mask Caching"
 (per-stage refresh intervals, stage 1 refreshed with the newest query); and
 the MInference page's Block-Sparse head estimation ("Online Dynamic Index
 Estimation: Block-Sparse Heads (Algorithm 3)": mean pooling, block-causal
-pooled logits, top-k_b blocks per query head and block).
+pooled logits, top-k_b blocks per query head and block); and its Vertical-Slash
+head estimation ("Online Dynamic Index Estimation: Vertical-Slash Heads
+(Algorithm 2)": last 64 queries, column and offset sums of their causal
+softmax, top-k_v columns and top-k_s offsets) with the index building of
+"Vertical-Slash Hybrid Kernel (Appendix C.4.2)".
 
 Readings taken where the pages are silent or garbled (each is listed with its
 reason in the project's design notes):
@@ -46,7 +50,14 @@ reason in the project's design notes):
   * block-sparse estimation: a key block is masked for query block m when it
     lies strictly after it (j > m; the diagonal block stays); blocks are ranked
     by the pooled logits in fp64 rounded to fp32 (the softmax and the scale are
-    monotone), ties to the lower block; each query head has its own rows.
+    monotone), ties to the lower block; each query head has its own rows;
+  * vertical-slash estimation: the last 64 queries of the sequence, each with
+    its causal mask; a slash offset d is query position minus key position
+    (d >= 0) and its sum runs over the estimation queries that reach key >= 0;
+    sums in fp64, ranked after one rounding to fp32, ties to the lower index;
+    per query block, each offset's key range is rounded out to the 64-aligned
+    blocks it touches (attended whole) and vertical columns outside those
+    blocks are attended singly.
 
 Every function here is pinned by tests/test_oracle.py against what the pages
 and the mathematics fix (closed forms, brute force, special cases reducing to
@@ -391,6 +402,81 @@ def bs_index_width(block: int, k_blocks: int) -> int:
     """Width of a block-sparse index row: k_b blocks of `block` positions,
     rounded up to 64."""
     return (block * k_blocks + 63) // 64 * 64
+
+
+# --------------------------------------------------------------------------- #
+# MInference Vertical-Slash heads: per-input vertical and slash estimation    #
+# ("Online Dynamic Index Estimation: Vertical-Slash Heads (Algorithm 2)";     #
+# index building of "Vertical-Slash Hybrid Kernel (Appendix C.4.2)")          #
+# --------------------------------------------------------------------------- #
+VS_LAST_Q = 64          # estimation queries: the last 64 of the sequence
+VS_BLOCK = 64           # query blocks and key blocks of the index rows
+
+
+def vs_sums(Q: np.ndarray, K, h: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Steps 1-3 for query head h of one sequence: the causal softmax of the
+    last 64 queries against every key (scale 1/sqrt(d), fp64 after exact fp32
+    dot products), summed over the queries for every key column (vertical) and
+    over the queries for every offset d = query position - key position >= 0
+    (slash). Q: [Hq, T, d], K: [Hkv, T, d]. Returns (sum_v [T], sum_s [T])."""
+    Hq, T, d = Q.shape
+    G = Hq // K.shape[0]
+    nq = min(VS_LAST_Q, T)
+    t = np.arange(T - nq, T)
+    q = np.asarray(Q[h, T - nq:], dtype=np.float32)
+    k = np.asarray(K[h // G, :T], dtype=np.float32)
+    z = (q @ k.T).astype(np.float64) * (1.0 / np.sqrt(np.float64(d)))
+    z = np.where(np.arange(T)[None, :] <= t[:, None], z, -np.inf)
+    a = np.exp(z - z.max(axis=1, keepdims=True))
+    a /= a.sum(axis=1, keepdims=True)
+    sum_v = a.sum(axis=0)
+    sum_s = np.zeros(T)
+    for i in range(nq):
+        sum_s[:t[i] + 1] += a[i, t[i]::-1]          # offset d pairs query t[i] with key t[i] - d
+    return sum_v, sum_s
+
+
+def vs_select(sums: np.ndarray, k: int) -> np.ndarray:
+    """Steps 2-3: the k highest sums, ranked in fp32 (the sums rounded once),
+    ties to the lower index; ascending."""
+    return top_k(np.asarray(sums).astype(np.float32), k)
+
+
+def vs_row(i_v: np.ndarray, i_s: np.ndarray, m: int) -> np.ndarray:
+    """Step 4 for query block m (queries [64m, 64m+64)): every slash offset d
+    covers keys [64m - d, 64m + 63 - d] in this block's rows; those ranges,
+    clipped to keys >= 0 and rounded out to the 64-aligned key blocks they
+    touch, are attended whole; vertical columns before the block's end that
+    lie in none of those blocks are attended as single columns. Returns the
+    ascending key positions (the causal mask inside the block is applied by
+    the attention)."""
+    s, e = VS_BLOCK * m, VS_BLOCK * (m + 1)
+    blocks = set()
+    for d in np.asarray(i_s, dtype=np.int64):
+        lo, hi = max(0, s - int(d)), e - 1 - int(d)
+        if hi >= 0:
+            blocks.update(range(lo // VS_BLOCK, hi // VS_BLOCK + 1))
+    cols = [int(v) for v in i_v if v < e and int(v) // VS_BLOCK not in blocks]
+    pos = [VS_BLOCK * b + x for b in sorted(blocks) for x in range(VS_BLOCK)] + cols
+    return np.array(sorted(pos), dtype=np.int64)
+
+
+def vs_index_width(T: int, k_v: int, k_s: int) -> int:
+    """Row width: at most 2 key blocks per slash offset (and no more than the
+    sequence's blocks) plus k_v columns, rounded up to 64 and at most T."""
+    n = VS_BLOCK * min(T // VS_BLOCK, 2 * k_s) + k_v
+    return min(T, (n + 63) // 64 * 64)
+
+
+def vs_rows(Q: np.ndarray, K, k_v: int, k_s: int) -> List[List[np.ndarray]]:
+    """rows[h][m] of one sequence: estimation, selection and index building."""
+    Hq, T, _ = Q.shape
+    rows = []
+    for h in range(Hq):
+        sv, ss = vs_sums(Q, K, h)
+        iv, is_ = vs_select(sv, k_v), vs_select(ss, k_s)
+        rows.append([vs_row(iv, is_, m) for m in range(T // VS_BLOCK)])
+    return rows
 
 
 # --------------------------------------------------------------------------- #

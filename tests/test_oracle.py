@@ -657,3 +657,146 @@ def test_block_sparse_equation_3_speedup():
         pairs += int((row[None, :] <= t[:, None]).sum())
     dense = S_s * (S_s + 1) // 2
     assert abs((dense / pairs) / (S_s / (2 * 64 * kb_s)) - 1) < 0.03
+
+
+# --------------------------------------------------------------------------- #
+# f3: vertical-slash estimation and index building (MInference page,         #
+# "Online Dynamic Index Estimation: Vertical-Slash Heads (Algorithm 2)",      #
+# "Vertical-Slash Hybrid Kernel (Appendix C.4.2)")                            #
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("T", [40, 64, 300])
+def test_vs_sums_are_attention_mass(T):
+    """Every estimation query's causal softmax sums to one and each (query,
+    key) pair lies on exactly one column and one offset: both sums total the
+    number of estimation queries."""
+    rng = np.random.default_rng(T)
+    Q, K = grid(rng, (2, T, 16)), grid(rng, (1, T, 16))
+    for h in range(2):
+        sv, ss = ref.vs_sums(Q, K, h)
+        nq = min(64, T)
+        assert abs(sv.sum() - nq) < 1e-10 and abs(ss.sum() - nq) < 1e-10
+        assert sv.min() >= 0 and ss.min() >= 0 and len(sv) == len(ss) == T
+
+
+def test_vs_constant_keys_closed_form():
+    """Identical keys make every causal row uniform: query t gives 1/(t+1) to
+    each key <= t, so column j and offset d both collect sum over the
+    estimation queries t >= j (t >= d) of 1/(t+1)."""
+    T = 200
+    rng = np.random.default_rng(3)
+    Q = grid(rng, (1, T, 8))
+    K = np.broadcast_to(grid(rng, (1, 1, 8)), (1, T, 8)).copy()
+    sv, ss = ref.vs_sums(Q, K, 0)
+    t = np.arange(T - 64, T)
+    want = np.array([sum(1.0 / (x + 1) for x in t if x >= j) for j in range(T)])
+    assert np.abs(sv - want).max() < 1e-12 and np.abs(ss - want).max() < 1e-12
+
+
+def test_vs_planted_column_and_offset_are_found():
+    """A key aligned with every estimation query is the top column; keys that
+    each align with one estimation query at the same distance behind it make
+    that distance the top offset."""
+    rng = np.random.default_rng(5)
+    T, d = 512, 32
+    Q = grid(rng, (1, T, d)) * np.float32(0.25)
+    K = grid(rng, (1, T, d)) * np.float32(0.25)
+    u = np.sign(rng.normal(size=d)).astype(np.float32)
+    Kv = K.copy()
+    Qv = Q.copy()
+    Qv[0, T - 64:] += u                          # every estimation query points along u
+    Kv[0, 137] = u                               # a vertical line at key 137
+    sv, _ = ref.vs_sums(Qv, Kv, 0)
+    assert list(ref.vs_select(sv, 1)) == [137]
+    d_star = 300
+    for t in range(T - 64, T):                  # a slash line at offset 300
+        K[0, t - d_star] = np.sign(Q[0, t]) * np.float32(4)
+    _, ss = ref.vs_sums(Q, K, 0)
+    assert list(ref.vs_select(ss, 1)) == [d_star]
+
+
+def test_vs_select_ranks_in_fp32_with_lower_index_ties():
+    base = 0.1
+    sums = np.array([base, base * (1 + 1e-12), 0.05, base, 0.2])   # 0, 1, 3 tie in fp32
+    assert list(ref.vs_select(sums, 2)) == [0, 4]
+    assert list(ref.vs_select(sums, 3)) == [0, 1, 4]
+    assert list(ref.vs_select(sums, 0)) == []
+
+
+def test_vs_row_worked_example():
+    g = _load("p3_vs_rows_example.json")
+    iv, is_ = np.array(g["i_v"]), np.array(g["i_s"])
+    for r in g["rows"]:
+        want = sorted([64 * b + x for b in r["blocks"] for x in range(64)] + r["columns"])
+        assert list(ref.vs_row(iv, is_, r["m"])) == want, r["why"]
+
+
+def test_vs_row_structure_and_width():
+    rng = np.random.default_rng(9)
+    T = 64 * 20
+    for k_v, k_s in [(7, 3), (30, 11), (0, 5), (12, 0)]:
+        iv = np.sort(rng.choice(T, size=k_v, replace=False))
+        is_ = np.sort(rng.choice(T, size=k_s, replace=False))
+        L = ref.vs_index_width(T, k_v, k_s)
+        assert L % 64 == 0 and L <= T
+        for m in range(T // 64):
+            row = ref.vs_row(iv, is_, m)
+            assert len(row) <= L and np.all(np.diff(row) > 0) and (len(row) == 0 or row.max() < 64 * (m + 1))
+            cols = [p for p in row if not np.all(np.isin(p - p % 64 + np.arange(64), row))]
+            assert set(cols) <= set(iv.tolist())               # everything else is whole blocks
+            for v in iv:                                       # every visible vertical is present
+                if v < 64 * (m + 1):
+                    assert v in set(row.tolist())
+
+
+def test_vs_every_offset_is_dense_causal_attention():
+    """k_s covering every offset keeps every causal block: vertical-slash
+    attention is then dense causal attention (library SDPA)."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(12)
+    Hq, T, d = 2, 192, 16
+    Q, K = grid(rng, (Hq, T, d)), grid(rng, (1, T, d))
+    V = rng.normal(size=(1, T, d)).astype(np.float32)
+    rows = ref.vs_rows(Q, K, 3, T)
+    scale = ref.default_scale(d)
+    out = np.zeros((Hq, T, d), np.float32)
+    for h in range(Hq):
+        for m in range(T // 64):
+            out[h:h + 1, 64 * m:64 * m + 64] = ref.attend_block(Q[h:h + 1, 64 * m:64 * m + 64], K, V,
+                                                                rows[h][m], 64 * m, scale)
+    want = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(Q).double(), torch.from_numpy(np.repeat(K, Hq, 0)).double(),
+        torch.from_numpy(np.repeat(V, Hq, 0)).double(), is_causal=True, scale=scale).numpy()
+    assert np.abs(out - want).max() < 1e-5
+
+
+def test_vs_diagonal_plus_columns_matches_masked_sdpa():
+    """Offset 0 alone keeps each query block's own block; with vertical columns
+    the attended set of query t is {j <= t: j in t's block or j a column},
+    checked against library SDPA with that boolean mask."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(13)
+    T, d = 256, 16
+    Q, K = grid(rng, (1, T, d)), grid(rng, (1, T, d))
+    V = rng.normal(size=(1, T, d)).astype(np.float32)
+    iv = np.array([3, 70, 71, 200])
+    scale = ref.default_scale(d)
+    out = np.zeros((1, T, d), np.float32)
+    for m in range(T // 64):
+        row = ref.vs_row(iv, np.array([0]), m)
+        out[:, 64 * m:64 * m + 64] = ref.attend_block(Q[:, 64 * m:64 * m + 64], K, V, row, 64 * m, scale)
+    t, j = np.arange(T)[:, None], np.arange(T)[None, :]
+    mask = (j <= t) & ((j // 64 == t // 64) | np.isin(j, iv))
+    want = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(Q).double(), torch.from_numpy(K).double(), torch.from_numpy(V).double(),
+        attn_mask=torch.from_numpy(mask), scale=scale).numpy()
+    assert np.abs(out - want).max() < 1e-5
+
+
+def test_vs_page_numbers():
+    g = _load("p3_vertical_slash.json")
+    assert ref.VS_LAST_Q == g["last_q"] and ref.VS_BLOCK == 64
+    assert abs(g["last_q"] * g["S_1m"] * g["d_h"] / g["estimation_multiply_adds_1m_approx"] - 1) < 0.01
+    k_v, k_s = g["search_space_vs"][0]
+    assert k_v + k_s == g["example_lines"]
+    assert g["S_1m"] // 64 == g["blocks_per_row_1m"]
+    assert abs((k_v + k_s) / g["blocks_per_row_1m"] - g["example_fraction_approx"]) < 0.001
