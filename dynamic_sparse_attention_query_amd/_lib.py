@@ -22,7 +22,8 @@ MAX_STAGES = 4
 EXPORTS = ("dsa_index_width", "dsa_workspace_bytes", "dsa_prune_select", "dsa_sparse_attn",
            "dsa_dense_attn", "dsa_mask_cache_bytes", "dsa_cached_index_width", "dsa_prune_select_cached",
            "dsa_block_sparse_index_width", "dsa_block_sparse_workspace_bytes", "dsa_block_sparse_select",
-           "dsa_sparse_attn_heads", "dsa_profile_begin", "dsa_profile_end", "dsa_status_str", "dsa_last_error")
+           "dsa_sparse_attn_heads", "dsa_vertical_slash_index_width", "dsa_vertical_slash_workspace_bytes",
+           "dsa_vertical_slash_select", "dsa_profile_begin", "dsa_profile_end", "dsa_status_str", "dsa_last_error")
 
 
 class CParams(ctypes.Structure):
@@ -89,6 +90,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dsa_sparse_attn_heads.argtypes = [ctypes.POINTER(CShape), vp, vp, vp, vp, ctypes.c_int32, ctypes.c_float,
                                           vp, vp]
     lib.dsa_sparse_attn_heads.restype = ctypes.c_int
+    lib.dsa_vertical_slash_index_width.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+    lib.dsa_vertical_slash_index_width.restype = ctypes.c_int32
+    lib.dsa_vertical_slash_workspace_bytes.argtypes = [ctypes.POINTER(CShape), ctypes.c_int32, ctypes.c_int32,
+                                                       ctypes.POINTER(sz)]
+    lib.dsa_vertical_slash_workspace_bytes.restype = ctypes.c_int
+    lib.dsa_vertical_slash_select.argtypes = [ctypes.POINTER(CShape), vp, vp, ctypes.c_int32, ctypes.c_int32, vp, vp,
+                                              vp, vp, sz, vp]
+    lib.dsa_vertical_slash_select.restype = ctypes.c_int
     lib.dsa_profile_begin.argtypes = []
     lib.dsa_profile_begin.restype = ctypes.c_int
     lib.dsa_profile_end.argtypes = [ctypes.POINTER(CKernelTime), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
@@ -242,6 +251,26 @@ def sparse_attn_heads_raw(shape: Shape, q: int, k: int, v: int, idx: int, idx_wi
     cs = shape.c()
     _check(load().dsa_sparse_attn_heads(ctypes.byref(cs), q, k, v, idx, idx_width, scale, out,
                                         stream or None))
+
+
+def vertical_slash_index_width(t: int, k_v: int, k_s: int) -> int:
+    w = load().dsa_vertical_slash_index_width(t, k_v, k_s)
+    if w < 0:
+        raise DsaError(1, f"invalid vertical-slash sizes t={t} k_v={k_v} k_s={k_s}")
+    return w
+
+
+def vertical_slash_workspace_bytes(shape: Shape, k_v: int, k_s: int) -> int:
+    cs, n = shape.c(), ctypes.c_size_t(0)
+    _check(load().dsa_vertical_slash_workspace_bytes(ctypes.byref(cs), k_v, k_s, ctypes.byref(n)))
+    return n.value
+
+
+def vertical_slash_select_raw(shape: Shape, q: int, k: int, k_v: int, k_s: int, idx: int, cols: int, offsets: int,
+                              ws: int, ws_bytes: int, stream: int = 0):
+    cs = shape.c()
+    _check(load().dsa_vertical_slash_select(ctypes.byref(cs), q, k, k_v, k_s, idx, cols or None, offsets or None,
+                                            ws or None, ws_bytes, stream or None))
 
 
 def profile_begin():

@@ -241,3 +241,33 @@ def sparse_attn_heads(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: to
                                scale, out.data_ptr(), _stream())
     return out
 
+
+# --------------------------------------------------------------------------- #
+# vertical-slash heads                                                        #
+# --------------------------------------------------------------------------- #
+def vertical_slash_select(q: torch.Tensor, k: torch.Tensor, k_v: int, k_s: int, *,
+                          out: Optional[torch.Tensor] = None, return_lines: bool = False):
+    """Per-head vertical-slash index estimation (prefill, bf16): rows
+    [B, Hq, T/64, L]; with return_lines also the kept columns [B, Hq, k_v] and
+    offsets [B, Hq, k_s]."""
+    shape = make_shape(q, k)
+    if shape.mode != DSA_PREFILL:
+        raise ValueError("vertical-slash estimation is a prefill call")
+    L = _lib.vertical_slash_index_width(shape.t, k_v, k_s)
+    nblk = shape.t // 64
+    n = shape.batch * shape.hq * nblk * L
+    if out is None:
+        out = torch.empty(n, dtype=torch.int32, device=q.device)
+    if out.numel() != n or out.dtype != torch.int32 or not out.is_contiguous():
+        raise ValueError("idx buffer has the wrong size, dtype or layout")
+    cols = torch.empty((shape.batch, shape.hq, max(k_v, 1)), dtype=torch.int32, device=q.device) if return_lines else None
+    offs = torch.empty((shape.batch, shape.hq, k_s), dtype=torch.int32, device=q.device) if return_lines else None
+    ws, wsb = _scratch(_lib.vertical_slash_workspace_bytes(shape, k_v, k_s), q.device)
+    _lib.vertical_slash_select_raw(shape, q.data_ptr(), k.data_ptr(), k_v, k_s, out.data_ptr(),
+                                   cols.data_ptr() if cols is not None else 0,
+                                   offs.data_ptr() if offs is not None else 0, ws, wsb, _stream())
+    idx = out.view(shape.batch, shape.hq, nblk, L)
+    if return_lines:
+        return idx, cols[..., :k_v], offs
+    return idx
+

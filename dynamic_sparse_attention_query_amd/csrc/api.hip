@@ -7,6 +7,7 @@
 
 #include "dsa.h"
 #include "dsa_internal.h"
+#include "vs_internal.h"
 
 namespace {
 
@@ -496,4 +497,106 @@ dsa_status dsa_sparse_attn_heads(const dsa_shape* s, const void* q, const void* 
   return DSA_OK;
 }
 
+
 }  // extern "C"
+
+namespace {
+
+dsa_status check_vertical_slash(const dsa_shape* s, int32_t k_v, int32_t k_s) {
+  dsa_status st = check_shape(s);
+  if (st != DSA_OK) return st;
+  if (s->mode != DSA_PREFILL) return fail(DSA_ERR_INVALID_ARG, "vertical-slash estimation is a prefill call");
+  if (s->dtype != DSA_BF16) return fail(DSA_ERR_UNSUPPORTED, "vertical-slash estimation takes bf16 inputs");
+  if (s->t % kBsBlock != 0) return fail(DSA_ERR_INVALID_ARG, "t = %d is not a multiple of 64", s->t);
+  if (s->t / kBsBlock > kBsMaxBlocks)
+    return fail(DSA_ERR_UNSUPPORTED, "t = %d; vertical-slash estimation supports up to %lld tokens", s->t,
+                kBsMaxBlocks * kBsBlock);
+  const int cap = std::min(dsa::kVsMaxKeep, s->t);
+  if (k_v < 0 || k_v > cap) return fail(DSA_ERR_INVALID_ARG, "k_v = %d not in [0, %d]", k_v, cap);
+  if (k_s < 1 || k_s > cap) return fail(DSA_ERR_INVALID_ARG, "k_s = %d not in [1, %d]", k_s, cap);
+  return DSA_OK;
+}
+
+long long vs_width_ll(long long t, long long k_v, long long k_s) {
+  const long long n = 64 * std::min(t / 64, 2 * k_s) + k_v;
+  return std::min(t, (n + 63) / 64 * 64);
+}
+
+struct VsLayout {
+  int nr;
+  size_t off_part, off_stat, off_sums, off_ckey[2], off_cidx[2], off_sel[2], bytes;
+};
+
+VsLayout vs_layout(const dsa_shape* s, int32_t k_v, int32_t k_s) {
+  VsLayout L{};
+  const size_t bh = static_cast<size_t>(s->batch) * s->hq;
+  L.nr = (s->t + dsa::kVsRange - 1) / dsa::kVsRange;
+  size_t o = 0;
+  L.off_part = o; o = align256(o + bh * L.nr * dsa::kVsLastQ * 2 * sizeof(double));
+  L.off_stat = o; o = align256(o + bh * dsa::kVsLastQ * 2 * sizeof(double));
+  L.off_sums = o; o = align256(o + bh * 2 * s->t * 4);
+  for (int i = 0; i < 2; ++i) { L.off_ckey[i] = o; o = align256(o + bh * 2 * s->t * 4); }
+  for (int i = 0; i < 2; ++i) { L.off_cidx[i] = o; o = align256(o + bh * 2 * s->t * 4); }
+  L.off_sel[0] = o; o = align256(o + bh * std::max(k_v, 1) * 4);
+  L.off_sel[1] = o; o = align256(o + bh * std::max(k_s, 1) * 4);
+  L.bytes = o;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t dsa_vertical_slash_index_width(int32_t t, int32_t k_v, int32_t k_s) {
+  if (t < 64 || t % 64 != 0 || k_v < 0 || k_s < 1 || k_v > t || k_s > t) return -1;
+  return static_cast<int32_t>(vs_width_ll(t, k_v, k_s));
+}
+
+dsa_status dsa_vertical_slash_workspace_bytes(const dsa_shape* s, int32_t k_v, int32_t k_s, size_t* out_bytes) {
+  g_err[0] = 0;
+  if (!out_bytes) return fail(DSA_ERR_INVALID_ARG, "out_bytes is NULL");
+  dsa_status st = check_vertical_slash(s, k_v, k_s);
+  if (st != DSA_OK) return st;
+  *out_bytes = vs_layout(s, k_v, k_s).bytes;
+  return DSA_OK;
+}
+
+dsa_status dsa_vertical_slash_select(const dsa_shape* s, const void* q, const void* k, int32_t k_v, int32_t k_s,
+                                     int32_t* idx, int32_t* cols, int32_t* offsets, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  g_err[0] = 0;
+  dsa_status st = check_vertical_slash(s, k_v, k_s);
+  if (st != DSA_OK) return st;
+  if (!q || !k || !idx) return fail(DSA_ERR_INVALID_ARG, "q, k and idx must be non-NULL");
+  if (!aligned16(q) || !aligned16(k)) return fail(DSA_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
+  const VsLayout lay = vs_layout(s, k_v, k_s);
+  if (!ws || ws_bytes < lay.bytes)
+    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, lay.bytes);
+  if (!aligned16(ws)) return fail(DSA_ERR_INVALID_ARG, "ws must be 16-byte aligned");
+  dsa::VsArgs a{};
+  a.kv = make_kv(s, kBsBlock);
+  a.q = q;
+  a.k = k;
+  a.keep[0] = k_v;
+  a.keep[1] = k_s;
+  a.scale = 1.0 / std::sqrt(static_cast<double>(s->d));
+  a.nr = lay.nr;
+  char* w = static_cast<char*>(ws);
+  a.part = reinterpret_cast<double*>(w + lay.off_part);
+  a.stat = reinterpret_cast<double*>(w + lay.off_stat);
+  a.sums = reinterpret_cast<uint32_t*>(w + lay.off_sums);
+  for (int i = 0; i < 2; ++i) {
+    a.ckey[i] = reinterpret_cast<uint32_t*>(w + lay.off_ckey[i]);
+    a.cidx[i] = reinterpret_cast<int32_t*>(w + lay.off_cidx[i]);
+  }
+  a.sel[0] = cols ? cols : reinterpret_cast<int32_t*>(w + lay.off_sel[0]);
+  a.sel[1] = offsets ? offsets : reinterpret_cast<int32_t*>(w + lay.off_sel[1]);
+  a.idx = idx;
+  a.L = static_cast<int>(vs_width_ll(s->t, k_v, k_s));
+  hipError_t err = dsa::launch_vertical_slash(a, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(DSA_ERR_HIP, "vertical-slash launch failed: %s", hipGetErrorString(err));
+  return DSA_OK;
+}
+
+}  // extern "C"
+

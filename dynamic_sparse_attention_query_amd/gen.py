@@ -104,7 +104,7 @@ class Config:
     n_sink: int
     n_window: int
     seed: int
-    structure: str = "plain"        # "planted" | "needles" | "plain"
+    structure: str = "plain"        # "planted" | "needles" | "local" | "plain"
     n_needles: int = 0
     ragged: Optional[Tuple[int, int]] = None   # decode: lengths ~ U[lo, hi]
     page_size: int = 0              # decode: > 0 -> paged KV pool
@@ -321,6 +321,14 @@ def make_case(cfg: Config | str, **overrides) -> Case:
                     for st in starts:
                         k_list[b].data[g, st:st + align, :] = sgn
         case.planted = planted
+    elif cfg.structure == "local":
+        # Every key points along the summed queries of its own position in its
+        # kv group: each query's largest logit is its own position, the local
+        # structure of attention heads (a strong diagonal).
+        for b in range(B):
+            for g in range(Hkv):
+                qs = q.data[b, g * (Hq // Hkv):(g + 1) * (Hq // Hkv)].astype(np.int32).sum(axis=0)
+                k_list[b].data[g] = _sign_codes(np.sign(qs).astype(np.int8))
     elif cfg.structure == "needles":
         origin, align = cfg.n_sink, cfg.chunk[0]
         lag = cfg.n_window + cfg.block_q

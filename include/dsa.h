@@ -27,6 +27,10 @@
  *                     The MInference page's Block-Sparse heads: per-head block
  *                     index estimation from mean-pooled queries and keys, and
  *                     attention over per-head index rows (see below).
+ *   dsa_vertical_slash_select
+ *                     The MInference page's Vertical-Slash heads: per-head
+ *                     column and offset estimation from the last 64 queries,
+ *                     rendered as index rows for dsa_sparse_attn_heads.
  *   dsa_dense_attn    Exact causal attention over all keys: the comparison
  *                     point (InfiniteHiP page, "Dense Attention Optimizations"
  *                     and "Formal Background: Standard Multi-Head Attention").
@@ -238,6 +242,41 @@ dsa_status dsa_block_sparse_select(const dsa_shape* shape, const void* q, const 
 dsa_status dsa_sparse_attn_heads(const dsa_shape* shape, const void* q, const void* k, const void* v,
                                  const int32_t* idx, int32_t idx_width, float scale, float* out,
                                  void* stream);
+
+/* ---- Vertical-slash heads ------------------------------------------------
+ * MInference page, "Online Dynamic Index Estimation: Vertical-Slash Heads
+ * (Algorithm 2)" and "Vertical-Slash Hybrid Kernel (Appendix C.4.2)".
+ * Prefill only, bf16. For every query head h (keys of kv head h / (Hq / Hkv)):
+ * the causal softmax of the last 64 queries (scale 1/sqrt(d)) is summed over
+ * those queries per key column and per offset d = query position - key
+ * position; the k_v columns and the k_s offsets with the largest sums (sums
+ * rounded once to fp32, ties to the lower index) are kept. Each query block m
+ * (queries 64m .. 64m+63) attends, whole, every 64-aligned key block that a
+ * kept offset's key range [64m - d, 64m + 63 - d] touches, and singly every
+ * kept column before the block's end that lies in none of those blocks.
+ *
+ * Layout: idx [B, Hq, T / 64, L] int32, L = dsa_vertical_slash_index_width();
+ * each row holds its key positions ascending, then -1 padding; the causal
+ * mask inside a block is applied by dsa_sparse_attn_heads, which consumes the
+ * rows. A query that sees no key of its row gets an undefined output.
+ * Requires t a multiple of 64 with t / 64 <= 16384, 0 <= k_v <= min(t, 8192),
+ * 1 <= k_s <= min(t, 8192). */
+
+/* Row width min(t, 64 * min(t / 64, 2 k_s) + k_v rounded up to 64); -1 if the
+ * arguments are out of range. */
+int32_t dsa_vertical_slash_index_width(int32_t t, int32_t k_v, int32_t k_s);
+
+/* Workspace bytes of dsa_vertical_slash_select for this shape. */
+dsa_status dsa_vertical_slash_workspace_bytes(const dsa_shape* shape, int32_t k_v, int32_t k_s,
+                                              size_t* out_bytes);
+
+/* Writes every index row of idx (see above). shape.mode DSA_PREFILL, dtype
+ * DSA_BF16; q [B, Hq, T, d], k [B, Hkv, T, d]; q, k and ws 16-byte aligned.
+ * cols (NULL or device int32 [B, Hq, k_v]) and offsets (NULL or device int32
+ * [B, Hq, k_s]) receive the kept columns and offsets of every head, ascending. */
+dsa_status dsa_vertical_slash_select(const dsa_shape* shape, const void* q, const void* k, int32_t k_v,
+                                     int32_t k_s, int32_t* idx, int32_t* cols, int32_t* offsets, void* ws,
+                                     size_t ws_bytes, void* stream);
 
 /* Per-kernel timing, a diagnostic for latency breakdowns. Between
  * dsa_profile_begin() and dsa_profile_end(), every kernel the library launches

@@ -181,3 +181,30 @@ def test_block_sparse_rejects_before_launch():
     with pytest.raises(_lib.DsaError) as ei:
         _lib.sparse_attn_heads_raw(good, 16, 16, 16, 16, 0, 0.0, 16)
     assert ei.value.status == DSA_ERR_INVALID_ARG
+
+
+def test_vertical_slash_sizes_and_rejections():
+    assert _lib.vertical_slash_index_width(4096, 100, 30) == 64 * 60 + 128      # 3840 + 100 -> 3968
+    assert _lib.vertical_slash_index_width(4096, 0, 4096) == 4096               # capped at t
+    assert _lib.vertical_slash_index_width(256, 3, 1) == 192                    # 64 * 2 + 3 -> 192
+    with pytest.raises(_lib.DsaError):
+        _lib.vertical_slash_index_width(4096, 10, 0)
+    good = Shape(DSA_PREFILL, DSA_BF16, 1, 32, 8, 128, 4096)
+    ws = _lib.vertical_slash_workspace_bytes(good, 100, 30)
+    assert ws >= 32 * 2 * 4096 * 4 * 5                                          # sums + 4 candidate lists
+    cases = [
+        (dict(shape=Shape(DSA_PREFILL, DSA_F32, 1, 32, 8, 128, 4096)), DSA_ERR_UNSUPPORTED),
+        (dict(shape=Shape(DSA_DECODE, DSA_BF16, 1, 32, 8, 128, 4096, seq_lens=16)), DSA_ERR_INVALID_ARG),
+        (dict(shape=Shape(DSA_PREFILL, DSA_BF16, 1, 32, 8, 128, 4096 + 32)), DSA_ERR_INVALID_ARG),
+        (dict(ks=0), DSA_ERR_INVALID_ARG),
+        (dict(kv=-1), DSA_ERR_INVALID_ARG),
+        (dict(kv=8193), DSA_ERR_INVALID_ARG),
+        (dict(ws_bytes=ws - 256), DSA_ERR_WORKSPACE),
+        (dict(q=0), DSA_ERR_INVALID_ARG),
+    ]
+    for over, code in cases:
+        a = dict(shape=good, kv=100, ks=30, q=256, ws_bytes=ws)
+        a.update(over)
+        with pytest.raises(_lib.DsaError) as ei:
+            _lib.vertical_slash_select_raw(a["shape"], a["q"], 256, a["kv"], a["ks"], 256, 0, 0, 256, a["ws_bytes"])
+        assert ei.value.status == code, over
