@@ -84,6 +84,7 @@ def parse():
     ap.add_argument("--no-cached", action="store_true", help="skip decoding with remembered stages")
     ap.add_argument("--no-other", action="store_true", help="skip the batch-32 paged and 3M-token decodes")
     ap.add_argument("--no-block-sparse", action="store_true", help="skip the block-sparse heads prefill")
+    ap.add_argument("--no-vertical-slash", action="store_true", help="skip the vertical-slash heads prefill")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-ref", action="store_true",
@@ -541,6 +542,67 @@ def block_sparse_bench(args, res, reps=3):
 
 
 # --------------------------------------------------------------------------- #
+# vertical-slash heads at the 128K prefill shape                              #
+# --------------------------------------------------------------------------- #
+VS_KEEP = (3000, 200)      # (k_v, k_s), one of the page's searched settings
+
+
+def visible_pairs(idx, chunk_heads=4):
+    """(query, key) pairs the rows [B, Hq, nblk, L] admit under the causal
+    mask: 64 per entry before the block, e - p for an entry p inside it."""
+    import torch
+    nblk = idx.shape[2]
+    s = (torch.arange(nblk, device=idx.device, dtype=torch.int64) * 64).view(1, 1, nblk, 1)
+    total = 0
+    for h0 in range(0, idx.shape[1], chunk_heads):
+        x = idx[:, h0:h0 + chunk_heads].to(torch.int64)
+        before = ((x >= 0) & (x < s)).sum().item()
+        inside = torch.where((x >= s) & (x < s + 64), s + 64 - x, torch.zeros_like(x)).sum().item()
+        total += 64 * before + inside
+        del x
+    return total
+
+
+def vertical_slash_bench(args, res, reps=3):
+    import torch
+    from dynamic_sparse_attention_query_amd import _lib, api, gen
+    from dynamic_sparse_attention_query_amd.inputs import to_device
+
+    case = gen.make_case("c2_128k", structure="local", n_needles=0)
+    cfg = case.cfg
+    dev = to_device(case)
+    del case
+    k_v, k_s = VS_KEEP
+    idx = api.vertical_slash_select(dev.q, dev.k, k_v, k_s)
+    out = api.sparse_attn_heads(dev.q, dev.k, dev.v, idx)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        api.vertical_slash_select(dev.q, dev.k, k_v, k_s, out=idx.view(-1))
+        api.sparse_attn_heads(dev.q, dev.k, dev.v, idx, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    _lib.profile_begin()
+    api.vertical_slash_select(dev.q, dev.k, k_v, k_s, out=idx.view(-1))
+    api.sparse_attn_heads(dev.q, dev.k, dev.v, idx, out=out)
+    prof = _lib.profile_end()
+    pairs = visible_pairs(idx)
+    entries = (idx >= 0).sum().item() / (idx.shape[0] * idx.shape[1] * idx.shape[2])
+    attn_f = pairs * 4 * cfg.d
+    est_ms = sum(v[1] for k, v in prof.items() if k.startswith("vs_"))
+    attn_ms = sum(v[1] for k, v in prof.items() if k.startswith("attn_"))
+    res["vertical_slash"] = dict(ms=ms, attn_tflop=attn_f / 1e12, est_ms=est_ms, attn_ms=attn_ms,
+                                 entries=entries, width=idx.shape[-1],
+                                 kernels_ms={k: round(v[1] / v[0], 3) for k, v in prof.items()})
+    log(f"vertical-slash 128K {VS_KEEP}: {ms:.2f} ms (estimation {est_ms:.2f}, attention {attn_ms:.2f}), "
+        f"{attn_f / (ms * 1e-3) / 1e12:.1f} TFLOP/s, {entries:.0f} keys per row")
+    del dev, idx, out
+    torch.cuda.empty_cache()
+
+
+# --------------------------------------------------------------------------- #
 # the other decode workloads: batch-32 ragged paged, and 3M tokens            #
 # --------------------------------------------------------------------------- #
 def other_decode(args, name, reps=20):
@@ -642,6 +704,8 @@ def main():
         prefill_bench(args, res)
     if not args.no_block_sparse:
         block_sparse_bench(args, res)
+    if not args.no_vertical_slash:
+        vertical_slash_bench(args, res)
     if not args.no_cpu:
         cpu_baseline(args, case, res)
 
@@ -723,6 +787,17 @@ def main():
             line["block_sparse_prefill_128k"]["attn_fabric_read_bytes_measured"] = rb
             line["block_sparse_prefill_128k"]["attn_fabric_read_gbps"] = round(g, 1)
             line["block_sparse_prefill_128k"]["attn_fabric_read_pct_hbm_peak"] = round(100 * g / PEAK_HBM_GBPS, 2)
+    if "vertical_slash" in res:
+        vs = res["vertical_slash"]
+        tf = vs["attn_tflop"] / (vs["ms"] * 1e-3)
+        dense_ms = res.get("block_sparse", {}).get("dense_ms")
+        line["vertical_slash_prefill_128k"] = {
+            "k_v": VS_KEEP[0], "k_s": VS_KEEP[1], "inputs": "c2 128K shape, keys along their own queries (local diagonal)",
+            "ms": round(vs["ms"], 2), "tflops": round(tf, 2), "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+            "attn_tflop": round(vs["attn_tflop"], 2), "estimation_ms": round(vs["est_ms"], 3),
+            "attn_ms": round(vs["attn_ms"], 2), "keys_per_row_mean": round(vs["entries"]), "row_width": vs["width"],
+            "speedup_vs_dense": round(dense_ms / vs["ms"], 2) if dense_ms else None,
+            "kernels_ms": vs["kernels_ms"]}
     if "cpu" in res:
         line["cpu_baseline"] = res["cpu"]
     print(json.dumps(line), flush=True)

@@ -300,21 +300,41 @@ __global__ void __launch_bounds__(256) k_vs_rows(VsArgs a) {
   __syncthreads();
   auto rank = [&](int blk) { return wpre[blk >> 5] + __popc(bits[blk >> 5] & ((1u << (blk & 31)) - 1u)); };
   int32_t* row = a.idx + (static_cast<size_t>(bh) * kv.nblk + m) * a.L;
-  for (int blk = tid; blk <= m; blk += 256) {
-    if (!marked(blk)) continue;
-    int lo = 0, hi = nc;                          // kept columns before the block
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (kept[mid] < 64 * blk) lo = mid + 1; else hi = mid;
+  // each attended block is written by one wave, one entry per lane; a wave
+  // walks every fourth bitmap word and visits only its set bits
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  for (int x = w; x < nw; x += 4) {
+    const uint32_t word = bits[x];
+    if (word == 0u) continue;
+    // lane l < 32 finds the kept columns before block 32x + l (all at once)
+    int lo = 0;
+    if (lane < 32 && ((word >> lane) & 1u)) {
+      int hi = nc;
+      const int key = 64 * (32 * x + lane);
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (kept[mid] < key) lo = mid + 1; else hi = mid;
+      }
     }
-    const int off = 64 * rank(blk) + lo;
-    for (int x = 0; x < 64; ++x) row[off + x] = 64 * blk + x;
+    int r = wpre[x];
+    for (uint32_t rest = word; rest != 0u; rest &= rest - 1u) {
+      const int l = __ffs(static_cast<int>(rest)) - 1;
+      const int blk = 32 * x + l;
+      const int before = __builtin_amdgcn_readlane(lo, l);
+      row[64 * r + before + lane] = 64 * blk + lane;
+      ++r;
+    }
   }
   for (int c = tid; c < nc; c += 256) {
     const int v = kept[c];
     row[64 * rank(v >> 6) + c] = v;
   }
-  for (int x = 64 * nb + nc + tid; x < a.L; x += 256) row[x] = -1;
+  // padding: single entries up to a multiple of 4, then 16-byte stores (L is a multiple of 64)
+  const int n_ent = 64 * nb + nc;
+  const int a4 = min((n_ent + 3) & ~3, a.L);
+  if (tid < a4 - n_ent) row[n_ent + tid] = -1;
+  int4* row4 = reinterpret_cast<int4*>(row);
+  for (int x = (a4 >> 2) + tid; x < (a.L >> 2); x += 256) row4[x] = make_int4(-1, -1, -1, -1);
 }
 
 template <int D>
