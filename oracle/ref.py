@@ -24,7 +24,8 @@ pooled logits, top-k_b blocks per query head and block); and its Vertical-Slash
 head estimation ("Online Dynamic Index Estimation: Vertical-Slash Heads
 (Algorithm 2)": last 64 queries, column and offset sums of their causal
 softmax, top-k_v columns and top-k_s offsets) with the index building of
-"Vertical-Slash Hybrid Kernel (Appendix C.4.2)".
+"Vertical-Slash Hybrid Kernel (Appendix C.4.2)"; and SelectRep with relative
+RoPE (InfiniteHiP page, "Four RoPE Styles for Context Pruning", Relative).
 
 Readings taken where the pages are silent or garbled (each is listed with its
 reason in the project's design notes):
@@ -57,7 +58,12 @@ reason in the project's design notes):
     sums in fp64, ranked after one rounding to fp32, ties to the lower index;
     per query block, each offset's key range is rounded out to the 64-aligned
     blocks it touches (attended whole) and vertical columns outside those
-    blocks are attended singly.
+    blocks are attended singly;
+  * relative RoPE in SelectRep: rotate-half pairing, theta_i = base^(-2i/d);
+    the rotation is carried by the queries (offsets n_stream + 1 left and
+    n_stream right, n_stream = the window), rounded to multiples of 1/128; a
+    representative that won from the right is scored again as the next left
+    one; a chunk's score is the one its representative won its last split with.
 
 Every function here is pinned by tests/test_oracle.py against what the pages
 and the mathematics fix (closed forms, brute force, special cases reducing to
@@ -200,6 +206,98 @@ def chunk_scores(Q: np.ndarray, K, P: np.ndarray, l: int,
             visited.extend((g, v) for v in vis)
         s = np.maximum(s, rep_score(Q[h], K[g, r]))
     return s
+
+
+# --------------------------------------------------------------------------- #
+# SelectRep with relative RoPE (InfiniteHiP page, "Four RoPE Styles for       #
+# Context Pruning": Relative (RT); "Layer-Specific Strategy Assignment")      #
+# --------------------------------------------------------------------------- #
+ROPE_QUANT = 128        # rotated queries are rounded to multiples of 1/128
+
+
+def rope_rotate(x: np.ndarray, pos: float, base: float) -> np.ndarray:
+    """Rotary embedding of x ([..., d]) at position pos, in fp64, with the
+    rotate-half pairing (element i with element i + d/2) and frequencies
+    theta_i = base^(-2i/d): x * cos(pos theta) + rotate(x) * sin(pos theta)."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    half = d // 2
+    theta = np.power(np.float64(base), -2.0 * np.arange(half, dtype=np.float64) / d)
+    ang = np.float64(pos) * theta
+    c, s = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def rt_queries(q: np.ndarray, n_stream: int, base: float) -> Tuple[np.ndarray, np.ndarray]:
+    """The two query sets of relative-RoPE SelectRep: the left-branch
+    representative sits n_stream + 1 positions behind the query, the right one
+    n_stream (keys unrotated; equal in exact arithmetic to rotating the query by
+    n_stream + 1 and the keys by 0 and 1). Rounded to multiples of 1/128, so
+    every score against grid keys is exact in fp32."""
+    ql = np.rint(rope_rotate(q, n_stream + 1, base) * ROPE_QUANT) / ROPE_QUANT
+    qr = np.rint(rope_rotate(q, n_stream, base) * ROPE_QUANT) / ROPE_QUANT
+    return ql.astype(np.float32), qr.astype(np.float32)
+
+
+def select_rep_rt_all(ql: np.ndarray, qr: np.ndarray, K, g: int, P2: np.ndarray,
+                      visited: Optional[list] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """SelectRep with relative RoPE for every chunk (row of P2): at each split
+    the left half's representative is scored with the left queries and the
+    right half's with the right queries; the right half wins only on a
+    strictly greater score; a representative that won from the right is scored
+    again as the left one of the next split. Returns (representatives, chunk
+    scores), the score being the one the representative won its last split
+    with (its left score when the chunk has a single key)."""
+    nc, l = P2.shape
+    rows = np.arange(nc)
+    a = np.zeros(nc, dtype=np.int64)
+    z = np.full(nc, l - 1, dtype=np.int64)
+    sl = rep_score(ql, K[g, P2[rows, a]])
+    if visited is not None:
+        visited.append(P2[rows, a])
+    win = sl.copy()
+    n_iter = int(np.ceil(np.log2(l))) if l > 1 else 0
+    for _ in range(n_iter):
+        mid = (a + z + 1) // 2
+        sr = rep_score(qr, K[g, P2[rows, mid]])
+        if visited is not None:
+            visited.append(P2[rows, mid])
+        right = sr > sl
+        win = np.where(right, sr, sl)
+        a = np.where(right, mid, a)
+        z = np.where(right, z, mid - 1)
+        sl = np.where(right, rep_score(ql, K[g, P2[rows, mid]]), sl)
+    return P2[rows, a], win
+
+
+def chunk_scores_rt(Q: np.ndarray, K, P: np.ndarray, l: int, n_stream: int, base: float) -> np.ndarray:
+    """Step 5 with relative-RoPE SelectRep: the max over heads of each head's
+    chunk score."""
+    Hq = Q.shape[0]
+    G = Hq // K.shape[0]
+    nc = len(P) // l
+    P2 = np.asarray(P).reshape(nc, l)
+    s = np.full(nc, -np.inf, dtype=np.float32)
+    for h in range(Hq):
+        ql, qr = rt_queries(Q[h], n_stream, base)
+        _, win = select_rep_rt_all(ql, qr, K, h // G, P2)
+        s = np.maximum(s, win)
+    return s
+
+
+def prune_block_rt(Q: np.ndarray, K, s: int, e: int, p: Params, base: float) -> np.ndarray:
+    """prune_block with relative-RoPE SelectRep (n_stream = the window)."""
+    geo = geometry(s, e, p)
+    P = np.arange(geo.mid_lo, geo.mid_hi, dtype=np.int64)
+    for l, k in zip(p.chunk, p.keep):
+        nc, kc = len(P) // l, k // l
+        if nc <= kc:
+            continue
+        sel = top_k(chunk_scores_rt(Q, K, P, l, p.n_window, base), kc)
+        P = np.asarray(P).reshape(nc, l)[sel].reshape(-1)
+    return np.concatenate([np.arange(0, geo.sink_hi, dtype=np.int64), P,
+                           np.arange(geo.mid_hi, e, dtype=np.int64)])
 
 
 def top_k(s: np.ndarray, k: int) -> np.ndarray:

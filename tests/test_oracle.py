@@ -800,3 +800,73 @@ def test_vs_page_numbers():
     assert k_v + k_s == g["example_lines"]
     assert g["S_1m"] // 64 == g["blocks_per_row_1m"]
     assert abs((k_v + k_s) / g["blocks_per_row_1m"] - g["example_fraction_approx"]) < 0.001
+
+
+# --------------------------------------------------------------------------- #
+# f4: relative RoPE in SelectRep (InfiniteHiP page, "Four RoPE Styles for     #
+# Context Pruning", Relative; "Layer-Specific Strategy Assignment")           #
+# --------------------------------------------------------------------------- #
+def _rope_complex(x, pos, base):
+    """Independent form: pairs (x_i, x_{i+d/2}) as complex numbers times
+    exp(i pos theta_i)."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    half = d // 2
+    z = x[..., :half] + 1j * x[..., half:]
+    theta = np.array([base ** (-2.0 * i / d) for i in range(half)])
+    w = z * np.exp(1j * pos * theta)
+    return np.concatenate([w.real, w.imag], axis=-1)
+
+
+def test_rope_rotation_matches_complex_form_and_is_relative():
+    rng = np.random.default_rng(30)
+    base = 10000.0
+    q, k = rng.normal(size=(5, 32)), rng.normal(size=(7, 32))
+    for pos in (0, 1, 17, 1025):
+        assert np.abs(ref.rope_rotate(q, pos, base) - _rope_complex(q, pos, base)).max() < 1e-12
+    assert np.array_equal(ref.rope_rotate(q, 0, base), q)
+    assert np.abs(np.linalg.norm(ref.rope_rotate(q, 77, base), axis=1) - np.linalg.norm(q, axis=1)).max() < 1e-12
+    lhs = ref.rope_rotate(q, 1025, base) @ ref.rope_rotate(k, 3, base).T     # absolute positions
+    rhs = ref.rope_rotate(q, 1022, base) @ k.T                               # their difference only
+    assert np.abs(lhs - rhs).max() < 1e-9
+
+
+def test_rt_queries_use_the_page_offsets_and_stay_exact():
+    g = _load("p1_rope_rt.json")
+    rng = np.random.default_rng(31)
+    q = grid(rng, (64, 128))
+    n_stream, base = 1024, 500000.0
+    ql, qr = ref.rt_queries(q, n_stream, base)
+    off_l = n_stream + g["query_position_minus_n_stream"] - g["left_branch_key_position"]
+    off_r = n_stream + g["query_position_minus_n_stream"] - g["right_branch_key_position"]
+    assert np.array_equal(ql, np.rint(_rope_complex(q, off_l, base) * 128) / 128)
+    assert np.array_equal(qr, np.rint(_rope_complex(q, off_r, base) * 128) / 128)
+    for x in (ql, qr):
+        n = x.astype(np.float64) * 128
+        assert np.array_equal(n, np.rint(n)) and np.abs(n).max() < 256      # bf16-exact
+    K = rng.integers(-8, 9, size=(300, 128))
+    exact = (np.rint(ql.astype(np.float64) * 128).astype(np.int64) @ K.T).max(axis=0) / 1024.0
+    assert np.array_equal(ref.rep_score(ql, K.astype(np.float32) / 8).astype(np.float64), exact)
+
+
+def test_rt_tournament_with_one_query_set_is_selectrep():
+    rng = np.random.default_rng(32)
+    q = grid(rng, (4, 16))
+    K = grid(rng, (1, 256, 16))
+    P2 = np.arange(256).reshape(8, 32)
+    reps, win = ref.select_rep_rt_all(q, q, K, 0, P2)
+    assert np.array_equal(reps, ref.select_rep_all(q, K, 0, P2))
+    assert np.array_equal(win, ref.rep_score(q, K[0, reps]))
+
+
+def test_rt_tournament_hand_example():
+    """Two-dimensional keys with the left queries reading coordinate 0 and the
+    right queries coordinate 1: the right half wins twice and the chunk scores
+    its last right win; when the final split goes left the chunk keeps the
+    representative's left score."""
+    ql, qr = np.array([[1.0, 0.0]], np.float32), np.array([[0.0, 1.0]], np.float32)
+    K = np.array([[[1, 0], [5, 5], [0, 2], [0, 3], [1, 0], [5, 5], [0, 2], [0, -1]]], np.float32)
+    reps, win = ref.select_rep_rt_all(ql, qr, K, 0, np.arange(8).reshape(2, 4))
+    assert list(reps) == [3, 6] and list(win) == [3.0, 0.0]
+    plain = ref.select_rep_all(ql, K, 0, np.arange(8).reshape(2, 4))      # without RoPE: key 1
+    assert list(plain) == [1, 5]
