@@ -23,7 +23,8 @@ EXPORTS = ("dsa_index_width", "dsa_workspace_bytes", "dsa_prune_select", "dsa_sp
            "dsa_dense_attn", "dsa_mask_cache_bytes", "dsa_cached_index_width", "dsa_prune_select_cached",
            "dsa_block_sparse_index_width", "dsa_block_sparse_workspace_bytes", "dsa_block_sparse_select",
            "dsa_sparse_attn_heads", "dsa_vertical_slash_index_width", "dsa_vertical_slash_workspace_bytes",
-           "dsa_vertical_slash_select", "dsa_profile_begin", "dsa_profile_end", "dsa_status_str", "dsa_last_error")
+           "dsa_vertical_slash_select", "dsa_prune_rope_workspace_bytes", "dsa_prune_select_rope",
+           "dsa_profile_begin", "dsa_profile_end", "dsa_status_str", "dsa_last_error")
 
 
 class CParams(ctypes.Structure):
@@ -38,6 +39,13 @@ class CShape(ctypes.Structure):
                 ("d", ctypes.c_int32), ("t", ctypes.c_int32),
                 ("seq_lens", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
                 ("page_size", ctypes.c_int32), ("max_pages", ctypes.c_int32)]
+
+
+class CRope(ctypes.Structure):
+    _fields_ = [("style", ctypes.c_int32), ("base", ctypes.c_double)]
+
+
+DSA_ROPE_RELATIVE = 1
 
 
 class CKernelTime(ctypes.Structure):
@@ -98,6 +106,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dsa_vertical_slash_select.argtypes = [ctypes.POINTER(CShape), vp, vp, ctypes.c_int32, ctypes.c_int32, vp, vp,
                                               vp, vp, sz, vp]
     lib.dsa_vertical_slash_select.restype = ctypes.c_int
+    lib.dsa_prune_rope_workspace_bytes.argtypes = [ctypes.POINTER(CShape), ctypes.POINTER(CParams), ctypes.POINTER(sz)]
+    lib.dsa_prune_rope_workspace_bytes.restype = ctypes.c_int
+    lib.dsa_prune_select_rope.argtypes = [ctypes.POINTER(CShape), vp, vp, ctypes.POINTER(CParams),
+                                          ctypes.POINTER(CRope), vp, vp, sz, vp]
+    lib.dsa_prune_select_rope.restype = ctypes.c_int
     lib.dsa_profile_begin.argtypes = []
     lib.dsa_profile_begin.restype = ctypes.c_int
     lib.dsa_profile_end.argtypes = [ctypes.POINTER(CKernelTime), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
@@ -271,6 +284,20 @@ def vertical_slash_select_raw(shape: Shape, q: int, k: int, k_v: int, k_s: int, 
     cs = shape.c()
     _check(load().dsa_vertical_slash_select(ctypes.byref(cs), q, k, k_v, k_s, idx, cols or None, offsets or None,
                                             ws or None, ws_bytes, stream or None))
+
+
+def prune_rope_workspace_bytes(shape: Shape, p: Params) -> int:
+    cs, cp, n = shape.c(), p.c(), ctypes.c_size_t(0)
+    _check(load().dsa_prune_rope_workspace_bytes(ctypes.byref(cs), ctypes.byref(cp), ctypes.byref(n)))
+    return n.value
+
+
+def prune_select_rope_raw(shape: Shape, q: int, k: int, p: Params, base: float, idx: int, ws: int, ws_bytes: int,
+                          stream: int = 0, style: int = DSA_ROPE_RELATIVE):
+    cs, cp = shape.c(), p.c()
+    rope = CRope(style, base)
+    _check(load().dsa_prune_select_rope(ctypes.byref(cs), q, k, ctypes.byref(cp), ctypes.byref(rope), idx,
+                                        ws or None, ws_bytes, stream or None))
 
 
 def profile_begin():

@@ -271,3 +271,26 @@ def vertical_slash_select(q: torch.Tensor, k: torch.Tensor, k_v: int, k_s: int, 
         return idx, cols[..., :k_v], offs
     return idx
 
+
+# --------------------------------------------------------------------------- #
+# pruning with relative RoPE in SelectRep                                     #
+# --------------------------------------------------------------------------- #
+def prune_select_rope(q: torch.Tensor, k: torch.Tensor, params: Params, base: float, *,
+                      seq_lens: Optional[torch.Tensor] = None, block_table: Optional[torch.Tensor] = None,
+                      t: Optional[int] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """prune_select with relative-RoPE SelectRep (q, k taken before any rotary embedding)."""
+    shape = make_shape(q, k, seq_lens=seq_lens, block_table=block_table, t=t)
+    L = _lib.index_width(params)
+    if L < 0:
+        raise _lib.DsaError(_lib.DSA_ERR_INVALID_ARG, "invalid params")
+    rows = shape.batch * (1 if shape.mode == DSA_DECODE else shape.t // params.block_q)
+    if out is None:
+        out = torch.empty(rows * L, dtype=torch.int32, device=q.device)
+    if out.numel() != rows * L or out.dtype != torch.int32:
+        raise ValueError("idx buffer has the wrong size or dtype")
+    ws, wsb = _scratch(_lib.prune_rope_workspace_bytes(shape, params), q.device)
+    _lib.prune_select_rope_raw(shape, q.data_ptr(), k.data_ptr(), params, base, out.data_ptr(), ws, wsb, _stream())
+    if shape.mode == DSA_DECODE:
+        return out.view(shape.batch, L)
+    return out.view(shape.batch, shape.t // params.block_q, L)
+

@@ -332,6 +332,12 @@ hipError_t launch_sparse_attn(const AttnArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_block_sparse(const BsArgs& a, int dtype, hipStream_t stream);
 bool launch_prefill_mfma(const AttnArgs& a, hipStream_t stream);   // bf16, b_q = 64
 struct PruneArgs;
+// top-K of one stage over every row (prune.hip)
+void launch_topk(const PruneArgs& a, int stage, int max_chunks, hipStream_t stream);
+// pruning with relative-RoPE SelectRep (prune_rope.hip); ql, qr: workspace for
+// the two rotated query sets, [R, Hq, b_q, D] bf16 each
+hipError_t launch_prune_rope(const PruneArgs& a, int dtype, uint16_t* ql, uint16_t* qr, double base,
+                             hipStream_t stream);
 bool launch_score_prefill_mfma(const PruneArgs& a, int stage, int max_chunks, hipStream_t stream,
                                const char* name);                  // bf16, b_q = 64
 

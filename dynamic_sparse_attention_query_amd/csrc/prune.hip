@@ -598,7 +598,7 @@ static void launch_decode_score(const PruneArgs& a, int stage, int max_chunks, h
   }
 }
 
-static void launch_topk(const PruneArgs& a, int stage, int max_chunks, hipStream_t st) {
+void launch_topk(const PruneArgs& a, int stage, int max_chunks, hipStream_t st) {
   const char* nm = kTopkNames[stage];
   if (max_chunks <= kTopkThreads * 4) {
     DSA_LAUNCH(nm, (k_topk<4>), dim3(a.R), dim3(kTopkThreads), st, a, stage);

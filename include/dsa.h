@@ -202,6 +202,35 @@ dsa_status dsa_sparse_attn(const dsa_shape* shape, const void* q, const void* k,
 dsa_status dsa_dense_attn(const dsa_shape* shape, const void* q, const void* k, const void* v,
                           float scale, float* out, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- Relative RoPE inside SelectRep -------------------------------------
+ * InfiniteHiP page, "Four RoPE Styles for Context Pruning" (Relative) and
+ * "Layer-Specific Strategy Assignment": q and k are taken before any rotary
+ * embedding; at every SelectRep split the left branch's representative is
+ * scored as sitting n_stream + 1 positions behind the query and the right
+ * branch's n_stream behind (n_stream = p->n_window), with the rotate-half
+ * pairing and frequencies theta_i = base^(-2i/d). The rotation is applied to
+ * the queries (equal, in exact arithmetic, to rotating the query to n_stream
+ * + 1 and the keys to 0 and 1), computed in fp64 and rounded to multiples of
+ * 1/128, so scores against grid-valued keys are exact. A representative that
+ * wins from the right is scored again as the next split's left one; a chunk's
+ * score is the score its representative won its last split with. Everything
+ * else is dsa_prune_select (rows, top-K ties, sinks and window). */
+typedef enum { DSA_ROPE_RELATIVE = 1 } dsa_rope_style;
+
+typedef struct {
+  int32_t style;     /* DSA_ROPE_RELATIVE */
+  double base;       /* rotary base (e.g. 10000 or 500000), > 1 */
+} dsa_rope;
+
+/* Workspace bytes of dsa_prune_select_rope (the pruning workspace plus two
+ * rotated copies of the queries in bf16). */
+dsa_status dsa_prune_rope_workspace_bytes(const dsa_shape* shape, const dsa_params* p, size_t* out_bytes);
+
+/* Hierarchical pruning with relative-RoPE SelectRep; arguments and idx as for
+ * dsa_prune_select (prefill or decode, contiguous or paged). */
+dsa_status dsa_prune_select_rope(const dsa_shape* shape, const void* q, const void* k, const dsa_params* p,
+                                 const dsa_rope* rope, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+
 /* ---- Block-sparse heads --------------------------------------------------
  * MInference page, "Online Dynamic Index Estimation: Block-Sparse Heads
  * (Algorithm 3)" and "Block-Sparse FlashAttention Kernel (Appendix C.4.1)".

@@ -208,3 +208,20 @@ def test_vertical_slash_sizes_and_rejections():
         with pytest.raises(_lib.DsaError) as ei:
             _lib.vertical_slash_select_raw(a["shape"], a["q"], 256, a["kv"], a["ks"], 256, 0, 0, 256, a["ws_bytes"])
         assert ei.value.status == code, over
+
+
+def test_prune_rope_sizes_and_rejections():
+    s = Shape(DSA_PREFILL, DSA_BF16, 1, 32, 8, 128, 4096)
+    plain = _lib.workspace_bytes(s, P2)
+    rope = _lib.prune_rope_workspace_bytes(s, P2)
+    assert rope >= plain and rope - plain >= 2 * 32 * 4096 * 128 * 2 - 4096      # two bf16 query copies
+    d = Shape(DSA_DECODE, DSA_BF16, 1, 32, 8, 128, 1 << 20, seq_lens=16)
+    assert _lib.prune_rope_workspace_bytes(d, P3) >= 2 * 32 * 128 * 2
+    for base, style, code in [(10000.0, 2, DSA_ERR_UNSUPPORTED), (1.0, 1, DSA_ERR_INVALID_ARG),
+                              (float("inf"), 1, DSA_ERR_INVALID_ARG)]:
+        with pytest.raises(_lib.DsaError) as ei:
+            _lib.prune_select_rope_raw(s, 256, 256, P2, base, 256, 256, rope, style=style)
+        assert ei.value.status == code
+    with pytest.raises(_lib.DsaError) as ei:
+        _lib.prune_select_rope_raw(s, 256, 256, P2, 10000.0, 256, 256, plain)
+    assert ei.value.status == DSA_ERR_WORKSPACE

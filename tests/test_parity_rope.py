@@ -1,0 +1,80 @@
+"""GPU parity of pruning with relative RoPE in SelectRep (InfiniteHiP page,
+"Four RoPE Styles for Context Pruning", Relative): dsa_prune_select_rope
+through the C ABI against the CPU oracle. The rotated queries are rounded to
+multiples of 1/128, so every SelectRep score against the grid-valued keys is
+exact on both sides and the index rows are compared bit-exactly."""
+import numpy as np
+import pytest
+import torch
+
+import helpers as H
+from dynamic_sparse_attention_query_amd import api, gen
+from dynamic_sparse_attention_query_amd.inputs import params_of, to_device
+from oracle import ref
+
+pytestmark = pytest.mark.gpu
+
+BASE = 500000.0
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from dynamic_sparse_attention_query_amd import _lib
+    _lib.load()
+
+
+def oracle_row_rt(case, b, m, qi=0):
+    cfg = case.cfg
+    p = H.oracle_params(cfg)
+    if cfg.mode == "prefill":
+        Q, s, e = H.prefill_block(case, b, m)
+    else:
+        Q, s, e = H.decode_query(case, b, qi)
+    return ref.pad_row(ref.prune_block_rt(Q, case.k[b], s, e, p, BASE), ref.index_width(p))
+
+
+def test_rope_prefill_fp32_full():
+    """The tiny fp32 workload: every block's row; RoPE changes some rows."""
+    case = gen.make_case("c1")
+    H.say("rope c1: all 128 rows")
+    dev = to_device(case)
+    p = params_of(case.cfg)
+    idx = api.prune_select_rope(dev.q, dev.k, p, BASE).cpu().numpy()
+    plain = api.prune_select(dev.q, dev.k, p).cpu().numpy()
+    for m in range(case.cfg.t // case.cfg.block_q):
+        want = oracle_row_rt(case, 0, m)
+        assert np.array_equal(idx[0, m], want), f"block {m}: first diff {np.flatnonzero(idx[0, m] != want)[:5]}"
+    changed = int((idx != plain).any(axis=-1).sum())
+    H.say(f"rope c1: {changed} of {idx.shape[1]} rows differ from plain SelectRep")
+    assert changed > 0
+
+
+def test_rope_prefill_llama_heads_4k():
+    """32 q / 8 kv heads, d = 128, bf16, three stages at T = 4096: 20 blocks."""
+    case = gen.make_case("c2", t=4096, keep=(1024, 512, 256), n_window=256, n_needles=2)
+    H.say("rope c2 4K: sampled rows")
+    dev = to_device(case)
+    idx = api.prune_select_rope(dev.q, dev.k, params_of(case.cfg), BASE).cpu().numpy()
+    for m in gen.sample_blocks(64, 18, 5):
+        want = oracle_row_rt(case, 0, m)
+        assert np.array_equal(idx[0, m], want), f"block {m}: first diff {np.flatnonzero(idx[0, m] != want)[:5]}"
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_rope_decode(paged):
+    """Decode with relative-RoPE SelectRep: a 64K-token sequence (contiguous)
+    and a ragged batch of 3 over a paged pool."""
+    if paged:
+        case = gen.make_case("c4", batch=3, ragged=(20000, 70000), t=70000)
+    else:
+        case = gen.make_case("c3", t=65536, n_queries=1)
+    H.say(f"rope decode paged={paged}")
+    dev = to_device(case)
+    q = dev.q[0].contiguous()
+    idx = api.prune_select_rope(q, dev.k, params_of(case.cfg), BASE, seq_lens=dev.seq_lens,
+                                block_table=dev.block_table, t=dev.t).cpu().numpy()
+    for b in range(case.cfg.batch):
+        want = oracle_row_rt(case, b, 0)
+        assert np.array_equal(idx[b], want), f"sequence {b}: first diff {np.flatnonzero(idx[b] != want)[:5]}"
