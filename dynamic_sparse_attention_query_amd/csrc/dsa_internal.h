@@ -338,7 +338,9 @@ void launch_topk(const PruneArgs& a, int stage, int max_chunks, hipStream_t stre
 // the two rotated query sets, [R, Hq, b_q, D] bf16 each
 hipError_t launch_prune_rope(const PruneArgs& a, int dtype, uint16_t* ql, uint16_t* qr, double base,
                              hipStream_t stream);
+// bf16, b_q = 64; ql and qr (the rotated query sets) select the relative-RoPE
+// tournaments, nullptr the plain ones
 bool launch_score_prefill_mfma(const PruneArgs& a, int stage, int max_chunks, hipStream_t stream,
-                               const char* name);                  // bf16, b_q = 64
+                               const char* name, const uint16_t* ql = nullptr, const uint16_t* qr = nullptr);
 
 }  // namespace dsa

@@ -165,61 +165,24 @@ __global__ void __launch_bounds__(kTopkThreads) k_assemble(PruneArgs a) {
 // ------------------------------------------------------------------------- //
 // decode scoring: one query per row                                         //
 // ------------------------------------------------------------------------- //
-constexpr int kChunkPages = 4;          // page ids a paged chunk loads up front
 // One lane group's SelectRep tournaments: the G query heads of kv head g over
 // the chunk of l = chunk[stage] keys starting at st; returns the best
 // representative score over the heads.
 template <typename T, int D, int G, int SPEC, bool PAGED>
 __device__ __forceinline__ float score_group(const PruneArgs& a, int stage, int b, int g, int li, int st,
                                              const RowSlice<T, D / 16> (&q)[G]) {
-  constexpr int EPL = D / 16;
-  using Row = RowSlice<T, EPL>;
-  const KvLayout& kv = a.kv;
-  const T* K = static_cast<const T*>(a.k);
+  using Row = RowSlice<T, D / 16>;
   const int l = a.chunk[stage];
   float best = -INFINITY;
   auto dot = [&](const Row& kr, int hh) { return group16_sum(kr.dot(q[hh])); };
-  // Paged K (compile-time): the chunk covers at most kChunkPages pages in the
-  // common case; their ids are loaded once, together, so a tournament step
-  // costs one dependent load (the row) instead of two (table entry, then row).
-  int pg0 = 0, npg = 0;
-  bool hoist = false;
-  int pid[kChunkPages];
-  if constexpr (PAGED) {
-    pg0 = st >> kv.page_shift;
-    npg = ((st + l - 1) >> kv.page_shift) - pg0 + 1;
-    hoist = npg <= kChunkPages;
-#pragma unroll
-    for (int i = 0; i < kChunkPages; ++i)
-      pid[i] = hoist && i < npg ? kv.block_table[static_cast<size_t>(b) * kv.max_pages + pg0 + i] : 0;
-  }
-  const T* Kc = K + (static_cast<size_t>(b) * kv.Hkv + g) * kv.T * D + li * EPL;   // contiguous K
-  auto row_at = [&](int pos) {
-    Row x;
-    if constexpr (PAGED) {
-      size_t off;
-      if (hoist) {
-        const int k = (pos >> kv.page_shift) - pg0;
-        int page = pid[0];
-#pragma unroll
-        for (int i = 1; i < kChunkPages; ++i) page = k == i ? pid[i] : page;
-        off = ((static_cast<size_t>(page) * kv.Hkv + g) * kv.page_size + (pos & (kv.page_size - 1))) * D;
-      } else {
-        off = kv_offset(kv, b, g, pos);
-      }
-      x.load(K + off + li * EPL);
-    } else {
-      x.load(Kc + static_cast<size_t>(pos) * D);
-    }
-    return x;
-  };
+  const ChunkRows<T, D, PAGED> rows(a, b, g, li, st, l);
 
   float sa[G];
   int lo[G], hi[G];
   unsigned long long nvis = 0;
   int width;                                   // size of every head's remaining range
   if (l == 1) {
-    const Row k0 = row_at(st);
+    const Row k0 = rows.at(st);
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) { sa[hh] = dot(k0, hh); lo[hh] = hi[hh] = 0; }
     nvis = 1;
@@ -232,7 +195,7 @@ __device__ __forceinline__ float score_group(const PruneArgs& a, int stage, int 
     {
       Row kr[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) kr[i] = row_at(st + i * u);
+      for (int i = 0; i < 4; ++i) kr[i] = rows.at(st + i * u);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -268,7 +231,7 @@ __device__ __forceinline__ float score_group(const PruneArgs& a, int stage, int 
     {
       Row kr[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) kr[i] = row_at(st + i * u);
+      for (int i = 0; i < 8; ++i) kr[i] = rows.at(st + i * u);
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -306,7 +269,7 @@ __device__ __forceinline__ float score_group(const PruneArgs& a, int stage, int 
     width = u;
   } else {
     const int mid0 = l >> 1;
-    const Row k0 = row_at(st), k1 = row_at(st + mid0);
+    const Row k0 = rows.at(st), k1 = rows.at(st + mid0);
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
       const float a0 = dot(k0, hh), a1 = dot(k1, hh);
@@ -322,7 +285,7 @@ __device__ __forceinline__ float score_group(const PruneArgs& a, int stage, int 
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
       mid[hh] = (lo[hh] + hi[hh] + 1) >> 1;
-      kk[hh] = row_at(st + mid[hh]);
+      kk[hh] = rows.at(st + mid[hh]);
     }
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {

@@ -51,4 +51,62 @@ __device__ __forceinline__ void record_stage(const PruneArgs& a, int stage, int 
   if (a.mid_end) a.mid_end[r * kMaxStages + stage] = stage_mid_end(a, stage, r, geo);
 }
 
+// Key rows of one chunk as seen by a lane group (lane li holds elements
+// li*D/16 .. of a row). Paged K (compile-time): the chunk covers at most
+// kChunkPages pages in the common case; their ids are loaded once, together,
+// so a tournament step costs one dependent load (the row) instead of two
+// (table entry, then row).
+constexpr int kChunkPages = 4;
+template <typename T, int D, bool PAGED>
+struct ChunkRows {
+  static constexpr int EPL = D / 16;
+  const T* K;                   // contiguous: row 0 of (b, g), this lane's slice; paged: the pool + slice
+  const int32_t* table;         // paged: this sequence's page table
+  int hkv_g;                    // paged: page-pool offset of kv head g, in rows (g * page_size)
+  int page_rows;                // paged: Hkv * page_size (rows per page)
+  int shift, pg0;
+  bool hoist;
+  int pid0, pid1, pid2, pid3;       // hoisted page ids
+
+  __device__ __forceinline__ ChunkRows(const PruneArgs& a, int b, int g, int li, int st, int l) {
+    const KvLayout& kv = a.kv;
+    const T* base = static_cast<const T*>(a.k) + li * EPL;
+    if constexpr (PAGED) {
+      K = base;
+      table = kv.block_table + static_cast<size_t>(b) * kv.max_pages;
+      shift = kv.page_shift;
+      hkv_g = g * kv.page_size;
+      page_rows = kv.Hkv * kv.page_size;
+      pg0 = st >> shift;
+      const int npg = ((st + l - 1) >> shift) - pg0 + 1;
+      hoist = npg <= kChunkPages;
+      pid0 = hoist ? table[pg0] : 0;
+      pid1 = hoist && npg > 1 ? table[pg0 + 1] : 0;
+      pid2 = hoist && npg > 2 ? table[pg0 + 2] : 0;
+      pid3 = hoist && npg > 3 ? table[pg0 + 3] : 0;
+    } else {
+      K = base + (static_cast<size_t>(b) * kv.Hkv + g) * kv.T * D;
+    }
+  }
+
+  __device__ __forceinline__ RowSlice<T, EPL> at(int pos) const {
+    RowSlice<T, EPL> x;
+    if constexpr (PAGED) {
+      const int k = pos >> shift;
+      int page;
+      if (hoist) {
+        const int i = k - pg0;
+        page = i == 0 ? pid0 : i == 1 ? pid1 : i == 2 ? pid2 : pid3;
+      } else {
+        page = table[k];
+      }
+      const size_t row = static_cast<size_t>(page) * page_rows + hkv_g + (pos - (k << shift));
+      x.load(K + row * D);
+    } else {
+      x.load(K + static_cast<size_t>(pos) * D);
+    }
+    return x;
+  }
+};
+
 }  // namespace dsa

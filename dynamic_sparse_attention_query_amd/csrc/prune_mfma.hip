@@ -26,6 +26,13 @@
 // and three waves share each SIMD, which hides more of each round's
 // dependent gather latency than two waves with twice the rows each. The chunk
 // score (max over all heads) is reduced in LDS.
+//
+// With RT (relative RoPE in SelectRep, InfiniteHiP page, "Four RoPE Styles
+// for Context Pruning"), the wave holds the fragments of the head's two
+// rotated query blocks (left and right offsets, bf16 on the 1/128 grid) and
+// scores every staged key against both; the tournament keeps the
+// representative's left score and the score it last won with. The doubled
+// fragments leave room for two waves per SIMD.
 #include "prune_common.h"
 
 namespace dsa {
@@ -36,9 +43,12 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));   // 16-byte s
 
 constexpr int kRowGroup = 16;           // neighbouring query blocks scheduled together
 constexpr int kScoreGroups = 2;         // T: 32-chunk tournament groups per wave
+constexpr int kScoreGroupsRt = 2;       // T of the relative-RoPE tournaments
 
-template <int D, int T>
-__global__ void __launch_bounds__(256, 3) k_score_prefill_mfma(PruneArgs a, int stage, int ncg) {
+template <int D, int T, bool RT>
+__global__ void __launch_bounds__(256, RT ? 2 : 3)
+k_score_prefill_mfma(PruneArgs a, int stage, int ncg, const uint16_t* ql_all, const uint16_t* qr_all) {
+  constexpr int NQ = RT ? 2 : 1;        // query sets: plain, or left and right
   constexpr int KS = D / 16;
   constexpr int CPB = 32 * T;           // chunks per workgroup
   constexpr int PPR = D / 8;            // 16-byte pieces per row
@@ -99,9 +109,11 @@ __global__ void __launch_bounds__(256, 3) k_score_prefill_mfma(PruneArgs a, int 
   for (int h = w; h < kv.Hq; h += 4) {
     const int g = h / G;
     const uint16_t* Kg = K + (static_cast<size_t>(b) * kv.Hkv + g) * kv.T * D;
-    bf16x8_t qf[2][KS];
-    {
-      const uint16_t* qblk = Q + ((static_cast<size_t>(b) * kv.Hq + h) * kv.T + s) * D;
+    bf16x8_t qf[NQ][2][KS];
+#pragma unroll
+    for (int set = 0; set < NQ; ++set) {
+      const uint16_t* qblk = RT ? (set ? qr_all : ql_all) + (static_cast<size_t>(r) * kv.Hq + h) * 64 * D
+                                : Q + ((static_cast<size_t>(b) * kv.Hq + h) * kv.T + s) * D;
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
         u32x4_t v[LPS];
@@ -111,11 +123,11 @@ __global__ void __launch_bounds__(256, 3) k_score_prefill_mfma(PruneArgs a, int 
         stage_set(v);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          qf[qt][ks] = *reinterpret_cast<const bf16x8_t*>(buf + l32 * KROW + ks * 16 + hi * 8);
+          qf[set][qt][ks] = *reinterpret_cast<const bf16x8_t*>(buf + l32 * KROW + ks * 16 + hi * 8);
       }
     }
-    // sigma of the staged key for this lane's chunk column
-    auto sigma_staged = [&]() __attribute__((always_inline)) {
+    // sigma of the staged key for this lane's chunk column, against query set `set`
+    auto sigma_staged = [&](int set) __attribute__((always_inline)) {
       f32x16_t acc[2];
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt)
@@ -126,7 +138,7 @@ __global__ void __launch_bounds__(256, 3) k_score_prefill_mfma(PruneArgs a, int 
         const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(buf + l32 * KROW + ks * 16 + hi * 8);
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt)
-          acc[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[qt][ks], kf, acc[qt], 0, 0, 0);
+          acc[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[set][qt][ks], kf, acc[qt], 0, 0, 0);
       }
       float m = acc[0][0];
 #pragma unroll
@@ -135,8 +147,9 @@ __global__ void __launch_bounds__(256, 3) k_score_prefill_mfma(PruneArgs a, int 
         for (int i2 = 0; i2 < 16; ++i2) m = fmaxf(m, acc[qt][i2]);
       return fmaxf(m, __shfl_xor(m, 32, 64));
     };
-    // one round: the rows at offsets off[t] of every group, scored
-    auto round = [&](const int (&off)[T], float (&sg)[T]) __attribute__((always_inline)) {
+    // one round: the rows at offsets off[t] of every group, scored against
+    // the first query set (sg) and, with RT and `right`, the right one (sr)
+    auto round = [&](const int (&off)[T], float (&sg)[T], float (&sr)[T], bool right) __attribute__((always_inline)) {
       if (hi == 0) {
 #pragma unroll
         for (int t = 0; t < T; ++t) spos[w][t][l32] = st[t] + off[t];
@@ -147,34 +160,43 @@ __global__ void __launch_bounds__(256, 3) k_score_prefill_mfma(PruneArgs a, int 
 #pragma unroll
       for (int t = 0; t < T; ++t) {
         stage_set(v[t]);
-        sg[t] = sigma_staged();
+        sg[t] = sigma_staged(0);
+        if constexpr (RT) {
+          if (right) sr[t] = sigma_staged(1);
+        }
       }
     };
 
-    float sa[T];
+    float sa[T], win[T], unused[T];
     int lo[T], hi_r[T];
     {
       int off[T];
 #pragma unroll
       for (int t = 0; t < T; ++t) off[t] = 0;
-      round(off, sa);
+      round(off, sa, unused, false);            // key 0 is never a right candidate
 #pragma unroll
-      for (int t = 0; t < T; ++t) { lo[t] = 0; hi_r[t] = l - 1; }
+      for (int t = 0; t < T; ++t) { lo[t] = 0; hi_r[t] = l - 1; win[t] = sa[t]; }
     }
     for (int wd = l >> 1; wd >= 1; wd >>= 1) {
       int mid[T];
-      float sm[T];
+      float sm[T], smr[T];
 #pragma unroll
       for (int t = 0; t < T; ++t) mid[t] = (lo[t] + hi_r[t] + 1) >> 1;
-      round(mid, sm);
+      round(mid, sm, smr, true);
 #pragma unroll
       for (int t = 0; t < T; ++t) {
-        if (sm[t] > sa[t]) { lo[t] = mid[t]; sa[t] = sm[t]; }
-        else               { hi_r[t] = mid[t] - 1; }
+        if constexpr (RT) {
+          if (smr[t] > sa[t]) { lo[t] = mid[t]; win[t] = smr[t]; sa[t] = sm[t]; }
+          else                { hi_r[t] = mid[t] - 1; win[t] = sa[t]; }
+        } else {
+          if (sm[t] > sa[t]) { lo[t] = mid[t]; sa[t] = sm[t]; }
+          else               { hi_r[t] = mid[t] - 1; }
+          win[t] = sa[t];
+        }
       }
     }
 #pragma unroll
-    for (int t = 0; t < T; ++t) best[t] = fmaxf(best[t], sa[t]);
+    for (int t = 0; t < T; ++t) best[t] = fmaxf(best[t], win[t]);
   }
   if (hi == 0) {
 #pragma unroll
@@ -189,19 +211,24 @@ __global__ void __launch_bounds__(256, 3) k_score_prefill_mfma(PruneArgs a, int 
   }
 }
 
-// bf16 prefill with query blocks of 64: score stage `stage` on the matrix cores.
+// bf16 prefill with query blocks of 64: score stage `stage` on the matrix cores
+// (with ql and qr, the relative-RoPE tournaments over those rotated queries).
 bool launch_score_prefill_mfma(const PruneArgs& a, int stage, int max_chunks, hipStream_t st,
-                               const char* name) {
+                               const char* name, const uint16_t* ql, const uint16_t* qr) {
   if (a.kv.decode || a.kv.bq != 64 || max_chunks <= 0) return false;
-  const int ncg = (max_chunks + 32 * kScoreGroups - 1) / (32 * kScoreGroups);
+  const bool rt = ql != nullptr;
+  const int T = rt ? kScoreGroupsRt : kScoreGroups;
+  const int ncg = (max_chunks + 32 * T - 1) / (32 * T);
   const long long groups = (a.R + 8LL * kRowGroup - 1) / (8LL * kRowGroup);   // per XCD
   const dim3 grid(static_cast<unsigned>(groups * 8 * kRowGroup * ncg));
   if (a.kv.D == 128) {
-    DSA_LAUNCH(name, (k_score_prefill_mfma<128, kScoreGroups>), grid, dim3(256), st, a, stage, ncg);
+    if (rt) DSA_LAUNCH(name, (k_score_prefill_mfma<128, kScoreGroupsRt, true>), grid, dim3(256), st, a, stage, ncg, ql, qr);
+    else    DSA_LAUNCH(name, (k_score_prefill_mfma<128, kScoreGroups, false>), grid, dim3(256), st, a, stage, ncg, ql, qr);
     return true;
   }
   if (a.kv.D == 64) {
-    DSA_LAUNCH(name, (k_score_prefill_mfma<64, kScoreGroups>), grid, dim3(256), st, a, stage, ncg);
+    if (rt) DSA_LAUNCH(name, (k_score_prefill_mfma<64, kScoreGroupsRt, true>), grid, dim3(256), st, a, stage, ncg, ql, qr);
+    else    DSA_LAUNCH(name, (k_score_prefill_mfma<64, kScoreGroups, false>), grid, dim3(256), st, a, stage, ncg, ql, qr);
     return true;
   }
   return false;

@@ -78,3 +78,41 @@ def test_rope_decode(paged):
     for b in range(case.cfg.batch):
         want = oracle_row_rt(case, b, 0)
         assert np.array_equal(idx[b], want), f"sequence {b}: first diff {np.flatnonzero(idx[b] != want)[:5]}"
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d,chunk,keep,paged", [
+    ("f32", 8, 8, 64, (64, 4, 1), (2048, 512, 128), False),      # one head per group; 8-key, 4-key, 1-key chunks
+    ("bf16", 16, 2, 128, (128, 16, 2), (2048, 512, 64), True),   # groups of 8; 2-key chunks take no first round
+    ("bf16", 8, 4, 64, (32, 8, 4), (1024, 256, 64), False),      # groups of 2 at d = 64
+])
+def test_rope_decode_shapes(dtype, hq, hkv, d, chunk, keep, paged):
+    """Decode tournaments across group sizes, head dims, key types and chunk
+    lengths (every first-round form: 4 and 8 keys, none, single keys)."""
+    kw = dict(batch=2, ragged=(9000, 16384), page_size=64) if paged else dict(batch=1)
+    case = gen.make_case("c4" if paged else "c3", hq=hq, hkv=hkv, d=d, t=16384, dtype=dtype, chunk=chunk,
+                         keep=keep, n_queries=1, **kw)
+    H.say(f"rope decode {dtype} {hq}/{hkv} d={d} chunk={chunk} paged={paged}")
+    dev = to_device(case)
+    q = dev.q[0].contiguous()
+    idx = api.prune_select_rope(q, dev.k, params_of(case.cfg), BASE, seq_lens=dev.seq_lens,
+                                block_table=dev.block_table, t=dev.t).cpu().numpy()
+    for b in range(case.cfg.batch):
+        want = oracle_row_rt(case, b, 0)
+        assert np.array_equal(idx[b], want), f"sequence {b}: first diff {np.flatnonzero(idx[b] != want)[:5]}"
+
+
+@pytest.mark.parametrize("hq,hkv,d,chunk,keep", [
+    (8, 1, 64, (32, 8, 1), (512, 256, 64)),      # matrix-core tournaments at d = 64, group of 8, single keys
+    (4, 2, 128, (16, 2), (512, 128)),            # 2-key chunks
+])
+def test_rope_prefill_shapes(hq, hkv, d, chunk, keep):
+    """bf16 prefill (the matrix-core tournaments) across head layouts and
+    chunk lengths: every block's row."""
+    case = gen.make_case("c2", hq=hq, hkv=hkv, d=d, t=2048, chunk=chunk, keep=keep, n_window=64,
+                         n_sink=64, n_needles=0, structure="plain")
+    H.say(f"rope prefill {hq}/{hkv} d={d} chunk={chunk}")
+    dev = to_device(case)
+    idx = api.prune_select_rope(dev.q, dev.k, params_of(case.cfg), BASE).cpu().numpy()
+    for m in range(case.cfg.t // case.cfg.block_q):
+        want = oracle_row_rt(case, 0, m)
+        assert np.array_equal(idx[0, m], want), f"block {m}: first diff {np.flatnonzero(idx[0, m] != want)[:5]}"
