@@ -25,7 +25,8 @@ head estimation ("Online Dynamic Index Estimation: Vertical-Slash Heads
 (Algorithm 2)": last 64 queries, column and offset sums of their causal
 softmax, top-k_v columns and top-k_s offsets) with the index building of
 "Vertical-Slash Hybrid Kernel (Appendix C.4.2)"; and SelectRep with relative
-RoPE (InfiniteHiP page, "Four RoPE Styles for Context Pruning", Relative).
+and chunk-indexed RoPE (InfiniteHiP page, "Four RoPE Styles for Context
+Pruning", Relative and Chunk-indexed; "Layer-Specific Strategy Assignment").
 
 Readings taken where the pages are silent or garbled (each is listed with its
 reason in the project's design notes):
@@ -63,7 +64,13 @@ reason in the project's design notes):
     the rotation is carried by the queries (offsets n_stream + 1 left and
     n_stream right, n_stream = the window), rounded to multiples of 1/128; a
     representative that won from the right is scored again as the next left
-    one; a chunk's score is the one its representative won its last split with.
+    one; a chunk's score is the one its representative won its last split with;
+  * chunk-indexed RoPE in SelectRep: within a stage of chunk length l a key at
+    position j sits at its chunk's index (j - n_sink) / l in the stage's tiling
+    of the middle, and every query at min(i_orig, c_last + n_stream), so the
+    last chunk c_last is n_stream behind it (the page's prose; its formula is
+    garbled); queries and keys are both rotated in fp64 and rounded to the
+    1/128 grid; the tournament is the plain SelectRep on the rotated vectors.
 
 Every function here is pinned by tests/test_oracle.py against what the pages
 and the mathematics fix (closed forms, brute force, special cases reducing to
@@ -295,6 +302,75 @@ def prune_block_rt(Q: np.ndarray, K, s: int, e: int, p: Params, base: float) -> 
         if nc <= kc:
             continue
         sel = top_k(chunk_scores_rt(Q, K, P, l, p.n_window, base), kc)
+        P = np.asarray(P).reshape(nc, l)[sel].reshape(-1)
+    return np.concatenate([np.arange(0, geo.sink_hi, dtype=np.int64), P,
+                           np.arange(geo.mid_hi, e, dtype=np.int64)])
+
+
+# --------------------------------------------------------------------------- #
+# chunk-indexed RoPE in SelectRep (InfiniteHiP page, "Four RoPE Styles for    #
+# Context Pruning": Chunk-indexed; "Layer-Specific Strategy Assignment")      #
+# --------------------------------------------------------------------------- #
+def rope_round(x: np.ndarray) -> np.ndarray:
+    """Round rotated values to multiples of 1/128 (bf16-exact below 2)."""
+    return (np.rint(np.asarray(x, dtype=np.float64) * ROPE_QUANT) / ROPE_QUANT).astype(np.float32)
+
+
+def rope_rotate_rows(x: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
+    """rope_rotate with its own position for each row: x [n, d], pos [n]."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    half = d // 2
+    theta = np.power(np.float64(base), -2.0 * np.arange(half, dtype=np.float64) / d)
+    ang = np.asarray(pos, dtype=np.float64)[:, None] * theta[None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def ci_chunk_index(pos, n_sink: int, l: int):
+    """Position ID of a key: the index of its chunk of length l in the tiling
+    of the middle that starts at n_sink."""
+    return (np.asarray(pos) - n_sink) // l
+
+
+def ci_query_positions(i_orig: np.ndarray, mid_hi: int, n_sink: int, n_stream: int, l: int) -> np.ndarray:
+    """Position ID of each query: the last chunk of the stage's tiling of
+    [n_sink, mid_hi) sits n_stream behind it, capped at the query's own
+    position."""
+    c_last = (mid_hi - n_sink) // l - 1
+    return np.minimum(np.asarray(i_orig), c_last + n_stream)
+
+
+class CiKeys:
+    """K seen through chunk-indexed RoPE: K[g, positions] returns the rows
+    rotated to their chunk index and rounded to the 1/128 grid."""
+
+    def __init__(self, K, n_sink: int, l: int, base: float):
+        self.K, self.n_sink, self.l, self.base = K, n_sink, l, base
+        self.shape = K.shape
+
+    def __getitem__(self, idx):
+        g, pos = idx
+        pos = np.asarray(pos)
+        rows = np.asarray(self.K[g, pos], dtype=np.float64).reshape(len(pos), -1)
+        return rope_round(rope_rotate_rows(rows, ci_chunk_index(pos, self.n_sink, self.l), self.base))
+
+
+def prune_block_ci(Q: np.ndarray, K, s: int, e: int, p: Params, base: float) -> np.ndarray:
+    """prune_block with chunk-indexed RoPE (n_stream = the window): in every
+    stage the queries and the keys are rotated to their position IDs and the
+    plain SelectRep, chunk score and top-K run on the rotated vectors."""
+    geo = geometry(s, e, p)
+    P = np.arange(geo.mid_lo, geo.mid_hi, dtype=np.int64)
+    i_orig = np.arange(s, e)
+    for l, k in zip(p.chunk, p.keep):
+        nc, kc = len(P) // l, k // l
+        if nc <= kc:
+            continue
+        qpos = ci_query_positions(i_orig, geo.mid_hi, p.n_sink, p.n_window, l)
+        Qr = np.stack([rope_round(rope_rotate_rows(Q[h], qpos, base)) for h in range(Q.shape[0])])
+        sel = top_k(chunk_scores(Qr, CiKeys(K, p.n_sink, l, base), P, l), kc)
         P = np.asarray(P).reshape(nc, l)[sel].reshape(-1)
     return np.concatenate([np.arange(0, geo.sink_hi, dtype=np.int64), P,
                            np.arange(geo.mid_hi, e, dtype=np.int64)])

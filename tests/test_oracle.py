@@ -870,3 +870,98 @@ def test_rt_tournament_hand_example():
     assert list(reps) == [3, 6] and list(win) == [3.0, 0.0]
     plain = ref.select_rep_all(ql, K, 0, np.arange(8).reshape(2, 4))      # without RoPE: key 1
     assert list(plain) == [1, 5]
+
+
+# --------------------------------------------------------------------------- #
+# f4: chunk-indexed RoPE in SelectRep (InfiniteHiP page, "Four RoPE Styles for #
+# Context Pruning", Chunk-indexed; "Layer-Specific Strategy Assignment")       #
+# --------------------------------------------------------------------------- #
+def test_rope_rows_match_complex_form():
+    rng = np.random.default_rng(40)
+    x = rng.normal(size=(6, 16))
+    pos = np.array([0, 1, 5, 99, 1000, 123457])
+    got = ref.rope_rotate_rows(x, pos, 10000.0)
+    for i in range(6):
+        assert np.abs(got[i] - _rope_complex(x[i], pos[i], 10000.0)).max() < 1e-9
+    assert np.array_equal(ref.rope_round(np.array([0.3, -1.0 / 256 - 1e-9, 1.999])) * 128, [38.0, -1.0, 256.0])
+
+
+def test_ci_positions_follow_the_page():
+    g = _load("p1_rope_ci.json")
+    p = ref.Params(1, (64, 8), (1024, 256), 16, 1024)
+    e = 100_000
+    geo = ref.geometry(e - 1, e, p)
+    for l in p.chunk:
+        pos = np.arange(geo.mid_lo, geo.mid_hi)
+        c = ref.ci_chunk_index(pos, p.n_sink, l)
+        assert g["keys_in_one_chunk_share_id"] and np.all(c.reshape(-1, l) == c[::l][:, None])
+        assert np.all(np.diff(c[::l]) == g["consecutive_chunks_id_step"]) and c[0] == 0
+        qpos = ref.ci_query_positions(np.array([e - 1]), geo.mid_hi, p.n_sink, p.n_window, l)
+        assert g["query_id_minus_last_chunk_id"] == "n_stream" and qpos[0] - c[-1] == p.n_window
+    # the cap: single-key chunks and no sinks put the last chunk's ID past
+    # the first queries of a block
+    p1 = ref.Params(64, (1,), (8,), 0, 64)
+    geo = ref.geometry(128, 192, p1)
+    qpos = ref.ci_query_positions(np.arange(128, 192), geo.mid_hi, 0, 64, 1)
+    assert g["query_id_cap"] == "i_orig"
+    assert np.array_equal(qpos, np.minimum(np.arange(128, 192), geo.mid_hi - 1 + 64)) and qpos[0] == 128
+
+
+def test_ci_rotated_scores_are_exact():
+    rng = np.random.default_rng(41)
+    Q = grid(rng, (64, 128))
+    K = grid(rng, (1, 512, 128))
+    qr = ref.rope_round(ref.rope_rotate_rows(Q, np.full(64, 4321), 500000.0))
+    kr = ref.CiKeys(K, 0, 8, 500000.0)[0, np.arange(512)]
+    for x in (qr, kr):
+        n = x.astype(np.float64) * 128
+        assert np.array_equal(n, np.rint(n)) and np.abs(n).max() < 256            # bf16-exact
+    exact = (np.rint(qr.astype(np.float64) * 128).astype(np.int64)
+             @ np.rint(kr.astype(np.float64) * 128).astype(np.int64).T).max(axis=0) / 16384.0
+    assert np.array_equal(ref.rep_score(qr, kr).astype(np.float64), exact)
+
+
+def test_ci_with_trivial_rotation_is_plain_pruning():
+    """Pair 0 (the only frequency that turns at any base) zero in Q and K and
+    a base so large that every other angle rounds away: chunk-indexed pruning
+    equals the plain pruning, in both modes and over three stages."""
+    rng = np.random.default_rng(42)
+    d = 32
+    K = grid(rng, (2, 4096, d))
+    K[:, :, 0] = K[:, :, d // 2] = 0
+    p = ref.Params(64, (64, 8, 1), (1024, 256, 64), 16, 128)
+    for s, e in ((4032, 4096), (4095, 4096), (1984, 2048)):
+        Q = grid(rng, (4, e - s, d))
+        Q[:, :, 0] = Q[:, :, d // 2] = 0
+        assert np.array_equal(ref.prune_block_ci(Q, K, s, e, p, 1e300), ref.prune_block(Q, K, s, e, p))
+
+
+def test_ci_hand_example_two_stages():
+    """d = 2 (one pair, angle = position): identical keys (1, 0) and query
+    (1, 0), so each chunk's score is the rounded cos(query ID - chunk ID); the
+    plain pruning ties everywhere and keeps the first chunks."""
+    n_sink, n_stream = 4, 8
+    p = ref.Params(1, (8, 4), (32, 8), n_sink, n_stream)
+    e = 4 + 10 * 8 + 8
+    K = np.tile(np.array([1.0, 0.0], np.float32), (1, e, 1))
+    Q = np.array([[[1.0, 0.0]]], np.float32)
+
+    def rnd(v):
+        return round(v * 128) / 128
+
+    def score(qid, cid):
+        return rnd(math.cos(qid)) * rnd(math.cos(cid)) + rnd(math.sin(qid)) * rnd(math.sin(cid))
+
+    # stage 1: ten chunks of 8 (IDs 0..9), query ID 9 + n_stream; keep 4
+    s1 = [score(9 + n_stream, c) for c in range(10)]
+    keep1 = sorted(sorted(range(10), key=lambda c: (-s1[c], c))[:4])
+    # stage 2: chunks of 4 of the kept ones (IDs (pos - n_sink) / 4), query ID 19 + n_stream; keep 2
+    c2 = [2 * c + h for c in keep1 for h in (0, 1)]
+    s2 = {c: score(19 + n_stream, c) for c in c2}
+    keep2 = sorted(sorted(c2, key=lambda c: (-s2[c], c))[:2])
+    want = list(range(n_sink)) + [n_sink + 4 * c + i for c in keep2 for i in range(4)] + list(range(84, e))
+    got = ref.prune_block_ci(Q, K, e - 1, e, p, 10000.0)
+    assert keep1 == [3, 4, 5, 6] and keep2 == [8, 9]
+    assert list(got) == want
+    plain = ref.prune_block(Q, K, e - 1, e, p)
+    assert list(plain[n_sink:n_sink + 8]) == list(range(n_sink, n_sink + 8))
