@@ -46,6 +46,7 @@ class CRope(ctypes.Structure):
 
 
 DSA_ROPE_RELATIVE = 1
+DSA_ROPE_CHUNK_INDEXED = 2
 
 
 class CKernelTime(ctypes.Structure):
@@ -106,7 +107,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dsa_vertical_slash_select.argtypes = [ctypes.POINTER(CShape), vp, vp, ctypes.c_int32, ctypes.c_int32, vp, vp,
                                               vp, vp, sz, vp]
     lib.dsa_vertical_slash_select.restype = ctypes.c_int
-    lib.dsa_prune_rope_workspace_bytes.argtypes = [ctypes.POINTER(CShape), ctypes.POINTER(CParams), ctypes.POINTER(sz)]
+    lib.dsa_prune_rope_workspace_bytes.argtypes = [ctypes.POINTER(CShape), ctypes.POINTER(CParams),
+                                                   ctypes.POINTER(CRope), ctypes.POINTER(sz)]
     lib.dsa_prune_rope_workspace_bytes.restype = ctypes.c_int
     lib.dsa_prune_select_rope.argtypes = [ctypes.POINTER(CShape), vp, vp, ctypes.POINTER(CParams),
                                           ctypes.POINTER(CRope), vp, vp, sz, vp]
@@ -286,9 +288,11 @@ def vertical_slash_select_raw(shape: Shape, q: int, k: int, k_v: int, k_s: int, 
                                             ws or None, ws_bytes, stream or None))
 
 
-def prune_rope_workspace_bytes(shape: Shape, p: Params) -> int:
+def prune_rope_workspace_bytes(shape: Shape, p: Params, style: int = DSA_ROPE_RELATIVE, base: float = 10000.0) -> int:
     cs, cp, n = shape.c(), p.c(), ctypes.c_size_t(0)
-    _check(load().dsa_prune_rope_workspace_bytes(ctypes.byref(cs), ctypes.byref(cp), ctypes.byref(n)))
+    rope = CRope(style, base)
+    _check(load().dsa_prune_rope_workspace_bytes(ctypes.byref(cs), ctypes.byref(cp), ctypes.byref(rope),
+                                                 ctypes.byref(n)))
     return n.value
 
 

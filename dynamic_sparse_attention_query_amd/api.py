@@ -273,12 +273,17 @@ def vertical_slash_select(q: torch.Tensor, k: torch.Tensor, k_v: int, k_s: int, 
 
 
 # --------------------------------------------------------------------------- #
-# pruning with relative RoPE in SelectRep                                     #
+# pruning with RoPE inside SelectRep (relative or chunk-indexed)              #
 # --------------------------------------------------------------------------- #
 def prune_select_rope(q: torch.Tensor, k: torch.Tensor, params: Params, base: float, *,
                       seq_lens: Optional[torch.Tensor] = None, block_table: Optional[torch.Tensor] = None,
-                      t: Optional[int] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """prune_select with relative-RoPE SelectRep (q, k taken before any rotary embedding)."""
+                      t: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                      style: str = "relative") -> torch.Tensor:
+    """prune_select with RoPE inside SelectRep (q, k taken before any rotary
+    embedding); style "relative" or "chunk_indexed"."""
+    styles = {"relative": _lib.DSA_ROPE_RELATIVE, "chunk_indexed": _lib.DSA_ROPE_CHUNK_INDEXED}
+    if style not in styles:
+        raise ValueError(f"rope style {style!r}; expected one of {sorted(styles)}")
     shape = make_shape(q, k, seq_lens=seq_lens, block_table=block_table, t=t)
     L = _lib.index_width(params)
     if L < 0:
@@ -288,8 +293,9 @@ def prune_select_rope(q: torch.Tensor, k: torch.Tensor, params: Params, base: fl
         out = torch.empty(rows * L, dtype=torch.int32, device=q.device)
     if out.numel() != rows * L or out.dtype != torch.int32:
         raise ValueError("idx buffer has the wrong size or dtype")
-    ws, wsb = _scratch(_lib.prune_rope_workspace_bytes(shape, params), q.device)
-    _lib.prune_select_rope_raw(shape, q.data_ptr(), k.data_ptr(), params, base, out.data_ptr(), ws, wsb, _stream())
+    ws, wsb = _scratch(_lib.prune_rope_workspace_bytes(shape, params, styles[style], base), q.device)
+    _lib.prune_select_rope_raw(shape, q.data_ptr(), k.data_ptr(), params, base, out.data_ptr(), ws, wsb, _stream(),
+                               style=styles[style])
     if shape.mode == DSA_DECODE:
         return out.view(shape.batch, L)
     return out.view(shape.batch, shape.t // params.block_q, L)

@@ -605,30 +605,42 @@ namespace {
 
 dsa_status check_rope(const dsa_rope* r) {
   if (!r) return fail(DSA_ERR_INVALID_ARG, "rope is NULL");
-  if (r->style != DSA_ROPE_RELATIVE) return fail(DSA_ERR_UNSUPPORTED, "rope style %d; supported: DSA_ROPE_RELATIVE", r->style);
+  if (r->style != DSA_ROPE_RELATIVE && r->style != DSA_ROPE_CHUNK_INDEXED)
+    return fail(DSA_ERR_UNSUPPORTED, "rope style %d; supported: DSA_ROPE_RELATIVE, DSA_ROPE_CHUNK_INDEXED", r->style);
   if (!(r->base > 1.0) || !std::isfinite(r->base)) return fail(DSA_ERR_INVALID_ARG, "rope base must be a finite value > 1");
   return DSA_OK;
 }
 
-// the plain pruning workspace, then the two rotated query sets (bf16)
+// the plain pruning workspace, then the rotated query sets (bf16), then (the
+// chunk-indexed style in prefill) the rotated keys
 size_t rope_query_bytes(const dsa_shape* s, const dsa_params* p, const PruneLayout& lay) {
   const long long bq = s->mode == DSA_DECODE ? 1 : p->block_q;
   return align256(static_cast<size_t>(lay.R) * s->hq * bq * s->d * 2);
+}
+size_t rope_key_bytes(const dsa_shape* s, const dsa_rope* r) {
+  if (r->style != DSA_ROPE_CHUNK_INDEXED || s->mode == DSA_DECODE) return 0;
+  return align256(static_cast<size_t>(s->batch) * s->hkv * s->t * s->d * 2);
+}
+size_t rope_bytes(const dsa_shape* s, const dsa_params* p, const dsa_rope* r, const PruneLayout& lay) {
+  const int sets = r->style == DSA_ROPE_RELATIVE ? 2 : 1;
+  return lay.bytes + sets * rope_query_bytes(s, p, lay) + rope_key_bytes(s, r);
 }
 
 }  // namespace
 
 extern "C" {
 
-dsa_status dsa_prune_rope_workspace_bytes(const dsa_shape* s, const dsa_params* p, size_t* out_bytes) {
+dsa_status dsa_prune_rope_workspace_bytes(const dsa_shape* s, const dsa_params* p, const dsa_rope* rope,
+                                          size_t* out_bytes) {
   g_err[0] = 0;
   if (!out_bytes) return fail(DSA_ERR_INVALID_ARG, "out_bytes is NULL");
   dsa_status st = check_shape(s);
   if (st != DSA_OK) return st;
   st = check_params(s, p);
   if (st != DSA_OK) return st;
-  const PruneLayout lay = prune_layout(s, p);
-  *out_bytes = lay.bytes + 2 * rope_query_bytes(s, p, lay);
+  st = check_rope(rope);
+  if (st != DSA_OK) return st;
+  *out_bytes = rope_bytes(s, p, rope, prune_layout(s, p));
   return DSA_OK;
 }
 
@@ -648,14 +660,16 @@ dsa_status dsa_prune_select_rope(const dsa_shape* s, const void* q, const void* 
   if (lay.maxNC > 32768)
     return fail(DSA_ERR_UNSUPPORTED, "a stage would score %lld chunks per row (limit 32768)", lay.maxNC);
   const size_t qb = rope_query_bytes(s, p, lay);
-  const size_t need = lay.bytes + 2 * qb;
+  const size_t need = rope_bytes(s, p, rope, lay);
   if (!ws || ws_bytes < need)
     return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, need);
   const dsa::PruneArgs a = prune_args(s, q, k, p, idx, L, lay, ws, nullptr);
   char* w = static_cast<char*>(ws);
-  uint16_t* ql = reinterpret_cast<uint16_t*>(w + lay.bytes);
-  uint16_t* qr = reinterpret_cast<uint16_t*>(w + lay.bytes + qb);
-  hipError_t err = dsa::launch_prune_rope(a, s->dtype, ql, qr, rope->base, static_cast<hipStream_t>(stream));
+  uint16_t* qa = reinterpret_cast<uint16_t*>(w + lay.bytes);
+  uint16_t* qb2 = rope->style == DSA_ROPE_RELATIVE ? reinterpret_cast<uint16_t*>(w + lay.bytes + qb) : nullptr;
+  uint16_t* kb = rope_key_bytes(s, rope) ? reinterpret_cast<uint16_t*>(w + lay.bytes + qb) : nullptr;
+  hipError_t err = dsa::launch_prune_rope(a, s->dtype, rope->style, qa, qb2, kb, rope->base,
+                                          static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return fail(DSA_ERR_HIP, "prune launch failed: %s", hipGetErrorString(err));
   return DSA_OK;
 }

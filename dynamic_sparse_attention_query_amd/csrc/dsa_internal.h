@@ -334,10 +334,14 @@ bool launch_prefill_mfma(const AttnArgs& a, hipStream_t stream);   // bf16, b_q 
 struct PruneArgs;
 // top-K of one stage over every row (prune.hip)
 void launch_topk(const PruneArgs& a, int stage, int max_chunks, hipStream_t stream);
-// pruning with relative-RoPE SelectRep (prune_rope.hip); ql, qr: workspace for
-// the two rotated query sets, [R, Hq, b_q, D] bf16 each
-hipError_t launch_prune_rope(const PruneArgs& a, int dtype, uint16_t* ql, uint16_t* qr, double base,
-                             hipStream_t stream);
+// pruning with RoPE inside SelectRep (prune_rope.hip). Relative style: qa, qb
+// receive the two rotated query sets, [R, Hq, b_q, D] bf16 each. Chunk-indexed
+// style: qa receives each stage's rotated queries in the layout of q (bf16),
+// kb (prefill) each stage's rotated keys in the layout of k (bf16).
+hipError_t launch_prune_rope(const PruneArgs& a, int dtype, int style, uint16_t* qa, uint16_t* qb, uint16_t* kb,
+                             double base, hipStream_t stream);
+// plain scoring of a prefill stage on bf16 rows (prune.hip)
+void launch_score_prefill_bf16(const PruneArgs& a, int stage, int max_chunks, hipStream_t stream, const char* name);
 // bf16, b_q = 64; ql and qr (the rotated query sets) select the relative-RoPE
 // tournaments, nullptr the plain ones
 bool launch_score_prefill_mfma(const PruneArgs& a, int stage, int max_chunks, hipStream_t stream,

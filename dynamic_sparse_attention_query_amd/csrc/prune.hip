@@ -18,6 +18,7 @@
 #include <algorithm>
 
 #include "prune_common.h"
+#include "selectrep.h"
 #include "topk_select.h"
 
 namespace dsa {
@@ -165,148 +166,13 @@ __global__ void __launch_bounds__(kTopkThreads) k_assemble(PruneArgs a) {
 // ------------------------------------------------------------------------- //
 // decode scoring: one query per row                                         //
 // ------------------------------------------------------------------------- //
-// One lane group's SelectRep tournaments: the G query heads of kv head g over
-// the chunk of l = chunk[stage] keys starting at st; returns the best
-// representative score over the heads.
+// One lane group's SelectRep tournaments over the chunk of chunk[stage] keys
+// starting at st, on the rows of kv head g as stored.
 template <typename T, int D, int G, int SPEC, bool PAGED>
 __device__ __forceinline__ float score_group(const PruneArgs& a, int stage, int b, int g, int li, int st,
                                              const RowSlice<T, D / 16> (&q)[G]) {
-  using Row = RowSlice<T, D / 16>;
-  const int l = a.chunk[stage];
-  float best = -INFINITY;
-  auto dot = [&](const Row& kr, int hh) { return group16_sum(kr.dot(q[hh])); };
-  const ChunkRows<T, D, PAGED> rows(a, b, g, li, st, l);
-
-  float sa[G];
-  int lo[G], hi[G];
-  unsigned long long nvis = 0;
-  int width;                                   // size of every head's remaining range
-  if (l == 1) {
-    const Row k0 = rows.at(st);
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) { sa[hh] = dot(k0, hh); lo[hh] = hi[hh] = 0; }
-    nvis = 1;
-    width = 1;
-  } else if (SPEC == 4 && l >= 4) {
-    // the 4 keys that can represent the first two splits (positions i*l/4)
-    // in one round
-    const int u = l >> 2;
-    float sc4[G][4];
-    {
-      Row kr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) kr[i] = rows.at(st + i * u);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) sc4[hh][i] = dot(kr[i], hh);
-    }
-    int a1[G];
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      int A = 0;
-      float s0 = sc4[hh][0];
-      if (sc4[hh][2] > s0) { A = 2; s0 = sc4[hh][2]; }
-      a1[hh] = A;
-      const float s2 = A ? sc4[hh][3] : sc4[hh][1];
-      if (s2 > s0) { A += 1; s0 = s2; }
-      lo[hh] = A * u;
-      hi[hh] = A * u + u - 1;
-      sa[hh] = s0;
-    }
-    if (a.visited) {
-      nvis = 2;                                 // split 1: keys 0 and l/2
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {          // split 2: distinct midpoints
-        bool f2 = true;
-#pragma unroll
-        for (int h2 = 0; h2 < hh; ++h2) f2 = f2 && (a1[h2] != a1[hh]);
-        nvis += f2 ? 1 : 0;
-      }
-    }
-    width = u;
-  } else if (SPEC == 8 && l >= 8) {
-    const int u = l >> 3;
-    float sc8[G][8];
-    {
-      Row kr[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) kr[i] = rows.at(st + i * u);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) sc8[hh][i] = dot(kr[i], hh);
-    }
-    int a1[G], a2[G];
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      int A = 0;
-      float s0 = sc8[hh][0];
-      if (sc8[hh][4] > s0) { A = 4; s0 = sc8[hh][4]; }
-      a1[hh] = A;
-      const float s2 = A ? sc8[hh][6] : sc8[hh][2];
-      if (s2 > s0) { A += 2; s0 = s2; }
-      a2[hh] = A;
-      const float s3 = A == 0 ? sc8[hh][1] : A == 2 ? sc8[hh][3] : A == 4 ? sc8[hh][5] : sc8[hh][7];
-      if (s3 > s0) { A += 1; s0 = s3; }
-      lo[hh] = A * u;
-      hi[hh] = A * u + u - 1;
-      sa[hh] = s0;
-    }
-    if (a.visited) {
-      nvis = 2;                                 // split 1: keys 0 and l/2
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {          // splits 2 and 3: distinct midpoints
-        bool f2 = true, f3 = true;
-#pragma unroll
-        for (int h2 = 0; h2 < hh; ++h2) {
-          f2 = f2 && (a1[h2] != a1[hh]);
-          f3 = f3 && (a2[h2] != a2[hh]);
-        }
-        nvis += (f2 ? 1 : 0) + (f3 ? 1 : 0);
-      }
-    }
-    width = u;
-  } else {
-    const int mid0 = l >> 1;
-    const Row k0 = rows.at(st), k1 = rows.at(st + mid0);
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      const float a0 = dot(k0, hh), a1 = dot(k1, hh);
-      if (a1 > a0) { lo[hh] = mid0; hi[hh] = l - 1; sa[hh] = a1; }
-      else         { lo[hh] = 0;    hi[hh] = mid0 - 1; sa[hh] = a0; }
-    }
-    nvis = 2;
-    width = mid0;
-  }
-  for (int wdt = width >> 1; wdt >= 1; wdt >>= 1) {   // remaining splits
-    Row kk[G];
-    int mid[G];
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      mid[hh] = (lo[hh] + hi[hh] + 1) >> 1;
-      kk[hh] = rows.at(st + mid[hh]);
-    }
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      const float acc = dot(kk[hh], hh);
-      if (acc > sa[hh]) { lo[hh] = mid[hh]; sa[hh] = acc; }
-      else              { hi[hh] = mid[hh] - 1; }
-    }
-    if (a.visited) {
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        bool fresh = true;
-#pragma unroll
-        for (int h2 = 0; h2 < hh; ++h2) fresh = fresh && (mid[h2] != mid[hh]);
-        nvis += fresh ? 1 : 0;
-      }
-    }
-  }
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) best = fmaxf(best, sa[hh]);
-  if (a.visited && li == 0) atomicAdd(a.visited + stage, nvis);
-  return best;
+  const ChunkRows<T, D, PAGED> rows(a, b, g, li, st, a.chunk[stage]);
+  return selectrep_group<T, D, G, SPEC>(a, stage, li, st, rows, q);
 }
 
 // Workgroup = 16 lane groups of 16 lanes; a group owns one (chunk, kv head)
@@ -707,6 +573,15 @@ static hipError_t launch_typed(const PruneArgs& a, hipStream_t st) {
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
+}
+
+// Plain scoring of one prefill stage on bf16 rows (the matrix-core kernel for
+// query blocks of 64, else the generic one).
+void launch_score_prefill_bf16(const PruneArgs& a, int stage, int max_chunks, hipStream_t st, const char* name) {
+  if (max_chunks <= 0 || launch_score_prefill_mfma(a, stage, max_chunks, st, name)) return;
+  const dim3 grid((max_chunks + 15) / 16, a.R);
+  if (a.kv.D == 128) DSA_LAUNCH(name, (k_score_prefill<uint16_t, 128>), grid, dim3(256), st, a, stage);
+  else               DSA_LAUNCH(name, (k_score_prefill<uint16_t, 64>), grid, dim3(256), st, a, stage);
 }
 
 hipError_t launch_prune(const PruneArgs& a, int dtype, hipStream_t st) {

@@ -14,11 +14,24 @@
 // next split's left representative with its left score already at hand. A
 // chunk's score is the one its representative won its last split with.
 // The stage's top-K and the index row are those of the plain pruning.
+//
+// Chunk-indexed RoPE (same section, Chunk-indexed): within a stage of chunk
+// length l a key sits at its chunk's index (position - n_sink) / l and every
+// query n_stream after the stage's last chunk (capped at the query's own
+// position); queries and keys are each rotated in fp64 and rounded to the
+// 1/128 grid, and the plain tournaments run on the rotated rows. The queries
+// are rotated once per stage; prefill rotates the keys once per stage into a
+// bf16 copy that the plain scoring kernels read, decode rotates each row it
+// evaluates in registers (the partner half of every pair comes from lane
+// li ^ 8 of the lane group).
 #include "prune_common.h"
+#include "selectrep.h"
 
 namespace dsa {
 
 constexpr int kRopeQuant = 128;
+constexpr int kRopeRelative = 1;        // the ABI's rope styles
+constexpr int kRopeChunkIndexed = 2;
 
 // cos and sin of the angle pos * theta_i (fp64)
 __device__ __forceinline__ void rope_angle(double theta, double pos, double& c, double& s) {
@@ -340,8 +353,242 @@ __global__ void __launch_bounds__(256) k_score_rope(PruneArgs a, int stage, cons
   if (active && li == 0) stage_scores(a, stage, r)[j] = score_key(best);
 }
 
+// ------------------------------------------------------------------------- //
+// chunk-indexed RoPE                                                        //
+// ------------------------------------------------------------------------- //
+constexpr int kDppRowRor8 = 0x128;      // lane i <- lane (i + 8) mod 16 of its row
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_perm_d(double v) {
+  const uint64_t u = __double_as_longlong(v);
+  const uint32_t lo = static_cast<uint32_t>(dpp_perm<CTRL>(static_cast<int>(static_cast<uint32_t>(u))));
+  const uint32_t hi = static_cast<uint32_t>(dpp_perm<CTRL>(static_cast<int>(static_cast<uint32_t>(u >> 32))));
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+__device__ __forceinline__ double rope_theta(double base, int i, int d) { return pow(base, (-2.0 * i) / d); }
+
+// x * c + p * ss with ss = -s for the first half of a pair (x1 c - x2 s) and
+// +s for the second (x2 c + x1 s), rounded to the 1/128 grid
+__device__ __forceinline__ float rope_half(double x, double p, double c, double ss) {
+#pragma clang fp contract(off)
+  const double y = x * c + p * ss;
+  return static_cast<float>(rint(y * kRopeQuant) / kRopeQuant);
+}
+
+// Query ID of a stage: n_stream after the last chunk of the stage's tiling of
+// the middle [n_sink, mid_hi).
+__device__ __forceinline__ int ci_query_id(const PruneArgs& a, int stage, const Geo& geo) {
+  return ((geo.mid_hi - a.n_sink) >> a.lchunk[stage]) - 1 + a.n_window;
+}
+
+// Rotated queries of one stage, in the layout of q (bf16): workgroup = (row,
+// head); the angles of the stage's query ID are tabled once, a query capped
+// at its own position computes its own.
+template <typename T, int D>
+__global__ void __launch_bounds__(256) k_ci_queries(PruneArgs a, int stage, uint16_t* qo, double base) {
+  constexpr int half = D / 2;
+  __shared__ double cs[half][2];
+  const KvLayout& kv = a.kv;
+  const int r = blockIdx.x, h = blockIdx.y;
+  int b, s, e;
+  row_bounds(kv, r, b, s, e);
+  const Geo geo = make_geo(s, e, a.n_sink, a.n_window, a.chunk[0]);
+  const int qid = ci_query_id(a, stage, geo);
+  for (int i = threadIdx.x; i < half; i += blockDim.x) rope_angle(rope_theta(base, i, D), qid, cs[i][0], cs[i][1]);
+  __syncthreads();
+  const int bq = kv.bq;
+  const T* Q = static_cast<const T*>(a.q);
+  constexpr int QG = half / 4;
+  for (int x = threadIdx.x; x < bq * QG; x += blockDim.x) {
+    const int t = x / QG, i0 = (x - t * QG) * 4;
+    const size_t o = kv.decode ? (static_cast<size_t>(b) * kv.Hq + h) * D
+                               : ((static_cast<size_t>(b) * kv.Hq + h) * kv.T + s + t) * D;
+    float x1[4], x2[4];
+    SliceLoad<T, 4>::run(Q + o + i0, x1);
+    SliceLoad<T, 4>::run(Q + o + i0 + half, x2);
+    const int i_orig = kv.decode ? e - 1 : s + t;
+    uint32_t lo[2] = {0, 0}, hi[2] = {0, 0};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      double c = cs[i0 + k][0], sn = cs[i0 + k][1];
+      if (i_orig < qid) rope_angle(rope_theta(base, i0 + k, D), i_orig, c, sn);
+      float y1, y2;
+      rope_pair(x1[k], x2[k], c, sn, y1, y2);
+      lo[k >> 1] |= exact_bf16(y1) << (16 * (k & 1));
+      hi[k >> 1] |= exact_bf16(y2) << (16 * (k & 1));
+    }
+    *reinterpret_cast<uint2*>(qo + o + i0) = make_uint2(lo[0], lo[1]);
+    *reinterpret_cast<uint2*>(qo + o + i0 + half) = make_uint2(hi[0], hi[1]);
+  }
+}
+
+// Rotated keys of one prefill stage, in the layout of k (bf16): workgroup =
+// 32 positions of every (sequence, kv head); the angles of the (at most 33)
+// chunk indices the tile touches are tabled in LDS. Positions before n_sink
+// are never candidates and are left as they are.
+constexpr int kCiTile = 32;
+template <typename T, int D>
+__global__ void __launch_bounds__(256) k_ci_keys(PruneArgs a, int stage, uint16_t* ko, double base) {
+  constexpr int half = D / 2;
+  __shared__ double cs[kCiTile + 1][half][2];
+  const KvLayout& kv = a.kv;
+  const int p0 = max(blockIdx.x * kCiTile, a.n_sink);
+  const int p1 = min(static_cast<int>(blockIdx.x + 1) * kCiTile, kv.T);
+  if (p0 >= p1) return;
+  const int lc = a.lchunk[stage];
+  const int c0 = (p0 - a.n_sink) >> lc, nch = ((p1 - 1 - a.n_sink) >> lc) - c0 + 1;
+  for (int x = threadIdx.x; x < nch * half; x += blockDim.x) {
+    const int cc = x / half, i = x - cc * half;
+    rope_angle(rope_theta(base, i, D), static_cast<double>(c0 + cc), cs[cc][i][0], cs[cc][i][1]);
+  }
+  __syncthreads();
+  const T* K = static_cast<const T*>(a.k);
+  constexpr int QG = half / 4;
+  const int np = p1 - p0;
+  const int rows = kv.B * kv.Hkv;
+  for (int x = threadIdx.x; x < rows * np * QG; x += blockDim.x) {
+    const int i0 = (x % QG) * 4, rp = x / QG;
+    const int pos = p0 + rp % np, bg = rp / np;
+    const size_t o = (static_cast<size_t>(bg) * kv.T + pos) * D;
+    float x1[4], x2[4];
+    SliceLoad<T, 4>::run(K + o + i0, x1);
+    SliceLoad<T, 4>::run(K + o + i0 + half, x2);
+    const int cc = ((pos - a.n_sink) >> lc) - c0;
+    uint32_t lo[2] = {0, 0}, hi[2] = {0, 0};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float y1, y2;
+      rope_pair(x1[k], x2[k], cs[cc][i0 + k][0], cs[cc][i0 + k][1], y1, y2);
+      lo[k >> 1] |= exact_bf16(y1) << (16 * (k & 1));
+      hi[k >> 1] |= exact_bf16(y2) << (16 * (k & 1));
+    }
+    *reinterpret_cast<uint2*>(ko + o + i0) = make_uint2(lo[0], lo[1]);
+    *reinterpret_cast<uint2*>(ko + o + i0 + half) = make_uint2(hi[0], hi[1]);
+  }
+}
+
+// Key rows of one decode chunk rotated to the chunk's index: lane li holds
+// elements li*EPL .. of a row, so its pair partners sit in lane li ^ 8 (one
+// DPP rotation of the 16-lane row). The lane's EPL angles are computed once
+// per chunk, split between the two lanes of each pair (each takes EPL/2 and
+// receives the other half), from the workgroup's table of theta_i. The
+// rotation runs in fp64 as in the oracle. (An fp32 evaluation with an fp64
+// re-evaluation of the elements near a rounding half-step was slower: the
+// re-evaluation reaches about one row in eight per wave.)
+template <typename T, int D, bool PAGED>
+struct CiRows {
+  static constexpr int EPL = D / 16;
+  ChunkRows<T, D, PAGED> raw;
+  double c[EPL], ss[EPL];                       // cos, and sin signed for this lane's half
+
+  __device__ __forceinline__ CiRows(const PruneArgs& a, int stage, int b, int g, int li, int st, const double* theta)
+      : raw(a, b, g, li, st, a.chunk[stage]) {
+    const double cid = static_cast<double>((st - a.n_sink) >> a.lchunk[stage]);
+    const bool first = li < 8;
+    const int k0 = first ? 0 : EPL / 2;         // the half of the angles computed here
+    double mc[EPL / 2], ms[EPL / 2];
+#pragma unroll
+    for (int k = 0; k < EPL / 2; ++k) rope_angle(theta[(li & 7) * EPL + k0 + k], cid, mc[k], ms[k]);
+#pragma unroll
+    for (int k = 0; k < EPL / 2; ++k) {
+      const double oc = dpp_perm_d<kDppRowRor8>(mc[k]), os = dpp_perm_d<kDppRowRor8>(ms[k]);
+      const double c_lo = first ? mc[k] : oc, s_lo = first ? ms[k] : os;     // angle k
+      const double c_hi = first ? oc : mc[k], s_hi = first ? os : ms[k];     // angle EPL/2 + k
+      c[k] = c_lo;
+      ss[k] = first ? -s_lo : s_lo;
+      c[EPL / 2 + k] = c_hi;
+      ss[EPL / 2 + k] = first ? -s_hi : s_hi;
+    }
+  }
+
+  __device__ __forceinline__ RowSlice<T, EPL> at(int pos) const {
+    RowSlice<T, EPL> x = raw.at(pos), y;
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int w = 0; w < EPL / 2; ++w) {
+        const uint32_t mine = x.w[w];
+        const uint32_t other = static_cast<uint32_t>(dpp_perm<kDppRowRor8>(static_cast<int>(mine)));
+        const float a0 = rope_half(__uint_as_float(mine << 16), __uint_as_float(other << 16), c[2 * w], ss[2 * w]);
+        const float a1 = rope_half(__uint_as_float(mine & 0xffff0000u), __uint_as_float(other & 0xffff0000u),
+                                   c[2 * w + 1], ss[2 * w + 1]);
+        y.w[w] = exact_bf16(a0) | (exact_bf16(a1) << 16);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) {
+        const float other = dpp_perm_f<kDppRowRor8>(x.v[k]);
+        y.v[k] = rope_half(x.v[k], other, c[k], ss[k]);
+      }
+    }
+    return y;
+  }
+};
+
+// Decode scoring of one stage with chunk-indexed RoPE: the plain lane-group
+// tournaments on rotated rows, against the stage's rotated queries.
+template <typename T, int D, int G, int SPEC, bool PAGED>
+__global__ void __launch_bounds__(256, (G > 4 || (G == 4 && sizeof(T) == 4)) ? 2 : 4)
+k_score_decode_ci(PruneArgs a, int stage, const uint16_t* q_all, double base) {
+  constexpr int EPL = D / 16;
+  using Row = RowSlice<T, EPL>;
+  __shared__ double theta[D / 2];
+  for (int i = threadIdx.x; i < D / 2; i += blockDim.x) theta[i] = rope_theta(base, i, D);
+  __syncthreads();
+  const KvLayout& kv = a.kv;
+  const int r = blockIdx.y, b = r;
+  const int cpw = 16 / kv.Hkv;
+  const int j0 = blockIdx.x * cpw;
+  const int tid = threadIdx.x;
+  const int gi = tid >> 4, li = tid & 15;
+  const int cl = gi / kv.Hkv, g = gi - cl * kv.Hkv;
+  const int j = j0 + cl;
+  __shared__ float red[16];
+
+  const int e = kv.seq_lens[r];
+  int nc_prev = 0, st;
+  if (stage == 0) {
+    st = a.n_sink + (j << a.lchunk[0]);
+  } else {
+    const int sh = a.lchunk[stage - 1] - a.lchunk[stage];
+    nc_prev = a.cnt[r * kMaxStages + stage - 1];
+    const int32_t* prev = stage_starts(a, stage - 1, r);
+    st = prev[min(j >> sh, a.maxK - 1)] + ((j & ((1 << sh) - 1)) << a.lchunk[stage]);
+  }
+  Row q[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh)
+    load_rotated(q[hh], q_all + (static_cast<size_t>(r) * kv.Hq + g * G + hh) * D + li * EPL);
+
+  const Geo geo = make_geo(e - 1, e, a.n_sink, a.n_window, a.chunk[0]);
+  const int nc = stage == 0 ? geo.n1 : nc_prev << (a.lchunk[stage - 1] - a.lchunk[stage]);
+  if (nc <= (a.keep[stage] >> a.lchunk[stage])) return;   // stage keeps everything for this row
+  if (j0 >= nc) return;
+  const bool active = j < nc;
+
+  float best = -INFINITY;
+  if (active) {
+    const CiRows<T, D, PAGED> rows(a, stage, b, g, li, st, theta);
+    best = selectrep_group<T, D, G, SPEC>(a, stage, li, st, rows, q);
+  }
+  if (li == 0) red[gi] = best;
+  __syncthreads();
+  if (tid < cpw) {
+    const int jj = j0 + tid;
+    if (jj < nc) {
+      float m = red[tid * kv.Hkv];
+      for (int x = 1; x < kv.Hkv; ++x) m = fmaxf(m, red[tid * kv.Hkv + x]);
+      stage_scores(a, stage, r)[jj] = score_key(m);
+    }
+  }
+}
+
 static const char* const kRopeNames[kMaxStages] = {"prune_rope_score1", "prune_rope_score2", "prune_rope_score3",
                                                    "prune_rope_score4"};
+static const char* const kCiQueryNames[kMaxStages] = {"prune_ci_queries1", "prune_ci_queries2", "prune_ci_queries3",
+                                                      "prune_ci_queries4"};
+static const char* const kCiKeyNames[kMaxStages] = {"prune_ci_keys1", "prune_ci_keys2", "prune_ci_keys3",
+                                                    "prune_ci_keys4"};
 
 // Speculative first round of a decode tournament: 8 keys for chunks of 8..64,
 // 4 for longer chunks (register budget), none below 8.
@@ -367,27 +614,69 @@ static void launch_decode_rt_g(const PruneArgs& a, int stage, int max_chunks, co
   else                  launch_decode_rt<T, D, G, false>(a, stage, max_chunks, ql, qr, st);
 }
 
-// Rotation, then per stage: scoring (decode: lane-group tournaments; bf16
-// prefill with 64-query blocks: the matrix-core tournaments; otherwise the
-// generic kernel) and the plain top-K.
+template <typename T, int D, int G, bool PAGED>
+static void launch_decode_ci(const PruneArgs& a, int stage, int max_chunks, const uint16_t* q, double base,
+                             hipStream_t st) {
+  const int cpw = 16 / a.kv.Hkv;
+  const dim3 grid((max_chunks + cpw - 1) / cpw, a.R);
+  const char* nm = kRopeNames[stage];
+  switch (rope_spec(a.chunk[stage])) {
+    case 8:  DSA_LAUNCH(nm, (k_score_decode_ci<T, D, G, 8, PAGED>), grid, dim3(256), st, a, stage, q, base); break;
+    case 4:  DSA_LAUNCH(nm, (k_score_decode_ci<T, D, G, 4, PAGED>), grid, dim3(256), st, a, stage, q, base); break;
+    default: DSA_LAUNCH(nm, (k_score_decode_ci<T, D, G, 0, PAGED>), grid, dim3(256), st, a, stage, q, base); break;
+  }
+}
+
+template <typename T, int D, int G>
+static void launch_decode_ci_g(const PruneArgs& a, int stage, int max_chunks, const uint16_t* q, double base,
+                               hipStream_t st) {
+  if (a.kv.block_table) launch_decode_ci<T, D, G, true>(a, stage, max_chunks, q, base, st);
+  else                  launch_decode_ci<T, D, G, false>(a, stage, max_chunks, q, base, st);
+}
+
+// Relative style: rotation once, then per stage the scoring (decode:
+// lane-group tournaments; bf16 prefill with 64-query blocks: the matrix-core
+// tournaments; otherwise the generic kernel) and the plain top-K.
+// Chunk-indexed style: per stage the queries (and, in prefill, the keys) are
+// rotated to the stage's position IDs, scored by the plain tournaments
+// (decode: on rows rotated in registers), and the plain top-K follows.
 template <typename T, int D>
-static hipError_t launch_rope_typed(const PruneArgs& a, uint16_t* ql, uint16_t* qr, double base, hipStream_t st) {
-  DSA_LAUNCH("prune_rope_queries", (k_rope_queries<T, D>), dim3(a.R, a.kv.Hq), dim3(256), st, a, ql, qr, base);
+static hipError_t launch_rope_typed(const PruneArgs& a, int style, uint16_t* qa, uint16_t* qb, uint16_t* kb,
+                                    double base, hipStream_t st) {
+  const bool rt = style == kRopeRelative;
+  if (rt) DSA_LAUNCH("prune_rope_queries", (k_rope_queries<T, D>), dim3(a.R, a.kv.Hq), dim3(256), st, a, qa, qb, base);
   const int G = a.kv.Hq / a.kv.Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return hipErrorInvalidValue;
   for (int stage = 0; stage < a.n_stages; ++stage) {
     const int max_chunks = stage == 0 ? a.n1max : a.keep[stage - 1] / a.chunk[stage];
-    if (max_chunks > 0) {
+    if (max_chunks > 0 && rt) {
       if (a.kv.decode) {
         switch (G) {
-          case 1: launch_decode_rt_g<T, D, 1>(a, stage, max_chunks, ql, qr, st); break;
-          case 2: launch_decode_rt_g<T, D, 2>(a, stage, max_chunks, ql, qr, st); break;
-          case 4: launch_decode_rt_g<T, D, 4>(a, stage, max_chunks, ql, qr, st); break;
-          case 8: launch_decode_rt_g<T, D, 8>(a, stage, max_chunks, ql, qr, st); break;
-          default: return hipErrorInvalidValue;
+          case 1: launch_decode_rt_g<T, D, 1>(a, stage, max_chunks, qa, qb, st); break;
+          case 2: launch_decode_rt_g<T, D, 2>(a, stage, max_chunks, qa, qb, st); break;
+          case 4: launch_decode_rt_g<T, D, 4>(a, stage, max_chunks, qa, qb, st); break;
+          default: launch_decode_rt_g<T, D, 8>(a, stage, max_chunks, qa, qb, st); break;
         }
-      } else if (!(sizeof(T) == 2 && launch_score_prefill_mfma(a, stage, max_chunks, st, kRopeNames[stage], ql, qr))) {
+      } else if (!(sizeof(T) == 2 && launch_score_prefill_mfma(a, stage, max_chunks, st, kRopeNames[stage], qa, qb))) {
         DSA_LAUNCH(kRopeNames[stage], (k_score_rope<T, D>), dim3((max_chunks + 15) / 16, a.R), dim3(256), st, a,
-                   stage, ql, qr);
+                   stage, qa, qb);
+      }
+    } else if (max_chunks > 0) {
+      DSA_LAUNCH(kCiQueryNames[stage], (k_ci_queries<T, D>), dim3(a.R, a.kv.Hq), dim3(256), st, a, stage, qa, base);
+      if (a.kv.decode) {
+        switch (G) {
+          case 1: launch_decode_ci_g<T, D, 1>(a, stage, max_chunks, qa, base, st); break;
+          case 2: launch_decode_ci_g<T, D, 2>(a, stage, max_chunks, qa, base, st); break;
+          case 4: launch_decode_ci_g<T, D, 4>(a, stage, max_chunks, qa, base, st); break;
+          default: launch_decode_ci_g<T, D, 8>(a, stage, max_chunks, qa, base, st); break;
+        }
+      } else {
+        DSA_LAUNCH(kCiKeyNames[stage], (k_ci_keys<T, D>), dim3((a.kv.T + kCiTile - 1) / kCiTile), dim3(256), st, a,
+                   stage, kb, base);
+        PruneArgs ar = a;                       // the plain scoring, on the rotated copies
+        ar.q = qa;
+        ar.k = kb;
+        launch_score_prefill_bf16(ar, stage, max_chunks, st, kRopeNames[stage]);
       }
     }
     launch_topk(a, stage, max_chunks, st);
@@ -397,14 +686,15 @@ static hipError_t launch_rope_typed(const PruneArgs& a, uint16_t* ql, uint16_t* 
   return hipSuccess;
 }
 
-hipError_t launch_prune_rope(const PruneArgs& a, int dtype, uint16_t* ql, uint16_t* qr, double base,
-                             hipStream_t st) {
+hipError_t launch_prune_rope(const PruneArgs& a, int dtype, int style, uint16_t* qa, uint16_t* qb, uint16_t* kb,
+                             double base, hipStream_t st) {
+  if (style != kRopeRelative && style != kRopeChunkIndexed) return hipErrorInvalidValue;
   if (dtype == 1) {
-    if (a.kv.D == 128) return launch_rope_typed<uint16_t, 128>(a, ql, qr, base, st);
-    if (a.kv.D == 64) return launch_rope_typed<uint16_t, 64>(a, ql, qr, base, st);
+    if (a.kv.D == 128) return launch_rope_typed<uint16_t, 128>(a, style, qa, qb, kb, base, st);
+    if (a.kv.D == 64) return launch_rope_typed<uint16_t, 64>(a, style, qa, qb, kb, base, st);
   } else {
-    if (a.kv.D == 128) return launch_rope_typed<float, 128>(a, ql, qr, base, st);
-    if (a.kv.D == 64) return launch_rope_typed<float, 64>(a, ql, qr, base, st);
+    if (a.kv.D == 128) return launch_rope_typed<float, 128>(a, style, qa, qb, kb, base, st);
+    if (a.kv.D == 64) return launch_rope_typed<float, 64>(a, style, qa, qb, kb, base, st);
   }
   return hipErrorInvalidValue;
 }

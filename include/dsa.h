@@ -202,32 +202,48 @@ dsa_status dsa_sparse_attn(const dsa_shape* shape, const void* q, const void* k,
 dsa_status dsa_dense_attn(const dsa_shape* shape, const void* q, const void* k, const void* v,
                           float scale, float* out, void* ws, size_t ws_bytes, void* stream);
 
-/* ---- Relative RoPE inside SelectRep -------------------------------------
- * InfiniteHiP page, "Four RoPE Styles for Context Pruning" (Relative) and
- * "Layer-Specific Strategy Assignment": q and k are taken before any rotary
- * embedding; at every SelectRep split the left branch's representative is
- * scored as sitting n_stream + 1 positions behind the query and the right
- * branch's n_stream behind (n_stream = p->n_window), with the rotate-half
- * pairing and frequencies theta_i = base^(-2i/d). The rotation is applied to
- * the queries (equal, in exact arithmetic, to rotating the query to n_stream
- * + 1 and the keys to 0 and 1), computed in fp64 and rounded to multiples of
- * 1/128, so scores against grid-valued keys are exact. A representative that
- * wins from the right is scored again as the next split's left one; a chunk's
- * score is the score its representative won its last split with. Everything
- * else is dsa_prune_select (rows, top-K ties, sinks and window). */
-typedef enum { DSA_ROPE_RELATIVE = 1 } dsa_rope_style;
+/* ---- RoPE inside SelectRep ------------------------------------------------
+ * InfiniteHiP page, "Four RoPE Styles for Context Pruning" (Relative,
+ * Chunk-indexed) and "Layer-Specific Strategy Assignment": q and k are taken
+ * before any rotary embedding (rotate-half pairing, theta_i = base^(-2i/d),
+ * n_stream = p->n_window). Rotated vectors are computed in fp64 and rounded
+ * to multiples of 1/128, so scores between them and grid-valued vectors are
+ * exact. Everything else is dsa_prune_select (rows, top-K ties, sinks and
+ * window).
+ *
+ * DSA_ROPE_RELATIVE: at every SelectRep split the left branch's
+ * representative is scored as sitting n_stream + 1 positions behind the query
+ * and the right branch's n_stream behind. The rotation is applied to the
+ * queries (equal, in exact arithmetic, to rotating the query to n_stream + 1
+ * and the keys to 0 and 1). A representative that wins from the right is
+ * scored again as the next split's left one; a chunk's score is the score its
+ * representative won its last split with.
+ *
+ * DSA_ROPE_CHUNK_INDEXED: in a stage of chunk length l, a key at position j
+ * is rotated to its chunk's index (j - n_sink) / l, and every query to
+ * min(its position, c_last + n_stream), c_last = (mid_end - n_sink) / l - 1
+ * being the stage's last chunk of the middle (the query sits n_stream after
+ * it); the plain SelectRep, chunk score and top-K run on the rotated vectors.
+ * The page assigns this style to a model's first three layers and the
+ * relative one to the rest. */
+typedef enum { DSA_ROPE_RELATIVE = 1, DSA_ROPE_CHUNK_INDEXED = 2 } dsa_rope_style;
 
 typedef struct {
-  int32_t style;     /* DSA_ROPE_RELATIVE */
+  int32_t style;     /* DSA_ROPE_RELATIVE or DSA_ROPE_CHUNK_INDEXED */
   double base;       /* rotary base (e.g. 10000 or 500000), > 1 */
 } dsa_rope;
 
-/* Workspace bytes of dsa_prune_select_rope (the pruning workspace plus two
- * rotated copies of the queries in bf16). */
-dsa_status dsa_prune_rope_workspace_bytes(const dsa_shape* shape, const dsa_params* p, size_t* out_bytes);
+/* Workspace bytes of dsa_prune_select_rope for this rope style: the pruning
+ * workspace plus rotated copies in bf16 (relative: two of the queries;
+ * chunk-indexed: one of the queries, and in prefill one of the keys). */
+dsa_status dsa_prune_rope_workspace_bytes(const dsa_shape* shape, const dsa_params* p, const dsa_rope* rope,
+                                          size_t* out_bytes);
 
-/* Hierarchical pruning with relative-RoPE SelectRep; arguments and idx as for
- * dsa_prune_select (prefill or decode, contiguous or paged). */
+/* Hierarchical pruning with RoPE inside SelectRep; arguments and idx as for
+ * dsa_prune_select (prefill or decode, contiguous or paged). Returns
+ * DSA_ERR_UNSUPPORTED for an unknown style, DSA_ERR_INVALID_ARG for a base
+ * that is not a finite value > 1, DSA_ERR_WORKSPACE when ws_bytes is below
+ * dsa_prune_rope_workspace_bytes. */
 dsa_status dsa_prune_select_rope(const dsa_shape* shape, const void* q, const void* k, const dsa_params* p,
                                  const dsa_rope* rope, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 

@@ -213,15 +213,26 @@ def test_vertical_slash_sizes_and_rejections():
 def test_prune_rope_sizes_and_rejections():
     s = Shape(DSA_PREFILL, DSA_BF16, 1, 32, 8, 128, 4096)
     plain = _lib.workspace_bytes(s, P2)
+    qcopy = 32 * 4096 * 128 * 2
     rope = _lib.prune_rope_workspace_bytes(s, P2)
-    assert rope >= plain and rope - plain >= 2 * 32 * 4096 * 128 * 2 - 4096      # two bf16 query copies
+    assert rope >= plain and rope - plain >= 2 * qcopy - 4096                  # two bf16 query copies
+    ci = _lib.prune_rope_workspace_bytes(s, P2, _lib.DSA_ROPE_CHUNK_INDEXED)
+    assert ci - plain >= qcopy + 8 * 4096 * 128 * 2 - 4096 and ci - plain < 2 * qcopy + 8 * 4096 * 256  # + keys
     d = Shape(DSA_DECODE, DSA_BF16, 1, 32, 8, 128, 1 << 20, seq_lens=16)
     assert _lib.prune_rope_workspace_bytes(d, P3) >= 2 * 32 * 128 * 2
-    for base, style, code in [(10000.0, 2, DSA_ERR_UNSUPPORTED), (1.0, 1, DSA_ERR_INVALID_ARG),
-                              (float("inf"), 1, DSA_ERR_INVALID_ARG)]:
+    ci_d = _lib.prune_rope_workspace_bytes(d, P3, _lib.DSA_ROPE_CHUNK_INDEXED)        # decode copies no keys
+    assert ci_d - _lib.workspace_bytes(d, P3) < 1 << 20
+    for base, style, code in [(10000.0, 3, DSA_ERR_UNSUPPORTED), (1.0, 1, DSA_ERR_INVALID_ARG),
+                              (float("inf"), 2, DSA_ERR_INVALID_ARG)]:
         with pytest.raises(_lib.DsaError) as ei:
-            _lib.prune_select_rope_raw(s, 256, 256, P2, base, 256, 256, rope, style=style)
+            _lib.prune_select_rope_raw(s, 256, 256, P2, base, 256, 256, ci, style=style)
         assert ei.value.status == code
     with pytest.raises(_lib.DsaError) as ei:
+        _lib.prune_rope_workspace_bytes(s, P2, 0)
+    assert ei.value.status == DSA_ERR_UNSUPPORTED
+    with pytest.raises(_lib.DsaError) as ei:
         _lib.prune_select_rope_raw(s, 256, 256, P2, 10000.0, 256, 256, plain)
+    assert ei.value.status == DSA_ERR_WORKSPACE
+    with pytest.raises(_lib.DsaError) as ei:
+        _lib.prune_select_rope_raw(s, 256, 256, P2, 10000.0, 256, 256, ci - 1, style=_lib.DSA_ROPE_CHUNK_INDEXED)
     assert ei.value.status == DSA_ERR_WORKSPACE

@@ -1,8 +1,8 @@
-"""GPU parity of pruning with relative RoPE in SelectRep (InfiniteHiP page,
-"Four RoPE Styles for Context Pruning", Relative): dsa_prune_select_rope
-through the C ABI against the CPU oracle. The rotated queries are rounded to
-multiples of 1/128, so every SelectRep score against the grid-valued keys is
-exact on both sides and the index rows are compared bit-exactly."""
+"""GPU parity of pruning with RoPE inside SelectRep (InfiniteHiP page, "Four
+RoPE Styles for Context Pruning": Relative and Chunk-indexed):
+dsa_prune_select_rope through the C ABI against the CPU oracle. Rotated
+vectors are rounded to multiples of 1/128, so every SelectRep score is exact
+on both sides and the index rows are compared bit-exactly."""
 import numpy as np
 import pytest
 import torch
@@ -25,58 +25,65 @@ def _gpu():
     _lib.load()
 
 
-def oracle_row_rt(case, b, m, qi=0):
+STYLES = ["relative", "chunk_indexed"]
+
+
+def oracle_row_rt(case, b, m, qi=0, style="relative"):
     cfg = case.cfg
     p = H.oracle_params(cfg)
     if cfg.mode == "prefill":
         Q, s, e = H.prefill_block(case, b, m)
     else:
         Q, s, e = H.decode_query(case, b, qi)
-    return ref.pad_row(ref.prune_block_rt(Q, case.k[b], s, e, p, BASE), ref.index_width(p))
+    prune = ref.prune_block_rt if style == "relative" else ref.prune_block_ci
+    return ref.pad_row(prune(Q, case.k[b], s, e, p, BASE), ref.index_width(p))
 
 
-def test_rope_prefill_fp32_full():
+@pytest.mark.parametrize("style", STYLES)
+def test_rope_prefill_fp32_full(style):
     """The tiny fp32 workload: every block's row; RoPE changes some rows."""
     case = gen.make_case("c1")
-    H.say("rope c1: all 128 rows")
+    H.say(f"rope {style} c1: all 128 rows")
     dev = to_device(case)
     p = params_of(case.cfg)
-    idx = api.prune_select_rope(dev.q, dev.k, p, BASE).cpu().numpy()
+    idx = api.prune_select_rope(dev.q, dev.k, p, BASE, style=style).cpu().numpy()
     plain = api.prune_select(dev.q, dev.k, p).cpu().numpy()
     for m in range(case.cfg.t // case.cfg.block_q):
-        want = oracle_row_rt(case, 0, m)
+        want = oracle_row_rt(case, 0, m, style=style)
         assert np.array_equal(idx[0, m], want), f"block {m}: first diff {np.flatnonzero(idx[0, m] != want)[:5]}"
     changed = int((idx != plain).any(axis=-1).sum())
-    H.say(f"rope c1: {changed} of {idx.shape[1]} rows differ from plain SelectRep")
+    H.say(f"rope {style} c1: {changed} of {idx.shape[1]} rows differ from plain SelectRep")
     assert changed > 0
 
 
-def test_rope_prefill_llama_heads_4k():
+@pytest.mark.parametrize("style", STYLES)
+def test_rope_prefill_llama_heads_4k(style):
     """32 q / 8 kv heads, d = 128, bf16, three stages at T = 4096: 20 blocks."""
     case = gen.make_case("c2", t=4096, keep=(1024, 512, 256), n_window=256, n_needles=2)
-    H.say("rope c2 4K: sampled rows")
+    H.say(f"rope {style} c2 4K: sampled rows")
     dev = to_device(case)
-    idx = api.prune_select_rope(dev.q, dev.k, params_of(case.cfg), BASE).cpu().numpy()
+    idx = api.prune_select_rope(dev.q, dev.k, params_of(case.cfg), BASE, style=style).cpu().numpy()
     for m in gen.sample_blocks(64, 18, 5):
-        want = oracle_row_rt(case, 0, m)
+        want = oracle_row_rt(case, 0, m, style=style)
         assert np.array_equal(idx[0, m], want), f"block {m}: first diff {np.flatnonzero(idx[0, m] != want)[:5]}"
 
 
+@pytest.mark.parametrize("style", STYLES)
 @pytest.mark.parametrize("paged", [False, True])
-def test_rope_decode(paged):
+def test_rope_decode(paged, style):
     """Decode with relative-RoPE SelectRep: a 64K-token sequence (contiguous)
     and a ragged batch of 3 over a paged pool."""
     if paged:
         case = gen.make_case("c4", batch=3, ragged=(20000, 70000), t=70000)
     else:
         case = gen.make_case("c3", t=65536, n_queries=1)
-    H.say(f"rope decode paged={paged}")
+    H.say(f"rope {style} decode paged={paged}")
     dev = to_device(case)
     q = dev.q[0].contiguous()
     idx = api.prune_select_rope(q, dev.k, params_of(case.cfg), BASE, seq_lens=dev.seq_lens,
-                                block_table=dev.block_table, t=dev.t).cpu().numpy()
+                                block_table=dev.block_table, t=dev.t, style=style).cpu().numpy()
     for b in range(case.cfg.batch):
-        want = oracle_row_rt(case, b, 0)
+        want = oracle_row_rt(case, b, 0, style=style)
         assert np.array_equal(idx[b], want), f"sequence {b}: first diff {np.flatnonzero(idx[b] != want)[:5]}"
 
 
@@ -85,19 +92,20 @@ def test_rope_decode(paged):
     ("bf16", 16, 2, 128, (128, 16, 2), (2048, 512, 64), True),   # groups of 8; 2-key chunks take no first round
     ("bf16", 8, 4, 64, (32, 8, 4), (1024, 256, 64), False),      # groups of 2 at d = 64
 ])
-def test_rope_decode_shapes(dtype, hq, hkv, d, chunk, keep, paged):
+@pytest.mark.parametrize("style", STYLES)
+def test_rope_decode_shapes(dtype, hq, hkv, d, chunk, keep, paged, style):
     """Decode tournaments across group sizes, head dims, key types and chunk
     lengths (every first-round form: 4 and 8 keys, none, single keys)."""
     kw = dict(batch=2, ragged=(9000, 16384), page_size=64) if paged else dict(batch=1)
     case = gen.make_case("c4" if paged else "c3", hq=hq, hkv=hkv, d=d, t=16384, dtype=dtype, chunk=chunk,
                          keep=keep, n_queries=1, **kw)
-    H.say(f"rope decode {dtype} {hq}/{hkv} d={d} chunk={chunk} paged={paged}")
+    H.say(f"rope {style} decode {dtype} {hq}/{hkv} d={d} chunk={chunk} paged={paged}")
     dev = to_device(case)
     q = dev.q[0].contiguous()
     idx = api.prune_select_rope(q, dev.k, params_of(case.cfg), BASE, seq_lens=dev.seq_lens,
-                                block_table=dev.block_table, t=dev.t).cpu().numpy()
+                                block_table=dev.block_table, t=dev.t, style=style).cpu().numpy()
     for b in range(case.cfg.batch):
-        want = oracle_row_rt(case, b, 0)
+        want = oracle_row_rt(case, b, 0, style=style)
         assert np.array_equal(idx[b], want), f"sequence {b}: first diff {np.flatnonzero(idx[b] != want)[:5]}"
 
 
@@ -105,14 +113,15 @@ def test_rope_decode_shapes(dtype, hq, hkv, d, chunk, keep, paged):
     (8, 1, 64, (32, 8, 1), (512, 256, 64)),      # matrix-core tournaments at d = 64, group of 8, single keys
     (4, 2, 128, (16, 2), (512, 128)),            # 2-key chunks
 ])
-def test_rope_prefill_shapes(hq, hkv, d, chunk, keep):
+@pytest.mark.parametrize("style", STYLES)
+def test_rope_prefill_shapes(hq, hkv, d, chunk, keep, style):
     """bf16 prefill (the matrix-core tournaments) across head layouts and
     chunk lengths: every block's row."""
     case = gen.make_case("c2", hq=hq, hkv=hkv, d=d, t=2048, chunk=chunk, keep=keep, n_window=64,
                          n_sink=64, n_needles=0, structure="plain")
-    H.say(f"rope prefill {hq}/{hkv} d={d} chunk={chunk}")
+    H.say(f"rope {style} prefill {hq}/{hkv} d={d} chunk={chunk}")
     dev = to_device(case)
-    idx = api.prune_select_rope(dev.q, dev.k, params_of(case.cfg), BASE).cpu().numpy()
+    idx = api.prune_select_rope(dev.q, dev.k, params_of(case.cfg), BASE, style=style).cpu().numpy()
     for m in range(case.cfg.t // case.cfg.block_q):
-        want = oracle_row_rt(case, 0, m)
+        want = oracle_row_rt(case, 0, m, style=style)
         assert np.array_equal(idx[0, m], want), f"block {m}: first diff {np.flatnonzero(idx[0, m] != want)[:5]}"
