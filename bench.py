@@ -85,7 +85,7 @@ def parse():
     ap.add_argument("--no-other", action="store_true", help="skip the batch-32 paged and 3M-token decodes")
     ap.add_argument("--no-block-sparse", action="store_true", help="skip the block-sparse heads prefill")
     ap.add_argument("--no-vertical-slash", action="store_true", help="skip the vertical-slash heads prefill")
-    ap.add_argument("--no-rope", action="store_true", help="skip pruning with relative RoPE in SelectRep")
+    ap.add_argument("--no-rope", action="store_true", help="skip pruning with RoPE in SelectRep (both styles)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-ref", action="store_true",
@@ -477,25 +477,28 @@ def prefill_bench(args, res):
                           kernels_ms={k: round(v[1] / v[0], 3) for k, v in prof.items()})
     log(f"prefill 128K: {ms:.1f} ms, {res['prefill']['tflops']:.1f} TFLOP/s")
     if not args.no_rope:
-        idx_rt = api.prune_select_rope(dev.q, dev.k, p, ROPE_BASE)
-        api.sparse_attn(dev.q, dev.k, dev.v, idx_rt, p, out=out)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(reps):
-            api.prune_select_rope(dev.q, dev.k, p, ROPE_BASE, out=idx_rt.view(-1))
+        res["rope_prefill"] = {}
+        for style in ROPE_STYLES:
+            idx_rt = api.prune_select_rope(dev.q, dev.k, p, ROPE_BASE, style=style)
             api.sparse_attn(dev.q, dev.k, dev.v, idx_rt, p, out=out)
-        e1.record()
-        torch.cuda.synchronize()
-        ms_rt = e0.elapsed_time(e1) / reps
-        _lib.profile_begin()
-        api.prune_select_rope(dev.q, dev.k, p, ROPE_BASE, out=idx_rt.view(-1))
-        prof_rt = _lib.profile_end()
-        res["rope_prefill"] = dict(ms=ms_rt, prune_ms=sum(v[1] for v in prof_rt.values()), plain_ms=ms,
-                                   plain_prune_ms=prune_ms,
-                                   rows_changed=float((idx_rt != idx).any(-1).float().mean().item()),
-                                   kernels_ms={k: round(v[1] / v[0], 3) for k, v in prof_rt.items()})
-        log(f"prefill 128K with relative RoPE: {ms_rt:.1f} ms (pruning {res['rope_prefill']['prune_ms']:.1f} ms)")
-        del idx_rt
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                api.prune_select_rope(dev.q, dev.k, p, ROPE_BASE, out=idx_rt.view(-1), style=style)
+                api.sparse_attn(dev.q, dev.k, dev.v, idx_rt, p, out=out)
+            e1.record()
+            torch.cuda.synchronize()
+            ms_rt = e0.elapsed_time(e1) / reps
+            _lib.profile_begin()
+            api.prune_select_rope(dev.q, dev.k, p, ROPE_BASE, out=idx_rt.view(-1), style=style)
+            prof_rt = _lib.profile_end()
+            res["rope_prefill"][style] = dict(
+                ms=ms_rt, prune_ms=sum(v[1] for v in prof_rt.values()), plain_ms=ms, plain_prune_ms=prune_ms,
+                rows_changed=float((idx_rt != idx).any(-1).float().mean().item()),
+                kernels_ms={k: round(v[1] / v[0], 3) for k, v in prof_rt.items()})
+            log(f"prefill 128K with {style} RoPE: {ms_rt:.1f} ms "
+                f"(pruning {res['rope_prefill'][style]['prune_ms']:.1f} ms)")
+            del idx_rt
     del dev, idx, out
     torch.cuda.empty_cache()
 
@@ -677,12 +680,13 @@ def other_decode(args, name, reps=20):
 # relative RoPE in SelectRep at the 1M decode shape                           #
 # --------------------------------------------------------------------------- #
 ROPE_BASE = 500000.0       # the rotary base of the Llama-3 shape
+ROPE_STYLES = ("relative", "chunk_indexed")
 
 
 def rope_decode(args, reps=20):
     """Graph-replayed 1M-token decode step (pruning + attention) with plain
-    and with relative-RoPE SelectRep on the same inputs: microseconds per
-    step of each."""
+    SelectRep and with each RoPE style inside it, on the same inputs:
+    microseconds per step of each."""
     import torch
     from dynamic_sparse_attention_query_amd import api, gen
     from dynamic_sparse_attention_query_amd.inputs import params_of, to_device
@@ -695,8 +699,11 @@ def rope_decode(args, reps=20):
     q = dev.q[0].contiguous()
     kw = dict(seq_lens=dev.seq_lens, block_table=dev.block_table, t=dev.t)
     res = {}
-    for name, prune in [("plain", lambda out=None: api.prune_select(q, dev.k, p, out=out, **kw)),
-                        ("rope", lambda out=None: api.prune_select_rope(q, dev.k, p, ROPE_BASE, out=out, **kw))]:
+    variants = [("plain", lambda out=None: api.prune_select(q, dev.k, p, out=out, **kw))]
+    for style in ROPE_STYLES:
+        variants.append((style, lambda out=None, style=style: api.prune_select_rope(q, dev.k, p, ROPE_BASE, out=out,
+                                                                                     style=style, **kw)))
+    for name, prune in variants:
         idx = prune()
         out = api.sparse_attn(q, dev.k, dev.v, idx, p, **kw)
         torch.cuda.synchronize()
@@ -715,13 +722,17 @@ def rope_decode(args, reps=20):
         res[name] = e0.elapsed_time(e1) * 1e3 / reps
         res[name + "_idx"] = idx.clone()
         del g, out, idx
-    changed = bool((res.pop("plain_idx") != res.pop("rope_idx")).any().item())
-    log(f"1M decode step: plain {res['plain']:.1f} us, relative RoPE {res['rope']:.1f} us")
+    plain_idx = res.pop("plain_idx")
+    out = {"plain_us": round(res["plain"], 2),
+           "note": "back-to-back graph replays of one step (same query, one KV copy)"}
+    for style in ROPE_STYLES:
+        out[style] = {"us": round(res[style], 2), "overhead": round(res[style] / res["plain"], 3),
+                      "index_row_changed": bool((res.pop(style + "_idx") != plain_idx).any().item())}
+    log("1M decode step: plain {:.1f} us, ".format(res["plain"]) +
+        ", ".join(f"{st} RoPE {res[st]:.1f} us" for st in ROPE_STYLES))
     del dev
     torch.cuda.empty_cache()
-    return {"plain_us": round(res["plain"], 2), "rope_us": round(res["rope"], 2),
-            "overhead": round(res["rope"] / res["plain"], 3), "index_row_changed": changed,
-            "note": "back-to-back graph replays of one step (same query, one KV copy)"}
+    return out
 
 
 # --------------------------------------------------------------------------- #
@@ -873,17 +884,17 @@ def main():
             "speedup_vs_dense": round(dense_ms / vs["ms"], 2) if dense_ms else None,
             "kernels_ms": vs["kernels_ms"]}
     if "rope_decode" in res or "rope_prefill" in res:
-        rt = {"rotary_base": ROPE_BASE, "style": "relative"}
+        rt = {"rotary_base": ROPE_BASE}
         if "rope_decode" in res:
             rt["decode_1m"] = res["rope_decode"]
-        if "rope_prefill" in res:
-            r = res["rope_prefill"]
-            rt["prefill_128k"] = {"ms": round(r["ms"], 2), "prune_ms": round(r["prune_ms"], 2),
-                                  "plain_ms": round(r["plain_ms"], 2), "plain_prune_ms": round(r["plain_prune_ms"], 2),
-                                  "prune_overhead": round(r["prune_ms"] / r["plain_prune_ms"], 3),
-                                  "rows_changed_fraction": round(r["rows_changed"], 4),
-                                  "kernels_ms": r["kernels_ms"]}
-        line["relative_rope_selectrep"] = rt
+        for style, r in res.get("rope_prefill", {}).items():
+            rt.setdefault("prefill_128k", {"plain_ms": round(r["plain_ms"], 2),
+                                           "plain_prune_ms": round(r["plain_prune_ms"], 2)})
+            rt["prefill_128k"][style] = {"ms": round(r["ms"], 2), "prune_ms": round(r["prune_ms"], 2),
+                                         "prune_overhead": round(r["prune_ms"] / r["plain_prune_ms"], 3),
+                                         "rows_changed_fraction": round(r["rows_changed"], 4),
+                                         "kernels_ms": r["kernels_ms"]}
+        line["rope_in_selectrep"] = rt
     if "cpu" in res:
         line["cpu_baseline"] = res["cpu"]
     print(json.dumps(line), flush=True)
