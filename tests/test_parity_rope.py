@@ -125,3 +125,22 @@ def test_rope_prefill_shapes(hq, hkv, d, chunk, keep, style):
     for m in range(case.cfg.t // case.cfg.block_q):
         want = oracle_row_rt(case, 0, m, style=style)
         assert np.array_equal(idx[0, m], want), f"block {m}: first diff {np.flatnonzero(idx[0, m] != want)[:5]}"
+
+
+def test_ci_query_ids_capped_at_own_position():
+    """Chunk-indexed RoPE with 4 sinks and single-key chunks in the last stage:
+    the stage's query ID passes most queries' own positions, so each of them
+    is rotated to its own position (the cap); every block's row."""
+    case = gen.make_case("c2", hq=4, hkv=2, d=64, t=1024, chunk=(16, 1), keep=(256, 32), n_window=64,
+                         n_sink=4, n_needles=0, structure="plain")
+    cfg = case.cfg
+    H.say("rope chunk_indexed prefill with capped query IDs")
+    p = H.oracle_params(cfg)
+    geo = ref.geometry(1024 - 64, 1024, p)
+    ids = ref.ci_query_positions(np.arange(1024 - 64, 1024), geo.mid_hi, p.n_sink, p.n_window, 1)
+    assert (ids < np.arange(1024 - 64, 1024)).sum() < 64 and (ids == np.arange(1024 - 64, 1024)).sum() > 32
+    dev = to_device(case)
+    idx = api.prune_select_rope(dev.q, dev.k, params_of(cfg), BASE, style="chunk_indexed").cpu().numpy()
+    for m in range(cfg.t // cfg.block_q):
+        want = oracle_row_rt(case, 0, m, style="chunk_indexed")
+        assert np.array_equal(idx[0, m], want), f"block {m}: first diff {np.flatnonzero(idx[0, m] != want)[:5]}"
