@@ -144,3 +144,33 @@ def test_ci_query_ids_capped_at_own_position():
     for m in range(cfg.t // cfg.block_q):
         want = oracle_row_rt(case, 0, m, style="chunk_indexed")
         assert np.array_equal(idx[0, m], want), f"block {m}: first diff {np.flatnonzero(idx[0, m] != want)[:5]}"
+
+
+@pytest.mark.parametrize("style", STYLES)
+def test_rope_decode_edge_lengths_and_budgets(style):
+    """Ragged contiguous decode batch with lengths below the sinks, inside
+    sinks + window, on a chunk-grid tail and long enough for all three stages;
+    then a zero budget (sinks and window only) and a budget above every length
+    (nothing pruned)."""
+    cfg = gen.Config("decode-edge", "decode", 6, 8, 2, 128, 9000, "bf16", 1,
+                     (64, 16, 4), (2048, 512, 128), 16, 64, seed=11, n_queries=1)
+    case = gen.make_case(cfg)
+    case.seq_lens[:] = [1, 7, 80, 300, 5000, 9000]
+    for b, L in enumerate(case.seq_lens):
+        case.k[b] = case.k[b].sub((slice(None), slice(0, int(L))))
+        case.v[b] = case.v[b].sub((slice(None), slice(0, int(L))))
+    for keep in ((2048, 512, 128), (0, 0, 0), (16384, 16384, 16384)):
+        case.cfg = cfg.replace(keep=keep)
+        H.say(f"rope {style} decode edge lengths, keep={keep}")
+        dev = to_device(case)
+        q = dev.q[0].contiguous()
+        idx = api.prune_select_rope(q, dev.k, params_of(case.cfg), BASE, seq_lens=dev.seq_lens,
+                                    block_table=dev.block_table, t=dev.t, style=style).cpu().numpy()
+        for b in range(cfg.batch):
+            want = oracle_row_rt(case, b, 0, style=style)
+            assert np.array_equal(idx[b], want), f"keep {keep} sequence {b}: first diff {np.flatnonzero(idx[b] != want)[:5]}"
+        if keep[0] == 0:
+            T = 9000
+            mid_hi = 16 + ((T - 64 - 16) // 64) * 64
+            row = idx[5]
+            assert np.array_equal(row[row >= 0], np.r_[np.arange(16), np.arange(mid_hi, T)])
