@@ -1,6 +1,8 @@
-// Hierarchical pruning whose SelectRep tournaments use relative RoPE
-// (InfiniteHiP page, 2502.08910, "Four RoPE Styles for Context Pruning":
-// Relative; "Layer-Specific Strategy Assignment"): at every split the left
+// Hierarchical pruning with RoPE inside the SelectRep tournaments
+// (InfiniteHiP page, 2502.08910, "Four RoPE Styles for Context Pruning" and
+// "Layer-Specific Strategy Assignment").
+//
+// Relative RoPE (the section's Relative style): at every split the left
 // branch's representative is scored as if it sat n_stream + 1 positions
 // behind the query and the right branch's as n_stream behind (n_stream = the
 // window), the right half winning only on a strictly greater score.
@@ -32,6 +34,9 @@ namespace dsa {
 constexpr int kRopeQuant = 128;
 constexpr int kRopeRelative = 1;        // the ABI's rope styles
 constexpr int kRopeChunkIndexed = 2;
+
+// theta_i = base^(-2i/d) (fp64)
+__device__ __forceinline__ double rope_theta(double base, int i, int d) { return pow(base, (-2.0 * i) / d); }
 
 // cos and sin of the angle pos * theta_i (fp64)
 __device__ __forceinline__ void rope_angle(double theta, double pos, double& c, double& s) {
@@ -69,8 +74,8 @@ __global__ void __launch_bounds__(256) k_rope_queries(PruneArgs a, uint16_t* ql,
   const T* Q = static_cast<const T*>(a.q);
   for (int x = threadIdx.x; x < 2 * half; x += blockDim.x) {
     const int side = x / half, i = x - side * half;
-    const double theta = pow(base, (-2.0 * i) / D);
-    rope_angle(theta, static_cast<double>(side ? a.n_window : a.n_window + 1), cs[side][i][0], cs[side][i][1]);
+    rope_angle(rope_theta(base, i, D), static_cast<double>(side ? a.n_window : a.n_window + 1), cs[side][i][0],
+               cs[side][i][1]);
   }
   __syncthreads();
   constexpr int QG = half / 4;                  // groups of 4 pairs per query
@@ -365,8 +370,6 @@ __device__ __forceinline__ double dpp_perm_d(double v) {
   const uint32_t hi = static_cast<uint32_t>(dpp_perm<CTRL>(static_cast<int>(static_cast<uint32_t>(u >> 32))));
   return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
 }
-
-__device__ __forceinline__ double rope_theta(double base, int i, int d) { return pow(base, (-2.0 * i) / d); }
 
 // x * c + p * ss with ss = -s for the first half of a pair (x1 c - x2 s) and
 // +s for the second (x2 c + x1 s), rounded to the 1/128 grid
