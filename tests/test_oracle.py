@@ -965,3 +965,27 @@ def test_ci_hand_example_two_stages():
     assert list(got) == want
     plain = ref.prune_block(Q, K, e - 1, e, p)
     assert list(plain[n_sink:n_sink + 8]) == list(range(n_sink, n_sink + 8))
+
+
+def test_streamed_active_count_follows_closed_form():
+    """The InfLLM page's test idea (stream 10,000 tokens, watch the number of
+    active keys), for this method: a decode row holds the sinks, min(M, k_N)
+    middle keys (M = the whole stage-1 chunks of the middle; the stages keep
+    k_1 >= ... >= k_N), the window, and the chunk-grid tail (the part of the
+    middle that does not fill a stage-1 chunk), which cycles through [0, l_1)
+    as tokens arrive; once M exceeds k_N the count is that constant plus the
+    tail."""
+    rng = np.random.default_rng(50)
+    d, T0, n = 8, 64, 10_000
+    p = ref.Params(1, (8, 2), (64, 16), 4, 32)
+    K = grid(rng, (1, T0 + n, d))
+    seen = set()
+    for e in range(T0 + 1, T0 + n + 1):
+        q = grid(rng, (1, 1, d))
+        row = ref.prune_block(q, K, e - 1, e, p)
+        rem = (e - p.n_window - p.n_sink) % p.chunk[0]
+        M = (e - p.n_window - p.n_sink) // p.chunk[0] * p.chunk[0]
+        assert len(row) == p.n_sink + min(M, p.keep[-1]) + p.n_window + rem, e
+        if M > p.keep[-1]:
+            seen.add(rem)
+    assert seen == set(range(p.chunk[0]))

@@ -184,6 +184,30 @@ def test_decode_small_edge_lengths():
         check_decode(case, dev, range(6), qi)
 
 
+def test_decode_streamed_lengths_active_count():
+    """The InfLLM page's streaming test idea on the GPU: one decode step for
+    each of 250 context lengths 40 + 41 i (i = 0..249, up to 10,249 tokens) in
+    one ragged batch; every row holds the sinks, min(M, k_N) middle keys, the
+    window and the chunk-grid tail (the closed form pinned on the oracle), and
+    sampled rows equal the oracle's."""
+    n = 250
+    cfg = gen.Config("decode-stream", "decode", n, 4, 1, 64, 40 + 41 * (n - 1), "bf16", 1,
+                     (8, 2), (64, 16), 4, 32, seed=13, n_queries=1)
+    case = gen.make_case(cfg)
+    case.seq_lens[:] = 40 + 41 * np.arange(n)
+    for b, L in enumerate(case.seq_lens):
+        case.k[b] = case.k[b].sub((slice(None), slice(0, int(L))))
+        case.v[b] = case.v[b].sub((slice(None), slice(0, int(L))))
+    dev = to_device(case)
+    idx, _, _ = check_decode(case, dev, [0, 1, 2, 17, 128, n - 1])
+    counts = (idx.cpu().numpy() >= 0).sum(axis=1)
+    e = case.seq_lens.astype(np.int64)
+    rem = (e - 32 - 4) % 8
+    M = (e - 32 - 4) // 8 * 8
+    assert np.array_equal(counts, 4 + np.minimum(M, 16) + 32 + rem)
+    assert len(set(rem[M > 16].tolist())) == 8                    # the tail takes every value
+
+
 def test_decode_zero_budget_and_full_budget():
     base = gen.Config("decode-budget", "decode", 2, 8, 2, 64, 3000, "bf16", 1,
                       (32, 8), (0, 0), 8, 64, seed=12, n_queries=1)
