@@ -26,44 +26,6 @@ namespace dsa {
 // ------------------------------------------------------------------------- //
 // top-K of one row + index assembly                                         //
 // ------------------------------------------------------------------------- //
-constexpr int kMaxKeptChunks = 8192;    // keep / chunk of any stage (validated by the API)
-
-// This thread's keys: chunks j0 .. j0+E-1 of row r's score list of `stage` (read within
-// the row for every j0 of the launch; the selection masks j >= nc).
-template <int E>
-__device__ __forceinline__ void load_keys(const PruneArgs& a, int stage, int r, int j0, uint32_t (&key)[E]) {
-  static_assert(E % 4 == 0, "keys are loaded four at a time");
-  const uint4* sc4 = reinterpret_cast<const uint4*>(stage_scores(a, stage, r));
-  const int nv = a.maxNC >> 2;
-#pragma unroll
-  for (int v = 0; v < E / 4; ++v) {
-    const uint4 u = sc4[min((j0 >> 2) + v, nv - 1)];
-    key[4 * v + 0] = u.x; key[4 * v + 1] = u.y; key[4 * v + 2] = u.z; key[4 * v + 3] = u.w;
-  }
-}
-
-// The kept starts of stage `stage` for row r (at most keep/chunk of them)
-// into LDS; published by the caller's next barrier.
-template <int NT = kTopkThreads>
-__device__ __forceinline__ void load_kept_starts(const PruneArgs& a, int stage, int r, int* sp) {
-  const int tid = threadIdx.x;
-  const int kmax = a.keep[stage] >> a.lchunk[stage];
-  const int32_t* src = stage_starts(a, stage, r);
-  for (int i0 = 0; i0 < kmax; i0 += 4 * NT) {
-    int v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * NT + tid;
-      v[u] = i < kmax ? src[i] : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * NT + tid;
-      if (i < kmax) sp[i] = v[u];
-    }
-  }
-}
-
 // The index row of row r is sinks [0, sink_hi), the n_sel kept chunks of l
 // keys (ascending), every position from win_lo (the end of the stage-1 middle
 // the kept chunks descend from) up to the newest key, then -1 padding; L is a

@@ -26,6 +26,8 @@
 // bf16 copy that the plain scoring kernels read, decode rotates each row it
 // evaluates in registers (the partner half of every pair comes from lane
 // li ^ 8 of the lane group).
+#include <algorithm>
+
 #include "prune_common.h"
 #include "selectrep.h"
 
@@ -586,10 +588,102 @@ k_score_decode_ci(PruneArgs a, int stage, const uint16_t* q_all, double base) {
   }
 }
 
+// ------------------------------------------------------------------------- //
+// decode: top-K of one stage fused with the RoPE scoring of the next        //
+// ------------------------------------------------------------------------- //
+// As k_topk_score_decode (bf16, contiguous K): every workgroup selects the
+// row's kept chunks of stage `stage - 1` itself (workgroup 0 also writes the
+// kept starts and their count), then scores its chunks of `stage` with the
+// tournaments of k_score_decode_rt (KIND relative: qa, qb the rotated query
+// sets) or k_score_decode_ci (KIND chunk-indexed: qa the stage's rotated
+// queries).
+template <int D, int G, int SPEC, int E, int KIND>
+__global__ void __launch_bounds__(256, 2)
+k_topk_score_decode_rope(PruneArgs a, int stage, const uint16_t* qa, const uint16_t* qb, double base) {
+  using T = uint16_t;
+  constexpr int EPL = D / 16;
+  using Row = RowSlice<T, EPL>;
+  __shared__ SelectLds<> L;
+  __shared__ int sprev[kMaxKeptChunks];
+  __shared__ int ssel[kMaxKeptChunks];
+  __shared__ float red[16];
+  __shared__ double theta[D / 2];
+  const KvLayout& kv = a.kv;
+  const int ps = stage - 1;                     // the stage selected here
+  const int r = blockIdx.y, b = r;              // one row per sequence
+  const int cpw = 16 / kv.Hkv;                  // chunks per workgroup
+  const int j0 = blockIdx.x * cpw;
+  const int tid = threadIdx.x;
+  const int gi = tid >> 4, li = tid & 15;
+  const int cl = gi / kv.Hkv, g = gi - cl * kv.Hkv;
+
+  const int e = kv.seq_lens[r];
+  const int nc_before = ps > 0 ? a.cnt[r * kMaxStages + ps - 1] : 0;
+  const int js = tid * E;
+  uint32_t key[E];
+  load_keys<E>(a, ps, r, js, key);
+  if (ps > 0) load_kept_starts(a, ps - 1, r, sprev);
+  Row qx[G], qy[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    const size_t o = (static_cast<size_t>(r) * kv.Hq + g * G + hh) * D + li * EPL;
+    load_rotated(qx[hh], qa + o);
+    if constexpr (KIND == kRopeRelative) load_rotated(qy[hh], qb + o);
+  }
+  if constexpr (KIND == kRopeChunkIndexed) {    // published by the selection's barriers
+    for (int i = tid; i < D / 2; i += blockDim.x) theta[i] = rope_theta(base, i, D);
+  }
+
+  const Geo geo = make_geo(e - 1, e, a.n_sink, a.n_window, a.chunk[0]);
+  const int lgp = a.lchunk[ps];
+  const int shp = ps > 0 ? a.lchunk[ps - 1] - lgp : 0;
+  const int nc_ps = ps == 0 ? geo.n1 : nc_before << shp;
+  const int kc_ps = a.keep[ps] >> lgp;
+  const int n_sel = nc_ps <= kc_ps ? nc_ps : kc_ps;
+  const bool writer = blockIdx.x == 0;
+  int32_t* out = stage_starts(a, ps, r);
+  select_row<E>(key, js, nc_ps, kc_ps, L, [&](int j, int pos) {
+    const int st = ps == 0 ? a.n_sink + (j << lgp) : sprev[j >> shp] + ((j & ((1 << shp) - 1)) << lgp);
+    ssel[pos] = st;
+    if (writer) out[pos] = st;
+  });
+  if (writer && tid == 0) record_stage(a, ps, r, n_sel, geo);
+  __syncthreads();                              // the kept starts are in ssel
+
+  const int sh = lgp - a.lchunk[stage];
+  const int nc = n_sel << sh;
+  if (nc <= (a.keep[stage] >> a.lchunk[stage])) return;   // stage keeps everything for this row
+  if (j0 >= nc) return;
+  const int j = j0 + cl;
+  const bool active = j < nc;
+  const int st = ssel[min(j >> sh, n_sel - 1)] + ((j & ((1 << sh) - 1)) << a.lchunk[stage]);
+  float best = -INFINITY;
+  if (active) {
+    if constexpr (KIND == kRopeRelative) {
+      best = score_group_rt<T, D, G, SPEC, false>(a, stage, b, g, li, st, qx, qy);
+    } else {
+      const CiRows<T, D, false> rows(a, stage, b, g, li, st, theta);
+      best = selectrep_group<T, D, G, SPEC>(a, stage, li, st, rows, qx);
+    }
+  }
+  if (li == 0) red[gi] = best;
+  __syncthreads();
+  if (tid < cpw) {
+    const int jj = j0 + tid;
+    if (jj < nc) {
+      float m = red[tid * kv.Hkv];
+      for (int x = 1; x < kv.Hkv; ++x) m = fmaxf(m, red[tid * kv.Hkv + x]);
+      stage_scores(a, stage, r)[jj] = score_key(m);
+    }
+  }
+}
+
 static const char* const kRopeNames[kMaxStages] = {"prune_rope_score1", "prune_rope_score2", "prune_rope_score3",
                                                    "prune_rope_score4"};
 static const char* const kCiQueryNames[kMaxStages] = {"prune_ci_queries1", "prune_ci_queries2", "prune_ci_queries3",
                                                       "prune_ci_queries4"};
+static const char* const kRopeFusedNames[kMaxStages] = {"", "prune_topk1_rope_score2", "prune_topk2_rope_score3",
+                                                        "prune_topk3_rope_score4"};
 static const char* const kCiKeyNames[kMaxStages] = {"prune_ci_keys1", "prune_ci_keys2", "prune_ci_keys3",
                                                     "prune_ci_keys4"};
 
@@ -637,12 +731,74 @@ static void launch_decode_ci_g(const PruneArgs& a, int stage, int max_chunks, co
   else                  launch_decode_ci<T, D, G, false>(a, stage, max_chunks, q, base, st);
 }
 
-// Relative style: rotation once, then per stage the scoring (decode:
-// lane-group tournaments; bf16 prefill with 64-query blocks: the matrix-core
-// tournaments; otherwise the generic kernel) and the plain top-K.
-// Chunk-indexed style: per stage the queries (and, in prefill, the keys) are
-// rotated to the stage's position IDs, scored by the plain tournaments
-// (decode: on rows rotated in registers), and the plain top-K follows.
+constexpr long long kRopeFuseMaxWorkgroups = 2048;   // largest fused top-K + scoring launch
+
+// Top-K of stage - 1 and RoPE scoring of `stage` in one launch (bf16 decode,
+// contiguous K, one sequence's worth of workgroups); false if this shape takes
+// the separate kernels.
+template <typename T, int D, int G>
+static bool launch_rope_fused(const PruneArgs& a, int style, int stage, int max_chunks, int sel_chunks,
+                              const uint16_t* qa, const uint16_t* qb, double base, hipStream_t st) {
+  if constexpr (sizeof(T) != 2) {
+    return false;
+  } else {
+    const int cpw = 16 / a.kv.Hkv;
+    const dim3 grid(std::max(1, (max_chunks + cpw - 1) / cpw), a.R);
+    if (static_cast<long long>(grid.x) * grid.y > kRopeFuseMaxWorkgroups || a.kv.block_table) return false;
+    if (sel_chunks > kTopkThreads * 16) return false;
+    const bool e4 = sel_chunks <= kTopkThreads * 4;
+    const int spec = rope_spec(a.chunk[stage]);
+    const char* nm = kRopeFusedNames[stage];
+#define DSA_ROPE_FUSED(SP, EE)                                                                              \
+  do {                                                                                                      \
+    if (style == kRopeRelative)                                                                             \
+      DSA_LAUNCH(nm, (k_topk_score_decode_rope<D, G, SP, EE, kRopeRelative>), grid, dim3(256), st, a, stage, \
+                 qa, qb, base);                                                                             \
+    else                                                                                                    \
+      DSA_LAUNCH(nm, (k_topk_score_decode_rope<D, G, SP, EE, kRopeChunkIndexed>), grid, dim3(256), st, a,    \
+                 stage, qa, qb, base);                                                                      \
+  } while (0)
+    if (spec == 8)      { if (e4) DSA_ROPE_FUSED(8, 4); else DSA_ROPE_FUSED(8, 16); }
+    else if (spec == 4) { if (e4) DSA_ROPE_FUSED(4, 4); else DSA_ROPE_FUSED(4, 16); }
+    else                { if (e4) DSA_ROPE_FUSED(0, 4); else DSA_ROPE_FUSED(0, 16); }
+#undef DSA_ROPE_FUSED
+    return true;
+  }
+}
+
+// Decode: score stage 1; for every later stage, the previous stage's top-K and
+// this stage's scoring (fused where possible); the last top-K writes idx. The
+// chunk-indexed style rotates the queries to each stage's position ID first.
+template <typename T, int D, int G>
+static void launch_rope_decode(const PruneArgs& a, int style, uint16_t* qa, uint16_t* qb, double base,
+                               hipStream_t st) {
+  auto chunks_of = [&](int stage) { return stage == 0 ? a.n1max : a.keep[stage - 1] / a.chunk[stage]; };
+  const bool rt = style == kRopeRelative;
+  auto score = [&](int stage) {
+    if (chunks_of(stage) <= 0) return;
+    if (rt) launch_decode_rt_g<T, D, G>(a, stage, chunks_of(stage), qa, qb, st);
+    else    launch_decode_ci_g<T, D, G>(a, stage, chunks_of(stage), qa, base, st);
+  };
+  auto rotate = [&](int stage) {
+    if (!rt) DSA_LAUNCH(kCiQueryNames[stage], (k_ci_queries<T, D>), dim3(a.R, a.kv.Hq), dim3(256), st, a, stage, qa, base);
+  };
+  rotate(0);
+  score(0);
+  for (int stage = 1; stage < a.n_stages; ++stage) {
+    rotate(stage);
+    if (!launch_rope_fused<T, D, G>(a, style, stage, chunks_of(stage), chunks_of(stage - 1), qa, qb, base, st)) {
+      launch_topk(a, stage - 1, chunks_of(stage - 1), st);
+      score(stage);
+    }
+  }
+  launch_topk(a, a.n_stages - 1, chunks_of(a.n_stages - 1), st);
+}
+
+// Relative style: the queries are rotated once; chunk-indexed: per stage.
+// Decode runs launch_rope_decode; prefill scores each stage (relative: the
+// matrix-core tournaments for bf16 with 64-query blocks, else the generic
+// kernel; chunk-indexed: the plain scoring on rotated copies of the queries
+// and keys) and runs the plain top-K.
 template <typename T, int D>
 static hipError_t launch_rope_typed(const PruneArgs& a, int style, uint16_t* qa, uint16_t* qb, uint16_t* kb,
                                     double base, hipStream_t st) {
@@ -650,37 +806,30 @@ static hipError_t launch_rope_typed(const PruneArgs& a, int style, uint16_t* qa,
   if (rt) DSA_LAUNCH("prune_rope_queries", (k_rope_queries<T, D>), dim3(a.R, a.kv.Hq), dim3(256), st, a, qa, qb, base);
   const int G = a.kv.Hq / a.kv.Hkv;
   if (G != 1 && G != 2 && G != 4 && G != 8) return hipErrorInvalidValue;
+  if (a.kv.decode) {
+    switch (G) {
+      case 1: launch_rope_decode<T, D, 1>(a, style, qa, qb, base, st); break;
+      case 2: launch_rope_decode<T, D, 2>(a, style, qa, qb, base, st); break;
+      case 4: launch_rope_decode<T, D, 4>(a, style, qa, qb, base, st); break;
+      default: launch_rope_decode<T, D, 8>(a, style, qa, qb, base, st); break;
+    }
+    return hipGetLastError();
+  }
   for (int stage = 0; stage < a.n_stages; ++stage) {
     const int max_chunks = stage == 0 ? a.n1max : a.keep[stage - 1] / a.chunk[stage];
     if (max_chunks > 0 && rt) {
-      if (a.kv.decode) {
-        switch (G) {
-          case 1: launch_decode_rt_g<T, D, 1>(a, stage, max_chunks, qa, qb, st); break;
-          case 2: launch_decode_rt_g<T, D, 2>(a, stage, max_chunks, qa, qb, st); break;
-          case 4: launch_decode_rt_g<T, D, 4>(a, stage, max_chunks, qa, qb, st); break;
-          default: launch_decode_rt_g<T, D, 8>(a, stage, max_chunks, qa, qb, st); break;
-        }
-      } else if (!(sizeof(T) == 2 && launch_score_prefill_mfma(a, stage, max_chunks, st, kRopeNames[stage], qa, qb))) {
+      if (!(sizeof(T) == 2 && launch_score_prefill_mfma(a, stage, max_chunks, st, kRopeNames[stage], qa, qb))) {
         DSA_LAUNCH(kRopeNames[stage], (k_score_rope<T, D>), dim3((max_chunks + 15) / 16, a.R), dim3(256), st, a,
                    stage, qa, qb);
       }
     } else if (max_chunks > 0) {
       DSA_LAUNCH(kCiQueryNames[stage], (k_ci_queries<T, D>), dim3(a.R, a.kv.Hq), dim3(256), st, a, stage, qa, base);
-      if (a.kv.decode) {
-        switch (G) {
-          case 1: launch_decode_ci_g<T, D, 1>(a, stage, max_chunks, qa, base, st); break;
-          case 2: launch_decode_ci_g<T, D, 2>(a, stage, max_chunks, qa, base, st); break;
-          case 4: launch_decode_ci_g<T, D, 4>(a, stage, max_chunks, qa, base, st); break;
-          default: launch_decode_ci_g<T, D, 8>(a, stage, max_chunks, qa, base, st); break;
-        }
-      } else {
-        DSA_LAUNCH(kCiKeyNames[stage], (k_ci_keys<T, D>), dim3((a.kv.T + kCiTile - 1) / kCiTile), dim3(256), st, a,
-                   stage, kb, base);
-        PruneArgs ar = a;                       // the plain scoring, on the rotated copies
-        ar.q = qa;
-        ar.k = kb;
-        launch_score_prefill_bf16(ar, stage, max_chunks, st, kRopeNames[stage]);
-      }
+      DSA_LAUNCH(kCiKeyNames[stage], (k_ci_keys<T, D>), dim3((a.kv.T + kCiTile - 1) / kCiTile), dim3(256), st, a,
+                 stage, kb, base);
+      PruneArgs ar = a;                         // the plain scoring, on the rotated copies
+      ar.q = qa;
+      ar.k = kb;
+      launch_score_prefill_bf16(ar, stage, max_chunks, st, kRopeNames[stage]);
     }
     launch_topk(a, stage, max_chunks, st);
     hipError_t err = hipGetLastError();
