@@ -2,7 +2,8 @@
 
     python -m dynamic_sparse_attention_query_amd.build
 
-Compiles every csrc/*.hip into one shared library with hipcc. Always rebuilds.
+Compiles every csrc/*.hip to an object (in parallel) and links them into one
+shared library with hipcc. Always rebuilds.
 """
 from __future__ import annotations
 
@@ -25,19 +26,17 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    srcs = sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
-           # packed fp32 instructions stay off on this target
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           # matrix-core accumulators in ordinary VGPRs: the softmax and
-           # max-reductions read them with vector ALU instructions, which
-           # cannot address the accumulation registers directly
-           "-mllvm", "-amdgpu-mfma-vgpr-form=1",
-           "-Wno-unused-command-line-argument",
-           "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
-           *srcs, "-o", tmp]
+FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+         # packed fp32 instructions stay off on this target
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # matrix-core accumulators in ordinary VGPRs: the softmax and
+         # max-reductions read them with vector ALU instructions, which
+         # cannot address the accumulation registers directly
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+         "-Wno-unused-command-line-argument"]
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -47,6 +46,23 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if err.strip() and verbose:
         print(err, file=sys.stderr)
+
+
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    """Compile each source to an object in parallel, then link the library."""
+    from concurrent.futures import ThreadPoolExecutor
+    srcs = sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc")]
+    objs = [os.path.join(objdir, os.path.basename(src)[:-4] + ".o") for src in srcs]
+    jobs = jobs or max(1, min(len(srcs), os.cpu_count() or 1, 16))
+    with ThreadPoolExecutor(jobs) as pool:
+        for f in [pool.submit(_run, [hipcc(), *FLAGS, *inc, "-c", src, "-o", obj], verbose)
+                  for src, obj in zip(srcs, objs)]:
+            f.result()
+    tmp = LIB + ".tmp"
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 
