@@ -174,3 +174,32 @@ def test_rope_decode_edge_lengths_and_budgets(style):
             mid_hi = 16 + ((T - 64 - 16) // 64) * 64
             row = idx[5]
             assert np.array_equal(row[row >= 0], np.r_[np.arange(16), np.arange(mid_hi, T)])
+
+
+@pytest.fixture(scope="module")
+def c4_full():
+    case = gen.make_case("c4", n_queries=1)
+    return case, to_device(case)
+
+
+@pytest.mark.parametrize("style", STYLES)
+def test_rope_decode_batch32_paged_full(c4_full, style):
+    """The batch-32 ragged paged workload at full size (lengths 65,536 to
+    262,144): the launches exceed one sequence's worth of workgroups, so each
+    stage's top-K runs as its own kernel; three sampled sequences against the
+    oracle, every row's shape checked."""
+    case, dev = c4_full
+    H.say(f"rope {style} decode batch-32 paged full size")
+    q = dev.q[0].contiguous()
+    idx = api.prune_select_rope(q, dev.k, params_of(case.cfg), BASE, seq_lens=dev.seq_lens,
+                                block_table=dev.block_table, t=dev.t, style=style).cpu().numpy()
+    p = H.oracle_params(case.cfg)
+    for b in (0, 17, 31):
+        want = oracle_row_rt(case, b, 0, style=style)
+        assert np.array_equal(idx[b], want), f"sequence {b}: first diff {np.flatnonzero(idx[b] != want)[:5]}"
+    for b in range(case.cfg.batch):
+        row = idx[b][idx[b] >= 0]
+        e = int(case.seq_lens[b])
+        rem = (e - p.n_window - p.n_sink) % p.chunk[0]
+        assert len(row) == p.n_sink + p.keep[-1] + p.n_window + rem and np.all(np.diff(row) > 0), b
+        assert np.array_equal(row[:p.n_sink], np.arange(p.n_sink)) and row[-1] == e - 1, b
