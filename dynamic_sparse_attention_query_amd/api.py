@@ -275,6 +275,16 @@ def vertical_slash_select(q: torch.Tensor, k: torch.Tensor, k_v: int, k_s: int, 
 # --------------------------------------------------------------------------- #
 # pruning with RoPE inside SelectRep (relative or chunk-indexed)              #
 # --------------------------------------------------------------------------- #
+def rope_style_for_layer(layer: int, n_chunk_indexed: int = 3) -> str:
+    """RoPE style of a model layer (1-based) under the InfiniteHiP page's
+    layer-specific assignment ("Layer-Specific Strategy Assignment"): the
+    chunk-indexed style for the first three layers, the relative style for
+    the rest."""
+    if layer < 1:
+        raise ValueError(f"layer {layer}: layers are numbered from 1")
+    return "chunk_indexed" if layer <= n_chunk_indexed else "relative"
+
+
 def prune_select_rope(q: torch.Tensor, k: torch.Tensor, params: Params, base: float, *,
                       seq_lens: Optional[torch.Tensor] = None, block_table: Optional[torch.Tensor] = None,
                       t: Optional[int] = None, out: Optional[torch.Tensor] = None,

@@ -236,3 +236,11 @@ def test_prune_rope_sizes_and_rejections():
     with pytest.raises(_lib.DsaError) as ei:
         _lib.prune_select_rope_raw(s, 256, 256, P2, 10000.0, 256, 256, ci - 1, style=_lib.DSA_ROPE_CHUNK_INDEXED)
     assert ei.value.status == DSA_ERR_WORKSPACE
+
+
+def test_rope_style_for_layer_follows_the_page_assignment():
+    from dynamic_sparse_attention_query_amd import api
+    assert [api.rope_style_for_layer(l) for l in (1, 2, 3)] == ["chunk_indexed"] * 3
+    assert {api.rope_style_for_layer(l) for l in range(4, 33)} == {"relative"}
+    with pytest.raises(ValueError):
+        api.rope_style_for_layer(0)
