@@ -203,3 +203,18 @@ def test_rope_decode_batch32_paged_full(c4_full, style):
         rem = (e - p.n_window - p.n_sink) % p.chunk[0]
         assert len(row) == p.n_sink + p.keep[-1] + p.n_window + rem and np.all(np.diff(row) > 0), b
         assert np.array_equal(row[:p.n_sink], np.arange(p.n_sink)) and row[-1] == e - 1, b
+
+
+@pytest.mark.parametrize("style", STYLES)
+def test_rope_prefill_two_sequences(style):
+    """Two prefill sequences in one call (the key rotation and the rotated
+    query copies index sequence and kv head): every block of both."""
+    case = gen.make_case("c2", hq=8, hkv=2, d=128, t=1024, batch=2, chunk=(16, 4), keep=(256, 64), n_window=64,
+                         n_sink=16, n_needles=0, structure="plain")
+    H.say(f"rope {style} prefill, two sequences")
+    dev = to_device(case)
+    idx = api.prune_select_rope(dev.q, dev.k, params_of(case.cfg), BASE, style=style).cpu().numpy()
+    for b in range(2):
+        for m in range(case.cfg.t // case.cfg.block_q):
+            want = oracle_row_rt(case, b, m, style=style)
+            assert np.array_equal(idx[b, m], want), f"seq {b} block {m}: first diff {np.flatnonzero(idx[b, m] != want)[:5]}"
