@@ -1,10 +1,12 @@
 #!/usr/bin/env python3
 """Benchmark of the sparse-attention hot path on one MI355X.
 
-Headline: 1M-context decode attention, one step = prune_select (three pruning
-stages) + sparse_attn for one new query of a batch-1 sequence with 32 query /
-8 KV heads, d=128, T=1,048,576 bf16. Reported as microseconds per token, with
-the step's algorithmic HBM bytes / time against the 8 TB/s HBM peak.
+Headline: 1M-context decode attention, one step = hierarchical pruning (three
+stages) + sparse attention for one new query of a batch-1 sequence with 32
+query / 8 KV heads, d=128, T=1,048,576 bf16, through dsa_prune_attend (the
+one-call step; the two-call prune_select + sparse_attn figure is reported
+next to it). Reported as microseconds per token, with the step's algorithmic
+HBM bytes / time against the 8 TB/s HBM peak.
 
 Secondary figures on the same JSON line: 128K sparse prefill TFLOP/s against
 the bf16 MFMA peak, the library's dense decode at 1M, per-kernel durations
@@ -79,6 +81,8 @@ def parse():
     ap.add_argument("--replicas", type=int, default=8,
                     help="KV copies cycled through so consecutive steps share no cache lines")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
+    ap.add_argument("--graph-steps", type=int, default=8,
+                    help="decode steps captured per HIP graph (a model captures a whole decode step)")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cached", action="store_true", help="skip decoding with remembered stages")
@@ -211,7 +215,7 @@ def decode_bench(args, res):
     out = torch.empty((1, Hq, d), dtype=torch.float32, device="cuda")
     cs, cp = shape.c(), p.c()
 
-    def launch(i, visited=None):
+    def launch_two(i, visited=None):
         q, r = Qs[i % NQ], i % args.replicas
         sp = torch.cuda.current_stream().cuda_stream
         st = lib.dsa_prune_select(ctypes.byref(cs), q.data_ptr(), Ks[r].data_ptr(), ctypes.byref(cp),
@@ -219,6 +223,15 @@ def decode_bench(args, res):
                                   visited.data_ptr() if visited is not None else None, sp)
         st |= lib.dsa_sparse_attn(ctypes.byref(cs), q.data_ptr(), Ks[r].data_ptr(), Vs[r].data_ptr(),
                                   idx.data_ptr(), L, 1, 0.0, out.data_ptr(), ws.data_ptr(), wsb, sp)
+        if st:
+            raise RuntimeError(lib.dsa_last_error().decode())
+
+    def launch(i, visited=None):
+        q, r = Qs[i % NQ], i % args.replicas
+        sp = torch.cuda.current_stream().cuda_stream
+        st = lib.dsa_prune_attend(ctypes.byref(cs), q.data_ptr(), Ks[r].data_ptr(), Vs[r].data_ptr(),
+                                  ctypes.byref(cp), 0.0, idx.data_ptr(), out.data_ptr(), ws.data_ptr(), wsb,
+                                  visited.data_ptr() if visited is not None else None, sp)
         if st:
             raise RuntimeError(lib.dsa_last_error().decode())
 
@@ -237,39 +250,54 @@ def decode_bench(args, res):
     step_bytes = stage_bytes.sum(1) + attn_bytes
 
     K, W = args.steps, args.warmup
-    graphs = None
-    if not args.eager:
-        graphs = []
-        torch.cuda.synchronize()
-        for i in range(NQ):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                launch(i)
-            graphs.append(g)
-        torch.cuda.synchronize()
+    GS = args.graph_steps if args.graph_steps > 0 and K % args.graph_steps == 0 else 1
 
-    def run(i):
-        if graphs is not None:
-            graphs[i % NQ].replay()
-        else:
-            launch(i)
+    def timed(fn):
+        """(wall us/step, event us/step, wall ms, step indices) of K steps after
+        the warm-up: graph replays of GS steps each (step i uses query i mod NQ
+        and KV replica i mod replicas), or eager launches with --eager."""
+        n_w = max(1, W // GS)
+        n_runs = K // GS if not args.eager else K
+        steps_of = lambda j: list(range(j * GS, j * GS + GS)) if not args.eager else [j]
+        graphs = None
+        if not args.eager:
+            graphs = []
+            torch.cuda.synchronize()
+            for j in range(n_w + n_runs):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for i in steps_of(j):
+                        fn(i)
+                graphs.append(g)
+            torch.cuda.synchronize()
 
-    for i in range(W):
-        run(i)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_start = time.perf_counter()
-    e0.record()
-    for i in range(W, W + K):
-        run(i)
-    e1.record()
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t_start) * 1e3
-    ev_ms = e0.elapsed_time(e1)
-    used = [i % NQ for i in range(W, W + K)]
+        def run(j):
+            if graphs is not None:
+                graphs[j].replay()
+            else:
+                fn(j)
+
+        for j in range(n_w):
+            run(j)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t_start = time.perf_counter()
+        e0.record()
+        for j in range(n_w, n_w + n_runs):
+            run(j)
+        e1.record()
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t_start) * 1e3
+        del graphs
+        steps = [i for j in range(n_w, n_w + n_runs) for i in steps_of(j)]
+        return wall_ms * 1e3 / K, e0.elapsed_time(e1) * 1e3 / K, wall_ms, steps
+
+    us_step, ev_us, wall_ms, steps = timed(launch)
+    two_us, _, _, _ = timed(launch_two)
+    used = [i % NQ for i in steps]
     bytes_avg = float(step_bytes[used].mean())
-    us_step = wall_ms * 1e3 / K
-    log(f"decode 1M: {us_step:.1f} us/step wall, {ev_ms * 1e3 / K:.1f} us/step events")
+    log(f"decode 1M: {us_step:.1f} us/step wall, {ev_us:.1f} us/step events ({GS} steps per graph); "
+        f"two-call path {two_us:.1f} us/step")
 
     # per-kernel durations: HIP events around graph replays of each kernel of a
     # captured step (kernel names from the library's own launch record)
@@ -283,9 +311,9 @@ def decode_bench(args, res):
     kern_us = dict(zip(names, gt))
     per_launch_bytes = {
         "prune_score_stage1": float(stage_bytes[used, 0].mean()),
-        "prune_score_stage2": float(stage_bytes[used, 1].mean()),
-        "prune_score_stage3": float(stage_bytes[used, 2].mean()),
-        "attn_decode_partial": float(attn_bytes[used].mean()),
+        "prune_topk1_score2": float(stage_bytes[used, 1].mean()),
+        "prune_topk2_score3": float(stage_bytes[used, 2].mean()),
+        "decode_topk_attend_partial": float(attn_bytes[used].mean()),
     }
     dom = max(kern_us, key=kern_us.get)
     roof = None
@@ -295,16 +323,18 @@ def decode_bench(args, res):
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": tr,
                 "avg_us": round(kern_us[dom], 2), "algorithmic_bytes_per_launch": int(per_launch_bytes[dom])}
-    res["decode"] = dict(us_per_step=us_step, event_us_per_step=ev_ms * 1e3 / K, wall_ms=wall_ms,
+    res["decode"] = dict(us_per_step=us_step, event_us_per_step=ev_us, wall_ms=wall_ms,
+                         two_call_us_per_step=two_us, graph_steps=GS,
                          bytes_per_step=bytes_avg, stage_rows=(stage_bytes[used].mean(0) / row_bytes).tolist(),
                          kernels_us={k: round(v, 2) for k, v in kern_us.items()}, roofline=roof,
-                         mode="graph" if graphs is not None else "eager")
+                         mode="graph" if not args.eager else "eager")
 
     if not args.no_cached:
         res["cached"] = cached_decode(args, lib, p, Qs, Ks, Vs, shape, ws, wsb, out, dev.seq_lens)
 
     if not args.no_dense:
         reps = 5
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         dshape_ws = _lib.workspace_bytes(shape, None)
         dws = torch.empty(dshape_ws, dtype=torch.uint8, device="cuda")
         for i in range(reps + 1):

@@ -19,7 +19,7 @@ DSA_F32, DSA_BF16 = 0, 1
 DSA_PREFILL, DSA_DECODE = 0, 1
 MAX_STAGES = 4
 
-EXPORTS = ("dsa_index_width", "dsa_workspace_bytes", "dsa_prune_select", "dsa_sparse_attn",
+EXPORTS = ("dsa_index_width", "dsa_workspace_bytes", "dsa_prune_select", "dsa_sparse_attn", "dsa_prune_attend",
            "dsa_dense_attn", "dsa_mask_cache_bytes", "dsa_cached_index_width", "dsa_prune_select_cached",
            "dsa_block_sparse_index_width", "dsa_block_sparse_workspace_bytes", "dsa_block_sparse_select",
            "dsa_sparse_attn_heads", "dsa_vertical_slash_index_width", "dsa_vertical_slash_workspace_bytes",
@@ -76,6 +76,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dsa_workspace_bytes.argtypes = [ctypes.POINTER(CShape), ctypes.POINTER(CParams), ctypes.POINTER(sz)]
     lib.dsa_workspace_bytes.restype = ctypes.c_int
     lib.dsa_prune_select.argtypes = [ctypes.POINTER(CShape), vp, vp, ctypes.POINTER(CParams), vp, vp, sz, vp, vp]
+    lib.dsa_prune_attend.argtypes = [ctypes.POINTER(CShape), vp, vp, vp, ctypes.POINTER(CParams), ctypes.c_float,
+                                     vp, vp, vp, sz, vp, vp]
+    lib.dsa_prune_attend.restype = ctypes.c_int
     lib.dsa_prune_select.restype = ctypes.c_int
     lib.dsa_mask_cache_bytes.argtypes = [ctypes.POINTER(CShape), ctypes.POINTER(CParams), ctypes.POINTER(sz)]
     lib.dsa_mask_cache_bytes.restype = ctypes.c_int
@@ -202,6 +205,13 @@ def prune_select_raw(shape: Shape, q: int, k: int, p: Params, idx: int, ws: int,
                      visited: int = 0, stream: int = 0):
     cs, cp = shape.c(), p.c()
     _check(load().dsa_prune_select(ctypes.byref(cs), q, k, ctypes.byref(cp), idx, ws, ws_bytes,
+                                   visited or None, stream or None))
+
+
+def prune_attend_raw(shape: Shape, q: int, k: int, v: int, p: Params, scale: float, idx: int, out: int,
+                     ws: int, ws_bytes: int, visited: int = 0, stream: int = 0):
+    cs, cp = shape.c(), p.c()
+    _check(load().dsa_prune_attend(ctypes.byref(cs), q, k, v, ctypes.byref(cp), scale, idx, out, ws, ws_bytes,
                                    visited or None, stream or None))
 
 

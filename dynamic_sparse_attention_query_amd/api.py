@@ -117,6 +117,38 @@ def prune_select(q: torch.Tensor, k: torch.Tensor, params: Params, *,
     return out.view(shape.batch, shape.t // params.block_q, L)
 
 
+def prune_attend(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, params: Params, *, scale: float = 0.0,
+                 seq_lens: Optional[torch.Tensor] = None, block_table: Optional[torch.Tensor] = None,
+                 t: Optional[int] = None, idx: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                 visited: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """prune_select followed by sparse_attn in one call: (idx, out)."""
+    shape = make_shape(q, k, seq_lens=seq_lens, block_table=block_table, t=t)
+    _need(v, "v")
+    if v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("v must match k")
+    L = _lib.index_width(params)
+    if L < 0:
+        raise _lib.DsaError(_lib.DSA_ERR_INVALID_ARG, "invalid params")
+    rows = shape.batch * (1 if shape.mode == DSA_DECODE else shape.t // params.block_q)
+    if idx is None:
+        idx = torch.empty(rows * L, dtype=torch.int32, device=q.device)
+    if idx.numel() != rows * L or idx.dtype != torch.int32:
+        raise ValueError("idx buffer has the wrong size or dtype")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    ws, wsb = workspace(shape, params, q.device)
+    vis = 0
+    if visited is not None:
+        if visited.dtype != torch.int64 or visited.numel() < len(params.chunk):
+            raise ValueError("visited must be int64 with one entry per stage")
+        vis = visited.data_ptr()
+    _lib.prune_attend_raw(shape, q.data_ptr(), k.data_ptr(), v.data_ptr(), params, scale, idx.data_ptr(),
+                          out.data_ptr(), ws, wsb, vis, _stream())
+    if shape.mode == DSA_DECODE:
+        return idx.view(shape.batch, L), out
+    return idx.view(shape.batch, shape.t // params.block_q, L), out
+
+
 class MaskCache:
     """Remembered stage outputs of one stream of decode steps (mask caching).
 

@@ -121,6 +121,26 @@ size_t attn_bytes(const dsa_shape* s, long long n_total) {
   return align256(static_cast<size_t>(s->batch) * s->hq * n_splits * (s->d + 2) * 4);
 }
 
+// Workspace of dsa_prune_attend: the pruning state and the attention partials
+// (split partials of the fused decode tail or of the separate kernels).
+struct StepLayout {
+  PruneLayout pl;
+  long long nsp;
+  size_t off_part, bytes;
+};
+
+StepLayout step_layout(const dsa_shape* s, const dsa_params* p) {
+  StepLayout L{};
+  L.pl = prune_layout(s, p);
+  const long long width = index_width_ll(p);
+  L.nsp = (width + dsa::kStepSplitKeys - 1) / dsa::kStepSplitKeys;
+  const size_t fused = s->mode == DSA_DECODE
+                           ? static_cast<size_t>(s->batch) * s->hq * L.nsp * (s->d + 2) * 4 : 0;
+  L.off_part = align256(L.pl.bytes);
+  L.bytes = L.off_part + align256(std::max(fused, attn_bytes(s, width)));
+  return L;
+}
+
 dsa::KvLayout make_kv(const dsa_shape* s, int bq) {
   dsa::KvLayout kv{};
   kv.B = s->batch;
@@ -200,6 +220,7 @@ dsa_status dsa_workspace_bytes(const dsa_shape* s, const dsa_params* p, size_t* 
     if (st != DSA_OK) return st;
     bytes = std::max(bytes, prune_layout(s, p).bytes);
     bytes = std::max(bytes, attn_bytes(s, index_width_ll(p)));
+    bytes = std::max(bytes, step_layout(s, p).bytes);
   }
   *out_bytes = bytes;
   return DSA_OK;
@@ -367,6 +388,57 @@ dsa_status dsa_sparse_attn(const dsa_shape* s, const void* q, const void* k, con
     if (s->t % block_q != 0) return fail(DSA_ERR_INVALID_ARG, "t %% block_q != 0");
   }
   return run_attn(s, q, k, v, idx, idx_width, block_q, scale, out, ws, ws_bytes, stream);
+}
+
+dsa_status dsa_prune_attend(const dsa_shape* s, const void* q, const void* k, const void* v,
+                            const dsa_params* p, float scale, int32_t* idx, float* out, void* ws,
+                            size_t ws_bytes, uint64_t* visited, void* stream) {
+  g_err[0] = 0;
+  dsa_status st = check_shape(s);
+  if (st != DSA_OK) return st;
+  st = check_params(s, p);
+  if (st != DSA_OK) return st;
+  if (!q || !k || !v || !idx || !out) return fail(DSA_ERR_INVALID_ARG, "q, k, v, idx and out must be non-NULL");
+  const long long L = index_width_ll(p);
+  if (L > (1LL << 30)) return fail(DSA_ERR_INVALID_ARG, "index width overflows");
+  const StepLayout lay = step_layout(s, p);
+  if (lay.pl.maxNC > 32768)
+    return fail(DSA_ERR_UNSUPPORTED, "a stage would score %lld chunks per row (limit 32768)", lay.pl.maxNC);
+  if (!ws || ws_bytes < lay.bytes)
+    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, lay.bytes);
+  char* wsc = static_cast<char*>(ws);
+  dsa::PruneArgs a = prune_args(s, q, k, p, idx, L, lay.pl, ws, visited);
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const float sc = scale > 0.f ? scale : 1.0f / std::sqrt(static_cast<float>(s->d));
+  hipError_t err = hipSuccess;
+  bool fused = false;
+  if (s->mode == DSA_DECODE && s->dtype == DSA_BF16) {
+    err = dsa::launch_prune_decode_stages(a, s->dtype, hs);
+    if (err != hipSuccess) return fail(DSA_ERR_HIP, "prune launch failed: %s", hipGetErrorString(err));
+    dsa::StepArgs sa{};
+    sa.p = a;
+    sa.v = v;
+    sa.part = reinterpret_cast<float*>(wsc + lay.off_part);
+    sa.out = out;
+    sa.scale_log2 = sc * 1.4426950408889634f;
+    sa.nsp = static_cast<int>(lay.nsp);
+    {
+      const int ls = p->n_stages - 1;
+      const long long kept_hi = static_cast<long long>(p->n_sink) + p->keep[ls];   // most kept entries
+      sa.ks0 = std::min<int>(sa.nsp, p->n_sink / dsa::kStepSplitKeys);
+      sa.ks1 = static_cast<int>(std::min<long long>(sa.nsp, (kept_hi + dsa::kStepSplitKeys - 1) / dsa::kStepSplitKeys));
+      sa.ks1 = std::max(sa.ks1, sa.ks0);
+    }
+    fused = dsa::launch_decode_attend(sa, dsa::last_stage_chunks(a), hs);
+    if (!fused) dsa::launch_topk(a, p->n_stages - 1, dsa::last_stage_chunks(a), hs);
+    err = hipGetLastError();
+  } else {
+    err = dsa::launch_prune(a, s->dtype, hs);
+  }
+  if (err != hipSuccess) return fail(DSA_ERR_HIP, "prune launch failed: %s", hipGetErrorString(err));
+  if (fused) return DSA_OK;
+  return run_attn(s, q, k, v, idx, static_cast<int32_t>(L), p->block_q, scale, out, wsc + lay.off_part,
+                  lay.bytes - lay.off_part, stream);
 }
 
 dsa_status dsa_dense_attn(const dsa_shape* s, const void* q, const void* k, const void* v, float scale,

@@ -310,6 +310,13 @@ static void launch_decode(const AttnArgs& a, hipStream_t st) {
              dim3(a.kv.Hq, a.kv.B), dim3(kCombineThreads), st, a);
 }
 
+void launch_decode_combine(const AttnArgs& a, hipStream_t st) {
+  if (a.kv.D == 128)
+    DSA_LAUNCH("attn_decode_combine", (k_decode_combine<128>), dim3(a.kv.Hq, a.kv.B), dim3(kCombineThreads), st, a);
+  else
+    DSA_LAUNCH("attn_decode_combine", (k_decode_combine<64>), dim3(a.kv.Hq, a.kv.B), dim3(kCombineThreads), st, a);
+}
+
 template <typename T, int D>
 static hipError_t launch_attn_typed(const AttnArgs& a, hipStream_t st) {
   if (a.kv.decode) {

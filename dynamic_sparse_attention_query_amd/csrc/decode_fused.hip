@@ -1,0 +1,257 @@
+// One decode step of pruning and attention with the tail fused: the last
+// stage's top-K and the gathered split attention in a single launch.
+//
+// The selection is the last stage's step 6 of the InfiniteHiP page's pruning
+// stage (section 3.4, "Formal Mechanism of a Single Pruning Stage"); the
+// attention is the split-key "Flash Decoding" pass of its "Block Sparse
+// Attention Implementation", with the partial softmax merge of the InfLLM blog
+// page ("Mathematical Formulation of Efficient Softmax Normalization").
+//
+// The index row of a sequence is cut into splits of kSplitKeys entries; one
+// workgroup owns one (split, kv head, sequence):
+//   * a split that holds kept chunks of the last stage selects the row's kept
+//     chunks itself from the stage's complete score list (select_cols, the
+//     same selection as k_topk: score descending, lower chunk first), so the
+//     selection needs no kernel of its own; splits of sinks, window or padding
+//     skip it and start their loads at once;
+//   * the workgroups of kv head 0 write the row's entries (the idx output);
+//   * the split's K and V rows are gathered (16 lanes per 256-byte row, eight
+//     rows per lane group), scored against the kv head's query heads, and an
+//     unnormalised partial (local max m, sum l, o[d]) per query head is
+//     written, as the split-partial decode kernel does.
+// A second kernel (the split-partial merge of the separate decode path) turns
+// the partials into the output. (Merging in the last-arriving workgroup was
+// measured slower: the device-scope release and acquire around the arrival
+// counter write back and invalidate the L2 of every XCD, about 10 us per
+// step at 1M.)
+#include <algorithm>
+
+#include "prune_common.h"
+#include "topk_select.h"
+
+namespace dsa {
+
+template <int D, int G, int E, bool PAGED, int kSplitKeys = kStepSplitKeys>
+__global__ void __launch_bounds__(256, 2) k_decode_attend(StepArgs s) {
+  constexpr int kKeysPerGroup = kSplitKeys / 16;
+  using T = uint16_t;
+  constexpr int EPL = D / 16;
+  using Row = RowSlice<T, EPL>;
+  constexpr int NO = (G * D) / 256;           // outputs per thread in the reduction (G * D >= 256)
+  static_assert(G * D % 256 == 0, "whole outputs per thread");
+  __shared__ SelectColLds<kTopkWaves> LS;
+  __shared__ int sprev[kFusedMaxKept];
+  __shared__ int skept[kFusedMaxKept + 64];
+  __shared__ int spos[kSplitKeys];
+  __shared__ float smax[16][G];
+  __shared__ float sred[4][G * D + G];
+
+  const PruneArgs& a = s.p;
+  const KvLayout& kv = a.kv;
+  // workgroup order: the splits that hold kept chunks (and select) first, for
+  // every kv head, then the sink / window / padding splits, so the selecting
+  // workgroups are the first ones placed on the CUs
+  const int b = blockIdx.z, r = b;
+  int sp, g;
+  {
+    const int lin = blockIdx.y * gridDim.x + blockIdx.x;
+    const int nk = (s.ks1 - s.ks0) * kv.Hkv;
+    if (lin < nk) {
+      sp = s.ks0 + lin / kv.Hkv;
+      g = lin % kv.Hkv;
+    } else {
+      const int o = (lin - nk) / kv.Hkv;
+      sp = o < s.ks0 ? o : o + (s.ks1 - s.ks0);
+      g = (lin - nk) % kv.Hkv;
+    }
+  }
+  const int tid = threadIdx.x, gi = tid >> 4, li = tid & 15, lane = tid & 63, w = tid >> 6;
+  const T* Q = static_cast<const T*>(a.q);
+  const T* K = static_cast<const T*>(a.k);
+  const T* V = static_cast<const T*>(s.v);
+
+  // row geometry of the last stage (uniform over the row's workgroups)
+  const int e = kv.seq_lens[b];
+  const int ls = a.n_stages - 1;
+  const int lg = a.lchunk[ls];
+  const int shp = ls > 0 ? a.lchunk[ls - 1] - lg : 0;
+  const int nc_before = ls > 0 ? a.cnt[r * kMaxStages + ls - 1] : 0;
+  Row q[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) q[hh].load(Q + (static_cast<size_t>(b) * kv.Hq + g * G + hh) * D + li * EPL);
+  const Geo geo = make_geo(e - 1, e, a.n_sink, a.n_window, a.chunk[0]);
+  const int nc = ls == 0 ? geo.n1 : nc_before << shp;
+  const int kc = a.keep[ls] >> lg;
+  const int n_sel = min(nc, kc);
+  const int win0 = geo.sink_hi + (n_sel << lg);   // kept chunks fill [sink_hi, win0)
+  const int end = win0 + max(0, e - geo.mid_hi);  // then the window [mid_hi, e)
+  const int i0 = sp * kSplitKeys;
+
+  if (i0 < win0 && i0 + kSplitKeys > geo.sink_hi) {
+    uint32_t key[E];
+    load_keys_cols<E>(a, ls, r, key);
+    if (ls > 0) load_kept_starts(a, ls - 1, r, sprev);
+    select_cols<E>(key, nc, kc, LS, skept);
+    __syncthreads();                            // skept holds the kept chunk indices
+  }
+  if (tid < kSplitKeys) {
+    const int i = i0 + tid;
+    int p = -1;
+    if (i < geo.sink_hi) {
+      p = i;
+    } else if (i < win0) {
+      const int c = i - geo.sink_hi;
+      p = kept_start(a, ls, skept[c >> lg], sprev) + (c & ((1 << lg) - 1));
+    } else if (i < end) {
+      p = geo.mid_hi + (i - win0);
+    }
+    if (g == 0 && i < a.L) a.idx[static_cast<size_t>(r) * a.L + i] = p;
+    spos[tid] = p;
+  }
+  __syncthreads();
+
+  // gather the split's K and V rows: lane group gi takes entries gi + 16u
+  int pu[kKeysPerGroup];
+  Row kr[kKeysPerGroup], vr[kKeysPerGroup];
+#pragma unroll
+  for (int u = 0; u < kKeysPerGroup; ++u) {
+    pu[u] = spos[gi + 16 * u];
+    const int pp = max(pu[u], 0);               // padding reads row 0 and is masked below
+    size_t off;
+    if constexpr (PAGED) off = kv_offset(kv, b, g, pp);
+    else off = ((static_cast<size_t>(b) * kv.Hkv + g) * kv.T + pp) * D;
+    kr[u].load(K + off + li * EPL);
+    vr[u].load(V + off + li * EPL);
+  }
+  float sc[kKeysPerGroup][G];
+  float mloc[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) mloc[hh] = kNegBig;
+#pragma unroll
+  for (int u = 0; u < kKeysPerGroup; ++u) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const float d = group16_sum(kr[u].dot(q[hh])) * s.scale_log2;
+      sc[u][hh] = pu[u] >= 0 ? d : -INFINITY;
+      mloc[hh] = fmaxf(mloc[hh], sc[u][hh]);
+    }
+  }
+  if (li == 0) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) smax[gi][hh] = mloc[hh];
+  }
+  __syncthreads();
+  float M[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    float m = smax[0][hh];
+#pragma unroll
+    for (int x = 1; x < 16; ++x) m = fmaxf(m, smax[x][hh]);
+    M[hh] = m;
+  }
+  // this group's share of l and o = sum_u 2^(s_u - M) v_u
+  float lsum[G], o[G][EPL];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    lsum[hh] = 0.f;
+#pragma unroll
+    for (int x = 0; x < EPL; ++x) o[hh][x] = 0.f;
+  }
+#pragma unroll
+  for (int u = 0; u < kKeysPerGroup; ++u) {
+    float vf[EPL];
+#pragma unroll
+    for (int x = 0; x < EPL / 2; ++x) {
+      vf[2 * x] = __uint_as_float(vr[u].w[x] << 16);
+      vf[2 * x + 1] = __uint_as_float(vr[u].w[x] & 0xffff0000u);
+    }
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const float pz = sc[u][hh] == -INFINITY ? 0.f : exp2f(sc[u][hh] - M[hh]);
+      lsum[hh] += pz;
+#pragma unroll
+      for (int x = 0; x < EPL; ++x) o[hh][x] = fmaf(pz, vf[x], o[hh][x]);
+    }
+  }
+  // sum over the wave's four lane groups, then over the waves in LDS
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    lsum[hh] += __shfl_xor(lsum[hh], 16);
+    lsum[hh] += __shfl_xor(lsum[hh], 32);
+#pragma unroll
+    for (int x = 0; x < EPL; ++x) {
+      o[hh][x] += __shfl_xor(o[hh][x], 16);
+      o[hh][x] += __shfl_xor(o[hh][x], 32);
+    }
+  }
+  if (lane < 16) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+#pragma unroll
+      for (int x = 0; x < EPL; ++x) sred[w][hh * D + li * EPL + x] = o[hh][x];
+      if (li == 0) sred[w][G * D + hh] = lsum[hh];
+    }
+  }
+  __syncthreads();
+  float* P = s.part;
+  const size_t head0 = static_cast<size_t>(b) * kv.Hq + g * G;
+#pragma unroll
+  for (int i = 0; i < NO; ++i) {
+    const int oi = tid + 256 * i;
+    const int hh = oi / D, dd = oi - hh * D;
+    const float v = (sred[0][oi] + sred[1][oi]) + (sred[2][oi] + sred[3][oi]);
+    P[((head0 + hh) * s.nsp + sp) * (D + 2) + dd] = v;
+  }
+  if (tid < G) {
+    const float lt = (sred[0][G * D + tid] + sred[1][G * D + tid]) + (sred[2][G * D + tid] + sred[3][G * D + tid]);
+    float* mlp = P + ((head0 + tid) * s.nsp + sp) * (D + 2) + D;
+    mlp[0] = M[tid];
+    mlp[1] = lt;
+  }
+}
+
+// ------------------------------------------------------------------------- //
+// launcher                                                                  //
+// ------------------------------------------------------------------------- //
+// True if the fused tail was launched; false if this shape takes the separate
+// selection, partial and merge kernels.
+template <int D, int G>
+static bool launch_attend_typed(const StepArgs& s, int sel_chunks, hipStream_t st) {
+  const PruneArgs& a = s.p;
+  const dim3 grid(s.nsp, a.kv.Hkv, a.kv.B);
+  const int ls = a.n_stages - 1;
+  if (static_cast<long long>(grid.x) * grid.y * grid.z > 2048) return false;
+  if ((a.keep[ls] >> a.lchunk[ls]) > kFusedMaxKept) return false;
+  if (ls > 0 && (a.keep[ls - 1] >> a.lchunk[ls - 1]) > kFusedMaxKept) return false;
+  const bool paged = a.kv.block_table != nullptr;
+  const char* nm = "decode_topk_attend_partial";
+  if (sel_chunks <= kTopkThreads * 4) {
+    if (paged) DSA_LAUNCH(nm, (k_decode_attend<D, G, 4, true>), grid, dim3(256), st, s);
+    else       DSA_LAUNCH(nm, (k_decode_attend<D, G, 4, false>), grid, dim3(256), st, s);
+  } else if (sel_chunks <= kTopkThreads * 16) {
+    if (paged) DSA_LAUNCH(nm, (k_decode_attend<D, G, 16, true>), grid, dim3(256), st, s);
+    else       DSA_LAUNCH(nm, (k_decode_attend<D, G, 16, false>), grid, dim3(256), st, s);
+  } else {
+    return false;
+  }
+  AttnArgs m{};
+  m.kv = a.kv;
+  m.out = s.out;
+  m.part = s.part;
+  m.n_splits = s.nsp;
+  launch_decode_combine(m, st);
+  return true;
+}
+
+bool launch_decode_attend(const StepArgs& s, int sel_chunks, hipStream_t st) {
+  const PruneArgs& a = s.p;
+  if (a.kv.D != 128) return false;
+  switch (a.kv.Hq / a.kv.Hkv) {
+    case 2: return launch_attend_typed<128, 2>(s, sel_chunks, st);
+    case 4: return launch_attend_typed<128, 4>(s, sel_chunks, st);
+    case 8: return launch_attend_typed<128, 8>(s, sel_chunks, st);
+    default: return false;
+  }
+}
+
+}  // namespace dsa

@@ -67,6 +67,18 @@ struct AttnArgs {
                              // 1 = one row per (b, q head, block): row (b * Hq + h) * nblk + m
 };
 
+// One fused decode step (decode_fused.hip): the pruning state of the call,
+// V, the split partials and the output.
+struct StepArgs {
+  PruneArgs p;               // pruning state; p.idx receives the index rows
+  const void* v;
+  float* part;               // [B, Hq, nsp, D + 2] split partials (o[D], m, l)
+  float* out;                // [B, Hq, D]
+  float scale_log2;
+  int nsp;                   // splits per row
+  int ks0, ks1;              // splits [ks0, ks1) may hold kept chunks (scheduled first)
+};
+
 // Block-sparse index estimation (MInference page, "Online Dynamic Index
 // Estimation: Block-Sparse Heads (Algorithm 3)"): prefill, blocks of 64.
 struct BsArgs {
@@ -326,9 +338,20 @@ ProfSlot prof_slot(const char* name);
 // host launchers (defined in prune.hip / attn.hip)                          //
 // ------------------------------------------------------------------------- //
 hipError_t launch_prune(const PruneArgs& a, int dtype, hipStream_t stream);
+// decode: every stage up to the last stage's scoring; the last top-K is left to
+// the caller (the fused decode step).
+hipError_t launch_prune_decode_stages(const PruneArgs& a, int dtype, hipStream_t stream);
+// chunks the last stage's selection may see in one row
+int last_stage_chunks(const PruneArgs& a);
+// the fused tail of a decode step (last top-K + attention + merge); false if
+// the shape takes the separate kernels (nothing launched then)
+bool launch_decode_attend(const StepArgs& s, int sel_chunks, hipStream_t stream);
+constexpr int kStepSplitKeys = 128;   // index-row entries per workgroup of the fused tail
 // decode with remembered stages: only the stages flagged in due[] are recomputed
 hipError_t launch_prune_cached(const PruneArgs& a, const bool* due, int dtype, hipStream_t stream);
 hipError_t launch_sparse_attn(const AttnArgs& a, int dtype, hipStream_t stream);
+// merge of decode split partials a.part [B, Hq, a.n_splits, D + 2] into a.out
+void launch_decode_combine(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_block_sparse(const BsArgs& a, int dtype, hipStream_t stream);
 bool launch_prefill_mfma(const AttnArgs& a, hipStream_t stream);   // bf16, b_q = 64
 struct PruneArgs;

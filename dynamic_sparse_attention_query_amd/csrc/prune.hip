@@ -203,17 +203,18 @@ k_score_decode(PruneArgs a, int stage) {
 
 // Top-K of stage `stage - 1` fused with the SelectRep scoring of stage `stage`
 // (decode, bf16). Every workgroup of the scoring launch selects the row's kept
-// chunks of the previous stage itself from that stage's complete score list,
-// so the two steps meet at one kernel boundary instead of two; workgroup 0
-// also writes the kept starts and their count for the stages after. The
-// tournaments are those of k_score_decode.
+// chunks of the previous stage itself from that stage's complete score list
+// (select_cols, the latency-oriented selection), so the two steps meet at one
+// kernel boundary instead of two; workgroup 0 also writes the kept starts and
+// their count for the stages after. The tournaments are those of
+// k_score_decode.
 template <typename T, int D, int G, int SPEC, int E, bool PAGED>
 __global__ void __launch_bounds__(256, 2) k_topk_score_decode(PruneArgs a, int stage) {
   constexpr int EPL = D / 16;
   using Row = RowSlice<T, EPL>;
-  __shared__ SelectLds<> L;
-  __shared__ int sprev[kMaxKeptChunks];
-  __shared__ int ssel[kMaxKeptChunks];
+  __shared__ SelectColLds<kTopkWaves> L;
+  __shared__ int sprev[kFusedMaxKept];
+  __shared__ int skept[kFusedMaxKept + 64];
   __shared__ float red[16];
   const KvLayout& kv = a.kv;
   const int ps = stage - 1;                     // the stage selected here
@@ -229,9 +230,8 @@ __global__ void __launch_bounds__(256, 2) k_topk_score_decode(PruneArgs a, int s
   // this thread's keys of stage ps, the kept starts of stage ps-1, the query
   const int e = kv.seq_lens[r];
   const int nc_before = ps > 0 ? a.cnt[r * kMaxStages + ps - 1] : 0;
-  const int js = tid * E;
   uint32_t key[E];
-  load_keys<E>(a, ps, r, js, key);
+  load_keys_cols<E>(a, ps, r, key);
   if (ps > 0) load_kept_starts(a, ps - 1, r, sprev);
   Row q[G];
 #pragma unroll
@@ -242,16 +242,13 @@ __global__ void __launch_bounds__(256, 2) k_topk_score_decode(PruneArgs a, int s
   const int shp = ps > 0 ? a.lchunk[ps - 1] - lgp : 0;
   const int nc_ps = ps == 0 ? geo.n1 : nc_before << shp;
   const int kc_ps = a.keep[ps] >> lgp;
-  const int n_sel = nc_ps <= kc_ps ? nc_ps : kc_ps;
-  const bool writer = blockIdx.x == 0;
-  int32_t* out = stage_starts(a, ps, r);
-  select_row<E>(key, js, nc_ps, kc_ps, L, [&](int j, int pos) {
-    const int st = ps == 0 ? a.n_sink + (j << lgp) : sprev[j >> shp] + ((j & ((1 << shp) - 1)) << lgp);
-    ssel[pos] = st;
-    if (writer) out[pos] = st;
-  });
-  if (writer && tid == 0) record_stage(a, ps, r, n_sel, geo);
-  __syncthreads();                              // the kept starts are in ssel
+  const int n_sel = select_cols<E>(key, nc_ps, kc_ps, L, skept);
+  __syncthreads();                              // the kept chunk indices are in skept
+  if (blockIdx.x == 0) {                        // workgroup 0 records the stage's output
+    int32_t* out = stage_starts(a, ps, r);
+    for (int i = tid; i < n_sel; i += 256) out[i] = kept_start(a, ps, skept[i], sprev);
+    if (tid == 0) record_stage(a, ps, r, n_sel, geo);
+  }
 
   // stage `stage`: chunks of chunk[stage] keys tiling the kept chunks
   const int sh = lgp - a.lchunk[stage];
@@ -260,7 +257,8 @@ __global__ void __launch_bounds__(256, 2) k_topk_score_decode(PruneArgs a, int s
   if (j0 >= nc) return;
   const int j = j0 + cl;
   const bool active = j < nc;
-  const int st = ssel[min(j >> sh, n_sel - 1)] + ((j & ((1 << sh) - 1)) << a.lchunk[stage]);
+  const int st = kept_start(a, ps, skept[min(j >> sh, n_sel - 1)], sprev) +
+                 ((j & ((1 << sh) - 1)) << a.lchunk[stage]);
   float best = -INFINITY;
   if (active) best = score_group<T, D, G, SPEC, PAGED>(a, stage, b, g, li, st, q);
   if (li == 0) red[gi] = best;
@@ -418,10 +416,14 @@ static bool launch_decode_fused(const PruneArgs& a, int stage, int max_chunks, i
     // redundant work is small next to a kernel boundary (one sequence); a
     // batch takes the one-workgroup-per-row selection kernel instead
     if (static_cast<long long>(grid.x) * grid.y > kFuseMaxWorkgroups) return false;
-    const int spec = spec_of(a.chunk[stage]);
-    const char* nm = kFusedNames[stage];
     // the fused launch is for one sequence: contiguous K only
     if (a.kv.block_table) return false;
+    // kept lists held in LDS: the selected stage's and the one before it
+    const int ps = stage - 1;
+    if ((a.keep[ps] >> a.lchunk[ps]) > kFusedMaxKept) return false;
+    if (ps > 0 && (a.keep[ps - 1] >> a.lchunk[ps - 1]) > kFusedMaxKept) return false;
+    const int spec = spec_of(a.chunk[stage]);
+    const char* nm = kFusedNames[stage];
     if (sel_chunks <= kTopkThreads * 4) {
       if (spec == 8)      DSA_LAUNCH(nm, (k_topk_score_decode<T, D, G, 8, 4, false>), grid, dim3(256), st, a, stage);
       else if (spec == 4) DSA_LAUNCH(nm, (k_topk_score_decode<T, D, G, 4, 4, false>), grid, dim3(256), st, a, stage);
@@ -438,9 +440,10 @@ static bool launch_decode_fused(const PruneArgs& a, int stage, int max_chunks, i
 }
 
 // Decode: score stage 1; for every later stage, the previous stage's top-K
-// and this stage's scoring (fused where possible); the last top-K writes idx.
+// and this stage's scoring (fused where possible); the last top-K writes idx
+// (unless `last_topk` is false: the fused decode step selects it itself).
 template <typename T, int D, int G>
-static void launch_decode(const PruneArgs& a, hipStream_t st) {
+static void launch_decode(const PruneArgs& a, hipStream_t st, bool last_topk = true) {
   auto chunks_of = [&](int stage) {               // longest input list of a stage
     return stage == 0 ? a.n1max : a.keep[stage - 1] / a.chunk[stage];
   };
@@ -451,7 +454,12 @@ static void launch_decode(const PruneArgs& a, hipStream_t st) {
       launch_decode_score<T, D, G>(a, stage, chunks_of(stage), st);
     }
   }
-  launch_topk(a, a.n_stages - 1, chunks_of(a.n_stages - 1), st);
+  if (last_topk) launch_topk(a, a.n_stages - 1, chunks_of(a.n_stages - 1), st);
+}
+
+int last_stage_chunks(const PruneArgs& a) {
+  const int ls = a.n_stages - 1;
+  return ls == 0 ? a.n1max : a.keep[ls - 1] / a.chunk[ls];
 }
 
 // Decode with remembered stages: each due stage is scored from the current
@@ -544,6 +552,30 @@ void launch_score_prefill_bf16(const PruneArgs& a, int stage, int max_chunks, hi
   const dim3 grid((max_chunks + 15) / 16, a.R);
   if (a.kv.D == 128) DSA_LAUNCH(name, (k_score_prefill<uint16_t, 128>), grid, dim3(256), st, a, stage);
   else               DSA_LAUNCH(name, (k_score_prefill<uint16_t, 64>), grid, dim3(256), st, a, stage);
+}
+
+template <typename T, int D>
+static hipError_t launch_stages_typed(const PruneArgs& a, hipStream_t st) {
+  switch (a.kv.Hq / a.kv.Hkv) {
+    case 1: launch_decode<T, D, 1>(a, st, false); break;
+    case 2: launch_decode<T, D, 2>(a, st, false); break;
+    case 4: launch_decode<T, D, 4>(a, st, false); break;
+    case 8: launch_decode<T, D, 8>(a, st, false); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prune_decode_stages(const PruneArgs& a, int dtype, hipStream_t st) {
+  if (!a.kv.decode) return hipErrorInvalidValue;
+  if (dtype == 1) {
+    if (a.kv.D == 128) return launch_stages_typed<uint16_t, 128>(a, st);
+    if (a.kv.D == 64) return launch_stages_typed<uint16_t, 64>(a, st);
+  } else {
+    if (a.kv.D == 128) return launch_stages_typed<float, 128>(a, st);
+    if (a.kv.D == 64) return launch_stages_typed<float, 64>(a, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_prune(const PruneArgs& a, int dtype, hipStream_t st) {

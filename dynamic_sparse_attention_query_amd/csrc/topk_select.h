@@ -226,3 +226,185 @@ __device__ __forceinline__ void select_row(uint32_t (&key)[E], int j0, int nc, i
 }
 
 }  // namespace dsa
+
+namespace dsa {
+
+// ------------------------------------------------------------------------- //
+// Latency-oriented top-K of one row, keys in column layout                  //
+// ------------------------------------------------------------------------- //
+// The same selection as select_row (larger key first, lower index first among
+// equal keys), written for the shortest instruction stream per wave: the
+// decode kernels run it in every workgroup, on the critical path. Lane l of
+// wave w holds the keys of indices j = w*64*E + 64*x + l (x = 0 .. E-1), so
+// for a fixed x a wave's 64 keys are consecutive indices and per-column lane
+// masks (ballots) are in index order.
+//   * Every key becomes its distance below the OR of the row's keys,
+//     d = (vor - key) >> lsb, with lsb the lowest bit in which the keys differ:
+//     vor >= every key and all keys share the bits below lsb, so d is exact
+//     and ascending d is descending key.
+//     Absent keys (index >= nc) take the value 0: they are below every real
+//     key and above it in index, so while more than K real keys exist (the
+//     only case that selects) they are never kept; the first pass clamps their
+//     bin to the last one, where they cannot be the boundary.
+//   * The K-th smallest d is found by histogramming d into 2048 bins of width
+//     2^s (s just large enough for the row's varying bits) with LDS atomics,
+//     one barrier per pass, after which every wave scans the histogram by
+//     itself (lane l sums bins 32l .. 32l+31, then the boundary lane's 32
+//     bins), so sharing the result takes no further barrier. A boundary bin
+//     that is not kept whole is split again at a finer width until its width
+//     is one; the exact-score keys of the decode workloads take two passes.
+//   * The kept keys of each column are two ballots (strictly inside, equal to
+//     the threshold); a block-wide scan of the waves' counts and a running
+//     count per column give each kept key its output slot, mbcnt its place in
+//     the column. Ties at the threshold go to the lowest indices.
+// kept[0 .. min(nc, kc)) receives the kept indices in ascending order; it is
+// complete after the caller's next barrier; kept[] needs kc + 64 entries (the
+// last 64 take the writes of keys that are not kept, one per lane, so the
+// writes need no branch). Keys are 0 for absent chunks (real keys are never
+// 0). Returns the number kept.
+constexpr int kHistBins = 2048;
+
+template <int NW>
+struct SelectColLds {
+  uint32_t hist[2][kHistBins + 64];              // + one spare bin per lane (second pass)
+  uint32_t wred[2][NW];
+  uint32_t wcnt[NW];
+};
+
+template <int E, int NT = kTopkThreads>
+__device__ __forceinline__ int select_cols(const uint32_t (&key)[E], int nc, int kc, SelectColLds<NT / 64>& L,
+                                           int* kept) {
+  constexpr int NW = NT / 64;
+  constexpr uint32_t kSpare = kHistBins;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int jw = w * 64 * E + lane;                // index of column x: jw + 64 x
+  if (nc <= kc) {                                  // every chunk is kept, in index order
+    __syncthreads();                               // publishes the caller's LDS data, as below
+#pragma unroll
+    for (int x = 0; x < E; ++x)
+      if (jw + 64 * x < nc) kept[jw + 64 * x] = jw + 64 * x;
+    return nc;
+  }
+  uint32_t k[E];
+  uint32_t vand = 0xffffffffu, vor = 0u;
+#pragma unroll
+  for (int x = 0; x < E; ++x) {
+    k[x] = jw + 64 * x < nc ? key[x] : 0u;
+    vand &= k[x] ? k[x] : 0xffffffffu;
+    vor |= k[x];
+  }
+  vand = wave_and_u32(vand);
+  vor = wave_or_u32(vor);
+  if (lane == 0) {
+    L.wred[0][w] = vand;
+    L.wred[1][w] = vor;
+  }
+  {
+    constexpr int N4 = 2 * (kHistBins + 64) / 4;
+    uint4* h4 = reinterpret_cast<uint4*>(&L.hist[0][0]);
+#pragma unroll
+    for (int i = 0; i < (N4 + NT - 1) / NT; ++i)
+      if (i * NT + tid < N4) h4[i * NT + tid] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  __syncthreads();                                 // also publishes the caller's LDS data
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    vand &= L.wred[0][i];
+    vor |= L.wred[1][i];
+  }
+  const uint32_t varying = vand ^ vor;
+  const int lsb = varying ? __ffs(static_cast<int>(varying)) - 1 : 0;
+  const int bits = varying ? 32 - __clz(static_cast<int>(varying)) - lsb : 0;
+  int s = max(0, bits - 11);
+  uint32_t d[E];
+#pragma unroll
+  for (int x = 0; x < E; ++x) {
+    d[x] = (vor - k[x]) >> lsb;
+    atomicAdd(&L.hist[0][min(d[x] >> s, static_cast<uint32_t>(kHistBins - 1))], 1u);
+  }
+  __syncthreads();
+  uint32_t base = 0u;                              // lower edge (in d) of the boundary bin
+  int need = kc;                                   // keys of the boundary bin still to keep
+  bool whole = false;
+  for (int p = 0;; ++p) {
+    const uint32_t* H = L.hist[p & 1];
+    const uint4* H4 = reinterpret_cast<const uint4*>(H) + lane * 8;
+    uint32_t sl = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint4 u = H4[i];
+      sl += (u.x + u.y) + (u.z + u.w);
+    }
+    const uint32_t il = wave_incl_scan_u32(sl);
+    const int bl = __ffsll(static_cast<long long>(__ballot(il >= static_cast<uint32_t>(need)))) - 1;
+    const uint32_t above_l = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(il - sl), bl));
+    const uint32_t c = lane < 32 ? H[bl * 32 + lane] : 0u;
+    const uint32_t ic = wave_incl_scan_u32(c);
+    const int bi = __ffsll(static_cast<long long>(__ballot(above_l + ic >= static_cast<uint32_t>(need)))) - 1;
+    const int cnt_in = __builtin_amdgcn_readlane(static_cast<int>(c), bi);
+    need -= static_cast<int>(above_l) + __builtin_amdgcn_readlane(static_cast<int>(ic - c), bi);
+    base += static_cast<uint32_t>(bl * 32 + bi) << s;
+    if (cnt_in == need) { whole = true; break; }
+    if (s == 0) break;                             // the bin is the threshold value d == base
+    const uint32_t wprev = 1u << s;
+    s = max(0, s - 11);
+    uint32_t* Hn = L.hist[(p + 1) & 1];
+    if (p >= 1) {                                  // a third pass reuses the first buffer
+      __syncthreads();                             // every wave has scanned it
+      for (int i = tid; i < kHistBins; i += NT) Hn[i] = 0u;
+      __syncthreads();
+    }
+#pragma unroll
+    for (int x = 0; x < E; ++x) {
+      const uint32_t r = d[x] - base;              // wraps for keys above the bin
+      atomicAdd(&Hn[r < wprev ? r >> s : kSpare + lane], 1u);
+    }
+    __syncthreads();
+  }
+
+  // kept: d below the boundary bin (or inside it when it is kept whole), and
+  // the lowest-index `need` keys equal to the threshold d == base otherwise.
+  const int need_eq = whole ? 0 : need;
+  const uint32_t wbin = whole ? (1u << s) : 0u;    // width of the boundary bin kept whole
+  const uint32_t eqv = whole ? 0xffffffffu : base; // d of the ties (none when whole)
+  auto strict_of = [&](int x) { return d[x] < base || d[x] - base < wbin; };
+  int ns = 0, ne = 0;
+#pragma unroll
+  for (int x = 0; x < E; ++x) {
+    ns += __popcll(__ballot(strict_of(x)));
+    ne += __popcll(__ballot(d[x] == eqv));
+  }
+  if (lane == 0) L.wcnt[w] = (static_cast<uint32_t>(ns) << 16) | static_cast<uint32_t>(ne);
+  __syncthreads();
+  int cs = 0, ce = 0;                              // strict / equal keys of the waves before
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const uint32_t v = L.wcnt[i];
+    cs += i < w ? static_cast<int>(v >> 16) : 0;
+    ce += i < w ? static_cast<int>(v & 0xffffu) : 0;
+  }
+  int run = cs + min(ce, need_eq);                 // output slot of this wave's next kept key
+  int* spare = kept + kc + lane;
+#pragma unroll
+  for (int x = 0; x < E; ++x) {
+    unsigned long long t = __ballot(strict_of(x));
+    const unsigned long long e = __ballot(d[x] == eqv);
+    const int avail = need_eq - ce;
+    const int ec = __popcll(e);
+    if (avail >= ec) {
+      t |= e;
+    } else if (avail > 0) {                        // the boundary column: its lowest `avail` ties
+      unsigned long long m = e;
+      for (int i = 0; i < avail; ++i) m &= m - 1ull;
+      t |= e ^ m;
+    }
+    ce += ec;
+    const int mb = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(t >> 32),
+                                             __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(t), 0));
+    *(((t >> lane) & 1ull) ? kept + run + mb : spare) = jw + 64 * x;
+    run += __popcll(t);
+  }
+  return kc;
+}
+
+}  // namespace dsa

@@ -130,8 +130,9 @@ typedef struct {
  * rounded up to a multiple of 64; -1 if p is NULL or invalid. */
 int32_t dsa_index_width(const dsa_params* p);
 
-/* Workspace bytes for any of the three calls on this shape (p may be NULL when
- * only dsa_dense_attn is used). Returns DSA_ERR_INVALID_ARG for an invalid
+/* Workspace bytes for any of dsa_prune_select, dsa_sparse_attn,
+ * dsa_prune_attend and dsa_dense_attn on this shape (p may be NULL when only
+ * dsa_dense_attn is used). Returns DSA_ERR_INVALID_ARG for an invalid
  * shape or params. */
 dsa_status dsa_workspace_bytes(const dsa_shape* shape, const dsa_params* p, size_t* out_bytes);
 
@@ -197,6 +198,19 @@ dsa_status dsa_prune_select_cached(const dsa_shape* shape, const void* q, const 
 dsa_status dsa_sparse_attn(const dsa_shape* shape, const void* q, const void* k, const void* v,
                            const int32_t* idx, int32_t idx_width, int32_t block_q, float scale,
                            float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* One pass of the whole path: dsa_prune_select followed by dsa_sparse_attn
+ * over the rows it writes, in one call (same arguments and outputs: idx as
+ * written by dsa_prune_select, out as written by dsa_sparse_attn with
+ * block_q = p->block_q). For bf16 decode the last stage's top-K, the gathered
+ * attention and the merge of its split partials run as one kernel (every
+ * attention workgroup re-derives the kept chunks from the stage's scores),
+ * which removes two kernel boundaries from the step; the results are those of
+ * the two calls (idx bit for bit, out within rounding of the partial merge).
+ * ws: at least dsa_workspace_bytes() bytes (which covers this call). */
+dsa_status dsa_prune_attend(const dsa_shape* shape, const void* q, const void* k, const void* v,
+                            const dsa_params* p, float scale, int32_t* idx, float* out, void* ws,
+                            size_t ws_bytes, uint64_t* visited, void* stream);
 
 /* Exact causal attention over keys [0, t] for every query t. */
 dsa_status dsa_dense_attn(const dsa_shape* shape, const void* q, const void* k, const void* v,

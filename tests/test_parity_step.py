@@ -1,0 +1,161 @@
+"""GPU parity of dsa_prune_attend (pruning and attention in one call).
+
+For bf16 decode the call runs the fused tail (the last stage's top-K, the
+gathered attention and the merge of its split partials in one kernel); every
+other shape runs the separate kernels. Index rows must equal the oracle's bit
+for bit (and the two-call path's), outputs must be within the oracle
+tolerance (max-abs 1e-2, relative-L2 5e-3).
+"""
+import numpy as np
+import pytest
+import torch
+
+import helpers as H
+from dynamic_sparse_attention_query_amd import api, gen
+from dynamic_sparse_attention_query_amd.inputs import params_of, to_device
+from oracle import ref
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from dynamic_sparse_attention_query_amd import _lib
+    _lib.load()
+
+
+def step_decode(dev, p, qi=0):
+    q = dev.q[qi].contiguous()
+    kw = dict(seq_lens=dev.seq_lens, block_table=dev.block_table, t=dev.t)
+    idx, out = api.prune_attend(q, dev.k, dev.v, p, **kw)
+    torch.cuda.synchronize()
+    return idx, out
+
+
+def two_calls(dev, p, qi=0):
+    q = dev.q[qi].contiguous()
+    kw = dict(seq_lens=dev.seq_lens, block_table=dev.block_table, t=dev.t)
+    idx = api.prune_select(q, dev.k, p, **kw)
+    out = api.sparse_attn(q, dev.k, dev.v, idx, p, **kw)
+    torch.cuda.synchronize()
+    return idx, out
+
+
+def check_step(case, dev, seqs, qi=0):
+    p = params_of(case.cfg)
+    H.say(f"{case.cfg.name}: step for sequences {list(seqs)} query {qi}")
+    idx, out = step_decode(dev, p, qi)
+    idx2, out2 = two_calls(dev, p, qi)
+    idx_np, out_np = idx.cpu().numpy(), out.cpu().numpy()
+    assert np.array_equal(idx_np, idx2.cpu().numpy()), "index rows differ from the two-call path"
+    H.assert_close(out_np, out2.cpu().numpy(), "against the two-call path")
+    for b in seqs:
+        want = H.oracle_row(case, b, 0, qi)
+        assert np.array_equal(idx_np[b], want), f"seq {b}: first diff at {np.flatnonzero(idx_np[b] != want)[:5]}"
+        H.assert_close(out_np[b], H.oracle_attend(case, b, 0, want, qi)[:, 0], f"seq {b} attention")
+    return idx, out
+
+
+@pytest.fixture(scope="module")
+def c3():
+    H.say("generating c3 (1M-token decode)")
+    case = gen.make_case("c3", n_queries=3)
+    return case, to_device(case)
+
+
+def test_step_c3_decode_1m(c3):
+    case, dev = c3
+    for qi in range(3):
+        check_step(case, dev, [0], qi)
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (16, 8, 128), (64, 8, 128), (8, 2, 64)])
+def test_step_group_shapes(hq, hkv, d):
+    cfg = gen.Config(f"step-{hq}-{hkv}-{d}", "decode", 1, hq, hkv, d, 40000, "bf16", 1,
+                     (64, 16, 4), (4096, 1024, 256), 32, 256, seed=21, n_queries=2)
+    case = gen.make_case(cfg)
+    dev = to_device(case)
+    for qi in range(2):
+        check_step(case, dev, [0], qi)
+
+
+def test_step_edge_lengths_batch():
+    # lengths below the sinks, inside sinks + window, a chunk-grid tail, and
+    # long enough for every stage to prune, in one contiguous batch
+    cfg = gen.Config("step-edge", "decode", 6, 8, 2, 128, 9000, "bf16", 1,
+                     (64, 16, 4), (2048, 512, 128), 16, 64, seed=11, n_queries=2)
+    case = gen.make_case(cfg)
+    case.seq_lens[:] = [1, 7, 80, 300, 5000, 9000]
+    for b, L in enumerate(case.seq_lens):
+        case.k[b] = case.k[b].sub((slice(None), slice(0, int(L))))
+        case.v[b] = case.v[b].sub((slice(None), slice(0, int(L))))
+    dev = to_device(case)
+    for qi in range(2):
+        check_step(case, dev, range(6), qi)
+
+
+@pytest.mark.parametrize("chunk,keep", [((256,), (2048,)), ((64, 8), (4096, 1024)), ((32, 8), (0, 0)),
+                                        ((32, 8), (65536, 65536))])
+def test_step_stage_counts_and_budgets(chunk, keep):
+    # one stage (the selection runs over the stage-1 scores), two stages, zero
+    # budget (sinks and window only) and a budget above the context (dense)
+    cfg = gen.Config("step-stages", "decode", 1, 32, 8, 128, 30000, "bf16", 1, chunk, keep, 64, 1024,
+                     seed=22, n_queries=1)
+    case = gen.make_case(cfg)
+    dev = to_device(case)
+    idx, out = check_step(case, dev, [0])
+    if keep[0] >= 65536:
+        dense = api.dense_attn(dev.q[0].contiguous(), dev.k, dev.v, seq_lens=dev.seq_lens)
+        H.assert_close(out.cpu().numpy(), dense.cpu().numpy(), "full budget vs dense")
+
+
+def test_step_fp32_and_paged():
+    cfg = gen.Config("step-f32", "decode", 2, 8, 2, 64, 6000, "f32", 1, (32, 8), (1024, 256), 16, 128,
+                     seed=23, n_queries=1)
+    case = gen.make_case(cfg)
+    check_step(case, to_device(case), range(2))
+    H.say("generating a small paged ragged batch")
+    cfg = gen.CONFIGS["c4"].replace(batch=4, ragged=(9000, 30000), n_queries=1)
+    case = gen.make_case(cfg)
+    check_step(case, to_device(case), range(4))
+
+
+def test_step_prefill_matches_two_calls():
+    case = gen.make_case("c2", t=2048, keep=(512, 256, 128), n_window=128, n_needles=1)
+    dev = to_device(case)
+    p = params_of(case.cfg)
+    idx, out = api.prune_attend(dev.q, dev.k, dev.v, p)
+    idx2 = api.prune_select(dev.q, dev.k, p)
+    out2 = api.sparse_attn(dev.q, dev.k, dev.v, idx2, p)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2)
+    assert torch.equal(out, out2)
+
+
+def test_step_graph_replays_fresh_queries(c3):
+    """Graph replays of the fused step (counters cleared inside the step, no
+    memset) equal eager calls bit for bit, step after step."""
+    case, dev = c3
+    p = params_of(case.cfg)
+    q_buf = dev.q[0].contiguous().clone()
+    idx_buf = torch.empty(ref.index_width(H.oracle_params(case.cfg)), dtype=torch.int32, device="cuda")
+    out_buf = torch.empty_like(q_buf, dtype=torch.float32)
+    kw = dict(seq_lens=dev.seq_lens)
+    api.prune_attend(q_buf, dev.k, dev.v, p, idx=idx_buf, out=out_buf, **kw)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        api.prune_attend(q_buf, dev.k, dev.v, p, idx=idx_buf, out=out_buf, **kw)
+    torch.cuda.synchronize()
+    for rep in range(6):
+        qi = rep % 3
+        q_buf.copy_(dev.q[qi][...])
+        g.replay()
+        torch.cuda.synchronize()
+        gi, go = idx_buf.clone(), out_buf.clone()
+        ei, eo = api.prune_attend(dev.q[qi].contiguous(), dev.k, dev.v, p, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(gi.view(-1), ei.view(-1)), f"replay {rep}: index rows differ"
+        assert torch.equal(go, eo), f"replay {rep}: outputs differ"
