@@ -20,11 +20,12 @@ DSA_PREFILL, DSA_DECODE = 0, 1
 MAX_STAGES = 4
 
 EXPORTS = ("dsa_index_width", "dsa_workspace_bytes", "dsa_prune_select", "dsa_sparse_attn", "dsa_prune_attend",
+
            "dsa_dense_attn", "dsa_mask_cache_bytes", "dsa_cached_index_width", "dsa_prune_select_cached",
            "dsa_block_sparse_index_width", "dsa_block_sparse_workspace_bytes", "dsa_block_sparse_select",
            "dsa_sparse_attn_heads", "dsa_vertical_slash_index_width", "dsa_vertical_slash_workspace_bytes",
            "dsa_vertical_slash_select", "dsa_prune_rope_workspace_bytes", "dsa_prune_select_rope",
-           "dsa_profile_begin", "dsa_profile_end", "dsa_status_str", "dsa_last_error")
+           "dsa_check_decode_inputs", "dsa_profile_begin", "dsa_profile_end", "dsa_status_str", "dsa_last_error")
 
 
 class CParams(ctypes.Structure):
@@ -79,6 +80,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dsa_prune_attend.argtypes = [ctypes.POINTER(CShape), vp, vp, vp, ctypes.POINTER(CParams), ctypes.c_float,
                                      vp, vp, vp, sz, vp, vp]
     lib.dsa_prune_attend.restype = ctypes.c_int
+    lib.dsa_check_decode_inputs.argtypes = [ctypes.POINTER(CShape), vp, vp, ctypes.c_int64]
+    lib.dsa_check_decode_inputs.restype = ctypes.c_int
     lib.dsa_prune_select.restype = ctypes.c_int
     lib.dsa_mask_cache_bytes.argtypes = [ctypes.POINTER(CShape), ctypes.POINTER(CParams), ctypes.POINTER(sz)]
     lib.dsa_mask_cache_bytes.restype = ctypes.c_int
@@ -213,6 +216,17 @@ def prune_attend_raw(shape: Shape, q: int, k: int, v: int, p: Params, scale: flo
     cs, cp = shape.c(), p.c()
     _check(load().dsa_prune_attend(ctypes.byref(cs), q, k, v, ctypes.byref(cp), scale, idx, out, ws, ws_bytes,
                                    visited or None, stream or None))
+
+
+def check_decode_inputs(shape: Shape, seq_lens, block_table=None, n_pages: int = 0):
+    """Checked mode: validate host copies of seq_lens (int32 [B]) and the
+    block table (int32 [B, max_pages]); raises DsaError on the first bad entry."""
+    import numpy as np
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    bt = None if block_table is None else np.ascontiguousarray(block_table, dtype=np.int32)
+    cs = shape.c()
+    _check(load().dsa_check_decode_inputs(ctypes.byref(cs), sl.ctypes.data,
+                                          bt.ctypes.data if bt is not None else None, int(n_pages)))
 
 
 def mask_cache_bytes(shape: Shape, p: Params) -> int:

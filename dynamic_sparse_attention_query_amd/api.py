@@ -11,14 +11,20 @@ k/v [B,Hkv,t,d] or page pools [n_pages,Hkv,page_size,d] with block_table
 """
 from __future__ import annotations
 
-from typing import Dict, Optional, Tuple
+from typing import Dict, List, Optional, Tuple
 
 import torch
 
 from . import _lib
 from ._lib import DSA_BF16, DSA_DECODE, DSA_F32, DSA_PREFILL, Params, Shape
 
+# Workspaces: one per (device, stream), so calls on different streams never
+# share scratch memory. A workspace that is too small is replaced by a larger
+# one, but the old buffer is kept alive (never returned to the allocator): a
+# HIP graph captured earlier may still hold its address. Callers that want
+# full control pass their own buffer (ws=, at least workspace_bytes()).
 _WS: Dict[Tuple[int, int], torch.Tensor] = {}
+_RETIRED: List[torch.Tensor] = []
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -74,16 +80,34 @@ def make_shape(q: torch.Tensor, k: torch.Tensor, *, seq_lens: Optional[torch.Ten
                  seq_lens.data_ptr(), block_table.data_ptr(), ps, maxp)
 
 
-def workspace(shape: Shape, params: Optional[Params], device: torch.device) -> Tuple[int, int]:
-    """A per-device scratch buffer large enough for this call (grown on demand)."""
-    return _scratch(_lib.workspace_bytes(shape, params), device)
+def workspace_bytes(shape: Shape, params: Optional[Params]) -> int:
+    """Bytes of the scratch buffer the calls on this shape need."""
+    return _lib.workspace_bytes(shape, params)
 
 
-def _scratch(nbytes: int, device: torch.device) -> Tuple[int, int]:
-    key = (device.index if device.index is not None else torch.cuda.current_device(), 0)
+def workspace(shape: Shape, params: Optional[Params], device: torch.device,
+              ws: Optional[torch.Tensor] = None) -> Tuple[int, int]:
+    """Scratch buffer for one call: the caller's `ws`, else the workspace of
+    (device, current stream), grown on demand."""
+    return _scratch(_lib.workspace_bytes(shape, params), device, ws)
+
+
+def _scratch(nbytes: int, device: torch.device, ws: Optional[torch.Tensor] = None) -> Tuple[int, int]:
+    if ws is not None:
+        if not ws.is_cuda or not ws.is_contiguous():
+            raise ValueError("ws must be a contiguous GPU tensor")
+        size = ws.numel() * ws.element_size()
+        if size < nbytes:
+            raise ValueError(f"ws holds {size} bytes; this call needs {nbytes}")
+        return ws.data_ptr(), size
+    dev = device.index if device.index is not None else torch.cuda.current_device()
+    key = (dev, torch.cuda.current_stream(dev).cuda_stream)
     buf = _WS.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        if buf is not None:
+            _RETIRED.append(buf)
+        grow = 0 if buf is None else 2 * buf.numel()
+        buf = torch.empty(max(nbytes, grow, 256), dtype=torch.uint8, device=device)
         _WS[key] = buf
     return buf.data_ptr(), buf.numel()
 
@@ -95,7 +119,7 @@ def _stream() -> int:
 def prune_select(q: torch.Tensor, k: torch.Tensor, params: Params, *,
                  seq_lens: Optional[torch.Tensor] = None, block_table: Optional[torch.Tensor] = None,
                  t: Optional[int] = None, out: Optional[torch.Tensor] = None,
-                 visited: Optional[torch.Tensor] = None) -> torch.Tensor:
+                 visited: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     shape = make_shape(q, k, seq_lens=seq_lens, block_table=block_table, t=t)
     L = _lib.index_width(params)
     if L < 0:
@@ -105,13 +129,13 @@ def prune_select(q: torch.Tensor, k: torch.Tensor, params: Params, *,
         out = torch.empty(rows * L, dtype=torch.int32, device=q.device)
     if out.numel() != rows * L or out.dtype != torch.int32:
         raise ValueError("idx buffer has the wrong size or dtype")
-    ws, wsb = workspace(shape, params, q.device)
+    wsp, wsb = workspace(shape, params, q.device, ws)
     vis = 0
     if visited is not None:
         if visited.dtype != torch.int64 or visited.numel() < len(params.chunk):
             raise ValueError("visited must be int64 with one entry per stage")
         vis = visited.data_ptr()
-    _lib.prune_select_raw(shape, q.data_ptr(), k.data_ptr(), params, out.data_ptr(), ws, wsb, vis, _stream())
+    _lib.prune_select_raw(shape, q.data_ptr(), k.data_ptr(), params, out.data_ptr(), wsp, wsb, vis, _stream())
     if shape.mode == DSA_DECODE:
         return out.view(shape.batch, L)
     return out.view(shape.batch, shape.t // params.block_q, L)
@@ -120,7 +144,8 @@ def prune_select(q: torch.Tensor, k: torch.Tensor, params: Params, *,
 def prune_attend(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, params: Params, *, scale: float = 0.0,
                  seq_lens: Optional[torch.Tensor] = None, block_table: Optional[torch.Tensor] = None,
                  t: Optional[int] = None, idx: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                 visited: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                 visited: Optional[torch.Tensor] = None,
+                 ws: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """prune_select followed by sparse_attn in one call: (idx, out)."""
     shape = make_shape(q, k, seq_lens=seq_lens, block_table=block_table, t=t)
     _need(v, "v")
@@ -136,17 +161,29 @@ def prune_attend(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, params: Para
         raise ValueError("idx buffer has the wrong size or dtype")
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-    ws, wsb = workspace(shape, params, q.device)
+    wsp, wsb = workspace(shape, params, q.device, ws)
     vis = 0
     if visited is not None:
         if visited.dtype != torch.int64 or visited.numel() < len(params.chunk):
             raise ValueError("visited must be int64 with one entry per stage")
         vis = visited.data_ptr()
     _lib.prune_attend_raw(shape, q.data_ptr(), k.data_ptr(), v.data_ptr(), params, scale, idx.data_ptr(),
-                          out.data_ptr(), ws, wsb, vis, _stream())
+                          out.data_ptr(), wsp, wsb, vis, _stream())
     if shape.mode == DSA_DECODE:
         return idx.view(shape.batch, L), out
     return idx.view(shape.batch, shape.t // params.block_q, L), out
+
+
+def check_decode_inputs(q: torch.Tensor, k: torch.Tensor, *, seq_lens: torch.Tensor,
+                        block_table: Optional[torch.Tensor] = None, t: Optional[int] = None) -> None:
+    """Checked mode: copies seq_lens and the block table to the host (this
+    synchronises with their producers) and validates every length and every
+    page id a length reaches against the K pool; raises DsaError naming the
+    first bad entry."""
+    shape = make_shape(q, k, seq_lens=seq_lens, block_table=block_table, t=t)
+    n_pages = k.shape[0] if block_table is not None else 0
+    _lib.check_decode_inputs(shape, seq_lens.cpu().numpy(),
+                             block_table.cpu().numpy() if block_table is not None else None, n_pages)
 
 
 class MaskCache:
@@ -180,7 +217,7 @@ class MaskCache:
 def prune_select_cached(q: torch.Tensor, k: torch.Tensor, cache: MaskCache, step: int, *,
                         seq_lens: torch.Tensor, block_table: Optional[torch.Tensor] = None,
                         t: Optional[int] = None, out: Optional[torch.Tensor] = None,
-                        visited: Optional[torch.Tensor] = None) -> torch.Tensor:
+                        visited: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     """One decode step of pruning with remembered stages: [B, cache.width] rows."""
     shape = make_shape(q, k, seq_lens=seq_lens, block_table=block_table, t=t)
     params = cache.params
@@ -189,14 +226,14 @@ def prune_select_cached(q: torch.Tensor, k: torch.Tensor, cache: MaskCache, step
         out = torch.empty(shape.batch * L, dtype=torch.int32, device=q.device)
     if out.numel() != shape.batch * L or out.dtype != torch.int32:
         raise ValueError("idx buffer has the wrong size or dtype")
-    ws, wsb = workspace(shape, params, q.device)
+    wsp, wsb = workspace(shape, params, q.device, ws)
     vis = 0
     if visited is not None:
         if visited.dtype != torch.int64 or visited.numel() < len(params.chunk):
             raise ValueError("visited must be int64 with one entry per stage")
         vis = visited.data_ptr()
     _lib.prune_select_cached_raw(shape, q.data_ptr(), k.data_ptr(), params, cache.refresh, step,
-                                 cache.buf.data_ptr(), cache.buf.numel(), out.data_ptr(), L, ws, wsb, vis,
+                                 cache.buf.data_ptr(), cache.buf.numel(), out.data_ptr(), L, wsp, wsb, vis,
                                  _stream())
     return out.view(shape.batch, L)
 
@@ -204,7 +241,7 @@ def prune_select_cached(q: torch.Tensor, k: torch.Tensor, cache: MaskCache, step
 def sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor, params: Params, *,
                 scale: float = 0.0, seq_lens: Optional[torch.Tensor] = None,
                 block_table: Optional[torch.Tensor] = None, t: Optional[int] = None,
-                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Attention over the index rows written by prune_select with the same params."""
     shape = make_shape(q, k, seq_lens=seq_lens, block_table=block_table, t=t)
     _need(v, "v")
@@ -215,21 +252,22 @@ def sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Te
         raise TypeError("idx must be int32")
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-    ws, wsb = workspace(shape, params, q.device)
+    wsp, wsb = workspace(shape, params, q.device, ws)
     _lib.sparse_attn_raw(shape, q.data_ptr(), k.data_ptr(), v.data_ptr(), idx.data_ptr(), idx.shape[-1],
-                         params.block_q, scale, out.data_ptr(), ws, wsb, _stream())
+                         params.block_q, scale, out.data_ptr(), wsp, wsb, _stream())
     return out
 
 
 def dense_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: float = 0.0,
                seq_lens: Optional[torch.Tensor] = None, block_table: Optional[torch.Tensor] = None,
-               t: Optional[int] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+               t: Optional[int] = None, out: Optional[torch.Tensor] = None,
+               ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     shape = make_shape(q, k, seq_lens=seq_lens, block_table=block_table, t=t)
     _need(v, "v")
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-    ws, wsb = workspace(shape, None, q.device)
-    _lib.dense_attn_raw(shape, q.data_ptr(), k.data_ptr(), v.data_ptr(), scale, out.data_ptr(), ws, wsb,
+    wsp, wsb = workspace(shape, None, q.device, ws)
+    _lib.dense_attn_raw(shape, q.data_ptr(), k.data_ptr(), v.data_ptr(), scale, out.data_ptr(), wsp, wsb,
                         _stream())
     return out
 
@@ -238,7 +276,7 @@ def dense_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: floa
 # block-sparse heads                                                          #
 # --------------------------------------------------------------------------- #
 def block_sparse_select(q: torch.Tensor, k: torch.Tensor, k_blocks: int, *,
-                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                        out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Per-head block index estimation (prefill): [B, Hq, T/64, 64*k_blocks] rows."""
     shape = make_shape(q, k)
     if shape.mode != DSA_PREFILL:
@@ -250,8 +288,8 @@ def block_sparse_select(q: torch.Tensor, k: torch.Tensor, k_blocks: int, *,
         out = torch.empty(n, dtype=torch.int32, device=q.device)
     if out.numel() != n or out.dtype != torch.int32 or not out.is_contiguous():
         raise ValueError("idx buffer has the wrong size, dtype or layout")
-    ws, wsb = _scratch(_lib.block_sparse_workspace_bytes(shape, k_blocks), q.device)
-    _lib.block_sparse_select_raw(shape, q.data_ptr(), k.data_ptr(), k_blocks, out.data_ptr(), ws, wsb, _stream())
+    wsp, wsb = _scratch(_lib.block_sparse_workspace_bytes(shape, k_blocks), q.device, ws)
+    _lib.block_sparse_select_raw(shape, q.data_ptr(), k.data_ptr(), k_blocks, out.data_ptr(), wsp, wsb, _stream())
     return out.view(shape.batch, shape.hq, nblk, L)
 
 
@@ -278,7 +316,8 @@ def sparse_attn_heads(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: to
 # vertical-slash heads                                                        #
 # --------------------------------------------------------------------------- #
 def vertical_slash_select(q: torch.Tensor, k: torch.Tensor, k_v: int, k_s: int, *,
-                          out: Optional[torch.Tensor] = None, return_lines: bool = False):
+                          out: Optional[torch.Tensor] = None, return_lines: bool = False,
+                          ws: Optional[torch.Tensor] = None):
     """Per-head vertical-slash index estimation (prefill, bf16): rows
     [B, Hq, T/64, L]; with return_lines also the kept columns [B, Hq, k_v] and
     offsets [B, Hq, k_s]."""
@@ -294,10 +333,10 @@ def vertical_slash_select(q: torch.Tensor, k: torch.Tensor, k_v: int, k_s: int, 
         raise ValueError("idx buffer has the wrong size, dtype or layout")
     cols = torch.empty((shape.batch, shape.hq, max(k_v, 1)), dtype=torch.int32, device=q.device) if return_lines else None
     offs = torch.empty((shape.batch, shape.hq, k_s), dtype=torch.int32, device=q.device) if return_lines else None
-    ws, wsb = _scratch(_lib.vertical_slash_workspace_bytes(shape, k_v, k_s), q.device)
+    wsp, wsb = _scratch(_lib.vertical_slash_workspace_bytes(shape, k_v, k_s), q.device, ws)
     _lib.vertical_slash_select_raw(shape, q.data_ptr(), k.data_ptr(), k_v, k_s, out.data_ptr(),
                                    cols.data_ptr() if cols is not None else 0,
-                                   offs.data_ptr() if offs is not None else 0, ws, wsb, _stream())
+                                   offs.data_ptr() if offs is not None else 0, wsp, wsb, _stream())
     idx = out.view(shape.batch, shape.hq, nblk, L)
     if return_lines:
         return idx, cols[..., :k_v], offs
@@ -320,7 +359,7 @@ def rope_style_for_layer(layer: int, n_chunk_indexed: int = 3) -> str:
 def prune_select_rope(q: torch.Tensor, k: torch.Tensor, params: Params, base: float, *,
                       seq_lens: Optional[torch.Tensor] = None, block_table: Optional[torch.Tensor] = None,
                       t: Optional[int] = None, out: Optional[torch.Tensor] = None,
-                      style: str = "relative") -> torch.Tensor:
+                      style: str = "relative", ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     """prune_select with RoPE inside SelectRep (q, k taken before any rotary
     embedding); style "relative" or "chunk_indexed"."""
     styles = {"relative": _lib.DSA_ROPE_RELATIVE, "chunk_indexed": _lib.DSA_ROPE_CHUNK_INDEXED}
@@ -335,8 +374,8 @@ def prune_select_rope(q: torch.Tensor, k: torch.Tensor, params: Params, base: fl
         out = torch.empty(rows * L, dtype=torch.int32, device=q.device)
     if out.numel() != rows * L or out.dtype != torch.int32:
         raise ValueError("idx buffer has the wrong size or dtype")
-    ws, wsb = _scratch(_lib.prune_rope_workspace_bytes(shape, params, styles[style], base), q.device)
-    _lib.prune_select_rope_raw(shape, q.data_ptr(), k.data_ptr(), params, base, out.data_ptr(), ws, wsb, _stream(),
+    wsp, wsb = _scratch(_lib.prune_rope_workspace_bytes(shape, params, styles[style], base), q.device, ws)
+    _lib.prune_select_rope_raw(shape, q.data_ptr(), k.data_ptr(), params, base, out.data_ptr(), wsp, wsb, _stream(),
                                style=styles[style])
     if shape.mode == DSA_DECODE:
         return out.view(shape.batch, L)

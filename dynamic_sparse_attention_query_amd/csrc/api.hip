@@ -185,6 +185,8 @@ dsa_status run_attn(const dsa_shape* s, const void* q, const void* k, const void
   return DSA_OK;
 }
 
+
+
 }  // namespace
 
 extern "C" {
@@ -284,6 +286,64 @@ long long cached_width_ll(const dsa_params* p, long long max_growth) {
                       p->chunk[0] - 1 + max_growth;
   return (n + 63) / 64 * 64;
 }
+
+// Validation of dsa_prune_attend; fills
+// the workspace layout of the call.
+dsa_status check_prune_attend(const dsa_shape* s, const void* q, const void* k, const void* v,
+                              const dsa_params* p, const int32_t* idx, const float* out, StepLayout* lay) {
+  dsa_status st = check_shape(s);
+  if (st != DSA_OK) return st;
+  st = check_params(s, p);
+  if (st != DSA_OK) return st;
+  if (!q || !k || !v || !idx || !out) return fail(DSA_ERR_INVALID_ARG, "q, k, v, idx and out must be non-NULL");
+  if (index_width_ll(p) > (1LL << 30)) return fail(DSA_ERR_INVALID_ARG, "index width overflows");
+  *lay = step_layout(s, p);
+  if (lay->pl.maxNC > 32768)
+    return fail(DSA_ERR_UNSUPPORTED, "a stage would score %lld chunks per row (limit 32768)", lay->pl.maxNC);
+  return DSA_OK;
+}
+
+// The launches of one prune-and-attend call on a validated shape and a
+// workspace of at least lay.bytes bytes.
+dsa_status run_prune_attend(const dsa_shape* s, const void* q, const void* k, const void* v, const dsa_params* p,
+                            float scale, int32_t* idx, float* out, void* ws, const StepLayout& lay,
+                            uint64_t* visited, void* stream) {
+  const long long L = index_width_ll(p);
+  char* wsc = static_cast<char*>(ws);
+  dsa::PruneArgs a = prune_args(s, q, k, p, idx, L, lay.pl, ws, visited);
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const float sc = scale > 0.f ? scale : 1.0f / std::sqrt(static_cast<float>(s->d));
+  hipError_t err = hipSuccess;
+  bool fused = false;
+  if (s->mode == DSA_DECODE && s->dtype == DSA_BF16) {
+    err = dsa::launch_prune_decode_stages(a, s->dtype, hs);
+    if (err != hipSuccess) return fail(DSA_ERR_HIP, "prune launch failed: %s", hipGetErrorString(err));
+    dsa::StepArgs sa{};
+    sa.p = a;
+    sa.v = v;
+    sa.part = reinterpret_cast<float*>(wsc + lay.off_part);
+    sa.out = out;
+    sa.scale_log2 = sc * 1.4426950408889634f;
+    sa.nsp = static_cast<int>(lay.nsp);
+    {
+      const int ls = p->n_stages - 1;
+      const long long kept_hi = static_cast<long long>(p->n_sink) + p->keep[ls];   // most kept entries
+      sa.ks0 = std::min<int>(sa.nsp, p->n_sink / dsa::kStepSplitKeys);
+      sa.ks1 = static_cast<int>(std::min<long long>(sa.nsp, (kept_hi + dsa::kStepSplitKeys - 1) / dsa::kStepSplitKeys));
+      sa.ks1 = std::max(sa.ks1, sa.ks0);
+    }
+    fused = dsa::launch_decode_attend(sa, dsa::last_stage_chunks(a), hs);
+    if (!fused) dsa::launch_topk(a, p->n_stages - 1, dsa::last_stage_chunks(a), hs);
+    err = hipGetLastError();
+  } else {
+    err = dsa::launch_prune(a, s->dtype, hs);
+  }
+  if (err != hipSuccess) return fail(DSA_ERR_HIP, "prune launch failed: %s", hipGetErrorString(err));
+  if (fused) return DSA_OK;
+  return run_attn(s, q, k, v, idx, static_cast<int32_t>(L), p->block_q, scale, out, wsc + lay.off_part,
+                  lay.bytes - lay.off_part, stream);
+}
+
 
 }  // namespace
 
@@ -394,51 +454,38 @@ dsa_status dsa_prune_attend(const dsa_shape* s, const void* q, const void* k, co
                             const dsa_params* p, float scale, int32_t* idx, float* out, void* ws,
                             size_t ws_bytes, uint64_t* visited, void* stream) {
   g_err[0] = 0;
-  dsa_status st = check_shape(s);
+  StepLayout lay{};
+  dsa_status st = check_prune_attend(s, q, k, v, p, idx, out, &lay);
   if (st != DSA_OK) return st;
-  st = check_params(s, p);
-  if (st != DSA_OK) return st;
-  if (!q || !k || !v || !idx || !out) return fail(DSA_ERR_INVALID_ARG, "q, k, v, idx and out must be non-NULL");
-  const long long L = index_width_ll(p);
-  if (L > (1LL << 30)) return fail(DSA_ERR_INVALID_ARG, "index width overflows");
-  const StepLayout lay = step_layout(s, p);
-  if (lay.pl.maxNC > 32768)
-    return fail(DSA_ERR_UNSUPPORTED, "a stage would score %lld chunks per row (limit 32768)", lay.pl.maxNC);
   if (!ws || ws_bytes < lay.bytes)
     return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, lay.bytes);
-  char* wsc = static_cast<char*>(ws);
-  dsa::PruneArgs a = prune_args(s, q, k, p, idx, L, lay.pl, ws, visited);
-  const hipStream_t hs = static_cast<hipStream_t>(stream);
-  const float sc = scale > 0.f ? scale : 1.0f / std::sqrt(static_cast<float>(s->d));
-  hipError_t err = hipSuccess;
-  bool fused = false;
-  if (s->mode == DSA_DECODE && s->dtype == DSA_BF16) {
-    err = dsa::launch_prune_decode_stages(a, s->dtype, hs);
-    if (err != hipSuccess) return fail(DSA_ERR_HIP, "prune launch failed: %s", hipGetErrorString(err));
-    dsa::StepArgs sa{};
-    sa.p = a;
-    sa.v = v;
-    sa.part = reinterpret_cast<float*>(wsc + lay.off_part);
-    sa.out = out;
-    sa.scale_log2 = sc * 1.4426950408889634f;
-    sa.nsp = static_cast<int>(lay.nsp);
-    {
-      const int ls = p->n_stages - 1;
-      const long long kept_hi = static_cast<long long>(p->n_sink) + p->keep[ls];   // most kept entries
-      sa.ks0 = std::min<int>(sa.nsp, p->n_sink / dsa::kStepSplitKeys);
-      sa.ks1 = static_cast<int>(std::min<long long>(sa.nsp, (kept_hi + dsa::kStepSplitKeys - 1) / dsa::kStepSplitKeys));
-      sa.ks1 = std::max(sa.ks1, sa.ks0);
+  return run_prune_attend(s, q, k, v, p, scale, idx, out, ws, lay, visited, stream);
+}
+
+dsa_status dsa_check_decode_inputs(const dsa_shape* s, const int32_t* seq_lens, const int32_t* block_table,
+                                   int64_t n_pages) {
+  g_err[0] = 0;
+  dsa_status st = check_shape(s);
+  if (st != DSA_OK) return st;
+  if (s->mode != DSA_DECODE) return fail(DSA_ERR_INVALID_ARG, "checked mode covers decode shapes");
+  if (!seq_lens) return fail(DSA_ERR_INVALID_ARG, "seq_lens (host copy) is NULL");
+  for (int b = 0; b < s->batch; ++b)
+    if (seq_lens[b] < 1 || seq_lens[b] > s->t)
+      return fail(DSA_ERR_INVALID_ARG, "seq_lens[%d] = %d is not in [1, t = %d]", b, seq_lens[b], s->t);
+  if (s->block_table) {
+    if (!block_table) return fail(DSA_ERR_INVALID_ARG, "a paged shape needs the block table (host copy)");
+    if (n_pages < 1) return fail(DSA_ERR_INVALID_ARG, "n_pages = %lld must be >= 1", static_cast<long long>(n_pages));
+    for (int b = 0; b < s->batch; ++b) {
+      const long long used = (static_cast<long long>(seq_lens[b]) + s->page_size - 1) / s->page_size;
+      for (long long i = 0; i < used; ++i) {
+        const int32_t id = block_table[static_cast<size_t>(b) * s->max_pages + i];
+        if (id < 0 || id >= n_pages)
+          return fail(DSA_ERR_INVALID_ARG, "block_table[%d][%lld] = %d is not a page of the pool [0, %lld)", b, i, id,
+                      static_cast<long long>(n_pages));
+      }
     }
-    fused = dsa::launch_decode_attend(sa, dsa::last_stage_chunks(a), hs);
-    if (!fused) dsa::launch_topk(a, p->n_stages - 1, dsa::last_stage_chunks(a), hs);
-    err = hipGetLastError();
-  } else {
-    err = dsa::launch_prune(a, s->dtype, hs);
   }
-  if (err != hipSuccess) return fail(DSA_ERR_HIP, "prune launch failed: %s", hipGetErrorString(err));
-  if (fused) return DSA_OK;
-  return run_attn(s, q, k, v, idx, static_cast<int32_t>(L), p->block_q, scale, out, wsc + lay.off_part,
-                  lay.bytes - lay.off_part, stream);
+  return DSA_OK;
 }
 
 dsa_status dsa_dense_attn(const dsa_shape* s, const void* q, const void* k, const void* v, float scale,

@@ -27,7 +27,7 @@ __global__ void __launch_bounds__(256) k_decode_partial(AttnArgs a) {
   constexpr int NO = (G * D + 255) / 256;
   const KvLayout& kv = a.kv;
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int Tb = kv.seq_lens[b];
+  const int Tb = seq_len_of(kv, b);
   const int tq = Tb - 1;
   const int tid = threadIdx.x, gi = tid >> 4, li = tid & 15, lane = tid & 63, w = tid >> 6;
   __shared__ float sv[64][D + 4];
@@ -194,7 +194,7 @@ __global__ void __launch_bounds__(kCombineThreads) k_decode_combine(AttnArgs a) 
     float ot = 0.f;
 #pragma unroll
     for (int x = 0; x < SG; ++x) ot += so[x][dd];
-    a.out[(static_cast<size_t>(b) * a.kv.Hq + h) * D + dd] = ot / Ltot;
+    a.out[(static_cast<size_t>(b) * a.kv.Hq + h) * D + dd] = Ltot > 0.f ? ot / Ltot : 0.f;   // no visible key: 0
   }
 }
 
@@ -295,7 +295,7 @@ __global__ void __launch_bounds__(256) k_prefill_generic(AttnArgs a) {
     }
   }
   float* out = a.out + ((static_cast<size_t>(b) * kv.Hq + h) * kv.T + tq) * D;
-  for (int j = 0; j < DPT; ++j) out[sub + TPR * j] = o[j] / lrun;
+  for (int j = 0; j < DPT; ++j) out[sub + TPR * j] = lrun > 0.f ? o[j] / lrun : 0.f;   // no visible key: 0
 }
 
 // ------------------------------------------------------------------------- //

@@ -306,7 +306,7 @@ __global__ void __launch_bounds__(64 * NH * QH) k_prefill_mfma(AttnArgs a) {
 #undef DSA_LOAD_TILE
 
   // out[b, h, t, d] = O^T[d, t] / l
-  const float inv = 1.0f / lrun;
+  const float inv = lrun > 0.f ? 1.0f / lrun : 0.f;   // no visible key: output 0
   float* orow = a.out + ((static_cast<size_t>(b) * kv.Hq + h) * kv.T + q0 + l32) * D;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
@@ -569,7 +569,7 @@ __global__ void __launch_bounds__(64 * NH * QH, 2) k_prefill_mfma_lds(AttnArgs a
     if (ti + 1 < n_tiles) step(ti + 1, sk1, sv1, spos1, sflag1, sk0, sv0, spos0, sflag0);
   }
 
-  const float inv = 1.0f / lrun;
+  const float inv = lrun > 0.f ? 1.0f / lrun : 0.f;   // no visible key: output 0
   float* orow = a.out + ((static_cast<size_t>(b) * kv.Hq + h) * kv.T + q0 + l32) * D;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
@@ -812,7 +812,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
   __builtin_amdgcn_s_waitcnt(0);                  // no load into LDS outlives the workgroup
 
-  const float inv = 1.0f / lrun;
+  const float inv = lrun > 0.f ? 1.0f / lrun : 0.f;   // no visible key: output 0
   float* orow = a.out + ((static_cast<size_t>(b) * kv.Hq + h) * kv.T + q0 + l32) * D;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
@@ -1034,7 +1034,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
   __builtin_amdgcn_s_waitcnt(0);                  // no load into LDS outlives the workgroup
 
-  const float inv = 1.0f / lrun;
+  const float inv = lrun > 0.f ? 1.0f / lrun : 0.f;   // no visible key: output 0
   float* orow = a.out + ((static_cast<size_t>(b) * kv.Hq + h) * kv.T + q0 + l32) * D;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)

@@ -71,7 +71,7 @@ __global__ void __launch_bounds__(256, 2) k_decode_attend(StepArgs s) {
   const T* V = static_cast<const T*>(s.v);
 
   // row geometry of the last stage (uniform over the row's workgroups)
-  const int e = kv.seq_lens[b];
+  const int e = seq_len_of(kv, b);
   const int ls = a.n_stages - 1;
   const int lg = a.lchunk[ls];
   const int shp = ls > 0 ? a.lchunk[ls - 1] - lg : 0;

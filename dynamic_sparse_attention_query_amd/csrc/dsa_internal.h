@@ -126,11 +126,21 @@ __device__ __forceinline__ Geo make_geo(int s, int e, int n_sink, int n_window, 
   return g;
 }
 
+// Context length of decode sequence b, clamped to [0, T]: a length above the
+// capacity the launch was sized for would index past the K/V rows (or the
+// block table) and past the chunk lists; 0 makes an empty row (every index
+// entry -1, output 0). Out-of-range lengths are caller errors that the
+// checked mode (dsa_check_decode_inputs) reports; the clamp keeps them in
+// bounds.
+__device__ __forceinline__ int seq_len_of(const KvLayout& kv, int b) {
+  return min(max(kv.seq_lens[b], 0), kv.T);
+}
+
 // Query block bounds of row r (decode: the last position of sequence r).
 __device__ __forceinline__ void row_bounds(const KvLayout& kv, int r, int& b, int& s, int& e) {
   if (kv.decode) {
     b = r;
-    e = kv.seq_lens[r];
+    e = seq_len_of(kv, r);
     s = e - 1;
   } else {
     b = r / kv.nblk;

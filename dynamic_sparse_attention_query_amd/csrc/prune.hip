@@ -167,7 +167,7 @@ k_score_decode(PruneArgs a, int stage) {
   // checks that use them: the sequence length, the previous stage's kept
   // count, this chunk's start (read within the start list for every j of
   // the grid) and the query rows.
-  const int e = kv.seq_lens[r];
+  const int e = seq_len_of(kv, r);
   int nc_prev = 0, st;
   if (stage == 0) {
     st = a.n_sink + (j << a.lchunk[0]);
@@ -228,7 +228,7 @@ __global__ void __launch_bounds__(256, 2) k_topk_score_decode(PruneArgs a, int s
 
   // independent loads first: sequence length, the count before stage ps,
   // this thread's keys of stage ps, the kept starts of stage ps-1, the query
-  const int e = kv.seq_lens[r];
+  const int e = seq_len_of(kv, r);
   const int nc_before = ps > 0 ? a.cnt[r * kMaxStages + ps - 1] : 0;
   uint32_t key[E];
   load_keys_cols<E>(a, ps, r, key);

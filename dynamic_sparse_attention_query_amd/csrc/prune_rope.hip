@@ -239,7 +239,7 @@ k_score_decode_rt(PruneArgs a, int stage, const uint16_t* ql_all, const uint16_t
   const int j = j0 + cl;
   __shared__ float red[16];
 
-  const int e = kv.seq_lens[r];
+  const int e = seq_len_of(kv, r);
   int nc_prev = 0, st;
   if (stage == 0) {
     st = a.n_sink + (j << a.lchunk[0]);
@@ -550,7 +550,7 @@ k_score_decode_ci(PruneArgs a, int stage, const uint16_t* q_all, double base) {
   const int j = j0 + cl;
   __shared__ float red[16];
 
-  const int e = kv.seq_lens[r];
+  const int e = seq_len_of(kv, r);
   int nc_prev = 0, st;
   if (stage == 0) {
     st = a.n_sink + (j << a.lchunk[0]);
@@ -617,7 +617,7 @@ k_topk_score_decode_rope(PruneArgs a, int stage, const uint16_t* qa, const uint1
   const int gi = tid >> 4, li = tid & 15;
   const int cl = gi / kv.Hkv, g = gi - cl * kv.Hkv;
 
-  const int e = kv.seq_lens[r];
+  const int e = seq_len_of(kv, r);
   const int nc_before = ps > 0 ? a.cnt[r * kMaxStages + ps - 1] : 0;
   const int js = tid * E;
   uint32_t key[E];

@@ -353,6 +353,21 @@ typedef struct {
 dsa_status dsa_profile_begin(void);
 dsa_status dsa_profile_end(dsa_kernel_time* out, int32_t capacity, int32_t* n_out);
 
+/* Checked mode for decode inputs (a caller aid; the pages define no such
+ * step). The kernels read seq_lens and block_table from device memory and
+ * cannot report a bad value: a length above t is clamped to t and a length
+ * below 1 gives an empty row (every index entry -1, output 0), but a page id
+ * outside the pool makes the gathers read outside it. This call checks HOST
+ * copies of both arrays before the caller launches: every seq_lens[b] in
+ * [1, shape->t], and for a paged shape every page id that a sequence's
+ * length reaches (block_table[b][i], i < ceil(seq_lens[b] / page_size)) in
+ * [0, n_pages). seq_lens: host int32 [B]; block_table: host int32
+ * [B, max_pages] (ignored for contiguous K/V); n_pages: pages in the K/V
+ * pools. Returns DSA_OK, or DSA_ERR_INVALID_ARG with dsa_last_error() naming
+ * the first bad entry. Reads no device memory and launches nothing. */
+dsa_status dsa_check_decode_inputs(const dsa_shape* shape, const int32_t* seq_lens, const int32_t* block_table,
+                                   int64_t n_pages);
+
 /* Static description of a status code. */
 const char* dsa_status_str(dsa_status s);
 

@@ -662,6 +662,10 @@ def attend_block(Q: np.ndarray, K, V, row: np.ndarray, s: int, scale: float) -> 
     Q: [Hq, n_q, d] float32; K, V: [Hkv, >=T, d] indexable; row: key positions
     (entries < 0 are padding and ignored). Dot products are fp32 (exact on the
     input grid), softmax and P.V are fp64, the result is cast to fp32.
+
+    A query that sees no key of its row (possible for per-head rows such as
+    the vertical-slash ones) attends to nothing: its output is 0, the empty
+    sum (the pages define the softmax only over a non-empty key set).
     """
     row = np.asarray(row, dtype=np.int64)
     row = row[row >= 0]
@@ -677,9 +681,11 @@ def attend_block(Q: np.ndarray, K, V, row: np.ndarray, s: int, scale: float) -> 
         for h in range(g * G, (g + 1) * G):
             z = (np.asarray(Q[h], dtype=np.float32) @ kr.T).astype(np.float64) * scale
             z = np.where(visible, z, -np.inf)
-            zmax = z.max(axis=1, keepdims=True)
+            seen = visible.any(axis=1, keepdims=True)
+            zmax = np.where(seen, z.max(axis=1, keepdims=True, initial=-np.inf), 0.0)
             w = np.exp(z - zmax)
-            out[h] = ((w @ vr) / w.sum(axis=1, keepdims=True)).astype(np.float32)
+            den = w.sum(axis=1, keepdims=True)
+            out[h] = np.where(seen, (w @ vr) / np.where(seen, den, 1.0), 0.0).astype(np.float32)
     return out
 
 

@@ -244,3 +244,34 @@ def test_rope_style_for_layer_follows_the_page_assignment():
     assert {api.rope_style_for_layer(l) for l in range(4, 33)} == {"relative"}
     with pytest.raises(ValueError):
         api.rope_style_for_layer(0)
+
+
+def test_checked_mode_decode_inputs():
+    """Host-side validation of decode lengths and page ids (no device memory):
+    every length in [1, t], every page id a length reaches inside the pool."""
+    import numpy as np
+    t, ps, maxp, n_pages = 1000, 64, 16, 40
+    contig = Shape(DSA_DECODE, DSA_BF16, 3, 32, 8, 128, t, seq_lens=1)
+    _lib.check_decode_inputs(contig, [1, 500, 1000])
+    for bad in ([0, 5, 5], [5, 1001, 5], [5, 5, -3]):
+        with pytest.raises(_lib.DsaError) as ex:
+            _lib.check_decode_inputs(contig, bad)
+        assert ex.value.status == DSA_ERR_INVALID_ARG and "seq_lens[" in str(ex.value)
+    paged = Shape(DSA_DECODE, DSA_BF16, 2, 32, 8, 128, t, seq_lens=1, block_table=1, page_size=ps, max_pages=maxp)
+    table = np.full((2, maxp), -1, dtype=np.int32)              # unused slots may hold anything
+    table[0, :2] = [3, 39]                                      # 100 tokens: 2 pages
+    table[1, :16] = np.arange(16) + 20                          # 1000 tokens: 16 pages
+    _lib.check_decode_inputs(paged, [100, 1000], table, n_pages)
+    for (b, i, v) in ((0, 1, 40), (1, 15, -1), (0, 0, 1 << 20)):
+        bad = table.copy()
+        bad[b, i] = v
+        with pytest.raises(_lib.DsaError) as ex:
+            _lib.check_decode_inputs(paged, [100, 1000], bad, n_pages)
+        assert ex.value.status == DSA_ERR_INVALID_ARG and f"block_table[{b}][{i}]" in str(ex.value)
+    with pytest.raises(_lib.DsaError):
+        _lib.check_decode_inputs(paged, [100, 1000], None, n_pages)          # paged needs the table
+    with pytest.raises(_lib.DsaError):
+        _lib.check_decode_inputs(paged, [100, 1000], table, 0)               # empty pool
+    with pytest.raises(_lib.DsaError):
+        _lib.check_decode_inputs(Shape(DSA_PREFILL, DSA_BF16, 1, 32, 8, 128, 4096), [1])
+

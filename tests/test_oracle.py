@@ -314,6 +314,26 @@ def test_zero_budget_is_sink_plus_window_attention():
         np.testing.assert_allclose(out, expect[:, s:e], rtol=2e-6, atol=2e-6)
 
 
+def test_query_without_visible_key_outputs_zero():
+    """A row whose keys all lie after some of the block's queries: those
+    queries see nothing and output 0 (the empty sum); the others equal a
+    library attention restricted to the row's keys."""
+    Q, K, V = _small_case(37, T=128)
+    scale = ref.default_scale(16)
+    s, e = 64, 96
+    row = np.array([70, 75, 80, 90], dtype=np.int64)       # queries 64..69 see none
+    out = ref.attend_block(Q[:, s:e], K, V, row, s, scale)
+    t = np.arange(s, e)
+    ok = (row[None, :] <= t[:, None])
+    assert np.all(out[:, ~ok.any(axis=1)] == 0)
+    mask = np.zeros((e - s, K.shape[1]), dtype=bool)
+    mask[:, row] = ok
+    seen = ok.any(axis=1)
+    expect = _sdpa(Q[:, s:e][:, seen], K, V, scale, mask=mask[seen])
+    np.testing.assert_allclose(out[:, seen], expect, rtol=2e-6, atol=2e-6)
+    assert np.all(ref.attend_block(Q[:, s:e], K, V, np.array([], dtype=np.int64), s, scale) == 0)
+
+
 def test_no_causal_leak():
     Q, K, V = _small_case(31)
     T = Q.shape[1]

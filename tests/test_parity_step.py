@@ -159,3 +159,30 @@ def test_step_graph_replays_fresh_queries(c3):
         torch.cuda.synchronize()
         assert torch.equal(gi.view(-1), ei.view(-1)), f"replay {rep}: index rows differ"
         assert torch.equal(go, eo), f"replay {rep}: outputs differ"
+
+
+def test_lengths_outside_the_range_are_clamped():
+    """A length of 0 gives an empty row (every entry -1, output 0); a length
+    above the capacity t is read as t (both are caller errors that the checked
+    mode reports; the kernels stay inside the K/V rows either way)."""
+    cfg = gen.Config("step-clamp", "decode", 2, 8, 2, 128, 6000, "bf16", 1, (32, 8), (1024, 256), 16, 128,
+                     seed=24, n_queries=1)
+    case = gen.make_case(cfg)
+    dev = to_device(case)
+    p = params_of(cfg)
+    q = dev.q[0].contiguous()
+    want_idx, want_out = api.prune_attend(q, dev.k, dev.v, p, seq_lens=dev.seq_lens)
+    bad = torch.tensor([0, 6000 + 5000], dtype=torch.int32, device="cuda")
+    for fn in ("step", "two"):
+        if fn == "step":
+            idx, out = api.prune_attend(q, dev.k, dev.v, p, seq_lens=bad)
+        else:
+            idx = api.prune_select(q, dev.k, p, seq_lens=bad)
+            out = api.sparse_attn(q, dev.k, dev.v, idx, p, seq_lens=bad)
+        torch.cuda.synchronize()
+        assert torch.all(idx[0] == -1), fn
+        assert torch.all(out[0] == 0), fn
+        assert torch.equal(idx[1], want_idx[1]), fn
+        H.assert_close(out[1].cpu().numpy(), want_out[1].cpu().numpy(), f"{fn}: clamped length")
+    with pytest.raises(Exception):
+        api.check_decode_inputs(q, dev.k, seq_lens=bad)

@@ -55,13 +55,15 @@ def check(case, k_v, k_s, heads, blocks, attn, b=0, what=""):
             got = idx[b, h, m]
             assert np.array_equal(got, want), f"{what} row (h={h}, m={m}): first diff {np.flatnonzero(got != want)[:5]}"
             if m in attn:
+                # every query of the block, those that see no key of the row
+                # included (their output is 0)
                 row = want[want >= 0]
                 t = 64 * m + np.arange(64)
                 seen = (row[None, :] <= t[:, None]).any(axis=1) if len(row) else np.zeros(64, bool)
-                if seen.any():
-                    g = h // G
-                    o = ref.attend_block(Q[h:h + 1, 64 * m:64 * m + 64], K[g:g + 1], V[g:g + 1], want, 64 * m, scale)[0]
-                    H.assert_close(out[b, h, 64 * m:64 * m + 64][seen], o[seen], f"{what} attention (h={h}, m={m})")
+                g = h // G
+                o = ref.attend_block(Q[h:h + 1, 64 * m:64 * m + 64], K[g:g + 1], V[g:g + 1], want, 64 * m, scale)[0]
+                H.assert_close(out[b, h, 64 * m:64 * m + 64], o, f"{what} attention (h={h}, m={m})")
+                assert np.all(out[b, h, 64 * m:64 * m + 64][~seen] == 0), f"{what}: a query with no key is not 0"
     return idx, cols, offs, out
 
 
