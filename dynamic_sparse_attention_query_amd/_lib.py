@@ -20,7 +20,7 @@ DSA_PREFILL, DSA_DECODE = 0, 1
 MAX_STAGES = 4
 
 EXPORTS = ("dsa_index_width", "dsa_workspace_bytes", "dsa_prune_select", "dsa_sparse_attn", "dsa_prune_attend",
-
+           "dsa_prune_attend_static",
            "dsa_dense_attn", "dsa_mask_cache_bytes", "dsa_cached_index_width", "dsa_prune_select_cached",
            "dsa_block_sparse_index_width", "dsa_block_sparse_workspace_bytes", "dsa_block_sparse_select",
            "dsa_sparse_attn_heads", "dsa_vertical_slash_index_width", "dsa_vertical_slash_workspace_bytes",
@@ -80,6 +80,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dsa_prune_attend.argtypes = [ctypes.POINTER(CShape), vp, vp, vp, ctypes.POINTER(CParams), ctypes.c_float,
                                      vp, vp, vp, sz, vp, vp]
     lib.dsa_prune_attend.restype = ctypes.c_int
+    lib.dsa_prune_attend_static.argtypes = [ctypes.POINTER(CShape), vp, vp, vp, ctypes.POINTER(CParams),
+                                            ctypes.c_float, vp, vp, vp, vp]
+    lib.dsa_prune_attend_static.restype = ctypes.c_int
     lib.dsa_check_decode_inputs.argtypes = [ctypes.POINTER(CShape), vp, vp, ctypes.c_int64]
     lib.dsa_check_decode_inputs.restype = ctypes.c_int
     lib.dsa_prune_select.restype = ctypes.c_int

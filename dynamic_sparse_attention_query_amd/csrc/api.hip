@@ -4,10 +4,16 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "dsa.h"
 #include "dsa_internal.h"
 #include "vs_internal.h"
+
+// Scratch memory of dsa_prune_attend_static (see below): a file-scope device
+// array, one copy per GPU.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
 namespace {
 
@@ -186,6 +192,31 @@ dsa_status run_attn(const dsa_shape* s, const void* q, const void* k, const void
 }
 
 
+// Scratch memory of dsa_prune_attend_static, for callers that cannot allocate:
+// one array per GPU in the library's device code, held until the process
+// ends. Host code never uses the array's name as an address (on the host it
+// is only a handle): the device address comes from hipGetSymbolAddress, once
+// per device with that device current, and is kept per device.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+dsa_status static_scratch(void** out) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return fail(DSA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(err));
+  if (dev < 0 || dev >= kMaxDevices) return fail(DSA_ERR_UNSUPPORTED, "device %d beyond the static scratch table", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || !ptr)
+      return fail(DSA_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(err));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSA_OK;
+}
 
 }  // namespace
 
@@ -287,7 +318,7 @@ long long cached_width_ll(const dsa_params* p, long long max_growth) {
   return (n + 63) / 64 * 64;
 }
 
-// Validation of dsa_prune_attend; fills
+// Validation shared by dsa_prune_attend and dsa_prune_attend_static; fills
 // the workspace layout of the call.
 dsa_status check_prune_attend(const dsa_shape* s, const void* q, const void* k, const void* v,
                               const dsa_params* p, const int32_t* idx, const float* out, StepLayout* lay) {
@@ -459,6 +490,22 @@ dsa_status dsa_prune_attend(const dsa_shape* s, const void* q, const void* k, co
   if (st != DSA_OK) return st;
   if (!ws || ws_bytes < lay.bytes)
     return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, lay.bytes);
+  return run_prune_attend(s, q, k, v, p, scale, idx, out, ws, lay, visited, stream);
+}
+
+dsa_status dsa_prune_attend_static(const dsa_shape* s, const void* q, const void* k, const void* v,
+                                   const dsa_params* p, float scale, int32_t* idx, float* out,
+                                   uint64_t* visited, void* stream) {
+  g_err[0] = 0;
+  StepLayout lay{};
+  dsa_status st = check_prune_attend(s, q, k, v, p, idx, out, &lay);
+  if (st != DSA_OK) return st;
+  if (lay.bytes > kStaticScratchBytes)
+    return fail(DSA_ERR_UNSUPPORTED, "this shape needs %zu bytes of scratch; the static scratch holds %zu",
+                lay.bytes, kStaticScratchBytes);
+  void* ws = nullptr;
+  st = static_scratch(&ws);
+  if (st != DSA_OK) return st;
   return run_prune_attend(s, q, k, v, p, scale, idx, out, ws, lay, visited, stream);
 }
 

@@ -212,6 +212,23 @@ dsa_status dsa_prune_attend(const dsa_shape* shape, const void* q, const void* k
                             const dsa_params* p, float scale, int32_t* idx, float* out, void* ws,
                             size_t ws_bytes, uint64_t* visited, void* stream);
 
+/* dsa_prune_attend for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. It takes no
+ * workspace; its scratch memory is a 64 MiB array in the library's device
+ * code (one per GPU, held until the process ends), so it calls no hipMalloc,
+ * hipFree or allocating routine. Shapes whose scratch for this call exceeds
+ * 64 MiB are rejected with DSA_ERR_UNSUPPORTED before any launch (the 1M and
+ * 3M decode steps need about 1.5 MB, a batch of 32 ragged sequences of up to
+ * 256K tokens about 46 MB, a 128K prefill about 42 MB). Every call on one GPU
+ * shares that
+ * GPU's array: calls that may overlap on one GPU (several streams, several
+ * host threads) race and must not be issued; calls on different GPUs are
+ * independent. Nothing in the array needs to start at zero (every call writes
+ * what it reads). Arguments and results are those of dsa_prune_attend. */
+dsa_status dsa_prune_attend_static(const dsa_shape* shape, const void* q, const void* k, const void* v,
+                                   const dsa_params* p, float scale, int32_t* idx, float* out,
+                                   uint64_t* visited, void* stream);
+
 /* Exact causal attention over keys [0, t] for every query t. */
 dsa_status dsa_dense_attn(const dsa_shape* shape, const void* q, const void* k, const void* v,
                           float scale, float* out, void* ws, size_t ws_bytes, void* stream);

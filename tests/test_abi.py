@@ -275,3 +275,17 @@ def test_checked_mode_decode_inputs():
     with pytest.raises(_lib.DsaError):
         _lib.check_decode_inputs(Shape(DSA_PREFILL, DSA_BF16, 1, 32, 8, 128, 4096), [1])
 
+
+def test_static_scratch_entry_rejects_large_shapes_before_launch(lib):
+    """dsa_prune_attend_static: shapes whose scratch exceeds the 64 MiB static
+    array are refused with DSA_ERR_UNSUPPORTED before anything is launched
+    (dummy pointers: nothing is dereferenced)."""
+    big = Shape(DSA_PREFILL, DSA_BF16, 4, 32, 8, 128, 131072)     # four 128K sequences: ~168 MB
+    cs, cp = big.c(), P2.c()
+    st = lib.dsa_prune_attend_static(ctypes.byref(cs), 16, 16, 16, ctypes.byref(cp), 0.0, 16, 16, None, None)
+    assert st == DSA_ERR_UNSUPPORTED
+    assert b"static scratch" in lib.dsa_last_error()
+    bad = Shape(DSA_PREFILL, DSA_BF16, 1, 32, 8, 128, 100)         # t % b_q
+    cs = bad.c()
+    assert lib.dsa_prune_attend_static(ctypes.byref(cs), 16, 16, 16, ctypes.byref(cp), 0.0, 16, 16, None,
+                                       None) == DSA_ERR_INVALID_ARG
