@@ -91,7 +91,6 @@ def parse():
     ap.add_argument("--no-vertical-slash", action="store_true", help="skip the vertical-slash heads prefill")
     ap.add_argument("--no-rope", action="store_true", help="skip pruning with RoPE in SelectRep (both styles)")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-ref", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -443,6 +442,32 @@ def cached_decode(args, lib, p, Qs, Ks, Vs, shape, ws, wsb, out, seq_lens_full, 
 # --------------------------------------------------------------------------- #
 # prefill at 128K                                                             #
 # --------------------------------------------------------------------------- #
+def prefill_block_flops(cfg):
+    """Per query block: algorithmic flops of the SelectRep evaluations and of
+    the attention, from the geometry alone (the row of block m holds the
+    sinks, the kept keys of the last stage and the window up to the block's
+    end)."""
+    bq, d, Hq = cfg.block_q, cfg.d, cfg.hq
+    nblk = cfg.t // bq
+    sel = np.zeros(nblk)
+    attn = np.zeros(nblk)
+    for m in range(nblk):
+        e = (m + 1) * bq
+        n1 = max(0, e - cfg.n_window - cfg.n_sink) // cfg.chunk[0]
+        nc = n1
+        for i, (l, k) in enumerate(zip(cfg.chunk, cfg.keep)):
+            if i > 0:
+                nc = kept * (cfg.chunk[i - 1] // l)
+            kc = k // l
+            if nc > kc:
+                sel[m] += nc * Hq * (1 + int(math.log2(l))) * bq * 2 * d
+            kept = min(nc, kc)
+        mid_hi = cfg.n_sink + n1 * cfg.chunk[0]
+        n_row = min(cfg.n_sink, e) + kept * cfg.chunk[-1] + (e - mid_hi)
+        attn[m] = (bq * (n_row - bq) + bq * (bq + 1) // 2) * Hq * 4 * d
+    return sel, attn
+
+
 def prefill_algorithmic_flops(cfg, n_row: np.ndarray):
     """SelectRep evaluations (b_q * 2d flops each, one per distinct representative
     per (chunk, query head) of every stage that prunes) and attention over the
@@ -659,49 +684,91 @@ def vertical_slash_bench(args, res, reps=3):
 # --------------------------------------------------------------------------- #
 # the other decode workloads: batch-32 ragged paged, and 3M tokens            #
 # --------------------------------------------------------------------------- #
-def other_decode(args, name, reps=20):
-    """Graph-replayed decode step (prune_select + sparse_attn) of workload
-    `name`: microseconds per step, and HBM GB/s of its algorithmic bytes
-    (SelectRep rows counted by the kernels + K/V rows of every kept key)."""
+def other_decode(args, name, reps=24, n_queries=8, flush_bytes=1 << 30):
+    """Graph-replayed decode step (dsa_prune_attend) of workload `name`, a
+    fresh query each step, timed two ways: back to back (one KV copy, so later
+    steps may find rows in the caches) and cache-cold (a 1 GiB write between
+    steps, outside the timed region, evicts the L2s and the Infinity Cache;
+    each step is timed alone with HIP events). HBM GB/s uses the algorithmic
+    bytes of each step (SelectRep rows counted by the kernels + K/V rows of
+    every kept key)."""
     import torch
-    from dynamic_sparse_attention_query_amd import _lib, api, gen
+    from dynamic_sparse_attention_query_amd import api, gen
     from dynamic_sparse_attention_query_amd.inputs import params_of, to_device
 
     t0 = time.time()
-    case = gen.make_case(name)
+    case = gen.make_case(name, n_queries=n_queries)
     cfg = case.cfg
     dev = to_device(case)
     del case
     log(f"{name} inputs ready in {time.time() - t0:.1f}s")
     p = params_of(cfg)
-    q = dev.q[0].contiguous()
     kw = dict(seq_lens=dev.seq_lens, block_table=dev.block_table, t=dev.t)
+    qs = [dev.q[i].contiguous() for i in range(n_queries)]
+    idx = torch.empty((cfg.batch, api._lib.index_width(p)), dtype=torch.int32, device="cuda")
+    out = torch.empty(qs[0].shape, dtype=torch.float32, device="cuda")
     vis = torch.zeros(len(p.chunk), dtype=torch.int64, device="cuda")
-    idx = api.prune_select(q, dev.k, p, visited=vis, **kw)
-    out = api.sparse_attn(q, dev.k, dev.v, idx, p, **kw)
-    torch.cuda.synchronize()
     row_bytes = cfg.d * 2
-    nbytes = float(vis.sum().item()) * row_bytes + int((idx >= 0).sum().item()) * cfg.hkv * 2 * row_bytes
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        api.prune_select(q, dev.k, p, out=idx.view(-1), **kw)
-        api.sparse_attn(q, dev.k, dev.v, idx, p, out=out, **kw)
-    g.replay()
+    nbytes = []
+    for q in qs:
+        vis.zero_()
+        api.prune_attend(q, dev.k, dev.v, p, idx=idx, out=out, visited=vis, **kw)
+        torch.cuda.synchronize()
+        nbytes.append(float(vis.sum().item()) * row_bytes + int((idx >= 0).sum().item()) * cfg.hkv * 2 * row_bytes)
+    graphs = []
+    for q in qs:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            api.prune_attend(q, dev.k, dev.v, p, idx=idx, out=out, **kw)
+        graphs.append(g)
+    for g in graphs:
+        g.replay()
     torch.cuda.synchronize()
+    # back to back
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for _ in range(reps):
-        g.replay()
+    for i in range(reps):
+        graphs[i % n_queries].replay()
     e1.record()
     torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / reps
-    res = {"us_per_step": round(us, 2), "batch": cfg.batch, "us_per_token": round(us / cfg.batch, 2),
-           "algorithmic_bytes_per_step": int(nbytes), "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
-           "pct_peak": round(100 * nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 2),
-           "tokens_in_context": int(dev.seq_lens.sum().item()),
-           "note": "back-to-back graph replays of one step (same query, one KV copy)"}
-    log(f"{name}: {us:.1f} us/step, {res['gbps']} GB/s")
-    del dev, idx, out, g
+    us_b2b = e0.elapsed_time(e1) * 1e3 / reps
+    # cache-cold: flush, then time one step
+    junk = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(reps):
+        junk.fill_(float(i))
+        evs[i][0].record()
+        graphs[i % n_queries].replay()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    us_cold = sum(a.elapsed_time(b) for a, b in evs) * 1e3 / reps
+    # the same per-step timing without the flush: separates the cache effect
+    # from the cost of timing steps one at a time
+    for i in range(reps):
+        evs[i][0].record()
+        graphs[i % n_queries].replay()
+        evs[i][1].record()
+        torch.cuda.synchronize()
+    us_iso = sum(a.elapsed_time(b) for a, b in evs) * 1e3 / reps
+    nb = float(np.mean([nbytes[i % n_queries] for i in range(reps)]))
+
+    def rate(us):
+        g = nb / (us * 1e-6) / 1e9
+        return round(g, 1), round(100 * g / PEAK_HBM_GBPS, 2)
+
+    gb_cold, pct_cold = rate(us_cold)
+    gb_b2b, pct_b2b = rate(us_b2b)
+    res = {"us_per_step": round(us_cold, 2), "batch": cfg.batch, "us_per_token": round(us_cold / cfg.batch, 2),
+           "algorithmic_bytes_per_step": int(nb), "gbps": gb_cold, "pct_peak": pct_cold,
+           "timing": f"cache-cold: a {flush_bytes >> 30} GiB write between steps (outside the timed region), "
+                     f"each step timed alone; {n_queries} distinct queries",
+           "back_to_back": {"us_per_step": round(us_b2b, 2), "gbps": gb_b2b, "pct_peak": pct_b2b,
+                            "timing": "back-to-back graph replays, distinct queries, one KV copy"},
+           "isolated_warm_us_per_step": round(us_iso, 2),
+           "tokens_in_context": int(dev.seq_lens.sum().item())}
+    log(f"{name}: {us_cold:.1f} us/step cache-cold ({gb_cold} GB/s), {us_iso:.1f} isolated without flush, "
+        f"{us_b2b:.1f} back to back")
+    del dev, idx, out, graphs, junk
     torch.cuda.empty_cache()
     return res
 
@@ -768,25 +835,96 @@ def rope_decode(args, reps=20):
 # --------------------------------------------------------------------------- #
 # CPU oracle baseline                                                         #
 # --------------------------------------------------------------------------- #
-def cpu_baseline(args, case, res):
-    from threadpoolctl import threadpool_limits
+# --------------------------------------------------------------------------- #
+# CPU baseline: the oracle on the host's cores (a reported baseline only)     #
+# --------------------------------------------------------------------------- #
+_CPU_CASE = None             # the workload the pool workers read (inherited by fork)
 
+
+def _cpu_worker_init():
+    from threadpoolctl import threadpool_limits
+    global _CPU_LIMIT
+    _CPU_LIMIT = threadpool_limits(limits=1)      # one BLAS thread per worker: parallelism is the pool
+
+
+def _cpu_decode_step(qi):
     from oracle import ref
+    case = _CPU_CASE
     cfg = case.cfg
     rp = ref.Params(1, cfg.chunk, cfg.keep, cfg.n_sink, cfg.n_window)
     T = cfg.t
-    n = 0
-    t0 = time.perf_counter()
-    with threadpool_limits(limits=1):
-        while time.perf_counter() - t0 < args.cpu_seconds and n < case.q.shape[0]:
-            Q = case.q.sub((n, 0))[:, None, :]
-            row = ref.prune_block(Q, case.k[0], T - 1, T, rp)
-            ref.attend_block(Q, case.k[0], case.v[0], row, T - 1, ref.default_scale(cfg.d))
-            n += 1
-    el = time.perf_counter() - t0
-    res["cpu"] = {"value": round(el / n * 1e6, 1), "unit": "us/token", "cores": 1, "kind": "oracle",
-                  "sample": f"{n} decode steps (distinct queries) of the 1M-token workload, "
-                            f"oracle prune + attend, single thread, {el:.1f}s"}
+    Q = case.q.sub((qi, 0))[:, None, :]
+    row = ref.prune_block(Q, case.k[0], T - 1, T, rp)
+    ref.attend_block(Q, case.k[0], case.v[0], row, T - 1, ref.default_scale(cfg.d))
+    return qi
+
+
+def _cpu_prefill_block(m):
+    from oracle import ref
+    case = _CPU_CASE
+    cfg = case.cfg
+    rp = ref.Params(cfg.block_q, cfg.chunk, cfg.keep, cfg.n_sink, cfg.n_window)
+    s, e = m * cfg.block_q, (m + 1) * cfg.block_q
+    Q = case.q.sub(0)[:, s:e]
+    row = ref.prune_block(Q, case.k[0], s, e, rp)
+    ref.attend_block(Q, case.k[0], case.v[0], row, s, ref.default_scale(cfg.d))
+    return m
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(args):
+    """The oracle timed on the host's cores before the GPU is touched: a pool of
+    worker processes (fork, one BLAS thread each) over distinct decode queries
+    of the 1M workload, and over 64 stratified query blocks of the 128K prefill
+    (every 32nd block), extrapolated to all blocks by the per-block flop model."""
+    import multiprocessing as mp
+    from dynamic_sparse_attention_query_amd import gen
+    global _CPU_CASE
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    ctx = mp.get_context("fork")
+    res = {}
+    _CPU_CASE = gen.make_case("c3")
+    nq = _CPU_CASE.q.shape[0]
+    with ctx.Pool(workers, initializer=_cpu_worker_init) as pool:
+        pool.map(_cpu_decode_step, range(workers))              # warm-up: page in the inputs
+        t0 = time.perf_counter()
+        done = pool.map(_cpu_decode_step, range(nq))
+        el = time.perf_counter() - t0
+    res["decode"] = {"value": round(el / len(done) * 1e6, 1), "unit": "us/token", "cores": workers,
+                     "kind": "oracle", "cpu_model": _cpu_model(),
+                     "sample": f"{len(done)} decode steps (distinct queries) of the 1M-token workload, oracle "
+                               f"prune + attend, {workers} worker processes with one BLAS thread each, "
+                               f"{el:.1f}s wall ({el * workers:.0f} worker-seconds)"}
+    log(f"cpu oracle decode: {res['decode']['value']} us/token on {workers} workers")
+    _CPU_CASE = gen.make_case("c2_128k")
+    cfg = _CPU_CASE.cfg
+    nblk = cfg.t // cfg.block_q
+    blocks = list(range(nblk // 64 - 1, nblk, nblk // 64))      # 64 blocks, every 32nd, the last included
+    sel, attn = prefill_block_flops(cfg)
+    with ctx.Pool(workers, initializer=_cpu_worker_init) as pool:
+        t0 = time.perf_counter()
+        pool.map(_cpu_prefill_block, blocks, chunksize=1)
+        el = time.perf_counter() - t0
+    flops = sel + attn
+    sample_flops = float(flops[blocks].sum())
+    ms = el * 1e3 * float(flops.sum()) / sample_flops
+    res["prefill_128k"] = {"ms": round(ms, 1), "tflops": round(float(flops.sum()) / (ms * 1e-3) / 1e12, 4),
+                           "cores": workers, "kind": "oracle", "extrapolated": True,
+                           "sample": f"{len(blocks)} stratified query blocks (one in every {nblk // 64} of {nblk}) in "
+                                     f"{el:.1f}s wall on {workers} workers, extrapolated to all blocks by the "
+                                     f"per-block flop model (SelectRep evaluations + visible attention pairs)"}
+    log(f"cpu oracle prefill 128K: {ms / 1e3:.1f} s extrapolated ({el:.1f}s for {len(blocks)} blocks)")
+    _CPU_CASE = None
+    return res
 
 
 def main():
@@ -796,12 +934,14 @@ def main():
         print(f"bench.py measures one GPU: --gpus {args.gpus} (WORLD_SIZE {world}) is not supported; "
               "the library runs on one GPU and has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
+    res = {}
+    if not args.no_cpu:
+        res["cpu"] = cpu_baseline(args)         # before the GPU is initialised (the pool forks)
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
-    res = {}
     if args.copy_ref:
         src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -821,8 +961,6 @@ def main():
         vertical_slash_bench(args, res)
     if not args.no_rope:
         res["rope_decode"] = rope_decode(args)
-    if not args.no_cpu:
-        cpu_baseline(args, case, res)
 
     dec = res["decode"]
     gbps = dec["bytes_per_step"] / (dec["us_per_step"] * 1e-6) / 1e9
@@ -926,7 +1064,8 @@ def main():
                                          "kernels_ms": r["kernels_ms"]}
         line["rope_in_selectrep"] = rt
     if "cpu" in res:
-        line["cpu_baseline"] = res["cpu"]
+        line["cpu_baseline"] = res["cpu"]["decode"]
+        line["cpu_baseline"]["prefill_128k"] = res["cpu"]["prefill_128k"]
     print(json.dumps(line), flush=True)
 
 

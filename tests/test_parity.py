@@ -146,7 +146,10 @@ def test_c2_prefill_32k_sampled():
     idx, out = gpu_prefill(dev, p)
     nblk = cfg.t // cfg.block_q
     blocks = gen.sample_blocks(nblk, 64, cfg.seed)
-    check_prefill_blocks(case, idx, out, blocks, attn_blocks=blocks[::11] + [nblk - 1])
+    last8 = list(range(nblk - 8, nblk))                   # the widest rows
+    blocks = sorted(set(blocks) | set(last8))
+    # index rows and attention on every sampled block and the last eight
+    check_prefill_blocks(case, idx, out, blocks, attn_blocks=blocks)
     idx_np = idx.cpu().numpy()
     for nd in case.needles:
         row = set(idx_np[nd.b, nd.query // cfg.block_q].tolist())
