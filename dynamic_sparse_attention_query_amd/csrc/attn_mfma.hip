@@ -18,6 +18,8 @@
 // masks are applied only on tiles that need them.
 #include "dsa_internal.h"
 
+#include <type_traits>
+
 namespace dsa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -42,6 +44,13 @@ __device__ __forceinline__ i16x4_t lds_read_tr16(const uint16_t* p) {
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const f32x2_t f = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+// the sum of the two bf16 values of a packed pair, in fp32. Plain adds: the
+// bf16 dot-product instruction waits for the matrix core while another wave
+// of the SIMD issues products, the adds run beside them.
+__device__ __forceinline__ float bf16_pair_sum(uint32_t pw) {
+  return __uint_as_float(pw << 16) + __uint_as_float(pw & 0xffff0000u);
 }
 
 // Workgroup = NH heads of one GQA group x QH query halves (32 queries each),
@@ -529,7 +538,6 @@ __global__ void __launch_bounds__(64 * NH * QH, 2) k_prefill_mfma_lds(AttnArgs a
       }
       lrun *= alpha;
     }
-    const bf16x2_t ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
     float ps = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -540,7 +548,7 @@ __global__ void __launch_bounds__(64 * NH * QH, 2) k_prefill_mfma_lds(AttnArgs a
         // the packed pair feeds the sum from its own register (reading it
         // back out of the vector has been compiled to the wrong element)
         const uint32_t pw = pack_bf16x2(sacc[kt][half * 8 + 2 * x], sacc[kt][half * 8 + 2 * x + 1]);
-        ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw), ones, ps, false);
+        ps += bf16_pair_sum(pw);
         u[x] = pw;
       }
       const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, u);
@@ -779,7 +787,6 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))
     __builtin_amdgcn_s_waitcnt(0x0F7A);           // vmcnt(10); expcnt, lgkmcnt not waited
     barrier_keep_loads();
     if (flag & 2) {
-      const bf16x2_t ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
       float ps = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
@@ -788,7 +795,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
           const uint32_t pw = pack_bf16x2(sacc[kt][half * 8 + 2 * x], sacc[kt][half * 8 + 2 * x + 1]);
-          ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw), ones, ps, false);
+          ps += bf16_pair_sum(pw);
           u[x] = pw;
         }
         const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, u);
@@ -830,14 +837,33 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))
 // Shared rows, d = 128, groups of at least 4 query heads: one workgroup per
 // (query block, 4 heads of a kv group) with all 64 queries, eight waves
 // (4 heads x 2 query halves), so each K/V tile is loaded into LDS once for 256
-// (query, head) rows. Three tile buffers: the loads of tile i+2 are issued
-// when tile i begins and run under two tiles of products. Tile entry e lives
-// in LDS row 32 * (e % 2) + e / 2: lane group g = 4 * wave + lane / 16 (0..31)
-// takes entries 2g, 2g+1 (one 8-byte load of the index row, made two tiles
-// ahead of its use) and its two row loads land in rows 32u + g. Padding and
-// tiles past the row load through an out-of-range offset (zeros, no traffic).
-// The barriers leave the loads in flight; the vector-memory waits are counted
-// by hand: each step issues four row loads and one index load per wave.
+// (query, head) rows. Tile entry e lives in LDS row 32 * (e % 2) + e / 2: lane
+// group g = 4 * wave + lane / 16 (0..31) takes entries 2g, 2g+1 (one 8-byte
+// load of the index row) and its two row loads land in rows 32u + g. Padding
+// and tiles past the row load through an out-of-range offset (zeros, no
+// traffic).
+//
+// The two waves of each SIMD run a phase apart ("ping-pong"). A tile's work
+// per wave is S = K Q^T (16 matrix products), the online softmax (vector ALU
+// only) and O += V^T P^T (16 products, plus 4 that give the row sums of P).
+// Waves 0-3 (query half 0) and 4-7 (query half 1) share the four SIMDs in
+// pairs, and the half-1 waves run one phase behind: in every phase one wave
+// of each SIMD issues the products of P_i V_i and S_i+1 while the other
+// computes a softmax, so the matrix core is fed while its partner runs the
+// exponentials. Phases end at workgroup barriers, and each wave passes the
+// same number of them. Measured on gfx950: the bf16 dot-product instruction
+// waits for the matrix core of its SIMD (about one product per use), so the
+// softmax keeps none; every value that crosses lanes or waves in the loop
+// stays out of LDS (the tile flags come from a ballot over one index entry
+// per lane, the half-wave max from a lane swap), since an LDS round trip
+// costs several hundred cycles while the tile loads stream into LDS.
+//
+// Tile buffers rotate over three slots per operand. In phase 2m every wave
+// issues its rows of V_m+1 and K_m+2 and the index entries of tile m+3;
+// K_m+2 lands in the slot K_m-1 left at the end of phase 2m-1, V_m+1 in the
+// slot of V_m-2, so each load has two phases (one tile) to arrive before the
+// wait at the end of phase 2m+1 (vmcnt 6: the six loads of phase 2m stay in
+// flight) and the barrier after it.
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) k_prefill_gqa8(AttnArgs a) {
   constexpr int D = 128;
   constexpr int NH = 4;
@@ -847,7 +873,6 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   __shared__ __align__(16) uint16_t sk0[64 * D], sk1[64 * D], sk2[64 * D];
   __shared__ __align__(16) uint16_t sv0[64 * D], sv1[64 * D], sv2[64 * D];
   __shared__ __align__(16) int spos0[64], spos1[64], spos2[64];
-  __shared__ __align__(16) int sflag0[NWV], sflag1[NWV], sflag2[NWV];
   asm volatile("" ::"r"(sk0), "r"(sk1), "r"(sk2), "r"(sv0), "r"(sv1), "r"(sv2) : "memory");
 
   const KvLayout& kv = a.kv;
@@ -888,7 +913,12 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
-  float mrun = kNegBig, lrun = 0.f;
+  // row sums of P by the matrix cores: O_sum^T += 1 P^T (every row of the
+  // product holds the sum over the tile's keys for the lane's query)
+  f32x16_t osum = {};
+  float mrun = kNegBig;
+  f32x16_t sacc[2];
+  bf16x8_t pb[4] = {};
 
   const int32_t* row = a.idx + static_cast<size_t>(b * kv.nblk + m) * a.L;
   const int n_tiles = a.L / 64;                   // whole tiles (checked by the launcher)
@@ -897,68 +927,148 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   auto load_raw = [&](int ti) __attribute__((always_inline)) {
     return *reinterpret_cast<const int2*>(row + min(ti, n_tiles - 1) * 64 + 2 * lg);
   };
-  auto issue = [&](int ti, int2 raw, uint16_t* skb, uint16_t* svb, int* sposb, int* sflagb) __attribute__((always_inline)) {
+  // entry `lane` of tile ti, for the tile's flags
+  auto load_ent = [&](int ti) __attribute__((always_inline)) { return row[min(ti, n_tiles - 1) * 64 + lane]; };
+  // this wave's two rows of tile ti (entries 2 lg, 2 lg + 1) into sb
+  auto issue_rows = [&](int ti, int2 raw, __amdgpu_buffer_rsrc_t rs, uint16_t* sb) __attribute__((always_inline)) {
     const bool live = ti < n_tiles;
-    const int pp[2] = {live ? raw.x : -1, live ? raw.y : -1};
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
+      const int p = live ? (u ? raw.y : raw.x) : -1;
       const int rr = 32 * u + lg;
-      const int off = pp[u] < 0 ? static_cast<int>(kv_bytes) : pp[u] * (D * 2) + ((lslot ^ swz(rr)) << 4);
-      const int lbase = (32 * u + 4 * w) * D;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void_t*)(skb + lbase), 16, off, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void_t*)(svb + lbase), 16, off, 0, 0, 0);
+      const int off = p < 0 ? static_cast<int>(kv_bytes) : p * (D * 2) + ((lslot ^ swz(rr)) << 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(sb + (32 * u + 4 * w) * D), 16, off, 0, 0, 0);
     }
-    if (lslot < 2) sposb[32 * lslot + lg] = lslot == 0 ? pp[0] : pp[1];
-    const unsigned u0 = static_cast<unsigned>(pp[0]), u1 = static_cast<unsigned>(pp[1]);
-    const unsigned long long nb = __ballot(max(u0, u1) > static_cast<unsigned>(wq_lo));
-    const unsigned long long ab = __ballot(min(u0, u1) <= static_cast<unsigned>(wq_hi));
-    if (lane == 0) sflagb[w] = (nb != 0 ? 1 : 0) | (ab != 0 ? 2 : 0);
+  };
+  // positions of tile ti in LDS row order, for the causal mask
+  auto publish = [&](int ti, int2 raw, int* sposb) __attribute__((always_inline)) {
+    const bool live = ti < n_tiles;
+    if (lslot < 2) sposb[32 * lslot + lg] = live ? (lslot == 0 ? raw.x : raw.y) : -1;
+  };
+  // flags of tile ti from its entries (one per lane): bit 0 some entry may
+  // follow a query of the block (masking needed), bit 1 some key is visible
+  auto flag_of = [&](int ti, int e) __attribute__((always_inline)) {
+    const bool live = ti < n_tiles;
+    const unsigned u = static_cast<unsigned>(e);
+    const unsigned long long nb = __ballot(live && u > static_cast<unsigned>(wq_lo));
+    const unsigned long long ab = __ballot(live && u <= static_cast<unsigned>(wq_hi));
+    return (nb != 0 ? 1 : 0) | (ab != 0 ? 2 : 0);
   };
 
-  // The prologue issues exactly what two steps would (tile rows, then the
-  // index load two tiles ahead), so every step sees the same loads in flight
-  // and the compiler's own waits before LDS reads match the steady state.
-  int2 rc = load_raw(0), rd = load_raw(1);
-  issue(0, rc, sk0, sv0, spos0, sflag0);
-  rc = load_raw(2);
-  issue(1, rd, sk1, sv1, spos1, sflag1);
-  rd = load_raw(3);
-  // raw entries in hand at step i: tiles i+2 (rc) and i+3 (rd)
+  int2 r1 = load_raw(0), r2 = load_raw(1);
+  int e1 = load_ent(0), e2 = load_ent(1);
+  // phase 2m's loads: index entries of tile m+3, rows of V_m+1 and K_m+2;
+  // returns the flags of tile m+1
+  auto issue_block = [&](int mm, uint16_t* svd, int* sposd, uint16_t* skd) __attribute__((always_inline)) {
+    const int2 r3 = load_raw(mm + 3);
+    const int e3 = load_ent(mm + 3);
+    asm volatile("" ::: "memory");
+    issue_rows(mm + 1, r1, vrs, svd);
+    publish(mm + 1, r1, sposd);
+    issue_rows(mm + 2, r2, krs, skd);
+    asm volatile("" ::: "memory");
+    const int f1 = flag_of(mm + 1, e1);
+    r1 = r2;
+    r2 = r3;
+    e1 = e2;
+    e2 = e3;
+    return f1;
+  };
+  // the max of x over lanes l and l ^ 32 (both halves get the same bits)
+  auto halves_max = [&](float x) __attribute__((always_inline)) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  };
 
-  auto step = [&](int ti, const uint16_t* skc, const uint16_t* svc, const int* sposc, const int* sflagc,
-                  uint16_t* skn, uint16_t* svn, int* sposn, int* sflagn) __attribute__((always_inline)) {
-    // tile ti's rows were followed by an index load, the next tile's four row
-    // loads and another index load
-    __builtin_amdgcn_s_waitcnt(0x0F76);            // vmcnt(6); expcnt, lgkmcnt not waited
-    barrier_keep_loads();                          // everyone's rows of tile ti; tile ti-1 retired
-    issue(ti + 2, rc, skn, svn, sposn, sflagn);
-    rc = rd;
-    asm volatile("" ::: "memory");
-    rd = load_raw(ti + 4);
-    asm volatile("" ::: "memory");
-    int flag = 2;
+  // operand fragments of one stream step: the K rows of key step ks (both
+  // 32-row halves) for S, or the V^T rows of two d-tiles for O
+  struct Frag {
+    u32x4_t r[2];
+  };
+  // per-lane byte offsets inside a tile: K rows of step ks (the second
+  // 32-row half adds 32 rows), V^T rows of step 0 for d-tile dt (row r0 and
+  // r0 + 8; step ks adds 16 rows). The swizzle of a V row depends only on
+  // the lane, since steps move by 16 rows.
+  int kofs[KS], vofs[2 * DT];
 #pragma unroll
-    for (int i = 0; i < NWV; ++i) {
-      flag |= sflagc[i] & 1;
-      if (sflagc[i] & 2) flag &= ~2;
+  for (int ks = 0; ks < KS; ++ks) kofs[ks] = (l32 * D + (((2 * ks + hi) ^ swz(l32)) << 3)) * 2;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const int r0 = hi * 4 + tr_row, c = dt * 32 + tr_col;
+    vofs[2 * dt] = (r0 * D + (((c >> 3) ^ swz(r0)) << 3) + (c & 7)) * 2;
+    vofs[2 * dt + 1] = ((r0 + 8) * D + (((c >> 3) ^ swz(r0 + 8)) << 3) + (c & 7)) * 2;
+  }
+  auto load_k = [&](Frag& f, const uint16_t* skc, int ks) __attribute__((always_inline)) {
+    const char* base = reinterpret_cast<const char*>(skc) + kofs[ks];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) f.r[kt] = *reinterpret_cast<const u32x4_t*>(base + kt * 32 * D * 2);
+  };
+  auto load_v = [&](Frag& f, const uint16_t* svc, int ks, int dt0) __attribute__((always_inline)) {
+    const char* base = reinterpret_cast<const char*>(svc) + ks * 16 * D * 2;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const i16x4_t lo4 = lds_read_tr16(reinterpret_cast<const uint16_t*>(base + vofs[2 * (dt0 + j)]));
+      const i16x4_t hi4 = lds_read_tr16(reinterpret_cast<const uint16_t*>(base + vofs[2 * (dt0 + j) + 1]));
+      f.r[j] = __builtin_bit_cast(u32x4_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
     }
-    flag = __builtin_amdgcn_readfirstlane(flag ^ 2);  // bit 1 now set when some key is visible
-    if (!(flag & 2)) return;
-    f32x16_t sacc[2];
+  };
+  // S accumulates from zero at key step 0, so it holds no value before
+  auto use_k = [&](const Frag& f, int ks) __attribute__((always_inline)) {
+    const f32x16_t zero = {};
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
+      sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f.r[kt]), qf[ks],
+                                                         ks == 0 ? zero : sacc[kt], 0, 0, 0);
+  };
+  auto use_v = [&](const Frag& f, int ks, int dt0) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[kt][i] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const int rr = kt * 32 + l32;
-        const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(skc + rr * D + ((2 * ks + hi) ^ swz(rr)) * 8);
-        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[ks], sacc[kt], 0, 0, 0);
-      }
+    for (int j = 0; j < 2; ++j)
+      o[dt0 + j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f.r[j]), pb[ks], o[dt0 + j],
+                                                           0, 0, 0);
+    if (dt0 == 2) {
+      const bf16x8_t ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f),
+                             static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f),
+                             static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+      osum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb[ks], osum, 0, 0, 0);
     }
-    if (flag & 1) {
+  };
+  // The matrix phase is a stream of up to 16 steps of two products each:
+  // steps 0-7 O += V_i^T P_i^T (key step st / 2, d-tiles 2 (st % 2) and
+  // 2 (st % 2) + 1), steps 8-15 S_i+1 (key step st - 8). The fragments of a
+  // step are read NF - 1 steps ahead of its products, so the LDS latency
+  // stays hidden while one wave of the SIMD issues all its products.
+  constexpr int NF = 4;
+  auto stream = [&](const uint16_t* svc, const uint16_t* skn, auto s0c, auto s1c) __attribute__((always_inline)) {
+    constexpr int S0 = decltype(s0c)::value, S1 = decltype(s1c)::value;
+    Frag F[NF];
+    auto load_step = [&](int st) __attribute__((always_inline)) {
+      if (st < 8) load_v(F[st % NF], svc, st >> 1, 2 * (st & 1));
+      else load_k(F[st % NF], skn, st - 8);
+    };
+#pragma unroll
+    for (int st = S0; st < S0 + NF - 1 && st < S1; ++st) load_step(st);
+#pragma unroll
+    for (int st = S0; st < S1; ++st) {
+      if (st + NF - 1 < S1) load_step(st + NF - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (st < 8) use_v(F[st % NF], st >> 1, 2 * (st & 1));
+      else use_k(F[st % NF], st - 8);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // the matrix phase: O += V_i^T P_i^T, then S_i+1, unless neither tile has
+  // a visible key (a tile without one has P = 0, its S is not used)
+  auto mfma_phase = [&](const uint16_t* svc, int fp, const uint16_t* skn, int fq) __attribute__((always_inline)) {
+    if ((fp | fq) & 2) stream(svc, skn, std::integral_constant<int, 0>{}, std::integral_constant<int, 16>{});
+  };
+  // online softmax of S_i (flag f): P_i in bf16 (pb), running max and sum
+  auto softmax = [&](const int* sposc, int f) __attribute__((always_inline)) {
+    if (!(f & 2)) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) pb[ks] = bf16x8_t{};
+      return;
+    }
+    if (f & 1) {
       const unsigned t = static_cast<unsigned>(q0 + l32);
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -971,69 +1081,111 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
             if (static_cast<unsigned>(pp[c]) > t) sacc[kt][rn * 4 + c] = -INFINITY;
         }
     }
-    {
-      float mx = -INFINITY;
+    float mx = -INFINITY;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kt][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * a.scale_log2;
-      const bool raise = mx > mrun + 8.0f;
-      const float m_use = raise ? mx : mrun;
-      const float alpha = __builtin_amdgcn_exp2f(mrun - m_use);
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kt][i]);
+    mx = halves_max(mx) * a.scale_log2;
+    const bool raise = mx > mrun + 8.0f;
+    const float m_use = raise ? mx : mrun;
+    const float alpha = __builtin_amdgcn_exp2f(mrun - m_use);
+    mrun = m_use;
+    if (__ballot(raise)) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[kt][i] = __builtin_amdgcn_exp2f(fmaf(sacc[kt][i], a.scale_log2, -m_use));
-      mrun = m_use;
-      if (__ballot(raise)) {
+        for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
-      }
-      lrun *= alpha;
+      for (int i = 0; i < 16; ++i) osum[i] *= alpha;
     }
-    const bf16x2_t ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-    float ps = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int kt = ks >> 1, half = ks & 1;
       u32x4_t u;
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        const uint32_t pw = pack_bf16x2(sacc[kt][half * 8 + 2 * x], sacc[kt][half * 8 + 2 * x + 1]);
-        ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw), ones, ps, false);
-        u[x] = pw;
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kt][half * 8 + 2 * x], a.scale_log2, -m_use));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kt][half * 8 + 2 * x + 1], a.scale_log2, -m_use));
+        u[x] = pack_bf16x2(p0, p1);
       }
-      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, u);
-      const int r0 = ks * 16 + hi * 4 + tr_row, r1 = r0 + 8;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int c = dt * 32 + tr_col;
-        const i16x4_t lo4 = lds_read_tr16(svc + r0 * D + (((c >> 3) ^ swz(r0)) << 3) + (c & 7));
-        const i16x4_t hi4 = lds_read_tr16(svc + r1 * D + (((c >> 3) ^ swz(r1)) << 3) + (c & 7));
-        const bf16x8_t av = __builtin_bit_cast(
-            bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb, o[dt], 0, 0, 0);
-      }
+      pb[ks] = __builtin_bit_cast(bf16x8_t, u);
     }
-    lrun += ps + __shfl_xor(ps, 32, 64);
   };
-  // whole rounds of three steps, then the one or two left: the loop body has no
-  // branch around a step, so every step's loads in flight are the same
-  int ti = 0;
-  for (; ti + 3 <= n_tiles; ti += 3) {
-    step(ti, sk0, sv0, spos0, sflag0, sk2, sv2, spos2, sflag2);
-    step(ti + 1, sk1, sv1, spos1, sflag1, sk0, sv0, spos0, sflag0);
-    step(ti + 2, sk2, sv2, spos2, sflag2, sk1, sv1, spos1, sflag1);
-  }
-  if (ti < n_tiles) {
-    step(ti, sk0, sv0, spos0, sflag0, sk2, sv2, spos2, sflag2);
-    if (ti + 1 < n_tiles) step(ti + 1, sk1, sv1, spos1, sflag1, sk0, sv0, spos0, sflag0);
+  auto wait_rows = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0F76);           // vmcnt(6); expcnt, lgkmcnt not waited
+  };
+
+  // prologue: K_0, then the loads a phase 2m = -2 would issue (index
+  // entries of tile 2, V_0, K_1)
+  issue_rows(0, r1, krs, sk0);
+  int f = issue_block(-1, sv0, spos0, sk1);      // tile 0's flags
+  wait_rows();
+  barrier_keep_loads();
+
+  // tile i of a wave that is in phase 2i+1 (half 0) or 2i+2 (half 1) for its
+  // softmax, with the flags fc of tile i and fn of tile i+1; slots of tile i:
+  // A, of i+1: B, of i+2: C
+  auto tile0 = [&](int i, int& fc, int& fn, const int* sposA, uint16_t* skA, uint16_t* svA, const uint16_t* skB,
+                   uint16_t* svC, int* sposC) __attribute__((always_inline)) {
+    softmax(sposA, fc);
+    wait_rows();
+    barrier_keep_loads();
+    const int fnn = issue_block(i + 1, svC, sposC, skA);
+    mfma_phase(svA, fc, skB, fn);
+    barrier_keep_loads();
+    fc = fn;
+    fn = fnn;
+  };
+  auto tile1 = [&](int i, int& fc, int& fn, const int* sposA, uint16_t* skA, uint16_t* svA, const uint16_t* skB,
+                   uint16_t* svC, int* sposC) __attribute__((always_inline)) {
+    const int fnn = issue_block(i + 1, svC, sposC, skA);
+    softmax(sposA, fc);
+    barrier_keep_loads();
+    mfma_phase(svA, fc, skB, fn);
+    wait_rows();
+    barrier_keep_loads();
+    fc = fn;
+    fn = fnn;
+  };
+
+  if (qg == 0) {
+    // phase 0: loads, S_0
+    int fn = issue_block(0, sv1, spos1, sk2);
+    if (f & 2) stream(sv0, sk0, std::integral_constant<int, 8>{}, std::integral_constant<int, 16>{});
+    barrier_keep_loads();
+    int i = 0;
+    for (; i + 3 <= n_tiles; i += 3) {
+      tile0(i, f, fn, spos0, sk0, sv0, sk1, sv2, spos2);
+      tile0(i + 1, f, fn, spos1, sk1, sv1, sk2, sv0, spos0);
+      tile0(i + 2, f, fn, spos2, sk2, sv2, sk0, sv1, spos1);
+    }
+    if (i < n_tiles) {
+      tile0(i, f, fn, spos0, sk0, sv0, sk1, sv2, spos2);
+      if (i + 1 < n_tiles) tile0(i + 1, f, fn, spos1, sk1, sv1, sk2, sv0, spos0);
+    }
+    barrier_keep_loads();                         // the half-1 waves' last phase
+  } else {
+    // phase 0: loads; phase 1: S_0
+    int fn = issue_block(0, sv1, spos1, sk2);
+    barrier_keep_loads();
+    if (f & 2) stream(sv0, sk0, std::integral_constant<int, 8>{}, std::integral_constant<int, 16>{});
+    wait_rows();
+    barrier_keep_loads();
+    int i = 0;
+    for (; i + 3 <= n_tiles; i += 3) {
+      tile1(i, f, fn, spos0, sk0, sv0, sk1, sv2, spos2);
+      tile1(i + 1, f, fn, spos1, sk1, sv1, sk2, sv0, spos0);
+      tile1(i + 2, f, fn, spos2, sk2, sv2, sk0, sv1, spos1);
+    }
+    if (i < n_tiles) {
+      tile1(i, f, fn, spos0, sk0, sv0, sk1, sv2, spos2);
+      if (i + 1 < n_tiles) tile1(i + 1, f, fn, spos1, sk1, sv1, sk2, sv0, spos0);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);                  // no load into LDS outlives the workgroup
 
+  const float lrun = osum[0];
   const float inv = lrun > 0.f ? 1.0f / lrun : 0.f;   // no visible key: output 0
   float* orow = a.out + ((static_cast<size_t>(b) * kv.Hq + h) * kv.T + q0 + l32) * D;
 #pragma unroll
