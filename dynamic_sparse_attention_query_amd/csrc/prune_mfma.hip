@@ -12,9 +12,15 @@
 // and partial sums of grid-valued inputs are exact in fp32, so the MFMA
 // result equals the scalar dot product bit for bit.
 //
-// Workgroup = 4 waves x 32*T chunks of one row (query block); the waves split
-// the query heads. For each of its heads a wave runs T groups of 32
-// tournaments side by side (the groups share the head's query fragments), so
+// Workgroup = 4 waves x 32*T chunks of one row (query block) and one kv head;
+// the waves split the query heads of that kv head's group. Consecutive
+// workgroups on an XCD take 16 neighbouring rows for the same (kv head, chunk
+// slice): the rows' chunk lists coincide (stage 1) or overlap (later stages),
+// so the key rows they gather are shared in L2. Each workgroup folds the
+// max over its heads into the row's score list with an atomic max (the list
+// is cleared first; max is order-independent, so the result is exact). For
+// each of its heads a wave runs T groups of 32 tournaments side by side (the
+// groups share the head's query fragments), so
 // every dependent round of key-row loads has T independent row sets in
 // flight. Rows reach the matrix-core operand layout through a per-wave LDS
 // staging buffer: a wave-wide 16-byte load covers whole rows (PPR lanes per
@@ -24,8 +30,7 @@
 // first split's two representatives are fetched as two rounds: the rows in
 // flight never exceed T sets per wave, the kernel stays under 168 registers
 // and three waves share each SIMD, which hides more of each round's
-// dependent gather latency than two waves with twice the rows each. The chunk
-// score (max over all heads) is reduced in LDS.
+// dependent gather latency than two waves with twice the rows each.
 //
 // With RT (relative RoPE in SelectRep, InfiniteHiP page, "Four RoPE Styles
 // for Context Pruning"), the wave holds the fragments of the head's two
@@ -61,10 +66,12 @@ k_score_prefill_mfma(PruneArgs a, int stage, int ncg, const uint16_t* ql_all, co
 
   const KvLayout& kv = a.kv;
   const int x = blockIdx.x & 7, i = blockIdx.x >> 3;
-  const int per_group = ncg * kRowGroup;
+  const int per_group = kv.Hkv * ncg * kRowGroup;
   const int rbl = i / per_group, rem = i - rbl * per_group;
   const int r = ((rbl << 3) + x) * kRowGroup + rem % kRowGroup;
-  const int j0 = (rem / kRowGroup) * CPB;
+  const int gj = rem / kRowGroup;
+  const int g = gj / ncg;
+  const int j0 = (gj - g * ncg) * CPB;
   if (r >= a.R) return;
   int b, s, e;
   row_bounds(kv, r, b, s, e);
@@ -86,8 +93,11 @@ k_score_prefill_mfma(PruneArgs a, int stage, int ncg, const uint16_t* ql_all, co
   }
   const int l = a.chunk[stage];
   const int G = kv.Hq / kv.Hkv;
+  // the first two rounds shared by the waves (every wave has the same number
+  // of heads, so the barriers inside are uniform)
+  const bool share = !RT && T == 2 && (G & 3) == 0 && l >= 2;
   const uint16_t* Q = static_cast<const uint16_t*>(a.q);
-  const uint16_t* K = static_cast<const uint16_t*>(a.k);
+  const uint16_t* Kg = static_cast<const uint16_t*>(a.k) + (static_cast<size_t>(b) * kv.Hkv + g) * kv.T * D;
 
   // a set of 32 rows at the positions published in spos[w][set]
   auto fetch = [&](const uint16_t* base, int set, u32x4_t (&v)[LPS]) __attribute__((always_inline)) {
@@ -106,9 +116,7 @@ k_score_prefill_mfma(PruneArgs a, int stage, int ncg, const uint16_t* ql_all, co
   float best[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) best[t] = -INFINITY;
-  for (int h = w; h < kv.Hq; h += 4) {
-    const int g = h / G;
-    const uint16_t* Kg = K + (static_cast<size_t>(b) * kv.Hkv + g) * kv.T * D;
+  for (int h = g * G + w; h < (g + 1) * G; h += 4) {
     bf16x8_t qf[NQ][2][KS];
 #pragma unroll
     for (int set = 0; set < NQ; ++set) {
@@ -126,8 +134,9 @@ k_score_prefill_mfma(PruneArgs a, int stage, int ncg, const uint16_t* ql_all, co
           qf[set][qt][ks] = *reinterpret_cast<const bf16x8_t*>(buf + l32 * KROW + ks * 16 + hi * 8);
       }
     }
-    // sigma of the staged key for this lane's chunk column, against query set `set`
-    auto sigma_staged = [&](int set) __attribute__((always_inline)) {
+    // sigma of the key staged in bb for this lane's chunk column, against
+    // query set `set`
+    auto sigma_in = [&](const uint16_t* bb, int set) __attribute__((always_inline)) {
       f32x16_t acc[2];
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt)
@@ -135,7 +144,7 @@ k_score_prefill_mfma(PruneArgs a, int stage, int ncg, const uint16_t* ql_all, co
         for (int i2 = 0; i2 < 16; ++i2) acc[qt][i2] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(buf + l32 * KROW + ks * 16 + hi * 8);
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(bb + l32 * KROW + ks * 16 + hi * 8);
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt)
           acc[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[set][qt][ks], kf, acc[qt], 0, 0, 0);
@@ -145,8 +154,11 @@ k_score_prefill_mfma(PruneArgs a, int stage, int ncg, const uint16_t* ql_all, co
       for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
         for (int i2 = 0; i2 < 16; ++i2) m = fmaxf(m, acc[qt][i2]);
-      return fmaxf(m, __shfl_xor(m, 32, 64));
+      // with the other half-wave's max (a lane swap, no LDS round trip)
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+      return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     };
+    auto sigma_staged = [&](int set) __attribute__((always_inline)) { return sigma_in(buf, set); };
     // one round: the rows at offsets off[t] of every group, scored against
     // the first query set (sg) and, with RT and `right`, the right one (sr)
     auto round = [&](const int (&off)[T], float (&sg)[T], float (&sr)[T], bool right) __attribute__((always_inline)) {
@@ -169,7 +181,38 @@ k_score_prefill_mfma(PruneArgs a, int stage, int ncg, const uint16_t* ql_all, co
 
     float sa[T], win[T], unused[T];
     int lo[T], hi_r[T];
-    {
+    int wd0 = l >> 1;
+    if (share) {
+      // The first two rounds of every head score key 0 and key l/2 of each
+      // chunk, so the four waves (the heads of one kv head's group) gather
+      // them once: wave w stages round w / 2 of group w % 2 in its buffer,
+      // and every wave scores its head against all four sets.
+      const int tw = w & 1, offw = (w >> 1) ? (l >> 1) : 0;
+      if (hi == 0) spos[w][0][l32] = (tw ? st[T - 1] : st[0]) + offw;
+      {
+        u32x4_t v[LPS];
+        fetch(Kg, 0, v);
+        stage_set(v);
+      }
+      __syncthreads();
+      float s1[T];
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        sa[t] = sigma_in(sbuf[t], 0);
+        s1[t] = sigma_in(sbuf[2 + t], 0);
+      }
+      __syncthreads();                          // the buffers are the waves' own again
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        lo[t] = 0;
+        hi_r[t] = l - 1;
+        const int mid = l >> 1;
+        if (s1[t] > sa[t]) { lo[t] = mid; sa[t] = s1[t]; }
+        else               { hi_r[t] = mid - 1; }
+        win[t] = sa[t];
+      }
+      wd0 = l >> 2;
+    } else {
       int off[T];
 #pragma unroll
       for (int t = 0; t < T; ++t) off[t] = 0;
@@ -177,7 +220,7 @@ k_score_prefill_mfma(PruneArgs a, int stage, int ncg, const uint16_t* ql_all, co
 #pragma unroll
       for (int t = 0; t < T; ++t) { lo[t] = 0; hi_r[t] = l - 1; win[t] = sa[t]; }
     }
-    for (int wd = l >> 1; wd >= 1; wd >>= 1) {
+    for (int wd = wd0; wd >= 1; wd >>= 1) {
       int mid[T];
       float sm[T], smr[T];
 #pragma unroll
@@ -206,8 +249,18 @@ k_score_prefill_mfma(PruneArgs a, int stage, int ncg, const uint16_t* ql_all, co
   for (int c = tid; c < CPB; c += 256) {
     if (j0 + c < nc) {
       const float m = fmaxf(fmaxf(red[0][c], red[1][c]), fmaxf(red[2][c], red[3][c]));
-      stage_scores(a, stage, r)[j0 + c] = score_key(m);
+      atomicMax(stage_scores(a, stage, r) + j0 + c, score_key(m));
     }
+  }
+}
+
+// Clears n keys (key 0 is below every score's key).
+__global__ void __launch_bounds__(256) k_clear_keys(uint32_t* p, long long n) {
+  const long long i = (static_cast<long long>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (i + 3 < n) {
+    *reinterpret_cast<uint4*>(p + i) = make_uint4(0, 0, 0, 0);
+  } else {
+    for (long long k = i; k < n; ++k) p[k] = 0;
   }
 }
 
@@ -220,7 +273,15 @@ bool launch_score_prefill_mfma(const PruneArgs& a, int stage, int max_chunks, hi
   const int T = rt ? kScoreGroupsRt : kScoreGroups;
   const int ncg = (max_chunks + 32 * T - 1) / (32 * T);
   const long long groups = (a.R + 8LL * kRowGroup - 1) / (8LL * kRowGroup);   // per XCD
-  const dim3 grid(static_cast<unsigned>(groups * 8 * kRowGroup * ncg));
+  const dim3 grid(static_cast<unsigned>(groups * 8 * kRowGroup * ncg * a.kv.Hkv));
+  if (a.kv.D != 128 && a.kv.D != 64) return false;
+  {
+    // the stage's score lists (the workgroups fold their maxima into them)
+    const long long n = static_cast<long long>(a.R) * a.maxNC;
+    uint32_t* sc = a.scores + static_cast<size_t>(stage & 1) * a.R * a.maxNC;
+    DSA_LAUNCH("prune_clear_scores", k_clear_keys, dim3(static_cast<unsigned>((n + 1023) / 1024)), dim3(256), st,
+               sc, n);
+  }
   if (a.kv.D == 128) {
     if (rt) DSA_LAUNCH(name, (k_score_prefill_mfma<128, kScoreGroupsRt, true>), grid, dim3(256), st, a, stage, ncg, ql, qr);
     else    DSA_LAUNCH(name, (k_score_prefill_mfma<128, kScoreGroups, false>), grid, dim3(256), st, a, stage, ncg, ql, qr);
