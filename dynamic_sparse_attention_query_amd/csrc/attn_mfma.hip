@@ -870,10 +870,10 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   constexpr int NWV = 8;
   constexpr int KS = D / 16;
   constexpr int DT = D / 32;
-  __shared__ __align__(16) uint16_t sk0[64 * D], sk1[64 * D], sk2[64 * D];
-  __shared__ __align__(16) uint16_t sv0[64 * D], sv1[64 * D], sv2[64 * D];
-  __shared__ __align__(16) int spos0[64], spos1[64], spos2[64];
-  asm volatile("" ::"r"(sk0), "r"(sk1), "r"(sk2), "r"(sv0), "r"(sv1), "r"(sv2) : "memory");
+  __shared__ __align__(16) uint16_t sk0[64 * D], sk1[64 * D], sk2[64 * D], sk3[64 * D];
+  __shared__ __align__(16) uint16_t sv0[64 * D], sv1[64 * D], sv2[64 * D], sv3[64 * D];
+  __shared__ __align__(16) int spos0[64], spos1[64], spos2[64], spos3[64];
+  asm volatile("" ::"r"(sk0), "r"(sk1), "r"(sk2), "r"(sk3), "r"(sv0), "r"(sv1), "r"(sv2), "r"(sv3) : "memory");
 
   const KvLayout& kv = a.kv;
   const int G = kv.Hq / kv.Hkv;
@@ -1059,7 +1059,9 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   // the matrix phase: O += V_i^T P_i^T, then S_i+1, unless neither tile has
   // a visible key (a tile without one has P = 0, its S is not used)
   auto mfma_phase = [&](const uint16_t* svc, int fp, const uint16_t* skn, int fq) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(3);                // the products first when both waves of a SIMD are ready
     if ((fp | fq) & 2) stream(svc, skn, std::integral_constant<int, 0>{}, std::integral_constant<int, 16>{});
+    __builtin_amdgcn_s_setprio(0);
   };
   // online softmax of S_i (flag f): P_i in bf16 (pb), running max and sum
   auto softmax = [&](const int* sposc, int f) __attribute__((always_inline)) {
@@ -1112,76 +1114,89 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
       pb[ks] = __builtin_bit_cast(bf16x8_t, u);
     }
   };
-  auto wait_rows = [&]() __attribute__((always_inline)) {
+  // waits for the rows of all but the last one (half 1) or two (half 0) load
+  // blocks this wave issued
+  auto wait_rows1 = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0x0F76);           // vmcnt(6); expcnt, lgkmcnt not waited
+  };
+  auto wait_rows0 = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0F7C);           // vmcnt(12); expcnt, lgkmcnt not waited
   };
 
   // prologue: K_0, then the loads a phase 2m = -2 would issue (index
-  // entries of tile 2, V_0, K_1)
+  // entries of tile 2, V_0, K_1); half 0 also issues the next block now
   issue_rows(0, r1, krs, sk0);
   int f = issue_block(-1, sv0, spos0, sk1);      // tile 0's flags
-  wait_rows();
+  int fn = 0;
+  if (qg == 0) {
+    fn = issue_block(0, sv1, spos1, sk2);
+    wait_rows0();
+  } else {
+    wait_rows1();
+  }
   barrier_keep_loads();
 
   // tile i of a wave that is in phase 2i+1 (half 0) or 2i+2 (half 1) for its
-  // softmax, with the flags fc of tile i and fn of tile i+1; slots of tile i:
-  // A, of i+1: B, of i+2: C
-  auto tile0 = [&](int i, int& fc, int& fn, const int* sposA, uint16_t* skA, uint16_t* svA, const uint16_t* skB,
-                   uint16_t* svC, int* sposC) __attribute__((always_inline)) {
+  // softmax, with the flags fc of tile i and fn of tile i+1. Slots of tile
+  // i: A, of i+1: B, of i+2: C, of i+3: D. The load block of the softmax
+  // phase writes V_i+2 (slot C) and K_i+3 (slot D); for half 0 that is
+  // phase 2i+1, when the half-1 waves still read V_i-1 and K_i (slots D and
+  // A), which four slots keep apart.
+  auto tile0 = [&](int i, int& fc, int& fn, const int* sposA, uint16_t* svA, const uint16_t* skB,
+                   uint16_t* svC, int* sposC, uint16_t* skD) __attribute__((always_inline)) {
+    const int fnn = issue_block(i + 1, svC, sposC, skD);
     softmax(sposA, fc);
-    wait_rows();
+    wait_rows0();
     barrier_keep_loads();
-    const int fnn = issue_block(i + 1, svC, sposC, skA);
     mfma_phase(svA, fc, skB, fn);
     barrier_keep_loads();
     fc = fn;
     fn = fnn;
   };
-  auto tile1 = [&](int i, int& fc, int& fn, const int* sposA, uint16_t* skA, uint16_t* svA, const uint16_t* skB,
-                   uint16_t* svC, int* sposC) __attribute__((always_inline)) {
-    const int fnn = issue_block(i + 1, svC, sposC, skA);
+  auto tile1 = [&](int i, int& fc, int& fn, const int* sposA, uint16_t* svA, const uint16_t* skB,
+                   uint16_t* svC, int* sposC, uint16_t* skD) __attribute__((always_inline)) {
+    const int fnn = issue_block(i + 1, svC, sposC, skD);
     softmax(sposA, fc);
     barrier_keep_loads();
     mfma_phase(svA, fc, skB, fn);
-    wait_rows();
+    wait_rows1();
     barrier_keep_loads();
     fc = fn;
     fn = fnn;
   };
 
   if (qg == 0) {
-    // phase 0: loads, S_0
-    int fn = issue_block(0, sv1, spos1, sk2);
+    // phase 0: S_0
     if (f & 2) stream(sv0, sk0, std::integral_constant<int, 8>{}, std::integral_constant<int, 16>{});
     barrier_keep_loads();
     int i = 0;
-    for (; i + 3 <= n_tiles; i += 3) {
-      tile0(i, f, fn, spos0, sk0, sv0, sk1, sv2, spos2);
-      tile0(i + 1, f, fn, spos1, sk1, sv1, sk2, sv0, spos0);
-      tile0(i + 2, f, fn, spos2, sk2, sv2, sk0, sv1, spos1);
+    for (; i + 4 <= n_tiles; i += 4) {
+      tile0(i, f, fn, spos0, sv0, sk1, sv2, spos2, sk3);
+      tile0(i + 1, f, fn, spos1, sv1, sk2, sv3, spos3, sk0);
+      tile0(i + 2, f, fn, spos2, sv2, sk3, sv0, spos0, sk1);
+      tile0(i + 3, f, fn, spos3, sv3, sk0, sv1, spos1, sk2);
     }
-    if (i < n_tiles) {
-      tile0(i, f, fn, spos0, sk0, sv0, sk1, sv2, spos2);
-      if (i + 1 < n_tiles) tile0(i + 1, f, fn, spos1, sk1, sv1, sk2, sv0, spos0);
-    }
+    if (i < n_tiles) tile0(i, f, fn, spos0, sv0, sk1, sv2, spos2, sk3);
+    if (i + 1 < n_tiles) tile0(i + 1, f, fn, spos1, sv1, sk2, sv3, spos3, sk0);
+    if (i + 2 < n_tiles) tile0(i + 2, f, fn, spos2, sv2, sk3, sv0, spos0, sk1);
     barrier_keep_loads();                         // the half-1 waves' last phase
   } else {
     // phase 0: loads; phase 1: S_0
-    int fn = issue_block(0, sv1, spos1, sk2);
+    fn = issue_block(0, sv1, spos1, sk2);
     barrier_keep_loads();
     if (f & 2) stream(sv0, sk0, std::integral_constant<int, 8>{}, std::integral_constant<int, 16>{});
-    wait_rows();
+    wait_rows1();
     barrier_keep_loads();
     int i = 0;
-    for (; i + 3 <= n_tiles; i += 3) {
-      tile1(i, f, fn, spos0, sk0, sv0, sk1, sv2, spos2);
-      tile1(i + 1, f, fn, spos1, sk1, sv1, sk2, sv0, spos0);
-      tile1(i + 2, f, fn, spos2, sk2, sv2, sk0, sv1, spos1);
+    for (; i + 4 <= n_tiles; i += 4) {
+      tile1(i, f, fn, spos0, sv0, sk1, sv2, spos2, sk3);
+      tile1(i + 1, f, fn, spos1, sv1, sk2, sv3, spos3, sk0);
+      tile1(i + 2, f, fn, spos2, sv2, sk3, sv0, spos0, sk1);
+      tile1(i + 3, f, fn, spos3, sv3, sk0, sv1, spos1, sk2);
     }
-    if (i < n_tiles) {
-      tile1(i, f, fn, spos0, sk0, sv0, sk1, sv2, spos2);
-      if (i + 1 < n_tiles) tile1(i + 1, f, fn, spos1, sk1, sv1, sk2, sv0, spos0);
-    }
+    if (i < n_tiles) tile1(i, f, fn, spos0, sv0, sk1, sv2, spos2, sk3);
+    if (i + 1 < n_tiles) tile1(i + 1, f, fn, spos1, sv1, sk2, sv3, spos3, sk0);
+    if (i + 2 < n_tiles) tile1(i + 2, f, fn, spos2, sv2, sk3, sv0, spos0, sk1);
   }
   __builtin_amdgcn_s_waitcnt(0);                  // no load into LDS outlives the workgroup
 
