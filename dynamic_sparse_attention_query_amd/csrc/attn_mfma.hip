@@ -1083,11 +1083,13 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
             if (static_cast<unsigned>(pp[c]) > t) sacc[kt][rn * 4 + c] = -INFINITY;
         }
     }
-    float mx = -INFINITY;
+    // four independent max chains, then their max
+    float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kt][i]);
+      for (int i = 0; i < 16; ++i) m4[(kt * 16 + i) & 3] = fmaxf(m4[(kt * 16 + i) & 3], sacc[kt][i]);
+    float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
     mx = halves_max(mx) * a.scale_log2;
     const bool raise = mx > mrun + 8.0f;
     const float m_use = raise ? mx : mrun;
