@@ -71,3 +71,33 @@ def assert_close(got: np.ndarray, want: np.ndarray, what: str):
     rel = np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-30)
     assert err <= MAX_ABS and rel <= REL_L2, f"{what}: max-abs {err:.3e}, rel-L2 {rel:.3e}"
     return err, rel
+
+
+def kept_set_or_legal_swap(got: np.ndarray, sums: np.ndarray, k: int, what: str) -> np.ndarray:
+    """Validity rule for a top-k of fp64 sums ranked after one rounding to fp32
+    (the vertical-slash columns and offsets): the kernel's sums are summed in
+    another order than the oracle's, so a sum that lies next to an fp32
+    rounding boundary may round one ulp apart on the two sides, and near the
+    k-th sum several kept sets are then correct. The kept set must equal the
+    oracle's exactly, except that an index may be swapped in or out when its
+    fp32 sum lies within one fp32 ulp of the k-th largest fp32 sum; every such
+    swap is reported. Returns the set the rows and the attention must be
+    checked against (the kernel's, once it is legal)."""
+    s32 = np.asarray(sums).astype(np.float32)
+    want = ref.top_k(s32, k)
+    got = np.asarray(got, dtype=np.int64)
+    if np.array_equal(got, want):
+        return want
+    assert len(got) == len(want), f"{what}: kept {len(got)} entries, the oracle {len(want)}"
+    assert np.all(np.diff(got) > 0), f"{what}: kept set not strictly ascending"
+    assert got.min() >= 0 and got.max() < len(s32), f"{what}: kept index out of range"
+    kth = np.float32(s32[want].min())
+    ulp = np.spacing(kth)
+    extra, missing = np.setdiff1d(got, want), np.setdiff1d(want, got)
+    near = lambda i: abs(np.float64(s32[i]) - np.float64(kth)) <= np.float64(ulp)
+    bad = [int(i) for i in np.concatenate([extra, missing]) if not near(i)]
+    assert not bad, (f"{what}: kept set differs beyond one fp32 ulp of the k-th sum {kth!r} "
+                     f"(indices {bad[:8]}, sums {[float(s32[i]) for i in bad[:8]]})")
+    say(f"{what}: legal swap at the k-th sum {kth!r} (ulp {ulp!r}): in {extra.tolist()[:8]}, "
+        f"out {missing.tolist()[:8]}")
+    return got

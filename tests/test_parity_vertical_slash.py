@@ -5,9 +5,14 @@ kept offsets, index rows) and dsa_sparse_attn_heads over its rows, through the
 C ABI, against the CPU oracle.
 
 The column and offset sums are fp64 on both sides (exact fp32 dot products,
-fp64 softmax) and are ranked after one rounding to fp32, so the kept sets are
-compared exactly; rows bit-exactly; outputs within max-abs 1e-2 and
-relative-L2 5e-3 for every query that sees at least one key of its row.
+fp64 softmax, summed in different orders) and are ranked after one rounding to
+fp32. The kept sets must equal the oracle's exactly, except that an index may
+swap in or out when its fp32 sum lies within one fp32 ulp of the k-th sum
+(where both roundings are correct); every such swap is reported and the rows
+and attention are then checked against the kernel's kept sets. Rows are
+compared bit-exactly with the oracle's row builder; outputs within max-abs
+1e-2 and relative-L2 5e-3, and exactly 0 for a query that sees no key of its
+row.
 """
 import numpy as np
 import pytest
@@ -47,9 +52,9 @@ def check(case, k_v, k_s, heads, blocks, attn, b=0, what=""):
     scale = ref.default_scale(Q.shape[2])
     for h in heads:
         sv, ss = ref.vs_sums(Q, K, h)
-        iv, is_ = ref.vs_select(sv, k_v), ref.vs_select(ss, k_s)
-        assert np.array_equal(cols[b, h], iv), f"{what} head {h} columns: {np.setxor1d(cols[b, h], iv)[:8]}"
-        assert np.array_equal(offs[b, h], is_), f"{what} head {h} offsets: {np.setxor1d(offs[b, h], is_)[:8]}"
+        # exact, except legal swaps at the k-th sum (see the helper)
+        iv = H.kept_set_or_legal_swap(cols[b, h], sv, k_v, f"{what} head {h} columns")
+        is_ = H.kept_set_or_legal_swap(offs[b, h], ss, k_s, f"{what} head {h} offsets")
         for m in blocks:
             want = ref.pad_row(ref.vs_row(iv, is_, m), L)
             got = idx[b, h, m]
