@@ -800,6 +800,17 @@ def rope_decode(args, reps=20):
     for style in ROPE_STYLES:
         variants.append((style, lambda out=None, style=style: api.prune_select_rope(q, dev.k, p, ROPE_BASE, out=out,
                                                                                      style=style, **kw)))
+    # chunk-indexed over keys rotated once per stage: the whole context is
+    # rotated before timing, and each timed step rotates the newest key (what
+    # one appended token costs) and prunes over the rotated copies
+    k_rot = api.rope_key_copies(dev.k, p)
+    api.rope_rotate_keys(dev.k, p, ROPE_BASE, k_rot, seq_lens=dev.seq_lens)
+    T = int(dev.k.shape[2])
+
+    def prune_rotated_keys(out=None):
+        api.rope_rotate_keys(dev.k, p, ROPE_BASE, k_rot, pos_begin=T - 1, pos_end=T, seq_lens=dev.seq_lens)
+        return api.prune_select_rope_keys(q, k_rot, p, ROPE_BASE, seq_lens=dev.seq_lens, out=out)
+    variants.append(("chunk_indexed_rotated_keys", prune_rotated_keys))
     for name, prune in variants:
         idx = prune()
         out = api.sparse_attn(q, dev.k, dev.v, idx, p, **kw)
@@ -822,12 +833,18 @@ def rope_decode(args, reps=20):
     plain_idx = res.pop("plain_idx")
     out = {"plain_us": round(res["plain"], 2),
            "note": "back-to-back graph replays of one step (same query, one KV copy)"}
+    ci_idx = res["chunk_indexed_idx"].clone()
     for style in ROPE_STYLES:
         out[style] = {"us": round(res[style], 2), "overhead": round(res[style] / res["plain"], 3),
                       "index_row_changed": bool((res.pop(style + "_idx") != plain_idx).any().item())}
+    rk = "chunk_indexed_rotated_keys"
+    out[rk] = {"us": round(res[rk], 2), "overhead": round(res[rk] / res["plain"], 3),
+               "same_rows_as_chunk_indexed": bool(torch.equal(res.pop(rk + "_idx"), ci_idx)),
+               "note": "keys rotated once per stage (3 bf16 copies of K); each step rotates the newest key"}
     log("1M decode step: plain {:.1f} us, ".format(res["plain"]) +
-        ", ".join(f"{st} RoPE {res[st]:.1f} us" for st in ROPE_STYLES))
-    del dev
+        ", ".join(f"{st} RoPE {res[st]:.1f} us" for st in ROPE_STYLES) +
+        f", chunk_indexed over rotated keys {res[rk]:.1f} us")
+    del dev, k_rot
     torch.cuda.empty_cache()
     return out
 

@@ -25,6 +25,7 @@ EXPORTS = ("dsa_index_width", "dsa_workspace_bytes", "dsa_prune_select", "dsa_sp
            "dsa_block_sparse_index_width", "dsa_block_sparse_workspace_bytes", "dsa_block_sparse_select",
            "dsa_sparse_attn_heads", "dsa_vertical_slash_index_width", "dsa_vertical_slash_workspace_bytes",
            "dsa_vertical_slash_select", "dsa_prune_rope_workspace_bytes", "dsa_prune_select_rope",
+           "dsa_rope_rotate_keys", "dsa_prune_select_rope_keys",
            "dsa_check_decode_inputs", "dsa_profile_begin", "dsa_profile_end", "dsa_status_str", "dsa_last_error")
 
 
@@ -122,6 +123,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dsa_prune_select_rope.argtypes = [ctypes.POINTER(CShape), vp, vp, ctypes.POINTER(CParams),
                                           ctypes.POINTER(CRope), vp, vp, sz, vp]
     lib.dsa_prune_select_rope.restype = ctypes.c_int
+    lib.dsa_rope_rotate_keys.argtypes = [ctypes.POINTER(CShape), vp, ctypes.POINTER(CParams), ctypes.POINTER(CRope),
+                                         ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(vp), vp]
+    lib.dsa_rope_rotate_keys.restype = ctypes.c_int
+    lib.dsa_prune_select_rope_keys.argtypes = [ctypes.POINTER(CShape), vp, ctypes.POINTER(vp), ctypes.POINTER(CParams),
+                                               ctypes.POINTER(CRope), vp, vp, sz, vp]
+    lib.dsa_prune_select_rope_keys.restype = ctypes.c_int
     lib.dsa_profile_begin.argtypes = []
     lib.dsa_profile_begin.restype = ctypes.c_int
     lib.dsa_profile_end.argtypes = [ctypes.POINTER(CKernelTime), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
@@ -329,6 +336,24 @@ def prune_select_rope_raw(shape: Shape, q: int, k: int, p: Params, base: float, 
     rope = CRope(style, base)
     _check(load().dsa_prune_select_rope(ctypes.byref(cs), q, k, ctypes.byref(cp), ctypes.byref(rope), idx,
                                         ws or None, ws_bytes, stream or None))
+
+
+def rope_rotate_keys_raw(shape: Shape, k: int, p: Params, base: float, pos_begin: int, pos_end: int,
+                         k_rot: list, stream: int = 0):
+    cs, cp = shape.c(), p.c()
+    rope = CRope(DSA_ROPE_CHUNK_INDEXED, base)
+    ptrs = (ctypes.c_void_p * MAX_STAGES)(*[ctypes.c_void_p(x) for x in k_rot])
+    _check(load().dsa_rope_rotate_keys(ctypes.byref(cs), k, ctypes.byref(cp), ctypes.byref(rope), pos_begin, pos_end,
+                                       ptrs, stream or None))
+
+
+def prune_select_rope_keys_raw(shape: Shape, q: int, k_rot: list, p: Params, base: float, idx: int, ws: int,
+                               ws_bytes: int, stream: int = 0):
+    cs, cp = shape.c(), p.c()
+    rope = CRope(DSA_ROPE_CHUNK_INDEXED, base)
+    ptrs = (ctypes.c_void_p * MAX_STAGES)(*[ctypes.c_void_p(x) for x in k_rot])
+    _check(load().dsa_prune_select_rope_keys(ctypes.byref(cs), q, ptrs, ctypes.byref(cp), ctypes.byref(rope), idx,
+                                             ws or None, ws_bytes, stream or None))
 
 
 def profile_begin():

@@ -356,6 +356,62 @@ def rope_style_for_layer(layer: int, n_chunk_indexed: int = 3) -> str:
     return "chunk_indexed" if layer <= n_chunk_indexed else "relative"
 
 
+def rope_key_copies(k: torch.Tensor, params: Params) -> list:
+    """Buffers for the chunk-indexed rotated keys: one bf16 tensor shaped like
+    k per stage (filled by rope_rotate_keys)."""
+    return [torch.empty(k.shape, dtype=torch.bfloat16, device=k.device) for _ in range(len(params.chunk))]
+
+
+def rope_rotate_keys(k: torch.Tensor, params: Params, base: float, k_rot: list, *, pos_begin: int = 0,
+                     pos_end: Optional[int] = None, seq_lens: Optional[torch.Tensor] = None,
+                     t: Optional[int] = None) -> list:
+    """Chunk-indexed RoPE: write every stage's rotated rows of the keys at
+    positions [pos_begin, pos_end) into k_rot (decode layout, contiguous k)."""
+    if seq_lens is None:
+        raise ValueError("rope_rotate_keys is a decode call: pass seq_lens")
+    if len(k_rot) != len(params.chunk):
+        raise ValueError("one rotated key buffer per stage")
+    for x in k_rot:
+        if x.shape != k.shape or x.dtype != torch.bfloat16 or not x.is_contiguous():
+            raise ValueError("rotated key buffers are contiguous bf16 tensors shaped like k")
+    q_dummy = torch.empty((k.shape[0], k.shape[1], k.shape[3]), dtype=k.dtype, device=k.device)
+    shape = make_shape(q_dummy, k, seq_lens=seq_lens, t=t)
+    end = shape.t if pos_end is None else pos_end
+    _lib.rope_rotate_keys_raw(shape, k.data_ptr(), params, base, pos_begin, end, [x.data_ptr() for x in k_rot],
+                              _stream())
+    return k_rot
+
+
+def prune_select_rope_keys(q: torch.Tensor, k_rot: list, params: Params, base: float, *,
+                           seq_lens: torch.Tensor, t: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                           ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Chunk-indexed decode pruning over the rotated key copies of
+    rope_rotate_keys; idx as prune_select_rope(style="chunk_indexed")."""
+    if len(k_rot) != len(params.chunk):
+        raise ValueError("one rotated key buffer per stage")
+    _need(q, "q")
+    _need(seq_lens, "seq_lens")
+    if q.dim() != 3 or seq_lens.dtype != torch.int32 or seq_lens.numel() != q.shape[0]:
+        raise ValueError("decode expects q [B,Hq,d] and int32 seq_lens [B]")
+    kr = k_rot[0]
+    if kr.dim() != 4 or kr.shape[0] != q.shape[0] or kr.shape[3] != q.shape[2]:
+        raise ValueError("rotated key buffers must be [B,Hkv,t,d]")
+    # q's dtype describes the call; the rotated keys are bf16 either way
+    shape = Shape(DSA_DECODE, _dtype_code(q), q.shape[0], q.shape[1], kr.shape[1], q.shape[2],
+                  kr.shape[2] if t is None else t, seq_lens.data_ptr())
+    L = _lib.index_width(params)
+    if L < 0:
+        raise _lib.DsaError(_lib.DSA_ERR_INVALID_ARG, "invalid params")
+    if out is None:
+        out = torch.empty(shape.batch * L, dtype=torch.int32, device=q.device)
+    if out.numel() != shape.batch * L or out.dtype != torch.int32:
+        raise ValueError("idx buffer has the wrong size or dtype")
+    wsp, wsb = _scratch(_lib.prune_rope_workspace_bytes(shape, params, _lib.DSA_ROPE_CHUNK_INDEXED, base), q.device, ws)
+    _lib.prune_select_rope_keys_raw(shape, q.data_ptr(), [x.data_ptr() for x in k_rot], params, base, out.data_ptr(),
+                                    wsp, wsb, _stream())
+    return out.view(shape.batch, L)
+
+
 def prune_select_rope(q: torch.Tensor, k: torch.Tensor, params: Params, base: float, *,
                       seq_lens: Optional[torch.Tensor] = None, block_table: Optional[torch.Tensor] = None,
                       t: Optional[int] = None, out: Optional[torch.Tensor] = None,

@@ -287,11 +287,13 @@ dsa::PruneArgs prune_args(const dsa_shape* s, const void* q, const void* k, cons
   a.maxK = static_cast<int>(lay.maxK);
   a.maxNC = static_cast<int>(lay.maxNC);
   a.n1max = static_cast<int>(lay.n1max);
-  char* w = static_cast<char*>(ws);
-  a.cnt = reinterpret_cast<int32_t*>(w + lay.off_cnt);
-  a.starts = reinterpret_cast<int32_t*>(w + lay.off_starts);
   for (int i = 0; i < DSA_MAX_STAGES; ++i) a.slot[i] = i & 1;
-  a.scores = reinterpret_cast<uint32_t*>(w + lay.off_scores);
+  if (ws) {                                       // no workspace: the call reads none of it
+    char* w = static_cast<char*>(ws);
+    a.cnt = reinterpret_cast<int32_t*>(w + lay.off_cnt);
+    a.starts = reinterpret_cast<int32_t*>(w + lay.off_starts);
+    a.scores = reinterpret_cast<uint32_t*>(w + lay.off_scores);
+  }
   a.visited = reinterpret_cast<unsigned long long*>(visited);
   return a;
 }
@@ -788,8 +790,23 @@ size_t rope_key_bytes(const dsa_shape* s, const dsa_rope* r) {
   return align256(static_cast<size_t>(s->batch) * s->hkv * s->t * s->d * 2);
 }
 size_t rope_bytes(const dsa_shape* s, const dsa_params* p, const dsa_rope* r, const PruneLayout& lay) {
-  const int sets = r->style == DSA_ROPE_RELATIVE ? 2 : 1;
+  // relative: two query sets; chunk-indexed decode: one per stage (the
+  // rotated-key call rotates every stage's query at once); else one
+  const int sets = r->style == DSA_ROPE_RELATIVE ? 2 : s->mode == DSA_DECODE ? p->n_stages : 1;
   return lay.bytes + sets * rope_query_bytes(s, p, lay) + rope_key_bytes(s, r);
+}
+
+// The rotated-key calls: a chunk-indexed decode shape with contiguous K and n
+// non-NULL rotated copies.
+dsa_status check_rope_keys(const dsa_shape* s, const dsa_params* p, const dsa_rope* r, const void* const* k_rot) {
+  if (r->style != DSA_ROPE_CHUNK_INDEXED)
+    return fail(DSA_ERR_UNSUPPORTED, "rotated key copies are for the chunk-indexed style only");
+  if (s->mode != DSA_DECODE) return fail(DSA_ERR_INVALID_ARG, "rotated key copies are a decode layout");
+  if (s->block_table) return fail(DSA_ERR_UNSUPPORTED, "rotated key copies need contiguous K (block_table NULL)");
+  if (!k_rot) return fail(DSA_ERR_INVALID_ARG, "k_rot is NULL");
+  for (int i = 0; i < p->n_stages; ++i)
+    if (!k_rot[i]) return fail(DSA_ERR_INVALID_ARG, "k_rot[%d] is NULL", i);
+  return DSA_OK;
 }
 
 }  // namespace
@@ -836,6 +853,62 @@ dsa_status dsa_prune_select_rope(const dsa_shape* s, const void* q, const void* 
   uint16_t* kb = rope_key_bytes(s, rope) ? reinterpret_cast<uint16_t*>(w + lay.bytes + qb) : nullptr;
   hipError_t err = dsa::launch_prune_rope(a, s->dtype, rope->style, qa, qb2, kb, rope->base,
                                           static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(DSA_ERR_HIP, "prune launch failed: %s", hipGetErrorString(err));
+  return DSA_OK;
+}
+
+dsa_status dsa_rope_rotate_keys(const dsa_shape* s, const void* k, const dsa_params* p, const dsa_rope* rope,
+                                int32_t pos_begin, int32_t pos_end, void* const* k_rot, void* stream) {
+  g_err[0] = 0;
+  dsa_status st = check_shape(s);
+  if (st != DSA_OK) return st;
+  st = check_params(s, p);
+  if (st != DSA_OK) return st;
+  st = check_rope(rope);
+  if (st != DSA_OK) return st;
+  st = check_rope_keys(s, p, rope, k_rot);
+  if (st != DSA_OK) return st;
+  if (!k) return fail(DSA_ERR_INVALID_ARG, "k is NULL");
+  if (pos_begin < 0 || pos_end < pos_begin || pos_end > s->t)
+    return fail(DSA_ERR_INVALID_ARG, "positions [%d, %d) are not inside [0, t = %d]", pos_begin, pos_end, s->t);
+  const PruneLayout lay = prune_layout(s, p);
+  const dsa::PruneArgs a = prune_args(s, nullptr, k, p, nullptr, 0, lay, nullptr, nullptr);
+  uint16_t* kr[dsa::kMaxStages] = {};
+  for (int i = 0; i < p->n_stages; ++i) kr[i] = static_cast<uint16_t*>(const_cast<void*>(k_rot[i]));
+  hipError_t err = dsa::launch_rope_rotate_keys(a, s->dtype, kr, rope->base, pos_begin, pos_end,
+                                                static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(DSA_ERR_HIP, "key rotation launch failed: %s", hipGetErrorString(err));
+  return DSA_OK;
+}
+
+dsa_status dsa_prune_select_rope_keys(const dsa_shape* s, const void* q, const void* const* k_rot,
+                                      const dsa_params* p, const dsa_rope* rope, int32_t* idx, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  dsa_status st = check_shape(s);
+  if (st != DSA_OK) return st;
+  st = check_params(s, p);
+  if (st != DSA_OK) return st;
+  st = check_rope(rope);
+  if (st != DSA_OK) return st;
+  st = check_rope_keys(s, p, rope, k_rot);
+  if (st != DSA_OK) return st;
+  if (!q || !idx) return fail(DSA_ERR_INVALID_ARG, "q and idx must be non-NULL");
+  const long long L = index_width_ll(p);
+  if (L > (1LL << 30)) return fail(DSA_ERR_INVALID_ARG, "index width overflows");
+  const PruneLayout lay = prune_layout(s, p);
+  if (lay.maxNC > 32768)
+    return fail(DSA_ERR_UNSUPPORTED, "a stage would score %lld chunks per row (limit 32768)", lay.maxNC);
+  const size_t need = rope_bytes(s, p, rope, lay);
+  if (!ws || ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, need);
+  const dsa::PruneArgs a = prune_args(s, q, k_rot[0], p, idx, L, lay, ws, nullptr);
+  uint16_t* qa = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + lay.bytes);
+  const size_t qstride = rope_query_bytes(s, p, lay) / 2;     // elements between the stages' query sets
+  uint16_t* kr[dsa::kMaxStages] = {};
+  for (int i = 0; i < p->n_stages; ++i) kr[i] = static_cast<uint16_t*>(const_cast<void*>(k_rot[i]));
+  hipError_t err = dsa::launch_prune_rope_keys(a, s->dtype, qa, qstride, kr, rope->base,
+                                               static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return fail(DSA_ERR_HIP, "prune launch failed: %s", hipGetErrorString(err));
   return DSA_OK;
 }

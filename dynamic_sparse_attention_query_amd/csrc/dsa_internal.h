@@ -373,6 +373,16 @@ void launch_topk(const PruneArgs& a, int stage, int max_chunks, hipStream_t stre
 // kb (prefill) each stage's rotated keys in the layout of k (bf16).
 hipError_t launch_prune_rope(const PruneArgs& a, int dtype, int style, uint16_t* qa, uint16_t* qb, uint16_t* kb,
                              double base, hipStream_t stream);
+// Chunk-indexed decode over per-stage rotated key copies (bf16, layout of k):
+// the queries rotated for every stage into qa (stage s at qa + s * qstride),
+// then the plain decode stages on the rotated vectors.
+hipError_t launch_prune_rope_keys(const PruneArgs& a, int dtype, uint16_t* qa, size_t qstride,
+                                  uint16_t* const* k_rot, double base, hipStream_t stream);
+// Rotated copies (bf16) of the keys at positions [p_lo, p_hi) for every stage.
+hipError_t launch_rope_rotate_keys(const PruneArgs& a, int dtype, uint16_t* const* k_rot, double base, int p_lo,
+                                   int p_hi, hipStream_t stream);
+// Decode stages with per-stage arguments (bf16 rows), as[0 .. n_stages).
+hipError_t launch_prune_decode_staged(const PruneArgs* as, hipStream_t stream);
 // plain scoring of a prefill stage on bf16 rows (prune.hip)
 void launch_score_prefill_bf16(const PruneArgs& a, int stage, int max_chunks, hipStream_t stream, const char* name);
 // bf16, b_q = 64; ql and qr (the rotated query sets) select the relative-RoPE

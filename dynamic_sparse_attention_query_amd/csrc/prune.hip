@@ -578,6 +578,42 @@ hipError_t launch_prune_decode_stages(const PruneArgs& a, int dtype, hipStream_t
   return hipErrorInvalidValue;
 }
 
+// Decode pruning with its own (query, keys) per stage: as[s] holds the
+// arguments of stage s (bf16 rows: the rotated copies of the chunk-indexed
+// RoPE style), everything else shared. The stages run as in launch_decode.
+template <int D, int G>
+static void launch_decode_staged(const PruneArgs* as, hipStream_t st) {
+  const PruneArgs& a = as[0];
+  auto chunks_of = [&](int stage) { return stage == 0 ? a.n1max : a.keep[stage - 1] / a.chunk[stage]; };
+  launch_decode_score<uint16_t, D, G>(as[0], 0, chunks_of(0), st);
+  for (int stage = 1; stage < a.n_stages; ++stage) {
+    if (!launch_decode_fused<uint16_t, D, G>(as[stage], stage, chunks_of(stage), chunks_of(stage - 1), st)) {
+      launch_topk(as[stage - 1], stage - 1, chunks_of(stage - 1), st);
+      launch_decode_score<uint16_t, D, G>(as[stage], stage, chunks_of(stage), st);
+    }
+  }
+  launch_topk(as[a.n_stages - 1], a.n_stages - 1, chunks_of(a.n_stages - 1), st);
+}
+
+template <int D>
+static hipError_t launch_staged_d(const PruneArgs* as, hipStream_t st) {
+  switch (as[0].kv.Hq / as[0].kv.Hkv) {
+    case 1: launch_decode_staged<D, 1>(as, st); break;
+    case 2: launch_decode_staged<D, 2>(as, st); break;
+    case 4: launch_decode_staged<D, 4>(as, st); break;
+    case 8: launch_decode_staged<D, 8>(as, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prune_decode_staged(const PruneArgs* as, hipStream_t st) {
+  if (!as[0].kv.decode) return hipErrorInvalidValue;
+  if (as[0].kv.D == 128) return launch_staged_d<128>(as, st);
+  if (as[0].kv.D == 64) return launch_staged_d<64>(as, st);
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_prune(const PruneArgs& a, int dtype, hipStream_t st) {
   if (dtype == 1) {
     if (a.kv.D == 128) return launch_typed<uint16_t, 128>(a, st);

@@ -389,13 +389,17 @@ __device__ __forceinline__ int ci_query_id(const PruneArgs& a, int stage, const 
 
 // Rotated queries of one stage, in the layout of q (bf16): workgroup = (row,
 // head); the angles of the stage's query ID are tabled once, a query capped
-// at its own position computes its own.
+// at its own position computes its own. blockIdx.z selects stage stage0 + z,
+// written qstride elements after the previous stage's.
 template <typename T, int D>
-__global__ void __launch_bounds__(256) k_ci_queries(PruneArgs a, int stage, uint16_t* qo, double base) {
+__global__ void __launch_bounds__(256) k_ci_queries(PruneArgs a, int stage0, uint16_t* qo, double base,
+                                                    size_t qstride) {
   constexpr int half = D / 2;
   __shared__ double cs[half][2];
   const KvLayout& kv = a.kv;
   const int r = blockIdx.x, h = blockIdx.y;
+  const int stage = stage0 + blockIdx.z;
+  qo += blockIdx.z * qstride;
   int b, s, e;
   row_bounds(kv, r, b, s, e);
   const Geo geo = make_geo(s, e, a.n_sink, a.n_window, a.chunk[0]);
@@ -428,18 +432,27 @@ __global__ void __launch_bounds__(256) k_ci_queries(PruneArgs a, int stage, uint
   }
 }
 
-// Rotated keys of one prefill stage, in the layout of k (bf16): workgroup =
-// 32 positions of every (sequence, kv head); the angles of the (at most 33)
-// chunk indices the tile touches are tabled in LDS. Positions before n_sink
-// are never candidates and are left as they are.
+// Rotated keys of one stage, in the layout of k (bf16): workgroup = 32
+// positions of every (sequence, kv head) from p_lo, up to p_hi; the angles of
+// the (at most 33) chunk indices the tile touches are tabled in LDS.
+// Positions before n_sink are never candidates and are left as they are.
+// blockIdx.y selects stage stage0 + y, written to out.ko[y]. A key's chunk
+// index in a stage depends only on its position (the tiling is anchored at
+// n_sink), so a rotated copy stays valid as the context grows.
 constexpr int kCiTile = 32;
+struct CiKeyOut {
+  uint16_t* ko[kMaxStages];
+};
 template <typename T, int D>
-__global__ void __launch_bounds__(256) k_ci_keys(PruneArgs a, int stage, uint16_t* ko, double base) {
+__global__ void __launch_bounds__(256) k_ci_keys(PruneArgs a, int stage0, CiKeyOut out, double base, int p_lo,
+                                                 int p_hi) {
   constexpr int half = D / 2;
   __shared__ double cs[kCiTile + 1][half][2];
   const KvLayout& kv = a.kv;
-  const int p0 = max(blockIdx.x * kCiTile, a.n_sink);
-  const int p1 = min(static_cast<int>(blockIdx.x + 1) * kCiTile, kv.T);
+  const int stage = stage0 + blockIdx.y;
+  uint16_t* ko = out.ko[blockIdx.y];
+  const int p0 = max(p_lo + static_cast<int>(blockIdx.x) * kCiTile, a.n_sink);
+  const int p1 = min(p_lo + static_cast<int>(blockIdx.x + 1) * kCiTile, p_hi);
   if (p0 >= p1) return;
   const int lc = a.lchunk[stage];
   const int c0 = (p0 - a.n_sink) >> lc, nch = ((p1 - 1 - a.n_sink) >> lc) - c0 + 1;
@@ -780,7 +793,9 @@ static void launch_rope_decode(const PruneArgs& a, int style, uint16_t* qa, uint
     else    launch_decode_ci_g<T, D, G>(a, stage, chunks_of(stage), qa, base, st);
   };
   auto rotate = [&](int stage) {
-    if (!rt) DSA_LAUNCH(kCiQueryNames[stage], (k_ci_queries<T, D>), dim3(a.R, a.kv.Hq), dim3(256), st, a, stage, qa, base);
+    if (!rt)
+      DSA_LAUNCH(kCiQueryNames[stage], (k_ci_queries<T, D>), dim3(a.R, a.kv.Hq), dim3(256), st, a, stage, qa, base,
+                 size_t{0});
   };
   rotate(0);
   score(0);
@@ -823,9 +838,12 @@ static hipError_t launch_rope_typed(const PruneArgs& a, int style, uint16_t* qa,
                    stage, qa, qb);
       }
     } else if (max_chunks > 0) {
-      DSA_LAUNCH(kCiQueryNames[stage], (k_ci_queries<T, D>), dim3(a.R, a.kv.Hq), dim3(256), st, a, stage, qa, base);
+      DSA_LAUNCH(kCiQueryNames[stage], (k_ci_queries<T, D>), dim3(a.R, a.kv.Hq), dim3(256), st, a, stage, qa, base,
+                 size_t{0});
+      CiKeyOut ko{};
+      ko.ko[0] = kb;
       DSA_LAUNCH(kCiKeyNames[stage], (k_ci_keys<T, D>), dim3((a.kv.T + kCiTile - 1) / kCiTile), dim3(256), st, a,
-                 stage, kb, base);
+                 stage, ko, base, 0, a.kv.T);
       PruneArgs ar = a;                         // the plain scoring, on the rotated copies
       ar.q = qa;
       ar.k = kb;
@@ -836,6 +854,48 @@ static hipError_t launch_rope_typed(const PruneArgs& a, int style, uint16_t* qa,
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
+}
+
+// Chunk-indexed decode over rotated key copies: the query is rotated to every
+// stage's position ID in one launch (stage s at qa + s * qstride), then the
+// plain decode kernels run stage by stage on (rotated query, rotated keys of
+// that stage).
+hipError_t launch_prune_rope_keys(const PruneArgs& a, int dtype, uint16_t* qa, size_t qstride,
+                                  uint16_t* const* k_rot, double base, hipStream_t st) {
+  if (!a.kv.decode || a.kv.block_table) return hipErrorInvalidValue;
+  const dim3 grid(a.R, a.kv.Hq, a.n_stages);
+  if (dtype == 1) {
+    if (a.kv.D == 128) DSA_LAUNCH("prune_ci_queries", (k_ci_queries<uint16_t, 128>), grid, dim3(256), st, a, 0, qa, base, qstride);
+    else               DSA_LAUNCH("prune_ci_queries", (k_ci_queries<uint16_t, 64>), grid, dim3(256), st, a, 0, qa, base, qstride);
+  } else {
+    if (a.kv.D == 128) DSA_LAUNCH("prune_ci_queries", (k_ci_queries<float, 128>), grid, dim3(256), st, a, 0, qa, base, qstride);
+    else               DSA_LAUNCH("prune_ci_queries", (k_ci_queries<float, 64>), grid, dim3(256), st, a, 0, qa, base, qstride);
+  }
+  PruneArgs as[kMaxStages];
+  for (int s = 0; s < a.n_stages; ++s) {
+    as[s] = a;
+    as[s].q = qa + s * qstride;
+    as[s].k = k_rot[s];
+  }
+  return launch_prune_decode_staged(as, st);
+}
+
+// Rotated copies of the keys at positions [p_lo, p_hi) for every stage (the
+// chunk-indexed style), contiguous K of a decode shape.
+hipError_t launch_rope_rotate_keys(const PruneArgs& a, int dtype, uint16_t* const* k_rot, double base, int p_lo,
+                                   int p_hi, hipStream_t st) {
+  if (p_hi <= p_lo) return hipSuccess;
+  CiKeyOut ko{};
+  for (int s = 0; s < a.n_stages; ++s) ko.ko[s] = k_rot[s];
+  const dim3 grid((p_hi - p_lo + kCiTile - 1) / kCiTile, a.n_stages);
+  if (dtype == 1) {
+    if (a.kv.D == 128) DSA_LAUNCH("rope_rotate_keys", (k_ci_keys<uint16_t, 128>), grid, dim3(256), st, a, 0, ko, base, p_lo, p_hi);
+    else               DSA_LAUNCH("rope_rotate_keys", (k_ci_keys<uint16_t, 64>), grid, dim3(256), st, a, 0, ko, base, p_lo, p_hi);
+  } else {
+    if (a.kv.D == 128) DSA_LAUNCH("rope_rotate_keys", (k_ci_keys<float, 128>), grid, dim3(256), st, a, 0, ko, base, p_lo, p_hi);
+    else               DSA_LAUNCH("rope_rotate_keys", (k_ci_keys<float, 64>), grid, dim3(256), st, a, 0, ko, base, p_lo, p_hi);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_prune_rope(const PruneArgs& a, int dtype, int style, uint16_t* qa, uint16_t* qb, uint16_t* kb,

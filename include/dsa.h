@@ -264,9 +264,11 @@ typedef struct {
   double base;       /* rotary base (e.g. 10000 or 500000), > 1 */
 } dsa_rope;
 
-/* Workspace bytes of dsa_prune_select_rope for this rope style: the pruning
+/* Workspace bytes of dsa_prune_select_rope (and, for a chunk-indexed decode
+ * shape, of dsa_prune_select_rope_keys) for this rope style: the pruning
  * workspace plus rotated copies in bf16 (relative: two of the queries;
- * chunk-indexed: one of the queries, and in prefill one of the keys). */
+ * chunk-indexed: one of the queries per stage in decode, one of the queries
+ * and one of the keys in prefill). */
 dsa_status dsa_prune_rope_workspace_bytes(const dsa_shape* shape, const dsa_params* p, const dsa_rope* rope,
                                           size_t* out_bytes);
 
@@ -277,6 +279,31 @@ dsa_status dsa_prune_rope_workspace_bytes(const dsa_shape* shape, const dsa_para
  * dsa_prune_rope_workspace_bytes. */
 dsa_status dsa_prune_select_rope(const dsa_shape* shape, const void* q, const void* k, const dsa_params* p,
                                  const dsa_rope* rope, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+
+/* Chunk-indexed decode with the keys rotated once. In a stage of chunk length
+ * l a key's chunk index (j - n_sink) / l depends only on its position, so its
+ * rotated row in that stage never changes as the context grows; only the
+ * query's position does. dsa_rope_rotate_keys writes, for every stage i, the
+ * rotated rows (bf16, the values dsa_prune_select_rope computes) of the keys
+ * at positions [pos_begin, pos_end) of every sequence and kv head into
+ * k_rot[i]; call it over [0, t) once and then for each appended range. Rows
+ * before n_sink are never candidates and are not written.
+ *   shape      DECODE, contiguous K (block_table NULL): k [B, Hkv, t, d]
+ *   k_rot      HOST array of p->n_stages DEVICE pointers, each a caller-owned
+ *              bf16 buffer [B, Hkv, t, d] (the layout of k)
+ *   pos_begin, pos_end   0 <= pos_begin <= pos_end <= t
+ *   rope       style DSA_ROPE_CHUNK_INDEXED (else DSA_ERR_UNSUPPORTED)
+ * dsa_prune_select_rope_keys then prunes as dsa_prune_select_rope does for the
+ * chunk-indexed style, reading the rotated copies instead of k (every
+ * position a sequence's stages can score must have been rotated: [n_sink,
+ * seq_len - n_window)); idx is identical to dsa_prune_select_rope's. Each
+ * step rotates only the query (one launch for all stages), then runs the
+ * plain decode kernels. ws: at least dsa_prune_rope_workspace_bytes() bytes. */
+dsa_status dsa_rope_rotate_keys(const dsa_shape* shape, const void* k, const dsa_params* p, const dsa_rope* rope,
+                                int32_t pos_begin, int32_t pos_end, void* const* k_rot, void* stream);
+dsa_status dsa_prune_select_rope_keys(const dsa_shape* shape, const void* q, const void* const* k_rot,
+                                      const dsa_params* p, const dsa_rope* rope, int32_t* idx, void* ws,
+                                      size_t ws_bytes, void* stream);
 
 /* ---- Block-sparse heads --------------------------------------------------
  * MInference page, "Online Dynamic Index Estimation: Block-Sparse Heads

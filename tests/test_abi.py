@@ -238,6 +238,34 @@ def test_prune_rope_sizes_and_rejections():
     assert ei.value.status == DSA_ERR_WORKSPACE
 
 
+def test_rotated_key_calls_reject_before_launch():
+    d = Shape(DSA_DECODE, DSA_BF16, 1, 32, 8, 128, 1 << 20, seq_lens=16)
+    pre = Shape(DSA_PREFILL, DSA_BF16, 1, 32, 8, 128, 4096)
+    paged = Shape(DSA_DECODE, DSA_BF16, 1, 32, 8, 128, 1 << 20, seq_lens=16, block_table=32, page_size=64,
+                  max_pages=1 << 14)
+    bufs = [256] * len(P3.chunk)
+    for shape, prm, code in [(pre, P2, DSA_ERR_INVALID_ARG), (paged, P3, DSA_ERR_UNSUPPORTED)]:
+        with pytest.raises(_lib.DsaError) as ei:
+            _lib.rope_rotate_keys_raw(shape, 256, prm, 10000.0, 0, 16, bufs)
+        assert ei.value.status == code
+    for lo, hi in [(-1, 16), (32, 16), (0, (1 << 20) + 1)]:
+        with pytest.raises(_lib.DsaError) as ei:
+            _lib.rope_rotate_keys_raw(d, 256, P3, 10000.0, lo, hi, bufs)
+        assert ei.value.status == DSA_ERR_INVALID_ARG, (lo, hi)
+    with pytest.raises(_lib.DsaError) as ei:
+        _lib.rope_rotate_keys_raw(d, 256, P3, 10000.0, 0, 16, [256, 0, 256])
+    assert ei.value.status == DSA_ERR_INVALID_ARG
+    need = _lib.prune_rope_workspace_bytes(d, P3, _lib.DSA_ROPE_CHUNK_INDEXED)
+    rel = _lib.prune_rope_workspace_bytes(d, P3, _lib.DSA_ROPE_RELATIVE)          # two query sets
+    assert need - rel == 32 * 128 * 2                                               # three: one per stage
+    with pytest.raises(_lib.DsaError) as ei:
+        _lib.prune_select_rope_keys_raw(d, 256, bufs, P3, 10000.0, 256, 256, need - 1)
+    assert ei.value.status == DSA_ERR_WORKSPACE
+    with pytest.raises(_lib.DsaError) as ei:
+        _lib.prune_select_rope_keys_raw(pre, 256, bufs, P2, 10000.0, 256, 256, need)
+    assert ei.value.status == DSA_ERR_INVALID_ARG
+
+
 def test_rope_style_for_layer_follows_the_page_assignment():
     from dynamic_sparse_attention_query_amd import api
     assert [api.rope_style_for_layer(l) for l in (1, 2, 3)] == ["chunk_indexed"] * 3

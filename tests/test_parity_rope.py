@@ -218,3 +218,44 @@ def test_rope_prefill_two_sequences(style):
         for m in range(case.cfg.t // case.cfg.block_q):
             want = oracle_row_rt(case, b, m, style=style)
             assert np.array_equal(idx[b, m], want), f"seq {b} block {m}: first diff {np.flatnonzero(idx[b, m] != want)[:5]}"
+
+
+def _rotated_keys_step(case, dev, p, q, pieces=1):
+    """Chunk-indexed decode over keys rotated once (dsa_rope_rotate_keys, in
+    `pieces` consecutive position ranges), then dsa_prune_select_rope_keys."""
+    k_rot = api.rope_key_copies(dev.k, p)
+    T = dev.k.shape[2]
+    cuts = np.linspace(0, T, pieces + 1).astype(int)
+    for lo, hi in zip(cuts[:-1], cuts[1:]):
+        api.rope_rotate_keys(dev.k, p, BASE, k_rot, pos_begin=int(lo), pos_end=int(hi), seq_lens=dev.seq_lens)
+    idx = api.prune_select_rope_keys(q, k_rot, p, BASE, seq_lens=dev.seq_lens)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), k_rot
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d,chunk,keep", [
+    ("bf16", 32, 8, 128, (256, 32, 8), (8192, 2048, 1024)),     # the 1M configuration's stage shapes
+    ("bf16", 8, 2, 64, (64, 16, 4), (2048, 512, 128)),
+    ("f32", 8, 8, 64, (64, 4, 1), (2048, 512, 128)),           # fp32 inputs, one-key chunks
+])
+def test_ci_decode_over_rotated_keys(dtype, hq, hkv, d, chunk, keep):
+    """Keys rotated once per stage give the rows of the chunk-indexed decode
+    that rotates them every step, bit for bit, and those of the oracle; the
+    rotation written in three position ranges equals one pass over all."""
+    case = gen.make_case("c3", hq=hq, hkv=hkv, d=d, t=40000, dtype=dtype, chunk=chunk, keep=keep, batch=2,
+                         n_queries=1)
+    case.seq_lens[:] = [40000, 23456]
+    H.say(f"rope chunk_indexed decode over rotated keys {dtype} {hq}/{hkv} d={d} chunk={chunk}")
+    dev = to_device(case)
+    p = params_of(case.cfg)
+    q = dev.q[0].contiguous()
+    want = api.prune_select_rope(q, dev.k, p, BASE, seq_lens=dev.seq_lens, style="chunk_indexed").cpu().numpy()
+    got, k1 = _rotated_keys_step(case, dev, p, q)
+    assert np.array_equal(got, want), f"first diff {np.flatnonzero(got != want)[:5]}"
+    for b in range(case.cfg.batch):
+        assert np.array_equal(got[b], oracle_row_rt(case, b, 0, style="chunk_indexed")), f"sequence {b}"
+    got3, k3 = _rotated_keys_step(case, dev, p, q, pieces=3)
+    assert np.array_equal(got3, want)
+    ns = case.cfg.n_sink
+    for s in range(len(k1)):
+        assert torch.equal(k1[s][:, :, ns:], k3[s][:, :, ns:]), f"stage {s}: rotated rows differ by range split"
