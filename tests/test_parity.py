@@ -41,20 +41,22 @@ def gpu_decode(dev, p, qi=0, visited=None):
 
 
 def check_prefill_blocks(case, idx, out, blocks, attn_blocks=None, b=0):
+    """Index rows of `blocks` bit for bit, attention of `attn_blocks` (default:
+    the same) within tolerance; each oracle row is computed once, and only
+    the checked blocks' outputs are copied to the host."""
     idx_np = idx.cpu().numpy()
-    for m in blocks:
-        want = H.oracle_row(case, b, m)
-        got = idx_np[b, m]
-        assert np.array_equal(got, want), f"block {m}: first diff at {np.flatnonzero(got != want)[:5]}"
     cfg = case.cfg
-    out_np = None
-    for m in (attn_blocks if attn_blocks is not None else blocks):
-        if out_np is None:
-            out_np = out.cpu().numpy()
-        row = H.oracle_row(case, b, m)
-        want = H.oracle_attend(case, b, m, row)
-        s, e = m * cfg.block_q, (m + 1) * cfg.block_q
-        H.assert_close(out_np[b, :, s:e], want, f"block {m} attention")
+    rows = set(blocks)
+    attn = set(attn_blocks if attn_blocks is not None else blocks)
+    for m in sorted(rows | attn):
+        want = H.oracle_row(case, b, m)
+        if m in rows:
+            got = idx_np[b, m]
+            assert np.array_equal(got, want), f"block {m}: first diff at {np.flatnonzero(got != want)[:5]}"
+        if m in attn:
+            s, e = m * cfg.block_q, (m + 1) * cfg.block_q
+            got_out = out[b, :, s:e].cpu().numpy()
+            H.assert_close(got_out, H.oracle_attend(case, b, m, want), f"block {m} attention")
 
 
 # --------------------------------------------------------------------------- #
@@ -154,6 +156,21 @@ def test_c2_prefill_32k_sampled():
     for nd in case.needles:
         row = set(idx_np[nd.b, nd.query // cfg.block_q].tolist())
         assert set(range(nd.slot_start, nd.slot_start + nd.length)) <= row
+
+
+def test_c2_prefill_128k_sampled():
+    """The 128K prefill the bench times (same shape, inputs and launches):
+    index rows and attention on about 35 sampled query blocks, among them the
+    first rows whose stage 1 prunes and the widest (last) rows."""
+    case = gen.make_case("c2_128k")
+    cfg = case.cfg
+    H.say("c2: 128K prefill, sampled blocks")
+    dev = to_device(case)
+    p = params_of(cfg)
+    idx, out = gpu_prefill(dev, p)
+    nblk = cfg.t // cfg.block_q
+    blocks = sorted(set(gen.sample_blocks(nblk, 32, cfg.seed + 1)) | {300, nblk - 2, nblk - 1})
+    check_prefill_blocks(case, idx, out, blocks, attn_blocks=blocks)
 
 
 # --------------------------------------------------------------------------- #
