@@ -176,13 +176,9 @@ __global__ void __launch_bounds__(256, 2) k_decode_attend(StepArgs s) {
   // sum over the wave's four lane groups, then over the waves in LDS
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
-    lsum[hh] += __shfl_xor(lsum[hh], 16);
-    lsum[hh] += __shfl_xor(lsum[hh], 32);
+    lsum[hh] = rows4_sum(lsum[hh]);
 #pragma unroll
-    for (int x = 0; x < EPL; ++x) {
-      o[hh][x] += __shfl_xor(o[hh][x], 16);
-      o[hh][x] += __shfl_xor(o[hh][x], 32);
-    }
+    for (int x = 0; x < EPL; ++x) o[hh][x] = rows4_sum(o[hh][x]);
   }
   if (lane < 16) {
 #pragma unroll

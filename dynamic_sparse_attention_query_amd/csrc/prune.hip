@@ -130,11 +130,11 @@ __global__ void __launch_bounds__(kTopkThreads) k_assemble(PruneArgs a) {
 // ------------------------------------------------------------------------- //
 // One lane group's SelectRep tournaments over the chunk of chunk[stage] keys
 // starting at st, on the rows of kv head g as stored.
-template <typename T, int D, int G, int SPEC, bool PAGED>
+template <typename T, int D, int G, int SPEC, bool PAGED, bool TAIL4 = false>
 __device__ __forceinline__ float score_group(const PruneArgs& a, int stage, int b, int g, int li, int st,
                                              const RowSlice<T, D / 16> (&q)[G]) {
   const ChunkRows<T, D, PAGED> rows(a, b, g, li, st, a.chunk[stage]);
-  return selectrep_group<T, D, G, SPEC>(a, stage, li, st, rows, q);
+  return selectrep_group<T, D, G, SPEC, ChunkRows<T, D, PAGED>, TAIL4>(a, stage, li, st, rows, q);
 }
 
 // Workgroup = 16 lane groups of 16 lanes; a group owns one (chunk, kv head)
@@ -260,7 +260,7 @@ __global__ void __launch_bounds__(256, 2) k_topk_score_decode(PruneArgs a, int s
   const int st = kept_start(a, ps, skept[min(j >> sh, n_sel - 1)], sprev) +
                  ((j & ((1 << sh) - 1)) << a.lchunk[stage]);
   float best = -INFINITY;
-  if (active) best = score_group<T, D, G, SPEC, PAGED>(a, stage, b, g, li, st, q);
+  if (active) best = score_group<T, D, G, SPEC, PAGED, true>(a, stage, b, g, li, st, q);
   if (li == 0) red[gi] = best;
   __syncthreads();
   if (tid < cpw) {

@@ -676,7 +676,7 @@ k_topk_score_decode_rope(PruneArgs a, int stage, const uint16_t* qa, const uint1
       best = score_group_rt<T, D, G, SPEC, false>(a, stage, b, g, li, st, qx, qy);
     } else {
       const CiRows<T, D, false> rows(a, stage, b, g, li, st, theta);
-      best = selectrep_group<T, D, G, SPEC>(a, stage, li, st, rows, qx);
+      best = selectrep_group<T, D, G, SPEC, CiRows<T, D, false>, true>(a, stage, li, st, rows, qx);
     }
   }
   if (li == 0) red[gi] = best;

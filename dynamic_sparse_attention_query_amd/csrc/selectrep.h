@@ -12,9 +12,10 @@ namespace dsa {
 // come from `rows` (rows.at(position) returns this lane's slice of a key row:
 // as stored, or transformed). The first split's two representatives are shared
 // by all heads; with SPEC, the SPEC keys that can represent the first
-// log2(SPEC) splits are loaded in one round. Returns the best representative
-// score over the heads.
-template <typename T, int D, int G, int SPEC, class Rows>
+// log2(SPEC) splits are loaded in one round; with TAIL4 (latency-bound
+// launches), the last two splits of a 4-key range too. Returns the best
+// representative score over the heads.
+template <typename T, int D, int G, int SPEC, class Rows, bool TAIL4 = false>
 __device__ __forceinline__ float selectrep_group(const PruneArgs& a, int stage, int li, int st, const Rows& rows,
                                                  const RowSlice<T, D / 16> (&q)[G]) {
   using Row = RowSlice<T, D / 16>;
@@ -125,6 +126,42 @@ __device__ __forceinline__ float selectrep_group(const PruneArgs& a, int stage, 
     width = mid0;
   }
   for (int wdt = width >> 1; wdt >= 1; wdt >>= 1) {   // remaining splits
+    if (TAIL4 && wdt == 2) {
+      // The last two splits of a 4-key range [lo, lo + 3]: its other three
+      // keys are loaded in one round (one dependent round fewer, one row per
+      // head more); the first split compares lo with lo + 2, the second the
+      // winner with its neighbour; the visits counted are the method's.
+      Row k1[G], k2[G], k3[G];
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        k1[hh] = rows.at(st + lo[hh] + 1);
+        k2[hh] = rows.at(st + lo[hh] + 2);
+        k3[hh] = rows.at(st + lo[hh] + 3);
+      }
+      int m1[G], m2[G];
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const float s1 = dot(k1[hh], hh), s2 = dot(k2[hh], hh), s3 = dot(k3[hh], hh);
+        m1[hh] = lo[hh] + 2;
+        float sn = s1;
+        if (s2 > sa[hh]) { lo[hh] += 2; sa[hh] = s2; sn = s3; }
+        m2[hh] = lo[hh] + 1;
+        if (sn > sa[hh]) { lo[hh] += 1; sa[hh] = sn; }
+      }
+      if (a.visited) {
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          bool f1 = true, f2 = true;
+#pragma unroll
+          for (int h2 = 0; h2 < hh; ++h2) {
+            f1 = f1 && (m1[h2] != m1[hh]);
+            f2 = f2 && (m2[h2] != m2[hh]);
+          }
+          nvis += (f1 ? 1 : 0) + (f2 ? 1 : 0);
+        }
+      }
+      break;
+    }
     Row kk[G];
     int mid[G];
 #pragma unroll

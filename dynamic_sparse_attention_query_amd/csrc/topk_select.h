@@ -263,10 +263,17 @@ namespace dsa {
 // writes need no branch). Keys are 0 for absent chunks (real keys are never
 // 0). Returns the number kept.
 constexpr int kHistBins = 2048;
+// The histogram is stored as 64 blocks of 32 bins, each followed by 4 words of
+// padding: a lane's block then starts 4 banks after its left neighbour's, so
+// the wave's 16-byte reads of whole blocks (the scan) are free of bank
+// conflicts (unpadded, every lane's block starts on the same bank).
+constexpr int kHistBlock = 36;
+constexpr int kHistWords = kHistBins / 32 * kHistBlock;
+__device__ __forceinline__ uint32_t hist_slot(uint32_t bin) { return bin + ((bin >> 5) << 2); }
 
 template <int NW>
 struct SelectColLds {
-  uint32_t hist[2][kHistBins + 64];              // + one spare bin per lane (second pass)
+  uint32_t hist[2][kHistWords + 64];             // + one spare bin per lane (second pass)
   uint32_t wred[2][NW];
   uint32_t wcnt[NW];
 };
@@ -275,7 +282,7 @@ template <int E, int NT = kTopkThreads>
 __device__ __forceinline__ int select_cols(const uint32_t (&key)[E], int nc, int kc, SelectColLds<NT / 64>& L,
                                            int* kept) {
   constexpr int NW = NT / 64;
-  constexpr uint32_t kSpare = kHistBins;
+  constexpr uint32_t kSpare = kHistWords;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int jw = w * 64 * E + lane;                // index of column x: jw + 64 x
   if (nc <= kc) {                                  // every chunk is kept, in index order
@@ -300,7 +307,7 @@ __device__ __forceinline__ int select_cols(const uint32_t (&key)[E], int nc, int
     L.wred[1][w] = vor;
   }
   {
-    constexpr int N4 = 2 * (kHistBins + 64) / 4;
+    constexpr int N4 = 2 * (kHistWords + 64) / 4;
     uint4* h4 = reinterpret_cast<uint4*>(&L.hist[0][0]);
 #pragma unroll
     for (int i = 0; i < (N4 + NT - 1) / NT; ++i)
@@ -320,7 +327,7 @@ __device__ __forceinline__ int select_cols(const uint32_t (&key)[E], int nc, int
 #pragma unroll
   for (int x = 0; x < E; ++x) {
     d[x] = (vor - k[x]) >> lsb;
-    atomicAdd(&L.hist[0][min(d[x] >> s, static_cast<uint32_t>(kHistBins - 1))], 1u);
+    atomicAdd(&L.hist[0][hist_slot(min(d[x] >> s, static_cast<uint32_t>(kHistBins - 1)))], 1u);
   }
   __syncthreads();
   uint32_t base = 0u;                              // lower edge (in d) of the boundary bin
@@ -328,7 +335,7 @@ __device__ __forceinline__ int select_cols(const uint32_t (&key)[E], int nc, int
   bool whole = false;
   for (int p = 0;; ++p) {
     const uint32_t* H = L.hist[p & 1];
-    const uint4* H4 = reinterpret_cast<const uint4*>(H) + lane * 8;
+    const uint4* H4 = reinterpret_cast<const uint4*>(H + lane * kHistBlock);
     uint32_t sl = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -338,7 +345,7 @@ __device__ __forceinline__ int select_cols(const uint32_t (&key)[E], int nc, int
     const uint32_t il = wave_incl_scan_u32(sl);
     const int bl = __ffsll(static_cast<long long>(__ballot(il >= static_cast<uint32_t>(need)))) - 1;
     const uint32_t above_l = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(il - sl), bl));
-    const uint32_t c = lane < 32 ? H[bl * 32 + lane] : 0u;
+    const uint32_t c = lane < 32 ? H[bl * kHistBlock + lane] : 0u;
     const uint32_t ic = wave_incl_scan_u32(c);
     const int bi = __ffsll(static_cast<long long>(__ballot(above_l + ic >= static_cast<uint32_t>(need)))) - 1;
     const int cnt_in = __builtin_amdgcn_readlane(static_cast<int>(c), bi);
@@ -351,20 +358,22 @@ __device__ __forceinline__ int select_cols(const uint32_t (&key)[E], int nc, int
     uint32_t* Hn = L.hist[(p + 1) & 1];
     if (p >= 1) {                                  // a third pass reuses the first buffer
       __syncthreads();                             // every wave has scanned it
-      for (int i = tid; i < kHistBins; i += NT) Hn[i] = 0u;
+      for (int i = tid; i < kHistWords; i += NT) Hn[i] = 0u;
       __syncthreads();
     }
 #pragma unroll
     for (int x = 0; x < E; ++x) {
       const uint32_t r = d[x] - base;              // wraps for keys above the bin
-      atomicAdd(&Hn[r < wprev ? r >> s : kSpare + lane], 1u);
+      atomicAdd(&Hn[r < wprev ? hist_slot(r >> s) : kSpare + lane], 1u);
     }
     __syncthreads();
   }
 
   // kept: d below the boundary bin (or inside it when it is kept whole), and
   // the lowest-index `need` keys equal to the threshold d == base otherwise.
-  const int need_eq = whole ? 0 : need;
+  // (the counts below are the same in every lane; readfirstlane lets the
+  // compiler keep them, and the branches on them, scalar)
+  const int need_eq = __builtin_amdgcn_readfirstlane(whole ? 0 : need);
   const uint32_t wbin = whole ? (1u << s) : 0u;    // width of the boundary bin kept whole
   const uint32_t eqv = whole ? 0xffffffffu : base; // d of the ties (none when whole)
   auto strict_of = [&](int x) { return d[x] < base || d[x] - base < wbin; };
@@ -383,6 +392,8 @@ __device__ __forceinline__ int select_cols(const uint32_t (&key)[E], int nc, int
     cs += i < w ? static_cast<int>(v >> 16) : 0;
     ce += i < w ? static_cast<int>(v & 0xffffu) : 0;
   }
+  cs = __builtin_amdgcn_readfirstlane(cs);
+  ce = __builtin_amdgcn_readfirstlane(ce);
   int run = cs + min(ce, need_eq);                 // output slot of this wave's next kept key
   int* spare = kept + kc + lane;
 #pragma unroll
