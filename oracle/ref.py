@@ -572,6 +572,17 @@ def bs_rows(Q: np.ndarray, K, block: int, k_blocks: int) -> List[List[np.ndarray
     return rows
 
 
+def bs_lists(Q: np.ndarray, K, block: int, k_blocks: int) -> List[List[np.ndarray]]:
+    """Step 4's block index lists as lists: lists[h][m] = the ascending ids of
+    the key blocks kept for query head h and query block m (the page's
+    block-sparse kernel takes these ids, not positions)."""
+    Qp = bs_pool(Q, block)
+    Kp = bs_pool(np.asarray(K[:, :Q.shape[1]]), block)
+    Hq, nblk = Qp.shape[0], Qp.shape[1]
+    return [[bs_select(bs_block_scores(Qp, Kp, h, m), k_blocks).astype(np.int64) for m in range(nblk)]
+            for h in range(Hq)]
+
+
 def bs_index_width(block: int, k_blocks: int) -> int:
     """Width of a block-sparse index row: k_b blocks of `block` positions,
     rounded up to 64."""
@@ -633,6 +644,48 @@ def vs_row(i_v: np.ndarray, i_s: np.ndarray, m: int) -> np.ndarray:
     cols = [int(v) for v in i_v if v < e and int(v) // VS_BLOCK not in blocks]
     pos = [VS_BLOCK * b + x for b in sorted(blocks) for x in range(VS_BLOCK)] + cols
     return np.array(sorted(pos), dtype=np.int64)
+
+
+def vs_lists(i_v: np.ndarray, i_s: np.ndarray, m: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Step 4 for query block m in the two lists of the hybrid kernel
+    (MInference page, "Vertical-Slash Hybrid Kernel (Appendix C.4.2,
+    Algorithms 4 and 5)": a block index list for the slash part, attended in
+    whole 64-key blocks, and a column index list for the vertical part,
+    gathered). Blocks: the ascending ids of the 64-aligned key blocks that
+    the kept offsets' key ranges [64m - d, 64m + 63 - d] (clipped at key 0)
+    touch. Columns: the kept columns before the block's end in none of those
+    blocks, ascending. The positions of the blocks and the columns together
+    are the row of vs_row."""
+    s, e = VS_BLOCK * m, VS_BLOCK * (m + 1)
+    touched = np.zeros(m + 1, dtype=bool)          # key blocks 0..m (later ones hold no key < e)
+    for d in np.asarray(i_s, dtype=np.int64):
+        lo, hi = max(0, s - int(d)), e - 1 - int(d)
+        if hi >= 0:
+            touched[lo // VS_BLOCK:hi // VS_BLOCK + 1] = True
+    iv = np.sort(np.asarray(i_v, dtype=np.int64))
+    iv = iv[iv < e]
+    cols = iv[~touched[iv // VS_BLOCK]]
+    return np.nonzero(touched)[0].astype(np.int64), cols
+
+
+def vs_lists_all(Q: np.ndarray, K, k_v: int, k_s: int) -> List[List[Tuple[np.ndarray, np.ndarray]]]:
+    """lists[h][m] = vs_lists(...) of one sequence (estimation and selection as
+    in vs_rows)."""
+    Hq, T, _ = Q.shape
+    out = []
+    for h in range(Hq):
+        sv, ss = vs_sums(Q, K, h)
+        iv, is_ = vs_select(sv, k_v), vs_select(ss, k_s)
+        out.append([vs_lists(iv, is_, m) for m in range(T // VS_BLOCK)])
+    return out
+
+
+def list_positions(blocks: np.ndarray, cols: np.ndarray, block: int = VS_BLOCK) -> np.ndarray:
+    """The key positions of a block list and a column list: every key of each
+    listed block and every listed column, ascending (the two are disjoint)."""
+    b = np.asarray(blocks, dtype=np.int64)
+    pos = (b[:, None] * block + np.arange(block)[None, :]).reshape(-1)
+    return np.sort(np.concatenate([pos, np.asarray(cols, dtype=np.int64)]))
 
 
 def vs_index_width(T: int, k_v: int, k_s: int) -> int:

@@ -768,6 +768,54 @@ def test_vs_row_structure_and_width():
                     assert v in set(row.tolist())
 
 
+def test_vs_lists_worked_example():
+    """The hybrid kernel's two lists on the hand-worked example: the blocks
+    and the columns of each query block as worked out by hand."""
+    g = _load("p3_vs_rows_example.json")
+    iv, is_ = np.array(g["i_v"]), np.array(g["i_s"])
+    for r in g["rows"]:
+        blocks, cols = ref.vs_lists(iv, is_, r["m"])
+        assert list(blocks) == r["blocks"], r["why"]
+        assert list(cols) == r["columns"], r["why"]
+
+
+def test_vs_lists_are_the_row():
+    """Blocks and columns are disjoint, ascending, causal, and together give
+    exactly the positions of vs_row (two independent restatements of the
+    index-building step)."""
+    rng = np.random.default_rng(21)
+    T = 64 * 24
+    for k_v, k_s in [(7, 3), (40, 11), (0, 5), (12, 0), (200, 60)]:
+        iv = np.sort(rng.choice(T, size=k_v, replace=False))
+        is_ = np.sort(rng.choice(T, size=k_s, replace=False))
+        for m in range(T // 64):
+            blocks, cols = ref.vs_lists(iv, is_, m)
+            assert np.all(np.diff(blocks) > 0) and (len(blocks) == 0 or (blocks.min() >= 0 and blocks.max() <= m))
+            assert np.all(np.diff(cols) > 0) and (len(cols) == 0 or cols.max() < 64 * (m + 1))
+            assert not np.isin(cols // 64, blocks).any()
+            assert len(blocks) <= min(m + 1, 2 * k_s) and len(cols) <= k_v
+            assert np.array_equal(ref.list_positions(blocks, cols), ref.vs_row(iv, is_, m))
+    # offsets on block boundaries: offset 64 covers exactly key block m - 1,
+    # offset 192 exactly block m - 3 (one key more would reach the next block)
+    for m in range(T // 64):
+        blocks, cols = ref.vs_lists(np.array([5, 700]), np.array([64, 192]), m)
+        assert list(blocks) == [x for x in (m - 3, m - 1) if x >= 0]
+        assert list(cols) == [c for c in (5, 700) if c < 64 * (m + 1) and c // 64 not in blocks]
+
+
+def test_bs_lists_are_the_rows():
+    """The block-sparse block lists expand to the block-sparse index rows."""
+    rng = np.random.default_rng(22)
+    Hq, Hkv, T, d = 4, 2, 64 * 9, 16
+    Q, K = grid(rng, (Hq, T, d)), grid(rng, (Hkv, T, d))
+    for kb in (1, 3, 20):
+        rows, lists = ref.bs_rows(Q, K, 64, kb), ref.bs_lists(Q, K, 64, kb)
+        for h in range(Hq):
+            for m in range(T // 64):
+                assert len(lists[h][m]) == min(m + 1, kb)
+                assert np.array_equal(ref.list_positions(lists[h][m], np.array([], np.int64)), rows[h][m])
+
+
 def test_vs_every_offset_is_dense_causal_attention():
     """k_s covering every offset keeps every causal block: vertical-slash
     attention is then dense causal attention (library SDPA)."""
