@@ -613,10 +613,32 @@ def block_sparse_bench(args, res, reps=3):
         dense_ms = e0.elapsed_time(e1)
     res["block_sparse"] = dict(ms=ms, attn_tflop=attn_f / 1e12, est_tflop_fp64=est_f / 1e12,
                                est_ms=est_ms, attn_ms=attn_ms, dense_ms=dense_ms,
-                               kernels_ms={k: round(v[1] / v[0], 3) for k, v in prof.items()})
+                               kernels_ms={k: round(v[1] / v[0], 3) for k, v in prof.items()},
+                               row_index_bytes=idx.numel() * 4)
     log(f"block-sparse 128K: {ms:.2f} ms (estimation {est_ms:.2f}, attention {attn_ms:.2f}), "
         f"{attn_f / (ms * 1e-3) / 1e12:.1f} TFLOP/s" + (f", dense {dense_ms:.1f} ms" if dense_ms else ""))
-    del dev, idx, out
+    # the same selection as block lists (the page's kernel takes block ids)
+    # and the attention over them
+    blocks, counts = api.block_sparse_select_lists(dev.q, dev.k, BS_K_BLOCKS)
+    api.sparse_attn_lists(dev.q, dev.k, dev.v, blocks, counts, out=out)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        api.block_sparse_select_lists(dev.q, dev.k, BS_K_BLOCKS, blocks=blocks, counts=counts)
+        api.sparse_attn_lists(dev.q, dev.k, dev.v, blocks, counts, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    lms = e0.elapsed_time(e1) / reps
+    _lib.profile_begin()
+    api.block_sparse_select_lists(dev.q, dev.k, BS_K_BLOCKS, blocks=blocks, counts=counts)
+    api.sparse_attn_lists(dev.q, dev.k, dev.v, blocks, counts, out=out)
+    lprof = _lib.profile_end()
+    res["block_sparse"]["lists"] = dict(
+        ms=lms, est_ms=sum(v[1] for k, v in lprof.items() if k.startswith("bs_")),
+        attn_ms=sum(v[1] for k, v in lprof.items() if k.startswith("attn_")),
+        index_bytes=(blocks.numel() + counts.numel()) * 4)
+    log(f"block-sparse 128K, block lists: {lms:.2f} ms")
+    del dev, idx, out, blocks, counts
     torch.cuda.empty_cache()
 
 
@@ -674,10 +696,36 @@ def vertical_slash_bench(args, res, reps=3):
     attn_ms = sum(v[1] for k, v in prof.items() if k.startswith("attn_"))
     res["vertical_slash"] = dict(ms=ms, attn_tflop=attn_f / 1e12, est_ms=est_ms, attn_ms=attn_ms,
                                  entries=entries, width=idx.shape[-1],
-                                 kernels_ms={k: round(v[1] / v[0], 3) for k, v in prof.items()})
+                                 kernels_ms={k: round(v[1] / v[0], 3) for k, v in prof.items()},
+                                 row_index_bytes=idx.numel() * 4)
     log(f"vertical-slash 128K {VS_KEEP}: {ms:.2f} ms (estimation {est_ms:.2f}, attention {attn_ms:.2f}), "
         f"{attn_f / (ms * 1e-3) / 1e12:.1f} TFLOP/s, {entries:.0f} keys per row")
-    del dev, idx, out
+    # the hybrid kernel's form: block and column lists, blocks loaded as
+    # contiguous tiles, columns gathered
+    del idx
+    torch.cuda.empty_cache()
+    blocks, cols, counts = api.vertical_slash_select_lists(dev.q, dev.k, k_v, k_s)
+    api.sparse_attn_lists(dev.q, dev.k, dev.v, blocks, counts, cols, out=out)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        api.vertical_slash_select_lists(dev.q, dev.k, k_v, k_s, blocks=blocks, cols=cols, counts=counts)
+        api.sparse_attn_lists(dev.q, dev.k, dev.v, blocks, counts, cols, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    lms = e0.elapsed_time(e1) / reps
+    _lib.profile_begin()
+    api.vertical_slash_select_lists(dev.q, dev.k, k_v, k_s, blocks=blocks, cols=cols, counts=counts)
+    api.sparse_attn_lists(dev.q, dev.k, dev.v, blocks, counts, cols, out=out)
+    lprof = _lib.profile_end()
+    cn = counts.to(torch.float64)
+    res["vertical_slash"]["lists"] = dict(
+        ms=lms, est_ms=sum(v[1] for k, v in lprof.items() if k.startswith("vs_")),
+        attn_ms=sum(v[1] for k, v in lprof.items() if k.startswith("attn_")),
+        index_bytes=(blocks.numel() + cols.numel() + counts.numel()) * 4,
+        blocks_per_row=cn[..., 0].mean().item(), cols_per_row=cn[..., 1].mean().item())
+    log(f"vertical-slash 128K, block and column lists: {lms:.2f} ms")
+    del dev, out, blocks, cols, counts
     torch.cuda.empty_cache()
 
 
@@ -1049,7 +1097,13 @@ def main():
             "attn_only_pct_bf16_peak": round(100 * bs["attn_tflop"] / (bs["attn_ms"] * 1e-3) / PEAK_BF16_TFLOPS, 2),
             "dense_ms": round(bs["dense_ms"], 1) if bs["dense_ms"] else None,
             "speedup_vs_dense": round(bs["dense_ms"] / bs["ms"], 2) if bs["dense_ms"] else None,
-            "kernels_ms": bs["kernels_ms"]}
+            "kernels_ms": bs["kernels_ms"], "row_index_mb": round(bs["row_index_bytes"] / 1e6, 1)}
+        if "lists" in bs:
+            li = bs["lists"]
+            line["block_sparse_prefill_128k"]["block_lists"] = {
+                "ms": round(li["ms"], 2), "estimation_ms": round(li["est_ms"], 3), "attn_ms": round(li["attn_ms"], 2),
+                "pct_bf16_peak": round(100 * bs["attn_tflop"] / (li["ms"] * 1e-3) / PEAK_BF16_TFLOPS, 2),
+                "index_mb": round(li["index_bytes"] / 1e6, 1)}
         kv = _counter_summary("block_sparse_128k_counters.md")
         if kv and "bs_attn_fabric_read_bytes" in kv:
             rb = int(kv["bs_attn_fabric_read_bytes"])
@@ -1067,7 +1121,15 @@ def main():
             "attn_tflop": round(vs["attn_tflop"], 2), "estimation_ms": round(vs["est_ms"], 3),
             "attn_ms": round(vs["attn_ms"], 2), "keys_per_row_mean": round(vs["entries"]), "row_width": vs["width"],
             "speedup_vs_dense": round(dense_ms / vs["ms"], 2) if dense_ms else None,
-            "kernels_ms": vs["kernels_ms"]}
+            "kernels_ms": vs["kernels_ms"], "row_index_mb": round(vs["row_index_bytes"] / 1e6, 1)}
+        if "lists" in vs:
+            li = vs["lists"]
+            line["vertical_slash_prefill_128k"]["block_and_column_lists"] = {
+                "ms": round(li["ms"], 2), "estimation_ms": round(li["est_ms"], 3), "attn_ms": round(li["attn_ms"], 2),
+                "pct_bf16_peak": round(100 * vs["attn_tflop"] / (li["ms"] * 1e-3) / PEAK_BF16_TFLOPS, 2),
+                "speedup_vs_dense": round(dense_ms / li["ms"], 2) if dense_ms else None,
+                "index_mb": round(li["index_bytes"] / 1e6, 1), "blocks_per_row_mean": round(li["blocks_per_row"], 1),
+                "cols_per_row_mean": round(li["cols_per_row"], 1)}
     if "rope_decode" in res or "rope_prefill" in res:
         rt = {"rotary_base": ROPE_BASE}
         if "rope_decode" in res:

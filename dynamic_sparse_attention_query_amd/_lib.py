@@ -26,6 +26,8 @@ EXPORTS = ("dsa_index_width", "dsa_workspace_bytes", "dsa_prune_select", "dsa_sp
            "dsa_sparse_attn_heads", "dsa_vertical_slash_index_width", "dsa_vertical_slash_workspace_bytes",
            "dsa_vertical_slash_select", "dsa_prune_rope_workspace_bytes", "dsa_prune_select_rope",
            "dsa_rope_rotate_keys", "dsa_prune_select_rope_keys",
+           "dsa_block_sparse_list_width", "dsa_block_sparse_select_lists", "dsa_sparse_attn_lists",
+           "dsa_vertical_slash_list_widths", "dsa_vertical_slash_select_lists",
            "dsa_check_decode_inputs", "dsa_profile_begin", "dsa_profile_end", "dsa_status_str", "dsa_last_error")
 
 
@@ -117,6 +119,19 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dsa_vertical_slash_select.argtypes = [ctypes.POINTER(CShape), vp, vp, ctypes.c_int32, ctypes.c_int32, vp, vp,
                                               vp, vp, sz, vp]
     lib.dsa_vertical_slash_select.restype = ctypes.c_int
+    lib.dsa_block_sparse_list_width.argtypes = [ctypes.c_int32]
+    lib.dsa_block_sparse_list_width.restype = ctypes.c_int32
+    lib.dsa_block_sparse_select_lists.argtypes = [ctypes.POINTER(CShape), vp, vp, ctypes.c_int32, vp, vp, vp, sz, vp]
+    lib.dsa_block_sparse_select_lists.restype = ctypes.c_int
+    lib.dsa_sparse_attn_lists.argtypes = [ctypes.POINTER(CShape), vp, vp, vp, vp, ctypes.c_int32, vp, ctypes.c_int32,
+                                          vp, ctypes.c_float, vp, vp]
+    lib.dsa_sparse_attn_lists.restype = ctypes.c_int
+    lib.dsa_vertical_slash_list_widths.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                   ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+    lib.dsa_vertical_slash_list_widths.restype = ctypes.c_int
+    lib.dsa_vertical_slash_select_lists.argtypes = [ctypes.POINTER(CShape), vp, vp, ctypes.c_int32, ctypes.c_int32,
+                                                    vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.dsa_vertical_slash_select_lists.restype = ctypes.c_int
     lib.dsa_prune_rope_workspace_bytes.argtypes = [ctypes.POINTER(CShape), ctypes.POINTER(CParams),
                                                    ctypes.POINTER(CRope), ctypes.POINTER(sz)]
     lib.dsa_prune_rope_workspace_bytes.restype = ctypes.c_int
@@ -300,6 +315,42 @@ def sparse_attn_heads_raw(shape: Shape, q: int, k: int, v: int, idx: int, idx_wi
     cs = shape.c()
     _check(load().dsa_sparse_attn_heads(ctypes.byref(cs), q, k, v, idx, idx_width, scale, out,
                                         stream or None))
+
+
+def block_sparse_list_width(k_blocks: int) -> int:
+    w = load().dsa_block_sparse_list_width(k_blocks)
+    if w < 0:
+        raise DsaError(1, f"invalid k_blocks {k_blocks}")
+    return w
+
+
+def block_sparse_select_lists_raw(shape: Shape, q: int, k: int, k_blocks: int, blocks: int, counts: int, ws: int,
+                                  ws_bytes: int, stream: int = 0):
+    cs = shape.c()
+    _check(load().dsa_block_sparse_select_lists(ctypes.byref(cs), q, k, k_blocks, blocks, counts, ws or None,
+                                                ws_bytes, stream or None))
+
+
+def sparse_attn_lists_raw(shape: Shape, q: int, k: int, v: int, blocks: int, wb: int, cols: int, wc: int,
+                          counts: int, scale: float, out: int, stream: int = 0):
+    cs = shape.c()
+    _check(load().dsa_sparse_attn_lists(ctypes.byref(cs), q, k, v, blocks, wb, cols or None, wc, counts, scale, out,
+                                        stream or None))
+
+
+def vertical_slash_list_widths(t: int, k_v: int, k_s: int):
+    wb, wc = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(load().dsa_vertical_slash_list_widths(t, k_v, k_s, ctypes.byref(wb), ctypes.byref(wc)))
+    return wb.value, wc.value
+
+
+def vertical_slash_select_lists_raw(shape: Shape, q: int, k: int, k_v: int, k_s: int, blocks: int, cols: int,
+                                    counts: int, kept_cols: int, kept_offsets: int, ws: int, ws_bytes: int,
+                                    stream: int = 0):
+    cs = shape.c()
+    _check(load().dsa_vertical_slash_select_lists(ctypes.byref(cs), q, k, k_v, k_s, blocks, cols, counts,
+                                                  kept_cols or None, kept_offsets or None, ws or None, ws_bytes,
+                                                  stream or None))
 
 
 def vertical_slash_index_width(t: int, k_v: int, k_s: int) -> int:

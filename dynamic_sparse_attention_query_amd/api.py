@@ -312,6 +312,57 @@ def sparse_attn_heads(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: to
     return out
 
 
+def _out_i32(t: Optional[torch.Tensor], shape, device, name: str) -> torch.Tensor:
+    """A caller's int32 output buffer of this shape, or a new one."""
+    if t is None:
+        return torch.empty(shape, dtype=torch.int32, device=device)
+    if tuple(t.shape) != tuple(shape) or t.dtype != torch.int32 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 tensor of shape {tuple(shape)}")
+    return t
+
+
+def block_sparse_select_lists(q: torch.Tensor, k: torch.Tensor, k_blocks: int, *,
+                              blocks: Optional[torch.Tensor] = None, counts: Optional[torch.Tensor] = None,
+                              ws: Optional[torch.Tensor] = None):
+    """Per-head block index estimation (prefill) as block lists: (blocks
+    [B, Hq, T/64, wb] ascending ids then -1, counts [B, Hq, T/64, 2])."""
+    shape = make_shape(q, k)
+    if shape.mode != DSA_PREFILL:
+        raise ValueError("block-sparse estimation is a prefill call")
+    wb = _lib.block_sparse_list_width(k_blocks)
+    nblk = shape.t // 64
+    blocks = _out_i32(blocks, (shape.batch, shape.hq, nblk, wb), q.device, "blocks")
+    counts = _out_i32(counts, (shape.batch, shape.hq, nblk, 2), q.device, "counts")
+    wsp, wsb = _scratch(_lib.block_sparse_workspace_bytes(shape, k_blocks), q.device, ws)
+    _lib.block_sparse_select_lists_raw(shape, q.data_ptr(), k.data_ptr(), k_blocks, blocks.data_ptr(),
+                                       counts.data_ptr(), wsp, wsb, _stream())
+    return blocks, counts
+
+
+def sparse_attn_lists(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, blocks: torch.Tensor,
+                      counts: torch.Tensor, cols: Optional[torch.Tensor] = None, *, scale: float = 0.0,
+                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Prefill attention over per-head block lists [B, Hq, T/64, wb] and
+    (optionally) column lists [B, Hq, T/64, wc], counts [B, Hq, T/64, 2]."""
+    shape = make_shape(q, k)
+    _need(v, "v")
+    if v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("v must match k")
+    lead = (shape.batch, shape.hq, shape.t // 64)
+    for name, x in (("blocks", blocks), ("counts", counts)) + ((("cols", cols),) if cols is not None else ()):
+        _need(x, name)
+        if x.dtype != torch.int32 or tuple(x.shape[:3]) != lead:
+            raise ValueError(f"{name} must be int32 [B, Hq, T/64, ...]")
+    if counts.shape[-1] != 2:
+        raise ValueError("counts must be [B, Hq, T/64, 2]")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    _lib.sparse_attn_lists_raw(shape, q.data_ptr(), k.data_ptr(), v.data_ptr(), blocks.data_ptr(), blocks.shape[-1],
+                               cols.data_ptr() if cols is not None else 0, cols.shape[-1] if cols is not None else 0,
+                               counts.data_ptr(), scale, out.data_ptr(), _stream())
+    return out
+
+
 # --------------------------------------------------------------------------- #
 # vertical-slash heads                                                        #
 # --------------------------------------------------------------------------- #
@@ -341,6 +392,32 @@ def vertical_slash_select(q: torch.Tensor, k: torch.Tensor, k_v: int, k_s: int, 
     if return_lines:
         return idx, cols[..., :k_v], offs
     return idx
+
+
+def vertical_slash_select_lists(q: torch.Tensor, k: torch.Tensor, k_v: int, k_s: int, *,
+                                blocks: Optional[torch.Tensor] = None, cols: Optional[torch.Tensor] = None,
+                                counts: Optional[torch.Tensor] = None, return_lines: bool = False,
+                                ws: Optional[torch.Tensor] = None):
+    """Per-head vertical-slash index estimation (prefill, bf16) as the hybrid
+    kernel's lists: (blocks [B, Hq, T/64, wb], cols [B, Hq, T/64, wc], counts
+    [B, Hq, T/64, 2]); with return_lines also the kept columns and offsets."""
+    shape = make_shape(q, k)
+    if shape.mode != DSA_PREFILL:
+        raise ValueError("vertical-slash estimation is a prefill call")
+    wb, wc = _lib.vertical_slash_list_widths(shape.t, k_v, k_s)
+    lead = (shape.batch, shape.hq, shape.t // 64)
+    blocks = _out_i32(blocks, lead + (wb,), q.device, "blocks")
+    cols = _out_i32(cols, lead + (wc,), q.device, "cols")
+    counts = _out_i32(counts, lead + (2,), q.device, "counts")
+    kc = torch.empty((shape.batch, shape.hq, max(k_v, 1)), dtype=torch.int32, device=q.device) if return_lines else None
+    ko = torch.empty((shape.batch, shape.hq, k_s), dtype=torch.int32, device=q.device) if return_lines else None
+    wsp, wsb = _scratch(_lib.vertical_slash_workspace_bytes(shape, k_v, k_s), q.device, ws)
+    _lib.vertical_slash_select_lists_raw(shape, q.data_ptr(), k.data_ptr(), k_v, k_s, blocks.data_ptr(),
+                                         cols.data_ptr(), counts.data_ptr(), kc.data_ptr() if kc is not None else 0,
+                                         ko.data_ptr() if ko is not None else 0, wsp, wsb, _stream())
+    if return_lines:
+        return blocks, cols, counts, kc[..., :k_v], ko
+    return blocks, cols, counts
 
 
 # --------------------------------------------------------------------------- #

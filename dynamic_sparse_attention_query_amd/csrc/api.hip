@@ -665,6 +665,82 @@ dsa_status dsa_sparse_attn_heads(const dsa_shape* s, const void* q, const void* 
   return DSA_OK;
 }
 
+int32_t dsa_block_sparse_list_width(int32_t k_blocks) {
+  if (k_blocks < 1 || k_blocks > kBsMaxBlocks) return -1;
+  return (k_blocks + 3) / 4 * 4;
+}
+
+dsa_status dsa_block_sparse_select_lists(const dsa_shape* s, const void* q, const void* k, int32_t k_blocks,
+                                         int32_t* blocks, int32_t* counts, void* ws, size_t ws_bytes,
+                                         void* stream) {
+  g_err[0] = 0;
+  dsa_status st = check_block_sparse(s, k_blocks);
+  if (st != DSA_OK) return st;
+  if (!q || !k || !blocks || !counts) return fail(DSA_ERR_INVALID_ARG, "q, k, blocks and counts must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(blocks))
+    return fail(DSA_ERR_INVALID_ARG, "q, k and blocks must be 16-byte aligned");
+  const BsLayout lay = bs_layout(s);
+  if (!ws || ws_bytes < lay.bytes)
+    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, lay.bytes);
+  if (!aligned16(ws)) return fail(DSA_ERR_INVALID_ARG, "ws must be 16-byte aligned");
+  dsa::BsArgs a{};
+  a.kv = make_kv(s, kBsBlock);
+  a.q = q;
+  a.k = k;
+  a.k_blocks = k_blocks;
+  a.nblkp = static_cast<int>(lay.nblkp);
+  char* w = static_cast<char*>(ws);
+  a.qp = reinterpret_cast<double*>(w + lay.off_qp);
+  a.kp = reinterpret_cast<double*>(w + lay.off_kp);
+  a.keys = reinterpret_cast<uint32_t*>(w + lay.off_keys);
+  a.lblk = blocks;
+  a.lcnt = counts;
+  a.wb = dsa_block_sparse_list_width(k_blocks);
+  hipError_t err = dsa::launch_block_sparse(a, s->dtype, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(DSA_ERR_HIP, "block-sparse launch failed: %s", hipGetErrorString(err));
+  return DSA_OK;
+}
+
+dsa_status dsa_sparse_attn_lists(const dsa_shape* s, const void* q, const void* k, const void* v,
+                                 const int32_t* blocks, int32_t wb, const int32_t* cols, int32_t wc,
+                                 const int32_t* counts, float scale, float* out, void* stream) {
+  g_err[0] = 0;
+  dsa_status st = check_shape(s);
+  if (st != DSA_OK) return st;
+  if (s->mode != DSA_PREFILL) return fail(DSA_ERR_INVALID_ARG, "block and column lists are a prefill layout");
+  if (s->dtype != DSA_BF16 || s->d != 128)
+    return fail(DSA_ERR_UNSUPPORTED, "attention over lists takes bf16 inputs with d = 128");
+  if (s->t % kBsBlock != 0) return fail(DSA_ERR_INVALID_ARG, "t = %d is not a multiple of 64", s->t);
+  if (static_cast<long long>(s->t) * s->d * 2 > 0x7fffffffLL)
+    return fail(DSA_ERR_UNSUPPORTED, "t = %d: a kv head's rows must fit 2^31 bytes", s->t);
+  if (!q || !k || !v || !blocks || !counts || !out)
+    return fail(DSA_ERR_INVALID_ARG, "q, k, v, blocks, counts and out must be non-NULL");
+  if (wb < 4 || wb % 4 != 0) return fail(DSA_ERR_INVALID_ARG, "wb = %d is not a positive multiple of 4", wb);
+  if (cols && (wc < 4 || wc % 4 != 0))
+    return fail(DSA_ERR_INVALID_ARG, "wc = %d is not a positive multiple of 4", wc);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(blocks) || (cols && !aligned16(cols)) ||
+      (reinterpret_cast<uintptr_t>(counts) & 7) != 0)
+    return fail(DSA_ERR_INVALID_ARG, "q, k, v, blocks and cols must be 16-byte aligned, counts 8-byte aligned");
+  dsa::AttnArgs a{};
+  a.kv = make_kv(s, kBsBlock);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.row_heads = 1;
+  a.lblk = blocks;
+  a.lcol = cols;
+  a.lcnt = counts;
+  a.wb = wb;
+  a.wc = cols ? wc : 0;
+  const float sc = scale > 0.f ? scale : 1.0f / std::sqrt(static_cast<float>(s->d));
+  a.scale_log2 = sc * 1.4426950408889634f;
+  dsa::launch_prefill_lists(a, static_cast<hipStream_t>(stream));
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return fail(DSA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(err));
+  return DSA_OK;
+}
+
 
 }  // extern "C"
 
@@ -761,6 +837,61 @@ dsa_status dsa_vertical_slash_select(const dsa_shape* s, const void* q, const vo
   a.sel[1] = offsets ? offsets : reinterpret_cast<int32_t*>(w + lay.off_sel[1]);
   a.idx = idx;
   a.L = static_cast<int>(vs_width_ll(s->t, k_v, k_s));
+  hipError_t err = dsa::launch_vertical_slash(a, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(DSA_ERR_HIP, "vertical-slash launch failed: %s", hipGetErrorString(err));
+  return DSA_OK;
+}
+
+dsa_status dsa_vertical_slash_list_widths(int32_t t, int32_t k_v, int32_t k_s, int32_t* wb, int32_t* wc) {
+  g_err[0] = 0;
+  if (!wb || !wc) return fail(DSA_ERR_INVALID_ARG, "wb and wc must be non-NULL");
+  if (t < 64 || t % 64 != 0 || k_v < 0 || k_s < 1 || k_v > t || k_s > t)
+    return fail(DSA_ERR_INVALID_ARG, "t = %d, k_v = %d, k_s = %d out of range", t, k_v, k_s);
+  const long long nb = std::min(static_cast<long long>(t) / 64, 2LL * k_s);
+  *wb = static_cast<int32_t>((nb + 3) / 4 * 4);
+  *wc = static_cast<int32_t>((std::max(k_v, 1) + 3) / 4 * 4);
+  return DSA_OK;
+}
+
+dsa_status dsa_vertical_slash_select_lists(const dsa_shape* s, const void* q, const void* k, int32_t k_v,
+                                           int32_t k_s, int32_t* blocks, int32_t* cols, int32_t* counts,
+                                           int32_t* kept_cols, int32_t* kept_offsets, void* ws, size_t ws_bytes,
+                                           void* stream) {
+  g_err[0] = 0;
+  dsa_status st = check_vertical_slash(s, k_v, k_s);
+  if (st != DSA_OK) return st;
+  if (!q || !k || !blocks || !cols || !counts)
+    return fail(DSA_ERR_INVALID_ARG, "q, k, blocks, cols and counts must be non-NULL");
+  if (!aligned16(q) || !aligned16(k)) return fail(DSA_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
+  const VsLayout lay = vs_layout(s, k_v, k_s);
+  if (!ws || ws_bytes < lay.bytes)
+    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, lay.bytes);
+  if (!aligned16(ws)) return fail(DSA_ERR_INVALID_ARG, "ws must be 16-byte aligned");
+  int32_t wb = 0, wc = 0;
+  dsa_vertical_slash_list_widths(s->t, k_v, k_s, &wb, &wc);
+  dsa::VsArgs a{};
+  a.kv = make_kv(s, kBsBlock);
+  a.q = q;
+  a.k = k;
+  a.keep[0] = k_v;
+  a.keep[1] = k_s;
+  a.scale = 1.0 / std::sqrt(static_cast<double>(s->d));
+  a.nr = lay.nr;
+  char* w = static_cast<char*>(ws);
+  a.part = reinterpret_cast<double*>(w + lay.off_part);
+  a.stat = reinterpret_cast<double*>(w + lay.off_stat);
+  a.sums = reinterpret_cast<uint32_t*>(w + lay.off_sums);
+  for (int i = 0; i < 2; ++i) {
+    a.ckey[i] = reinterpret_cast<uint32_t*>(w + lay.off_ckey[i]);
+    a.cidx[i] = reinterpret_cast<int32_t*>(w + lay.off_cidx[i]);
+  }
+  a.sel[0] = kept_cols ? kept_cols : reinterpret_cast<int32_t*>(w + lay.off_sel[0]);
+  a.sel[1] = kept_offsets ? kept_offsets : reinterpret_cast<int32_t*>(w + lay.off_sel[1]);
+  a.lblk = blocks;
+  a.lcol = cols;
+  a.lcnt = counts;
+  a.wb = wb;
+  a.wc = wc;
   hipError_t err = dsa::launch_vertical_slash(a, static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return fail(DSA_ERR_HIP, "vertical-slash launch failed: %s", hipGetErrorString(err));
   return DSA_OK;

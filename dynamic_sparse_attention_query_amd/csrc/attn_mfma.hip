@@ -614,6 +614,15 @@ __device__ __forceinline__ void barrier_keep_loads() {
   asm volatile("s_barrier" ::: "memory");
 }
 
+//
+// With LISTS, a (head, query block) gives a block list and a column list
+// instead of a row (the MInference page's "Vertical-Slash Hybrid Kernel
+// (Appendix C.4.2, Algorithms 4 and 5)"; the block-sparse heads have blocks
+// only): its tiles are the listed 64-key blocks, whose positions follow from
+// the block id, then the columns, 64 to a tile, gathered like row entries.
+// A block tile's index fetch reads the aligned quad of ids holding its own,
+// twice, so every tile still issues exactly two index loads.
+template <bool LISTS>
 __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) k_prefill_heads(AttnArgs a) {
   constexpr int D = 128;
   constexpr int KS = D / 16;
@@ -663,8 +672,18 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
   float mrun = kNegBig, lrun = 0.f;
 
-  const int32_t* row = a.idx + (static_cast<size_t>(b * kv.Hq + h) * kv.nblk + m) * a.L;
-  const int n_tiles = (a.L + 63) / 64;
+  const size_t rowid = static_cast<size_t>(b * kv.Hq + h) * kv.nblk + m;
+  const int32_t* row = LISTS ? nullptr : a.idx + rowid * a.L;
+  const int32_t* lb = LISTS ? a.lblk + rowid * a.wb : nullptr;
+  const int32_t* lc = LISTS && a.lcol ? a.lcol + rowid * a.wc : lb;   // (no columns: never read)
+  const int wcl = LISTS && a.lcol ? a.wc : 4;
+  int nbl = 0, ncl = 0;                           // listed blocks, listed columns
+  if constexpr (LISTS) {
+    const int2 c2 = *reinterpret_cast<const int2*>(a.lcnt + 2 * rowid);
+    nbl = min(max(c2.x, 0), a.wb);                // (counts never send a list read past its width)
+    ncl = min(max(c2.y, 0), a.wc);
+  }
+  const int n_tiles = LISTS ? nbl + (ncl + 63) / 64 : (a.L + 63) / 64;
   const int lg = 4 * w + (lane >> 4);             // entries 8lg .. 8lg+7 of a tile
   const int lslot = lane & 15;
   // Entries 8lg .. 8lg+7 of a tile: two 16-byte loads at clamped addresses
@@ -673,16 +692,43 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))
   // tile), so each step issues exactly two such loads and never waits on them
   // early: the waits below count them.
   auto load_raw = [&](int ti, int4& v0, int4& v1) __attribute__((always_inline)) {
-    const int i0 = min(ti, n_tiles - 1) * 64 + 8 * lg;
-    v0 = *reinterpret_cast<const int4*>(row + min(i0, a.L - 4));
-    v1 = *reinterpret_cast<const int4*>(row + min(i0 + 4, a.L - 4));
+    if constexpr (LISTS) {
+      const int tt = max(0, min(ti, n_tiles - 1));
+      if (tt < nbl) {                               // the quad holding the block id (wb is a multiple of 4)
+        v0 = *reinterpret_cast<const int4*>(lb + (tt & ~3));
+        v1 = *reinterpret_cast<const int4*>(lb + (tt & ~3));
+      } else {
+        const int i0 = (tt - nbl) * 64 + 8 * lg;
+        v0 = *reinterpret_cast<const int4*>(lc + min(i0, wcl - 4));
+        v1 = *reinterpret_cast<const int4*>(lc + min(i0 + 4, wcl - 4));
+      }
+    } else {
+      const int i0 = min(ti, n_tiles - 1) * 64 + 8 * lg;
+      v0 = *reinterpret_cast<const int4*>(row + min(i0, a.L - 4));
+      v1 = *reinterpret_cast<const int4*>(row + min(i0 + 4, a.L - 4));
+    }
   };
   auto decode = [&](int ti, const int4& v0, const int4& v1, int (&p)[8]) __attribute__((always_inline)) {
-    const int i0 = min(ti, n_tiles - 1) * 64 + 8 * lg;
-    const int raw[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
     const bool live = ti < n_tiles;
+    if constexpr (LISTS) {
+      const int tt = max(0, min(ti, n_tiles - 1));
+      if (tt < nbl) {
+        const int q4 = tt & 3;
+        const int blk = q4 == 0 ? v0.x : q4 == 1 ? v0.y : q4 == 2 ? v0.z : v0.w;
 #pragma unroll
-    for (int x = 0; x < 8; ++x) p[x] = (live && i0 + x < a.L) ? raw[x] : -1;
+        for (int x = 0; x < 8; ++x) p[x] = live ? 64 * blk + 8 * lg + x : -1;
+      } else {
+        const int i0 = (tt - nbl) * 64 + 8 * lg;
+        const int raw[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+        for (int x = 0; x < 8; ++x) p[x] = (live && i0 + x < ncl) ? raw[x] : -1;
+      }
+    } else {
+      const int i0 = min(ti, n_tiles - 1) * 64 + 8 * lg;
+      const int raw[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+      for (int x = 0; x < 8; ++x) p[x] = (live && i0 + x < a.L) ? raw[x] : -1;
+    }
   };
   auto issue = [&](const __amdgpu_buffer_rsrc_t& rs, uint16_t* dst, const int (&p)[8]) __attribute__((always_inline)) {
 #pragma unroll
@@ -1236,6 +1282,14 @@ static void launch_mfma(const AttnArgs& a, hipStream_t st) {
   DSA_LAUNCH(name, (k_prefill_mfma<D, NH, QH>), dim3(grid), dim3(64 * NH * QH), st, a);
 }
 
+// bf16 prefill over per-head block and column lists (d = 128, kv rows
+// addressable with 32-bit byte offsets, lists 16-byte aligned with widths
+// that are multiples of 4: checked by the caller).
+void launch_prefill_lists(const AttnArgs& a, hipStream_t st) {
+  const int nwork = a.kv.B * a.kv.Hq * a.kv.nblk;
+  DSA_LAUNCH("attn_prefill_lists", k_prefill_heads<true>, dim3(nwork), dim3(128), st, a);
+}
+
 // bf16 prefill with query blocks of 64 rows; 4 waves per workgroup: the 4
 // heads of a GQA group for one query half, or 2 heads / 1 head for both.
 bool launch_prefill_mfma(const AttnArgs& a, hipStream_t st) {
@@ -1250,7 +1304,7 @@ bool launch_prefill_mfma(const AttnArgs& a, hipStream_t st) {
   if (a.row_heads) {                              // one head per workgroup
     if (a.kv.D == 128 && lds_ok) {
       const int nwork = a.kv.B * a.kv.Hq * a.kv.nblk;
-      DSA_LAUNCH("attn_prefill_heads", k_prefill_heads, dim3(nwork), dim3(128), st, a);
+      DSA_LAUNCH("attn_prefill_heads", k_prefill_heads<false>, dim3(nwork), dim3(128), st, a);
       return true;
     }
     if (a.kv.D == 128) { launch_mfma<128, 1, 2>(a, st); return true; }

@@ -184,6 +184,17 @@ __global__ void __launch_bounds__(kTopkThreads) k_bs_topk(BsArgs a) {
       key[4 * v + 0] = u.x; key[4 * v + 1] = u.y; key[4 * v + 2] = u.z; key[4 * v + 3] = u.w;
     }
   }
+  if (a.lblk) {                                  // block lists: the ids, then -1
+    int32_t* lb = a.lblk + static_cast<size_t>(r) * a.wb;
+    select_row<E>(key, j0, nc, kc, L, [&](int j, int pos) { lb[pos] = j; });
+    const int n_sel = min(nc, kc);
+    for (int x = n_sel + tid; x < a.wb; x += kTopkThreads) lb[x] = -1;
+    if (tid == 0) {
+      a.lcnt[2 * static_cast<size_t>(r)] = n_sel;
+      a.lcnt[2 * static_cast<size_t>(r) + 1] = 0;
+    }
+    return;
+  }
   int32_t* row = a.idx + static_cast<size_t>(r) * a.L;
   select_row<E>(key, j0, nc, kc, L, [&](int j, int pos) {
     int4* dst = reinterpret_cast<int4*>(row + pos * kBsBlock);
@@ -208,11 +219,12 @@ static void launch_bs_typed(const BsArgs& a, hipStream_t st) {
   DSA_LAUNCH("bs_scores", (k_bs_scores<D>), dim3(static_cast<unsigned>((units + 3) / 4)), dim3(256), st, a, nmt);
   const dim3 grid(static_cast<unsigned>(static_cast<long long>(kv.B) * kv.Hq * kv.nblk));
   const int per = (kv.nblk + kTopkThreads - 1) / kTopkThreads;
-  if (per <= 4)       DSA_LAUNCH("bs_topk", (k_bs_topk<4>), grid, dim3(kTopkThreads), st, a);
-  else if (per <= 8)  DSA_LAUNCH("bs_topk", (k_bs_topk<8>), grid, dim3(kTopkThreads), st, a);
-  else if (per <= 16) DSA_LAUNCH("bs_topk", (k_bs_topk<16>), grid, dim3(kTopkThreads), st, a);
-  else if (per <= 32) DSA_LAUNCH("bs_topk", (k_bs_topk<32>), grid, dim3(kTopkThreads), st, a);
-  else                DSA_LAUNCH("bs_topk", (k_bs_topk<64>), grid, dim3(kTopkThreads), st, a);
+  const char* nm = a.lblk ? "bs_topk_lists" : "bs_topk";
+  if (per <= 4)       DSA_LAUNCH(nm, (k_bs_topk<4>), grid, dim3(kTopkThreads), st, a);
+  else if (per <= 8)  DSA_LAUNCH(nm, (k_bs_topk<8>), grid, dim3(kTopkThreads), st, a);
+  else if (per <= 16) DSA_LAUNCH(nm, (k_bs_topk<16>), grid, dim3(kTopkThreads), st, a);
+  else if (per <= 32) DSA_LAUNCH(nm, (k_bs_topk<32>), grid, dim3(kTopkThreads), st, a);
+  else                DSA_LAUNCH(nm, (k_bs_topk<64>), grid, dim3(kTopkThreads), st, a);
 }
 
 // Blocks per row are validated by the caller (at most 64 * kTopkThreads).

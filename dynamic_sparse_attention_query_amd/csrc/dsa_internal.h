@@ -65,6 +65,11 @@ struct AttnArgs {
   float scale_log2;          // softmax scale * log2(e)
   int row_heads;             // prefill: 0 = one idx row per (b, block) shared by the heads,
                              // 1 = one row per (b, q head, block): row (b * Hq + h) * nblk + m
+  // per-head block and column lists instead of rows (row (b * Hq + h) * nblk + m)
+  const int32_t* lblk;       // [.., wb] key-block ids, ascending
+  const int32_t* lcol;       // [.., wc] single key positions, ascending (nullptr: none)
+  const int32_t* lcnt;       // [.., 2] number of blocks, of columns
+  int wb, wc;
 };
 
 // One fused decode step (decode_fused.hip): the pruning state of the call,
@@ -92,6 +97,9 @@ struct BsArgs {
   uint32_t* keys;            // [B, Hq, nblk, nblkp] orderable pooled-logit keys
   int32_t* idx;              // [B, Hq, nblk, L] index rows
   int L;                     // row width: 64 * k_blocks
+  int32_t* lblk;             // block lists instead of rows (when set): [B, Hq, nblk, wb]
+  int32_t* lcnt;             // [B, Hq, nblk, 2] number of blocks, 0 columns
+  int wb;
 };
 
 // ------------------------------------------------------------------------- //
@@ -374,6 +382,7 @@ hipError_t launch_sparse_attn(const AttnArgs& a, int dtype, hipStream_t stream);
 void launch_decode_combine(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_block_sparse(const BsArgs& a, int dtype, hipStream_t stream);
 bool launch_prefill_mfma(const AttnArgs& a, hipStream_t stream);   // bf16, b_q = 64
+void launch_prefill_lists(const AttnArgs& a, hipStream_t stream);  // bf16, d = 128, per-head lists
 struct PruneArgs;
 // top-K of one stage over every row (prune.hip)
 void launch_topk(const PruneArgs& a, int stage, int max_chunks, hipStream_t stream);

@@ -298,6 +298,26 @@ __global__ void __launch_bounds__(256) k_vs_rows(VsArgs a) {
     wp += __popc(bits[x]);
   }
   __syncthreads();
+  if (a.lblk) {
+    // the hybrid kernel's two lists: the marked blocks ascending (each
+    // thread its bitmap words, from the block count before them), then the
+    // kept columns, each -1 padded
+    const size_t rr = static_cast<size_t>(bh) * kv.nblk + m;
+    int32_t* lb = a.lblk + rr * a.wb;
+    for (int x = tid * wpt; x < min(tid * wpt + wpt, nw); ++x) {
+      int r = wpre[x];
+      for (uint32_t word = bits[x]; word != 0u; word &= word - 1u) lb[r++] = 32 * x + __ffs(static_cast<int>(word)) - 1;
+    }
+    for (int i = nb + tid; i < a.wb; i += 256) lb[i] = -1;
+    int32_t* lc = a.lcol + rr * a.wc;
+    for (int c = tid; c < nc; c += 256) lc[c] = kept[c];
+    for (int i = nc + tid; i < a.wc; i += 256) lc[i] = -1;
+    if (tid == 0) {
+      a.lcnt[2 * rr] = nb;
+      a.lcnt[2 * rr + 1] = nc;
+    }
+    return;
+  }
   auto rank = [&](int blk) { return wpre[blk >> 5] + __popc(bits[blk >> 5] & ((1u << (blk & 31)) - 1u)); };
   int32_t* row = a.idx + (static_cast<size_t>(bh) * kv.nblk + m) * a.L;
   // each attended block is written by one wave, one entry per lane; a wave
@@ -360,7 +380,7 @@ static void launch_vs_typed(const VsArgs& a, hipStream_t st) {
     src = dst;
     dst ^= 1;
   }
-  DSA_LAUNCH("vs_rows", k_vs_rows, dim3(kv.nblk, kv.Hq, kv.B), dim3(256), st, a);
+  DSA_LAUNCH(a.lblk ? "vs_lists" : "vs_rows", k_vs_rows, dim3(kv.nblk, kv.Hq, kv.B), dim3(256), st, a);
 }
 
 // bf16, d in {64, 128}, T a multiple of 64 up to 64 * 16384; keep[] <= 8192

@@ -28,6 +28,11 @@ struct VsArgs {
   int32_t* sel[2];             // [B, Hq, k_v] kept columns, [B, Hq, k_s] kept offsets (ascending)
   int32_t* idx;                // [B, Hq, T / 64, L] index rows
   int L;
+  // the hybrid kernel's lists instead of rows (when lblk is set)
+  int32_t* lblk;               // [B, Hq, T / 64, wb] ascending key-block ids, then -1
+  int32_t* lcol;               // [B, Hq, T / 64, wc] ascending single columns, then -1
+  int32_t* lcnt;               // [B, Hq, T / 64, 2] number of blocks, of columns
+  int wb, wc;
 };
 
 hipError_t launch_vertical_slash(const VsArgs& a, hipStream_t stream);

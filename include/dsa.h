@@ -26,11 +26,14 @@
  *   dsa_block_sparse_select, dsa_sparse_attn_heads
  *                     The MInference page's Block-Sparse heads: per-head block
  *                     index estimation from mean-pooled queries and keys, and
- *                     attention over per-head index rows (see below).
+ *                     attention over per-head index rows (see below); the
+ *                     ..._lists calls give and take block lists instead.
  *   dsa_vertical_slash_select
  *                     The MInference page's Vertical-Slash heads: per-head
  *                     column and offset estimation from the last 64 queries,
- *                     rendered as index rows for dsa_sparse_attn_heads.
+ *                     rendered as index rows for dsa_sparse_attn_heads, or
+ *                     (..._select_lists) as the hybrid kernel's block and
+ *                     column lists for dsa_sparse_attn_lists.
  *   dsa_dense_attn    Exact causal attention over all keys: the comparison
  *                     point (InfiniteHiP page, "Dense Attention Optimizations"
  *                     and "Formal Background: Standard Multi-Head Attention").
@@ -346,6 +349,37 @@ dsa_status dsa_sparse_attn_heads(const dsa_shape* shape, const void* q, const vo
                                  const int32_t* idx, int32_t idx_width, float scale, float* out,
                                  void* stream);
 
+/* Block-sparse selection written as block lists (the form the page's
+ * block-sparse kernel takes: block ids, not positions) for
+ * dsa_sparse_attn_lists: blocks [B, Hq, T / 64, wb] int32, wb =
+ * dsa_block_sparse_list_width(k_blocks), row (b, h, m) = the kept block ids
+ * ascending, then -1; counts [B, Hq, T / 64, 2] int32 = (number of blocks, 0).
+ * Same selection, shapes, alignment and workspace as dsa_block_sparse_select;
+ * blocks 16-byte aligned. */
+int32_t dsa_block_sparse_list_width(int32_t k_blocks);   /* k_blocks rounded up to 4; -1 if out of range */
+dsa_status dsa_block_sparse_select_lists(const dsa_shape* shape, const void* q, const void* k, int32_t k_blocks,
+                                         int32_t* blocks, int32_t* counts, void* ws, size_t ws_bytes,
+                                         void* stream);
+
+/* Attention over per-head block and column lists (MInference page,
+ * "Vertical-Slash Hybrid Kernel (Appendix C.4.2, Algorithms 4 and 5)": the
+ * listed 64-key blocks are loaded whole as contiguous tiles, the columns
+ * gathered; block-sparse heads list blocks only). For query head h and query
+ * block m (row r = (b * Hq + h) * (T / 64) + m): the keys are every position
+ * of blocks[r][0 .. counts[r][0]) and the columns cols[r][0 .. counts[r][1]);
+ * out[h, t] = sum over those keys p <= t of softmax_p(scale * q_{h,t} . k_p)
+ * v_p, 0 for a query that sees none. The lists must be disjoint, ascending
+ * and inside [0, t) (as the list selections write them). shape.mode
+ * DSA_PREFILL, dtype DSA_BF16, d = 128, t a multiple of 64 with
+ * t * 256 < 2^31; blocks [B, Hq, T / 64, wb], cols [B, Hq, T / 64, wc] or
+ * NULL when every column count is 0, counts [B, Hq, T / 64, 2]; wb, wc
+ * positive multiples of 4; q, k, v, blocks, cols 16-byte aligned, counts
+ * 8-byte aligned; scale <= 0 selects 1/sqrt(d). Other shapes return
+ * DSA_ERR_UNSUPPORTED. Needs no workspace. */
+dsa_status dsa_sparse_attn_lists(const dsa_shape* shape, const void* q, const void* k, const void* v,
+                                 const int32_t* blocks, int32_t wb, const int32_t* cols, int32_t wc,
+                                 const int32_t* counts, float scale, float* out, void* stream);
+
 /* ---- Vertical-slash heads ------------------------------------------------
  * MInference page, "Online Dynamic Index Estimation: Vertical-Slash Heads
  * (Algorithm 2)" and "Vertical-Slash Hybrid Kernel (Appendix C.4.2)".
@@ -361,7 +395,7 @@ dsa_status dsa_sparse_attn_heads(const dsa_shape* shape, const void* q, const vo
  * Layout: idx [B, Hq, T / 64, L] int32, L = dsa_vertical_slash_index_width();
  * each row holds its key positions ascending, then -1 padding; the causal
  * mask inside a block is applied by dsa_sparse_attn_heads, which consumes the
- * rows. A query that sees no key of its row gets an undefined output.
+ * rows. A query that sees no key of its row gets output 0.
  * Requires t a multiple of 64 with t / 64 <= 16384, 0 <= k_v <= min(t, 8192),
  * 1 <= k_s <= min(t, 8192). */
 
@@ -380,6 +414,22 @@ dsa_status dsa_vertical_slash_workspace_bytes(const dsa_shape* shape, int32_t k_
 dsa_status dsa_vertical_slash_select(const dsa_shape* shape, const void* q, const void* k, int32_t k_v,
                                      int32_t k_s, int32_t* idx, int32_t* cols, int32_t* offsets, void* ws,
                                      size_t ws_bytes, void* stream);
+
+/* The same index as the hybrid kernel's two lists (Appendix C.4.2), for
+ * dsa_sparse_attn_lists: blocks [B, Hq, T / 64, wb] = the ascending ids of
+ * the 64-key blocks that row attends whole, then -1; cols [B, Hq, T / 64, wc]
+ * = its single columns (kept columns before the block's end in none of those
+ * blocks), ascending, then -1; counts [B, Hq, T / 64, 2] = (blocks, columns).
+ * The widths come from dsa_vertical_slash_list_widths (wb = min(T / 64,
+ * 2 k_s), wc = max(k_v, 1), each rounded up to 4): about 2 k_s + k_v entries
+ * per row instead of the row width L. kept_cols / kept_offsets as cols /
+ * offsets of dsa_vertical_slash_select. Same shapes, alignment and workspace
+ * as dsa_vertical_slash_select. */
+dsa_status dsa_vertical_slash_list_widths(int32_t t, int32_t k_v, int32_t k_s, int32_t* wb, int32_t* wc);
+dsa_status dsa_vertical_slash_select_lists(const dsa_shape* shape, const void* q, const void* k, int32_t k_v,
+                                           int32_t k_s, int32_t* blocks, int32_t* cols, int32_t* counts,
+                                           int32_t* kept_cols, int32_t* kept_offsets, void* ws, size_t ws_bytes,
+                                           void* stream);
 
 /* Per-kernel timing, a diagnostic for latency breakdowns. Between
  * dsa_profile_begin() and dsa_profile_end(), every kernel the library launches

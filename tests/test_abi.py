@@ -210,6 +210,57 @@ def test_vertical_slash_sizes_and_rejections():
         assert ei.value.status == code, over
 
 
+def test_list_calls_sizes_and_rejections():
+    """The block / column list calls (MInference hybrid kernel): widths, and
+    every host-side rejection before a launch (pointers are never touched)."""
+    assert _lib.block_sparse_list_width(100) == 100 and _lib.block_sparse_list_width(3) == 4
+    with pytest.raises(_lib.DsaError):
+        _lib.block_sparse_list_width(0)
+    assert _lib.vertical_slash_list_widths(4096, 100, 30) == (60, 100)
+    assert _lib.vertical_slash_list_widths(256, 3, 1) == (4, 4)           # 2 blocks, 3 columns, rounded to 4
+    assert _lib.vertical_slash_list_widths(4096, 0, 4096) == (64, 4)      # every block; no column
+    with pytest.raises(_lib.DsaError):
+        _lib.vertical_slash_list_widths(4096 + 32, 10, 3)
+    good = Shape(DSA_PREFILL, DSA_BF16, 1, 32, 8, 128, 4096)
+    cases = [
+        (dict(shape=Shape(DSA_PREFILL, DSA_F32, 1, 32, 8, 128, 4096)), DSA_ERR_UNSUPPORTED),
+        (dict(shape=Shape(DSA_PREFILL, DSA_BF16, 1, 32, 8, 64, 4096)), DSA_ERR_UNSUPPORTED),
+        (dict(shape=Shape(DSA_DECODE, DSA_BF16, 1, 32, 8, 128, 4096, seq_lens=16)), DSA_ERR_INVALID_ARG),
+        (dict(shape=Shape(DSA_PREFILL, DSA_BF16, 1, 32, 8, 128, 4096 + 32)), DSA_ERR_INVALID_ARG),
+        (dict(wb=6), DSA_ERR_INVALID_ARG),
+        (dict(wb=0), DSA_ERR_INVALID_ARG),
+        (dict(wc=2), DSA_ERR_INVALID_ARG),
+        (dict(blocks=0), DSA_ERR_INVALID_ARG),
+        (dict(counts=0), DSA_ERR_INVALID_ARG),
+        (dict(blocks=260), DSA_ERR_INVALID_ARG),
+        (dict(counts=260), DSA_ERR_INVALID_ARG),
+    ]
+    for over, code in cases:
+        a = dict(shape=good, blocks=256, wb=60, cols=512, wc=100, counts=1024)
+        a.update(over)
+        with pytest.raises(_lib.DsaError) as ei:
+            _lib.sparse_attn_lists_raw(a["shape"], 256, 256, 256, a["blocks"], a["wb"], a["cols"], a["wc"],
+                                       a["counts"], 0.0, 256)
+        assert ei.value.status == code, over
+    ws = _lib.vertical_slash_workspace_bytes(good, 100, 30)
+    for over, code in [(dict(cols=0), DSA_ERR_INVALID_ARG), (dict(ws_bytes=ws - 256), DSA_ERR_WORKSPACE),
+                       (dict(ks=0), DSA_ERR_INVALID_ARG)]:
+        a = dict(cols=512, ws_bytes=ws, ks=30)
+        a.update(over)
+        with pytest.raises(_lib.DsaError) as ei:
+            _lib.vertical_slash_select_lists_raw(good, 256, 256, 100, a["ks"], 256, a["cols"], 1024, 0, 0, 256,
+                                                 a["ws_bytes"])
+        assert ei.value.status == code, over
+    bws = _lib.block_sparse_workspace_bytes(good, 100)
+    for over, code in [(dict(counts=0), DSA_ERR_INVALID_ARG), (dict(ws_bytes=bws - 256), DSA_ERR_WORKSPACE),
+                       (dict(kb=0), DSA_ERR_INVALID_ARG)]:
+        a = dict(counts=1024, ws_bytes=bws, kb=100)
+        a.update(over)
+        with pytest.raises(_lib.DsaError) as ei:
+            _lib.block_sparse_select_lists_raw(good, 256, 256, a["kb"], 256, a["counts"], 256, a["ws_bytes"])
+        assert ei.value.status == code, over
+
+
 def test_prune_rope_sizes_and_rejections():
     s = Shape(DSA_PREFILL, DSA_BF16, 1, 32, 8, 128, 4096)
     plain = _lib.workspace_bytes(s, P2)

@@ -1,8 +1,10 @@
 """GPU parity of the vertical-slash heads (MInference page, "Online Dynamic
 Index Estimation: Vertical-Slash Heads (Algorithm 2)" and "Vertical-Slash
 Hybrid Kernel (Appendix C.4.2)"): dsa_vertical_slash_select (kept columns,
-kept offsets, index rows) and dsa_sparse_attn_heads over its rows, through the
-C ABI, against the CPU oracle.
+kept offsets, index rows) and dsa_sparse_attn_heads over its rows, and the
+hybrid kernel's form (dsa_vertical_slash_select_lists: block and column
+lists; dsa_sparse_attn_lists over them), through the C ABI, against the CPU
+oracle.
 
 The column and offset sums are fp64 on both sides (exact fp32 dot products,
 fp64 softmax, summed in different orders) and are ranked after one rounding to
@@ -134,3 +136,98 @@ def test_vs_identical_keys_tie_to_lower_indices():
     for h in range(2):
         assert np.array_equal(cols[0, h].cpu().numpy(), np.arange(50))
         assert np.array_equal(offs[0, h].cpu().numpy(), np.arange(9))
+
+
+# --------------------------------------------------------------------------- #
+# the hybrid kernel's block and column lists                                  #
+# --------------------------------------------------------------------------- #
+def run_lists(dev, k_v, k_s):
+    blocks, cols, counts, kc, ko = api.vertical_slash_select_lists(dev.q, dev.k, k_v, k_s, return_lines=True)
+    out = api.sparse_attn_lists(dev.q, dev.k, dev.v, blocks, counts, cols)
+    torch.cuda.synchronize()
+    return tuple(x.cpu().numpy() for x in (blocks, cols, counts, kc, ko, out))
+
+
+def check_lists(case, k_v, k_s, heads, blocks, attn, b=0, what=""):
+    dev = to_device(case)
+    bl, cl, cn, kc, ko, out = run_lists(dev, k_v, k_s)
+    Q, K, V = case.q.sub(b).f32(), case.k[b].f32(), case.v[b].f32()
+    T = Q.shape[1]
+    wb, wc = bl.shape[-1], cl.shape[-1]
+    assert wb == (min(T // 64, 2 * k_s) + 3) // 4 * 4 and wc == (max(k_v, 1) + 3) // 4 * 4
+    G = Q.shape[0] // K.shape[0]
+    scale = ref.default_scale(Q.shape[2])
+    for h in heads:
+        sv, ss = ref.vs_sums(Q, K, h)
+        iv = H.kept_set_or_legal_swap(kc[b, h], sv, k_v, f"{what} head {h} columns")
+        is_ = H.kept_set_or_legal_swap(ko[b, h], ss, k_s, f"{what} head {h} offsets")
+        for m in blocks:
+            wbl, wcl = ref.vs_lists(iv, is_, m)
+            assert tuple(cn[b, h, m]) == (len(wbl), len(wcl)), f"{what} counts (h={h}, m={m})"
+            assert np.array_equal(bl[b, h, m], ref.pad_row(wbl, wb)), f"{what} blocks (h={h}, m={m})"
+            assert np.array_equal(cl[b, h, m], ref.pad_row(wcl, wc)), f"{what} columns (h={h}, m={m})"
+            if m in attn:
+                row = ref.list_positions(wbl, wcl)
+                t = 64 * m + np.arange(64)
+                seen = (row[None, :] <= t[:, None]).any(axis=1) if len(row) else np.zeros(64, bool)
+                g = h // G
+                o = ref.attend_block(Q[h:h + 1, 64 * m:64 * m + 64], K[g:g + 1], V[g:g + 1], row, 64 * m, scale)[0]
+                H.assert_close(out[b, h, 64 * m:64 * m + 64], o, f"{what} list attention (h={h}, m={m})")
+                assert np.all(out[b, h, 64 * m:64 * m + 64][~seen] == 0), f"{what}: a query with no key is not 0"
+    return bl, cl, cn, out
+
+
+def test_vs_lists_small_random_all_rows():
+    """Random inputs, 4 q / 2 kv heads, 12 blocks, two sequences: every
+    block and column list, and the list attention of every block (d = 128:
+    the list attention's head size)."""
+    case = gen.make_case("c2", hq=4, hkv=2, d=128, t=64 * 12, batch=2, structure="plain", n_needles=0,
+                         n_sink=64, n_window=64, chunk=(64,), keep=(128,))
+    H.say("vs lists small random: (k_v, k_s) = (20, 5), batch 2")
+    for b in range(2):
+        check_lists(case, 20, 5, range(4), range(12), set(range(12)), b=b, what=f"seq {b}")
+
+
+def test_vs_lists_llama_heads_local_4k():
+    """Llama-shaped heads at T = 4096 (local diagonal), (100, 30): every list
+    of 8 heads against the oracle and list attention in 6 blocks; every list
+    of all 32 heads expands to the same call's rows; the list attention
+    matches the row attention; deterministic."""
+    case = gen.make_case("c2", t=4096, structure="local", n_needles=0)
+    H.say("vs lists 32/8 heads T=4096 local: (100, 30)")
+    bl, cl, cn, out = check_lists(case, 100, 30, [0, 3, 9, 14, 20, 25, 30, 31], range(64),
+                                  {0, 1, 17, 40, 62, 63}, what="4k lists")
+    dev = to_device(case)
+    idx, _, _, out_rows = run(dev, 100, 30)
+    for h in range(32):
+        for m in range(64):
+            pos = ref.list_positions(bl[0, h, m, :cn[0, h, m, 0]], cl[0, h, m, :cn[0, h, m, 1]])
+            row = idx[0, h, m]
+            assert np.array_equal(pos, row[row >= 0]), f"lists vs rows (h={h}, m={m})"
+    H.assert_close(out, out_rows, "list vs row attention")
+    bl2, cl2, cn2, _, _, out2 = run_lists(dev, 100, 30)
+    assert np.array_equal(bl, bl2) and np.array_equal(cl, cl2) and np.array_equal(out, out2), "not deterministic"
+
+
+def test_vs_lists_32k_sampled():
+    """The 32K workload (local diagonal) at the page's (3000, 200): lists of 4
+    heads in 15 sampled blocks, 4 of them through list attention."""
+    case = gen.make_case("c2", structure="local", n_needles=0)
+    rng = np.random.default_rng(4)
+    blocks = sorted(set([0, 1, 511] + rng.integers(0, 512, 12).tolist()))
+    H.say("vs lists 32K local: (3000, 200)")
+    check_lists(case, 3000, 200, [0, 5, 13, 31], blocks, set(blocks[:4]), what="32k lists")
+
+
+def test_vs_lists_every_offset_is_dense_attention():
+    """k_s = T lists every causal block and no column: the list attention
+    equals the library's dense path."""
+    case = gen.make_case("c2", hq=4, hkv=1, d=128, t=512, structure="plain", n_needles=0, n_sink=64,
+                         n_window=64, chunk=(64,), keep=(128,))
+    dev = to_device(case)
+    bl, cl, cn, kc, ko, out = run_lists(dev, 7, 512)
+    assert np.array_equal(cn[0, :, :, 0], np.broadcast_to(np.arange(1, 9), (4, 8)))
+    assert np.all(cn[0, :, :, 1] == 0)
+    dense = api.dense_attn(dev.q, dev.k, dev.v)
+    torch.cuda.synchronize()
+    H.assert_close(out, dense.cpu().numpy(), "every offset (lists) vs dense path")
