@@ -139,7 +139,7 @@ StepLayout step_layout(const dsa_shape* s, const dsa_params* p) {
   StepLayout L{};
   L.pl = prune_layout(s, p);
   const long long width = index_width_ll(p);
-  L.nsp = (width + dsa::kStepSplitKeys - 1) / dsa::kStepSplitKeys;
+  L.nsp = (width + dsa::step_split_shift(p->n_sink) + dsa::kStepSplitKeys - 1) / dsa::kStepSplitKeys;
   const size_t fused = s->mode == DSA_DECODE
                            ? static_cast<size_t>(s->batch) * s->hq * L.nsp * (s->d + 2) * 4 : 0;
   L.off_part = align256(L.pl.bytes);
@@ -361,8 +361,10 @@ dsa_status run_prune_attend(const dsa_shape* s, const void* q, const void* k, co
     {
       const int ls = p->n_stages - 1;
       const long long kept_hi = static_cast<long long>(p->n_sink) + p->keep[ls];   // most kept entries
-      sa.ks0 = std::min<int>(sa.nsp, p->n_sink / dsa::kStepSplitKeys);
-      sa.ks1 = static_cast<int>(std::min<long long>(sa.nsp, (kept_hi + dsa::kStepSplitKeys - 1) / dsa::kStepSplitKeys));
+      sa.sh0 = dsa::step_split_shift(p->n_sink);
+      sa.ks0 = std::min<int>(sa.nsp, (p->n_sink + sa.sh0) / dsa::kStepSplitKeys);
+      sa.ks1 = static_cast<int>(
+          std::min<long long>(sa.nsp, (kept_hi + sa.sh0 + dsa::kStepSplitKeys - 1) / dsa::kStepSplitKeys));
       sa.ks1 = std::max(sa.ks1, sa.ks0);
     }
     fused = dsa::launch_decode_attend(sa, dsa::last_stage_chunks(a), hs);

@@ -7,8 +7,10 @@
 // Attention Implementation", with the partial softmax merge of the InfLLM blog
 // page ("Mathematical Formulation of Efficient Softmax Normalization").
 //
-// The index row of a sequence is cut into splits of kSplitKeys entries; one
-// workgroup owns one (split, kv head, sequence):
+// The index row of a sequence is cut into splits of kSplitKeys entries, the
+// grid anchored where the sinks end so the kept entries fill whole splits
+// (split 0 then holds the sinks and padding before entry 0); one workgroup
+// owns one (split, kv head, sequence):
 //   * a split that holds kept chunks of the last stage selects the row's kept
 //     chunks itself from the stage's complete score list (select_cols, the
 //     same selection as k_topk: score descending, lower chunk first), so the
@@ -85,7 +87,7 @@ __global__ void __launch_bounds__(256, 2) k_decode_attend(StepArgs s) {
   const int n_sel = min(nc, kc);
   const int win0 = geo.sink_hi + (n_sel << lg);   // kept chunks fill [sink_hi, win0)
   const int end = win0 + max(0, e - geo.mid_hi);  // then the window [mid_hi, e)
-  const int i0 = sp * kSplitKeys;
+  const int i0 = sp * kSplitKeys - s.sh0;          // (split 0 may start before entry 0)
 
   if (i0 < win0 && i0 + kSplitKeys > geo.sink_hi) {
     uint32_t key[E];
@@ -97,7 +99,9 @@ __global__ void __launch_bounds__(256, 2) k_decode_attend(StepArgs s) {
   if (tid < kSplitKeys) {
     const int i = i0 + tid;
     int p = -1;
-    if (i < geo.sink_hi) {
+    if (i < 0) {
+      p = -1;
+    } else if (i < geo.sink_hi) {
       p = i;
     } else if (i < win0) {
       const int c = i - geo.sink_hi;
@@ -105,7 +109,7 @@ __global__ void __launch_bounds__(256, 2) k_decode_attend(StepArgs s) {
     } else if (i < end) {
       p = geo.mid_hi + (i - win0);
     }
-    if (g == 0 && i < a.L) a.idx[static_cast<size_t>(r) * a.L + i] = p;
+    if (g == 0 && i >= 0 && i < a.L) a.idx[static_cast<size_t>(r) * a.L + i] = p;
     spos[tid] = p;
   }
   __syncthreads();

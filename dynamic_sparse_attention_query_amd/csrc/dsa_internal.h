@@ -81,6 +81,7 @@ struct StepArgs {
   float* out;                // [B, Hq, D]
   float scale_log2;
   int nsp;                   // splits per row
+  int sh0;                   // split sp holds row entries [sp * kStepSplitKeys - sh0, + kStepSplitKeys)
   int ks0, ks1;              // splits [ks0, ks1) may hold kept chunks (scheduled first)
 };
 
@@ -375,6 +376,10 @@ int last_stage_chunks(const PruneArgs& a);
 // the shape takes the separate kernels (nothing launched then)
 bool launch_decode_attend(const StepArgs& s, int sel_chunks, hipStream_t stream);
 constexpr int kStepSplitKeys = 128;   // index-row entries per workgroup of the fused tail
+// Offset of the fused tail's split grid: the splits start at the end of the
+// sinks, so the kept entries fill whole splits (with 64 sinks, 4,096 kept
+// keys take 32 splits, not 33: one workgroup per CU for the 8 kv heads).
+inline int step_split_shift(int n_sink) { return (kStepSplitKeys - n_sink % kStepSplitKeys) % kStepSplitKeys; }
 // decode with remembered stages: only the stages flagged in due[] are recomputed
 hipError_t launch_prune_cached(const PruneArgs& a, const bool* due, int dtype, hipStream_t stream);
 hipError_t launch_sparse_attn(const AttnArgs& a, int dtype, hipStream_t stream);
