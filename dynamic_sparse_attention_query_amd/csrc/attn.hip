@@ -139,13 +139,18 @@ __global__ void __launch_bounds__(256) k_decode_partial(AttnArgs a) {
 }
 
 // Merge split partials: M = max m_s, out = sum o_s 2^(m_s-M) / sum l_s 2^(m_s-M).
-// 1024 threads: split weights go to LDS, then 1024/D groups of D threads each
-// sum a strided share of the splits with independent (unrolled) loads.
+// 1024 threads: 1024/D groups of D threads each take a strided share of the
+// splits. Every load a thread needs (its first kPrefetch shares of o, and
+// m_s, l_s of split tid) is issued before the first barrier, so a merge of up
+// to 1024 splits costs one memory round trip; longer rows (the dense path)
+// loop over the rest.
 constexpr int kCombineThreads = 1024;
 constexpr int kMaxSplits = 4096;
 
 template <int D>
 __global__ void __launch_bounds__(kCombineThreads) k_decode_combine(AttnArgs a) {
+  constexpr int kPrefetch = 8;
+  constexpr int SG = kCombineThreads / D;
   const int h = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   constexpr int NW = kCombineThreads / 64;
@@ -154,8 +159,21 @@ __global__ void __launch_bounds__(kCombineThreads) k_decode_combine(AttnArgs a) 
   __shared__ float wsh[kMaxSplits];
   __shared__ float red[NW];
   __shared__ float red2[NW];
-  float m = kNegBig;
-  for (int s = tid; s < ns; s += kCombineThreads) m = fmaxf(m, P[static_cast<size_t>(s) * (D + 2) + D]);
+  const int dd = tid % D, sg = tid / D;
+  float v[kPrefetch];
+#pragma unroll
+  for (int u = 0; u < kPrefetch; ++u) {
+    const int s = sg + u * SG;
+    v[u] = s < ns ? P[static_cast<size_t>(s) * (D + 2) + dd] : 0.f;
+  }
+  float m0 = kNegBig, l0 = 0.f;
+  if (tid < ns) {
+    const float2 ml = *reinterpret_cast<const float2*>(P + static_cast<size_t>(tid) * (D + 2) + D);
+    m0 = ml.x;
+    l0 = ml.y;
+  }
+  float m = m0;
+  for (int s = tid + kCombineThreads; s < ns; s += kCombineThreads) m = fmaxf(m, P[static_cast<size_t>(s) * (D + 2) + D]);
   m = wave_max_f(m);
   if (lane == 0) red[w] = m;
   __syncthreads();
@@ -163,7 +181,12 @@ __global__ void __launch_bounds__(kCombineThreads) k_decode_combine(AttnArgs a) 
 #pragma unroll
   for (int i = 1; i < NW; ++i) M = fmaxf(M, red[i]);
   float lsum = 0.f;
-  for (int s = tid; s < ns; s += kCombineThreads) {
+  if (tid < ns) {
+    const float f = exp2f(m0 - M);
+    wsh[tid] = f;
+    lsum = l0 * f;
+  }
+  for (int s = tid + kCombineThreads; s < ns; s += kCombineThreads) {
     const float* ps = P + static_cast<size_t>(s) * (D + 2);
     const float f = exp2f(ps[D] - M);
     wsh[s] = f;
@@ -175,16 +198,19 @@ __global__ void __launch_bounds__(kCombineThreads) k_decode_combine(AttnArgs a) 
   float Ltot = 0.f;
 #pragma unroll
   for (int i = 0; i < NW; ++i) Ltot += red2[i];
-  constexpr int SG = kCombineThreads / D;
-  const int dd = tid % D, sg = tid / D;
   float o = 0.f;
-  int s = sg;
+#pragma unroll
+  for (int u = 0; u < kPrefetch; ++u) {
+    const int s = sg + u * SG;
+    if (s < ns) o = fmaf(v[u], wsh[s], o);
+  }
+  int s = sg + kPrefetch * SG;
   for (; s + 7 * SG < ns; s += 8 * SG) {
-    float v[8];
+    float x[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = P[static_cast<size_t>(s + u * SG) * (D + 2) + dd];
+    for (int u = 0; u < 8; ++u) x[u] = P[static_cast<size_t>(s + u * SG) * (D + 2) + dd];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) o = fmaf(v[u], wsh[s + u * SG], o);
+    for (int u = 0; u < 8; ++u) o = fmaf(x[u], wsh[s + u * SG], o);
   }
   for (; s < ns; s += SG) o = fmaf(P[static_cast<size_t>(s) * (D + 2) + dd], wsh[s], o);
   __shared__ float so[SG][D];
