@@ -12,7 +12,7 @@
 // (split 0 then holds the sinks and padding before entry 0); one workgroup
 // owns one (split, kv head, sequence):
 //   * a split that holds kept chunks of the last stage selects the row's kept
-//     chunks itself from the stage's complete score list (select_cols, the
+//     chunks itself from the stage's complete score list (select_keys, the
 //     same selection as k_topk: score descending, lower chunk first), so the
 //     selection needs no kernel of its own; splits of sinks, window or padding
 //     skip it and start their loads at once;
@@ -41,7 +41,7 @@ __global__ void __launch_bounds__(256, 2) k_decode_attend(StepArgs s) {
   using Row = RowSlice<T, EPL>;
   constexpr int NO = (G * D) / 256;           // outputs per thread in the reduction (G * D >= 256)
   static_assert(G * D % 256 == 0, "whole outputs per thread");
-  __shared__ SelectColLds<kTopkWaves> LS;
+  __shared__ SelectKeysLds<kTopkWaves> LS;
   __shared__ int sprev[kFusedMaxKept];
   __shared__ int skept[kFusedMaxKept + 64];
   __shared__ int spos[kSplitKeys];
@@ -91,9 +91,9 @@ __global__ void __launch_bounds__(256, 2) k_decode_attend(StepArgs s) {
 
   if (i0 < win0 && i0 + kSplitKeys > geo.sink_hi) {
     uint32_t key[E];
-    load_keys_cols<E>(a, ls, r, key);
+    load_keys<E>(a, ls, r, threadIdx.x * E, key);
     if (ls > 0) load_kept_starts(a, ls - 1, r, sprev);
-    select_cols<E>(key, nc, kc, LS, skept);
+    select_keys<E>(key, nc, kc, LS, skept);
     __syncthreads();                            // skept holds the kept chunk indices
   }
   if (tid < kSplitKeys) {

@@ -204,7 +204,7 @@ k_score_decode(PruneArgs a, int stage) {
 // Top-K of stage `stage - 1` fused with the SelectRep scoring of stage `stage`
 // (decode, bf16). Every workgroup of the scoring launch selects the row's kept
 // chunks of the previous stage itself from that stage's complete score list
-// (select_cols, the latency-oriented selection), so the two steps meet at one
+// (select_keys, the latency-oriented selection), so the two steps meet at one
 // kernel boundary instead of two; workgroup 0 also writes the kept starts and
 // their count for the stages after. The tournaments are those of
 // k_score_decode.
@@ -212,7 +212,7 @@ template <typename T, int D, int G, int SPEC, int E, bool PAGED>
 __global__ void __launch_bounds__(256, 2) k_topk_score_decode(PruneArgs a, int stage) {
   constexpr int EPL = D / 16;
   using Row = RowSlice<T, EPL>;
-  __shared__ SelectColLds<kTopkWaves> L;
+  __shared__ SelectKeysLds<kTopkWaves> L;
   __shared__ int sprev[kFusedMaxKept];
   __shared__ int skept[kFusedMaxKept + 64];
   __shared__ float red[16];
@@ -231,7 +231,7 @@ __global__ void __launch_bounds__(256, 2) k_topk_score_decode(PruneArgs a, int s
   const int e = seq_len_of(kv, r);
   const int nc_before = ps > 0 ? a.cnt[r * kMaxStages + ps - 1] : 0;
   uint32_t key[E];
-  load_keys_cols<E>(a, ps, r, key);
+  load_keys<E>(a, ps, r, threadIdx.x * E, key);
   if (ps > 0) load_kept_starts(a, ps - 1, r, sprev);
   Row q[G];
 #pragma unroll
@@ -242,7 +242,7 @@ __global__ void __launch_bounds__(256, 2) k_topk_score_decode(PruneArgs a, int s
   const int shp = ps > 0 ? a.lchunk[ps - 1] - lgp : 0;
   const int nc_ps = ps == 0 ? geo.n1 : nc_before << shp;
   const int kc_ps = a.keep[ps] >> lgp;
-  const int n_sel = select_cols<E>(key, nc_ps, kc_ps, L, skept);
+  const int n_sel = select_keys<E>(key, nc_ps, kc_ps, L, skept);
   __syncthreads();                              // the kept chunk indices are in skept
   if (blockIdx.x == 0) {                        // workgroup 0 records the stage's output
     int32_t* out = stage_starts(a, ps, r);

@@ -71,17 +71,6 @@ __device__ __forceinline__ void load_keys(const PruneArgs& a, int stage, int r, 
   }
 }
 
-// This thread's keys in the column layout of select_cols: lane l of wave w
-// holds chunks w*64*E + 64*x + l (read within the row's list for every index
-// of the launch; select_cols masks indices >= nc).
-template <int E>
-__device__ __forceinline__ void load_keys_cols(const PruneArgs& a, int stage, int r, uint32_t (&key)[E]) {
-  const uint32_t* sc = stage_scores(a, stage, r);
-  const int jw = (threadIdx.x >> 6) * 64 * E + (threadIdx.x & 63);
-#pragma unroll
-  for (int x = 0; x < E; ++x) key[x] = sc[min(jw + 64 * x, a.maxNC - 1)];
-}
-
 // First key position of kept chunk j of stage ps, given the kept starts of
 // stage ps - 1 in sprev (chunk sizes are powers of two).
 __device__ __forceinline__ int kept_start(const PruneArgs& a, int ps, int j, const int* sprev) {

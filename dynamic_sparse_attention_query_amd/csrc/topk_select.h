@@ -230,14 +230,13 @@ __device__ __forceinline__ void select_row(uint32_t (&key)[E], int j0, int nc, i
 namespace dsa {
 
 // ------------------------------------------------------------------------- //
-// Latency-oriented top-K of one row, keys in column layout                  //
+// Latency-oriented top-K of one row, keys in thread order                   //
 // ------------------------------------------------------------------------- //
 // The same selection as select_row (larger key first, lower index first among
 // equal keys), written for the shortest instruction stream per wave: the
-// decode kernels run it in every workgroup, on the critical path. Lane l of
-// wave w holds the keys of indices j = w*64*E + 64*x + l (x = 0 .. E-1), so
-// for a fixed x a wave's 64 keys are consecutive indices and per-column lane
-// masks (ballots) are in index order.
+// decode kernels run it in every workgroup, on the critical path. Thread t
+// holds the keys of indices j = t*E .. t*E+E-1, so thread order is index
+// order and one block-wide scan ranks every key.
 //   * Every key becomes its distance below the OR of the row's keys,
 //     d = (vor - key) >> lsb, with lsb the lowest bit in which the keys differ:
 //     vor >= every key and all keys share the bits below lsb, so d is exact
@@ -253,15 +252,14 @@ namespace dsa {
 //     bins), so sharing the result takes no further barrier. A boundary bin
 //     that is not kept whole is split again at a finer width until its width
 //     is one; the exact-score keys of the decode workloads take two passes.
-//   * The kept keys of each column are two ballots (strictly inside, equal to
-//     the threshold); a block-wide scan of the waves' counts and a running
-//     count per column give each kept key its output slot, mbcnt its place in
-//     the column. Ties at the threshold go to the lowest indices.
+//   * Each thread counts its keys strictly inside the kept range and equal to
+//     the threshold; one block-wide scan of the packed counts gives each
+//     thread the number of kept keys before its own (ties at the threshold go
+//     to the lowest indices), and the thread writes its kept indices in
+//     order from there.
 // kept[0 .. min(nc, kc)) receives the kept indices in ascending order; it is
-// complete after the caller's next barrier; kept[] needs kc + 64 entries (the
-// last 64 take the writes of keys that are not kept, one per lane, so the
-// writes need no branch). Keys are 0 for absent chunks (real keys are never
-// 0). Returns the number kept.
+// complete after the caller's next barrier. Keys are 0 for absent chunks
+// (real keys are never 0). Returns the number kept.
 constexpr int kHistBins = 2048;
 // The histogram is stored as 64 blocks of 32 bins, each followed by 4 words of
 // padding: a lane's block then starts 4 banks after its left neighbour's, so
@@ -272,31 +270,31 @@ constexpr int kHistWords = kHistBins / 32 * kHistBlock;
 __device__ __forceinline__ uint32_t hist_slot(uint32_t bin) { return bin + ((bin >> 5) << 2); }
 
 template <int NW>
-struct SelectColLds {
+struct SelectKeysLds {
   uint32_t hist[2][kHistWords + 64];             // + one spare bin per lane (second pass)
   uint32_t wred[2][NW];
   uint32_t wcnt[NW];
 };
 
 template <int E, int NT = kTopkThreads>
-__device__ __forceinline__ int select_cols(const uint32_t (&key)[E], int nc, int kc, SelectColLds<NT / 64>& L,
+__device__ __forceinline__ int select_keys(const uint32_t (&key)[E], int nc, int kc, SelectKeysLds<NT / 64>& L,
                                            int* kept) {
   constexpr int NW = NT / 64;
   constexpr uint32_t kSpare = kHistWords;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int jw = w * 64 * E + lane;                // index of column x: jw + 64 x
+  const int j0 = tid * E;                          // this thread's first index
   if (nc <= kc) {                                  // every chunk is kept, in index order
     __syncthreads();                               // publishes the caller's LDS data, as below
 #pragma unroll
     for (int x = 0; x < E; ++x)
-      if (jw + 64 * x < nc) kept[jw + 64 * x] = jw + 64 * x;
+      if (j0 + x < nc) kept[j0 + x] = j0 + x;
     return nc;
   }
   uint32_t k[E];
   uint32_t vand = 0xffffffffu, vor = 0u;
 #pragma unroll
   for (int x = 0; x < E; ++x) {
-    k[x] = jw + 64 * x < nc ? key[x] : 0u;
+    k[x] = j0 + x < nc ? key[x] : 0u;
     vand &= k[x] ? k[x] : 0xffffffffu;
     vor |= k[x];
   }
@@ -376,44 +374,31 @@ __device__ __forceinline__ int select_cols(const uint32_t (&key)[E], int nc, int
   const int need_eq = __builtin_amdgcn_readfirstlane(whole ? 0 : need);
   const uint32_t wbin = whole ? (1u << s) : 0u;    // width of the boundary bin kept whole
   const uint32_t eqv = whole ? 0xffffffffu : base; // d of the ties (none when whole)
-  auto strict_of = [&](int x) { return d[x] < base || d[x] - base < wbin; };
-  int ns = 0, ne = 0;
+  uint32_t ms = 0u, me = 0u;                       // this thread's strict / equal keys, by x
 #pragma unroll
   for (int x = 0; x < E; ++x) {
-    ns += __popcll(__ballot(strict_of(x)));
-    ne += __popcll(__ballot(d[x] == eqv));
+    ms |= static_cast<uint32_t>(d[x] < base || d[x] - base < wbin) << x;
+    me |= static_cast<uint32_t>(d[x] == eqv) << x;
   }
-  if (lane == 0) L.wcnt[w] = (static_cast<uint32_t>(ns) << 16) | static_cast<uint32_t>(ne);
+  // counts packed (strict << 16 | equal): a workgroup holds at most 65,535
+  // keys of each, so the halves never carry into each other
+  const uint32_t cnt = (static_cast<uint32_t>(__popc(ms)) << 16) | static_cast<uint32_t>(__popc(me));
+  const uint32_t inc = wave_incl_scan_u32(cnt);
+  if (lane == 63) L.wcnt[w] = inc;
   __syncthreads();
-  int cs = 0, ce = 0;                              // strict / equal keys of the waves before
+  uint32_t before = inc - cnt;                     // keys of the threads before, this wave
 #pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    const uint32_t v = L.wcnt[i];
-    cs += i < w ? static_cast<int>(v >> 16) : 0;
-    ce += i < w ? static_cast<int>(v & 0xffffu) : 0;
-  }
-  cs = __builtin_amdgcn_readfirstlane(cs);
-  ce = __builtin_amdgcn_readfirstlane(ce);
-  int run = cs + min(ce, need_eq);                 // output slot of this wave's next kept key
-  int* spare = kept + kc + lane;
+  for (int i = 0; i < NW; ++i) before += i < w ? L.wcnt[i] : 0u;
+  int erank = static_cast<int>(before & 0xffffu);  // ties at the threshold before this thread's
+  int slot = static_cast<int>(before >> 16) + min(erank, need_eq);
 #pragma unroll
   for (int x = 0; x < E; ++x) {
-    unsigned long long t = __ballot(strict_of(x));
-    const unsigned long long e = __ballot(d[x] == eqv);
-    const int avail = need_eq - ce;
-    const int ec = __popcll(e);
-    if (avail >= ec) {
-      t |= e;
-    } else if (avail > 0) {                        // the boundary column: its lowest `avail` ties
-      unsigned long long m = e;
-      for (int i = 0; i < avail; ++i) m &= m - 1ull;
-      t |= e ^ m;
+    bool keep = (ms >> x) & 1u;
+    if ((me >> x) & 1u) {                          // (strict and equal only when need_eq is 0)
+      keep = keep || erank < need_eq;
+      ++erank;
     }
-    ce += ec;
-    const int mb = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(t >> 32),
-                                             __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(t), 0));
-    *(((t >> lane) & 1ull) ? kept + run + mb : spare) = jw + 64 * x;
-    run += __popcll(t);
+    if (keep) kept[slot++] = j0 + x;
   }
   return kc;
 }
