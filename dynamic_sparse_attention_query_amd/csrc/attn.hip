@@ -98,11 +98,11 @@ __global__ void __launch_bounds__(256) k_decode_partial(AttnArgs a) {
       const float z = sp[hh][lane];
       const float m_old = sm[hh];
       const float m_new = fmaxf(m_old, wave_max_f(z));
-      const float pz = (z == -INFINITY) ? 0.f : exp2f(z - m_new);
+      const float pz = (z == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(z - m_new);
       const float ls = wave_sum_f(pz);
       sp[hh][lane] = pz;
       if (lane == 0) {
-        const float alpha = exp2f(m_old - m_new);
+        const float alpha = __builtin_amdgcn_exp2f(m_old - m_new);
         salpha[hh] = alpha;
         sl[hh] = sl[hh] * alpha + ls;
         sm[hh] = m_new;
@@ -139,6 +139,9 @@ __global__ void __launch_bounds__(256) k_decode_partial(AttnArgs a) {
 }
 
 // Merge split partials: M = max m_s, out = sum o_s 2^(m_s-M) / sum l_s 2^(m_s-M).
+// (Exponentials of the decode kernels use the hardware 2^x: every argument is
+// <= 0, and below -126 it returns 0 where the library routine would return a
+// denormal.)
 // 1024 threads: 1024/D groups of D threads each take a strided share of the
 // splits. Every load a thread needs (its first kPrefetch shares of o, and
 // m_s, l_s of split tid) is issued before the first barrier, so a merge of up
@@ -182,13 +185,13 @@ __global__ void __launch_bounds__(kCombineThreads) k_decode_combine(AttnArgs a) 
   for (int i = 1; i < NW; ++i) M = fmaxf(M, red[i]);
   float lsum = 0.f;
   if (tid < ns) {
-    const float f = exp2f(m0 - M);
+    const float f = __builtin_amdgcn_exp2f(m0 - M);
     wsh[tid] = f;
     lsum = l0 * f;
   }
   for (int s = tid + kCombineThreads; s < ns; s += kCombineThreads) {
     const float* ps = P + static_cast<size_t>(s) * (D + 2);
-    const float f = exp2f(ps[D] - M);
+    const float f = __builtin_amdgcn_exp2f(ps[D] - M);
     wsh[s] = f;
     lsum = fmaf(ps[D + 1], f, lsum);
   }

@@ -171,7 +171,10 @@ __global__ void __launch_bounds__(256, 2) k_decode_attend(StepArgs s) {
     }
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      const float pz = sc[u][hh] == -INFINITY ? 0.f : exp2f(sc[u][hh] - M[hh]);
+      // (the hardware exponential: arguments are <= 0; below -126 it returns
+      // 0 where the library routine would give a denormal, a difference
+      // under 1e-38 in the sums)
+      const float pz = sc[u][hh] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[u][hh] - M[hh]);
       lsum[hh] += pz;
 #pragma unroll
       for (int x = 0; x < EPL; ++x) o[hh][x] = fmaf(pz, vf[x], o[hh][x]);
