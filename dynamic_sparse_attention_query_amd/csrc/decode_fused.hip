@@ -180,20 +180,27 @@ __global__ void __launch_bounds__(256, 2) k_decode_attend(StepArgs s) {
       for (int x = 0; x < EPL; ++x) o[hh][x] = fmaf(pz, vf[x], o[hh][x]);
     }
   }
-  // sum over the wave's four lane groups, then over the waves in LDS
+  // Sum over the wave's four lane groups (16-lane rows), four values at a
+  // time: a row swap of values (a, b) and one of (c, d) leave the pair sums
+  // of a and b, c and d interleaved by row, and a half swap of those leaves
+  // in row r the total of value r, added as (r0 + r1) + (r2 + r3); each row
+  // writes its value. Then over the waves in LDS.
+  constexpr int NV = G * EPL + G;               // per lane: o[hh][x], then lsum[hh]
+  auto val = [&](int i) -> float {
+    return i < G * EPL ? o[i / EPL][i % EPL] : i < NV ? lsum[i - G * EPL] : 0.f;
+  };
+  const int row = lane >> 4;
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    lsum[hh] = rows4_sum(lsum[hh]);
-#pragma unroll
-    for (int x = 0; x < EPL; ++x) o[hh][x] = rows4_sum(o[hh][x]);
-  }
-  if (lane < 16) {
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-#pragma unroll
-      for (int x = 0; x < EPL; ++x) sred[w][hh * D + li * EPL + x] = o[hh][x];
-      if (li == 0) sred[w][G * D + hh] = lsum[hh];
-    }
+  for (int i = 0; i < NV; i += 4) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(val(i)), __float_as_uint(val(i + 1)), false, false);
+    const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(val(i + 2)), __float_as_uint(val(i + 3)), false, false);
+    const float s01 = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    const float s23 = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+    const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(s01), __float_as_uint(s23), false, false);
+    const float tot = __uint_as_float(t[0]) + __uint_as_float(t[1]);
+    const int vi = i + row;                     // the value whose total this row holds
+    if (vi < G * EPL) sred[w][(vi / EPL) * D + li * EPL + vi % EPL] = tot;
+    else if (vi < NV && li == 0) sred[w][G * D + vi - G * EPL] = tot;
   }
   __syncthreads();
   float* P = s.part;

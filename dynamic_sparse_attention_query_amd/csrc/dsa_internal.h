@@ -296,16 +296,6 @@ __device__ __forceinline__ float group16_max(float v) {
   return v;
 }
 
-// Sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48), in
-// every lane: the gfx950 row-swap moves (VALU, no LDS round trip) pair rows
-// 0-1 and 2-3, then the halves; every lane adds (r0 + r1) + (r2 + r3).
-__device__ __forceinline__ float rows4_sum(float v) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
 // Whole-wave reductions: rows first, then the four row results through
 // scalar registers (the result is wave-uniform).
 template <typename Op>
