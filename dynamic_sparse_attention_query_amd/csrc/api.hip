@@ -186,6 +186,19 @@ dsa_status run_attn(const dsa_shape* s, const void* q, const void* k, const void
   a.n_splits = static_cast<int>((n_total + a.kps - 1) / a.kps);
   const float sc = scale > 0.f ? scale : 1.0f / std::sqrt(static_cast<float>(s->d));
   a.scale_log2 = sc * 1.4426950408889634f;
+  // bf16 decode over index rows: the fused step's split kernel (splits of
+  // kStepSplitKeys entries, which the workspace holds while they are no fewer
+  // entries than keys_per_split's)
+  if (s->mode == DSA_DECODE && s->dtype == DSA_BF16 && idx && a.kps <= dsa::kStepSplitKeys) {
+    dsa::AttnArgs r = a;
+    r.kps = dsa::kStepSplitKeys;
+    r.n_splits = static_cast<int>((n_total + r.kps - 1) / r.kps);
+    if (dsa::launch_decode_rows(r, static_cast<hipStream_t>(stream))) {
+      const hipError_t e2 = hipGetLastError();
+      if (e2 != hipSuccess) return fail(DSA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e2));
+      return DSA_OK;
+    }
+  }
   hipError_t err = dsa::launch_sparse_attn(a, s->dtype, static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return fail(DSA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(err));
   return DSA_OK;

@@ -33,6 +33,131 @@
 
 namespace dsa {
 
+// One split's partial softmax for the G query heads of kv head g of sequence
+// b: the split's row positions are in spos (negative = padding, masked); lane
+// group gi gathers the K and V rows of entries gi + 16u (16-lane 256-byte row
+// loads, all issued before any arithmetic), scores them against the heads'
+// queries in registers, and the workgroup writes (o[D], m, l) per head to
+// part[((b * Hq + g * G + hh) * nsp + sp) * (D + 2)]: the split partials that
+// k_decode_combine merges ("Flash Decoding" of the InfiniteHiP page's "Block
+// Sparse Attention Implementation"; the merge of the InfLLM blog page's
+// "Mathematical Formulation of Efficient Softmax Normalization").
+template <int D, int G, bool PAGED, int kKeysPerGroup>
+__device__ __forceinline__ void split_partial(const KvLayout& kv, const uint16_t* K, const uint16_t* V,
+                                              const RowSlice<uint16_t, D / 16> (&q)[G], const int* spos,
+                                              float (&smax)[16][G], float (&sred)[4][G * D + G], float* part,
+                                              int nsp, int sp, int b, int g, float scale_log2) {
+  constexpr int EPL = D / 16;
+  using Row = RowSlice<uint16_t, EPL>;
+  constexpr int NO = (G * D) / 256;           // outputs per thread in the reduction (G * D >= 256)
+  static_assert(G * D % 256 == 0, "whole outputs per thread");
+  const int tid = threadIdx.x, gi = tid >> 4, li = tid & 15, lane = tid & 63, w = tid >> 6;
+  // gather the split's K and V rows: lane group gi takes entries gi + 16u
+  int pu[kKeysPerGroup];
+  Row kr[kKeysPerGroup], vr[kKeysPerGroup];
+#pragma unroll
+  for (int u = 0; u < kKeysPerGroup; ++u) {
+    pu[u] = spos[gi + 16 * u];
+    const int pp = max(pu[u], 0);               // padding reads row 0 and is masked below
+    size_t off;
+    if constexpr (PAGED) off = kv_offset(kv, b, g, pp);
+    else off = ((static_cast<size_t>(b) * kv.Hkv + g) * kv.T + pp) * D;
+    kr[u].load(K + off + li * EPL);
+    vr[u].load(V + off + li * EPL);
+  }
+  float sc[kKeysPerGroup][G];
+  float mloc[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) mloc[hh] = kNegBig;
+#pragma unroll
+  for (int u = 0; u < kKeysPerGroup; ++u) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const float d = group16_sum(kr[u].dot(q[hh])) * scale_log2;
+      sc[u][hh] = pu[u] >= 0 ? d : -INFINITY;
+      mloc[hh] = fmaxf(mloc[hh], sc[u][hh]);
+    }
+  }
+  if (li == 0) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) smax[gi][hh] = mloc[hh];
+  }
+  __syncthreads();
+  float M[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    float m = smax[0][hh];
+#pragma unroll
+    for (int x = 1; x < 16; ++x) m = fmaxf(m, smax[x][hh]);
+    M[hh] = m;
+  }
+  // this group's share of l and o = sum_u 2^(s_u - M) v_u
+  float lsum[G], o[G][EPL];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    lsum[hh] = 0.f;
+#pragma unroll
+    for (int x = 0; x < EPL; ++x) o[hh][x] = 0.f;
+  }
+#pragma unroll
+  for (int u = 0; u < kKeysPerGroup; ++u) {
+    float vf[EPL];
+#pragma unroll
+    for (int x = 0; x < EPL / 2; ++x) {
+      vf[2 * x] = __uint_as_float(vr[u].w[x] << 16);
+      vf[2 * x + 1] = __uint_as_float(vr[u].w[x] & 0xffff0000u);
+    }
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      // (the hardware exponential: arguments are <= 0; below -126 it returns
+      // 0 where the library routine would give a denormal, a difference
+      // under 1e-38 in the sums)
+      const float pz = sc[u][hh] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[u][hh] - M[hh]);
+      lsum[hh] += pz;
+#pragma unroll
+      for (int x = 0; x < EPL; ++x) o[hh][x] = fmaf(pz, vf[x], o[hh][x]);
+    }
+  }
+  // Sum over the wave's four lane groups (16-lane rows), four values at a
+  // time: a row swap of values (a, b) and one of (c, d) leave the pair sums
+  // of a and b, c and d interleaved by row, and a half swap of those leaves
+  // in row r the total of value r, added as (r0 + r1) + (r2 + r3); each row
+  // writes its value. Then over the waves in LDS.
+  constexpr int NV = G * EPL + G;               // per lane: o[hh][x], then lsum[hh]
+  auto val = [&](int i) -> float {
+    return i < G * EPL ? o[i / EPL][i % EPL] : i < NV ? lsum[i - G * EPL] : 0.f;
+  };
+  const int row = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < NV; i += 4) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(val(i)), __float_as_uint(val(i + 1)), false, false);
+    const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(val(i + 2)), __float_as_uint(val(i + 3)), false, false);
+    const float s01 = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    const float s23 = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+    const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(s01), __float_as_uint(s23), false, false);
+    const float tot = __uint_as_float(t[0]) + __uint_as_float(t[1]);
+    const int vi = i + row;                     // the value whose total this row holds
+    if (vi < G * EPL) sred[w][(vi / EPL) * D + li * EPL + vi % EPL] = tot;
+    else if (vi < NV && li == 0) sred[w][G * D + vi - G * EPL] = tot;
+  }
+  __syncthreads();
+  float* P = part;
+  const size_t head0 = static_cast<size_t>(b) * kv.Hq + g * G;
+#pragma unroll
+  for (int i = 0; i < NO; ++i) {
+    const int oi = tid + 256 * i;
+    const int hh = oi / D, dd = oi - hh * D;
+    const float v = (sred[0][oi] + sred[1][oi]) + (sred[2][oi] + sred[3][oi]);
+    P[((head0 + hh) * nsp + sp) * (D + 2) + dd] = v;
+  }
+  if (tid < G) {
+    const float lt = (sred[0][G * D + tid] + sred[1][G * D + tid]) + (sred[2][G * D + tid] + sred[3][G * D + tid]);
+    float* mlp = P + ((head0 + tid) * nsp + sp) * (D + 2) + D;
+    mlp[0] = M[tid];
+    mlp[1] = lt;
+  }
+}
+
 template <int D, int G, int E, bool PAGED, int kSplitKeys = kStepSplitKeys>
 __global__ void __launch_bounds__(256, 2) k_decode_attend(StepArgs s) {
   constexpr int kKeysPerGroup = kSplitKeys / 16;
@@ -114,110 +239,42 @@ __global__ void __launch_bounds__(256, 2) k_decode_attend(StepArgs s) {
   }
   __syncthreads();
 
-  // gather the split's K and V rows: lane group gi takes entries gi + 16u
-  int pu[kKeysPerGroup];
-  Row kr[kKeysPerGroup], vr[kKeysPerGroup];
+  split_partial<D, G, PAGED, kKeysPerGroup>(kv, K, V, q, spos, smax, sred, s.part, s.nsp, sp, b, g, s.scale_log2);
+}
+
+// Split partials over index rows given in memory (the two-call decode path:
+// dsa_sparse_attn after a separate prune_select): the same splits of
+// kStepSplitKeys entries and the same gather and reduction as the fused step,
+// with the positions read from the row (entries past the row, negative or
+// after the query are padding).
+template <int D, int G, bool PAGED>
+__global__ void __launch_bounds__(256, 2) k_decode_rows(AttnArgs a) {
+  constexpr int kKeysPerGroup = kStepSplitKeys / 16;
+  constexpr int EPL = D / 16;
+  using Row = RowSlice<uint16_t, EPL>;
+  __shared__ int spos[kStepSplitKeys];
+  __shared__ float smax[16][G];
+  __shared__ float sred[4][G * D + G];
+  const KvLayout& kv = a.kv;
+  const int sp = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, li = tid & 15;
+  const uint16_t* Q = static_cast<const uint16_t*>(a.q);
+  Row q[G];
 #pragma unroll
-  for (int u = 0; u < kKeysPerGroup; ++u) {
-    pu[u] = spos[gi + 16 * u];
-    const int pp = max(pu[u], 0);               // padding reads row 0 and is masked below
-    size_t off;
-    if constexpr (PAGED) off = kv_offset(kv, b, g, pp);
-    else off = ((static_cast<size_t>(b) * kv.Hkv + g) * kv.T + pp) * D;
-    kr[u].load(K + off + li * EPL);
-    vr[u].load(V + off + li * EPL);
-  }
-  float sc[kKeysPerGroup][G];
-  float mloc[G];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) mloc[hh] = kNegBig;
-#pragma unroll
-  for (int u = 0; u < kKeysPerGroup; ++u) {
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      const float d = group16_sum(kr[u].dot(q[hh])) * s.scale_log2;
-      sc[u][hh] = pu[u] >= 0 ? d : -INFINITY;
-      mloc[hh] = fmaxf(mloc[hh], sc[u][hh]);
+  for (int hh = 0; hh < G; ++hh) q[hh].load(Q + (static_cast<size_t>(b) * kv.Hq + g * G + hh) * D + li * EPL);
+  const int tq = seq_len_of(kv, b) - 1;
+  if (tid < kStepSplitKeys) {
+    const int i = sp * kStepSplitKeys + tid;
+    int p = -1;
+    if (i < a.L) {
+      p = a.idx[static_cast<size_t>(b) * a.L + i];
+      if (p < 0 || p > tq) p = -1;
     }
-  }
-  if (li == 0) {
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) smax[gi][hh] = mloc[hh];
+    spos[tid] = p;
   }
   __syncthreads();
-  float M[G];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    float m = smax[0][hh];
-#pragma unroll
-    for (int x = 1; x < 16; ++x) m = fmaxf(m, smax[x][hh]);
-    M[hh] = m;
-  }
-  // this group's share of l and o = sum_u 2^(s_u - M) v_u
-  float lsum[G], o[G][EPL];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    lsum[hh] = 0.f;
-#pragma unroll
-    for (int x = 0; x < EPL; ++x) o[hh][x] = 0.f;
-  }
-#pragma unroll
-  for (int u = 0; u < kKeysPerGroup; ++u) {
-    float vf[EPL];
-#pragma unroll
-    for (int x = 0; x < EPL / 2; ++x) {
-      vf[2 * x] = __uint_as_float(vr[u].w[x] << 16);
-      vf[2 * x + 1] = __uint_as_float(vr[u].w[x] & 0xffff0000u);
-    }
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      // (the hardware exponential: arguments are <= 0; below -126 it returns
-      // 0 where the library routine would give a denormal, a difference
-      // under 1e-38 in the sums)
-      const float pz = sc[u][hh] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[u][hh] - M[hh]);
-      lsum[hh] += pz;
-#pragma unroll
-      for (int x = 0; x < EPL; ++x) o[hh][x] = fmaf(pz, vf[x], o[hh][x]);
-    }
-  }
-  // Sum over the wave's four lane groups (16-lane rows), four values at a
-  // time: a row swap of values (a, b) and one of (c, d) leave the pair sums
-  // of a and b, c and d interleaved by row, and a half swap of those leaves
-  // in row r the total of value r, added as (r0 + r1) + (r2 + r3); each row
-  // writes its value. Then over the waves in LDS.
-  constexpr int NV = G * EPL + G;               // per lane: o[hh][x], then lsum[hh]
-  auto val = [&](int i) -> float {
-    return i < G * EPL ? o[i / EPL][i % EPL] : i < NV ? lsum[i - G * EPL] : 0.f;
-  };
-  const int row = lane >> 4;
-#pragma unroll
-  for (int i = 0; i < NV; i += 4) {
-    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(val(i)), __float_as_uint(val(i + 1)), false, false);
-    const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(val(i + 2)), __float_as_uint(val(i + 3)), false, false);
-    const float s01 = __uint_as_float(p[0]) + __uint_as_float(p[1]);
-    const float s23 = __uint_as_float(q[0]) + __uint_as_float(q[1]);
-    const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(s01), __float_as_uint(s23), false, false);
-    const float tot = __uint_as_float(t[0]) + __uint_as_float(t[1]);
-    const int vi = i + row;                     // the value whose total this row holds
-    if (vi < G * EPL) sred[w][(vi / EPL) * D + li * EPL + vi % EPL] = tot;
-    else if (vi < NV && li == 0) sred[w][G * D + vi - G * EPL] = tot;
-  }
-  __syncthreads();
-  float* P = s.part;
-  const size_t head0 = static_cast<size_t>(b) * kv.Hq + g * G;
-#pragma unroll
-  for (int i = 0; i < NO; ++i) {
-    const int oi = tid + 256 * i;
-    const int hh = oi / D, dd = oi - hh * D;
-    const float v = (sred[0][oi] + sred[1][oi]) + (sred[2][oi] + sred[3][oi]);
-    P[((head0 + hh) * s.nsp + sp) * (D + 2) + dd] = v;
-  }
-  if (tid < G) {
-    const float lt = (sred[0][G * D + tid] + sred[1][G * D + tid]) + (sred[2][G * D + tid] + sred[3][G * D + tid]);
-    float* mlp = P + ((head0 + tid) * s.nsp + sp) * (D + 2) + D;
-    mlp[0] = M[tid];
-    mlp[1] = lt;
-  }
+  split_partial<D, G, PAGED, kKeysPerGroup>(kv, static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
+                                            q, spos, smax, sred, a.part, a.n_splits, sp, b, g, a.scale_log2);
 }
 
 // ------------------------------------------------------------------------- //
@@ -251,6 +308,27 @@ static bool launch_attend_typed(const StepArgs& s, int sel_chunks, hipStream_t s
   m.n_splits = s.nsp;
   launch_decode_combine(m, st);
   return true;
+}
+
+// Split partials over index rows (bf16, d = 128, 2 to 8 query heads per kv
+// head) and their merge; a.n_splits must be ceil(a.L / kStepSplitKeys).
+template <int G>
+static void launch_rows_typed(const AttnArgs& a, hipStream_t st) {
+  const dim3 grid(a.n_splits, a.kv.Hkv, a.kv.B);
+  const char* nm = "attn_decode_partial";
+  if (a.kv.block_table) DSA_LAUNCH(nm, (k_decode_rows<128, G, true>), grid, dim3(256), st, a);
+  else                  DSA_LAUNCH(nm, (k_decode_rows<128, G, false>), grid, dim3(256), st, a);
+  launch_decode_combine(a, st);
+}
+
+bool launch_decode_rows(const AttnArgs& a, hipStream_t st) {
+  if (!a.kv.decode || a.kv.D != 128 || !a.idx) return false;
+  switch (a.kv.Hq / a.kv.Hkv) {
+    case 2: launch_rows_typed<2>(a, st); return true;
+    case 4: launch_rows_typed<4>(a, st); return true;
+    case 8: launch_rows_typed<8>(a, st); return true;
+    default: return false;
+  }
 }
 
 bool launch_decode_attend(const StepArgs& s, int sel_chunks, hipStream_t st) {
