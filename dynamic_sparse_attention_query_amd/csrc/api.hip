@@ -199,6 +199,12 @@ dsa_status run_attn(const dsa_shape* s, const void* q, const void* k, const void
       return DSA_OK;
     }
   }
+  // other bf16 decode (the dense path, longer rows): spans of a.kps entries
+  if (s->mode == DSA_DECODE && s->dtype == DSA_BF16 && dsa::launch_decode_span(a, static_cast<hipStream_t>(stream))) {
+    const hipError_t e2 = hipGetLastError();
+    if (e2 != hipSuccess) return fail(DSA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e2));
+    return DSA_OK;
+  }
   hipError_t err = dsa::launch_sparse_attn(a, s->dtype, static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return fail(DSA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(err));
   return DSA_OK;

@@ -913,7 +913,6 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) k_prefill_gqa8(AttnArgs a) {
   constexpr int D = 128;
   constexpr int NH = 4;
-  constexpr int NWV = 8;
   constexpr int KS = D / 16;
   constexpr int DT = D / 32;
   __shared__ __align__(16) uint16_t sk0[64 * D], sk1[64 * D], sk2[64 * D], sk3[64 * D];

@@ -33,6 +33,58 @@
 
 namespace dsa {
 
+// The workgroup's partial (o[D], m, l) per head from each lane's share of
+// o and l (already relative to the workgroup maximum M): summed over the
+// wave's four lane groups by lane swaps, then over the four waves in LDS, and
+// written as split sp's partial.
+template <int D, int G>
+__device__ __forceinline__ void write_partials(const float (&o)[G][D / 16], const float (&lsum)[G], const float (&M)[G],
+                                               float (&sred)[4][G * D + G], float* part, int nsp, int sp,
+                                               const KvLayout& kv, int b, int g) {
+  constexpr int EPL = D / 16;
+  constexpr int NO = (G * D) / 256;           // outputs per thread in the reduction (G * D >= 256)
+  static_assert(G * D % 256 == 0, "whole outputs per thread");
+  const int tid = threadIdx.x, li = tid & 15, lane = tid & 63, w = tid >> 6;
+  // Sum over the wave's four lane groups (16-lane rows), four values at a
+  // time: a row swap of values (a, b) and one of (c, d) leave the pair sums
+  // of a and b, c and d interleaved by row, and a half swap of those leaves
+  // in row r the total of value r, added as (r0 + r1) + (r2 + r3); each row
+  // writes its value. Then over the waves in LDS.
+  constexpr int NV = G * EPL + G;               // per lane: o[hh][x], then lsum[hh]
+  auto val = [&](int i) -> float {
+    return i < G * EPL ? o[i / EPL][i % EPL] : i < NV ? lsum[i - G * EPL] : 0.f;
+  };
+  const int row = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < NV; i += 4) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(val(i)), __float_as_uint(val(i + 1)), false, false);
+    const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(val(i + 2)), __float_as_uint(val(i + 3)), false, false);
+    const float s01 = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    const float s23 = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+    const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(s01), __float_as_uint(s23), false, false);
+    const float tot = __uint_as_float(t[0]) + __uint_as_float(t[1]);
+    const int vi = i + row;                     // the value whose total this row holds
+    if (vi < G * EPL) sred[w][(vi / EPL) * D + li * EPL + vi % EPL] = tot;
+    else if (vi < NV && li == 0) sred[w][G * D + vi - G * EPL] = tot;
+  }
+  __syncthreads();
+  float* P = part;
+  const size_t head0 = static_cast<size_t>(b) * kv.Hq + g * G;
+#pragma unroll
+  for (int i = 0; i < NO; ++i) {
+    const int oi = tid + 256 * i;
+    const int hh = oi / D, dd = oi - hh * D;
+    const float v = (sred[0][oi] + sred[1][oi]) + (sred[2][oi] + sred[3][oi]);
+    P[((head0 + hh) * nsp + sp) * (D + 2) + dd] = v;
+  }
+  if (tid < G) {
+    const float lt = (sred[0][G * D + tid] + sred[1][G * D + tid]) + (sred[2][G * D + tid] + sred[3][G * D + tid]);
+    float* mlp = P + ((head0 + tid) * nsp + sp) * (D + 2) + D;
+    mlp[0] = M[tid];
+    mlp[1] = lt;
+  }
+}
+
 // One split's partial softmax for the G query heads of kv head g of sequence
 // b: the split's row positions are in spos (negative = padding, masked); lane
 // group gi gathers the K and V rows of entries gi + 16u (16-lane 256-byte row
@@ -49,9 +101,7 @@ __device__ __forceinline__ void split_partial(const KvLayout& kv, const uint16_t
                                               int nsp, int sp, int b, int g, float scale_log2) {
   constexpr int EPL = D / 16;
   using Row = RowSlice<uint16_t, EPL>;
-  constexpr int NO = (G * D) / 256;           // outputs per thread in the reduction (G * D >= 256)
-  static_assert(G * D % 256 == 0, "whole outputs per thread");
-  const int tid = threadIdx.x, gi = tid >> 4, li = tid & 15, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, gi = tid >> 4, li = tid & 15;
   // gather the split's K and V rows: lane group gi takes entries gi + 16u
   int pu[kKeysPerGroup];
   Row kr[kKeysPerGroup], vr[kKeysPerGroup];
@@ -118,44 +168,7 @@ __device__ __forceinline__ void split_partial(const KvLayout& kv, const uint16_t
       for (int x = 0; x < EPL; ++x) o[hh][x] = fmaf(pz, vf[x], o[hh][x]);
     }
   }
-  // Sum over the wave's four lane groups (16-lane rows), four values at a
-  // time: a row swap of values (a, b) and one of (c, d) leave the pair sums
-  // of a and b, c and d interleaved by row, and a half swap of those leaves
-  // in row r the total of value r, added as (r0 + r1) + (r2 + r3); each row
-  // writes its value. Then over the waves in LDS.
-  constexpr int NV = G * EPL + G;               // per lane: o[hh][x], then lsum[hh]
-  auto val = [&](int i) -> float {
-    return i < G * EPL ? o[i / EPL][i % EPL] : i < NV ? lsum[i - G * EPL] : 0.f;
-  };
-  const int row = lane >> 4;
-#pragma unroll
-  for (int i = 0; i < NV; i += 4) {
-    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(val(i)), __float_as_uint(val(i + 1)), false, false);
-    const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(val(i + 2)), __float_as_uint(val(i + 3)), false, false);
-    const float s01 = __uint_as_float(p[0]) + __uint_as_float(p[1]);
-    const float s23 = __uint_as_float(q[0]) + __uint_as_float(q[1]);
-    const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(s01), __float_as_uint(s23), false, false);
-    const float tot = __uint_as_float(t[0]) + __uint_as_float(t[1]);
-    const int vi = i + row;                     // the value whose total this row holds
-    if (vi < G * EPL) sred[w][(vi / EPL) * D + li * EPL + vi % EPL] = tot;
-    else if (vi < NV && li == 0) sred[w][G * D + vi - G * EPL] = tot;
-  }
-  __syncthreads();
-  float* P = part;
-  const size_t head0 = static_cast<size_t>(b) * kv.Hq + g * G;
-#pragma unroll
-  for (int i = 0; i < NO; ++i) {
-    const int oi = tid + 256 * i;
-    const int hh = oi / D, dd = oi - hh * D;
-    const float v = (sred[0][oi] + sred[1][oi]) + (sred[2][oi] + sred[3][oi]);
-    P[((head0 + hh) * nsp + sp) * (D + 2) + dd] = v;
-  }
-  if (tid < G) {
-    const float lt = (sred[0][G * D + tid] + sred[1][G * D + tid]) + (sred[2][G * D + tid] + sred[3][G * D + tid]);
-    float* mlp = P + ((head0 + tid) * nsp + sp) * (D + 2) + D;
-    mlp[0] = M[tid];
-    mlp[1] = lt;
-  }
+  write_partials<D, G>(o, lsum, M, sred, part, nsp, sp, kv, b, g);
 }
 
 template <int D, int G, int E, bool PAGED, int kSplitKeys = kStepSplitKeys>
@@ -164,8 +177,6 @@ __global__ void __launch_bounds__(256, 2) k_decode_attend(StepArgs s) {
   using T = uint16_t;
   constexpr int EPL = D / 16;
   using Row = RowSlice<T, EPL>;
-  constexpr int NO = (G * D) / 256;           // outputs per thread in the reduction (G * D >= 256)
-  static_assert(G * D % 256 == 0, "whole outputs per thread");
   __shared__ SelectKeysLds<kTopkWaves> LS;
   __shared__ int sprev[kFusedMaxKept];
   __shared__ int skept[kFusedMaxKept + 64];
@@ -192,7 +203,7 @@ __global__ void __launch_bounds__(256, 2) k_decode_attend(StepArgs s) {
       g = (lin - nk) % kv.Hkv;
     }
   }
-  const int tid = threadIdx.x, gi = tid >> 4, li = tid & 15, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, li = tid & 15;
   const T* Q = static_cast<const T*>(a.q);
   const T* K = static_cast<const T*>(a.k);
   const T* V = static_cast<const T*>(s.v);
@@ -310,6 +321,118 @@ static bool launch_attend_typed(const StepArgs& s, int sel_chunks, hipStream_t s
   return true;
 }
 
+// Split partials over spans of a.kps entries, several chunks of
+// kStepSplitKeys each: the dense decode (entry i is key position i) and index
+// rows longer than one chunk per split. Each lane group keeps an online
+// softmax (running max, sum and output) over its own entries, gi + 16u of
+// every chunk, so the chunks need no barrier; at the end the groups' maxima
+// meet in LDS, each group rescales its sums to the workgroup maximum, and the
+// partial is written as the one-chunk splits write theirs.
+template <int D, int G, bool PAGED, bool ROWS>
+__global__ void __launch_bounds__(256, 2) k_decode_span(AttnArgs a) {
+  constexpr int KPG = kStepSplitKeys / 16;
+  constexpr int EPL = D / 16;
+  using Row = RowSlice<uint16_t, EPL>;
+  __shared__ float smax[16][G];
+  __shared__ float sred[4][G * D + G];
+  const KvLayout& kv = a.kv;
+  const int sp = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, gi = tid >> 4, li = tid & 15;
+  const uint16_t* Q = static_cast<const uint16_t*>(a.q);
+  const uint16_t* K = static_cast<const uint16_t*>(a.k);
+  const uint16_t* V = static_cast<const uint16_t*>(a.v);
+  Row q[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) q[hh].load(Q + (static_cast<size_t>(b) * kv.Hq + g * G + hh) * D + li * EPL);
+  const int tq = seq_len_of(kv, b) - 1;
+  const int n_total = ROWS ? a.L : tq + 1;      // (dense: the keys after the query are not visited)
+  const int k_begin = sp * a.kps;
+  const int k_end = min(n_total, k_begin + a.kps);
+  const int32_t* row = ROWS ? a.idx + static_cast<size_t>(b) * a.L : nullptr;
+  float m[G], l[G], o[G][EPL];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    m[hh] = kNegBig;
+    l[hh] = 0.f;
+#pragma unroll
+    for (int x = 0; x < EPL; ++x) o[hh][x] = 0.f;
+  }
+  for (int base = k_begin; base < k_end; base += kStepSplitKeys) {
+    int pu[KPG];
+    Row kr[KPG], vr[KPG];
+#pragma unroll
+    for (int u = 0; u < KPG; ++u) {
+      const int i = base + gi + 16 * u;
+      int p = -1;
+      if (i < k_end) {
+        p = ROWS ? row[i] : i;
+        if (p < 0 || p > tq) p = -1;
+      }
+      pu[u] = p;
+      const int pp = max(p, 0);                   // padding reads row 0 and is masked below
+      size_t off;
+      if constexpr (PAGED) off = kv_offset(kv, b, g, pp);
+      else off = ((static_cast<size_t>(b) * kv.Hkv + g) * kv.T + pp) * D;
+      kr[u].load(K + off + li * EPL);
+      vr[u].load(V + off + li * EPL);
+    }
+    float sc[KPG][G], mc[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) mc[hh] = m[hh];
+#pragma unroll
+    for (int u = 0; u < KPG; ++u) {
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const float d = group16_sum(kr[u].dot(q[hh])) * a.scale_log2;
+        sc[u][hh] = pu[u] >= 0 ? d : -INFINITY;
+        mc[hh] = fmaxf(mc[hh], sc[u][hh]);
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {              // the group's sums relative to its new maximum
+      const float alpha = __builtin_amdgcn_exp2f(m[hh] - mc[hh]);
+      l[hh] *= alpha;
+#pragma unroll
+      for (int x = 0; x < EPL; ++x) o[hh][x] *= alpha;
+      m[hh] = mc[hh];
+    }
+#pragma unroll
+    for (int u = 0; u < KPG; ++u) {
+      float vf[EPL];
+#pragma unroll
+      for (int x = 0; x < EPL / 2; ++x) {
+        vf[2 * x] = __uint_as_float(vr[u].w[x] << 16);
+        vf[2 * x + 1] = __uint_as_float(vr[u].w[x] & 0xffff0000u);
+      }
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const float pz = sc[u][hh] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[u][hh] - m[hh]);
+        l[hh] += pz;
+#pragma unroll
+        for (int x = 0; x < EPL; ++x) o[hh][x] = fmaf(pz, vf[x], o[hh][x]);
+      }
+    }
+  }
+  if (li == 0) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) smax[gi][hh] = m[hh];
+  }
+  __syncthreads();
+  float M[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    float mm = smax[0][hh];
+#pragma unroll
+    for (int x = 1; x < 16; ++x) mm = fmaxf(mm, smax[x][hh]);
+    M[hh] = mm;
+    const float f = __builtin_amdgcn_exp2f(m[hh] - mm);
+    l[hh] *= f;
+#pragma unroll
+    for (int x = 0; x < EPL; ++x) o[hh][x] *= f;
+  }
+  write_partials<D, G>(o, l, M, sred, a.part, a.n_splits, sp, kv, b, g);
+}
+
 // Split partials over index rows (bf16, d = 128, 2 to 8 query heads per kv
 // head) and their merge; a.n_splits must be ceil(a.L / kStepSplitKeys).
 template <int G>
@@ -327,6 +450,34 @@ bool launch_decode_rows(const AttnArgs& a, hipStream_t st) {
     case 2: launch_rows_typed<2>(a, st); return true;
     case 4: launch_rows_typed<4>(a, st); return true;
     case 8: launch_rows_typed<8>(a, st); return true;
+    default: return false;
+  }
+}
+
+// Split partials over spans of a.kps entries (the dense decode when a.idx is
+// null, else index rows) and their merge; bf16, d = 128, 2-8 query heads per
+// kv head, else false.
+template <int G>
+static void launch_span_typed(const AttnArgs& a, hipStream_t st) {
+  const dim3 grid(a.n_splits, a.kv.Hkv, a.kv.B);
+  const char* nm = a.idx ? "attn_decode_partial" : "dense_decode_partial";
+  const bool paged = a.kv.block_table != nullptr;
+  if (a.idx) {
+    if (paged) DSA_LAUNCH(nm, (k_decode_span<128, G, true, true>), grid, dim3(256), st, a);
+    else       DSA_LAUNCH(nm, (k_decode_span<128, G, false, true>), grid, dim3(256), st, a);
+  } else {
+    if (paged) DSA_LAUNCH(nm, (k_decode_span<128, G, true, false>), grid, dim3(256), st, a);
+    else       DSA_LAUNCH(nm, (k_decode_span<128, G, false, false>), grid, dim3(256), st, a);
+  }
+  launch_decode_combine(a, st);
+}
+
+bool launch_decode_span(const AttnArgs& a, hipStream_t st) {
+  if (!a.kv.decode || a.kv.D != 128) return false;
+  switch (a.kv.Hq / a.kv.Hkv) {
+    case 2: launch_span_typed<2>(a, st); return true;
+    case 4: launch_span_typed<4>(a, st); return true;
+    case 8: launch_span_typed<8>(a, st); return true;
     default: return false;
   }
 }

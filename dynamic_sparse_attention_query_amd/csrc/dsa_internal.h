@@ -368,6 +368,10 @@ bool launch_decode_attend(const StepArgs& s, int sel_chunks, hipStream_t stream)
 // bf16 decode split partials over index rows (d = 128, 2-8 query heads per kv head)
 // and their merge; false for other shapes. a.n_splits = ceil(a.L / kStepSplitKeys).
 bool launch_decode_rows(const AttnArgs& a, hipStream_t stream);
+// bf16 decode split partials over spans of a.kps entries (dense when a.idx is
+// null, else index rows; d = 128, 2-8 query heads per kv head) and their merge;
+// false for other shapes.
+bool launch_decode_span(const AttnArgs& a, hipStream_t stream);
 constexpr int kStepSplitKeys = 128;   // index-row entries per workgroup of the fused tail
 // Offset of the fused tail's split grid: the splits start at the end of the
 // sinks, so the kept entries fill whole splits (with 64 sinks, 4,096 kept

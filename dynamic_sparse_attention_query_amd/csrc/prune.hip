@@ -159,7 +159,6 @@ k_score_decode(PruneArgs a, int stage) {
   const int gi = tid >> 4, li = tid & 15;
   const int cl = gi / kv.Hkv, g = gi - cl * kv.Hkv;
   const int j = j0 + cl;
-  const int l = a.chunk[stage];
   const T* Q = static_cast<const T*>(a.q);
   __shared__ float red[16];
 

@@ -245,6 +245,28 @@ def test_decode_zero_budget_and_full_budget():
             H.assert_close(out.cpu().numpy(), dense.cpu().numpy(), "full budget vs dense")
 
 
+@pytest.mark.parametrize("hq,hkv,d,page", [(16, 8, 128, 0), (32, 8, 128, 64), (64, 8, 128, 0),
+                                           (8, 8, 128, 0), (32, 8, 64, 0)])
+def test_dense_decode_ragged_shapes(hq, hkv, d, page):
+    """Dense decode over a ragged batch whose longest sequence spans several
+    chunks per split (100,000 keys: splits of 256 entries), at 1, 2, 4 and 8
+    query heads per kv head, d = 64 and 128, paged and contiguous: sequences
+    of one key and of fewer keys than a split leave most splits empty."""
+    cfg = gen.Config("decode-dense", "decode", 4, hq, hkv, d, 100000, "bf16", 1,
+                     (64,), (0,), 0, 64, seed=21, n_queries=1, page_size=page)
+    case = gen.make_case(cfg)
+    case.seq_lens[:] = [1, 70, 5000, 100000]
+    for b, L in enumerate(case.seq_lens):
+        case.k[b] = case.k[b].sub((slice(None), slice(0, int(L))))
+        case.v[b] = case.v[b].sub((slice(None), slice(0, int(L))))
+    dev = to_device(case)
+    q = dev.q[0].contiguous()
+    out = api.dense_attn(q, dev.k, dev.v, seq_lens=dev.seq_lens, block_table=dev.block_table,
+                         t=dev.t).cpu().numpy()
+    for b in range(4):
+        H.assert_close(out[b], H.oracle_dense(case, b, 0)[:, 0], f"dense decode seq {b}")
+
+
 @pytest.fixture(scope="module")
 def c3():
     H.say("generating c3 (1M-token decode)")
