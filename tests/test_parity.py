@@ -267,6 +267,29 @@ def test_dense_decode_ragged_shapes(hq, hkv, d, page):
         H.assert_close(out[b], H.oracle_dense(case, b, 0)[:, 0], f"dense decode seq {b}")
 
 
+@pytest.mark.parametrize("page", [0, 64])
+def test_decode_wide_rows(page):
+    """Two-call decode over index rows wider than 65,536 entries (a one-stage
+    budget of 80,000 keys in 100,000): the attention takes spans of several
+    128-entry chunks per split; contiguous and paged, one sequence shorter
+    than the budget (everything kept)."""
+    cfg = gen.Config("decode-wide", "decode", 2, 32, 8, 128, 100000, "bf16", 1,
+                     (64,), (80000,), 64, 1024, seed=22, n_queries=1, page_size=page)
+    case = gen.make_case(cfg)
+    case.seq_lens[:] = [100000, 60000]
+    for b, L in enumerate(case.seq_lens):
+        case.k[b] = case.k[b].sub((slice(None), slice(0, int(L))))
+        case.v[b] = case.v[b].sub((slice(None), slice(0, int(L))))
+    dev = to_device(case)
+    assert _lib_width(case) > 65536
+    check_decode(case, dev, range(2))
+
+
+def _lib_width(case):
+    from dynamic_sparse_attention_query_amd import _lib
+    return _lib.index_width(params_of(case.cfg))
+
+
 @pytest.fixture(scope="module")
 def c3():
     H.say("generating c3 (1M-token decode)")
