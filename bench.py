@@ -322,7 +322,41 @@ def decode_bench(args, res):
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": tr,
                 "avg_us": round(kern_us[dom], 2), "algorithmic_bytes_per_launch": int(per_launch_bytes[dom])}
-    res["decode"] = dict(us_per_step=us_step, event_us_per_step=ev_us, wall_ms=wall_ms,
+    # per-step distribution: each of 64 steps (fresh query, KV replica cycled)
+    # replayed alone between HIP events, cache-cold (a 1 GiB read before it,
+    # outside the timed region) and without the flush
+    n_ps = 64
+    one = []
+    for i in range(min(n_ps, NQ * args.replicas)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            launch(i)
+        one.append(g)
+    for g in one:
+        g.replay()
+    torch.cuda.synchronize()
+    junk = torch.zeros((1 << 30) // 4, dtype=torch.float32, device="cuda")
+    flush = torch.zeros((), dtype=torch.float32, device="cuda")
+    torch.sum(junk, dim=0, out=flush)
+    per_step = {}
+    for mode in ("cold", "warm"):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ps)]
+        for i in range(n_ps):
+            if mode == "cold":
+                torch.sum(junk, dim=0, out=flush)      # read: the caches end clean
+            evs[i][0].record()
+            one[i % len(one)].replay()
+            evs[i][1].record()
+            if mode == "warm":
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        t = np.array([a_.elapsed_time(b_) * 1e3 for a_, b_ in evs])
+        per_step[mode] = (float(np.median(t)), float(np.percentile(t, 90)), float(t.mean()))
+    del one, junk, flush
+    log(f"decode 1M per step: cache-cold median {per_step['cold'][0]:.1f} us, p90 {per_step['cold'][1]:.1f}; "
+        f"without the flush median {per_step['warm'][0]:.1f}, p90 {per_step['warm'][1]:.1f}")
+
+    res["decode"] = dict(us_per_step=us_step, event_us_per_step=ev_us, wall_ms=wall_ms, per_step=per_step,
                          two_call_us_per_step=two_us, graph_steps=GS,
                          bytes_per_step=bytes_avg, stage_rows=(stage_bytes[used].mean(0) / row_bytes).tolist(),
                          kernels_us={k: round(v, 2) for k, v in kern_us.items()}, roofline=roof,
@@ -735,7 +769,7 @@ def vertical_slash_bench(args, res, reps=3):
 def other_decode(args, name, reps=24, n_queries=8, flush_bytes=1 << 30):
     """Graph-replayed decode step (dsa_prune_attend) of workload `name`, a
     fresh query each step, timed two ways: back to back (one KV copy, so later
-    steps may find rows in the caches) and cache-cold (a 1 GiB write between
+    steps may find rows in the caches) and cache-cold (a 1 GiB read between
     steps, outside the timed region, evicts the L2s and the Infinity Cache;
     each step is timed alone with HIP events). HBM GB/s uses the algorithmic
     bytes of each step (SelectRep rows counted by the kernels + K/V rows of
@@ -780,11 +814,16 @@ def other_decode(args, name, reps=24, n_queries=8, flush_bytes=1 << 30):
     e1.record()
     torch.cuda.synchronize()
     us_b2b = e0.elapsed_time(e1) * 1e3 / reps
-    # cache-cold: flush, then time one step
-    junk = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda")
+    # cache-cold: flush, then time one step. The flush reads a buffer larger
+    # than the Infinity Cache, so the caches end holding clean lines (a write
+    # would leave them dirty, and the timed step would pay for writing them
+    # back).
+    junk = torch.zeros(flush_bytes // 4, dtype=torch.float32, device="cuda")
+    flush = torch.zeros((), dtype=torch.float32, device="cuda")
+    torch.sum(junk, dim=0, out=flush)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for i in range(reps):
-        junk.fill_(float(i))
+        torch.sum(junk, dim=0, out=flush)
         evs[i][0].record()
         graphs[i % n_queries].replay()
         evs[i][1].record()
@@ -808,7 +847,7 @@ def other_decode(args, name, reps=24, n_queries=8, flush_bytes=1 << 30):
     gb_b2b, pct_b2b = rate(us_b2b)
     res = {"us_per_step": round(us_cold, 2), "batch": cfg.batch, "us_per_token": round(us_cold / cfg.batch, 2),
            "algorithmic_bytes_per_step": int(nb), "gbps": gb_cold, "pct_peak": pct_cold,
-           "timing": f"cache-cold: a {flush_bytes >> 30} GiB write between steps (outside the timed region), "
+           "timing": f"cache-cold: a {flush_bytes >> 30} GiB read between steps (outside the timed region), "
                      f"each step timed alone; {n_queries} distinct queries",
            "back_to_back": {"us_per_step": round(us_b2b, 2), "gbps": gb_b2b, "pct_peak": pct_b2b,
                             "timing": "back-to-back graph replays, distinct queries, one KV copy"},
@@ -816,7 +855,7 @@ def other_decode(args, name, reps=24, n_queries=8, flush_bytes=1 << 30):
            "tokens_in_context": int(dev.seq_lens.sum().item())}
     log(f"{name}: {us_cold:.1f} us/step cache-cold ({gb_cold} GB/s), {us_iso:.1f} isolated without flush, "
         f"{us_b2b:.1f} back to back")
-    del dev, idx, out, graphs, junk
+    del dev, idx, out, graphs, junk, flush
     torch.cuda.empty_cache()
     return res
 
@@ -1053,6 +1092,14 @@ def main():
         "timing_mode": dec["mode"],
         "kernels_us": dec["kernels_us"],
         "roofline": dec["roofline"],
+        "per_step_us": {"cache_cold": {"median": round(dec["per_step"]["cold"][0], 2),
+                                       "p90": round(dec["per_step"]["cold"][1], 2),
+                                       "mean": round(dec["per_step"]["cold"][2], 2)},
+                        "isolated_warm": {"median": round(dec["per_step"]["warm"][0], 2),
+                                          "p90": round(dec["per_step"]["warm"][1], 2),
+                                          "mean": round(dec["per_step"]["warm"][2], 2)},
+                        "timing": "64 steps (fresh query, KV replica cycled), each replayed alone between HIP "
+                                  "events; cache-cold: a 1 GiB read before each step, outside the timed region"},
     }
     if "dense" in res:
         line["dense_decode_1m"] = {"us": round(res["dense"]["us"], 1), "gbps": round(res["dense"]["gbps"], 1),
