@@ -208,9 +208,18 @@ __global__ void __launch_bounds__(256, 2) k_decode_attend(StepArgs s) {
   const T* K = static_cast<const T*>(a.k);
   const T* V = static_cast<const T*>(s.v);
 
+  // The last stage's scores and the previous stage's kept starts are loaded
+  // by every workgroup as it starts, together with the row length and kept
+  // count that decide whether the workgroup selects at all: one memory round
+  // trip instead of two (the loads of a workgroup that does not select are
+  // not used; all are within the lists).
+  const int ls = a.n_stages - 1;
+  uint32_t key[E];
+  load_keys<E>(a, ls, r, threadIdx.x * E, key);
+  if (ls > 0) load_kept_starts(a, ls - 1, r, sprev);
+
   // row geometry of the last stage (uniform over the row's workgroups)
   const int e = seq_len_of(kv, b);
-  const int ls = a.n_stages - 1;
   const int lg = a.lchunk[ls];
   const int shp = ls > 0 ? a.lchunk[ls - 1] - lg : 0;
   const int nc_before = ls > 0 ? a.cnt[r * kMaxStages + ls - 1] : 0;
@@ -226,9 +235,6 @@ __global__ void __launch_bounds__(256, 2) k_decode_attend(StepArgs s) {
   const int i0 = sp * kSplitKeys - s.sh0;          // (split 0 may start before entry 0)
 
   if (i0 < win0 && i0 + kSplitKeys > geo.sink_hi) {
-    uint32_t key[E];
-    load_keys<E>(a, ls, r, threadIdx.x * E, key);
-    if (ls > 0) load_kept_starts(a, ls - 1, r, sprev);
     select_keys<E>(key, nc, kc, LS, skept);
     __syncthreads();                            // skept holds the kept chunk indices
   }

@@ -391,15 +391,14 @@ __device__ __forceinline__ int select_keys(const uint32_t (&key)[E], int nc, int
   for (int i = 0; i < NW; ++i) before += i < w ? L.wcnt[i] : 0u;
   int erank = static_cast<int>(before & 0xffffu);  // ties at the threshold before this thread's
   int slot = static_cast<int>(before >> 16) + min(erank, need_eq);
-#pragma unroll
-  for (int x = 0; x < E; ++x) {
-    bool keep = (ms >> x) & 1u;
-    if ((me >> x) & 1u) {                          // (strict and equal only when need_eq is 0)
-      keep = keep || erank < need_eq;
-      ++erank;
-    }
-    if (keep) kept[slot++] = j0 + x;
-  }
+  // this thread's kept keys: the strict ones and, in index order, its ties
+  // while fewer than need_eq ties come before them; then one store per kept
+  // key (a lane loops over its own kept keys only: few of them when K is a
+  // small share of the row)
+  uint32_t km = ms;
+  if (need_eq > 0)
+    for (uint32_t m = me; m != 0u && erank < need_eq; m &= m - 1u, ++erank) km |= m & (0u - m);
+  for (; km != 0u; km &= km - 1u) kept[slot++] = j0 + __builtin_ctz(km);
   return kc;
 }
 
