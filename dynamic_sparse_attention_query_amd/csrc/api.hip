@@ -75,7 +75,6 @@ dsa_status check_params(const dsa_shape* s, const dsa_params* p) {
   if (s) {
     if (s->mode == DSA_DECODE) {
       if (p->block_q != 1) return fail(DSA_ERR_INVALID_ARG, "decode requires block_q == 1");
-      if (16 % s->hkv != 0) return fail(DSA_ERR_UNSUPPORTED, "decode pruning needs hkv to divide 16");
     } else {
       if (p->block_q < 4 || p->block_q > 64 || !is_pow2(p->block_q))
         return fail(DSA_ERR_UNSUPPORTED, "prefill block_q = %d; supported: 4, 8, 16, 32, 64", p->block_q);
@@ -92,8 +91,23 @@ long long index_width_ll(const dsa_params* p) {
 
 struct PruneLayout {
   long long R, maxK, maxNC, n1max;
+  int hpw, nsl;                       // decode scoring: kv heads per workgroup, score slices
   size_t off_cnt, off_starts, off_scores, bytes;
 };
+
+// Decode scoring holds the kv heads of a chunk in one workgroup of 16 lane
+// groups when they fit: hpw = the largest divisor of hkv up to 16, and the
+// hkv / hpw slices of heads write score lists of their own (maxed by the
+// readers). Prefill scoring keeps every head of a row in one workgroup.
+void head_slices(const dsa_shape* s, int& hpw, int& nsl) {
+  hpw = s->hkv;
+  nsl = 1;
+  if (s->mode != DSA_DECODE) return;
+  hpw = 1;
+  for (int x = 1; x <= 16; ++x)
+    if (s->hkv % x == 0) hpw = x;
+  nsl = s->hkv / hpw;
+}
 
 PruneLayout prune_layout(const dsa_shape* s, const dsa_params* p) {
   PruneLayout L{};
@@ -107,10 +121,12 @@ PruneLayout prune_layout(const dsa_shape* s, const dsa_params* p) {
   for (int i = 1; i < p->n_stages; ++i) maxNC = std::max<long long>(maxNC, p->keep[i - 1] / p->chunk[i]);
   L.maxK = maxK;
   L.maxNC = (maxNC + 63) / 64 * 64;   // rows of whole 16-byte key groups
+  head_slices(s, L.hpw, L.nsl);
   L.off_cnt = 0;
   L.off_starts = align256(L.off_cnt + static_cast<size_t>(L.R) * dsa::kMaxStages * 4);
   L.off_scores = align256(L.off_starts + 2 * static_cast<size_t>(L.R) * maxK * 4);
-  L.bytes = align256(L.off_scores + 2 * static_cast<size_t>(L.R) * L.maxNC * 4);   // two score lists
+  // two sets of score lists (stage parity), one list per head slice
+  L.bytes = align256(L.off_scores + 2 * static_cast<size_t>(L.nsl) * L.R * L.maxNC * 4);
   return L;
 }
 
@@ -306,6 +322,8 @@ dsa::PruneArgs prune_args(const dsa_shape* s, const void* q, const void* k, cons
   a.maxK = static_cast<int>(lay.maxK);
   a.maxNC = static_cast<int>(lay.maxNC);
   a.n1max = static_cast<int>(lay.n1max);
+  a.hpw = lay.hpw;
+  a.nsl = lay.nsl;
   for (int i = 0; i < DSA_MAX_STAGES; ++i) a.slot[i] = i & 1;
   if (ws) {                                       // no workspace: the call reads none of it
     char* w = static_cast<char*>(ws);

@@ -47,8 +47,15 @@ struct PruneArgs {
   int32_t* mid_end;          // mask caching: [R, kMaxStages] end of the stage-1 middle each
                              // stage's record descends from; nullptr otherwise
   int32_t* row_status;       // mask caching: [R] 1 if the last row did not fit in L; or nullptr
-  uint32_t* scores;          // [2, R, maxNC] orderable chunk-score keys, by stage parity
+  uint32_t* scores;          // [2, nsl, R, maxNC] orderable chunk-score keys, by stage parity
   unsigned long long* visited;  // [n_stages] or nullptr
+  // Decode scoring: a workgroup holds the kv heads [s * hpw, (s + 1) * hpw) of
+  // 16 / hpw chunks, hpw the largest divisor of Hkv up to 16; with more kv heads
+  // than that (nsl = Hkv / hpw > 1) each slice s of workgroups writes its own
+  // score list (the chunk maxima over its heads) and the readers take the max
+  // over the nsl lists. Prefill and the generic paths: hpw = Hkv, nsl = 1.
+  int hpw;
+  int nsl;
 };
 
 struct AttnArgs {

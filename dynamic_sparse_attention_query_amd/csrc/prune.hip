@@ -153,12 +153,11 @@ k_score_decode(PruneArgs a, int stage) {
   using Row = RowSlice<T, EPL>;
   const KvLayout& kv = a.kv;
   const int r = blockIdx.y, b = r;              // one row per sequence
-  const int cpw = 16 / kv.Hkv;                  // chunks per workgroup
-  const int j0 = blockIdx.x * cpw;
   const int tid = threadIdx.x;
   const int gi = tid >> 4, li = tid & 15;
-  const int cl = gi / kv.Hkv, g = gi - cl * kv.Hkv;
-  const int j = j0 + cl;
+  const DecodeLane dl = decode_lane(a, blockIdx.x, gi);
+  const int cpw = dl.cpw, j0 = dl.j0, g = dl.g;  // chunks per workgroup, first chunk, kv head
+  const int j = j0 + dl.cl;
   const T* Q = static_cast<const T*>(a.q);
   __shared__ float red[16];
 
@@ -184,7 +183,7 @@ k_score_decode(PruneArgs a, int stage) {
   const int nc = stage == 0 ? geo.n1 : nc_prev << (a.lchunk[stage - 1] - a.lchunk[stage]);
   if (nc <= (a.keep[stage] >> a.lchunk[stage])) return;   // stage keeps everything for this row
   if (j0 >= nc) return;
-  const bool active = j < nc;
+  const bool active = dl.used && j < nc;
 
   float best = -INFINITY;
   if (active) best = score_group<T, D, G, SPEC, PAGED>(a, stage, b, g, li, st, q);
@@ -193,9 +192,9 @@ k_score_decode(PruneArgs a, int stage) {
   if (tid < cpw) {
     const int jj = j0 + tid;
     if (jj < nc) {
-      float m = red[tid * kv.Hkv];
-      for (int x = 1; x < kv.Hkv; ++x) m = fmaxf(m, red[tid * kv.Hkv + x]);
-      stage_scores(a, stage, r)[jj] = score_key(m);
+      float m = red[tid * a.hpw];
+      for (int x = 1; x < a.hpw; ++x) m = fmaxf(m, red[tid * a.hpw + x]);
+      stage_scores(a, stage, r, dl.sl)[jj] = score_key(m);
     }
   }
 }
@@ -218,11 +217,10 @@ __global__ void __launch_bounds__(256, 2) k_topk_score_decode(PruneArgs a, int s
   const KvLayout& kv = a.kv;
   const int ps = stage - 1;                     // the stage selected here
   const int r = blockIdx.y, b = r;              // one row per sequence
-  const int cpw = 16 / kv.Hkv;                  // chunks per workgroup
-  const int j0 = blockIdx.x * cpw;
   const int tid = threadIdx.x;
   const int gi = tid >> 4, li = tid & 15;
-  const int cl = gi / kv.Hkv, g = gi - cl * kv.Hkv;
+  const DecodeLane dl = decode_lane(a, blockIdx.x, gi);
+  const int cpw = dl.cpw, j0 = dl.j0, g = dl.g;  // chunks per workgroup, first chunk, kv head
   const T* Q = static_cast<const T*>(a.q);
 
   // independent loads first: sequence length, the count before stage ps,
@@ -254,8 +252,8 @@ __global__ void __launch_bounds__(256, 2) k_topk_score_decode(PruneArgs a, int s
   const int nc = n_sel << sh;
   if (nc <= (a.keep[stage] >> a.lchunk[stage])) return;   // stage keeps everything for this row
   if (j0 >= nc) return;
-  const int j = j0 + cl;
-  const bool active = j < nc;
+  const int j = j0 + dl.cl;
+  const bool active = dl.used && j < nc;
   const int st = kept_start(a, ps, skept[min(j >> sh, n_sel - 1)], sprev) +
                  ((j & ((1 << sh) - 1)) << a.lchunk[stage]);
   float best = -INFINITY;
@@ -265,9 +263,9 @@ __global__ void __launch_bounds__(256, 2) k_topk_score_decode(PruneArgs a, int s
   if (tid < cpw) {
     const int jj = j0 + tid;
     if (jj < nc) {
-      float m = red[tid * kv.Hkv];
-      for (int x = 1; x < kv.Hkv; ++x) m = fmaxf(m, red[tid * kv.Hkv + x]);
-      stage_scores(a, stage, r)[jj] = score_key(m);
+      float m = red[tid * a.hpw];
+      for (int x = 1; x < a.hpw; ++x) m = fmaxf(m, red[tid * a.hpw + x]);
+      stage_scores(a, stage, r, dl.sl)[jj] = score_key(m);
     }
   }
 }
@@ -370,9 +368,9 @@ constexpr long long kFuseMaxWorkgroups = 2048;   // largest fused top-K + scorin
 
 template <typename T, int D, int G>
 static void launch_decode_score(const PruneArgs& a, int stage, int max_chunks, hipStream_t st) {
-  const int cpw = 16 / a.kv.Hkv;
+  const int cpw = 16 / a.hpw;
   if (max_chunks <= 0) return;
-  dim3 grid((max_chunks + cpw - 1) / cpw, a.R);
+  dim3 grid((max_chunks + cpw - 1) / cpw * a.nsl, a.R);
   const char* nm = kScoreNames[stage];
   const int spec = spec_of(a.chunk[stage]);
   if (a.kv.block_table) {
@@ -408,9 +406,9 @@ static bool launch_decode_fused(const PruneArgs& a, int stage, int max_chunks, i
   if constexpr (sizeof(T) != 2) {
     return false;
   } else {
-    const int cpw = 16 / a.kv.Hkv;
+    const int cpw = 16 / a.hpw;
     // at least one workgroup: workgroup 0 writes the selected stage's starts
-    const dim3 grid(std::max(1, (max_chunks + cpw - 1) / cpw), a.R);
+    const dim3 grid(std::max(1, (max_chunks + cpw - 1) / cpw) * a.nsl, a.R);
     // every workgroup repeats the row's selection: worth it only while that
     // redundant work is small next to a kernel boundary (one sequence); a
     // batch takes the one-workgroup-per-row selection kernel instead

@@ -16,10 +16,12 @@ __device__ __forceinline__ int stage_input_chunks(const PruneArgs& a, int stage,
   return a.cnt[r * kMaxStages + stage - 1] << (a.lchunk[stage - 1] - a.lchunk[stage]);
 }
 
-// Chunk-score list of row r for `stage`. Two lists alternate by stage parity,
-// so one kernel can read a stage's scores while writing the next stage's.
-__device__ __forceinline__ uint32_t* stage_scores(const PruneArgs& a, int stage, int r) {
-  return a.scores + (static_cast<size_t>(stage & 1) * a.R + r) * a.maxNC;
+// Chunk-score list of row r for `stage`, written by the workgroups of head
+// slice sl (decode with more than 16 kv heads; else the only slice, 0). Two
+// sets of lists alternate by stage parity, so one kernel can read a stage's
+// scores while writing the next stage's.
+__device__ __forceinline__ uint32_t* stage_scores(const PruneArgs& a, int stage, int r, int sl = 0) {
+  return a.scores + ((static_cast<size_t>(stage & 1) * a.nsl + sl) * a.R + r) * a.maxNC;
 }
 
 // Kept chunk starts of `stage` for row r (ascending, cnt[r][stage] of them).
@@ -59,6 +61,9 @@ constexpr int kMaxKeptChunks = 8192;    // keep / chunk of any stage (validated 
 
 // This thread's keys: chunks j0 .. j0+E-1 of row r's score list of `stage` (read within
 // the row for every j0 of the launch; the selection masks j >= nc).
+// With several head slices (a.nsl > 1) a chunk's key is the largest of its
+// slices' keys: the keys are order-preserving, so that is the key of the max
+// over all heads.
 template <int E>
 __device__ __forceinline__ void load_keys(const PruneArgs& a, int stage, int r, int j0, uint32_t (&key)[E]) {
   static_assert(E % 4 == 0, "keys are loaded four at a time");
@@ -69,6 +74,36 @@ __device__ __forceinline__ void load_keys(const PruneArgs& a, int stage, int r, 
     const uint4 u = sc4[min((j0 >> 2) + v, nv - 1)];
     key[4 * v + 0] = u.x; key[4 * v + 1] = u.y; key[4 * v + 2] = u.z; key[4 * v + 3] = u.w;
   }
+  for (int sl = 1; sl < a.nsl; ++sl) {
+    const uint4* s4 = reinterpret_cast<const uint4*>(stage_scores(a, stage, r, sl));
+#pragma unroll
+    for (int v = 0; v < E / 4; ++v) {
+      const uint4 u = s4[min((j0 >> 2) + v, nv - 1)];
+      key[4 * v + 0] = max(key[4 * v + 0], u.x);
+      key[4 * v + 1] = max(key[4 * v + 1], u.y);
+      key[4 * v + 2] = max(key[4 * v + 2], u.z);
+      key[4 * v + 3] = max(key[4 * v + 3], u.w);
+    }
+  }
+}
+
+// Lane group gi of a decode scoring workgroup of the launch's block bx: its
+// chunk (j, or past the workgroup's share when the 16 lane groups are not a
+// multiple of the heads per workgroup), kv head g and head slice sl.
+struct DecodeLane {
+  int sl, j0, cpw, cl, g;
+  bool used;
+};
+__device__ __forceinline__ DecodeLane decode_lane(const PruneArgs& a, int bx, int gi) {
+  DecodeLane d;
+  d.cpw = 16 / a.hpw;
+  d.sl = bx % a.nsl;
+  d.j0 = (bx / a.nsl) * d.cpw;
+  d.cl = gi / a.hpw;
+  d.used = d.cl < d.cpw;
+  d.cl = min(d.cl, d.cpw - 1);
+  d.g = d.sl * a.hpw + (gi - (gi / a.hpw) * a.hpw);
+  return d;
 }
 
 // First key position of kept chunk j of stage ps, given the kept starts of

@@ -231,12 +231,11 @@ k_score_decode_rt(PruneArgs a, int stage, const uint16_t* ql_all, const uint16_t
   using Row = RowSlice<T, EPL>;
   const KvLayout& kv = a.kv;
   const int r = blockIdx.y, b = r;              // one row per sequence
-  const int cpw = 16 / kv.Hkv;                  // chunks per workgroup
-  const int j0 = blockIdx.x * cpw;
   const int tid = threadIdx.x;
   const int gi = tid >> 4, li = tid & 15;
-  const int cl = gi / kv.Hkv, g = gi - cl * kv.Hkv;
-  const int j = j0 + cl;
+  const DecodeLane dl = decode_lane(a, blockIdx.x, gi);
+  const int cpw = dl.cpw, j0 = dl.j0, g = dl.g;  // chunks per workgroup, first chunk, kv head
+  const int j = j0 + dl.cl;
   __shared__ float red[16];
 
   const int e = seq_len_of(kv, r);
@@ -261,7 +260,7 @@ k_score_decode_rt(PruneArgs a, int stage, const uint16_t* ql_all, const uint16_t
   const int nc = stage == 0 ? geo.n1 : nc_prev << (a.lchunk[stage - 1] - a.lchunk[stage]);
   if (nc <= (a.keep[stage] >> a.lchunk[stage])) return;   // stage keeps everything for this row
   if (j0 >= nc) return;
-  const bool active = j < nc;
+  const bool active = dl.used && j < nc;
 
   float best = -INFINITY;
   if (active) best = score_group_rt<T, D, G, SPEC, PAGED>(a, stage, b, g, li, st, ql, qr);
@@ -270,9 +269,9 @@ k_score_decode_rt(PruneArgs a, int stage, const uint16_t* ql_all, const uint16_t
   if (tid < cpw) {
     const int jj = j0 + tid;
     if (jj < nc) {
-      float m = red[tid * kv.Hkv];
-      for (int x = 1; x < kv.Hkv; ++x) m = fmaxf(m, red[tid * kv.Hkv + x]);
-      stage_scores(a, stage, r)[jj] = score_key(m);
+      float m = red[tid * a.hpw];
+      for (int x = 1; x < a.hpw; ++x) m = fmaxf(m, red[tid * a.hpw + x]);
+      stage_scores(a, stage, r, dl.sl)[jj] = score_key(m);
     }
   }
 }
@@ -555,12 +554,11 @@ k_score_decode_ci(PruneArgs a, int stage, const uint16_t* q_all, double base) {
   __syncthreads();
   const KvLayout& kv = a.kv;
   const int r = blockIdx.y, b = r;
-  const int cpw = 16 / kv.Hkv;
-  const int j0 = blockIdx.x * cpw;
   const int tid = threadIdx.x;
   const int gi = tid >> 4, li = tid & 15;
-  const int cl = gi / kv.Hkv, g = gi - cl * kv.Hkv;
-  const int j = j0 + cl;
+  const DecodeLane dl = decode_lane(a, blockIdx.x, gi);
+  const int cpw = dl.cpw, j0 = dl.j0, g = dl.g;  // chunks per workgroup, first chunk, kv head
+  const int j = j0 + dl.cl;
   __shared__ float red[16];
 
   const int e = seq_len_of(kv, r);
@@ -582,7 +580,7 @@ k_score_decode_ci(PruneArgs a, int stage, const uint16_t* q_all, double base) {
   const int nc = stage == 0 ? geo.n1 : nc_prev << (a.lchunk[stage - 1] - a.lchunk[stage]);
   if (nc <= (a.keep[stage] >> a.lchunk[stage])) return;   // stage keeps everything for this row
   if (j0 >= nc) return;
-  const bool active = j < nc;
+  const bool active = dl.used && j < nc;
 
   float best = -INFINITY;
   if (active) {
@@ -594,9 +592,9 @@ k_score_decode_ci(PruneArgs a, int stage, const uint16_t* q_all, double base) {
   if (tid < cpw) {
     const int jj = j0 + tid;
     if (jj < nc) {
-      float m = red[tid * kv.Hkv];
-      for (int x = 1; x < kv.Hkv; ++x) m = fmaxf(m, red[tid * kv.Hkv + x]);
-      stage_scores(a, stage, r)[jj] = score_key(m);
+      float m = red[tid * a.hpw];
+      for (int x = 1; x < a.hpw; ++x) m = fmaxf(m, red[tid * a.hpw + x]);
+      stage_scores(a, stage, r, dl.sl)[jj] = score_key(m);
     }
   }
 }
@@ -624,11 +622,10 @@ k_topk_score_decode_rope(PruneArgs a, int stage, const uint16_t* qa, const uint1
   const KvLayout& kv = a.kv;
   const int ps = stage - 1;                     // the stage selected here
   const int r = blockIdx.y, b = r;              // one row per sequence
-  const int cpw = 16 / kv.Hkv;                  // chunks per workgroup
-  const int j0 = blockIdx.x * cpw;
   const int tid = threadIdx.x;
   const int gi = tid >> 4, li = tid & 15;
-  const int cl = gi / kv.Hkv, g = gi - cl * kv.Hkv;
+  const DecodeLane dl = decode_lane(a, blockIdx.x, gi);
+  const int cpw = dl.cpw, j0 = dl.j0, g = dl.g;  // chunks per workgroup, first chunk, kv head
 
   const int e = seq_len_of(kv, r);
   const int nc_before = ps > 0 ? a.cnt[r * kMaxStages + ps - 1] : 0;
@@ -667,8 +664,8 @@ k_topk_score_decode_rope(PruneArgs a, int stage, const uint16_t* qa, const uint1
   const int nc = n_sel << sh;
   if (nc <= (a.keep[stage] >> a.lchunk[stage])) return;   // stage keeps everything for this row
   if (j0 >= nc) return;
-  const int j = j0 + cl;
-  const bool active = j < nc;
+  const int j = j0 + dl.cl;
+  const bool active = dl.used && j < nc;
   const int st = ssel[min(j >> sh, n_sel - 1)] + ((j & ((1 << sh) - 1)) << a.lchunk[stage]);
   float best = -INFINITY;
   if (active) {
@@ -684,9 +681,9 @@ k_topk_score_decode_rope(PruneArgs a, int stage, const uint16_t* qa, const uint1
   if (tid < cpw) {
     const int jj = j0 + tid;
     if (jj < nc) {
-      float m = red[tid * kv.Hkv];
-      for (int x = 1; x < kv.Hkv; ++x) m = fmaxf(m, red[tid * kv.Hkv + x]);
-      stage_scores(a, stage, r)[jj] = score_key(m);
+      float m = red[tid * a.hpw];
+      for (int x = 1; x < a.hpw; ++x) m = fmaxf(m, red[tid * a.hpw + x]);
+      stage_scores(a, stage, r, dl.sl)[jj] = score_key(m);
     }
   }
 }
@@ -707,8 +704,8 @@ static int rope_spec(int l) { return l >= 8 && l <= 64 ? 8 : l > 64 ? 4 : l >= 4
 template <typename T, int D, int G, bool PAGED>
 static void launch_decode_rt(const PruneArgs& a, int stage, int max_chunks, const uint16_t* ql,
                              const uint16_t* qr, hipStream_t st) {
-  const int cpw = 16 / a.kv.Hkv;
-  const dim3 grid((max_chunks + cpw - 1) / cpw, a.R);
+  const int cpw = 16 / a.hpw;
+  const dim3 grid((max_chunks + cpw - 1) / cpw * a.nsl, a.R);
   const char* nm = kRopeNames[stage];
   switch (rope_spec(a.chunk[stage])) {
     case 8:  DSA_LAUNCH(nm, (k_score_decode_rt<T, D, G, 8, PAGED>), grid, dim3(256), st, a, stage, ql, qr); break;
@@ -727,8 +724,8 @@ static void launch_decode_rt_g(const PruneArgs& a, int stage, int max_chunks, co
 template <typename T, int D, int G, bool PAGED>
 static void launch_decode_ci(const PruneArgs& a, int stage, int max_chunks, const uint16_t* q, double base,
                              hipStream_t st) {
-  const int cpw = 16 / a.kv.Hkv;
-  const dim3 grid((max_chunks + cpw - 1) / cpw, a.R);
+  const int cpw = 16 / a.hpw;
+  const dim3 grid((max_chunks + cpw - 1) / cpw * a.nsl, a.R);
   const char* nm = kRopeNames[stage];
   switch (rope_spec(a.chunk[stage])) {
     case 8:  DSA_LAUNCH(nm, (k_score_decode_ci<T, D, G, 8, PAGED>), grid, dim3(256), st, a, stage, q, base); break;
@@ -755,8 +752,8 @@ static bool launch_rope_fused(const PruneArgs& a, int style, int stage, int max_
   if constexpr (sizeof(T) != 2) {
     return false;
   } else {
-    const int cpw = 16 / a.kv.Hkv;
-    const dim3 grid(std::max(1, (max_chunks + cpw - 1) / cpw), a.R);
+    const int cpw = 16 / a.hpw;
+    const dim3 grid(std::max(1, (max_chunks + cpw - 1) / cpw) * a.nsl, a.R);
     if (static_cast<long long>(grid.x) * grid.y > kRopeFuseMaxWorkgroups || a.kv.block_table) return false;
     if (sel_chunks > kTopkThreads * 16) return false;
     const bool e4 = sel_chunks <= kTopkThreads * 4;

@@ -111,7 +111,7 @@ typedef struct {
 
 /* Problem shape.
  *   mode, dtype   dsa_mode / dsa_dtype values
- *   batch, hq, hkv, d   B >= 1; hq % hkv == 0, hq / hkv <= 8; d in {64, 128}
+ *   batch, hq, hkv, d   B >= 1; hq % hkv == 0, hq / hkv in {1, 2, 4, 8}; d in {64, 128}
  *   t             PREFILL: tokens per sequence. DECODE: the largest context
  *                 length any sequence may have, and the token stride of
  *                 contiguous k / v

@@ -53,6 +53,15 @@ def test_workspace_sizes():
     assert _lib.workspace_bytes(d, None) > 0
 
 
+def test_decode_any_kv_head_count_is_accepted():
+    # decode scoring workgroups hold up to 16 kv heads of a chunk; more heads
+    # (or a count that does not divide 16) split into slices with a score
+    # list each
+    for hq, hkv in [(32, 8), (32, 16), (32, 32), (64, 64), (24, 12), (6, 3)]:
+        d = Shape(DSA_DECODE, DSA_BF16, 1, hq, hkv, 128, 1 << 16, seq_lens=1)
+        assert _lib.workspace_bytes(d, P3) > 0
+
+
 @pytest.mark.parametrize("shape,params,code", [
     (Shape(DSA_PREFILL, DSA_BF16, 1, 32, 8, 128, 100), P2, DSA_ERR_INVALID_ARG),     # t % b_q
     (Shape(DSA_PREFILL, DSA_BF16, 1, 30, 8, 128, 4096), P2, DSA_ERR_INVALID_ARG),    # hq % hkv

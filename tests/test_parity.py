@@ -285,6 +285,33 @@ def test_decode_wide_rows(page):
     check_decode(case, dev, range(2))
 
 
+@pytest.mark.parametrize("hq,hkv,d,page,batch", [(32, 32, 128, 0, 1), (32, 32, 128, 64, 2), (24, 12, 64, 0, 2),
+                                                 (64, 64, 128, 0, 1)])
+def test_decode_head_slices(hq, hkv, d, page, batch):
+    """Decode pruning with more kv heads than the 16 lane groups of a scoring
+    workgroup hold (32 and 64: a score list per slice of 16 heads, maxed by
+    the readers) or a head count that does not divide 16 (12 heads, one chunk
+    per workgroup); one sequence takes the fused top-K kernels, two the
+    per-row selection; the one-call step gives the same rows and outputs."""
+    cfg = gen.Config("decode-slices", "decode", batch, hq, hkv, d, 24000, "bf16", 1,
+                     (64, 16, 4), (2048, 512, 128), 16, 64, seed=31, n_queries=1, page_size=page)
+    case = gen.make_case(cfg)
+    if batch == 2:
+        case.seq_lens[:] = [24000, 15000]
+        for b, L in enumerate(case.seq_lens):
+            case.k[b] = case.k[b].sub((slice(None), slice(0, int(L))))
+            case.v[b] = case.v[b].sub((slice(None), slice(0, int(L))))
+    H.say(f"decode head slices {hq}/{hkv} d={d} page={page} batch={batch}")
+    dev = to_device(case)
+    idx, out, _ = check_decode(case, dev, range(batch))
+    q = dev.q[0].contiguous()
+    idx1, out1 = api.prune_attend(q, dev.k, dev.v, params_of(cfg), seq_lens=dev.seq_lens,
+                                  block_table=dev.block_table, t=dev.t)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx1.cpu().numpy().reshape(idx.shape), idx.cpu().numpy())
+    H.assert_close(out1.cpu().numpy(), out.cpu().numpy(), "one-call step vs two calls")
+
+
 def _lib_width(case):
     from dynamic_sparse_attention_query_amd import _lib
     return _lib.index_width(params_of(case.cfg))

@@ -91,6 +91,8 @@ def test_rope_decode(paged, style):
     ("f32", 8, 8, 64, (64, 4, 1), (2048, 512, 128), False),      # one head per group; 8-key, 4-key, 1-key chunks
     ("bf16", 16, 2, 128, (128, 16, 2), (2048, 512, 64), True),   # groups of 8; 2-key chunks take no first round
     ("bf16", 8, 4, 64, (32, 8, 4), (1024, 256, 64), False),      # groups of 2 at d = 64
+    ("bf16", 32, 32, 128, (64, 16, 4), (2048, 512, 128), False),  # 32 kv heads: two score slices
+    ("bf16", 24, 12, 64, (32, 8, 4), (1024, 256, 64), True),     # 12 kv heads per scoring workgroup
 ])
 @pytest.mark.parametrize("style", STYLES)
 def test_rope_decode_shapes(dtype, hq, hkv, d, chunk, keep, paged, style):
