@@ -93,6 +93,7 @@ struct PruneLayout {
   long long R, maxK, maxNC, n1max;
   int hpw, nsl;                       // decode scoring: kv heads per workgroup, score slices
   size_t off_cnt, off_starts, off_scores, bytes;
+  size_t off_kpages, off_prow;        // paged decode: resolved pages (0: not laid out)
 };
 
 // Decode scoring holds the kv heads of a chunk in one workgroup of 16 lane
@@ -127,6 +128,12 @@ PruneLayout prune_layout(const dsa_shape* s, const dsa_params* p) {
   L.off_scores = align256(L.off_starts + 2 * static_cast<size_t>(L.R) * maxK * 4);
   // two sets of score lists (stage parity), one list per head slice
   L.bytes = align256(L.off_scores + 2 * static_cast<size_t>(L.nsl) * L.R * L.maxNC * 4);
+  if (s->mode == DSA_DECODE && s->block_table) {
+    // paged: the kept chunks' page ids (two slots) and the page-resolved row
+    L.off_kpages = L.bytes;
+    L.off_prow = align256(L.off_kpages + 2 * static_cast<size_t>(L.R) * maxK * dsa::kKeptPages * 4);
+    L.bytes = align256(L.off_prow + static_cast<size_t>(L.R) * index_width_ll(p) * 4);
+  }
   return L;
 }
 
@@ -183,8 +190,11 @@ dsa::KvLayout make_kv(const dsa_shape* s, int bq) {
   return kv;
 }
 
+// prow (paged decode, or nullptr): idx with its pages resolved, written by the
+// same call's pruning.
 dsa_status run_attn(const dsa_shape* s, const void* q, const void* k, const void* v, const int32_t* idx,
-                    int32_t L, int bq, float scale, float* out, void* ws, size_t ws_bytes, void* stream) {
+                    int32_t L, int bq, float scale, float* out, void* ws, size_t ws_bytes, void* stream,
+                    const int32_t* prow = nullptr) {
   const long long n_total = idx ? L : s->t;
   const size_t need = attn_bytes(s, n_total);
   if (need > 0 && (!ws || ws_bytes < need))
@@ -195,6 +205,7 @@ dsa_status run_attn(const dsa_shape* s, const void* q, const void* k, const void
   a.k = k;
   a.v = v;
   a.idx = idx;
+  a.prow = prow;
   a.L = L;
   a.out = out;
   a.part = static_cast<float*>(ws);
@@ -332,7 +343,19 @@ dsa::PruneArgs prune_args(const dsa_shape* s, const void* q, const void* k, cons
     a.scores = reinterpret_cast<uint32_t*>(w + lay.off_scores);
   }
   a.visited = reinterpret_cast<unsigned long long*>(visited);
+  a.kpages = nullptr;
+  a.prow = nullptr;
   return a;
+}
+
+// Plain paged decode (no remembered stages, no RoPE): the per-row top-K
+// resolves the kept chunks' pages for the next stage, and with `row` the last
+// stage's index row too.
+void attach_pages(dsa::PruneArgs& a, const dsa_shape* s, const PruneLayout& lay, void* ws, bool row) {
+  if (s->mode != DSA_DECODE || !s->block_table || !ws || lay.off_kpages == 0) return;
+  char* w = static_cast<char*>(ws);
+  a.kpages = reinterpret_cast<int32_t*>(w + lay.off_kpages);
+  if (row) a.prow = reinterpret_cast<int32_t*>(w + lay.off_prow);
 }
 
 // Mask cache layout: status [B], then per-sequence stage records (kept counts,
@@ -381,6 +404,7 @@ dsa_status run_prune_attend(const dsa_shape* s, const void* q, const void* k, co
   const long long L = index_width_ll(p);
   char* wsc = static_cast<char*>(ws);
   dsa::PruneArgs a = prune_args(s, q, k, p, idx, L, lay.pl, ws, visited);
+  attach_pages(a, s, lay.pl, ws, true);
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   const float sc = scale > 0.f ? scale : 1.0f / std::sqrt(static_cast<float>(s->d));
   hipError_t err = hipSuccess;
@@ -413,7 +437,7 @@ dsa_status run_prune_attend(const dsa_shape* s, const void* q, const void* k, co
   if (err != hipSuccess) return fail(DSA_ERR_HIP, "prune launch failed: %s", hipGetErrorString(err));
   if (fused) return DSA_OK;
   return run_attn(s, q, k, v, idx, static_cast<int32_t>(L), p->block_q, scale, out, wsc + lay.off_part,
-                  lay.bytes - lay.off_part, stream);
+                  lay.bytes - lay.off_part, stream, a.prow);
 }
 
 
@@ -436,7 +460,8 @@ dsa_status dsa_prune_select(const dsa_shape* s, const void* q, const void* k, co
     return fail(DSA_ERR_UNSUPPORTED, "a stage would score %lld chunks per row (limit 32768)", lay.maxNC);
   if (!ws || ws_bytes < lay.bytes)
     return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, lay.bytes);
-  const dsa::PruneArgs a = prune_args(s, q, k, p, idx, L, lay, ws, visited);
+  dsa::PruneArgs a = prune_args(s, q, k, p, idx, L, lay, ws, visited);
+  attach_pages(a, s, lay, ws, false);
   hipError_t err = dsa::launch_prune(a, s->dtype, static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return fail(DSA_ERR_HIP, "prune launch failed: %s", hipGetErrorString(err));
   return DSA_OK;

@@ -94,11 +94,15 @@ __device__ __forceinline__ void write_partials(const float (&o)[G][D / 16], cons
 // k_decode_combine merges ("Flash Decoding" of the InfiniteHiP page's "Block
 // Sparse Attention Implementation"; the merge of the InfLLM blog page's
 // "Mathematical Formulation of Efficient Softmax Normalization").
+// With sphys (paged, or nullptr) the split's rows come page-resolved
+// ((page id << page_shift) | offset in the page), and the page table is not
+// read.
 template <int D, int G, bool PAGED, int kKeysPerGroup>
 __device__ __forceinline__ void split_partial(const KvLayout& kv, const uint16_t* K, const uint16_t* V,
                                               const RowSlice<uint16_t, D / 16> (&q)[G], const int* spos,
                                               float (&smax)[16][G], float (&sred)[4][G * D + G], float* part,
-                                              int nsp, int sp, int b, int g, float scale_log2) {
+                                              int nsp, int sp, int b, int g, float scale_log2,
+                                              const int* sphys = nullptr) {
   constexpr int EPL = D / 16;
   using Row = RowSlice<uint16_t, EPL>;
   const int tid = threadIdx.x, gi = tid >> 4, li = tid & 15;
@@ -110,8 +114,17 @@ __device__ __forceinline__ void split_partial(const KvLayout& kv, const uint16_t
     pu[u] = spos[gi + 16 * u];
     const int pp = max(pu[u], 0);               // padding reads row 0 and is masked below
     size_t off;
-    if constexpr (PAGED) off = kv_offset(kv, b, g, pp);
-    else off = ((static_cast<size_t>(b) * kv.Hkv + g) * kv.T + pp) * D;
+    if constexpr (PAGED) {
+      if (sphys) {
+        const int pr = max(sphys[gi + 16 * u], 0);
+        off = ((static_cast<size_t>(pr >> kv.page_shift) * kv.Hkv + g) * kv.page_size +
+               (pr & (kv.page_size - 1))) * D;
+      } else {
+        off = kv_offset(kv, b, g, pp);
+      }
+    } else {
+      off = ((static_cast<size_t>(b) * kv.Hkv + g) * kv.T + pp) * D;
+    }
     kr[u].load(K + off + li * EPL);
     vr[u].load(V + off + li * EPL);
   }
@@ -270,6 +283,7 @@ __global__ void __launch_bounds__(256, 2) k_decode_rows(AttnArgs a) {
   constexpr int EPL = D / 16;
   using Row = RowSlice<uint16_t, EPL>;
   __shared__ int spos[kStepSplitKeys];
+  __shared__ int sphys[PAGED ? kStepSplitKeys : 1];
   __shared__ float smax[16][G];
   __shared__ float sred[4][G * D + G];
   const KvLayout& kv = a.kv;
@@ -280,18 +294,22 @@ __global__ void __launch_bounds__(256, 2) k_decode_rows(AttnArgs a) {
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) q[hh].load(Q + (static_cast<size_t>(b) * kv.Hq + g * G + hh) * D + li * EPL);
   const int tq = seq_len_of(kv, b) - 1;
+  const bool phys = PAGED && a.prow != nullptr;
   if (tid < kStepSplitKeys) {
     const int i = sp * kStepSplitKeys + tid;
-    int p = -1;
+    int p = -1, pr = -1;
     if (i < a.L) {
       p = a.idx[static_cast<size_t>(b) * a.L + i];
+      if (phys) pr = a.prow[static_cast<size_t>(b) * a.L + i];
       if (p < 0 || p > tq) p = -1;
     }
     spos[tid] = p;
+    if constexpr (PAGED) sphys[tid] = pr;
   }
   __syncthreads();
   split_partial<D, G, PAGED, kKeysPerGroup>(kv, static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
-                                            q, spos, smax, sred, a.part, a.n_splits, sp, b, g, a.scale_log2);
+                                            q, spos, smax, sred, a.part, a.n_splits, sp, b, g, a.scale_log2,
+                                            phys ? sphys : nullptr);
 }
 
 // ------------------------------------------------------------------------- //

@@ -15,6 +15,10 @@ constexpr float kNegBig = -1.0e30f;   // finite "no key yet" running max
 // ------------------------------------------------------------------------- //
 // argument blocks                                                           //
 // ------------------------------------------------------------------------- //
+// Paged decode: page ids kept per selected chunk (a chunk spanning more pages
+// is left to the page table).
+constexpr int kKeptPages = 8;
+
 struct KvLayout {
   int B, Hq, Hkv, D;
   int T;                     // prefill length, or decode token stride / capacity
@@ -56,6 +60,14 @@ struct PruneArgs {
   // over the nsl lists. Prefill and the generic paths: hpw = Hkv, nsl = 1.
   int hpw;
   int nsl;
+  // Paged decode (or nullptr): the per-row top-K resolves the pages once for
+  // the kernels after it. kpages [slots, R, maxK, kKeptPages]: the page ids of
+  // every kept chunk's pages (first page first, -1 past the last or when the
+  // chunk spans more than kKeptPages pages); prow [R, L]: the last stage's
+  // index row with each position p turned into (page id << page_shift) |
+  // (p mod page_size), -1 for padding.
+  int32_t* kpages;
+  int32_t* prow;
 };
 
 struct AttnArgs {
@@ -64,6 +76,7 @@ struct AttnArgs {
   const void* k;
   const void* v;
   const int32_t* idx;        // nullptr => dense causal rows [0, e)
+  const int32_t* prow;       // paged decode: idx with pages resolved (PruneArgs::prow), or nullptr
   int L;                     // idx row width
   float* out;
   float* part;               // decode split partials [B, Hq, n_splits, D + 2]

@@ -16,6 +16,7 @@
 // Every chunk of every stage is a contiguous run of positions: stage 1 tiles
 // [n_sink, mid_hi) and each later chunk size divides the previous one.
 #include <algorithm>
+#include <type_traits>
 
 #include "prune_common.h"
 #include "selectrep.h"
@@ -43,8 +44,10 @@ __device__ __forceinline__ void write_chunk_entries(int32_t* row, int L, int i0,
   }
 }
 
+// prow (paged decode, or nullptr): the same entries with their pages resolved
+// (paged_row) into the row r of prow; b is the row's sequence.
 __device__ __forceinline__ void write_row_rest(const PruneArgs& a, int r, const Geo& geo, int n_sel, int l,
-                                               int win_lo) {
+                                               int win_lo, int32_t* prow = nullptr, int b = 0) {
   const int win0 = geo.sink_hi + n_sel * l;        // kept chunks fill [sink_hi, win0)
   const int end = win0 + max(0, geo.e - win_lo);
   int32_t* row = a.idx + static_cast<size_t>(r) * a.L;
@@ -58,10 +61,18 @@ __device__ __forceinline__ void write_row_rest(const PruneArgs& a, int r, const 
     const int i = 4 * i4;
     if (i + 4 <= geo.sink_hi || i >= win0) {
       *reinterpret_cast<int4*>(row + i) = make_int4(value(i), value(i + 1), value(i + 2), value(i + 3));
+      if (prow) {
+        int32_t* pr = prow + static_cast<size_t>(r) * a.L;
+        *reinterpret_cast<int4*>(pr + i) = make_int4(paged_row(a.kv, b, value(i)), paged_row(a.kv, b, value(i + 1)),
+                                                     paged_row(a.kv, b, value(i + 2)), paged_row(a.kv, b, value(i + 3)));
+      }
     } else {                                        // a slot shared with kept-chunk entries
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        if (i + u < geo.sink_hi || i + u >= win0) row[i + u] = value(i + u);
+        if (i + u < geo.sink_hi || i + u >= win0) {
+          row[i + u] = value(i + u);
+          if (prow) prow[static_cast<size_t>(r) * a.L + i + u] = paged_row(a.kv, b, value(i + u));
+        }
     }
   }
   if (a.row_status && threadIdx.x == 0) a.row_status[r] = end > a.L ? 1 : 0;
@@ -98,13 +109,30 @@ __global__ void __launch_bounds__(NT) k_topk(PruneArgs a, int stage) {
   // stores share the vector memory counter with loads, so an earlier store
   // would hold up their wait. After the last stage each kept chunk writes
   // its own entries of the index row.
+  const bool pages = a.kv.block_table != nullptr && a.kpages != nullptr;
   select_row<E, NT>(key, j0, nc, kc, L, [&](int j, int pos) {
     const int st = stage == 0 ? a.n_sink + (j << lg) : sprev[j >> sh] + ((j & ((1 << sh) - 1)) << lg);
     out[pos] = st;
     if (last) write_chunk_entries(row, a.L, geo.sink_hi + pos * l, st, l);
+    if (pages && !last) {                       // the chunk's page ids for the next stage
+      const int* tb = a.kv.block_table + static_cast<size_t>(b) * a.kv.max_pages;
+      const int pg0 = st >> a.kv.page_shift;
+      const int npg = ((st + l - 1) >> a.kv.page_shift) - pg0 + 1;
+      int v[kKeptPages];
+#pragma unroll
+      for (int u = 0; u < kKeptPages; ++u) v[u] = npg <= kKeptPages && u < npg ? tb[pg0 + u] : -1;
+      int4* dst = reinterpret_cast<int4*>(stage_pages(a, stage, r) + pos * kKeptPages);
+#pragma unroll
+      for (int u = 0; u < kKeptPages / 4; ++u) dst[u] = make_int4(v[4 * u], v[4 * u + 1], v[4 * u + 2], v[4 * u + 3]);
+    }
+    if (pages && last && a.prow) {              // the kept entries with their pages resolved
+      int32_t* prw = a.prow + static_cast<size_t>(r) * a.L;
+      const int i0 = geo.sink_hi + pos * l;
+      for (int x = 0; x < l && i0 + x < a.L; ++x) prw[i0 + x] = paged_row(a.kv, b, st + x);
+    }
   });
   if (tid == 0) record_stage(a, stage, r, n_sel, geo);
-  if (last) write_row_rest(a, r, geo, n_sel, l, win_lo);
+  if (last) write_row_rest(a, r, geo, n_sel, l, win_lo, pages ? a.prow : nullptr, b);
 }
 
 // The last stage's remembered output turned into the index row of the current
@@ -132,9 +160,11 @@ __global__ void __launch_bounds__(kTopkThreads) k_assemble(PruneArgs a) {
 // starting at st, on the rows of kv head g as stored.
 template <typename T, int D, int G, int SPEC, bool PAGED, bool TAIL4 = false>
 __device__ __forceinline__ float score_group(const PruneArgs& a, int stage, int b, int g, int li, int st,
-                                             const RowSlice<T, D / 16> (&q)[G]) {
-  const ChunkRows<T, D, PAGED> rows(a, b, g, li, st, a.chunk[stage]);
-  return selectrep_group<T, D, G, SPEC, ChunkRows<T, D, PAGED>, TAIL4>(a, stage, li, st, rows, q);
+                                             const RowSlice<T, D / 16> (&q)[G], const int* pp = nullptr,
+                                             int pst = 0) {
+  return paged_rows<T, D, PAGED>(a, b, g, li, st, a.chunk[stage], pp, pst, [&](const auto& rows) {
+    return selectrep_group<T, D, G, SPEC, std::decay_t<decltype(rows)>, TAIL4>(a, stage, li, st, rows, q);
+  });
 }
 
 // Workgroup = 16 lane groups of 16 lanes; a group owns one (chunk, kv head)
@@ -166,14 +196,25 @@ k_score_decode(PruneArgs a, int stage) {
   // count, this chunk's start (read within the start list for every j of
   // the grid) and the query rows.
   const int e = seq_len_of(kv, r);
-  int nc_prev = 0, st;
+  int nc_prev = 0, st, pst = 0;
+  int pp[kKeptPages];                           // paged: the parent chunk's page ids
+  const bool pre = PAGED && stage > 0 && a.kpages != nullptr;
   if (stage == 0) {
     st = a.n_sink + (j << a.lchunk[0]);
   } else {
     const int sh = a.lchunk[stage - 1] - a.lchunk[stage];
     nc_prev = a.cnt[r * kMaxStages + stage - 1];
-    const int32_t* prev = stage_starts(a, stage - 1, r);
-    st = prev[min(j >> sh, a.maxK - 1)] + ((j & ((1 << sh) - 1)) << a.lchunk[stage]);
+    const int jp = min(j >> sh, a.maxK - 1);
+    pst = stage_starts(a, stage - 1, r)[jp];
+    st = pst + ((j & ((1 << sh) - 1)) << a.lchunk[stage]);
+    if (pre) {
+      const int4* p4 = reinterpret_cast<const int4*>(stage_pages(a, stage - 1, r) + jp * kKeptPages);
+#pragma unroll
+      for (int v = 0; v < kKeptPages / 4; ++v) {
+        const int4 u = p4[v];
+        pp[4 * v] = u.x; pp[4 * v + 1] = u.y; pp[4 * v + 2] = u.z; pp[4 * v + 3] = u.w;
+      }
+    }
   }
   Row q[G];
 #pragma unroll
@@ -186,7 +227,7 @@ k_score_decode(PruneArgs a, int stage) {
   const bool active = dl.used && j < nc;
 
   float best = -INFINITY;
-  if (active) best = score_group<T, D, G, SPEC, PAGED>(a, stage, b, g, li, st, q);
+  if (active) best = score_group<T, D, G, SPEC, PAGED>(a, stage, b, g, li, st, q, pre ? pp : nullptr, pst);
   if (li == 0) red[gi] = best;
   __syncthreads();
   if (tid < cpw) {

@@ -24,6 +24,20 @@ __device__ __forceinline__ uint32_t* stage_scores(const PruneArgs& a, int stage,
   return a.scores + ((static_cast<size_t>(stage & 1) * a.nsl + sl) * a.R + r) * a.maxNC;
 }
 
+// Page ids of the kept chunks of `stage` for row r (paged decode), kKeptPages
+// per chunk.
+__device__ __forceinline__ int32_t* stage_pages(const PruneArgs& a, int stage, int r) {
+  return a.kpages + (static_cast<size_t>(a.slot[stage]) * a.R + r) * a.maxK * kKeptPages;
+}
+
+// Pool row of position p of sequence b: (page id << page_shift) | offset in
+// the page; -1 for p < 0.
+__device__ __forceinline__ int32_t paged_row(const KvLayout& kv, int b, int p) {
+  if (p < 0) return -1;
+  const int page = kv.block_table[static_cast<size_t>(b) * kv.max_pages + (p >> kv.page_shift)];
+  return (page << kv.page_shift) | (p & (kv.page_size - 1));
+}
+
 // Kept chunk starts of `stage` for row r (ascending, cnt[r][stage] of them).
 __device__ __forceinline__ int32_t* stage_starts(const PruneArgs& a, int stage, int r) {
   return a.starts + (static_cast<size_t>(a.slot[stage]) * a.R + r) * a.maxK;
@@ -143,11 +157,16 @@ __device__ __forceinline__ void load_kept_starts(const PruneArgs& a, int stage, 
 
 // Key rows of one chunk as seen by a lane group (lane li holds elements
 // li*D/16 .. of a row). Paged K (compile-time): the chunk covers at most
-// kChunkPages pages in the common case; their ids are loaded once, together,
-// so a tournament step costs one dependent load (the row) instead of two
-// (table entry, then row).
+// kChunkPages pages in the common case (`hoist`); their ids are loaded once,
+// together, so a tournament step costs one dependent load (the row) instead
+// of two (table entry, then row), and at() holds no load but the row's. A
+// chunk over more pages takes the TABLE form, whose at() reads the page
+// table for every row. The two forms are separate tournament bodies
+// (paged_rows below): a table load inside at() behind a per-row branch made
+// the compiler wait for every load in flight at the branch's join, which
+// serialized a round's row loads.
 constexpr int kChunkPages = 4;
-template <typename T, int D, bool PAGED>
+template <typename T, int D, bool PAGED, bool TABLE = false>
 struct ChunkRows {
   static constexpr int EPL = D / 16;
   const T* K;                   // contiguous: row 0 of (b, g), this lane's slice; paged: the pool + slice
@@ -158,7 +177,12 @@ struct ChunkRows {
   bool hoist;
   int pid0, pid1, pid2, pid3;       // hoisted page ids
 
-  __device__ __forceinline__ ChunkRows(const PruneArgs& a, int b, int g, int li, int st, int l) {
+  // pp (paged, or nullptr): the page ids of the parent chunk that starts at
+  // pst, as the previous stage's top-K resolved them (kpages); the chunk's
+  // pages are then taken from those registers instead of the page table,
+  // which saves the dependent table load before the first row.
+  __device__ __forceinline__ ChunkRows(const PruneArgs& a, int b, int g, int li, int st, int l,
+                                       const int* pp = nullptr, int pst = 0) {
     const KvLayout& kv = a.kv;
     const T* base = static_cast<const T*>(a.k) + li * EPL;
     if constexpr (PAGED) {
@@ -169,11 +193,31 @@ struct ChunkRows {
       page_rows = kv.Hkv * kv.page_size;
       pg0 = st >> shift;
       const int npg = ((st + l - 1) >> shift) - pg0 + 1;
-      hoist = npg <= kChunkPages;
-      pid0 = hoist ? table[pg0] : 0;
-      pid1 = hoist && npg > 1 ? table[pg0 + 1] : 0;
-      pid2 = hoist && npg > 2 ? table[pg0 + 2] : 0;
-      pid3 = hoist && npg > 3 ? table[pg0 + 3] : 0;
+      hoist = !TABLE && npg <= kChunkPages;
+      if (TABLE) {
+        pid0 = pid1 = pid2 = pid3 = 0;
+      } else if (pp != nullptr) {
+        const int i0 = pg0 - (pst >> shift);     // the chunk's first page within the parent's
+        auto pick = [&](int i) {
+          int v = -1;
+#pragma unroll
+          for (int k = 0; k < kKeptPages; ++k) v = i == k ? pp[k] : v;
+          return v;
+        };
+        pid0 = pick(i0);
+        pid1 = npg > 1 ? pick(i0 + 1) : 0;
+        pid2 = npg > 2 ? pick(i0 + 2) : 0;
+        pid3 = npg > 3 ? pick(i0 + 3) : 0;
+        hoist = hoist && pid0 >= 0 && pid1 >= 0 && pid2 >= 0 && pid3 >= 0;
+      } else {
+        // four loads at once (indices kept inside the table row; the ids of
+        // pages past the chunk are never used)
+        const int last = kv.max_pages - 1;
+        pid0 = table[min(pg0, last)];
+        pid1 = table[min(pg0 + 1, last)];
+        pid2 = table[min(pg0 + 2, last)];
+        pid3 = table[min(pg0 + 3, last)];
+      }
     } else {
       K = base + (static_cast<size_t>(b) * kv.Hkv + g) * kv.T * D;
     }
@@ -184,11 +228,11 @@ struct ChunkRows {
     if constexpr (PAGED) {
       const int k = pos >> shift;
       int page;
-      if (hoist) {
+      if constexpr (TABLE) {
+        page = table[k];
+      } else {                                  // only used when hoist holds
         const int i = k - pg0;
         page = i == 0 ? pid0 : i == 1 ? pid1 : i == 2 ? pid2 : pid3;
-      } else {
-        page = table[k];
       }
       const size_t row = static_cast<size_t>(page) * page_rows + hkv_g + (pos - (k << shift));
       x.load(K + row * D);
@@ -198,5 +242,18 @@ struct ChunkRows {
     return x;
   }
 };
+
+// Calls body(rows) with the chunk's row provider: contiguous, or paged with
+// the page ids in registers when the chunk spans at most kChunkPages pages,
+// else paged through the page table (a divergent choice per lane group).
+template <typename T, int D, bool PAGED, class Body>
+__device__ __forceinline__ float paged_rows(const PruneArgs& a, int b, int g, int li, int st, int l, const int* pp,
+                                            int pst, Body&& body) {
+  const ChunkRows<T, D, PAGED> rows(a, b, g, li, st, l, pp, pst);
+  if constexpr (PAGED) {
+    if (!rows.hoist) return body(ChunkRows<T, D, true, true>(a, b, g, li, st, l));
+  }
+  return body(rows);
+}
 
 }  // namespace dsa

@@ -27,6 +27,7 @@
 // evaluates in registers (the partner half of every pair comes from lane
 // li ^ 8 of the lane group).
 #include <algorithm>
+#include <type_traits>
 
 #include "prune_common.h"
 #include "selectrep.h"
@@ -122,13 +123,12 @@ __device__ __forceinline__ void load_rotated(RowSlice<T, EPL>& q, const uint16_t
 // keys that can represent the first log2(SPEC) splits (positions i*l/SPEC)
 // are loaded and scored in one round and those splits are decided from them.
 // Returns the best chunk score over the heads.
-template <typename T, int D, int G, int SPEC, bool PAGED>
-__device__ __forceinline__ float score_group_rt(const PruneArgs& a, int stage, int b, int g, int li, int st,
-                                                const RowSlice<T, D / 16> (&ql)[G],
-                                                const RowSlice<T, D / 16> (&qr)[G]) {
+template <typename T, int D, int G, int SPEC, class Rows>
+__device__ __forceinline__ float score_group_rt_rows(const PruneArgs& a, int stage, int li, int st, const Rows& rows,
+                                                     const RowSlice<T, D / 16> (&ql)[G],
+                                                     const RowSlice<T, D / 16> (&qr)[G]) {
   using Row = RowSlice<T, D / 16>;
   const int l = a.chunk[stage];
-  const ChunkRows<T, D, PAGED> rows(a, b, g, li, st, l);
   auto dl = [&](const Row& kr, int hh) { return group16_sum(kr.dot(ql[hh])); };
   auto dr = [&](const Row& kr, int hh) { return group16_sum(kr.dot(qr[hh])); };
 
@@ -218,6 +218,17 @@ __device__ __forceinline__ float score_group_rt(const PruneArgs& a, int stage, i
 #pragma unroll
   for (int hh = 1; hh < G; ++hh) best = fmaxf(best, win[hh]);
   return best;
+}
+
+// The tournaments above on the chunk's rows: contiguous, or paged with the
+// page ids in registers when they fit, else through the page table.
+template <typename T, int D, int G, int SPEC, bool PAGED>
+__device__ __forceinline__ float score_group_rt(const PruneArgs& a, int stage, int b, int g, int li, int st,
+                                                const RowSlice<T, D / 16> (&ql)[G],
+                                                const RowSlice<T, D / 16> (&qr)[G]) {
+  return paged_rows<T, D, PAGED>(a, b, g, li, st, a.chunk[stage], nullptr, 0, [&](const auto& rows) {
+    return score_group_rt_rows<T, D, G, SPEC>(a, stage, li, st, rows, ql, qr);
+  });
 }
 
 // Decode scoring of one stage: workgroup = 16 lane groups; a group owns one
@@ -493,10 +504,10 @@ __global__ void __launch_bounds__(256) k_ci_keys(PruneArgs a, int stage0, CiKeyO
 // rotation runs in fp64 as in the oracle. (An fp32 evaluation with an fp64
 // re-evaluation of the elements near a rounding half-step was slower: the
 // re-evaluation reaches about one row in eight per wave.)
-template <typename T, int D, bool PAGED>
+template <typename T, int D, bool PAGED, bool TABLE = false>
 struct CiRows {
   static constexpr int EPL = D / 16;
-  ChunkRows<T, D, PAGED> raw;
+  ChunkRows<T, D, PAGED, TABLE> raw;
   double c[EPL], ss[EPL];                       // cos, and sin signed for this lane's half
 
   __device__ __forceinline__ CiRows(const PruneArgs& a, int stage, int b, int g, int li, int st, const double* theta)
@@ -585,7 +596,12 @@ k_score_decode_ci(PruneArgs a, int stage, const uint16_t* q_all, double base) {
   float best = -INFINITY;
   if (active) {
     const CiRows<T, D, PAGED> rows(a, stage, b, g, li, st, theta);
-    best = selectrep_group<T, D, G, SPEC>(a, stage, li, st, rows, q);
+    if (!PAGED || rows.raw.hoist) {
+      best = selectrep_group<T, D, G, SPEC>(a, stage, li, st, rows, q);
+    } else if constexpr (PAGED) {               // a chunk over more pages: rows through the page table
+      const CiRows<T, D, true, true> trows(a, stage, b, g, li, st, theta);
+      best = selectrep_group<T, D, G, SPEC>(a, stage, li, st, trows, q);
+    }
   }
   if (li == 0) red[gi] = best;
   __syncthreads();

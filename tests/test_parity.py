@@ -346,7 +346,15 @@ def test_c4_paged_ragged_batch():
     case = gen.make_case("c4")
     dev = to_device(case)
     bs = sorted({0, 31, *np.random.default_rng(7).choice(32, 5, replace=False).tolist()})
-    check_decode(case, dev, bs)
+    idx, out, _ = check_decode(case, dev, bs)
+    # the one-call step resolves the pages of its index rows while selecting;
+    # the attention over them is the two-call path's, bit for bit
+    q = dev.q[0].contiguous()
+    idx1, out1 = api.prune_attend(q, dev.k, dev.v, params_of(case.cfg), seq_lens=dev.seq_lens,
+                                  block_table=dev.block_table, t=dev.t)
+    torch.cuda.synchronize()
+    assert torch.equal(idx1.view(idx.shape), idx)
+    assert torch.equal(out1, out)
 
 
 def test_c5_decode_3m_needles():
