@@ -106,27 +106,41 @@ __device__ __forceinline__ void split_partial(const KvLayout& kv, const uint16_t
   constexpr int EPL = D / 16;
   using Row = RowSlice<uint16_t, EPL>;
   const int tid = threadIdx.x, gi = tid >> 4, li = tid & 15;
-  // gather the split's K and V rows: lane group gi takes entries gi + 16u
+  // gather the split's K and V rows: lane group gi takes entries gi + 16u.
+  // Every row's offset is formed first (paged: all page-table reads at once),
+  // then all row loads go out together: a table read behind a per-row branch
+  // would make the compiler wait for the loads in flight at every join.
   int pu[kKeysPerGroup];
+  size_t off[kKeysPerGroup];
+#pragma unroll
+  for (int u = 0; u < kKeysPerGroup; ++u) pu[u] = spos[gi + 16 * u];
+  if constexpr (PAGED) {
+    const int mask = kv.page_size - 1;
+    if (sphys) {
+#pragma unroll
+      for (int u = 0; u < kKeysPerGroup; ++u) {
+        const int pr = max(sphys[gi + 16 * u], 0);
+        off[u] = ((static_cast<size_t>(pr >> kv.page_shift) * kv.Hkv + g) * kv.page_size + (pr & mask)) * D;
+      }
+    } else {
+      const int32_t* tb = kv.block_table + static_cast<size_t>(b) * kv.max_pages;
+      int page[kKeysPerGroup];
+#pragma unroll
+      for (int u = 0; u < kKeysPerGroup; ++u) page[u] = tb[max(pu[u], 0) >> kv.page_shift];
+#pragma unroll
+      for (int u = 0; u < kKeysPerGroup; ++u)
+        off[u] = ((static_cast<size_t>(page[u]) * kv.Hkv + g) * kv.page_size + (max(pu[u], 0) & mask)) * D;
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < kKeysPerGroup; ++u)
+      off[u] = ((static_cast<size_t>(b) * kv.Hkv + g) * kv.T + max(pu[u], 0)) * D;   // padding reads row 0
+  }
   Row kr[kKeysPerGroup], vr[kKeysPerGroup];
 #pragma unroll
   for (int u = 0; u < kKeysPerGroup; ++u) {
-    pu[u] = spos[gi + 16 * u];
-    const int pp = max(pu[u], 0);               // padding reads row 0 and is masked below
-    size_t off;
-    if constexpr (PAGED) {
-      if (sphys) {
-        const int pr = max(sphys[gi + 16 * u], 0);
-        off = ((static_cast<size_t>(pr >> kv.page_shift) * kv.Hkv + g) * kv.page_size +
-               (pr & (kv.page_size - 1))) * D;
-      } else {
-        off = kv_offset(kv, b, g, pp);
-      }
-    } else {
-      off = ((static_cast<size_t>(b) * kv.Hkv + g) * kv.T + pp) * D;
-    }
-    kr[u].load(K + off + li * EPL);
-    vr[u].load(V + off + li * EPL);
+    kr[u].load(K + off[u] + li * EPL);
+    vr[u].load(V + off[u] + li * EPL);
   }
   float sc[kKeysPerGroup][G];
   float mloc[G];
@@ -382,23 +396,37 @@ __global__ void __launch_bounds__(256, 2) k_decode_span(AttnArgs a) {
     for (int x = 0; x < EPL; ++x) o[hh][x] = 0.f;
   }
   for (int base = k_begin; base < k_end; base += kStepSplitKeys) {
+    // positions, then (paged) pages, then rows, each step's loads issued
+    // together (no load behind a per-row branch: its join would wait for
+    // every load in flight)
     int pu[KPG];
-    Row kr[KPG], vr[KPG];
 #pragma unroll
     for (int u = 0; u < KPG; ++u) {
       const int i = base + gi + 16 * u;
-      int p = -1;
-      if (i < k_end) {
-        p = ROWS ? row[i] : i;
-        if (p < 0 || p > tq) p = -1;
-      }
+      int p = ROWS ? row[min(i, k_end - 1)] : i;
+      if (i >= k_end || p < 0 || p > tq) p = -1;
       pu[u] = p;
-      const int pp = max(p, 0);                   // padding reads row 0 and is masked below
-      size_t off;
-      if constexpr (PAGED) off = kv_offset(kv, b, g, pp);
-      else off = ((static_cast<size_t>(b) * kv.Hkv + g) * kv.T + pp) * D;
-      kr[u].load(K + off + li * EPL);
-      vr[u].load(V + off + li * EPL);
+    }
+    size_t off[KPG];
+    if constexpr (PAGED) {
+      const int32_t* tb = kv.block_table + static_cast<size_t>(b) * kv.max_pages;
+      int page[KPG];
+#pragma unroll
+      for (int u = 0; u < KPG; ++u) page[u] = tb[max(pu[u], 0) >> kv.page_shift];
+#pragma unroll
+      for (int u = 0; u < KPG; ++u)
+        off[u] = ((static_cast<size_t>(page[u]) * kv.Hkv + g) * kv.page_size + (max(pu[u], 0) & (kv.page_size - 1))) *
+                 D;
+    } else {
+#pragma unroll
+      for (int u = 0; u < KPG; ++u)
+        off[u] = ((static_cast<size_t>(b) * kv.Hkv + g) * kv.T + max(pu[u], 0)) * D;   // padding reads row 0
+    }
+    Row kr[KPG], vr[KPG];
+#pragma unroll
+    for (int u = 0; u < KPG; ++u) {
+      kr[u].load(K + off[u] + li * EPL);
+      vr[u].load(V + off[u] + li * EPL);
     }
     float sc[KPG][G], mc[G];
 #pragma unroll
