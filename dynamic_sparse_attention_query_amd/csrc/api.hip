@@ -351,8 +351,10 @@ dsa::PruneArgs prune_args(const dsa_shape* s, const void* q, const void* k, cons
 // Plain paged decode (no remembered stages, no RoPE): the per-row top-K
 // resolves the kept chunks' pages for the next stage, and with `row` the last
 // stage's index row too.
+// (Pages of at least 8 positions: the row writer resolves four consecutive
+// positions with two table reads.)
 void attach_pages(dsa::PruneArgs& a, const dsa_shape* s, const PruneLayout& lay, void* ws, bool row) {
-  if (s->mode != DSA_DECODE || !s->block_table || !ws || lay.off_kpages == 0) return;
+  if (s->mode != DSA_DECODE || !s->block_table || !ws || lay.off_kpages == 0 || s->page_size < 8) return;
   char* w = static_cast<char*>(ws);
   a.kpages = reinterpret_cast<int32_t*>(w + lay.off_kpages);
   if (row) a.prow = reinterpret_cast<int32_t*>(w + lay.off_prow);

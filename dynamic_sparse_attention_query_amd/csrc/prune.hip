@@ -61,17 +61,27 @@ __device__ __forceinline__ void write_row_rest(const PruneArgs& a, int r, const 
     const int i = 4 * i4;
     if (i + 4 <= geo.sink_hi || i >= win0) {
       *reinterpret_cast<int4*>(row + i) = make_int4(value(i), value(i + 1), value(i + 2), value(i + 3));
-      if (prow) {
-        int32_t* pr = prow + static_cast<size_t>(r) * a.L;
-        *reinterpret_cast<int4*>(pr + i) = make_int4(paged_row(a.kv, b, value(i)), paged_row(a.kv, b, value(i + 1)),
-                                                     paged_row(a.kv, b, value(i + 2)), paged_row(a.kv, b, value(i + 3)));
+      if (prow) {                                   // sinks, or window then padding: consecutive positions
+        int v[4];
+        const int nv = value(i) < 0 ? 0 : value(i + 3) >= 0 ? 4 : value(i + 2) >= 0 ? 3 : value(i + 1) >= 0 ? 2 : 1;
+        paged_rows_run(a.kv, b, value(i), nv, v);
+        *reinterpret_cast<int4*>(prow + static_cast<size_t>(r) * a.L + i) = make_int4(v[0], v[1], v[2], v[3]);
       }
     } else {                                        // a slot shared with kept-chunk entries
+      int id[4];
+      if (prow) {                                   // one table read per entry, all issued together
+        const int32_t* tb = a.kv.block_table + static_cast<size_t>(b) * a.kv.max_pages;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) id[u] = tb[min(max(value(i + u), 0) >> a.kv.page_shift, a.kv.max_pages - 1)];
+      }
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         if (i + u < geo.sink_hi || i + u >= win0) {
-          row[i + u] = value(i + u);
-          if (prow) prow[static_cast<size_t>(r) * a.L + i + u] = paged_row(a.kv, b, value(i + u));
+          const int p = value(i + u);
+          row[i + u] = p;
+          if (prow)
+            prow[static_cast<size_t>(r) * a.L + i + u] =
+                p < 0 ? -1 : (id[u] << a.kv.page_shift) | (p & (a.kv.page_size - 1));
         }
     }
   }
@@ -128,7 +138,13 @@ __global__ void __launch_bounds__(NT) k_topk(PruneArgs a, int stage) {
     if (pages && last && a.prow) {              // the kept entries with their pages resolved
       int32_t* prw = a.prow + static_cast<size_t>(r) * a.L;
       const int i0 = geo.sink_hi + pos * l;
-      for (int x = 0; x < l && i0 + x < a.L; ++x) prw[i0 + x] = paged_row(a.kv, b, st + x);
+      for (int x0 = 0; x0 < l && i0 + x0 < a.L; x0 += 4) {   // four entries (within two pages) at a time
+        int v[4];
+        paged_rows_run(a.kv, b, st + x0, min(4, l - x0), v);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (x0 + u < l && i0 + x0 + u < a.L) prw[i0 + x0 + u] = v[u];
+      }
     }
   });
   if (tid == 0) record_stage(a, stage, r, n_sel, geo);

@@ -30,12 +30,23 @@ __device__ __forceinline__ int32_t* stage_pages(const PruneArgs& a, int stage, i
   return a.kpages + (static_cast<size_t>(a.slot[stage]) * a.R + r) * a.maxK * kKeptPages;
 }
 
-// Pool row of position p of sequence b: (page id << page_shift) | offset in
-// the page; -1 for p < 0.
-__device__ __forceinline__ int32_t paged_row(const KvLayout& kv, int b, int p) {
-  if (p < 0) return -1;
-  const int page = kv.block_table[static_cast<size_t>(b) * kv.max_pages + (p >> kv.page_shift)];
-  return (page << kv.page_shift) | (p & (kv.page_size - 1));
+// Pool rows of the positions p0 .. p0 + n - 1 of sequence b (consecutive,
+// n <= page_size, so at most two pages): (page id << page_shift) | offset in
+// the page, into out[0 .. n); -1 where p0 + x < 0 or x >= valid. The two
+// table reads are unconditional (clamped to the row) so they go out together.
+template <int N>
+__device__ __forceinline__ void paged_rows_run(const KvLayout& kv, int b, int p0, int valid, int (&out)[N]) {
+  const int32_t* tb = kv.block_table + static_cast<size_t>(b) * kv.max_pages;
+  const int s = kv.page_shift, last = kv.max_pages - 1;
+  const int q0 = max(p0, 0);
+  const int pg0 = min(q0 >> s, last);
+  const int id0 = tb[pg0], id1 = tb[min(pg0 + 1, last)];
+#pragma unroll
+  for (int x = 0; x < N; ++x) {
+    const int p = p0 + x;
+    const int id = (p >> s) == pg0 ? id0 : id1;
+    out[x] = p < 0 || x >= valid ? -1 : (id << s) | (p & (kv.page_size - 1));
+  }
 }
 
 // Kept chunk starts of `stage` for row r (ascending, cnt[r][stage] of them).

@@ -312,6 +312,36 @@ def test_decode_head_slices(hq, hkv, d, page, batch):
     H.assert_close(out1.cpu().numpy(), out.cpu().numpy(), "one-call step vs two calls")
 
 
+@pytest.mark.parametrize("page", [4, 8, 16, 256])
+def test_decode_page_sizes(page):
+    """Paged decode across page sizes: 64-key stage-1 chunks over sixteen,
+    eight or four pages (row reads through the page table, or page ids held
+    in registers), later chunks resolved from the pages the top-K recorded
+    (pages of 8 keys and more), 256-key pages that chunks cross; 96 ragged
+    sequences; rows and outputs match the oracle, and the one-call step
+    (index rows resolved to pool rows for the attention) equals the two calls
+    bit for bit."""
+    # 96 sequences: the one-call step's tail is too wide for the fused kernel,
+    # so it takes the per-row top-K and the split attention over index rows
+    B = 96
+    cfg = gen.Config("decode-pages", "decode", B, 32, 8, 128, 6000, "bf16", 1,
+                     (64, 16, 4), (2048, 512, 128), 16, 64, seed=33, n_queries=1, page_size=page)
+    case = gen.make_case(cfg)
+    case.seq_lens[:] = [6000, 3500] + [6000 - 37 * b for b in range(2, B)]
+    for b, L in enumerate(case.seq_lens):
+        case.k[b] = case.k[b].sub((slice(None), slice(0, int(L))))
+        case.v[b] = case.v[b].sub((slice(None), slice(0, int(L))))
+    H.say(f"decode page size {page}")
+    dev = to_device(case)
+    idx, out, _ = check_decode(case, dev, [0, 1, 50, B - 1])
+    q = dev.q[0].contiguous()
+    idx1, out1 = api.prune_attend(q, dev.k, dev.v, params_of(cfg), seq_lens=dev.seq_lens,
+                                  block_table=dev.block_table, t=dev.t)
+    torch.cuda.synchronize()
+    assert torch.equal(idx1.view(idx.shape), idx)
+    assert torch.equal(out1, out)
+
+
 def _lib_width(case):
     from dynamic_sparse_attention_query_amd import _lib
     return _lib.index_width(params_of(case.cfg))
