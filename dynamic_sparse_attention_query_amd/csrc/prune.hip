@@ -128,9 +128,13 @@ __global__ void __launch_bounds__(NT) k_topk(PruneArgs a, int stage) {
       const int* tb = a.kv.block_table + static_cast<size_t>(b) * a.kv.max_pages;
       const int pg0 = st >> a.kv.page_shift;
       const int npg = ((st + l - 1) >> a.kv.page_shift) - pg0 + 1;
+      // all eight reads at once (clamped to the table row), then masked
+      const int last_pg = a.kv.max_pages - 1;
       int v[kKeptPages];
 #pragma unroll
-      for (int u = 0; u < kKeptPages; ++u) v[u] = npg <= kKeptPages && u < npg ? tb[pg0 + u] : -1;
+      for (int u = 0; u < kKeptPages; ++u) v[u] = tb[min(pg0 + u, last_pg)];
+#pragma unroll
+      for (int u = 0; u < kKeptPages; ++u) v[u] = npg <= kKeptPages && u < npg ? v[u] : -1;
       int4* dst = reinterpret_cast<int4*>(stage_pages(a, stage, r) + pos * kKeptPages);
 #pragma unroll
       for (int u = 0; u < kKeptPages / 4; ++u) dst[u] = make_int4(v[4 * u], v[4 * u + 1], v[4 * u + 2], v[4 * u + 3]);
