@@ -89,11 +89,17 @@ __device__ __forceinline__ void write_row_rest(const PruneArgs& a, int r, const 
 }
 
 // One workgroup per row: select the stage's kept chunks, write their starts
-// (and their count), and after the last stage the index row.
+// (and their count), and after the last stage the index row. Rows of up to
+// 4,096 chunks take the latency-oriented selection (select_keys: one pass
+// for bins sized to the row's range, the kept indices in LDS), after which
+// the threads write the kept chunks' outputs in kept order; longer rows take
+// select_row, whose owning thread writes each kept chunk.
 template <int E, int NT = kTopkThreads>
 __global__ void __launch_bounds__(NT) k_topk(PruneArgs a, int stage) {
-  __shared__ SelectLds<NT / 64> L;
+  constexpr bool kFast = NT == kTopkThreads && E <= 16;
+  __shared__ std::conditional_t<kFast, SelectKeysLds<NT / 64>, SelectLds<NT / 64>> L;
   __shared__ int sprev[kMaxKeptChunks];
+  __shared__ int skept[kFast ? E * NT : 1];           // kept indices (at most the row's E * NT chunks)
 
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
@@ -115,12 +121,11 @@ __global__ void __launch_bounds__(NT) k_topk(PruneArgs a, int stage) {
   int32_t* out = stage_starts(a, stage, r);
   int32_t* row = a.idx + static_cast<size_t>(r) * a.L;
   const int win_lo = last ? stage_mid_end(a, stage, r, geo) : 0;
-  // stores only after every load has been consumed (inside the selection):
-  // stores share the vector memory counter with loads, so an earlier store
-  // would hold up their wait. After the last stage each kept chunk writes
-  // its own entries of the index row.
   const bool pages = a.kv.block_table != nullptr && a.kpages != nullptr;
-  select_row<E, NT>(key, j0, nc, kc, L, [&](int j, int pos) {
+  // the outputs of kept chunk j in slot pos: its start, after the last stage
+  // its entries of the index row (and their pool rows), before it (paged
+  // decode) its page ids for the next stage
+  auto emit = [&](int j, int pos) {
     const int st = stage == 0 ? a.n_sink + (j << lg) : sprev[j >> sh] + ((j & ((1 << sh) - 1)) << lg);
     out[pos] = st;
     if (last) write_chunk_entries(row, a.L, geo.sink_hi + pos * l, st, l);
@@ -150,7 +155,17 @@ __global__ void __launch_bounds__(NT) k_topk(PruneArgs a, int stage) {
           if (x0 + u < l && i0 + x0 + u < a.L) prw[i0 + x0 + u] = v[u];
       }
     }
-  });
+  };
+  if constexpr (kFast) {
+    select_keys<E, NT>(key, nc, kc, L, skept);
+    __syncthreads();                            // skept holds the kept chunk indices, ascending
+    for (int pos = tid; pos < n_sel; pos += NT) emit(skept[pos], pos);
+  } else {
+    // stores only after every load has been consumed (inside the selection):
+    // stores share the vector memory counter with loads, so an earlier store
+    // would hold up their wait
+    select_row<E, NT>(key, j0, nc, kc, L, emit);
+  }
   if (tid == 0) record_stage(a, stage, r, n_sel, geo);
   if (last) write_row_rest(a, r, geo, n_sel, l, win_lo, pages ? a.prow : nullptr, b);
 }
